@@ -1,0 +1,33 @@
+"""Plain FP64 CPU oracle of the chunkwise state scan — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import anything from this package.  The product path (the
+HIP library and its Python binding) never imports, links or executes it, and
+this package shares no code with that path: the only thing both sides read is
+the seeded inputs drawn by ``workloads``.
+
+Contents
+--------
+gdr_ref   token-serial gated delta rule (outputs, pre-chunk states, final
+          states), per-segment summaries (local state and transition
+          product) and their serial composition.
+abc_ref   token-serial ABC normalised slot recurrence (cumulative
+          normaliser z, pre-chunk key/value slot states, final states).
+
+Every function is the plain definition, token by token, in float64 (or in
+exact rationals when handed ``fractions.Fraction`` object arrays); there is
+no blocking, chunking or reordering beyond recording the state at chunk
+starts.
+"""
+
+from .gdr_ref import (  # noqa: F401
+    CHUNK,
+    chunk_counts,
+    gdr_recurrent_fp64,
+    gdr_scan_sequence,
+    segment_bounds,
+    gdr_segment_summaries_fp64,
+    gdr_segment_compose_fp64,
+)
+from .abc_ref import abc_recurrent_fp64, abc_scan_sequence, abc_weighted_scan  # noqa: F401
+from .chunked_ref import gdr_chunked_fp64, chunked_scan_sequence, chunk_factors  # noqa: F401

@@ -1,0 +1,414 @@
+"""Pins of the FP64 oracle against facts that do not come from the oracle itself.
+
+Each ``check_*`` takes the oracle module(s) as arguments so the mutation tests
+can run the very same checks against deliberately broken copies of the
+oracle source.  A check raises AssertionError when the oracle disagrees with
+the independent fact it encodes:
+
+* brute force: dense transition matrices a_t (I - b_t k_t k_t^T) multiplied out
+  explicitly for short sequences;
+* exact rationals: the same products in ``fractions.Fraction`` arithmetic;
+* closed forms: pure decay when b = 0, exact recall of orthonormal keys when
+  a = b = 1, the ABC normaliser as a prefix log-sum-exp and the normalised
+  states as explicit weighted sums;
+* invariants: linearity in (S0, v), independence of packed sequences, linear
+  output scale, slot weights summing to one.
+"""
+
+from __future__ import annotations
+
+from fractions import Fraction as Fr
+
+import numpy as np
+
+TOL = 1e-12
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def _assert_close(a, b, tol=TOL, what=""):
+    r = rel(a, b)
+    assert r <= tol, f"{what}: relative L2 {r:.3e} > {tol:.1e}"
+
+
+def rand_problem(seed, L, H, DK, DV, contract=True):
+    """Small random float64 problem (one sequence): q, k unit rows, v normal,
+    a in (0, 1], b in (0, 1)."""
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((L, H, DK))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = r.standard_normal((L, H, DK))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((L, H, DV))
+    a = 1.0 / (1.0 + np.exp(-r.normal(3.0, 1.0, (L, H)))) if contract else np.ones((L, H))
+    b = 1.0 / (1.0 + np.exp(-r.standard_normal((L, H))))
+    S0 = 0.3 * r.standard_normal((H, DK, DV))
+    return q, k, v, a, b, S0
+
+
+# --------------------------------------------------------------------------- brute force
+def brute_force_states(k, v, a, b, S0):
+    """One head: explicit dense transitions.  Returns the list S_1..S_L where
+    S_t = P(t,1) S0 + sum_{i<=t} P(t,i+1) b_i k_i v_i^T and P(t,j) = A_t...A_j."""
+    L, DK = k.shape
+    A = [a[t] * (np.eye(DK) - b[t] * np.outer(k[t], k[t])) for t in range(L)]
+    out = []
+    for t in range(L):
+        # P(t, 1) = A_t ... A_1, built by left-multiplying in token order
+        P_all = np.eye(DK)
+        for j in range(0, t + 1):
+            P_all = A[j] @ P_all
+        S = P_all @ S0
+        for i in range(t + 1):
+            Pi = np.eye(DK)
+            for j in range(i + 1, t + 1):
+                Pi = A[j] @ Pi
+            S = S + Pi @ (b[i] * np.outer(k[i], v[i]))
+        out.append(S)
+    return out
+
+
+def check_brute_force(gdr_ref):
+    L, H, DK, DV, C = 13, 2, 5, 3, 4
+    q, k, v, a, b, S0 = rand_problem(11, L, H, DK, DV)
+    o, pre, ST = gdr_ref.gdr_scan_sequence(q, k, v, a, b, S0, 1.0, C)
+    for h in range(H):
+        Ss = brute_force_states(k[:, h], v[:, h], a[:, h], b[:, h], S0[h])
+        _assert_close(ST[h], Ss[-1], what="final state vs dense products")
+        o_bf = np.stack([Ss[t].T @ q[t, h] for t in range(L)])
+        _assert_close(o[:, h], o_bf, what="outputs vs dense products")
+        starts = list(range(0, L, C))
+        assert pre.shape[0] == len(starts), "one pre-chunk state per chunk"
+        for c, t0 in enumerate(starts):
+            ref = S0[h] if t0 == 0 else Ss[t0 - 1]
+            _assert_close(pre[c, h], ref, what=f"pre-chunk state {c}")
+
+
+# --------------------------------------------------------------------------- exact rationals
+def _fr_matmul(A, B):
+    n, m = len(A), len(B[0])
+    kk = len(B)
+    return [[sum((A[i][x] * B[x][j] for x in range(kk)), Fr(0)) for j in range(m)] for i in range(n)]
+
+
+def check_rationals(gdr_ref):
+    """dk = dv = 3, T = 5, one head, every input a small rational: exact equality."""
+    r = np.random.default_rng(5)
+    L, D = 5, 3
+
+    def fr(x, den=8):
+        return Fr(int(round(x * den)), den)
+
+    q = [[fr(x) for x in r.standard_normal(D)] for _ in range(L)]
+    k = [[fr(x) for x in r.standard_normal(D)] for _ in range(L)]
+    v = [[fr(x) for x in r.standard_normal(D)] for _ in range(L)]
+    a = [Fr(int(r.integers(5, 16)), 16) for _ in range(L)]
+    b = [Fr(int(r.integers(1, 8)), 8) for _ in range(L)]
+    S0 = [[fr(x, 4) for x in r.standard_normal(D)] for _ in range(D)]
+    # dense transition products in exact arithmetic
+    S = S0
+    o_ref, pre_ref = [], []
+    for t in range(L):
+        if t % 2 == 0:
+            pre_ref.append(S)
+        A = [[a[t] * ((Fr(1) if i == j else Fr(0)) - b[t] * k[t][i] * k[t][j]) for j in range(D)]
+             for i in range(D)]
+        S = _fr_matmul(A, S)
+        S = [[S[i][j] + b[t] * k[t][i] * v[t][j] for j in range(D)] for i in range(D)]
+        o_ref.append([sum((S[i][j] * q[t][i] for i in range(D)), Fr(0)) for j in range(D)])
+
+    def obj(x, shape):
+        arr = np.empty(shape, dtype=object)
+        arr[...] = np.array(x, dtype=object).reshape(shape)
+        return arr
+
+    o, pre, ST = gdr_ref.gdr_scan_sequence(
+        obj(q, (L, 1, D)), obj(k, (L, 1, D)), obj(v, (L, 1, D)), obj(a, (L, 1)), obj(b, (L, 1)),
+        obj(S0, (1, D, D)), Fr(1), 2)
+    assert all(ST[0, i, j] == S[i][j] for i in range(D) for j in range(D)), "final state not exact"
+    assert all(o[t, 0, j] == o_ref[t][j] for t in range(L) for j in range(D)), "outputs not exact"
+    assert len(pre) == len(pre_ref)
+    for c in range(len(pre_ref)):
+        assert all(pre[c, 0, i, j] == pre_ref[c][i][j] for i in range(D) for j in range(D)), \
+            f"pre-chunk state {c} not exact"
+
+
+# --------------------------------------------------------------------------- closed forms
+def check_pure_decay(gdr_ref):
+    L, H, DK, DV, C = 40, 3, 6, 4, 16
+    q, k, v, a, b, S0 = rand_problem(21, L, H, DK, DV)
+    b = np.zeros_like(b)
+    o, pre, ST = gdr_ref.gdr_scan_sequence(q, k, v, a, b, S0, 1.0, C)
+    cum = np.cumprod(a, axis=0)                              # prod_{s<=t} a_s
+    _assert_close(ST, cum[-1][:, None, None] * S0, what="b=0 final state")
+    o_cf = cum[:, :, None] * np.einsum("hkv,thk->thv", S0, q)
+    _assert_close(o, o_cf, what="b=0 outputs")
+    for c, t0 in enumerate(range(0, L, C)):
+        f = np.ones(H) if t0 == 0 else cum[t0 - 1]
+        _assert_close(pre[c], f[:, None, None] * S0, what=f"b=0 pre-chunk {c}")
+
+
+def check_exact_recall(gdr_ref):
+    DK, DV, L = 8, 5, 6
+    r = np.random.default_rng(31)
+    Qm, _ = np.linalg.qr(r.standard_normal((DK, DK)))
+    K = Qm[:L]                                              # orthonormal keys
+    V = r.standard_normal((L, DV))
+    S0 = r.standard_normal((DK, DV))
+    o, pre, ST = gdr_ref.gdr_scan_sequence(K[:, None], K[:, None], V[:, None], np.ones((L, 1)),
+                                           np.ones((L, 1)), S0[None], 1.0, 64)
+    _assert_close(ST[0], (np.eye(DK) - K.T @ K) @ S0 + K.T @ V, TOL, "recall closed form")
+    for t in range(L):
+        _assert_close(ST[0].T @ K[t], V[t], TOL, f"recall of key {t}")
+    # overwrite: the same key twice keeps only the second value
+    k1 = K[0]
+    kk = np.stack([k1, k1])[:, None]
+    vv = np.stack([V[0], V[1]])[:, None]
+    _, _, S2 = gdr_ref.gdr_scan_sequence(kk, kk, vv, np.ones((2, 1)), np.ones((2, 1)), S0[None], 1.0, 64)
+    _assert_close(S2[0].T @ k1, V[1], TOL, "overwrite")
+    _assert_close(S2[0], (np.eye(DK) - np.outer(k1, k1)) @ S0 + np.outer(k1, V[1]), TOL, "overwrite state")
+
+
+# --------------------------------------------------------------------------- invariants
+def check_linearity(gdr_ref):
+    L, H, DK, DV = 20, 2, 6, 5
+    q, k, v, a, b, S0 = rand_problem(41, L, H, DK, DV)
+    _, _, v2, _, _, S02 = rand_problem(42, L, H, DK, DV)
+    al, be = 0.7, -1.3
+    o1, p1, T1 = gdr_ref.gdr_scan_sequence(q, k, v, a, b, S0, 1.0, 8)
+    o2, p2, T2 = gdr_ref.gdr_scan_sequence(q, k, v2, a, b, S02, 1.0, 8)
+    o3, p3, T3 = gdr_ref.gdr_scan_sequence(q, k, al * v + be * v2, a, b, al * S0 + be * S02, 1.0, 8)
+    _assert_close(o3, al * o1 + be * o2, 1e-11, "linearity of outputs")
+    _assert_close(T3, al * T1 + be * T2, 1e-11, "linearity of final state")
+    _assert_close(p3, al * p1 + be * p2, 1e-11, "linearity of pre-chunk states")
+    o4, _, _ = gdr_ref.gdr_scan_sequence(q, k, v, a, b, S0, 0.25, 8)
+    _assert_close(o4, 0.25 * o1, 1e-14, "output scale")
+
+
+def check_sequence_independence(gdr_ref):
+    lengths = [5, 70, 1, 64, 0, 130]
+    H, DK, DV = 2, 6, 4
+    r = np.random.default_rng(51)
+    Ttot = sum(lengths)
+    q = r.standard_normal((1, Ttot, H, DK))
+    k = r.standard_normal((1, Ttot, H, DK)) / 3
+    v = r.standard_normal((1, Ttot, H, DV))
+    g = -np.abs(r.standard_normal((1, Ttot, H))) * 0.05
+    beta = r.uniform(0, 1, (1, Ttot, H))
+    h0 = r.standard_normal((len(lengths), H, DK, DV))
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    full = gdr_ref.gdr_recurrent_fp64(q, k, v, g, beta, h0, cu, 1.0)
+    offs = full["chunk_offsets"]
+    assert list(np.diff(offs)) == [(x + 63) // 64 for x in lengths], "chunk counts"
+    for n, L in enumerate(lengths):
+        s, e = cu[n], cu[n + 1]
+        one = gdr_ref.gdr_recurrent_fp64(q[:, s:e], k[:, s:e], v[:, s:e], g[:, s:e], beta[:, s:e],
+                                         h0[n:n + 1], None, 1.0)
+        _assert_close(full["o"][:, s:e], one["o"], 1e-15, f"seq {n} outputs")
+        _assert_close(full["hT"][n], one["hT"][0], 1e-15, f"seq {n} final")
+        _assert_close(full["h"][offs[n]:offs[n + 1]], one["h"], 1e-15, f"seq {n} pre-chunk")
+        if L == 0:
+            _assert_close(full["hT"][n], h0[n], 0.0, "empty sequence keeps h0")
+
+
+def check_delta_definition(gdr_ref):
+    """The recorded write vectors satisfy delta_t = b_t (v_t - a_t S_{t-1}^T k_t)."""
+    L, H, DK, DV = 9, 2, 5, 3
+    q, k, v, a, b, S0 = rand_problem(61, L, H, DK, DV)
+    _, _, _, d = gdr_ref.gdr_scan_sequence(q, k, v, a, b, S0, 1.0, 64, return_delta=True)
+    for h in range(H):
+        Ss = [S0[h]] + brute_force_states(k[:, h], v[:, h], a[:, h], b[:, h], S0[h])
+        for t in range(L):
+            ref = b[t, h] * (v[t, h] - a[t, h] * Ss[t].T @ k[t, h])
+            _assert_close(d[t, h], ref, TOL, f"delta_{t}")
+
+
+def check_chunk_algebra(gdr_ref, chunked_ref):
+    """The chunked WY form equals the token recurrence at several chunk sizes."""
+    lengths = [1, 63, 64, 65, 150]
+    H, DK, DV = 2, 8, 6
+    r = np.random.default_rng(71)
+    Ttot = sum(lengths)
+    q = r.standard_normal((1, Ttot, H, DK))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = r.standard_normal((1, Ttot, H, DK))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((1, Ttot, H, DV))
+    g = np.log(1 / (1 + np.exp(-r.normal(4, 1, (1, Ttot, H)))))
+    beta = 1 / (1 + np.exp(-r.standard_normal((1, Ttot, H))))
+    h0 = 0.1 * r.standard_normal((len(lengths), H, DK, DV))
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    for C in (1, 2, 7, 16, 64):
+        a = gdr_ref.gdr_recurrent_fp64(q, k, v, g, beta, h0, cu, 0.5, chunk=C)
+        c = chunked_ref.gdr_chunked_fp64(q, k, v, g, beta, h0, cu, 0.5, chunk=C)
+        for key in ("o", "v_new", "h", "hT"):
+            _assert_close(c[key], a[key], 1e-12, f"chunk {C} {key}")
+
+
+def check_segment_algebra(gdr_ref):
+    L, H, DK, DV, P = 600, 2, 6, 4, 4
+    q, k, v, a, b, S0 = rand_problem(81, L, H, DK, DV)
+    g = np.log(a)
+    bounds = gdr_ref.segment_bounds(L, P)
+    assert bounds[0][0] == 0 and bounds[-1][1] == L
+    assert all(bounds[i][1] == bounds[i + 1][0] for i in range(P - 1))
+    assert all(t0 % 64 == 0 for t0, _ in bounds)
+    S_loc, M = gdr_ref.gdr_segment_summaries_fp64(k, v, g, b, bounds)
+    # transition products against dense matrices
+    for s, (t0, t1) in enumerate(bounds):
+        for h in range(H):
+            D = np.eye(DK)
+            for t in range(t0, t1):
+                D = a[t, h] * (np.eye(DK) - b[t, h] * np.outer(k[t, h], k[t, h])) @ D
+            _assert_close(M[s, h], D, 1e-12, f"M_{s}")
+    inits, SP = gdr_ref.gdr_segment_compose_fp64(S_loc, M, S0)
+    serial = gdr_ref.gdr_recurrent_fp64(q[None], k[None], v[None], g[None], b[None], S0[None], None)
+    _assert_close(SP, serial["hT"][0], 1e-12, "composed final state")
+    for s, (t0, _) in enumerate(bounds):
+        _assert_close(inits[s], serial["h"][t0 // 64], 1e-12, f"segment {s} initial state")
+    # one segment: S_T = M S0 + S_loc
+    S_loc1, M1 = gdr_ref.gdr_segment_summaries_fp64(k, v, g, b, [(0, L)])
+    _assert_close(np.matmul(M1[0], S0) + S_loc1[0], serial["hT"][0], 1e-12, "affine summary")
+
+
+def check_segment_bounds(gdr_ref):
+    """The even chunk split: 1024 chunks over 16 segments, a ragged split, and
+    more segments than chunks."""
+    b = gdr_ref.segment_bounds(65536, 16)
+    assert b == [(64 * 64 * s, 64 * 64 * (s + 1)) for s in range(16)]
+    # 10 chunks over 4 segments -> 3, 3, 2, 2 chunks; the tail ends at L
+    b = gdr_ref.segment_bounds(600, 4)
+    assert b == [(0, 192), (192, 384), (384, 512), (512, 600)], b
+    b = gdr_ref.segment_bounds(100, 4)
+    assert b == [(0, 64), (64, 100), (100, 100), (100, 100)], b
+
+
+GDR_CHECKS = [check_segment_bounds, check_brute_force, check_rationals, check_pure_decay, check_exact_recall,
+              check_linearity, check_sequence_independence, check_delta_definition,
+              check_segment_algebra]
+
+
+# --------------------------------------------------------------------------- ABC
+def _cum_lse(s):
+    """log sum_{i<=t} exp(s_i) along axis 0, computed by explicit prefix sums of
+    exp(s - max) (a different route from the oracle's pairwise logaddexp)."""
+    m = np.max(s, axis=0, keepdims=True)
+    return np.log(np.cumsum(np.exp(s - m), axis=0)) + m
+
+
+def check_abc_closed_form(abc_ref):
+    T, H, K, M, V = 150, 2, 5, 4, 3
+    r = np.random.default_rng(91)
+    k = r.standard_normal((T, H, K))
+    v = r.standard_normal((T, H, V))
+    s = r.standard_normal((T, H, M)) * 2
+    z, hk_pre, hv_pre, hk, hv = abc_ref.abc_scan_sequence(k, v, s, 64)
+    zc = _cum_lse(s)
+    _assert_close(z, zc, 1e-13, "normaliser = prefix log-sum-exp")
+    for c, t0 in enumerate(range(0, T, 64)):
+        if t0 == 0:
+            assert np.all(hk_pre[0] == 0) and np.all(hv_pre[0] == 0)
+            continue
+        wts = np.exp(s[:t0] - zc[t0 - 1][None])              # [t0, H, M]
+        _assert_close(hk_pre[c], np.einsum("thk,thm->hkm", k[:t0], wts), 1e-12, f"Hk pre {c}")
+        _assert_close(hv_pre[c], np.einsum("thm,thv->hmv", wts, v[:t0]), 1e-12, f"Hv pre {c}")
+    wts = np.exp(s - zc[-1][None])
+    _assert_close(hk, np.einsum("thk,thm->hkm", k, wts), 1e-12, "Hk final")
+    _assert_close(hv, np.einsum("thm,thv->hmv", wts, v), 1e-12, "Hv final")
+
+
+def check_abc_ones(abc_ref):
+    T, H, K, M, V = 130, 2, 3, 4, 5
+    r = np.random.default_rng(92)
+    s = r.standard_normal((T, H, M)) * 3
+    _, hk_pre, hv_pre, hk, hv = abc_ref.abc_scan_sequence(np.ones((T, H, K)), np.ones((T, H, V)), s, 64)
+    _assert_close(hk, np.ones_like(hk), 1e-14, "weights sum to one (Hk)")
+    _assert_close(hv, np.ones_like(hv), 1e-14, "weights sum to one (Hv)")
+    _assert_close(hk_pre[1:], np.ones_like(hk_pre[1:]), 1e-14, "pre-chunk Hk")
+
+
+def check_abc_constant_logits(abc_ref):
+    T, H, K, M, V = 100, 1, 4, 3, 2
+    r = np.random.default_rng(93)
+    k = r.standard_normal((T, H, K))
+    v = r.standard_normal((T, H, V))
+    s = np.broadcast_to(r.standard_normal((1, H, M)), (T, H, M)).copy()
+    _, _, _, hk, hv = abc_ref.abc_scan_sequence(k, v, s, 64)
+    mk = k.mean(axis=0)                                       # [H, K]
+    mv = v.mean(axis=0)
+    _assert_close(hk, np.broadcast_to(mk[:, :, None], hk.shape), 1e-13, "running mean (Hk)")
+    _assert_close(hv, np.broadcast_to(mv[:, None, :], hv.shape), 1e-13, "running mean (Hv)")
+
+
+def check_abc_rationals(abc_ref):
+    """Weights given directly as rationals: exact match with the explicit sum
+    H_T = sum_t x_t (x) w_t prod_{u>t} r_u."""
+    T, K, M, V = 6, 2, 3, 2
+    r = np.random.default_rng(94)
+
+    def fr(x):
+        return Fr(int(round(x * 8)), 8)
+
+    def obj(a):
+        o = np.empty(a.shape, dtype=object)
+        o[...] = a
+        return o
+
+    k = obj(np.array([[fr(x) for x in r.standard_normal(K)] for _ in range(T)], dtype=object))
+    v = obj(np.array([[fr(x) for x in r.standard_normal(V)] for _ in range(T)], dtype=object))
+    w = obj(np.array([[Fr(int(r.integers(1, 9)), 8) for _ in range(M)] for _ in range(T)], dtype=object))
+    rr = obj(np.array([[Fr(int(r.integers(1, 9)), 9) for _ in range(M)] for _ in range(T)], dtype=object))
+    hk, hv = abc_ref.abc_weighted_scan(k, v, w, rr)
+    for i in range(K):
+        for m in range(M):
+            ref = Fr(0)
+            for t in range(T):
+                f = Fr(1)
+                for u in range(t + 1, T):
+                    f *= rr[u, m]
+                ref += k[t, i] * w[t, m] * f
+            assert hk[i, m] == ref, "Hk not exact"
+    for m in range(M):
+        for j in range(V):
+            ref = Fr(0)
+            for t in range(T):
+                f = Fr(1)
+                for u in range(t + 1, T):
+                    f *= rr[u, m]
+                ref += w[t, m] * v[t, j] * f
+            assert hv[m, j] == ref, "Hv not exact"
+
+
+def check_abc_chunk_affine(abc_ref):
+    """Chaining S_out = S_in * r_c + c_c per 64-token chunk reproduces the states."""
+    T, H, K, M, V = 200, 2, 4, 3, 5
+    r = np.random.default_rng(95)
+    k = r.standard_normal((T, H, K))
+    v = r.standard_normal((T, H, V))
+    s = r.standard_normal((T, H, M))
+    z, hk_pre, hv_pre, hk, hv = abc_ref.abc_scan_sequence(k, v, s, 64)
+    zc = _cum_lse(s)
+    Sk = np.zeros((H, K, M))
+    Sv = np.zeros((H, M, V))
+    zprev = np.full((H, M), -np.inf)
+    for c, t0 in enumerate(range(0, T, 64)):
+        t1 = min(t0 + 64, T)
+        _assert_close(hk_pre[c], Sk, 1e-12, f"affine Hk {c}")
+        _assert_close(hv_pre[c], Sv, 1e-12, f"affine Hv {c}")
+        zl = zc[t1 - 1]
+        E = np.exp(s[t0:t1] - zl[None])
+        rc = np.exp(zprev - zl)
+        Sk = Sk * rc[:, None, :] + np.einsum("thk,thm->hkm", k[t0:t1], E)
+        Sv = Sv * rc[:, :, None] + np.einsum("thm,thv->hmv", E, v[t0:t1])
+        zprev = zl
+    _assert_close(hk, Sk, 1e-12, "affine Hk final")
+    _assert_close(hv, Sv, 1e-12, "affine Hv final")
+
+
+ABC_CHECKS = [check_abc_closed_form, check_abc_ones, check_abc_constant_logits,
+              check_abc_rationals, check_abc_chunk_affine]

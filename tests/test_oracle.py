@@ -1,0 +1,22 @@
+"""CPU pins of the FP64 oracle (no GPU): every check encodes a fact that does
+not come from the oracle itself (dense products, exact rationals, closed
+forms, invariants)."""
+
+import pytest
+
+import oracle_pins as P
+from oracle import abc_ref, chunked_ref, gdr_ref
+
+
+@pytest.mark.parametrize("check", P.GDR_CHECKS, ids=lambda f: f.__name__)
+def test_gdr_oracle_pin(check):
+    check(gdr_ref)
+
+
+def test_chunked_form_equals_token_recurrence():
+    P.check_chunk_algebra(gdr_ref, chunked_ref)
+
+
+@pytest.mark.parametrize("check", P.ABC_CHECKS, ids=lambda f: f.__name__)
+def test_abc_oracle_pin(check):
+    check(abc_ref)

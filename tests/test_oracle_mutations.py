@@ -1,0 +1,93 @@
+"""Plant plausible mistakes in copies of the oracle source (on the CPU) and
+require the pins to catch every one of them."""
+
+import importlib.util
+import os
+import sys
+import types
+
+import pytest
+
+import oracle_pins as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _load_mutant(relpath, old, new, name):
+    src = open(os.path.join(ROOT, relpath)).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    src = src.replace(old, new, 1)
+    mod = types.ModuleType(name)
+    mod.__file__ = os.path.join(ROOT, relpath)
+    sys.modules[name] = mod
+    exec(compile(src, mod.__file__, "exec"), mod.__dict__)
+    return mod
+
+
+GDR_MUTANTS = {
+    "dropped_decay": ("S = a[t][:, None, None] * S", "S = S"),
+    "decay_after_write": ("S = a[t][:, None, None] * S\n", "S = S\n"),
+    "wrong_sign": ("err = v[t] - pred", "err = v[t] + pred"),
+    "dropped_beta": ("delta = b[t][:, None] * err", "delta = err"),
+    "query_for_key": ('pred = np.einsum("hk,hkv->hv", kt, S)', 'pred = np.einsum("hk,hkv->hv", q[t], S)'),
+    "transposed_state": ('pred = np.einsum("hk,hkv->hv", kt, S)', 'pred = np.einsum("hk,hvk->hv", kt, S)'),
+    "output_uses_key": ('o[t] = scale * np.einsum("hk,hkv->hv", q[t], S)',
+                        'o[t] = scale * np.einsum("hk,hkv->hv", kt, S)'),
+    "dropped_scale": ('o[t] = scale * np.einsum', 'o[t] = 1.0 * np.einsum'),
+    "prechunk_off_by_one": ("if t % chunk == 0:", "if t % chunk == 1:"),
+    "compose_order": ("S = np.matmul(M[s], S) + S_loc[s]", "S = np.matmul(S, M[s]) + S_loc[s]"),
+    "compose_drop_local": ("S = np.matmul(M[s], S) + S_loc[s]", "S = np.matmul(M[s], S)"),
+    "segment_extra_to_last": ("nc = base + (1 if s < extra else 0)",
+                              "nc = base + (1 if s >= n_segments - extra else 0)"),
+}
+
+
+@pytest.mark.parametrize("mut", sorted(GDR_MUTANTS))
+def test_gdr_pins_catch(mut):
+    old, new = GDR_MUTANTS[mut]
+    if mut == "decay_after_write":
+        # move the decay after the write: S_t = a (S + b k (v - S^T k)^T)
+        old = "        S = a[t][:, None, None] * S\n"
+        new = "        pass\n"
+        m = _load_mutant("oracle/gdr_ref.py", old, new, f"mut_{mut}")
+        src_old = "        vnew[t] = delta\n"
+        # re-load with the decay applied after the write instead
+        src = open(os.path.join(ROOT, "oracle/gdr_ref.py")).read()
+        src = src.replace(old, new, 1).replace(src_old, src_old + "        S = a[t][:, None, None] * S\n", 1)
+        m = types.ModuleType(f"mut_{mut}")
+        exec(compile(src, "gdr_ref_mut", "exec"), m.__dict__)
+    else:
+        m = _load_mutant("oracle/gdr_ref.py", old, new, f"mut_{mut}")
+    failures = 0
+    for check in P.GDR_CHECKS:
+        try:
+            check(m)
+        except Exception:
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {mut}"
+
+
+ABC_MUTANTS = {
+    "ratio_inverted": ("r = np.exp(z_prev - zt)", "r = np.exp(zt - z_prev)"),
+    "unnormalised_weight": ("w = np.exp(s[t] - zt)", "w = np.exp(s[t] - z_prev)"),
+    "missing_logaddexp": ("zt = np.logaddexp(z_prev, s[t])", "zt = np.maximum(z_prev, s[t])"),
+    "hk_scaled_on_rows": ("Hk = Hk * r[:, None, :]", "Hk = Hk * r[:, :1, None]"),
+    "hv_scaled_on_cols": ("Hv = Hv * r[:, :, None]", "Hv = Hv * r[:, None, :1]"),
+    "prechunk_after_update": ("        if t % chunk == 0:\n            hk_pre.append(Hk.copy())",
+                              "        if t % chunk == 1:\n            hk_pre.append(Hk.copy())"),
+    "weighted_scan_sign": ("Hk = Hk * r[t][None, :] + np.outer(k[t], w[t])",
+                           "Hk = Hk * r[t][None, :] - np.outer(k[t], w[t])"),
+}
+
+
+@pytest.mark.parametrize("mut", sorted(ABC_MUTANTS))
+def test_abc_pins_catch(mut):
+    old, new = ABC_MUTANTS[mut]
+    m = _load_mutant("oracle/abc_ref.py", old, new, f"mut_abc_{mut}")
+    failures = 0
+    for check in P.ABC_CHECKS:
+        try:
+            check(m)
+        except Exception:
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {mut}"
