@@ -1,0 +1,211 @@
+/*
+ * gdr.h — C ABI of the chunkwise gated-delta state scan for AMD Instinct
+ * MI355X (gfx950), and of its ABC diagonal-affine sibling.
+ *
+ * Sources of the operations (the pages the library is built from):
+ *   [kev#259]  kev pull request #259 (autotune cache split by sequence count
+ *              for fla's DeltaNet state-scan kernel) — the per-chunk state
+ *              scan run inside each DeltaNet layer, its value-block width BV,
+ *              packed variable-length batches counted from cu_seqlens, and the
+ *              property that all tile configs give bit-identical output
+ *              (opening section; "Why 4 sequences").
+ *   [cuLA#127] cuLA pull request #127 — intracard context parallelism: a
+ *              pre-scan that forms a segment's local state and its affine
+ *              transition kept canonically in FP32, composed segment after
+ *              segment ("Summary"; "Root cause and implementation"), and
+ *              initial/final-state and transposed-state layouts ("Validation").
+ *   [fla#23]   flash-linear-attention fork issue #23, "[Perf][B300]
+ *              Parallelize ABC chunk state construction with affine
+ *              summaries" — the ABC slot states advanced per 64-token chunk
+ *              as state_out = state_in * r + c, with r from the cumulative
+ *              normaliser z ("Problem"; "Proposed Dataflow").
+ *
+ * The recurrence (one sequence, one head; a_t = exp(g_t), b_t = beta_t):
+ *     S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T,   o_t = scale * S_t^T q_t
+ * computed per 64-token chunk in the WY form: prepare (g_cum, w, u), scan
+ * (v_new = u - w S; emit S before the chunk; S <- e^{g_last} S +
+ * K^T (v_new * e^{g_last - g})), output (o from q, k, v_new, h).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers without a _host suffix are DEVICE pointers owned by the caller;
+ *    the library never allocates, frees or retains them.  Every device
+ *    pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *    enqueued on it, nothing is synchronised, and GDR_OK means "enqueued".
+ *  - Arguments are validated completely before any launch: on an error
+ *    return nothing has been enqueued and no output was written.
+ *    gdr_last_error() gives a message for the calling thread.
+ *  - No C++ exception crosses the ABI; the library holds no mutable global
+ *    state, so concurrent calls from several threads are safe.
+ *  - Layouts are contiguous, time-major ("public layout", [fla#23] fixture
+ *    contract):
+ *        q, k, w            [B, T, H, DK]   storage dtype
+ *        v, u, v_new, o     [B, T, H, DV]   storage dtype
+ *        g, beta, g_cum     [B, T, H]       float32
+ *        h                  [NT, H, DV, DK] storage dtype; h[c, :, j, i] = S_c[i, j]
+ *                           (value-major: the state before chunk c, transposed)
+ *        h0, hT             [N, H, DK, DV] float32 (GDR_STATE_KV) or
+ *                           [N, H, DV, DK] float32 (GDR_STATE_VK)
+ *    A packed batch uses B = 1, T = total tokens and cu_seqlens_host with N+1
+ *    entries; sequence n is tokens [cu[n], cu[n+1]).  Chunks restart at each
+ *    sequence start; NT = sum_n ceil(L_n / 64), sequences in order.
+ *  - Supported: DK, DV in {64, 128}; float32 or bfloat16 storage.  Chunk size
+ *    is 64 tokens.
+ */
+#ifndef GDR_H_
+#define GDR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDR_OK = 0,
+  GDR_ERR_INVALID_ARG = 1, /* bad pointer, size, layout or cu_seqlens        */
+  GDR_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for     */
+  GDR_ERR_HIP = 3          /* a HIP runtime call or launch failed            */
+} gdr_status;
+
+typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+/* Layout of h0/hT: KV = [.., DK, DV] (the state as written), VK = its transpose
+ * ([cuLA#127] "Validation" lists both layouts). */
+typedef enum { GDR_STATE_KV = 0, GDR_STATE_VK = 1 } gdr_state_layout;
+
+typedef struct {
+  int32_t B;                       /* batch rows; 1 for a packed batch            */
+  int64_t T;                       /* tokens per row, or total packed tokens      */
+  int32_t H, DK, DV;               /* heads, key width, value width               */
+  int32_t N;                       /* sequences: B (dense) or len(cu_seqlens) - 1 */
+  const int32_t* cu_seqlens_host;  /* N+1 host ints, or NULL for dense rows; read
+                                      during the call only                        */
+  gdr_dtype dtype;                 /* storage of q, k, v, w, u, v_new, o and h    */
+  gdr_state_layout state_layout;   /* layout of h0 and hT                         */
+} gdr_problem;
+
+/* Tile of the serial scans.  bv: value columns per workgroup (the BV of
+ * [kev#259]); waves: wavefronts per workgroup, each owning bv/waves columns
+ * (a multiple of 16); stages: 1 = load a chunk then compute it, 2 = fetch the
+ * next chunk while computing the current one.  Every supported tile gives
+ * bit-identical results.  NULL = the scheduler's choice. */
+typedef struct {
+  int32_t bv, waves, stages;
+} gdr_tile;
+
+/* Segment-parallel final pass (see gdr_state_scan): each sequence is split
+ * into n_segments chunk-aligned segments and segment s of sequence n starts
+ * from seg_init[n * n_segments + s]. */
+typedef struct {
+  int32_t n_segments;
+  const float* seg_init;           /* [N * n_segments, H, DV, DK] float32 */
+} gdr_segments;
+
+/* Number of chunks NT = sum_n ceil(L_n / 64) (rows of h); -1 on invalid input. */
+int64_t gdr_num_chunks(const gdr_problem* p);
+
+/* Chunk preparation (WY factors).  Per (sequence, head, chunk) with n valid
+ * tokens, gamma = inclusive cumulative sum of g inside the chunk,
+ *   A[t,i] = beta_t exp(gamma_t - gamma_i) (k_t . k_i) for i < t,
+ *   T = (I + A)^-1 (forward substitution, FP32),
+ *   w = T diag(beta exp(gamma)) K,   u = T diag(beta) V.
+ * Writes g_cum = gamma (float32), w and u (storage dtype) for every valid
+ * token; nothing past a sequence's last token.  [kev#259] opening section
+ * (the scan consumes these factors). */
+gdr_status gdr_chunk_prepare(const gdr_problem* p, const void* k, const void* v,
+                             const float* g, const float* beta, float* g_cum, void* w,
+                             void* u, void* stream);
+
+/* The inter-chunk state scan ([kev#259] opening section): for every
+ * (sequence, head), serially over its chunks c with n valid tokens,
+ *   h[c] = S;  v_new = u_c - w_c S;  S <- e^{g_last} S + K_c^T (v_new * e^{g_last - g}),
+ * g_last = g_cum of the chunk's last valid token; rows past n are masked.
+ * S starts from h0[n] (NULL = zeros) and hT[n] receives the final state.
+ * h (NULL = not written) and v_new (NULL = not written) use the storage
+ * dtype; S is held in FP32 throughout.
+ * With `seg` non-NULL this is the segmented final pass of [cuLA#127]: every
+ * segment runs from seg->seg_init (h0 is then ignored), so segments of one
+ * sequence run in parallel; hT is written by each sequence's last segment.
+ * Results are bit-identical for every tile and between dense rows and the
+ * same rows packed with cu_seqlens. */
+gdr_status gdr_state_scan(const gdr_problem* p, const gdr_tile* tile, const gdr_segments* seg,
+                          const void* k, const void* w, const void* u, const float* g_cum,
+                          const float* h0, void* h, void* v_new, float* hT, void* stream);
+
+/* Chunk output: for token t of chunk c (same sequence),
+ *   o_t = scale * ( e^{gamma_t} q_t^T S_c + sum_{i <= t in chunk} e^{gamma_t - gamma_i} (q_t . k_i) v_new_i ),
+ * S_c read from h (storage dtype, value-major).  Equals scale * S_t^T q_t of the
+ * token recurrence.  Writes o for every valid token. */
+gdr_status gdr_chunk_output(const gdr_problem* p, const void* q, const void* k,
+                            const void* v_new, const void* h, const float* g_cum, float scale,
+                            void* o, void* stream);
+
+/* Segment summaries, the pre-scan of [cuLA#127] ("Root cause and
+ * implementation"): each sequence is split into n_segments chunk-aligned
+ * segments (NT_n chunks dealt out evenly, the first NT_n mod P segments one
+ * more).  For segment s the chunk recurrence runs from zero on the value
+ * columns (local state S_loc) and from the identity with zero values on DK
+ * extra columns (the transition M_s, the product of the segment's
+ * per-token transitions), so that a state entering the segment leaves as
+ * M_s S_in + S_loc.  Both are FP32:
+ *   seg_state  [N * P, H, DV, DK]   S_loc, value-major
+ *   seg_trans  [N * P, H, DK, DK]   M_s, row-major (M[i][j]) */
+gdr_status gdr_segment_summaries(const gdr_problem* p, const gdr_tile* tile, int32_t n_segments,
+                                 const void* k, const void* w, const void* u,
+                                 const float* g_cum, float* seg_state, float* seg_trans,
+                                 void* stream);
+
+/* Segment composition ([cuLA#127] "Root cause and implementation"), in FP32,
+ * serially over the segments of each sequence:
+ *   S_init(0) = h0[n] (NULL = zeros);  S_init(s+1) = M_s S_init(s) + S_loc(s).
+ * seg_init [N * P, H, DV, DK] value-major; hT (nullable) receives
+ * M_{P-1} S_init(P-1) + S_loc(P-1) in the state_layout of p. */
+gdr_status gdr_segment_compose(const gdr_problem* p, int32_t n_segments, const float* seg_state,
+                               const float* seg_trans, const float* h0, float* seg_init,
+                               float* hT, void* stream);
+
+/* ABC slot-state construction ([fla#23] "Problem", "Proposed Dataflow").
+ * Per batch row and head, with slot logits s_t and z_t = log(e^{z_{t-1}} + e^{s_t})
+ * (z_0 = -inf, no initial state), per 64-token chunk c ending at token e:
+ *   r_c = exp(z_{prev chunk end} - z_e),   E_t = exp(s_t - z_e),
+ *   Hk <- Hk * r_c[None, :] + K_c^T E      ([K x M], slots on columns)
+ *   Hv <- Hv * r_c[:, None] + E^T V_c      ([M x V], slots on rows)
+ * with the chunk contributions formed in FP32 and the states kept in FP32.
+ * Layouts: k [B, T, H, K], v [B, T, H, V], s [B, T, H, M] (storage dtype);
+ * z (nullable) [B, T, H, M] float32; hk [B, NC, H, K, M] and hv [B, NC, H, M, V]
+ * the states before every chunk (storage dtype); hk_final [B, H, K, M] and
+ * hv_final [B, H, M, V] float32 (nullable).  Supported: K, V multiples of 64,
+ * M = 64, bfloat16 storage. */
+typedef struct {
+  int32_t B;
+  int64_t T;
+  int32_t H, K, M, V;
+  gdr_dtype dtype;
+} abc_problem;
+
+/* Device workspace abc_affine_scan needs (bytes). */
+size_t abc_workspace_size(const abc_problem* p);
+
+gdr_status abc_affine_scan(const abc_problem* p, const void* k, const void* v, const void* s,
+                           float* z, void* hk, void* hv, float* hk_final, float* hv_final,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code. */
+const char* gdr_status_string(gdr_status s);
+/* Message of the last failed call on this thread ("" if none). */
+const char* gdr_last_error(void);
+
+/* Scheduler introspection (host only, no GPU needed): the tile and grid the
+ * scan would use.  out[0..5] = bv, waves, stages, workgroups, launches,
+ * rows per launch (max). */
+gdr_status gdr_plan_query(const gdr_problem* p, const gdr_tile* tile, int32_t n_segments,
+                          int64_t out[6]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H_ */

@@ -1,0 +1,20 @@
+"""MI355X-native chunkwise state scan of the gated delta rule (and the ABC
+diagonal-affine slot-state scan): hand-written gfx950 HIP kernels behind a
+C ABI (include/gdr.h), bound here with ctypes.  PyTorch supplies device
+memory and the HIP stream only."""
+
+from .binding import (  # noqa: F401
+    GdrError,
+    LIB_PATH,
+    abc_affine_scan,
+    abc_workspace_size,
+    chunk_gated_delta_rule,
+    gdr_chunk_output,
+    gdr_chunk_prepare,
+    gdr_num_chunks,
+    gdr_plan_query,
+    gdr_segment_compose,
+    gdr_segment_summaries,
+    gdr_state_scan,
+    lib,
+)

@@ -1,0 +1,299 @@
+// C-ABI entry points (include/gdr.h): argument checks, planning, dispatch.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/gdr.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+gdr_status fail(gdr_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+gdr_status need(const void* p, const char* name) {
+  if (p == nullptr) return fail(GDR_ERR_INVALID_ARG, std::string(name) + " must not be NULL");
+  if (!aligned16(p)) return fail(GDR_ERR_INVALID_ARG, std::string(name) + " must be 16-byte aligned");
+  return GDR_OK;
+}
+
+gdr_status opt(const void* p, const char* name) {
+  if (p != nullptr && !aligned16(p)) return fail(GDR_ERR_INVALID_ARG, std::string(name) + " must be 16-byte aligned");
+  return GDR_OK;
+}
+
+#define GDR_TRY(x)                   \
+  do {                               \
+    gdr_status _s = (x);             \
+    if (_s != GDR_OK) return _s;     \
+  } while (0)
+
+gdr_status parse(const gdr_problem* p, gdr::Problem& out) {
+  if (p == nullptr) return fail(GDR_ERR_INVALID_ARG, "problem must not be NULL");
+  std::string err;
+  if (!gdr::parse_problem(p->B, p->T, p->H, p->DK, p->DV, p->N, p->cu_seqlens_host, p->dtype, p->state_layout, out,
+                          err))
+    return fail(GDR_ERR_INVALID_ARG, err);
+  return GDR_OK;
+}
+
+gdr_status tile_for(const gdr::Problem& pr, const gdr_tile* tile, int mode, gdr::Tile& t) {
+  std::string err;
+  int32_t req[3];
+  const int32_t* r = nullptr;
+  if (tile != nullptr) {
+    req[0] = tile->bv;
+    req[1] = tile->waves;
+    req[2] = tile->stages;
+    r = req;
+  }
+  if (!gdr::choose_tile(pr, r, mode, t, err)) return fail(GDR_ERR_UNSUPPORTED, err);
+  return GDR_OK;
+}
+
+gdr_status hip_fail(hipError_t e, const char* what) {
+  return fail(GDR_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+gdr_status run_scan(const gdr::Problem& pr, const gdr::Tile& t, int mode, int P, const void* k, const void* w,
+                    const void* u, const float* g_cum, const float* h_in, int in_vk, void* h, void* v_new,
+                    float* h_out, int out_vk, float* trans_out, hipStream_t stream) {
+  const int kmode = (mode == 1) ? 1 : 0;
+  gdr::LaunchFn fn = gdr::find_scan(pr.dtype, pr.DK, t.bv, t.waves, t.stages, kmode);
+  if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no scan kernel for this dtype/DK/tile");
+  const bool has_in = (h_in != nullptr);
+  const bool has_out = (h_out != nullptr);
+  std::vector<gdr::Launch> plan = gdr::plan_scan(pr, t, mode, P, has_in, has_out);
+  gdr::ScanArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = k;
+  a.w = w;
+  a.u = u;
+  a.g_cum = g_cum;
+  a.h_in = h_in;
+  a.h = h;
+  a.v_new = v_new;
+  a.h_out = h_out;
+  a.trans_out = trans_out;
+  a.H = pr.H;
+  a.DV = pr.DV;
+  a.in_vk = in_vk;
+  a.out_vk = out_vk;
+  a.n_blk = (kmode == 1) ? (pr.DV + pr.DK) / t.bv : pr.DV / t.bv;
+  for (const gdr::Launch& l : plan) {
+    if (l.grid == 0) continue;
+    a.n_rows = static_cast<int32_t>(l.rows.size());
+    memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
+    hipError_t e = fn(&a, l.grid, stream);
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
+  }
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdr_status_string(gdr_status s) {
+  switch (s) {
+    case GDR_OK: return "GDR_OK";
+    case GDR_ERR_INVALID_ARG: return "GDR_ERR_INVALID_ARG";
+    case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED";
+    case GDR_ERR_HIP: return "GDR_ERR_HIP";
+  }
+  return "unknown gdr_status";
+}
+
+const char* gdr_last_error(void) { return g_err.c_str(); }
+
+int64_t gdr_num_chunks(const gdr_problem* p) {
+  gdr::Problem pr;
+  if (parse(p, pr) != GDR_OK) return -1;
+  return pr.n_chunks;
+}
+
+gdr_status gdr_chunk_prepare(const gdr_problem* p, const void* k, const void* v, const float* g,
+                             const float* beta, float* g_cum, void* w, void* u, void* stream) {
+  g_err.clear();
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  GDR_TRY(need(k, "k"));
+  GDR_TRY(need(v, "v"));
+  GDR_TRY(need(g, "g"));
+  GDR_TRY(need(beta, "beta"));
+  GDR_TRY(need(g_cum, "g_cum"));
+  GDR_TRY(need(w, "w"));
+  GDR_TRY(need(u, "u"));
+  gdr::LaunchFn fn = gdr::find_prepare(pr.dtype, pr.DK, pr.DV);
+  if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no prepare kernel for this dtype/DK/DV");
+  gdr::ChunkArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.g_cum = g_cum;
+  a.w = w;
+  a.u = u;
+  a.H = pr.H;
+  for (const gdr::Launch& l : gdr::plan_chunks(pr, 1)) {
+    a.n_rows = static_cast<int32_t>(l.rows.size());
+    a.n_chunks = l.n_chunks;
+    a.chunk_base = l.chunk_base;
+    memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
+    hipError_t e = fn(&a, l.grid, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "prepare launch");
+  }
+  return GDR_OK;
+}
+
+gdr_status gdr_state_scan(const gdr_problem* p, const gdr_tile* tile, const gdr_segments* seg, const void* k,
+                          const void* w, const void* u, const float* g_cum, const float* h0, void* h, void* v_new,
+                          float* hT, void* stream) {
+  g_err.clear();
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  GDR_TRY(need(k, "k"));
+  GDR_TRY(need(w, "w"));
+  GDR_TRY(need(u, "u"));
+  GDR_TRY(need(g_cum, "g_cum"));
+  GDR_TRY(opt(h0, "h0"));
+  GDR_TRY(opt(h, "h"));
+  GDR_TRY(opt(v_new, "v_new"));
+  GDR_TRY(opt(hT, "hT"));
+  int mode = 0, P = 1;
+  const float* h_in = h0;
+  int in_vk = pr.state_vk;
+  if (seg != nullptr) {
+    if (seg->n_segments < 1) return fail(GDR_ERR_INVALID_ARG, "n_segments must be >= 1");
+    GDR_TRY(need(seg->seg_init, "seg_init"));
+    mode = 2;
+    P = seg->n_segments;
+    h_in = seg->seg_init;
+    in_vk = 1;
+  }
+  gdr::Tile t;
+  GDR_TRY(tile_for(pr, tile, mode == 2 ? 0 : 0, t));
+  return run_scan(pr, t, mode, P, k, w, u, g_cum, h_in, in_vk, h, v_new, hT, pr.state_vk, nullptr,
+                  static_cast<hipStream_t>(stream));
+}
+
+gdr_status gdr_chunk_output(const gdr_problem* p, const void* q, const void* k, const void* v_new, const void* h,
+                            const float* g_cum, float scale, void* o, void* stream) {
+  g_err.clear();
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  GDR_TRY(need(q, "q"));
+  GDR_TRY(need(k, "k"));
+  GDR_TRY(need(v_new, "v_new"));
+  GDR_TRY(need(h, "h"));
+  GDR_TRY(need(g_cum, "g_cum"));
+  GDR_TRY(need(o, "o"));
+  gdr::LaunchFn fn = gdr::find_output(pr.dtype, pr.DK, pr.DV);
+  if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no output kernel for this dtype/DK/DV");
+  gdr::ChunkArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v_new;
+  a.g = g_cum;
+  a.h = h;
+  a.o = o;
+  a.scale = scale;
+  a.H = pr.H;
+  for (const gdr::Launch& l : gdr::plan_chunks(pr, pr.DV / 64)) {
+    a.n_rows = static_cast<int32_t>(l.rows.size());
+    a.n_chunks = l.n_chunks;
+    a.chunk_base = l.chunk_base;
+    memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
+    hipError_t e = fn(&a, l.grid, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "output launch");
+  }
+  return GDR_OK;
+}
+
+gdr_status gdr_segment_summaries(const gdr_problem* p, const gdr_tile* tile, int32_t n_segments, const void* k,
+                                 const void* w, const void* u, const float* g_cum, float* seg_state,
+                                 float* seg_trans, void* stream) {
+  g_err.clear();
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  if (n_segments < 1) return fail(GDR_ERR_INVALID_ARG, "n_segments must be >= 1");
+  GDR_TRY(need(k, "k"));
+  GDR_TRY(need(w, "w"));
+  GDR_TRY(need(u, "u"));
+  GDR_TRY(need(g_cum, "g_cum"));
+  GDR_TRY(need(seg_state, "seg_state"));
+  GDR_TRY(need(seg_trans, "seg_trans"));
+  gdr::Tile t;
+  GDR_TRY(tile_for(pr, tile, 1, t));
+  return run_scan(pr, t, 1, n_segments, k, w, u, g_cum, nullptr, 0, nullptr, nullptr, seg_state, 1, seg_trans,
+                  static_cast<hipStream_t>(stream));
+}
+
+gdr_status gdr_segment_compose(const gdr_problem* p, int32_t n_segments, const float* seg_state,
+                               const float* seg_trans, const float* h0, float* seg_init, float* hT, void* stream) {
+  g_err.clear();
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  if (n_segments < 1) return fail(GDR_ERR_INVALID_ARG, "n_segments must be >= 1");
+  GDR_TRY(need(seg_state, "seg_state"));
+  GDR_TRY(need(seg_trans, "seg_trans"));
+  GDR_TRY(need(seg_init, "seg_init"));
+  GDR_TRY(opt(h0, "h0"));
+  GDR_TRY(opt(hT, "hT"));
+  gdr::LaunchFn fn = gdr::find_compose(pr.DK);
+  if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no compose kernel for this DK");
+  if (pr.N == 0) return GDR_OK;
+  gdr::ComposeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.seg_state = seg_state;
+  a.seg_trans = seg_trans;
+  a.h0 = h0;
+  a.seg_init = seg_init;
+  a.hT = hT;
+  a.H = pr.H;
+  a.DV = pr.DV;
+  a.P = n_segments;
+  a.N = pr.N;
+  a.state_vk = pr.state_vk;
+  const int grid = pr.N * pr.H * (pr.DV / 16);
+  hipError_t e = fn(&a, grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "compose launch");
+  return GDR_OK;
+}
+
+gdr_status gdr_plan_query(const gdr_problem* p, const gdr_tile* tile, int32_t n_segments, int64_t out[6]) {
+  g_err.clear();
+  if (out == nullptr) return fail(GDR_ERR_INVALID_ARG, "out must not be NULL");
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  const int mode = n_segments > 0 ? 1 : 0;
+  gdr::Tile t;
+  GDR_TRY(tile_for(pr, tile, mode, t));
+  std::vector<gdr::Launch> plan = gdr::plan_scan(pr, t, mode, n_segments > 0 ? n_segments : 1, true, true);
+  int64_t wg = 0, maxrows = 0;
+  for (auto& l : plan) {
+    wg += l.grid;
+    maxrows = std::max<int64_t>(maxrows, static_cast<int64_t>(l.rows.size()));
+  }
+  out[0] = t.bv;
+  out[1] = t.waves;
+  out[2] = t.stages;
+  out[3] = wg;
+  out[4] = static_cast<int64_t>(plan.size());
+  out[5] = maxrows;
+  return GDR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Launch-argument structs and launcher declarations shared by the host API
+// and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace gdr {
+
+// Serial chunk scan (plain scan, segmented final pass, segment summaries).
+struct ScanArgs {
+  const void* k;
+  const void* w;
+  const void* u;
+  const float* g_cum;
+  const float* h_in;   // h0 or seg_init (nullable)
+  void* h;             // pre-chunk states (nullable)
+  void* v_new;         // (nullable)
+  float* h_out;        // hT or seg_state (nullable)
+  float* trans_out;    // seg_trans (summaries only)
+  int32_t H;
+  int32_t DV;
+  int32_t in_vk;       // layout of h_in: 1 = [.., DV, DK], 0 = [.., DK, DV]
+  int32_t out_vk;      // layout of h_out
+  int32_t n_rows;
+  int32_t n_blk;       // column blocks per (row, head)
+  Row rows[kMaxRows];
+};
+
+// Chunk-parallel kernels (prepare, output): rows in natural order, each
+// workgroup finds its row by the row's first chunk.
+struct ChunkArgs {
+  const void* q;
+  const void* k;
+  const void* v;       // v (prepare) or v_new (output)
+  const float* g;      // g (prepare) or g_cum (output)
+  const float* beta;
+  const void* h;       // output: pre-chunk states
+  float* g_cum;        // prepare output
+  void* w;             // prepare output
+  void* u;             // prepare output
+  void* o;             // output output
+  float scale;
+  int32_t H;
+  int32_t n_rows;
+  int32_t n_chunks;    // chunks covered by this launch
+  int32_t chunk_base;  // h row of this launch's first chunk
+  Row rows[kMaxRows];  // chunk_off relative to chunk_base
+};
+
+struct ComposeArgs {
+  const float* seg_state;
+  const float* seg_trans;
+  const float* h0;
+  float* seg_init;
+  float* hT;
+  int32_t H;
+  int32_t DV;
+  int32_t P;
+  int32_t N;
+  int32_t state_vk;
+};
+
+struct AbcArgs {
+  const void* k;
+  const void* v;
+  const void* s;
+  float* z;            // nullable full normaliser
+  float* zc;           // workspace: [B, NC, H, M] normaliser at chunk ends
+  void* hk;
+  void* hv;
+  float* hk_final;
+  float* hv_final;
+  int32_t B;
+  int32_t T;
+  int32_t H, K, M, V;
+  int32_t NC;
+};
+
+using LaunchFn = hipError_t (*)(const void* args, int grid, hipStream_t stream);
+
+// Lookup of an instantiated kernel; nullptr when the combination is not built.
+LaunchFn find_scan(int dtype, int dk, int bv, int waves, int stages, int mode);
+LaunchFn find_prepare(int dtype, int dk, int dv);
+LaunchFn find_output(int dtype, int dk, int dv);
+LaunchFn find_compose(int dk);
+hipError_t launch_abc_z(const AbcArgs& a, hipStream_t s);
+hipError_t launch_abc_scan(const AbcArgs& a, hipStream_t s);
+
+}  // namespace gdr

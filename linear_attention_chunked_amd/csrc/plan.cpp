@@ -1,0 +1,239 @@
+// Host-side scheduler (see plan.hpp).  Plain C++: no HIP calls, so the
+// argument checks and plans can be exercised without a GPU.
+#include "plan.hpp"
+
+#include <stdlib.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <numeric>
+
+namespace gdr {
+
+bool parse_problem(int B, int64_t T, int H, int DK, int DV, int N, const int32_t* cu, int dtype,
+                   int state_layout, Problem& p, std::string& err) {
+  if (B < 1 || T < 0 || H < 1) {
+    err = "B >= 1, T >= 0 and H >= 1 are required";
+    return false;
+  }
+  if (!((DK == 64 || DK == 128) && (DV == 64 || DV == 128))) {
+    err = "DK and DV must each be 64 or 128";
+    return false;
+  }
+  if (dtype != 0 && dtype != 1) {
+    err = "dtype must be GDR_F32 or GDR_BF16";
+    return false;
+  }
+  if (state_layout != 0 && state_layout != 1) {
+    err = "state_layout must be GDR_STATE_KV or GDR_STATE_VK";
+    return false;
+  }
+  if (static_cast<int64_t>(B) * T > INT32_MAX || static_cast<int64_t>(B) * T * H > (int64_t(1) << 40)) {
+    err = "too many tokens for one call (B*T must fit in int32)";
+    return false;
+  }
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.DK = DK;
+  p.DV = DV;
+  p.dtype = dtype;
+  p.state_vk = state_layout;
+  p.seqs.clear();
+  if (cu == nullptr) {
+    if (N != B) {
+      err = "dense rows need N == B";
+      return false;
+    }
+    for (int b = 0; b < B; ++b) p.seqs.push_back({static_cast<int64_t>(b) * T, T, 0});
+  } else {
+    if (B != 1) {
+      err = "packed sequences (cu_seqlens) need B == 1";
+      return false;
+    }
+    if (N < 0) {
+      err = "N must be >= 0";
+      return false;
+    }
+    if (cu[0] != 0) {
+      err = "cu_seqlens[0] must be 0";
+      return false;
+    }
+    for (int n = 0; n < N; ++n) {
+      if (cu[n + 1] < cu[n]) {
+        err = "cu_seqlens must be non-decreasing (entry " + std::to_string(n + 1) + ")";
+        return false;
+      }
+      p.seqs.push_back({cu[n], static_cast<int64_t>(cu[n + 1]) - cu[n], 0});
+    }
+    if (static_cast<int64_t>(cu[N]) != T) {
+      err = "cu_seqlens[N] must equal T";
+      return false;
+    }
+  }
+  p.N = static_cast<int>(p.seqs.size());
+  int64_t c = 0;
+  for (auto& s : p.seqs) {
+    s.chunk_off = c;
+    c += (s.len + kChunk - 1) / kChunk;
+  }
+  p.n_chunks = c;
+  if (c > INT32_MAX / 2) {
+    err = "too many chunks";
+    return false;
+  }
+  return true;
+}
+
+// Built tiles (must match the instantiations in scan.hip).
+static bool tile_built(int dtype, int bv, int waves, int stages) {
+  static const int bf16_tiles[][3] = {{32, 2, 1}, {32, 2, 2}, {64, 2, 2}, {64, 4, 1}, {64, 4, 2}, {128, 4, 2}};
+  static const int f32_tiles[][3] = {{32, 2, 1}, {32, 2, 2}, {64, 4, 1}, {64, 4, 2}};
+  if (dtype == 1) {
+    for (auto& t : bf16_tiles)
+      if (t[0] == bv && t[1] == waves && t[2] == stages) return true;
+  } else {
+    for (auto& t : f32_tiles)
+      if (t[0] == bv && t[1] == waves && t[2] == stages) return true;
+  }
+  return false;
+}
+
+bool choose_tile(const Problem& p, const int32_t* req, int mode, Tile& t, std::string& err) {
+  int r[3] = {0, 0, 0};
+  if (req != nullptr) {
+    r[0] = req[0];
+    r[1] = req[1];
+    r[2] = req[2];
+  } else if (const char* env = getenv("GDR_FORCE_TILE")) {
+    if (sscanf(env, "%d,%d,%d", &r[0], &r[1], &r[2]) != 3) {
+      err = "GDR_FORCE_TILE must be 'bv,waves,stages'";
+      return false;
+    }
+  } else {
+    // Fixed shape-class table.  64-column blocks with 4 waves and one chunk
+    // of prefetch is the default; problems whose (row, head) pairs alone
+    // cannot fill the 256 CUs twice over use 32-column blocks for more units.
+    const int64_t pairs = static_cast<int64_t>(p.N) * p.H;
+    r[0] = 64;
+    r[1] = 4;
+    r[2] = 2;
+    if (pairs * (p.DV / 64) < 512 && p.DV >= 64) {
+      r[0] = 32;
+      r[1] = 2;
+      r[2] = 2;
+    }
+  }
+  if (!tile_built(p.dtype, r[0], r[1], r[2])) {
+    err = "tile (bv=" + std::to_string(r[0]) + ", waves=" + std::to_string(r[1]) +
+          ", stages=" + std::to_string(r[2]) + ") is not built for this dtype";
+    return false;
+  }
+  if (r[0] > p.DV || p.DV % r[0] != 0) {
+    err = "bv must divide DV";
+    return false;
+  }
+  if (mode == 1 && p.DK % r[0] != 0) {
+    err = "bv must divide DK for segment summaries";
+    return false;
+  }
+  t.bv = r[0];
+  t.waves = r[1];
+  t.stages = r[2];
+  return true;
+}
+
+void segment_bounds(int64_t len, int P, std::vector<int64_t>& t0, std::vector<int64_t>& t1) {
+  // NT chunks dealt out evenly; the first NT mod P segments get one more.
+  const int64_t nt = (len + kChunk - 1) / kChunk;
+  const int64_t base = nt / P, extra = nt % P;
+  t0.clear();
+  t1.clear();
+  int64_t c = 0;
+  for (int s = 0; s < P; ++s) {
+    const int64_t nc = base + (s < extra ? 1 : 0);
+    t0.push_back(std::min(c * kChunk, len));
+    t1.push_back(std::min((c + nc) * kChunk, len));
+    c += nc;
+  }
+}
+
+static void finish_scan_launch(Launch& l, int H, int nblk) {
+  const int64_t pairs = static_cast<int64_t>(l.rows.size()) * H;
+  l.grid = static_cast<int>(8 * nblk * ((pairs + 7) / 8));
+}
+
+std::vector<Launch> plan_scan(const Problem& p, const Tile& t, int mode, int P, bool has_h0, bool has_hT) {
+  std::vector<Row> rows;
+  if (mode == 0) {
+    for (int n = 0; n < p.N; ++n) {
+      const Seq& s = p.seqs[n];
+      rows.push_back(Row{static_cast<int32_t>(s.bos), static_cast<int32_t>(s.len),
+                         static_cast<int32_t>(s.chunk_off), has_h0 ? n : -1, has_hT ? n : -1});
+    }
+  } else {
+    std::vector<int64_t> t0, t1;
+    for (int n = 0; n < p.N; ++n) {
+      const Seq& s = p.seqs[n];
+      segment_bounds(s.len, P, t0, t1);
+      for (int k = 0; k < P; ++k) {
+        const int seg = n * P + k;
+        Row r;
+        r.bos = static_cast<int32_t>(s.bos + t0[k]);
+        r.len = static_cast<int32_t>(t1[k] - t0[k]);
+        r.chunk_off = static_cast<int32_t>(s.chunk_off + t0[k] / kChunk);
+        if (mode == 1) {
+          r.in_idx = -1;
+          r.out_idx = seg;
+        } else {
+          r.in_idx = seg;
+          r.out_idx = (k == P - 1 && has_hT) ? n : -1;
+        }
+        rows.push_back(r);
+      }
+    }
+  }
+  // longest first (stable, so equal lengths keep their order)
+  std::stable_sort(rows.begin(), rows.end(), [](const Row& a, const Row& b) { return a.len > b.len; });
+  const int nblk = (mode == 1) ? (p.DV + p.DK) / t.bv : p.DV / t.bv;
+  std::vector<Launch> out;
+  for (size_t i = 0; i < rows.size(); i += kMaxRows) {
+    Launch l;
+    l.rows.assign(rows.begin() + i, rows.begin() + std::min(rows.size(), i + kMaxRows));
+    finish_scan_launch(l, p.H, nblk);
+    out.push_back(std::move(l));
+  }
+  return out;
+}
+
+std::vector<Launch> plan_chunks(const Problem& p, int blocks_per_chunk) {
+  std::vector<Launch> out;
+  Launch cur;
+  int64_t base = -1;
+  auto flush = [&]() {
+    if (!cur.rows.empty()) {
+      cur.grid = cur.n_chunks * p.H * blocks_per_chunk;
+      out.push_back(std::move(cur));
+    }
+    cur = Launch();
+    base = -1;
+  };
+  const int64_t max_chunks = (int64_t(1) << 30) / (static_cast<int64_t>(p.H) * blocks_per_chunk);
+  for (const Seq& s : p.seqs) {
+    const int64_t nc = (s.len + kChunk - 1) / kChunk;
+    if (nc == 0) continue;
+    if (!cur.rows.empty() && (cur.rows.size() >= static_cast<size_t>(kMaxRows) || cur.n_chunks + nc > max_chunks))
+      flush();
+    if (base < 0) {
+      base = s.chunk_off;
+      cur.chunk_base = static_cast<int>(base);
+    }
+    cur.rows.push_back(Row{static_cast<int32_t>(s.bos), static_cast<int32_t>(s.len),
+                           static_cast<int32_t>(s.chunk_off - base), -1, -1});
+    cur.n_chunks += static_cast<int>(nc);
+  }
+  flush();
+  return out;
+}
+
+}  // namespace gdr

@@ -1,0 +1,69 @@
+// Host-side scheduler: turns a problem description into per-launch plans.
+//
+// The scan is serial over chunks inside a unit, so what the scheduler
+// controls is which units exist and in which order the hardware dispatches
+// them:
+//   * a unit is (row, head, block of BV value columns); a row is a sequence,
+//     or a chunk-aligned segment of one in the segment-parallel passes;
+//   * rows are ordered longest first, so the longest serial chains start
+//     first and short rows fill in behind them;
+//   * the plan travels by value in the kernel arguments (at most kMaxRows rows
+//     per launch; more rows take more launches), so a call needs no device
+//     workspace, no host-to-device copy and no synchronisation;
+//   * the tile (BV, waves, stages) comes from a fixed table keyed by the
+//     problem's shape class, never from timing at run time, so the first call
+//     cannot decide the tile of later ones (the failure mode kev pull request
+//     #259 describes in its opening section).
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "common.hpp"
+
+namespace gdr {
+
+struct Seq {
+  int64_t bos;
+  int64_t len;
+  int64_t chunk_off;  // first chunk (row of h) of this sequence
+};
+
+struct Problem {
+  int B = 0, H = 0, DK = 0, DV = 0, N = 0;
+  int64_t T = 0;
+  int dtype = 0;
+  int state_vk = 0;
+  std::vector<Seq> seqs;
+  int64_t n_chunks = 0;
+};
+
+struct Tile {
+  int bv = 0, waves = 0, stages = 0;
+};
+
+struct Launch {
+  std::vector<Row> rows;
+  int grid = 0;
+  int n_chunks = 0;    // chunk-parallel launches
+  int chunk_base = 0;  // chunk-parallel launches
+};
+
+// Parses and validates; on failure returns false and sets err.
+bool parse_problem(int B, int64_t T, int H, int DK, int DV, int N, const int32_t* cu_host, int dtype,
+                   int state_layout, Problem& out, std::string& err);
+
+// Tile for the serial scans: explicit request (validated) or the table.
+bool choose_tile(const Problem& p, const int32_t* req /* bv, waves, stages or null */, int mode, Tile& out,
+                 std::string& err);
+
+// Segment boundaries of one sequence: [t0, t1) token ranges relative to its start.
+void segment_bounds(int64_t len, int P, std::vector<int64_t>& t0, std::vector<int64_t>& t1);
+
+// Plans.  mode 0 = plain scan, 2 = segmented final pass, 1 = summaries.
+std::vector<Launch> plan_scan(const Problem& p, const Tile& t, int mode, int P, bool has_h0, bool has_hT);
+std::vector<Launch> plan_chunks(const Problem& p, int blocks_per_chunk);
+
+}  // namespace gdr

@@ -1,0 +1,141 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, validates arguments before any launch, and the scheduler's
+plans are what the design says."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_chunked_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n.startswith(("gdr_", "abc_"))))
+
+
+def test_every_declared_symbol_is_exported():
+    L = B.lib()
+    names = _declared()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(L, n), f"missing export {n}"
+
+
+def _prob(B_=1, T=128, H=2, DK=128, DV=128, N=None, cu=None, dtype=B.GDR_BF16, layout=0):
+    arr = None
+    if cu is not None:
+        arr = (ctypes.c_int32 * len(cu))(*cu)
+        N = len(cu) - 1
+    elif N is None:
+        N = B_
+    p = B.gdr_problem(B_, T, H, DK, DV, N, arr, dtype, layout)
+    return p, arr
+
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
+
+
+def _scan(p, k=FAKE, w=FAKE, u=FAKE, g=FAKE, h0=None, tile=None):
+    t = None if tile is None else ctypes.byref(B.gdr_tile(*tile))
+    return B.lib().gdr_state_scan(ctypes.byref(p), t, None, k, w, u, g, h0, None, None, None, None)
+
+
+@pytest.mark.parametrize("cu,T", [([1, 5, 9], 9), ([0, 5, 3], 5), ([0, 5, 9], 10)])
+def test_bad_cu_seqlens_rejected(cu, T):
+    p, keep = _prob(T=T, cu=cu)
+    assert _scan(p) == B.GDR_ERR_INVALID_ARG
+    assert B.lib().gdr_last_error().decode()
+
+
+def test_packed_needs_single_row():
+    p, keep = _prob(B_=2, T=9, cu=[0, 4, 9])
+    assert _scan(p) == B.GDR_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 128), (128, 96), (256, 128)])
+def test_unsupported_dims(dk, dv):
+    p, _ = _prob(DK=dk, DV=dv)
+    assert _scan(p) == B.GDR_ERR_INVALID_ARG
+
+
+def test_null_and_misaligned_pointers():
+    p, _ = _prob()
+    assert _scan(p, k=None) == B.GDR_ERR_INVALID_ARG
+    assert b"k must not be NULL" in B.lib().gdr_last_error()
+    assert _scan(p, u=ctypes.c_void_p(0x10004)) == B.GDR_ERR_INVALID_ARG
+    assert b"aligned" in B.lib().gdr_last_error()
+    assert _scan(p, h0=ctypes.c_void_p(0x10008)) == B.GDR_ERR_INVALID_ARG
+
+
+def test_unbuilt_tile_rejected():
+    p, _ = _prob()
+    assert _scan(p, tile=(48, 3, 1)) == B.GDR_ERR_UNSUPPORTED
+    p, _ = _prob(DV=64)
+    assert _scan(p, tile=(128, 4, 2)) == B.GDR_ERR_UNSUPPORTED  # bv must divide DV
+
+
+def test_num_chunks():
+    p, keep = _prob(T=3400, cu=[0, 130, 130, 269, 3400])
+    # ceil(130/64)=3, 0, ceil(139/64)=3, ceil(3131/64)=49
+    assert B.lib().gdr_num_chunks(ctypes.byref(p)) == 3 + 0 + 3 + 49
+    p, _ = _prob(B_=3, T=65)
+    assert B.lib().gdr_num_chunks(ctypes.byref(p)) == 6
+
+
+def _query(p, tile=None, nseg=0):
+    out = (ctypes.c_int64 * 6)()
+    t = None if tile is None else ctypes.byref(B.gdr_tile(*tile))
+    st = B.lib().gdr_plan_query(ctypes.byref(p), t, nseg, out)
+    assert st == B.GDR_OK, B.lib().gdr_last_error()
+    return tuple(out)
+
+
+def test_plan_grid_and_launch_split():
+    # 300 sequences -> 3 launches of <= 112 rows; grid padded to whole XCD groups of 8 pairs
+    cu = [0]
+    for i in range(300):
+        cu.append(cu[-1] + 1 + (i % 70))
+    p, keep = _prob(T=cu[-1], cu=cu, H=3)
+    bv, waves, stages, wgs, launches, maxrows = _query(p, tile=(64, 4, 2))
+    assert (bv, waves, stages) == (64, 4, 2)
+    assert launches == 3 and maxrows == 112
+    pairs = [112 * 3, 112 * 3, 76 * 3]
+    assert wgs == sum(8 * 2 * ((x + 7) // 8) for x in pairs)
+
+
+def test_plan_segments_and_table():
+    p, _ = _prob(B_=1, T=65536, H=8)
+    bv, waves, stages, wgs, launches, maxrows = _query(p, nseg=16)
+    assert maxrows == 16 and launches == 1
+    # summaries run DV + DK columns
+    assert wgs == 8 * ((128 + 128) // bv) * ((16 * 8 + 7) // 8)
+
+
+def test_force_tile_env(monkeypatch):
+    p, _ = _prob(B_=4, T=256, H=32)
+    monkeypatch.setenv("GDR_FORCE_TILE", "128,4,2")
+    assert _query(p)[:3] == (128, 4, 2)
+    monkeypatch.setenv("GDR_FORCE_TILE", "bogus")
+    out = (ctypes.c_int64 * 6)()
+    assert B.lib().gdr_plan_query(ctypes.byref(p), None, 0, out) == B.GDR_ERR_UNSUPPORTED
+
+
+def test_cpu_tensors_rejected():
+    import torch
+
+    k = torch.zeros(1, 64, 1, 64)
+    with pytest.raises(ValueError):
+        B.gdr_chunk_prepare(k, k, torch.zeros(1, 64, 1), torch.zeros(1, 64, 1))
+
+
+def test_status_strings():
+    L = B.lib()
+    assert L.gdr_status_string(0) == b"GDR_OK"
+    assert L.gdr_status_string(3) == b"GDR_ERR_HIP"

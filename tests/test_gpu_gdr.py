@@ -1,0 +1,298 @@
+"""GPU parity of the gated-delta path against the FP64 oracle, plus the
+bit-identity contracts (tiles, dense vs packed, resume at a chunk boundary,
+run-to-run).  Every call goes through the C ABI (ctypes binding).
+
+Tolerances (relative L2 over a whole tensor, oracle as reference): 1e-5 for
+float32 storage and 1e-2 for bfloat16 storage.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import make_config, make_gdr
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-5, torch.bfloat16: 1e-2}
+
+
+@pytest.fixture(scope="module")
+def pkg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_attention_chunked_amd as p
+
+    p.lib()
+    return p
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def to_np(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def dev(t):
+    return None if t is None else t.cuda()
+
+
+def run_path(pkg, inp, n_segments=None, tile=None, scale=None, state_layout="kv"):
+    h0 = dev(inp.h0)
+    if h0 is not None and state_layout == "vk":
+        h0 = h0.transpose(-1, -2).contiguous()
+    q, k, v, g, b = (dev(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    g_cum, w, u = pkg.gdr_chunk_prepare(k, v, g, b, inp.cu_seqlens)
+    if n_segments is None:
+        h, v_new, hT = pkg.gdr_state_scan(k, w, u, g_cum, h0, inp.cu_seqlens, tile, state_layout=state_layout)
+        extra = {}
+    else:
+        ss, st = pkg.gdr_segment_summaries(k, w, u, g_cum, n_segments, inp.cu_seqlens, tile)
+        si, hTc = pkg.gdr_segment_compose(k, v.shape[-1], ss, st, n_segments, h0, inp.cu_seqlens,
+                                          state_layout=state_layout, emit_final=True)
+        h, v_new, hT = pkg.gdr_state_scan(k, w, u, g_cum, None, inp.cu_seqlens, tile, n_segments, si,
+                                          state_layout=state_layout)
+        extra = {"seg_state": ss, "seg_trans": st, "seg_init": si, "hT_compose": hTc}
+    o = pkg.gdr_chunk_output(q, k, v_new, h, g_cum, inp.scale if scale is None else scale, inp.cu_seqlens)
+    torch.cuda.synchronize()
+    if state_layout == "vk":
+        hT = hT.transpose(-1, -2)
+    return dict(o=o, h=h, v_new=v_new, hT=hT, g_cum=g_cum, w=w, u=u, **extra)
+
+
+_CACHE = {}
+
+
+def config(name):
+    if name not in _CACHE:
+        _CACHE[name] = make_config(name)
+    return _CACHE[name]
+
+
+def ref_of(inp, scale=None, heads=None):
+    key = (inp.name, scale, tuple(heads) if heads else None)
+    if inp.name != "custom" and key in _CACHE:
+        return _CACHE[key]
+    d = inp.f64()
+    r = oracle.gdr_recurrent_fp64(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"],
+                                  inp.scale if scale is None else scale, heads=heads)
+    if inp.name != "custom":
+        _CACHE[key] = r
+    return r
+
+
+def check(r, ref, tol, heads=None, what=""):
+    errs = {
+        "o": rel(to_np(r["o"][:, :, heads] if heads else r["o"]), ref["o"]),
+        "v_new": rel(to_np(r["v_new"][:, :, heads] if heads else r["v_new"]), ref["v_new"]),
+        "hT": rel(to_np(r["hT"][:, heads] if heads else r["hT"]), ref["hT"]),
+        "h": rel(to_np((r["h"][:, heads] if heads else r["h"]).transpose(-1, -2)), ref["h"]),
+    }
+    print(what, " ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+    for k, e in errs.items():
+        assert e <= tol, f"{what} {k}: rel-L2 {e:.3e} > {tol:.1e}"
+    return errs
+
+
+# --------------------------------------------------------------------------- named workloads
+def test_tiny_fp32_workload(pkg):
+    inp = config("tiny_fp32")
+    r = run_path(pkg, inp)
+    ref = ref_of(inp)
+    check(r, ref, TOL[torch.float32], what="tiny_fp32")
+    d = inp.f64()
+    c = oracle.gdr_chunked_fp64(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"])
+    for key in ("g_cum", "w", "u"):
+        e = rel(to_np(r[key]), c[key])
+        assert e <= 1e-5, f"prepare {key}: {e:.3e}"
+
+
+def test_question_rows_workload(pkg):
+    inp = config("question_rows")
+    r = run_path(pkg, inp)
+    check(r, ref_of(inp), TOL[torch.bfloat16], what="question_rows")
+
+
+def test_new_states_workload_sampled_heads(pkg):
+    inp = config("new_states")
+    r = run_path(pkg, inp)
+    heads = [0, 13, 31]
+    check(r, ref_of(inp, heads=heads), TOL[torch.bfloat16], heads=heads, what="new_states heads 0,13,31")
+
+
+@pytest.mark.parametrize("segmented", [False, True])
+def test_long_state_h1(pkg, segmented):
+    inp = config("long_state_h1")
+    r = run_path(pkg, inp, n_segments=16 if segmented else None)
+    check(r, ref_of(inp), TOL[torch.bfloat16], what=f"long_state_h1 segmented={segmented}")
+
+
+@pytest.mark.parametrize("segmented", [False, True])
+def test_long_state_h8_sampled_heads(pkg, segmented):
+    inp = config("long_state_h8")
+    r = run_path(pkg, inp, n_segments=16 if segmented else None)
+    heads = [0, 5]
+    check(r, ref_of(inp, heads=heads), TOL[torch.bfloat16], heads=heads, what=f"long_state_h8 seg={segmented}")
+
+
+# --------------------------------------------------------------------------- shapes and edges
+CASES = [
+    # dtype, DK, DV, lengths, h0, scale
+    (torch.float32, 64, 64, [1, 63, 64, 65, 127, 257, 0], True, 1.0),
+    (torch.float32, 128, 128, [200, 70], False, 128 ** -0.5),
+    (torch.float32, 64, 128, [130, 5], True, 1.0),
+    (torch.float32, 128, 64, [64, 191], True, 1.0),
+    (torch.bfloat16, 64, 64, [1, 63, 64, 65, 127, 257, 0], True, 1.0),
+    (torch.bfloat16, 128, 128, [200, 70, 1], True, 128 ** -0.5),
+    (torch.bfloat16, 64, 128, [130, 5], False, 1.0),
+    (torch.bfloat16, 128, 64, [64, 191], True, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{str(c[0])[6:]}-dk{c[1]}-dv{c[2]}-L{len(c[3])}")
+def test_parity_shapes(pkg, case):
+    dt, DK, DV, lengths, h0, scale = case
+    inp = make_gdr(101 + DK + DV, lengths=lengths, H=3, DK=DK, DV=DV, dtype=dt, varlen=True,
+                   h0_std=0.1 if h0 else None, scale=scale)
+    r = run_path(pkg, inp)
+    check(r, ref_of(inp), TOL[dt], what=f"shape {case[:3]}")
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_segment_summaries_and_compose(pkg, dt):
+    lengths = [700, 130]
+    P = 4
+    inp = make_gdr(303, lengths=lengths, H=2, DK=128, DV=128, dtype=dt, varlen=True, h0_std=0.1)
+    r = run_path(pkg, inp, n_segments=P)
+    d = inp.f64()
+    cu = d["cu_seqlens"]
+    tol = TOL[dt]
+    for n in range(len(lengths)):
+        s, e = cu[n], cu[n + 1]
+        bounds = oracle.segment_bounds(e - s, P)
+        S_loc, M = oracle.gdr_segment_summaries_fp64(d["k"][0, s:e], d["v"][0, s:e], d["g"][0, s:e],
+                                                     d["beta"][0, s:e], bounds)
+        inits, fin = oracle.gdr_segment_compose_fp64(S_loc, M, d["h0"][n])
+        gs = to_np(r["seg_state"][n * P:(n + 1) * P]).transpose(0, 1, 3, 2)
+        gm = to_np(r["seg_trans"][n * P:(n + 1) * P])
+        gi = to_np(r["seg_init"][n * P:(n + 1) * P]).transpose(0, 1, 3, 2)
+        es, em, ei = rel(gs, S_loc), rel(gm, M), rel(gi, inits)
+        ef = rel(to_np(r["hT_compose"][n]), fin)
+        print(f"seq {n}: S_loc {es:.3e} M {em:.3e} S_init {ei:.3e} composed final {ef:.3e}")
+        assert max(es, em, ei, ef) <= tol
+    check(r, ref_of(inp), tol, what="segmented path")
+
+
+def test_empty_and_single_token_sequences(pkg):
+    inp = make_gdr(404, lengths=[0, 1, 0, 2, 0], H=2, DK=64, DV=64, dtype=torch.float32, varlen=True, h0_std=0.3)
+    r = run_path(pkg, inp)
+    hT = to_np(r["hT"])
+    h0 = inp.h0.double().numpy()
+    for n in (0, 2, 4):
+        assert np.array_equal(hT[n], h0[n]), "an empty sequence keeps its initial state"
+    check(r, ref_of(inp), 1e-5, what="empty/single")
+
+
+def test_state_layout_vk(pkg):
+    inp = make_gdr(505, lengths=[150, 77], H=2, DK=128, DV=64, dtype=torch.bfloat16, varlen=True, h0_std=0.1)
+    a = run_path(pkg, inp, state_layout="kv")
+    b = run_path(pkg, inp, state_layout="vk")
+    assert torch.equal(a["hT"], b["hT"])
+    assert torch.equal(a["o"], b["o"])
+
+
+# --------------------------------------------------------------------------- bit identity
+TILES = {torch.bfloat16: [(32, 2, 1), (32, 2, 2), (64, 2, 2), (64, 4, 1), (64, 4, 2), (128, 4, 2)],
+         torch.float32: [(32, 2, 1), (32, 2, 2), (64, 4, 1), (64, 4, 2)]}
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_bit_identical_across_tiles(pkg, dt):
+    inp = make_gdr(606, lengths=[1, 64, 65, 300, 129], H=3, DK=128, DV=128, dtype=dt, varlen=True, h0_std=0.1)
+    base = run_path(pkg, inp, tile=TILES[dt][0])
+    for t in TILES[dt][1:]:
+        r = run_path(pkg, inp, tile=t)
+        for key in ("h", "v_new", "hT", "o"):
+            assert torch.equal(r[key], base[key]), f"tile {t} changed {key}"
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_bit_identical_segment_summaries_across_tiles(pkg, dt):
+    inp = make_gdr(607, lengths=[900], H=2, DK=128, DV=128, dtype=dt, varlen=True)
+    base = run_path(pkg, inp, n_segments=3, tile=TILES[dt][0])
+    for t in TILES[dt][1:]:
+        r = run_path(pkg, inp, n_segments=3, tile=t)
+        for key in ("seg_state", "seg_trans", "seg_init", "h", "hT", "o"):
+            assert torch.equal(r[key], base[key]), f"tile {t} changed {key}"
+
+
+def test_packed_equals_dense(pkg):
+    lengths = [190, 190, 190]
+    dense = make_gdr(707, lengths=lengths, H=2, DK=128, DV=128, dtype=torch.bfloat16, varlen=False, h0_std=0.1)
+    packed = make_gdr(707, lengths=lengths, H=2, DK=128, DV=128, dtype=torch.bfloat16, varlen=True, h0_std=0.1)
+    for name in ("q", "k", "v", "g", "beta"):
+        assert torch.equal(getattr(dense, name).reshape(-1), getattr(packed, name).reshape(-1))
+    a = run_path(pkg, dense)
+    b = run_path(pkg, packed)
+    assert torch.equal(a["o"].reshape(-1), b["o"].reshape(-1))
+    assert torch.equal(a["h"], b["h"])
+    assert torch.equal(a["hT"], b["hT"])
+
+
+def test_each_packed_sequence_equals_itself_alone(pkg):
+    inp = make_gdr(708, lengths=[100, 257, 3], H=2, DK=64, DV=128, dtype=torch.bfloat16, varlen=True, h0_std=0.1)
+    full = run_path(pkg, inp)
+    cu = inp.cu_seqlens.tolist()
+    offs = np.concatenate([[0], np.cumsum([(L + 63) // 64 for L in inp.lengths])])
+    for n in range(inp.N):
+        s, e = cu[n], cu[n + 1]
+        one = make_gdr(0, lengths=[e - s], H=2, DK=64, DV=128, dtype=torch.bfloat16, varlen=False)
+        one.q, one.k, one.v = inp.q[:, s:e], inp.k[:, s:e], inp.v[:, s:e]
+        one.g, one.beta, one.h0 = inp.g[:, s:e], inp.beta[:, s:e], inp.h0[n:n + 1]
+        r = run_path(pkg, one)
+        assert torch.equal(r["o"][0], full["o"][0, s:e])
+        assert torch.equal(r["hT"][0], full["hT"][n])
+        assert torch.equal(r["h"], full["h"][offs[n]:offs[n + 1]])
+
+
+def test_resume_at_chunk_boundary(pkg):
+    inp = make_gdr(709, lengths=[320], H=2, DK=128, DV=128, dtype=torch.bfloat16, varlen=False, h0_std=0.1)
+    full = run_path(pkg, inp)
+    first = make_gdr(0, lengths=[192], H=2, DK=128, DV=128, dtype=torch.bfloat16, varlen=False)
+    first.q, first.k, first.v, first.g, first.beta = (x[:, :192] for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    first.h0 = inp.h0
+    a = run_path(pkg, first)
+    second = make_gdr(0, lengths=[128], H=2, DK=128, DV=128, dtype=torch.bfloat16, varlen=False)
+    second.q, second.k, second.v, second.g, second.beta = (x[:, 192:] for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    second.h0 = a["hT"].cpu()
+    b = run_path(pkg, second)
+    assert torch.equal(b["hT"], full["hT"])
+    assert torch.equal(torch.cat([a["o"], b["o"]], 1), full["o"])
+    assert torch.equal(torch.cat([a["h"], b["h"]], 0), full["h"])
+
+
+def test_run_to_run_determinism(pkg):
+    inp = make_gdr(710, lengths=[500, 33, 1000], H=4, DK=128, DV=128, dtype=torch.bfloat16, varlen=True, h0_std=0.1)
+    a = run_path(pkg, inp)
+    b = run_path(pkg, inp)
+    for key in ("o", "h", "v_new", "hT", "w", "u", "g_cum"):
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_poisoned_outputs_fully_written(pkg):
+    inp = make_gdr(711, lengths=[65, 1, 128], H=2, DK=128, DV=128, dtype=torch.bfloat16, varlen=True, h0_std=0.1)
+    k, v, g, b = (dev(x) for x in (inp.k, inp.v, inp.g, inp.beta))
+    g_cum, w, u = pkg.gdr_chunk_prepare(k, v, g, b, inp.cu_seqlens)
+    nt = pkg.gdr_num_chunks(k, 128, inp.cu_seqlens)
+    out = {"h": torch.full((nt, 2, 128, 128), float("nan"), dtype=k.dtype, device=k.device),
+           "v_new": torch.full_like(u, float("nan")),
+           "hT": torch.full((3, 2, 128, 128), float("nan"), device=k.device)}
+    h, v_new, hT = pkg.gdr_state_scan(k, w, u, g_cum, dev(inp.h0), inp.cu_seqlens, out=out)
+    torch.cuda.synchronize()
+    for name, t in (("h", h), ("v_new", v_new), ("hT", hT)):
+        assert not torch.isnan(t).any(), f"{name} has unwritten elements"
