@@ -1,0 +1,269 @@
+"""Throughput of the gated-delta state-scan path on one MI355X.
+
+One step = one pass of the whole forward path over one batch of the
+synthetic "question rows" workload (24 packed sequences of 16..256 tokens,
+16 heads, dk = dv = 128, bfloat16 q/k/v, FP32 initial and final states):
+chunk preparation -> inter-chunk state scan -> chunk output.  Inputs are
+resident in HBM before the timed region; W untimed warm-up steps, then K
+timed steps between two device synchronisations.
+
+Printed (one JSON line): token-heads per second of the whole step (in
+Mtok-head/s), plus
+  roofline      the state scan (the dominant kernel): algorithmic bytes per
+                launch / its mean duration from HIP events recorded around
+                each scan launch inside the timed region, against 8 TB/s;
+  cpu_baseline  the FP64 numpy oracle timed on the host on the same batch;
+  long_state    the 64K-token single-sequence workload (8 heads), serial
+                and 16-segment, measured after the timed region.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def scan_alg_bytes(lengths, H, DK, DV, in_bytes, h_bytes, has_h0, has_hT):
+    """Bytes the state scan must move: read k, w (DK each), u (DV), g_cum (4 B)
+    per token-head and h0 per sequence-head; write v_new (DV) per token-head,
+    h (DK x DV) per chunk-head and hT per sequence-head."""
+    toks = sum(lengths)
+    chunks = sum((L + 63) // 64 for L in lengths)
+    n = len(lengths)
+    per_tok = (2 * DK + DV) * in_bytes + 4 + DV * in_bytes
+    b = toks * H * per_tok + chunks * H * DK * DV * h_bytes
+    b += n * H * DK * DV * 4 * (int(has_h0) + int(has_hT))
+    return b
+
+
+def scan_flops(lengths, H, DK, DV):
+    """4 DK DV per token-head: W S (2 DK DV) and K^T D' (2 DK DV)."""
+    return 4 * DK * DV * sum(lengths) * H
+
+
+def source_sha():
+    h = hashlib.sha256()
+    for f in ("scan.hip", "common.hpp", "kernels.hpp"):
+        with open(os.path.join(ROOT, "linear_attention_chunked_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per scan launch from the committed rocprofv3 counter summary,
+    or None when the scan sources changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", f"scan_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        t = json.load(fh)
+    if t.get("source_sha") != source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp):
+    """The FP64 oracle on the same batch, on the host cores."""
+    import oracle
+
+    d = inp.f64()
+    t0, c0 = time.perf_counter(), time.process_time()
+    oracle.gdr_recurrent_fp64(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"], inp.scale)
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    return {
+        "value": inp.token_heads / wall / 1e6,
+        "unit": "Mtok-head/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"the whole {inp.name} batch ({inp.N} sequences, {sum(inp.lengths)} tokens x {inp.H} heads), "
+                  f"token-serial FP64 numpy; {wall:.2f} s wall, {cpu:.2f} s CPU",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="question_rows", choices=["question_rows", "new_states"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long-state", action="store_true")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="also run a plain 'copy' of this many MiB (counter reference for rocprofv3 --pmc)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_attention_chunked_amd as pkg
+    from workloads import make_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pkg.lib()
+    dev = torch.device("cuda:0")
+    inp = make_config(args.workload)
+    q, k, v, g, beta = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    h0 = inp.h0.to(dev) if inp.h0 is not None else None
+    cu = inp.cu_seqlens
+    DV = v.shape[-1]
+    nt = pkg.gdr_num_chunks(k, DV, cu)
+    # outputs allocated once; the step writes into them
+    g_cum = torch.empty(g.shape, dtype=torch.float32, device=dev)
+    w = torch.empty_like(k)
+    u = torch.empty_like(v)
+    h = torch.empty((nt, inp.H, DV, inp.DK), dtype=k.dtype, device=dev)
+    v_new = torch.empty_like(v)
+    hT = torch.empty((inp.N, inp.H, inp.DK, DV), dtype=torch.float32, device=dev)
+    o = torch.empty_like(v)
+    B = pkg.binding
+    L = pkg.lib()
+    P = B.Problem(k, DV, cu)
+    stream = torch.cuda.current_stream()
+    s_ptr = B._stream(stream)
+    ptr = B._ptr
+
+    def step(ev=None):
+        B._check(L.gdr_chunk_prepare(P.ref, ptr(k), ptr(v), ptr(g), ptr(beta), ptr(g_cum), ptr(w), ptr(u), s_ptr),
+                 "prepare")
+        if ev is not None:
+            ev[0].record(stream)
+        B._check(L.gdr_state_scan(P.ref, None, None, ptr(k), ptr(w), ptr(u), ptr(g_cum), ptr(h0), ptr(h),
+                                  ptr(v_new), ptr(hT), s_ptr), "scan")
+        if ev is not None:
+            ev[1].record(stream)
+        B._check(L.gdr_chunk_output(P.ref, ptr(q), ptr(k), ptr(v_new), ptr(h), ptr(g_cum), float(inp.scale),
+                                    ptr(o), s_ptr), "output")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    scan_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    scan_mean_ms = sum(scan_ms) / len(scan_ms)
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = inp.token_heads / (elapsed / args.steps) / 1e6
+
+    in_bytes = 2 if inp.dtype == torch.bfloat16 else 4
+    alg = scan_alg_bytes(inp.lengths, inp.H, inp.DK, DV, in_bytes, in_bytes, h0 is not None, True)
+    achieved = alg / (scan_mean_ms * 1e-3) / 1e9
+    tile = pkg.gdr_plan_query(k, DV, cu)
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": load_traffic(args.workload),
+        "kernel": f"gdr state scan (bv={tile[0]}, waves={tile[1]}, stages={tile[2]}, {tile[3]} workgroups)",
+        "alg_bytes_per_launch": alg,
+        "launch_us_mean": round(scan_mean_ms * 1e3, 2),
+        "launch_us_median": round(scan_ms[len(scan_ms) // 2] * 1e3, 2),
+        "mfma_frac": round(scan_flops(inp.lengths, inp.H, inp.DK, DV) / (scan_mean_ms * 1e-3) / 1e12
+                           / BF16_PEAK_TFLOPS, 4),
+    }
+
+    out = {
+        "metric": "gated-delta state-scan Mtok-head/s + % roofline (varlen batch, 64K seq)",
+        "value": round(value, 2),
+        "unit": "Mtok-head/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "sequences": inp.N,
+            "tokens": sum(inp.lengths),
+            "heads": inp.H,
+            "dk": inp.DK,
+            "dv": DV,
+            "step": "chunk prepare + state scan + chunk output",
+        },
+        "roofline": roofline,
+    }
+
+    if args.copy_ref_mib:
+        n = args.copy_ref_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        out["copy_ref"] = {"bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}
+
+    if not args.no_long_state:
+        out["long_state"] = long_state(pkg, torch, dev)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp)
+
+    print(json.dumps(out), flush=True)
+
+
+def long_state(pkg, torch, dev, reps=5):
+    """64K-token single sequence, 8 heads: serial scan and the 16-segment
+    path (summaries + compose + segmented final pass), timed with HIP events."""
+    from workloads import make_config
+
+    inp = make_config("long_state_h8")
+    k, v, g, beta = (x.to(dev) for x in (inp.k, inp.v, inp.g, inp.beta))
+    g_cum, w, u = pkg.gdr_chunk_prepare(k, v, g, beta)
+    DV = v.shape[-1]
+    P = 16
+
+    def serial():
+        return pkg.gdr_state_scan(k, w, u, g_cum)
+
+    def segmented():
+        ss, st = pkg.gdr_segment_summaries(k, w, u, g_cum, P)
+        si, _ = pkg.gdr_segment_compose(k, DV, ss, st, P)
+        return pkg.gdr_state_scan(k, w, u, g_cum, None, None, None, P, si)
+
+    res = {}
+    for name, fn in (("serial", serial), ("segmented", segmented)):
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        t = sorted(times)[len(times) // 2] * 1e-3
+        alg = scan_alg_bytes(inp.lengths, inp.H, inp.DK, DV, 2, 2, False, True)
+        res[name] = {"us": round(t * 1e6, 1), "Mtok_head_per_s": round(inp.token_heads / t / 1e6, 1),
+                     "serial_alg_bytes": alg, "frac_of_hbm_at_serial_bytes": round(alg / t / 8e12, 4)}
+    res["workload"] = "long_state_h8 (T=65536, H=8, dk=dv=128, bf16, 16 segments)"
+    return res
+
+
+if __name__ == "__main__":
+    main()
