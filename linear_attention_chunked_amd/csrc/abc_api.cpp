@@ -1,23 +1,117 @@
 // ABC slot-state construction entry points (include/gdr.h).
 #include <hip/hip_runtime.h>
+#include <string.h>
 
 #include <string>
 
 #include "../../include/gdr.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_abc_err;
+
+bool abc_valid(const abc_problem* p, std::string& err) {
+  if (p == nullptr) {
+    err = "problem must not be NULL";
+    return false;
+  }
+  if (p->B < 1 || p->T < 0 || p->H < 1) {
+    err = "B >= 1, T >= 0 and H >= 1 are required";
+    return false;
+  }
+  if (p->T > (int64_t(1) << 30)) {
+    err = "T too large";
+    return false;
+  }
+  if (p->M != 64) {
+    err = "M (slots) must be 64";
+    return false;
+  }
+  if (p->K < 64 || p->K % 64 != 0 || p->V < 64 || p->V % 64 != 0 || p->K > 4096 || p->V > 4096) {
+    err = "K and V must be multiples of 64 (64..4096)";
+    return false;
+  }
+  if (p->dtype != GDR_BF16) {
+    err = "abc_affine_scan supports bfloat16 storage";
+    return false;
+  }
+  return true;
+}
+
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
+
+}  // namespace
+
+// Shares the thread-local message with the gated-delta entry points.
+extern "C" const char* gdr_last_error(void);
+namespace gdr_internal {
+void set_last_error(const std::string& m);
+}
 
 extern "C" {
 
 size_t abc_workspace_size(const abc_problem* p) {
-  (void)p;
-  return 0;
+  std::string err;
+  if (!abc_valid(p, err)) return 0;
+  const int64_t nc = (p->T + 63) / 64;
+  return static_cast<size_t>(p->B) * nc * p->H * p->M * sizeof(float);
 }
 
 gdr_status abc_affine_scan(const abc_problem* p, const void* k, const void* v, const void* s, float* z, void* hk,
                            void* hv, float* hk_final, float* hv_final, void* workspace, size_t workspace_bytes,
                            void* stream) {
-  (void)p; (void)k; (void)v; (void)s; (void)z; (void)hk; (void)hv; (void)hk_final; (void)hv_final;
-  (void)workspace; (void)workspace_bytes; (void)stream;
-  return GDR_ERR_UNSUPPORTED;
+  std::string err;
+  if (!abc_valid(p, err)) {
+    gdr_internal::set_last_error(err);
+    return GDR_ERR_INVALID_ARG;
+  }
+  const void* req[] = {k, v, s, hk, hv, workspace};
+  const char* names[] = {"k", "v", "s", "hk", "hv", "workspace"};
+  for (int i = 0; i < 6; ++i) {
+    if (req[i] == nullptr || !aligned16(req[i])) {
+      gdr_internal::set_last_error(std::string(names[i]) + " must be non-NULL and 16-byte aligned");
+      return GDR_ERR_INVALID_ARG;
+    }
+  }
+  const void* opt[] = {z, hk_final, hv_final};
+  for (const void* q : opt) {
+    if (q != nullptr && !aligned16(q)) {
+      gdr_internal::set_last_error("optional outputs must be 16-byte aligned");
+      return GDR_ERR_INVALID_ARG;
+    }
+  }
+  if (workspace_bytes < abc_workspace_size(p)) {
+    gdr_internal::set_last_error("workspace smaller than abc_workspace_size()");
+    return GDR_ERR_INVALID_ARG;
+  }
+  gdr::AbcArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = k;
+  a.v = v;
+  a.s = s;
+  a.z = z;
+  a.zc = static_cast<float*>(workspace);
+  a.hk = hk;
+  a.hv = hv;
+  a.hk_final = hk_final;
+  a.hv_final = hv_final;
+  a.B = p->B;
+  a.T = static_cast<int32_t>(p->T);
+  a.H = p->H;
+  a.K = p->K;
+  a.M = p->M;
+  a.V = p->V;
+  a.NC = static_cast<int32_t>((p->T + 63) / 64);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (a.NC > 0) e = gdr::launch_abc_z(a, st);
+  if (e == hipSuccess) e = gdr::launch_abc_scan(a, st);
+  if (e != hipSuccess) {
+    gdr_internal::set_last_error(std::string("abc launch: ") + hipGetErrorString(e));
+    return GDR_ERR_HIP;
+  }
+  return GDR_OK;
 }
 
 }  // extern "C"

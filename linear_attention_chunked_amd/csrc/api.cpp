@@ -102,6 +102,10 @@ gdr_status run_scan(const gdr::Problem& pr, const gdr::Tile& t, int mode, int P,
 
 }  // namespace
 
+namespace gdr_internal {
+void set_last_error(const std::string& m) { g_err = m; }
+}  // namespace gdr_internal
+
 extern "C" {
 
 const char* gdr_status_string(gdr_status s) {

@@ -1,0 +1,88 @@
+"""GPU parity of the ABC slot-state construction against the FP64 oracle.
+
+States and finals: relative L2 <= 1e-2 (bfloat16 storage of k, v, s and of the
+pre-chunk states).  The normaliser z is FP32 arithmetic on the stored logits:
+relative L2 <= 1e-5.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import make_abc, make_config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_attention_chunked_amd as p
+
+    p.lib()
+    return p
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def np64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def run(pkg, inp, emit_z=True):
+    z, hk, hv, hkf, hvf = pkg.abc_affine_scan(inp.k.cuda(), inp.v.cuda(), inp.s.cuda(), emit_z=emit_z)
+    torch.cuda.synchronize()
+    return {"z": z, "hk": hk, "hv": hv, "hk_final": hkf, "hv_final": hvf}
+
+
+def compare(r, ref, batches=None, heads=None, what=""):
+    def pick(t, bdim, hdim):
+        x = np64(t)
+        if batches is not None:
+            x = np.take(x, batches, axis=bdim)
+        if heads is not None:
+            x = np.take(x, heads, axis=hdim)
+        return x
+
+    errs = {
+        "z": rel(pick(r["z"], 0, 2), ref["z"]) if r["z"] is not None else 0.0,
+        "hk": rel(pick(r["hk"], 0, 2), ref["hk"]),
+        "hv": rel(pick(r["hv"], 0, 2), ref["hv"]),
+        "hk_final": rel(pick(r["hk_final"], 0, 1), ref["hk_final"]),
+        "hv_final": rel(pick(r["hv_final"], 0, 1), ref["hv_final"]),
+    }
+    print(what, " ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+    assert errs["z"] <= 1e-5
+    for key in ("hk", "hv", "hk_final", "hv_final"):
+        assert errs[key] <= 1e-2, f"{what} {key} {errs[key]:.3e}"
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 257])
+def test_abc_small(pkg, T):
+    inp = make_abc(900 + T, B=2, T=T, H=2, K=128, M=64, V=192)
+    d = inp.f64()
+    ref = oracle.abc_recurrent_fp64(d["k"], d["v"], d["s"])
+    compare(run(pkg, inp), ref, what=f"abc T={T}")
+
+
+def test_abc_affine_workload_sampled(pkg):
+    inp = make_config("abc_affine")
+    r = run(pkg, inp)
+    d = inp.f64()
+    for b, heads in ((0, [0, 3]), (1, [2])):
+        ref = oracle.abc_recurrent_fp64(d["k"], d["v"], d["s"], batches=[b], heads=heads)
+        compare(r, ref, batches=[b], heads=heads, what=f"abc_affine b={b} heads={heads}")
+
+
+def test_abc_deterministic(pkg):
+    inp = make_abc(950, B=1, T=300, H=3, K=64, M=64, V=128)
+    a = run(pkg, inp)
+    b = run(pkg, inp)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
