@@ -89,9 +89,13 @@ typedef struct {
 
 /* Tile of the serial scans.  bv: value columns per workgroup (the BV of
  * [kev#259]); waves: wavefronts per workgroup, each owning bv/waves columns
- * (a multiple of 16); stages: 1 = load a chunk then compute it, 2 = fetch the
- * next chunk while computing the current one.  Every supported tile gives
- * bit-identical results.  NULL = the scheduler's choice. */
+ * (a multiple of 16); stages: chunks in flight per workgroup (1 = load a chunk
+ * then compute it, 2 = fetch the next chunk while computing the current one,
+ * 3 = two chunks ahead with two LDS buffers).  Built tiles: bfloat16 (32,2,2)
+ * (32,2,3) (64,2,3) (64,4,2) (64,4,3) (128,4,2) (128,4,3); float32 (32,2,1)
+ * (32,2,2) (64,4,1) (64,4,2).
+ * Every supported tile gives bit-identical results.  NULL = the scheduler's
+ * choice. */
 typedef struct {
   int32_t bv, waves, stages;
 } gdr_tile;

@@ -23,10 +23,13 @@ COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed-FP32 VALU forms are kept out of generated code on purpose
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in arch VGPRs: the scan's state is also touched by VALU
+    # every chunk, and the AGPR form would copy it back and forth
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
 ]
-SOURCES = ["scan.hip", "prepare.hip", "output.hip", "compose.hip", "abc.hip", "plan.cpp", "api.cpp", "abc_api.cpp"]
+SOURCES = ["scan.hip", "scan2.hip", "prepare.hip", "output.hip", "compose.hip", "abc.hip", "plan.cpp", "api.cpp", "abc_api.cpp"]
 
 
 def _compile(src: str) -> str:

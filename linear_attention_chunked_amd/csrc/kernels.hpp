@@ -83,6 +83,7 @@ using LaunchFn = hipError_t (*)(const void* args, int grid, hipStream_t stream);
 
 // Lookup of an instantiated kernel; nullptr when the combination is not built.
 LaunchFn find_scan(int dtype, int dk, int bv, int waves, int stages, int mode);
+LaunchFn find_scan2(int dk, int bv, int waves, int stages, int mode);
 LaunchFn find_prepare(int dtype, int dk, int dv);
 LaunchFn find_output(int dtype, int dk, int dv);
 LaunchFn find_compose(int dk);

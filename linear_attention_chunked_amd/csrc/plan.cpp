@@ -87,7 +87,8 @@ bool parse_problem(int B, int64_t T, int H, int DK, int DV, int N, const int32_t
 
 // Built tiles (must match the instantiations in scan.hip).
 static bool tile_built(int dtype, int bv, int waves, int stages) {
-  static const int bf16_tiles[][3] = {{32, 2, 1}, {32, 2, 2}, {64, 2, 2}, {64, 4, 1}, {64, 4, 2}, {128, 4, 2}};
+  static const int bf16_tiles[][3] = {{32, 2, 2}, {32, 2, 3}, {64, 2, 3}, {64, 4, 2},
+                                      {64, 4, 3}, {128, 4, 2}, {128, 4, 3}};
   static const int f32_tiles[][3] = {{32, 2, 1}, {32, 2, 2}, {64, 4, 1}, {64, 4, 2}};
   if (dtype == 1) {
     for (auto& t : bf16_tiles)
@@ -111,17 +112,32 @@ bool choose_tile(const Problem& p, const int32_t* req, int mode, Tile& t, std::s
       return false;
     }
   } else {
-    // Fixed shape-class table.  64-column blocks with 4 waves and one chunk
-    // of prefetch is the default; problems whose (row, head) pairs alone
-    // cannot fill the 256 CUs twice over use 32-column blocks for more units.
+    // Fixed shape-class table, from measured sweeps on MI355X (bfloat16,
+    // dk = dv = 128): with enough (row, head) pairs to give every CU at least
+    // a quarter of a 64-column unit, 64-column blocks of 4 waves with one LDS
+    // buffer (several workgroups per CU) win; with very few pairs (one long
+    // sequence, a handful of heads) 32-column blocks of 2 waves give more
+    // units and a shorter chain per chunk.
     const int64_t pairs = static_cast<int64_t>(p.N) * p.H;
-    r[0] = 64;
-    r[1] = 4;
-    r[2] = 2;
-    if (pairs * (p.DV / 64) < 512 && p.DV >= 64) {
-      r[0] = 32;
-      r[1] = 2;
+    const int64_t units64 = pairs * (p.DV / 64);
+    if (p.dtype == 1) {
+      r[0] = 64;
+      r[1] = 4;
       r[2] = 2;
+      if (units64 < 64) {
+        r[0] = 32;
+        r[1] = 2;
+        r[2] = 2;
+      }
+    } else {
+      r[0] = 64;
+      r[1] = 4;
+      r[2] = 2;
+      if (units64 < 512) {
+        r[0] = 32;
+        r[1] = 2;
+        r[2] = 2;
+      }
     }
   }
   if (!tile_built(p.dtype, r[0], r[1], r[2])) {

@@ -370,24 +370,20 @@ static hipError_t launch_scan(const void* args, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Built tiles: (dtype, DK, BV, waves, stages, mode).
+// Built tiles for float32 storage (bfloat16 storage uses scan2.hip):
+// (dtype, DK, BV, waves, stages, mode).
 #define GDR_SCAN_TILES(X, T, DTYPE, DK, MODE) \
   X(T, DTYPE, DK, 32, 2, 1, MODE)             \
   X(T, DTYPE, DK, 32, 2, 2, MODE)             \
-  X(T, DTYPE, DK, 64, 2, 2, MODE)             \
   X(T, DTYPE, DK, 64, 4, 1, MODE)             \
-  X(T, DTYPE, DK, 64, 4, 2, MODE)             \
-  X(T, DTYPE, DK, 128, 4, 2, MODE)
+  X(T, DTYPE, DK, 64, 4, 2, MODE)
 
 #define GDR_SCAN_CASE(T, DTYPE, DK, BV, NW, ST, MODE)                                        \
   if (dtype == DTYPE && dk == DK && bv == BV && waves == NW && stages == ST && mode == MODE) \
     return &launch_scan<T, DK, BV, NW, ST, MODE>;
 
 LaunchFn find_scan(int dtype, int dk, int bv, int waves, int stages, int mode) {
-  GDR_SCAN_TILES(GDR_SCAN_CASE, bf16_t, 1, 128, 0)
-  GDR_SCAN_TILES(GDR_SCAN_CASE, bf16_t, 1, 128, 1)
-  GDR_SCAN_TILES(GDR_SCAN_CASE, bf16_t, 1, 64, 0)
-  GDR_SCAN_TILES(GDR_SCAN_CASE, bf16_t, 1, 64, 1)
+  if (dtype == 1) return find_scan2(dk, bv, waves, stages, mode);
   GDR_SCAN_TILES(GDR_SCAN_CASE, float, 0, 128, 0)
   GDR_SCAN_TILES(GDR_SCAN_CASE, float, 0, 128, 1)
   GDR_SCAN_TILES(GDR_SCAN_CASE, float, 0, 64, 0)

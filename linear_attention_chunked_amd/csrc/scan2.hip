@@ -1,0 +1,464 @@
+// The inter-chunk state scan for bfloat16 storage on gfx950 (the fast path;
+// float32 storage keeps the simpler kernel in scan.hip).
+//
+// Same recurrence and same per-column instruction sequence as scan.hip
+// (kev pull request #259, opening section: one program per value block,
+// serial over 64-token chunks), organised for latency:
+//
+//   * Buffer resources.  Every chunk gets scalar resource descriptors whose
+//     base is the chunk's first token of this head and whose size ends at the
+//     chunk's last valid token.  Per-lane offsets are fixed for the whole loop;
+//     rows past a ragged tail read as zero and stores to them are dropped by
+//     the hardware range check, so there is no per-lane masking and no 64-bit
+//     address arithmetic in the loop.
+//   * Row-major LDS tiles written straight from the 16-byte loads, rows padded
+//     (W by 16 bytes, K and U by 32) so the two read patterns below hit distinct
+//     banks and every operand address is a per-lane base plus an immediate.
+//     The contraction over tokens needs K and U with the token index running
+//     inside a lane; gfx950's ds_read_b64_tr_b16 delivers exactly that from the
+//     row-major tile (within 16 lanes, lane j names 4 elements of a 4x16 block
+//     and lane i receives its column i).
+//   * The chunk's decay weights exp(g_last - g_t) (zero past the tail) and
+//     exp(g_last) are computed once per chunk by the first wave and shared
+//     through LDS.  With one wave per SIMD every wave64 VALU instruction costs
+//     the SIMD four cycles, so the chunk step is kept lean in VALU work.
+//   * Two LDS buffers and a register prefetch of PF chunks, one barrier per
+//     chunk: the global loads of chunk c+PF are in flight while chunk c
+//     computes.
+//   * U enters the accumulator negated and the sign is folded into the decay
+//     weights, so W needs no negation: acc = -U + W S = -D, v_new = -acc,
+//     D' = acc * (-exp(g_last - g)).
+#include "kernels.hpp"
+
+namespace gdr {
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+__device__ __forceinline__ u32x2_t lds_tr16(const char* base, int byte_off) {
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + byte_off));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+__device__ __forceinline__ u32x2_t lds_b64(const char* base, int byte_off) {
+  return *reinterpret_cast<const u32x2_t*>(base + byte_off);
+}
+
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF>
+struct Scan2 {
+  using S = St<bf16_t>;
+  using frag = S::frag;
+  static constexpr int NT = NW * 64;
+  static constexpr int NC = BV / (16 * NW);
+  static constexpr int KS = DK / 32;
+  static constexpr int DT = DK / 16;
+  static constexpr int RBW = DK * 2;      // bytes per W / K row
+  static constexpr int RBU = BV * 2;      // bytes per U row (this block's columns)
+  static constexpr int SW = RBW + 16;     // padded LDS row strides (bytes)
+  static constexpr int SK = RBW + 32;
+  static constexpr int SU = RBU + 32;
+  static constexpr int CPW = RBW / 16;    // 16-byte chunks per W row
+  static constexpr int CPU = RBU / 16;
+  static constexpr int OFF_W = 0, OFF_K = kChunk * SW, OFF_U = OFF_K + kChunk * SK;
+  static constexpr int OFF_D = OFF_U + kChunk * SU;   // 64 negated decay weights, then exp(g_last)
+  static constexpr int BUF = OFF_D + kChunk * 4 + 16;
+  static constexpr int W_PT = kChunk * CPW / NT;   // 16-byte vectors per thread (W, and K)
+  static constexpr int U_PT = (kChunk * CPU + NT - 1) / NT;
+  static_assert(NC >= 1 && BV % (16 * NW) == 0, "each wave owns whole 16-column tiles");
+  static_assert((kChunk * CPW) % NT == 0, "W/K tiles split evenly over the threads");
+
+  struct Stage {
+    u32x4_t w[W_PT];
+    u32x4_t k[W_PT];
+    u32x4_t u[U_PT];
+    float g;
+  };
+
+  struct Ctx {
+    const ScanArgs* a;
+    int hd, col_blk, H, DV;
+    bool has_u;
+    int vo_wk[W_PT];   // global byte offsets of this thread's W/K vectors (row-relative)
+    int vo_u[U_PT];
+  };
+
+  __device__ static __forceinline__ void load(Stage& st, const Ctx& x, int64_t tok0, int nvalid) {
+    const ScanArgs& a = *x.a;
+    const int64_t H = x.H;
+    const uint32_t wk_bytes = static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2);
+    const uint16_t* wp = static_cast<const uint16_t*>(a.w) + (tok0 * H + x.hd) * DK;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (tok0 * H + x.hd) * DK;
+    const rsrc_t rw = make_rsrc(wp, wk_bytes);
+    const rsrc_t rk = make_rsrc(kp, wk_bytes);
+#pragma unroll
+    for (int i = 0; i < W_PT; ++i) st.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, x.vo_wk[i], 0, 0);
+#pragma unroll
+    for (int i = 0; i < W_PT; ++i) st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, x.vo_wk[i], 0, 0);
+    if (x.has_u) {
+      const uint16_t* up = static_cast<const uint16_t*>(a.u) + (tok0 * H + x.hd) * x.DV + x.col_blk;
+      const rsrc_t ru = make_rsrc(up, static_cast<uint32_t>(((nvalid - 1) * H * x.DV + BV) * 2));
+#pragma unroll
+      for (int i = 0; i < U_PT; ++i) st.u[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, x.vo_u[i], 0, 0);
+    }
+    const float* gp = a.g_cum + tok0 * H + x.hd;
+    const rsrc_t rg = make_rsrc(gp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * 4));
+    st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, static_cast<int>(threadIdx.x * H * 4), 0, 0));
+  }
+
+  __device__ static __forceinline__ void store(const Stage& st, const Ctx& x, char* buf, int nvalid) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < W_PT; ++i) {
+      const int v = tid + i * NT;
+      const int r = v / CPW, c = v % CPW;
+      *reinterpret_cast<u32x4_t*>(buf + OFF_W + r * SW + c * 16) = st.w[i];
+      *reinterpret_cast<u32x4_t*>(buf + OFF_K + r * SK + c * 16) = st.k[i];
+    }
+    if (x.has_u) {
+#pragma unroll
+      for (int i = 0; i < U_PT; ++i) {
+        const int v = tid + i * NT;
+        if ((kChunk * CPU) % NT == 0 || v < kChunk * CPU) {
+          const int r = v / CPU, c = v % CPU;
+          *reinterpret_cast<u32x4_t*>(buf + OFF_U + r * SU + c * 16) = st.u[i];
+        }
+      }
+    }
+    if (tid < kChunk) {  // first wave: decay weights of the chunk
+      const float g_last = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, st.g), nvalid - 1));
+      float* d = reinterpret_cast<float*>(buf + OFF_D);
+      d[tid] = (tid < nvalid) ? -exp_fast(g_last - st.g) : 0.f;
+      if (tid == 0) d[kChunk] = exp_fast(g_last);
+    }
+  }
+
+  // One chunk.  The W operand reads are issued before the first matrix
+  // instruction, the K operand reads while GEMM1 runs, and the accumulator
+  // chains are interleaved, so the chunk pays the LDS and MFMA latencies about
+  // once instead of once per product.
+  __device__ static __forceinline__ void compute(f32x4_t (&Sacc)[DT][NC], const Ctx& x, const Row& row, int c,
+                                                 const char* buf) {
+    const ScanArgs& a = *x.a;
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int colw = wave * (BV / NW);
+    const int64_t H = x.H;
+    const int DV = x.DV;
+    const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(c) * kChunk;
+    const int nvalid = min(kChunk, row.len - c * kChunk);
+
+    // per-lane LDS bases (immediates carry the tile/step offsets)
+    const char* wb = buf + OFF_W + c16 * SW + (g4 >> 1) * 16 + (g4 & 1) * 8;            // + 16 mt SW + 64 s (+32)
+    const char* kb = buf + OFF_K + (4 * g4 + (c16 >> 2)) * SK + (c16 & 3) * 8;          // + 32 s2 SK (+16 SK) + 32 dt
+    const char* ub = buf + OFF_U + (4 * g4 + (c16 >> 2)) * SU + (colw + 4 * (c16 & 3)) * 2;  // + 16 mt SU + 32 ct
+    const float* nd_l = reinterpret_cast<const float*>(buf + OFF_D) + 4 * g4;          // + 16 mt
+
+    u32x2_t uq[4][NC];
+    if (x.has_u) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) uq[mt][ct] = lds_tr16(ub, 16 * mt * SU + 32 * ct);
+    }
+    frag aw[KS][4];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        aw[s][mt] = S::frag_from_quads(lds_b64(wb, 16 * mt * SW + 64 * s), lds_b64(wb, 16 * mt * SW + 64 * s + 32));
+
+    // ---- S as B operand; pre-chunk state h[c] ----
+    frag Sb[KS][NC];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) Sb[s][ct] = S::frag_from_f32(Sacc[2 * s][ct], Sacc[2 * s + 1][ct]);
+
+    // ---- acc = -U + W S  (= -D); independent chains interleaved ----
+    f32x4_t acc[4][NC];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        if (x.has_u) {
+          const u32x2_t q = uq[mt][ct];  // bf16 -> f32 with the sign flipped in the same instruction
+          acc[mt][ct] = f32x4_t{__builtin_bit_cast(float, (q.x << 16) + 0x80000000u),
+                                __builtin_bit_cast(float, (q.x & 0xffff0000u) ^ 0x80000000u),
+                                __builtin_bit_cast(float, (q.y << 16) + 0x80000000u),
+                                __builtin_bit_cast(float, (q.y & 0xffff0000u) ^ 0x80000000u)};
+        } else {
+          acc[mt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) S::mma(acc[mt][ct], aw[s][mt], Sb[s][ct]);
+
+    if (MODE == 0 && a.h != nullptr) {
+      uint16_t* hp = static_cast<uint16_t*>(a.h) +
+                     ((static_cast<int64_t>(row.chunk_off) + c) * H + x.hd) * DV * DK +
+                     static_cast<int64_t>(x.col_blk + colw) * DK;
+      const rsrc_t rh = make_rsrc(hp, static_cast<uint32_t>((BV / NW) * DK * 2));
+      const int hoff = (c16 * DK + 4 * g4) * 2;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
+          const u32x4_t q = __builtin_bit_cast(u32x4_t, Sb[s][ct].v);
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{q.x, q.y}, rh, hoff, (16 * ct * DK + 32 * s) * 2, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{q.z, q.w}, rh, hoff, (16 * ct * DK + 32 * s + 16) * 2, 0);
+        }
+    }
+
+    // ---- K operand reads overlap GEMM1 ----
+    frag ak[2][DT];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        ak[s2][dt] = S::frag_from_quads(lds_tr16(kb, 32 * s2 * SK + 32 * dt),
+                                        lds_tr16(kb, (32 * s2 + 16) * SK + 32 * dt));
+    f32x4_t nd[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) nd[mt] = *reinterpret_cast<const f32x4_t*>(nd_l + 16 * mt);
+    const float eg = reinterpret_cast<const float*>(buf + OFF_D)[kChunk];
+
+    // ---- v_new = -acc (tail rows dropped by the range check); D' = acc * nd ----
+    if (MODE == 0 && a.v_new != nullptr) {
+      uint16_t* vp = static_cast<uint16_t*>(a.v_new) + (tok0 * H + x.hd) * DV + x.col_blk + colw;
+      const rsrc_t rv = make_rsrc(vp, static_cast<uint32_t>(((nvalid - 1) * H * DV + BV - colw) * 2));
+      const int rs = static_cast<int>(H * DV * 2);
+      const int voff = (4 * g4) * rs + c16 * 2;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; r += 2) {
+            const uint32_t pk = pack_bf16x2(-acc[mt][ct][r], -acc[mt][ct][r + 1]);
+            const int so = (16 * mt + r) * rs + 32 * ct;
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk), rv, voff, so, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk >> 16), rv, voff, so + rs, 0);
+          }
+    }
+    frag Db[2][NC];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) Db[s2][ct] = S::frag_from_f32(acc[2 * s2][ct] * nd[2 * s2], acc[2 * s2 + 1][ct] * nd[2 * s2 + 1]);
+
+    // ---- S = exp(g_last) S + K^T D' ----
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) Sacc[dt][ct] *= eg;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) S::mma(Sacc[dt][ct], ak[s2][dt], Db[s2][ct]);
+  }
+
+  __device__ static void run(const ScanArgs& a, char* smem) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int NJ = a.n_blk;
+    const int bx = blockIdx.x;
+    const int xcd = bx & 7, slot = bx >> 3;
+    const int pair = 8 * (slot / NJ) + xcd;
+    const int jb = slot % NJ;
+    if (pair >= a.n_rows * a.H) return;
+    const int ri = pair / a.H;
+    const Row row = a.rows[ri];
+    Ctx x;
+    x.a = &a;
+    x.hd = pair % a.H;
+    x.H = a.H;
+    x.DV = a.DV;
+    x.col_blk = jb * BV;
+    const bool trans = (MODE == 1) && (x.col_blk >= x.DV);
+    x.has_u = !trans;
+    const int64_t H = a.H;
+#pragma unroll
+    for (int i = 0; i < W_PT; ++i) {
+      const int v = tid + i * NT;
+      x.vo_wk[i] = static_cast<int>((v / CPW) * H * DK * 2 + (v % CPW) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < U_PT; ++i) {
+      const int v = min(tid + i * NT, kChunk * CPU - 1);
+      x.vo_u[i] = static_cast<int>((v / CPU) * H * x.DV * 2 + (v % CPU) * 16);
+    }
+    const int colw = wave * (BV / NW);
+    const int DV = x.DV;
+    const int hd = x.hd;
+    const int nchunks = (row.len + kChunk - 1) / kChunk;
+
+    f32x4_t Sacc[DT][NC];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) Sacc[dt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (MODE == 0 && row.in_idx >= 0 && a.h_in != nullptr) {
+      const float* base = a.h_in + (static_cast<int64_t>(row.in_idx) * H + hd) * DV * DK;
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        const int j = x.col_blk + colw + 16 * ct + c16;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int i0 = 16 * dt + 4 * g4;
+          if (a.in_vk) {
+            Sacc[dt][ct] = *reinterpret_cast<const f32x4_t*>(base + static_cast<int64_t>(j) * DK + i0);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sacc[dt][ct][r] = base[static_cast<int64_t>(i0 + r) * DV + j];
+          }
+        }
+      }
+    }
+    if (MODE == 1 && trans) {
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        const int jj = x.col_blk + colw + 16 * ct + c16 - DV;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Sacc[dt][ct][r] = (16 * dt + 4 * g4 + r == jj) ? 1.f : 0.f;
+      }
+    }
+
+    char* buf0 = smem;
+    char* buf1 = smem + (NBUF == 2 ? BUF : 0);
+    auto tok_of = [&](int c) { return static_cast<int64_t>(row.bos) + static_cast<int64_t>(c) * kChunk; };
+    auto nv_of = [&](int c) { return min(kChunk, row.len - c * kChunk); };
+    if (nchunks > 0) {
+      if (NBUF == 1) {
+        // one LDS buffer: fill, compute, and refill behind a second barrier;
+        // the next chunk's loads are in flight during the compute
+        Stage st;
+        load(st, x, tok_of(0), nv_of(0));
+        for (int c = 0; c < nchunks; ++c) {
+          __syncthreads();
+          store(st, x, buf0, nv_of(c));
+          __syncthreads();
+          if (c + 1 < nchunks) load(st, x, tok_of(c + 1), nv_of(c + 1));
+          compute(Sacc, x, row, c, buf0);
+        }
+      } else if (PF == 1) {
+        Stage st;
+        load(st, x, tok_of(0), nv_of(0));
+        store(st, x, buf0, nv_of(0));
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+          char* cur = (c & 1) ? buf1 : buf0;
+          char* nxt = (c & 1) ? buf0 : buf1;
+          if (c + 1 < nchunks) load(st, x, tok_of(c + 1), nv_of(c + 1));
+          compute(Sacc, x, row, c, cur);
+          if (c + 1 < nchunks) store(st, x, nxt, nv_of(c + 1));
+          __syncthreads();
+        }
+      } else {
+        Stage A, B;
+        load(A, x, tok_of(0), nv_of(0));
+        if (nchunks > 1) load(B, x, tok_of(1), nv_of(1));
+        store(A, x, buf0, nv_of(0));
+        __syncthreads();
+        for (int c = 0; c < nchunks; c += 2) {
+          if (c + 2 < nchunks) load(A, x, tok_of(c + 2), nv_of(c + 2));
+          compute(Sacc, x, row, c, buf0);
+          if (c + 1 < nchunks) store(B, x, buf1, nv_of(c + 1));
+          __syncthreads();
+          if (c + 1 >= nchunks) break;
+          if (c + 3 < nchunks) load(B, x, tok_of(c + 3), nv_of(c + 3));
+          compute(Sacc, x, row, c + 1, buf1);
+          if (c + 2 < nchunks) store(A, x, buf0, nv_of(c + 2));
+          __syncthreads();
+        }
+      }
+    }
+
+    if (row.out_idx < 0) return;
+    if (MODE == 0 || !trans) {
+      if (a.h_out == nullptr) return;
+      float* base = a.h_out + (static_cast<int64_t>(row.out_idx) * H + hd) * DV * DK;
+      const bool vk = (MODE == 1) ? true : (a.out_vk != 0);
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        const int j = x.col_blk + colw + 16 * ct + c16;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int i0 = 16 * dt + 4 * g4;
+          if (vk) {
+            *reinterpret_cast<f32x4_t*>(base + static_cast<int64_t>(j) * DK + i0) = Sacc[dt][ct];
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) base[static_cast<int64_t>(i0 + r) * DV + j] = Sacc[dt][ct][r];
+          }
+        }
+      }
+    } else {
+      float* base = a.trans_out + (static_cast<int64_t>(row.out_idx) * H + hd) * DK * DK;
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        const int jj = x.col_blk + colw + 16 * ct + c16 - DV;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) base[static_cast<int64_t>(16 * dt + 4 * g4 + r) * DK + jj] = Sacc[dt][ct][r];
+      }
+    }
+  }
+};
+
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF>
+__global__ __launch_bounds__(NW * 64) void scan2_kernel(const ScanArgs a) {
+  using K = Scan2<DK, BV, NW, PF, MODE, NBUF>;
+  __shared__ __align__(16) char smem[NBUF * K::BUF];
+  K::run(a, smem);
+}
+
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF>
+static hipError_t launch_scan2(const void* args, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((scan2_kernel<DK, BV, NW, PF, MODE, NBUF>), dim3(grid), dim3(NW * 64), 0, stream,
+                     *static_cast<const ScanArgs*>(args));
+  return hipGetLastError();
+}
+
+// Built bf16 tiles (BV, waves, stages):
+//   stages 2: one LDS buffer, the next chunk prefetched in registers (small LDS
+//             footprint, several workgroups per CU: for many units)
+//   stages 3: two LDS buffers, two chunks prefetched (for few, long units)
+#define GDR_SCAN2_TILES(X, DK, MODE) \
+  X(DK, 32, 2, 2, MODE, 1, 1)        \
+  X(DK, 32, 2, 3, MODE, 2, 2)        \
+  X(DK, 64, 2, 3, MODE, 2, 2)        \
+  X(DK, 64, 4, 2, MODE, 1, 1)        \
+  X(DK, 64, 4, 3, MODE, 2, 2)        \
+  X(DK, 128, 4, 2, MODE, 1, 1)       \
+  X(DK, 128, 4, 3, MODE, 2, 2)
+
+#define GDR_SCAN2_CASE(DK, BV, NW, ST, MODE, PF, NBUF) \
+  if (dk == DK && bv == BV && waves == NW && stages == ST && mode == MODE) return &launch_scan2<DK, BV, NW, PF, MODE, NBUF>;
+
+LaunchFn find_scan2(int dk, int bv, int waves, int stages, int mode) {
+  GDR_SCAN2_TILES(GDR_SCAN2_CASE, 128, 0)
+  GDR_SCAN2_TILES(GDR_SCAN2_CASE, 128, 1)
+  GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 0)
+  GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 1)
+  return nullptr;
+}
+
+}  // namespace gdr

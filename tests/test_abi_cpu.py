@@ -78,7 +78,7 @@ def test_unbuilt_tile_rejected():
     p, _ = _prob()
     assert _scan(p, tile=(48, 3, 1)) == B.GDR_ERR_UNSUPPORTED
     p, _ = _prob(DV=64)
-    assert _scan(p, tile=(128, 4, 2)) == B.GDR_ERR_UNSUPPORTED  # bv must divide DV
+    assert _scan(p, tile=(128, 4, 3)) == B.GDR_ERR_UNSUPPORTED  # bv must divide DV
 
 
 def test_num_chunks():
@@ -103,8 +103,8 @@ def test_plan_grid_and_launch_split():
     for i in range(300):
         cu.append(cu[-1] + 1 + (i % 70))
     p, keep = _prob(T=cu[-1], cu=cu, H=3)
-    bv, waves, stages, wgs, launches, maxrows = _query(p, tile=(64, 4, 2))
-    assert (bv, waves, stages) == (64, 4, 2)
+    bv, waves, stages, wgs, launches, maxrows = _query(p, tile=(64, 4, 3))
+    assert (bv, waves, stages) == (64, 4, 3)
     assert launches == 3 and maxrows == 112
     pairs = [112 * 3, 112 * 3, 76 * 3]
     assert wgs == sum(8 * 2 * ((x + 7) // 8) for x in pairs)
@@ -120,8 +120,8 @@ def test_plan_segments_and_table():
 
 def test_force_tile_env(monkeypatch):
     p, _ = _prob(B_=4, T=256, H=32)
-    monkeypatch.setenv("GDR_FORCE_TILE", "128,4,2")
-    assert _query(p)[:3] == (128, 4, 2)
+    monkeypatch.setenv("GDR_FORCE_TILE", "128,4,3")
+    assert _query(p)[:3] == (128, 4, 3)
     monkeypatch.setenv("GDR_FORCE_TILE", "bogus")
     out = (ctypes.c_int64 * 6)()
     assert B.lib().gdr_plan_query(ctypes.byref(p), None, 0, out) == B.GDR_ERR_UNSUPPORTED

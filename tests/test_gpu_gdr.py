@@ -207,7 +207,7 @@ def test_state_layout_vk(pkg):
 
 
 # --------------------------------------------------------------------------- bit identity
-TILES = {torch.bfloat16: [(32, 2, 1), (32, 2, 2), (64, 2, 2), (64, 4, 1), (64, 4, 2), (128, 4, 2)],
+TILES = {torch.bfloat16: [(32, 2, 2), (32, 2, 3), (64, 2, 3), (64, 4, 2), (64, 4, 3), (128, 4, 2), (128, 4, 3)],
          torch.float32: [(32, 2, 1), (32, 2, 2), (64, 4, 1), (64, 4, 2)]}
 
 
