@@ -47,7 +47,7 @@ gdr_status parse(const gdr_problem* p, gdr::Problem& out) {
   return GDR_OK;
 }
 
-gdr_status tile_for(const gdr::Problem& pr, const gdr_tile* tile, int mode, gdr::Tile& t) {
+gdr_status tile_for(const gdr::Problem& pr, const gdr_tile* tile, int mode, int64_t rows, gdr::Tile& t) {
   std::string err;
   int32_t req[3];
   const int32_t* r = nullptr;
@@ -57,7 +57,7 @@ gdr_status tile_for(const gdr::Problem& pr, const gdr_tile* tile, int mode, gdr:
     req[2] = tile->stages;
     r = req;
   }
-  if (!gdr::choose_tile(pr, r, mode, t, err)) return fail(GDR_ERR_UNSUPPORTED, err);
+  if (!gdr::choose_tile(pr, r, mode, rows, t, err)) return fail(GDR_ERR_UNSUPPORTED, err);
   return GDR_OK;
 }
 
@@ -187,7 +187,7 @@ gdr_status gdr_state_scan(const gdr_problem* p, const gdr_tile* tile, const gdr_
     in_vk = 1;
   }
   gdr::Tile t;
-  GDR_TRY(tile_for(pr, tile, mode == 2 ? 0 : 0, t));
+  GDR_TRY(tile_for(pr, tile, 0, static_cast<int64_t>(pr.N) * P, t));
   return run_scan(pr, t, mode, P, k, w, u, g_cum, h_in, in_vk, h, v_new, hT, pr.state_vk, nullptr,
                   static_cast<hipStream_t>(stream));
 }
@@ -240,7 +240,7 @@ gdr_status gdr_segment_summaries(const gdr_problem* p, const gdr_tile* tile, int
   GDR_TRY(need(seg_state, "seg_state"));
   GDR_TRY(need(seg_trans, "seg_trans"));
   gdr::Tile t;
-  GDR_TRY(tile_for(pr, tile, 1, t));
+  GDR_TRY(tile_for(pr, tile, 1, static_cast<int64_t>(pr.N) * n_segments, t));
   return run_scan(pr, t, 1, n_segments, k, w, u, g_cum, nullptr, 0, nullptr, nullptr, seg_state, 1, seg_trans,
                   static_cast<hipStream_t>(stream));
 }
@@ -284,7 +284,7 @@ gdr_status gdr_plan_query(const gdr_problem* p, const gdr_tile* tile, int32_t n_
   GDR_TRY(parse(p, pr));
   const int mode = n_segments > 0 ? 1 : 0;
   gdr::Tile t;
-  GDR_TRY(tile_for(pr, tile, mode, t));
+  GDR_TRY(tile_for(pr, tile, mode, static_cast<int64_t>(pr.N) * (n_segments > 0 ? n_segments : 1), t));
   std::vector<gdr::Launch> plan = gdr::plan_scan(pr, t, mode, n_segments > 0 ? n_segments : 1, true, true);
   int64_t wg = 0, maxrows = 0;
   for (auto& l : plan) {

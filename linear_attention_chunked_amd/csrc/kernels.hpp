@@ -85,7 +85,9 @@ using LaunchFn = hipError_t (*)(const void* args, int grid, hipStream_t stream);
 LaunchFn find_scan(int dtype, int dk, int bv, int waves, int stages, int mode);
 LaunchFn find_scan2(int dk, int bv, int waves, int stages, int mode);
 LaunchFn find_prepare(int dtype, int dk, int dv);
+LaunchFn find_prepare2(int dk, int dv);
 LaunchFn find_output(int dtype, int dk, int dv);
+LaunchFn find_output2(int dk, int dv);
 LaunchFn find_compose(int dk);
 hipError_t launch_abc_z(const AbcArgs& a, hipStream_t s);
 hipError_t launch_abc_scan(const AbcArgs& a, hipStream_t s);

@@ -192,6 +192,7 @@ static hipError_t launch_output(const void* args, int grid, hipStream_t stream) 
 }
 
 LaunchFn find_output(int dtype, int dk, int dv) {
+  if (dtype == 1) return find_output2(dk, dv);  // bfloat16 storage: the gfx950 fast path
 #define GDR_OUT_CASE(T, DT, DK, DV) \
   if (dtype == DT && dk == DK && dv == DV) return &launch_output<T, DK, DV>;
   GDR_OUT_CASE(bf16_t, 1, 128, 128)

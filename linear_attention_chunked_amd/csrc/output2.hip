@@ -1,0 +1,199 @@
+// Chunk output for bfloat16 storage on gfx950 (float32 storage keeps
+// output.hip).  For token t of a chunk (gamma = chunk-local cumulative g):
+//
+//   o_t = scale * ( e^{gamma_t} q_t^T S_c + sum_{i <= t} e^{gamma_t - gamma_i} (q_t . k_i) v_new_i )
+//
+// One workgroup (4 waves) per (chunk, head, 64 value columns); wave w owns the
+// rows of token tile w.  Q, K, v_new and the pre-chunk state land in LDS
+// row-major through range-checked buffer loads (tail rows read as zero).
+// P^T = K Q^T is formed in accumulator layout, which (with the k(g, e) map of
+// common.hpp) is already the A operand of P v_new; v_new's operand, whose
+// contraction runs over tokens, comes from ds_read_b64_tr_b16.
+#include "kernels.hpp"
+
+namespace gdr {
+
+namespace {
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc3(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x2_t tr16o(const char* base, int off) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + off)));
+}
+__device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+}  // namespace
+
+template <int DK, int DV>
+struct Output2 {
+  using S = St<bf16_t>;
+  using frag = S::frag;
+  static constexpr int NT = 256;
+  static constexpr int BVO = 64;
+  static constexpr int NCT = BVO / 16;
+  static constexpr int SQ = DK * 2 + 16;   // Q, K, h rows (bytes): 16 consecutive rows hit distinct banks
+  static constexpr int SV = BVO * 2 + 32;  // v_new rows (transpose reads)
+  static constexpr int KS = DK / 32;
+
+  struct Smem {
+    char q[kChunk * SQ];
+    char k[kChunk * SQ];
+    char h[BVO * SQ];
+    char v[kChunk * SV];
+    float gam[kChunk];
+  };
+
+  __device__ static int find_row(const ChunkArgs& a, int chunk) {
+    int lo = 0, hi = a.n_rows - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.rows[mid].chunk_off <= chunk) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  }
+
+  __device__ static void run(const ChunkArgs& a, Smem& sm) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    constexpr int NVB = DV / BVO;
+    const int vb = blockIdx.x % NVB;
+    const int rest = blockIdx.x / NVB;
+    const int hd = rest % a.H;
+    const int chunk = rest / a.H;
+    if (chunk >= a.n_chunks) return;
+    const Row row = a.rows[find_row(a, chunk)];
+    const int cl = chunk - row.chunk_off;
+    const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(cl) * kChunk;
+    const int nvalid = min(kChunk, row.len - cl * kChunk);
+    const int64_t H = a.H;
+    const int col0 = vb * BVO;
+
+    {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (tok0 * H + hd) * DK;
+      const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (tok0 * H + hd) * DK;
+      const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + hd) * DV + col0;
+      const uint16_t* hp = static_cast<const uint16_t*>(a.h) +
+                           ((static_cast<int64_t>(a.chunk_base) + chunk) * H + hd) * DV * DK +
+                           static_cast<int64_t>(col0) * DK;
+      const uint32_t qk_bytes = static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2);
+      const rsrc_t rq = make_rsrc3(qp, qk_bytes);
+      const rsrc_t rk = make_rsrc3(kp, qk_bytes);
+      const rsrc_t rv = make_rsrc3(vp, static_cast<uint32_t>(((nvalid - 1) * H * DV + BVO) * 2));
+      const rsrc_t rh = make_rsrc3(hp, static_cast<uint32_t>(BVO * DK * 2));
+      constexpr int CQ = DK / 8, CV = BVO / 8;
+#pragma unroll
+      for (int i = 0; i < kChunk * CQ / NT; ++i) {
+        const int vv = tid + i * NT, r = vv / CQ, c = vv % CQ;
+        const int go = static_cast<int>(r * H * DK * 2 + c * 16);
+        *reinterpret_cast<u32x4_t*>(sm.q + r * SQ + c * 16) = __builtin_amdgcn_raw_buffer_load_b128(rq, go, 0, 0);
+        *reinterpret_cast<u32x4_t*>(sm.k + r * SQ + c * 16) = __builtin_amdgcn_raw_buffer_load_b128(rk, go, 0, 0);
+        *reinterpret_cast<u32x4_t*>(sm.h + r * SQ + c * 16) =
+            __builtin_amdgcn_raw_buffer_load_b128(rh, static_cast<int>(r * DK * 2 + c * 16), 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kChunk * CV / NT; ++i) {
+        const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
+        *reinterpret_cast<u32x4_t*>(sm.v + r * SV + c * 16) =
+            __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
+      }
+      if (tid < kChunk) sm.gam[tid] = (tid < nvalid) ? a.g[(tok0 + tid) * H + hd] : 0.f;
+    }
+    __syncthreads();
+
+    const char* rowq = sm.q + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;  // + 16 tile SQ + 64 s (+32)
+    const char* rowk = sm.k + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;
+    const char* rowh = sm.h + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;
+    auto rfrag = [&](const char* base, int tile, int s) {
+      return S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(base + 16 * tile * SQ + 64 * s),
+                                *reinterpret_cast<const u32x2_t*>(base + 16 * tile * SQ + 64 * s + 32));
+    };
+
+    // ---- P^T[i][t] = k_i . q_t for t in tile `wave`, i tiles 0..wave; O = Q S_c ----
+    f32x4_t pt[4], acc[NCT];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) pt[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const frag fq = rfrag(rowq, wave, s);
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+        if (it <= wave) S::mma(pt[it], rfrag(rowk, it, s), fq);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) S::mma(acc[ct], fq, rfrag(rowh, ct, s));
+    }
+    const int t = 16 * wave + c16;
+    const float gt = sm.gam[t];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const f32x4_t gi = *reinterpret_cast<const f32x4_t*>(&sm.gam[16 * it + 4 * g4]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * it + 4 * g4 + r;
+        pt[it][r] = (i <= t && t < nvalid) ? pt[it][r] * exp_f(gt - gi[r]) : 0.f;
+      }
+    }
+    const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(&sm.gam[16 * wave + 4 * g4]);
+    f32x4_t eg;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) eg[r] = exp_f(gr[r]);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] *= eg;
+
+    // ---- O += P v_new (B operand from transpose reads of the row-major v_new tile) ----
+    const char* vb_ = sm.v + (4 * g4 + (c16 >> 2)) * SV + 8 * (c16 & 3);  // + 32 s SV (+16 SV) + 32 ct
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (32 * s <= 16 * wave + 15) {
+        const frag fa = S::frag_from_f32(pt[2 * s], pt[2 * s + 1]);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          S::mma(acc[ct], fa, S::frag_from_quads(tr16o(vb_, 32 * s * SV + 32 * ct), tr16o(vb_, (32 * s + 16) * SV + 32 * ct)));
+      }
+    }
+
+    // ---- store o (rows past the tail dropped by the range check) ----
+    uint16_t* op = static_cast<uint16_t*>(a.o) + (tok0 * H + hd) * DV + col0;
+    const rsrc_t ro = make_rsrc3(op, static_cast<uint32_t>(((nvalid - 1) * H * DV + BVO) * 2));
+    const int rs = static_cast<int>(H * DV * 2);
+    const int voff = (16 * wave + 4 * g4) * rs + c16 * 2;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const uint32_t pk = pack_bf16x2(a.scale * acc[ct][r], a.scale * acc[ct][r + 1]);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk), ro, voff, r * rs + 32 * ct, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk >> 16), ro, voff, (r + 1) * rs + 32 * ct, 0);
+      }
+  }
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void output2_kernel(const ChunkArgs a) {
+  using K = Output2<DK, DV>;
+  __shared__ __align__(16) typename K::Smem sm;
+  K::run(a, sm);
+}
+
+template <int DK, int DV>
+static hipError_t launch_output2(const void* args, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((output2_kernel<DK, DV>), dim3(grid), dim3(256), 0, stream, *static_cast<const ChunkArgs*>(args));
+  return hipGetLastError();
+}
+
+LaunchFn find_output2(int dk, int dv) {
+  if (dk == 128 && dv == 128) return &launch_output2<128, 128>;
+  if (dk == 128 && dv == 64) return &launch_output2<128, 64>;
+  if (dk == 64 && dv == 128) return &launch_output2<64, 128>;
+  if (dk == 64 && dv == 64) return &launch_output2<64, 64>;
+  return nullptr;
+}
+
+}  // namespace gdr

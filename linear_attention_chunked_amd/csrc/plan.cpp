@@ -100,7 +100,7 @@ static bool tile_built(int dtype, int bv, int waves, int stages) {
   return false;
 }
 
-bool choose_tile(const Problem& p, const int32_t* req, int mode, Tile& t, std::string& err) {
+bool choose_tile(const Problem& p, const int32_t* req, int mode, int64_t rows, Tile& t, std::string& err) {
   int r[3] = {0, 0, 0};
   if (req != nullptr) {
     r[0] = req[0];
@@ -118,8 +118,8 @@ bool choose_tile(const Problem& p, const int32_t* req, int mode, Tile& t, std::s
     // buffer (several workgroups per CU) win; with very few pairs (one long
     // sequence, a handful of heads) 32-column blocks of 2 waves give more
     // units and a shorter chain per chunk.
-    const int64_t pairs = static_cast<int64_t>(p.N) * p.H;
-    const int64_t units64 = pairs * (p.DV / 64);
+    const int64_t pairs = rows * p.H;
+    const int64_t units64 = pairs * ((mode == 1 ? p.DV + p.DK : p.DV) / 64);
     if (p.dtype == 1) {
       r[0] = 64;
       r[1] = 4;

@@ -56,8 +56,10 @@ bool parse_problem(int B, int64_t T, int H, int DK, int DV, int N, const int32_t
                    int state_layout, Problem& out, std::string& err);
 
 // Tile for the serial scans: explicit request (validated) or the table.
-bool choose_tile(const Problem& p, const int32_t* req /* bv, waves, stages or null */, int mode, Tile& out,
-                 std::string& err);
+// `rows` is the number of serial chains per head (sequences, or sequences x
+// segments); mode 1 (summaries) also runs DK transition columns.
+bool choose_tile(const Problem& p, const int32_t* req /* bv, waves, stages or null */, int mode, int64_t rows,
+                 Tile& out, std::string& err);
 
 // Segment boundaries of one sequence: [t0, t1) token ranges relative to its start.
 void segment_bounds(int64_t len, int P, std::vector<int64_t>& t0, std::vector<int64_t>& t1);

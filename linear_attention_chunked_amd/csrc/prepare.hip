@@ -277,6 +277,7 @@ static hipError_t launch_prepare(const void* args, int grid, hipStream_t stream)
 }
 
 LaunchFn find_prepare(int dtype, int dk, int dv) {
+  if (dtype == 1) return find_prepare2(dk, dv);  // bfloat16 storage: the gfx950 fast path
 #define GDR_PREP_CASE(T, DT, DK, DV) \
   if (dtype == DT && dk == DK && dv == DV) return &launch_prepare<T, DK, DV>;
   GDR_PREP_CASE(bf16_t, 1, 128, 128)

@@ -1,0 +1,314 @@
+// Chunk preparation for bfloat16 storage on gfx950 (float32 storage keeps
+// prepare.hip).  Same factors:
+//
+//   gamma  = chunk-local inclusive cumsum of g
+//   A[t,i] = beta_t exp(gamma_t - gamma_i) (k_t . k_i)     (i < t)
+//   T      = (I + A)^-1                                      FP32
+//   w      = T diag(beta exp(gamma)) K,   u = T diag(beta) V
+//
+// One workgroup (4 waves) per (chunk, head).  Layout of the work:
+//   * K and V land in LDS row-major (tail rows read as zero through the buffer
+//     range check); the products that contract over tokens read them as MFMA
+//     operands with ds_read_b64_tr_b16.
+//   * The Gram matrix runs on bf16 MFMA in FP32.
+//   * T by blocks of 16: the four diagonal blocks by forward substitution
+//     (one wave each), then every off-diagonal block as FP32 MFMA products:
+//       T[1][0] = -T[1][1] (A[1][0] T[0][0]),  T[3][2] likewise,
+//       T[2:4][0:2] = -T[2:4][2:4] (A[2:4][0:2] T[0:2][0:2]).
+//     In the 16x16x4 FP32 MFMA a product's accumulator (lane (g, c) holds rows
+//     4g + r of column c) is directly the B operand of the next product when
+//     the contraction index is ordered k = 4g + r, so chained products need
+//     no LDS round trip.
+//   * w and u from T' = T diag(.) split into bf16 hi + lo parts (one rounding:
+//     the final store).
+#include "kernels.hpp"
+
+namespace gdr {
+
+namespace {
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc2(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x2_t tr16(const char* base, int off) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + off)));
+}
+__device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+// D (16x16, C layout) += X (16x16) Y (16x16) in FP32 with k = 4g + r:
+// a[r] = X[c][4g + r] (row c of X), b[r] = Y[4g + r][c] (the C layout of Y).
+__device__ __forceinline__ void mm16(f32x4_t& d, const f32x4_t& a, const f32x4_t& b) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], d, 0, 0, 0);
+}
+
+}  // namespace
+
+template <int DK, int DV>
+struct Prepare2 {
+  using S = St<bf16_t>;
+  using frag = S::frag;
+  static constexpr int NT = 256;
+  static constexpr int SKB = DK * 2 + 32;   // padded row strides (bytes)
+  static constexpr int SVB = DV * 2 + 32;
+  static constexpr int LDA = 64 + 4;        // FP32 64x64 matrices (floats)
+  static constexpr int KS = DK / 32;
+
+  struct Smem {
+    char k[kChunk * SKB];
+    char v[kChunk * SVB];
+    float a[kChunk * LDA];
+    float t[kChunk * LDA];
+    float gam[kChunk];
+    float beta[kChunk];
+    float bg[kChunk];  // beta exp(gamma)
+  };
+
+  __device__ static int find_row(const ChunkArgs& a, int chunk) {
+    int lo = 0, hi = a.n_rows - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.rows[mid].chunk_off <= chunk) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  }
+
+  __device__ static void run(const ChunkArgs& a, Smem& sm) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int chunk = blockIdx.x / a.H;
+    const int hd = blockIdx.x % a.H;
+    if (chunk >= a.n_chunks) return;
+    const Row row = a.rows[find_row(a, chunk)];
+    const int cl = chunk - row.chunk_off;
+    const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(cl) * kChunk;
+    const int nvalid = min(kChunk, row.len - cl * kChunk);
+    const int64_t H = a.H;
+
+    // ---- K, V rows (zero past the tail), gamma, beta ----
+    {
+      const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (tok0 * H + hd) * DK;
+      const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + hd) * DV;
+      const rsrc_t rk = make_rsrc2(kp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
+      const rsrc_t rv = make_rsrc2(vp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
+      constexpr int CK = DK / 8, CV = DV / 8;  // 16-byte chunks per row
+#pragma unroll
+      for (int i = 0; i < kChunk * CK / NT; ++i) {
+        const int vv = tid + i * NT, r = vv / CK, c = vv % CK;
+        *reinterpret_cast<u32x4_t*>(sm.k + r * SKB + c * 16) =
+            __builtin_amdgcn_raw_buffer_load_b128(rk, static_cast<int>(r * H * DK * 2 + c * 16), 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kChunk * CV / NT; ++i) {
+        const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
+        *reinterpret_cast<u32x4_t*>(sm.v + r * SVB + c * 16) =
+            __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
+      }
+      if (wave == 0) {
+        float x = (lane < nvalid) ? a.g[(tok0 + lane) * H + hd] : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(x, off, 64);
+          if (lane >= off) x += y;
+        }
+        const float b = (lane < nvalid) ? a.beta[(tok0 + lane) * H + hd] : 0.f;
+        sm.gam[lane] = x;
+        sm.beta[lane] = b;
+        sm.bg[lane] = b * exp2f_fast(x);
+        if (lane < nvalid) a.g_cum[(tok0 + lane) * H + hd] = x;
+      }
+    }
+    __syncthreads();
+
+    // ---- Gram matrix row tile `wave`; A = beta_t e^{gamma_t - gamma_i} G (i < t) ----
+    {
+      f32x4_t acc[4];
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj) acc[tj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const char* kr = sm.k + c16 * SKB + (g4 >> 1) * 16 + (g4 & 1) * 8;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const frag fa = S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(kr + 16 * wave * SKB + 64 * s),
+                                           *reinterpret_cast<const u32x2_t*>(kr + 16 * wave * SKB + 64 * s + 32));
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+          if (tj <= wave) {
+            const frag fb = S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(kr + 16 * tj * SKB + 64 * s),
+                                               *reinterpret_cast<const u32x2_t*>(kr + 16 * tj * SKB + 64 * s + 32));
+            S::mma(acc[tj], fa, fb);
+          }
+        }
+      }
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj) {
+        const int i = 16 * tj + c16;
+        const float gi = sm.gam[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * wave + 4 * g4 + r;
+          sm.a[t * LDA + i] = (i < t) ? sm.beta[t] * exp2f_fast(sm.gam[t] - gi) * acc[tj][r] : 0.f;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- diagonal blocks: T[b][b] = (I + A[b][b])^-1, wave b, lane j = column ----
+    if (lane < 16) {
+      const int b0 = 16 * wave, j = lane;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s = (r == j) ? 1.f : 0.f;
+        const float* ar = &sm.a[(b0 + r) * LDA + b0];
+#pragma unroll
+        for (int i = 0; i < r; ++i) s -= ar[i] * x[i];
+        x[r] = s;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.t[(b0 + r) * LDA + b0 + j] = x[r];
+    }
+    // strictly-upper blocks of T are zero
+    for (int e = tid; e < kChunk * kChunk; e += NT) {
+      const int r = e >> 6, c = e & 63;
+      if ((c >> 4) > (r >> 4)) sm.t[r * LDA + c] = 0.f;
+    }
+    __syncthreads();
+
+    // FP32 operand reads for mm16: row-major rows (a) and C-layout columns (b)
+    auto a_rows = [&](const float* m, int r0, int c0) {  // X[c16][4 g4 + r] of the block at (r0, c0)
+      return *reinterpret_cast<const f32x4_t*>(m + (r0 + c16) * LDA + c0 + 4 * g4);
+    };
+    auto b_cols = [&](const float* m, int r0, int c0) {  // Y[4 g4 + r][c16]
+      f32x4_t y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = m[(r0 + 4 * g4 + r) * LDA + c0 + c16];
+      return y;
+    };
+    auto store_c = [&](float* m, int r0, int c0, const f32x4_t& d) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m[(r0 + 4 * g4 + r) * LDA + c0 + c16] = d[r];
+    };
+
+    // ---- T[1][0] (wave 0) and T[3][2] (wave 1) ----
+    if (wave < 2) {
+      const int p = 32 * wave;  // block (p+16, p)
+      f32x4_t y{0.f, 0.f, 0.f, 0.f}, x{0.f, 0.f, 0.f, 0.f};
+      mm16(y, a_rows(sm.a, p + 16, p), b_cols(sm.t, p, p));      // A[1][0] T[0][0]
+      mm16(x, a_rows(sm.t, p + 16, p + 16), y);                  // T[1][1] (.)
+      store_c(sm.t, p + 16, p, -x);
+    }
+    __syncthreads();
+
+    // ---- T[2+i][j] = -(T_hi[i][0] Y[0][j] + T_hi[i][1] Y[1][j]),  Y = A[2:4][0:2] T[0:2][j] ----
+    {
+      const int i = wave >> 1, j = wave & 1;
+      f32x4_t y0{0.f, 0.f, 0.f, 0.f}, y1{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (k >= j) {  // T[0][1] is zero
+          const f32x4_t tb = b_cols(sm.t, 16 * k, 16 * j);
+          mm16(y0, a_rows(sm.a, 32, 16 * k), tb);
+          mm16(y1, a_rows(sm.a, 48, 16 * k), tb);
+        }
+      }
+      f32x4_t x{0.f, 0.f, 0.f, 0.f};
+      mm16(x, a_rows(sm.t, 32 + 16 * i, 32), y0);                   // T_hi[i][0] (T[2][2] or T[3][2])
+      if (i == 1) mm16(x, a_rows(sm.t, 48, 48), y1);                // T_hi[1][1] = T[3][3]
+      store_c(sm.t, 32 + 16 * i, 16 * j, -x);
+    }
+    __syncthreads();
+
+    // ---- w^T = K^T T'^T and u^T = V^T T''^T; wave = token tile of the output ----
+    const int t = 16 * wave + c16;
+    frag bw_hi[2], bw_lo[2], bu_hi[2], bu_lo[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int i0 = 32 * s + 4 * g4;
+      const f32x4_t t0 = *reinterpret_cast<const f32x4_t*>(&sm.t[t * LDA + i0]);
+      const f32x4_t t1 = *reinterpret_cast<const f32x4_t*>(&sm.t[t * LDA + i0 + 16]);
+      const f32x4_t bg0 = *reinterpret_cast<const f32x4_t*>(&sm.bg[i0]);
+      const f32x4_t bg1 = *reinterpret_cast<const f32x4_t*>(&sm.bg[i0 + 16]);
+      const f32x4_t be0 = *reinterpret_cast<const f32x4_t*>(&sm.beta[i0]);
+      const f32x4_t be1 = *reinterpret_cast<const f32x4_t*>(&sm.beta[i0 + 16]);
+      const f32x4_t w0 = t0 * bg0, w1 = t1 * bg1, u0 = t0 * be0, u1 = t1 * be1;
+      bw_hi[s] = S::frag_from_f32(w0, w1);
+      bu_hi[s] = S::frag_from_f32(u0, u1);
+      f32x4_t wl0, wl1, ul0, ul1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        wl0[r] = w0[r] - bf16_to_f32(f32_to_bf16(w0[r]));
+        wl1[r] = w1[r] - bf16_to_f32(f32_to_bf16(w1[r]));
+        ul0[r] = u0[r] - bf16_to_f32(f32_to_bf16(u0[r]));
+        ul1[r] = u1[r] - bf16_to_f32(f32_to_bf16(u1[r]));
+      }
+      bw_lo[s] = S::frag_from_f32(wl0, wl1);
+      bu_lo[s] = S::frag_from_f32(ul0, ul1);
+    }
+    const int nsteps = (16 * wave + 15) / 32 + 1;  // T is lower triangular
+    // A operand K^T[d][i] / V^T[d][i] via transpose reads of the row-major tiles
+    const int tr_row = 4 * g4 + (c16 >> 2);
+    const int tr_col = 8 * (c16 & 3);
+    uint16_t* wo = static_cast<uint16_t*>(a.w) + (tok0 * H + hd) * DK;
+    uint16_t* uo = static_cast<uint16_t*>(a.u) + (tok0 * H + hd) * DV;
+    const rsrc_t rwo = make_rsrc2(wo, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
+    const rsrc_t ruo = make_rsrc2(uo, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
+#pragma unroll
+    for (int dt = 0; dt < DK / 16; ++dt) {
+      f32x4_t acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (s < nsteps) {
+          const char* base = sm.k + (32 * s + tr_row) * SKB + 32 * dt + tr_col;
+          const frag fa = S::frag_from_quads(tr16(base, 0), tr16(base, 16 * SKB));
+          S::mma(acc, fa, bw_hi[s]);
+          S::mma(acc, fa, bw_lo[s]);
+        }
+      }
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])}, rwo,
+                                            static_cast<int>(t * H * DK * 2 + (16 * dt + 4 * g4) * 2), 0, 0);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) {
+      f32x4_t acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (s < nsteps) {
+          const char* base = sm.v + (32 * s + tr_row) * SVB + 32 * dt + tr_col;
+          const frag fa = S::frag_from_quads(tr16(base, 0), tr16(base, 16 * SVB));
+          S::mma(acc, fa, bu_hi[s]);
+          S::mma(acc, fa, bu_lo[s]);
+        }
+      }
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])}, ruo,
+                                            static_cast<int>(t * H * DV * 2 + (16 * dt + 4 * g4) * 2), 0, 0);
+    }
+  }
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void prepare2_kernel(const ChunkArgs a) {
+  using K = Prepare2<DK, DV>;
+  __shared__ __align__(16) typename K::Smem sm;
+  K::run(a, sm);
+}
+
+template <int DK, int DV>
+static hipError_t launch_prepare2(const void* args, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((prepare2_kernel<DK, DV>), dim3(grid), dim3(256), 0, stream, *static_cast<const ChunkArgs*>(args));
+  return hipGetLastError();
+}
+
+LaunchFn find_prepare2(int dk, int dv) {
+  if (dk == 128 && dv == 128) return &launch_prepare2<128, 128>;
+  if (dk == 128 && dv == 64) return &launch_prepare2<128, 64>;
+  if (dk == 64 && dv == 128) return &launch_prepare2<64, 128>;
+  if (dk == 64 && dv == 64) return &launch_prepare2<64, 64>;
+  return nullptr;
+}
+
+}  // namespace gdr
