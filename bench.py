@@ -53,7 +53,7 @@ def scan_flops(lengths, H, DK, DV):
 
 def source_sha():
     h = hashlib.sha256()
-    for f in ("scan.hip", "common.hpp", "kernels.hpp"):
+    for f in ("scan2.hip", "common.hpp", "kernels.hpp"):
         with open(os.path.join(ROOT, "linear_attention_chunked_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -219,6 +219,8 @@ def main():
 
     if not args.no_long_state:
         out["long_state"] = long_state(pkg, torch, dev)
+        out["new_states"] = new_states(pkg, torch, dev)
+        out["abc_affine"] = abc_affine(pkg, torch, dev)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
@@ -263,6 +265,59 @@ def long_state(pkg, torch, dev, reps=5):
                      "serial_alg_bytes": alg, "frac_of_hbm_at_serial_bytes": round(alg / t / 8e12, 4)}
     res["workload"] = "long_state_h8 (T=65536, H=8, dk=dv=128, bf16, 16 segments)"
     return res
+
+
+def _event_median_us(torch, fn, reps=10):
+    fn()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+    return sorted(times)[len(times) // 2]
+
+
+def new_states(pkg, torch, dev):
+    """8 packed sequences of 1306..3597 tokens, 32 heads: the state scan alone
+    (pre-chunk states emitted in bf16)."""
+    from workloads import make_config
+
+    inp = make_config("new_states")
+    k, v, g, beta = (x.to(dev) for x in (inp.k, inp.v, inp.g, inp.beta))
+    cu = inp.cu_seqlens
+    g_cum, w, u = pkg.gdr_chunk_prepare(k, v, g, beta, cu)
+    h, v_new, hT = pkg.gdr_state_scan(k, w, u, g_cum, None, cu)
+    bufs = {"h": h, "v_new": v_new, "hT": hT}
+    us = _event_median_us(torch, lambda: pkg.gdr_state_scan(k, w, u, g_cum, None, cu, out=bufs))
+    alg = scan_alg_bytes(inp.lengths, inp.H, inp.DK, inp.DV, 2, 2, False, True)
+    return {"workload": "new_states (8 seqs, 18261 tokens, H=32, dk=dv=128, bf16)", "scan_us": round(us, 1),
+            "Mtok_head_per_s": round(inp.token_heads / us, 1), "alg_bytes": alg,
+            "frac_of_hbm": round(alg / (us * 1e-6) / 8e12, 4)}
+
+
+def abc_alg_bytes(B, T, H, K, M, V):
+    """Read k, v, s once; write the bf16 pre-chunk states and the FP32 finals;
+    the chunk-end normaliser workspace is written once and read once."""
+    nc = (T + 63) // 64
+    return (B * T * H * (K + V + M) * 2 + B * nc * H * (K * M + M * V) * 2 + B * H * (K * M + M * V) * 4
+            + 2 * B * nc * H * M * 4)
+
+
+def abc_affine(pkg, torch, dev):
+    """ABC slot-state construction at B=2, T=16384, H=4, K=256, M=64, V=512."""
+    from workloads import make_config
+
+    inp = make_config("abc_affine")
+    k, v, s = (x.to(dev) for x in (inp.k, inp.v, inp.s))
+    us = _event_median_us(torch, lambda: pkg.abc_affine_scan(k, v, s), reps=5)
+    alg = abc_alg_bytes(inp.B, inp.T, inp.H, inp.K, inp.M, inp.V)
+    return {"workload": "abc_affine (B=2, T=16384, H=4, K=256, M=64, V=512, bf16)", "us": round(us, 1),
+            "Mtok_head_per_s": round(inp.token_heads / us, 1), "alg_bytes": alg,
+            "frac_of_hbm": round(alg / (us * 1e-6) / 8e12, 4)}
 
 
 if __name__ == "__main__":
