@@ -2,235 +2,466 @@
 // #23, "[Perf][B300] Parallelize ABC chunk state construction with affine
 // summaries": "Problem" and "Proposed Dataflow").
 //
-// Normaliser: z_t = log(e^{z_{t-1}} + e^{s_t}) per slot.  Two levels:
-//   abc_chunk_lse   one wave per (b, chunk, h), lane = slot: the chunk-local
-//                   running log-sum-exp (written to z when requested) and the
-//                   chunk total;
-//   abc_carry       one wave per (b, h): z at chunk ends,
-//                   zc[c] = logaddexp(zc[c-1], lse[c]), serial over chunks;
-//   abc_fix_z       (only when z is requested) z_t = logaddexp(zc[c-1], local_t).
+// Normaliser: z_t = log(e^{z_{t-1}} + e^{s_t}) per slot.  Three levels:
+//   abc_chunk_lse   one workgroup per (b, chunk, h): four waves take 16 tokens
+//                   each (lane = slot), combine through LDS, and write the
+//                   chunk's total (and, when requested, the chunk-local
+//                   running values into z);
+//   abc_carry       one workgroup per (b, h): zc[c] = logaddexp(zc[c-1], lse[c])
+//                   in four interleaved quarters of the chunk range;
+//   abc_weights     one workgroup per (b, chunk, h): the chunk's weights
+//                   E_t = exp(s_t - zc[c]) in the storage dtype, once for all
+//                   the state tiles that use them, and (when z is requested)
+//                   z_t = logaddexp(zc[c-1], local_t).
+// log-add-exp runs on the hardware base-2 exponential and logarithm: the
+// correction term log(1 + e^{-|a-b|}) lies in [0, ln 2], so its absolute
+// error (a few 1e-8) stays below the rounding of the FP32 sum it is added to.
 //
 // States: every 64-token chunk applies the exact diagonal affine map
 //   S <- S * r_c + c_c,   r_c = exp(zc[c-1] - zc[c]),  E_t = exp(s_t - zc[c]),
 //   Hk [K x M]:  c_c = K_c^T E   (r over columns)
 //   Hv [M x V]:  c_c = E^T V_c   (r over rows)
 // One workgroup owns a 64x64 tile of Hk or Hv of one (b, h) and walks the
-// chunks in order: the chunk contribution is formed on MFMA in FP32
-// accumulators and added to the FP32 state in registers, so the "FP32
-// summary" of the page never leaves the chip; the state before each chunk is
-// written once, in the storage dtype.
+// chunks in order.  c_c does not depend on the state, so the walk is a
+// stream, not a latency chain: the global loads of the next D chunks are in
+// flight (a ring of register stages), each chunk is staged once in LDS
+// row-major exactly as loaded, and the MFMA operands, which contract over
+// tokens, come from the row-major tiles through ds_read_b64_tr_b16 (E
+// arrives precomputed, so a chunk costs the state tile no exponentials).  The
+// contribution is accumulated in FP32 on top of the scaled state, so the
+// page's FP32 summary never leaves the chip; the state before each chunk is
+// written once, in the storage dtype.  The tile is held transposed (rows =
+// the contiguous dimension of the stored state), so each lane's four
+// accumulator rows are four adjacent elements in memory: one 8-byte store.
 #include <math.h>
+#include <stdlib.h>
 
+#include "gfx950.hpp"
 #include "kernels.hpp"
 
 namespace gdr {
 
 __device__ __forceinline__ float logaddexp_f(float a, float b) {
   const float m = fmaxf(a, b);
-  if (m == -INFINITY) return -INFINITY;
-  return m + log1pf(expf(-fabsf(a - b)));
+  const float d = exp_fast(-fabsf(a - b));  // in [0, 1]; NaN only when both are -inf
+  const float l = m + 0.69314718055994531f * __builtin_amdgcn_logf(1.f + d);
+  return m == -INFINITY ? -INFINITY : l;
 }
 
 // ---------------------------------------------------------------- normaliser
-__global__ __launch_bounds__(64) void abc_chunk_lse(const AbcArgs a) {
-  const int m = threadIdx.x;  // slot (M == 64)
+__global__ __launch_bounds__(256) void abc_chunk_lse(const AbcArgs a) {
+  __shared__ float tot[4][64];
+  const int m = threadIdx.x & 63;  // slot (M == 64)
+  const int grp = threadIdx.x >> 6;  // 16-token group
   const int bx = blockIdx.x;
   const int h = bx % a.H;
   const int c = (bx / a.H) % a.NC;
   const int b = bx / (a.H * a.NC);
   const uint16_t* s = static_cast<const uint16_t*>(a.s);
-  const int t0 = c * kChunk;
-  const int n = min(kChunk, a.T - t0);
+  const int t0 = c * kChunk + 16 * grp;
+  const int n = max(0, min(16, a.T - t0));
+  float run[16];
   float L = -INFINITY;
-  for (int t = 0; t < n; ++t) {
-    const int64_t off = ((static_cast<int64_t>(b) * a.T + t0 + t) * a.H + h) * a.M + m;
-    L = logaddexp_f(L, bf16_to_f32(s[off]));
-    if (a.z != nullptr) a.z[off] = L;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < n) L = logaddexp_f(L, bf16_to_f32(s[((static_cast<int64_t>(b) * a.T + t0 + i) * a.H + h) * a.M + m]));
+    run[i] = L;
   }
-  a.zc[((static_cast<int64_t>(b) * a.NC + c) * a.H + h) * a.M + m] = L;
+  tot[grp][m] = L;
+  __syncthreads();
+  float off = -INFINITY;
+  for (int g = 0; g < grp; ++g) off = logaddexp_f(off, tot[g][m]);
+  if (a.z != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < n) a.z[((static_cast<int64_t>(b) * a.T + t0 + i) * a.H + h) * a.M + m] = logaddexp_f(off, run[i]);
+  }
+  if (grp == 3) a.lse[((static_cast<int64_t>(b) * a.NC + c) * a.H + h) * a.M + m] = logaddexp_f(off, L);
 }
 
-__global__ __launch_bounds__(64) void abc_carry(const AbcArgs a) {
-  const int m = threadIdx.x;
+__global__ __launch_bounds__(256) void abc_carry(const AbcArgs a) {
+  // pass 1: each quarter's total; pass 2: each quarter re-runs its chain from
+  // the log-sum-exp of the quarters before it and writes zc
+  __shared__ float tot[4][64];
+  const int m = threadIdx.x & 63;
+  const int q = threadIdx.x >> 6;  // quarter of the chunk range
   const int h = blockIdx.x % a.H;
   const int b = blockIdx.x / a.H;
-  float z = -INFINITY;
-  for (int c = 0; c < a.NC; ++c) {
-    const int64_t off = ((static_cast<int64_t>(b) * a.NC + c) * a.H + h) * a.M + m;
-    z = logaddexp_f(z, a.zc[off]);
-    a.zc[off] = z;
-  }
+  const int per = (a.NC + 3) / 4;
+  const int c0 = min(a.NC, q * per), c1 = min(a.NC, c0 + per);
+  const float* lse = a.lse + (static_cast<int64_t>(b) * a.NC * a.H + h) * a.M + m;
+  float* zc = a.zc + (static_cast<int64_t>(b) * a.NC * a.H + h) * a.M + m;
+  const int64_t step = static_cast<int64_t>(a.H) * a.M;
+  auto chain = [&](float z, bool write) {
+    int c = c0;
+    for (; c + 8 <= c1; c += 8) {  // eight independent loads ahead of the serial chain
+      float l[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) l[i] = lse[(c + i) * step];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        z = logaddexp_f(z, l[i]);
+        if (write) zc[(c + i) * step] = z;
+      }
+    }
+    for (; c < c1; ++c) {
+      z = logaddexp_f(z, lse[c * step]);
+      if (write) zc[c * step] = z;
+    }
+    return z;
+  };
+  tot[q][m] = chain(-INFINITY, false);
+  __syncthreads();
+  float off = -INFINITY;
+  for (int g = 0; g < q; ++g) off = logaddexp_f(off, tot[g][m]);
+  chain(off, true);
 }
 
-__global__ __launch_bounds__(256) void abc_fix_z(const AbcArgs a) {
-  // one workgroup per (b, chunk >= 1, h): 64 tokens x 64 slots
+__global__ __launch_bounds__(256) void abc_weights(const AbcArgs a) {
+  // 64 tokens x 64 slots: thread = (row, 8 slots), rows row and row + 32
   const int bx = blockIdx.x;
   const int h = bx % a.H;
-  const int c = 1 + (bx / a.H) % (a.NC - 1);
-  const int b = bx / (a.H * (a.NC - 1));
-  const int t0 = c * kChunk;
-  const int n = min(kChunk, a.T - t0);
-  for (int e = threadIdx.x; e < kChunk * 64; e += 256) {
-    const int t = e / 64, m = e % 64;
-    if (t < n) {
-      const float zp = a.zc[((static_cast<int64_t>(b) * a.NC + c - 1) * a.H + h) * a.M + m];
-      const int64_t off = ((static_cast<int64_t>(b) * a.T + t0 + t) * a.H + h) * a.M + m;
-      a.z[off] = logaddexp_f(zp, a.z[off]);
+  const int c = (bx / a.H) % a.NC;
+  const int b = bx / (a.H * a.NC);
+  const int tid = threadIdx.x;
+  const int row = tid >> 3, cv = tid & 7;
+  const int n = min(kChunk, a.T - c * kChunk);
+  const int64_t H = a.H, M = a.M;
+  const float* zp = a.zc + ((static_cast<int64_t>(b) * a.NC + c) * H + h) * M + 8 * cv;
+  const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(zp);
+  const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(zp + 4);
+  const float zz[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = row + 32 * i;
+    if (r >= n) continue;
+    const int64_t off = ((static_cast<int64_t>(b) * a.T + static_cast<int64_t>(c) * kChunk + r) * H + h) * M + 8 * cv;
+    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.s) + off);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    uint32_t pk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      pk[j] = pack_bf16x2(exp_fast(__builtin_bit_cast(float, w[j] << 16) - zz[2 * j]),
+                          exp_fast(__builtin_bit_cast(float, w[j] & 0xffff0000u) - zz[2 * j + 1]));
+    *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.e) + off) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+    if (a.z != nullptr && c > 0) {
+      const float* zq = zp - H * M;  // zc[c - 1]
+      const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(zq);
+      const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(zq + 4);
+      f32x4_t* zl = reinterpret_cast<f32x4_t*>(a.z + off);
+      f32x4_t l0 = zl[0], l1 = zl[1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        l0[j] = logaddexp_f(p0[j], l0[j]);
+        l1[j] = logaddexp_f(p1[j], l1[j]);
+      }
+      zl[0] = l0;
+      zl[1] = l1;
     }
   }
 }
 
 // ---------------------------------------------------------------- states
+// IS_K: the tile is XW rows (k) of Hk, held as Hk^T [slot][k]; otherwise XW
+// columns (v) of Hv, held as Hv^T [v][slot].  XW (64, 32 or 16) sets how many
+// workgroups share one (b, h): the chunk walk is a fixed-latency loop, so
+// narrower tiles put more of the chip to work when B * H is small.
+// The chunk loop runs over a multiple of D chunks; chunks past the end read
+// and write empty buffer ranges and act as the identity (E = 0, r = 1), so
+// every iteration issues the same memory operations and the compiler's wait
+// counts keep D chunks in flight.
+template <bool IS_K, int XW>
 struct AbcStates {
   using S = St<bf16_t>;
-  using quad = S::quad;
   using frag = S::frag;
-  static constexpr int LDT = kChunk + 4;  // transposed tiles, bf16 elements
+  static constexpr int D = 8;             // chunks in flight
+  static constexpr int NR = XW / 16;      // 16-wide blocks of the x dimension = MFMA tiles per wave
+  static constexpr int STE = 128 + 32;    // LDS row stride (bytes) of the 64-slot E tile
+  static constexpr int STX = XW * 2 + (XW == 64 ? 32 : 16);  // ... and of the x tile
+  static constexpr int XB = XW / 2;       // x bytes per thread per chunk (64 rows x XW bf16 / 256 threads)
+
+  // pre-chunk state staged in its memory layout: Hk rows (k) of 64 slots, or
+  // Hv rows (slots) of XW columns; written out the next chunk in whole rows
+  static constexpr int STH = IS_K ? 64 * 2 + 16 : XW * 2 + 16;
+  static constexpr int HSZ = (XW * (64 * 2 + 16) > 64 * (XW * 2 + 16)) ? XW * (64 * 2 + 16) : 64 * (XW * 2 + 16);
 
   struct Smem {
-    uint16_t xt[64 * LDT];   // X^T: 64 state rows/cols (k or v) x 64 tokens
-    uint16_t et[64 * LDT];   // E^T: 64 slots x 64 tokens
-    float r[64];
+    char x[2][kChunk * STX];  // k or v tile of the chunk, row-major [token][column]
+    char e[2][kChunk * STE];  // E, row-major [token][slot]
+    char hs[2][HSZ];          // staged pre-chunk state, by chunk parity
+    float r[3][64];           // r_c by chunk modulo 3
   };
 
-  __device__ static void run(const AbcArgs& a, Smem& sm) {
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
-    const int nk = a.K / 64, nv = a.V / 64;
-    const int tiles = nk + nv;
-    const int bx = blockIdx.x;
-    const int tile = bx % tiles;
-    const int h = (bx / tiles) % a.H;
-    const int b = bx / (tiles * a.H);
-    const bool is_k = tile < nk;
-    const int x0 = is_k ? 64 * tile : 64 * (tile - nk);  // first k row / v column of the tile
-    const int X = is_k ? a.K : a.V;
-    const uint16_t* xp = static_cast<const uint16_t*>(is_k ? a.k : a.v);
-    const uint16_t* sp = static_cast<const uint16_t*>(a.s);
-    const int64_t H = a.H, M = a.M;
+  struct Stage {
+    u32x4_t x[XB >= 16 ? XB / 16 : 1];
+    u32x4_t e[2];
+    float z;                  // zc of the chunk for slot tid % 64
+  };
 
-    f32x4_t acc[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  struct Ctx {
+    const AbcArgs* a;
+    int b, h, x0, X;
+    int vo_x[XB >= 16 ? XB / 16 : 1], vo_e[2];  // per-thread byte offsets inside a chunk
+    int lo_x[XB >= 16 ? XB / 16 : 1];           // ... and in the LDS x tile
+    int vo_h[NR];             // per-lane byte offsets of the state tile (finals)
+    int lo_h[NR];             // ... and in the staging buffer
+    int vo_o[XB >= 16 ? XB / 16 : 1], lo_o[XB >= 16 ? XB / 16 : 1];  // write-out: global / staging
+  };
 
-    for (int c = 0; c < a.NC; ++c) {
-      const int t0 = c * kChunk;
-      const int n = min(kChunk, a.T - t0);
-      const int64_t zrow = ((static_cast<int64_t>(b) * a.NC + c) * H + h) * M;
-      __syncthreads();
-      // X^T and E^T (4x4 register transposes), r
-      {
-        const int blk = tid;  // 16 token quads x 16 column quads = 256 blocks
-        const int cq = blk % 16, tq = blk / 16;
-        quad in[4], tr[4];
+  __device__ static __forceinline__ void load(Stage& st, const Ctx& x, int c) {
+    const AbcArgs& a = *x.a;
+    const int64_t H = a.H;
+    const int64_t tok0 = static_cast<int64_t>(x.b) * a.T + static_cast<int64_t>(c) * kChunk;
+    const int n = min(kChunk, a.T - c * kChunk);
+    const bool any = n > 0;
+    const uint16_t* xp = static_cast<const uint16_t*>(IS_K ? a.k : a.v) + (tok0 * H + x.h) * x.X + x.x0;
+    const uint16_t* ep = static_cast<const uint16_t*>(a.e) + (tok0 * H + x.h) * a.M;
+    const float* lp = a.zc + ((static_cast<int64_t>(x.b) * a.NC + c) * H + x.h) * a.M;
+    const rsrc_t rx = make_rsrc(xp, any ? static_cast<uint32_t>(((n - 1) * H * x.X + XW) * 2) : 0u);
+    const rsrc_t re = make_rsrc(ep, any ? static_cast<uint32_t>(((n - 1) * H * a.M + 64) * 2) : 0u);
+    const rsrc_t rl = make_rsrc(lp, any ? 256u : 0u);
+    if constexpr (XB >= 16) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 4 * tq + r;
-          in[r] = (t < n) ? ld_quad<bf16_t>(reinterpret_cast<const bf16_t*>(
-                                xp + ((static_cast<int64_t>(b) * a.T + t0 + t) * H + h) * X + x0 + 4 * cq))
-                          : S::zero_quad();
-        }
-        S::transpose4(in, tr);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<quad*>(&sm.xt[(4 * cq + j) * LDT + 4 * tq]) = tr[j];
-        const f32x4_t zl = *reinterpret_cast<const f32x4_t*>(a.zc + zrow + 4 * cq);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 4 * tq + r;
-          float e[4] = {0.f, 0.f, 0.f, 0.f};
-          if (t < n) {
-            const quad sq = ld_quad<bf16_t>(reinterpret_cast<const bf16_t*>(
-                sp + ((static_cast<int64_t>(b) * a.T + t0 + t) * H + h) * M + 4 * cq));
-            float sv[4];
-            S::quad_to_f32(sq, sv);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) e[j] = expf(sv[j] - zl[j]);
-          }
-          in[r] = S::f32_to_quad(e);
-        }
-        S::transpose4(in, tr);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<quad*>(&sm.et[(4 * cq + j) * LDT + 4 * tq]) = tr[j];
-        if (tid < 64) {
-          const float zc = a.zc[zrow + tid];
-          const float zp = (c == 0) ? -INFINITY : a.zc[zrow - H * M + tid];
-          sm.r[tid] = (c == 0) ? 0.f : expf(zp - zc);
-        }
-      }
-      __syncthreads();
-
-      // pre-chunk state (storage dtype)
-      uint16_t* hp = static_cast<uint16_t*>(is_k ? a.hk : a.hv);
-      const int64_t hbase = (static_cast<int64_t>(b) * a.NC + c) * H + h;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * wave + 4 * g4 + r, col = 16 * ct + c16;
-          int64_t off;
-          if (is_k) off = (hbase * a.K + x0 + row) * M + col;           // Hk[k][m]
-          else off = (hbase * M + row) * a.V + x0 + col;                 // Hv[m][v]
-          hp[off] = f32_to_bf16(acc[ct][r]);
-        }
-      }
-
-      // S <- S * r + contribution
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float rr = is_k ? sm.r[16 * ct + c16] : sm.r[16 * wave + 4 * g4 + r];
-          acc[ct][r] *= rr;
-        }
-      }
-      // Hk: A = X^T rows (k), B = E^T rows (m).  Hv: A = E^T rows (m), B = X^T rows (v).
-      const uint16_t* arows = is_k ? sm.xt : sm.et;
-      const uint16_t* brows = is_k ? sm.et : sm.xt;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const uint16_t* ar = &arows[(16 * wave + c16) * LDT + 32 * s + 4 * g4];
-        const frag fa = S::frag_from_quads(*reinterpret_cast<const quad*>(ar), *reinterpret_cast<const quad*>(ar + 16));
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const uint16_t* br = &brows[(16 * ct + c16) * LDT + 32 * s + 4 * g4];
-          S::mma(acc[ct], fa, S::frag_from_quads(*reinterpret_cast<const quad*>(br), *reinterpret_cast<const quad*>(br + 16)));
-        }
-      }
+      for (int i = 0; i < XB / 16; ++i) st.x[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, x.vo_x[i], 0, 0);
+    } else {
+      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rx, x.vo_x[0], 0, 0);
+      st.x[0] = u32x4_t{v.x, v.y, 0u, 0u};
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) st.e[i] = __builtin_amdgcn_raw_buffer_load_b128(re, x.vo_e[i], 0, 0);
+    st.z = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * (threadIdx.x & 63), 0, 0));
+  }
 
-    float* fp = is_k ? a.hk_final : a.hv_final;
-    if (fp == nullptr) return;
-    const int64_t fbase = static_cast<int64_t>(b) * H + h;
+  // Chunk c, first half: stage -> LDS as loaded (rows past the chunk's end
+  // read as zero); the first wave publishes r of chunk c+1 (zc of c+1 in `nxt`).
+  __device__ static __forceinline__ void stage_in(const Stage& st, const Stage& nxt, const Ctx& x, int c, Smem& sm) {
+    const AbcArgs& a = *x.a;
+    const int tid = threadIdx.x;
+    char* xb = sm.x[c & 1];
+    char* eb = sm.e[c & 1];
+    if constexpr (XB >= 16) {
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+      for (int i = 0; i < XB / 16; ++i) *reinterpret_cast<u32x4_t*>(xb + x.lo_x[i]) = st.x[i];
+    } else {
+      *reinterpret_cast<u32x2_t*>(xb + x.lo_x[0]) = u32x2_t{st.x[0].x, st.x[0].y};
+    }
+    const int row = tid >> 3, cv = tid & 7;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * wave + 4 * g4 + r, col = 16 * ct + c16;
-        if (is_k) fp[(fbase * a.K + x0 + row) * M + col] = acc[ct][r];
-        else fp[(fbase * M + row) * a.V + x0 + col] = acc[ct][r];
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4_t*>(eb + (row + 32 * i) * STE + 16 * cv) = st.e[i];
+    if (tid < 64) sm.r[(c + 1) % 3][tid] = (c + 1 < a.NC) ? exp_fast(st.z - nxt.z) : 1.f;  // past the end: r = 1
+  }
+
+  // The staged state of chunk c (written before the last barrier) goes out in
+  // whole rows: the Hk slab is contiguous, Hv rows are XW columns long.
+  // Chunks outside [0, NC) write an empty range.
+  __device__ static __forceinline__ void write_out(const Ctx& x, int c, const Smem& sm) {
+    const AbcArgs& a = *x.a;
+    const int64_t H = a.H, M = a.M;
+    const bool live = c >= 0 && c < a.NC;
+    const int64_t cc = live ? c : 0;
+    const int64_t plane = static_cast<int64_t>(x.b * a.NC + cc) * H + x.h;
+    uint16_t* hp = static_cast<uint16_t*>(IS_K ? a.hk : a.hv) +
+                   (IS_K ? (plane * a.K + x.x0) * M : plane * M * a.V + x.x0);
+    const uint32_t slab = IS_K ? static_cast<uint32_t>(XW * M * 2) : static_cast<uint32_t>(((M - 1) * a.V + XW) * 2);
+    const rsrc_t rh = make_rsrc(hp, live ? slab : 0u);
+    const char* hs = sm.hs[c & 1];
+    if constexpr (XB >= 16) {
+#pragma unroll
+      for (int i = 0; i < XB / 16; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t*>(hs + x.lo_o[i]), rh, x.vo_o[i], 0, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b64(*reinterpret_cast<const u32x2_t*>(hs + x.lo_o[0]), rh, x.vo_o[0], 0, 0);
+    }
+  }
+
+  // Chunk c, second half: stage the pre-chunk state, scale, add K^T E or E^T V.
+  __device__ static __forceinline__ void accumulate(f32x4_t (&acc)[NR], const Ctx& x, int c, Smem& sm) {
+    const AbcArgs& a = *x.a;
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t H = a.H, M = a.M;
+#pragma unroll
+    for (int j = 0; j < NR; ++j)
+      *reinterpret_cast<u32x2_t*>(sm.hs[c & 1] + x.lo_h[j]) =
+          u32x2_t{pack_bf16x2(acc[j][0], acc[j][1]), pack_bf16x2(acc[j][2], acc[j][3])};
+    const float* rr = sm.r[c % 3];
+    // Hk^T: wave w owns slot block w, tiles j = k blocks.  Hv^T: wave w owns
+    // v block w % NR, tiles j = slot blocks (w / NR) * NR + j.
+    const int rt = IS_K ? wave : wave % NR;
+    const int ct0 = IS_K ? 0 : (wave / NR) * NR;
+    if (IS_K) {  // Hk^T rows are slots
+      const f32x4_t r4 = *reinterpret_cast<const f32x4_t*>(rr + 16 * wave + 4 * g4);
+#pragma unroll
+      for (int j = 0; j < NR; ++j) acc[j] *= r4;
+    } else {     // Hv^T columns are slots
+#pragma unroll
+      for (int j = 0; j < NR; ++j) acc[j] *= rr[16 * (ct0 + j) + c16];
+    }
+    // A rows: Hk^T -> slots (E), Hv^T -> v (x); B columns: Hk^T -> k (x), Hv^T -> slots (E)
+    const char* xt = sm.x[c & 1];
+    const char* et = sm.e[c & 1];
+    const int lbx = (4 * g4 + (c16 >> 2)) * STX + (c16 & 3) * 8;
+    const int lbe = (4 * g4 + (c16 >> 2)) * STE + (c16 & 3) * 8;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const frag fa = IS_K ? S::frag_from_quads(lds_tr16(et, lbe + 32 * s * STE + 32 * rt),
+                                                lds_tr16(et, lbe + (32 * s + 16) * STE + 32 * rt))
+                           : S::frag_from_quads(lds_tr16(xt, lbx + 32 * s * STX + 32 * rt),
+                                                lds_tr16(xt, lbx + (32 * s + 16) * STX + 32 * rt));
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        const frag fb = IS_K ? S::frag_from_quads(lds_tr16(xt, lbx + 32 * s * STX + 32 * j),
+                                                  lds_tr16(xt, lbx + (32 * s + 16) * STX + 32 * j))
+                             : S::frag_from_quads(lds_tr16(et, lbe + 32 * s * STE + 32 * (ct0 + j)),
+                                                  lds_tr16(et, lbe + (32 * s + 16) * STE + 32 * (ct0 + j)));
+        S::mma(acc[j], fa, fb);
       }
     }
   }
+
+  __device__ static void run(const AbcArgs& a, Smem& sm, int b, int h, int x0) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    Ctx x;
+    x.a = &a;
+    x.b = b;
+    x.h = h;
+    x.x0 = x0;
+    x.X = IS_K ? a.K : a.V;
+    if constexpr (XB >= 16) {
+#pragma unroll
+      for (int i = 0; i < XB / 16; ++i) {
+        const int v = tid + 256 * i;
+        const int row = v / (XW / 8), cv = v % (XW / 8);
+        x.vo_x[i] = (row * a.H * x.X + 8 * cv) * 2;
+        x.lo_x[i] = row * STX + 16 * cv;
+      }
+    } else {
+      const int row = tid >> 2, cv = tid & 3;
+      x.vo_x[0] = (row * a.H * x.X + 4 * cv) * 2;
+      x.lo_x[0] = row * STX + 8 * cv;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = (tid >> 3) + 32 * i;
+      x.vo_e[i] = (row * a.H * a.M + 8 * (tid & 7)) * 2;
+    }
+    const int rt = IS_K ? wave : wave % NR;
+    const int ct0 = IS_K ? 0 : (wave / NR) * NR;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      // element (row, col) of the transposed tile held by this lane: rows 4 g4 + r, column c16
+      x.vo_h[j] = IS_K ? ((16 * j + c16) * a.M + 16 * rt + 4 * g4) * 2
+                       : ((16 * (ct0 + j) + c16) * a.V + 16 * rt + 4 * g4) * 2;
+      x.lo_h[j] = IS_K ? (16 * j + c16) * STH + (16 * rt + 4 * g4) * 2
+                       : (16 * (ct0 + j) + c16) * STH + (16 * rt + 4 * g4) * 2;
+    }
+    {
+      // write-out: thread tid moves bytes [tid XB, tid XB + XB) of the slab's rows
+      constexpr int RB = IS_K ? 64 * 2 : XW * 2;  // bytes per staged row
+      constexpr int NV = XB >= 16 ? XB / 16 : 1;
+      constexpr int VB = XB >= 16 ? 16 : 8;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int byte = (tid + 256 * i) * VB;
+        const int row = byte / RB, off = byte % RB;
+        x.lo_o[i] = row * STH + off;
+        x.vo_o[i] = IS_K ? row * a.M * 2 + off : row * a.V * 2 + off;
+      }
+    }
+    f32x4_t acc[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int NC = a.NC;
+    if (NC > 0) {
+      Stage st[D];
+#pragma unroll
+      for (int i = 0; i < D; ++i) load(st[i], x, i);
+      if (tid < 64) sm.r[0][tid] = 0.f;
+      __syncthreads();
+      const int ncp = (NC + D - 1) / D * D;
+      for (int c0 = 0; c0 < ncp; c0 += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+          const int c = c0 + i;
+          stage_in(st[i], st[(i + 1) % D], x, c, sm);
+          load(st[i], x, c + D);
+          __syncthreads();
+          write_out(x, c - 1, sm);
+          accumulate(acc, x, c, sm);
+        }
+      }
+      __syncthreads();
+      write_out(x, ncp - 1, sm);
+    }
+
+    float* fp = IS_K ? a.hk_final : a.hv_final;
+    if (fp == nullptr) return;
+    const int64_t fb = static_cast<int64_t>(b) * a.H + h;
+    float* base = fp + (IS_K ? (fb * a.K + x0) * a.M : fb * a.M * a.V + x0);
+#pragma unroll
+    for (int j = 0; j < NR; ++j) *reinterpret_cast<f32x4_t*>(base + x.vo_h[j] / 2) = acc[j];
+  }
 };
 
+template <int XW>
 __global__ __launch_bounds__(256) void abc_states(const AbcArgs a) {
-  __shared__ __align__(16) AbcStates::Smem sm;
-  AbcStates::run(a, sm);
+  using SK = AbcStates<true, XW>;
+  using SV = AbcStates<false, XW>;
+  static_assert(sizeof(typename SK::Smem) == sizeof(typename SV::Smem), "one LDS layout");
+  __shared__ __align__(16) typename SK::Smem sm;
+  const int nk = a.K / XW, tiles = nk + a.V / XW;
+  // tiles of one (b, h) share blockIdx modulo 8 (one XCD, so E comes from its L2)
+  const int bx = blockIdx.x;
+  const int xcd = bx & 7, slot = bx >> 3;
+  const int pair = 8 * (slot / tiles) + xcd;
+  const int tile = slot % tiles;
+  if (pair >= a.B * a.H) return;
+  if (tile < nk) {
+    SK::run(a, sm, pair / a.H, pair % a.H, XW * tile);
+  } else {
+    SV::run(a, *reinterpret_cast<typename SV::Smem*>(&sm), pair / a.H, pair % a.H, XW * (tile - nk));
+  }
 }
 
-hipError_t launch_abc_z(const AbcArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(abc_chunk_lse, dim3(a.B * a.NC * a.H), dim3(64), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(abc_carry, dim3(a.B * a.H), dim3(64), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess || a.z == nullptr || a.NC < 2) return e;
-  hipLaunchKernelGGL(abc_fix_z, dim3(a.B * (a.NC - 1) * a.H), dim3(256), 0, stream, a);
-  return hipGetLastError();
+// Tile width: the widest that gives at least half as many workgroups as
+// CUs, else 16 (B=2, H=4, K=256, V=512 on MI355X: 64 -> 258 us, 32 -> 178 us,
+// 16 -> 216 us).  GDR_ABC_XW forces a width (16, 32 or 64).
+int abc_tile_width(const AbcArgs& a) {
+  if (const char* env = getenv("GDR_ABC_XW")) {
+    const int w = atoi(env);
+    if (w == 16 || w == 32 || w == 64) return w;
+  }
+  const int64_t pairs = static_cast<int64_t>(a.B) * a.H;
+  for (int w = 64; w > 16; w /= 2)
+    if (pairs * ((a.K + a.V) / w) >= 128) return w;
+  return 16;
 }
 
-hipError_t launch_abc_scan(const AbcArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(abc_states, dim3(a.B * a.H * (a.K / 64 + a.V / 64)), dim3(256), 0, stream, a);
+hipError_t launch_abc(const AbcArgs& a, hipStream_t stream) {
+  if (a.NC > 0) {
+    hipLaunchKernelGGL(abc_chunk_lse, dim3(a.B * a.NC * a.H), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.NC > 0) {
+    hipLaunchKernelGGL(abc_carry, dim3(a.B * a.H), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.NC > 0) {
+    hipLaunchKernelGGL(abc_weights, dim3(a.B * a.NC * a.H), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int xw = abc_tile_width(a);
+  const int tiles_w = (a.K + a.V) / xw;
+  const dim3 grid(8 * tiles_w * ((a.B * a.H + 7) / 8));
+  if (xw == 64) hipLaunchKernelGGL(abc_states<64>, grid, dim3(256), 0, stream, a);
+  else if (xw == 32) hipLaunchKernelGGL(abc_states<32>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(abc_states<16>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -55,7 +55,9 @@ size_t abc_workspace_size(const abc_problem* p) {
   std::string err;
   if (!abc_valid(p, err)) return 0;
   const int64_t nc = (p->T + 63) / 64;
-  return static_cast<size_t>(p->B) * nc * p->H * p->M * sizeof(float);
+  // chunk log-sum-exps and chunk-end normalisers (FP32), then the weights E (storage dtype)
+  return 2 * static_cast<size_t>(p->B) * nc * p->H * p->M * sizeof(float) +
+         static_cast<size_t>(p->B) * p->T * p->H * p->M * 2;
 }
 
 gdr_status abc_affine_scan(const abc_problem* p, const void* k, const void* v, const void* s, float* z, void* hk,
@@ -91,7 +93,7 @@ gdr_status abc_affine_scan(const abc_problem* p, const void* k, const void* v, c
   a.v = v;
   a.s = s;
   a.z = z;
-  a.zc = static_cast<float*>(workspace);
+  a.lse = static_cast<float*>(workspace);
   a.hk = hk;
   a.hv = hv;
   a.hk_final = hk_final;
@@ -103,10 +105,10 @@ gdr_status abc_affine_scan(const abc_problem* p, const void* k, const void* v, c
   a.M = p->M;
   a.V = p->V;
   a.NC = static_cast<int32_t>((p->T + 63) / 64);
+  a.zc = a.lse + static_cast<int64_t>(a.B) * a.NC * a.H * a.M;
+  a.e = a.zc + static_cast<int64_t>(a.B) * a.NC * a.H * a.M;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-  if (a.NC > 0) e = gdr::launch_abc_z(a, st);
-  if (e == hipSuccess) e = gdr::launch_abc_scan(a, st);
+  hipError_t e = gdr::launch_abc(a, st);
   if (e != hipSuccess) {
     gdr_internal::set_last_error(std::string("abc launch: ") + hipGetErrorString(e));
     return GDR_ERR_HIP;

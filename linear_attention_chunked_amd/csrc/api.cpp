@@ -271,7 +271,8 @@ gdr_status gdr_segment_compose(const gdr_problem* p, int32_t n_segments, const f
   a.P = n_segments;
   a.N = pr.N;
   a.state_vk = pr.state_vk;
-  const int grid = pr.N * pr.H * (pr.DV / 16);
+  // XCD-major order: the column blocks of one (sequence, head) share blockIdx modulo 8
+  const int grid = 8 * (pr.DV / 16) * ((pr.N * pr.H + 7) / 8);
   hipError_t e = fn(&a, grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "compose launch");
   return GDR_OK;

@@ -9,10 +9,16 @@
 // state in FP32 accumulator registers and produces its rows of the next one
 // with FP32 MFMA (v_mfma_f32_16x16x4_f32, one independent accumulator per
 // 32-wide k-step so the products overlap): the A operand is its 16 rows of M_s,
-// read straight from HBM, the B operand the whole current state, shared
-// through LDS (double-buffered, one barrier per segment).  The next segment's
-// rows of M and of S_loc are fetched while the current product runs, and
-// S_init(s) is written straight from the accumulators.
+// read straight from global memory, the B operand the whole current state,
+// shared through LDS (double-buffered, one barrier per segment).
+//
+// The chain is latency-bound (a few dozen workgroups, one product per
+// segment), so the operands of segment s+2 are requested while segment s
+// computes: three register sets rotate through an unrolled loop, and each
+// set's loads are issued ahead of the state stores so that waiting for them
+// never waits for a store.  The workgroups of one (sequence, head) share an
+// XCD (blockIdx modulo 8), so M_s and S_loc(s) come from HBM once per XCD and
+// from that XCD's L2 for the other column blocks.
 #include "kernels.hpp"
 
 namespace gdr {
@@ -30,101 +36,113 @@ struct ComposeKernel {
     float s[2][BVC * LDS_];
   };
 
-  __device__ static void load_m(frag (&am)[KS], const float* mb, int wave, int g4, int c16) {
-    const float* mr = mb + static_cast<int64_t>(16 * wave + c16) * DK;
+  struct Ops {
+    frag m[KS];  // this lane's part of the wave's 16 rows of M_s
+    f32x4_t l;   // this lane's four rows of S_loc(s) in its column
+  };
+
+  struct Ctx {
+    const ComposeArgs* a;
+    int64_t n, hd, H;
+    int col, row0, wave, g4, c16;
+  };
+
+  __device__ static __forceinline__ void load(Ops& o, const Ctx& x, int s) {
+    const ComposeArgs& a = *x.a;
+    const int64_t seg = x.n * a.P + s;
+    const float* mr = a.seg_trans + (seg * x.H + x.hd) * DK * DK + static_cast<int64_t>(16 * x.wave + x.c16) * DK;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(mr + 32 * ks + 4 * g4);
-      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(mr + 32 * ks + 16 + 4 * g4);
-      am[ks] = S::frag_from_f32(x0, x1);
+      const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(mr + 32 * ks + 4 * x.g4);
+      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(mr + 32 * ks + 16 + 4 * x.g4);
+      o.m[ks] = S::frag_from_f32(x0, x1);
     }
+    o.l = *reinterpret_cast<const f32x4_t*>(a.seg_state + (seg * x.H + x.hd) * a.DV * DK +
+                                            static_cast<int64_t>(x.col) * DK + x.row0);
+  }
+
+  // Segment s: operands in `cur_ops`, requests segment s+2 into `next2`.
+  __device__ static __forceinline__ void step(f32x4_t& cur, const Ops& ops, Ops& next2, const Ctx& x, int s,
+                                              Smem& sm) {
+    const ComposeArgs& a = *x.a;
+    if (s + 2 < a.P) load(next2, x, s + 2);
+    const int64_t seg = x.n * a.P + s;
+    *reinterpret_cast<f32x4_t*>(a.seg_init + (seg * x.H + x.hd) * a.DV * DK + static_cast<int64_t>(x.col) * DK +
+                                x.row0) = cur;
+    const float* sb = &sm.s[s & 1][x.c16 * LDS_ + 4 * x.g4];
+    frag bs[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      bs[ks] = S::frag_from_f32(*reinterpret_cast<const f32x4_t*>(sb + 32 * ks),
+                                *reinterpret_cast<const f32x4_t*>(sb + 32 * ks + 16));
+    f32x4_t part[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) part[ks] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        part[ks] = __builtin_amdgcn_mfma_f32_16x16x4f32(ops.m[ks].v[e], bs[ks].v[e], part[ks], 0, 0, 0);
+    f32x4_t acc = ops.l;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc += part[ks];
+    cur = acc;
+    *reinterpret_cast<f32x4_t*>(&sm.s[(s + 1) & 1][x.c16 * LDS_ + x.row0]) = cur;
+    __syncthreads();
   }
 
   __device__ static void run(const ComposeArgs& a, Smem& sm) {
     const int tid = threadIdx.x;
-    const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int NVB = a.DV / BVC;
-    const int vb = blockIdx.x % NVB;
-    const int rest = blockIdx.x / NVB;
-    const int hd = rest % a.H;
-    const int n = rest / a.H;
-    if (n >= a.N) return;
-    const int64_t H = a.H;
+    const int bx = blockIdx.x;
+    const int xcd = bx & 7, slot = bx >> 3;
+    const int pair = 8 * (slot / NVB) + xcd;
+    const int vb = slot % NVB;
+    if (pair >= a.N * a.H) return;
+    Ctx x;
+    x.a = &a;
+    x.n = pair / a.H;
+    x.hd = pair % a.H;
+    x.H = a.H;
+    x.g4 = lane >> 4;
+    x.c16 = lane & 15;
+    x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    x.col = vb * BVC + x.c16;           // this lane's value column
+    x.row0 = 16 * x.wave + 4 * x.g4;    // this lane's four state rows
     const int DV = a.DV;
-    const int col = vb * BVC + c16;           // this lane's value column
-    const int row0 = 16 * wave + 4 * g4;      // this lane's four state rows
     const int P = a.P;
 
     // S_init(0) rows of this wave (C layout)
     f32x4_t cur{0.f, 0.f, 0.f, 0.f};
     if (a.h0 != nullptr) {
-      const float* hb = a.h0 + (static_cast<int64_t>(n) * H + hd) * DV * DK;
+      const float* hb = a.h0 + (x.n * x.H + x.hd) * DV * DK;
       if (a.state_vk) {
-        cur = *reinterpret_cast<const f32x4_t*>(hb + static_cast<int64_t>(col) * DK + row0);
+        cur = *reinterpret_cast<const f32x4_t*>(hb + static_cast<int64_t>(x.col) * DK + x.row0);
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) cur[r] = hb[static_cast<int64_t>(row0 + r) * DV + col];
+        for (int r = 0; r < 4; ++r) cur[r] = hb[static_cast<int64_t>(x.row0 + r) * DV + x.col];
       }
     }
-    *reinterpret_cast<f32x4_t*>(&sm.s[0][c16 * LDS_ + row0]) = cur;
-    frag am[KS];
-    f32x4_t sl{0.f, 0.f, 0.f, 0.f};
-    if (P > 0) {
-      const int64_t seg = static_cast<int64_t>(n) * P;
-      load_m(am, a.seg_trans + (seg * H + hd) * DK * DK, wave, g4, c16);
-      sl = *reinterpret_cast<const f32x4_t*>(a.seg_state + (seg * H + hd) * DV * DK + static_cast<int64_t>(col) * DK + row0);
-    }
+    *reinterpret_cast<f32x4_t*>(&sm.s[0][x.c16 * LDS_ + x.row0]) = cur;
+    Ops A, B, C;
+    if (P > 0) load(A, x, 0);
+    if (P > 1) load(B, x, 1);
     __syncthreads();
-
-    for (int s = 0; s < P; ++s) {
-      const int64_t seg = static_cast<int64_t>(n) * P + s;
-      // emit S_init(s)
-      *reinterpret_cast<f32x4_t*>(a.seg_init + (seg * H + hd) * DV * DK + static_cast<int64_t>(col) * DK + row0) = cur;
-      // B operand: the whole S_init(s) from LDS
-      const float* sb = &sm.s[s & 1][c16 * LDS_ + 4 * g4];
-      frag bs[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        bs[ks] = S::frag_from_f32(*reinterpret_cast<const f32x4_t*>(sb + 32 * ks),
-                                  *reinterpret_cast<const f32x4_t*>(sb + 32 * ks + 16));
-      // next segment's operands in flight during the product
-      frag an[KS];
-      f32x4_t sn{0.f, 0.f, 0.f, 0.f};
-      const bool more = (s + 1 < P);
-      if (more) {
-        load_m(an, a.seg_trans + ((seg + 1) * H + hd) * DK * DK, wave, g4, c16);
-        sn = *reinterpret_cast<const f32x4_t*>(a.seg_state + ((seg + 1) * H + hd) * DV * DK +
-                                               static_cast<int64_t>(col) * DK + row0);
-      }
-      // independent accumulators per 32-wide k-step break the MFMA dependency chain
-      f32x4_t part[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) part[ks] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          part[ks] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[ks].v[e], bs[ks].v[e], part[ks], 0, 0, 0);
-      f32x4_t acc = sl;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc += part[ks];
-      cur = acc;
-      *reinterpret_cast<f32x4_t*>(&sm.s[(s + 1) & 1][c16 * LDS_ + row0]) = cur;
-      if (more) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) am[ks] = an[ks];
-        sl = sn;
-      }
-      __syncthreads();
+    for (int s = 0; s < P; s += 3) {
+      step(cur, A, C, x, s, sm);
+      if (s + 1 >= P) break;
+      step(cur, B, A, x, s + 1, sm);
+      if (s + 2 >= P) break;
+      step(cur, C, B, x, s + 2, sm);
     }
     if (a.hT != nullptr) {
-      float* hb = a.hT + (static_cast<int64_t>(n) * H + hd) * DV * DK;
+      float* hb = a.hT + (x.n * x.H + x.hd) * DV * DK;
       if (a.state_vk) {
-        *reinterpret_cast<f32x4_t*>(hb + static_cast<int64_t>(col) * DK + row0) = cur;
+        *reinterpret_cast<f32x4_t*>(hb + static_cast<int64_t>(x.col) * DK + x.row0) = cur;
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hb[static_cast<int64_t>(row0 + r) * DV + col] = cur[r];
+        for (int r = 0; r < 4; ++r) hb[static_cast<int64_t>(x.row0 + r) * DV + x.col] = cur[r];
       }
     }
   }

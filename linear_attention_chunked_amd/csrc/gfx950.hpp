@@ -1,0 +1,33 @@
+// Small gfx950 device helpers shared by the bfloat16 kernels.
+#pragma once
+
+#include "common.hpp"
+
+namespace gdr {
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zero and stores past the end are dropped by the hardware range check.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, static_cast<int>(bytes), 0x00020000);
+}
+
+// e^x on the hardware base-2 exponential.
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j names 8 bytes
+// (four bf16 of a row-major 4 x 16 block) and lane i receives column i of
+// that block, i.e. four consecutive rows of one column.
+__device__ __forceinline__ u32x2_t lds_tr16(const char* base, int byte_off) {
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + byte_off));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+__device__ __forceinline__ u32x2_t lds_b64(const char* base, int byte_off) {
+  return *reinterpret_cast<const u32x2_t*>(base + byte_off);
+}
+
+}  // namespace gdr

@@ -68,7 +68,9 @@ struct AbcArgs {
   const void* v;
   const void* s;
   float* z;            // nullable full normaliser
+  float* lse;          // workspace: [B, NC, H, M] log-sum-exp of each chunk
   float* zc;           // workspace: [B, NC, H, M] normaliser at chunk ends
+  void* e;             // workspace: [B, T, H, M] weights exp(s - zc), storage dtype
   void* hk;
   void* hv;
   float* hk_final;
@@ -89,7 +91,6 @@ LaunchFn find_prepare2(int dk, int dv);
 LaunchFn find_output(int dtype, int dk, int dv);
 LaunchFn find_output2(int dk, int dv);
 LaunchFn find_compose(int dk);
-hipError_t launch_abc_z(const AbcArgs& a, hipStream_t s);
-hipError_t launch_abc_scan(const AbcArgs& a, hipStream_t s);
+hipError_t launch_abc(const AbcArgs& a, hipStream_t s);
 
 }  // namespace gdr

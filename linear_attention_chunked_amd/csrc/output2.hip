@@ -9,25 +9,10 @@
 // P^T = K Q^T is formed in accumulator layout, which (with the k(g, e) map of
 // common.hpp) is already the A operand of P v_new; v_new's operand, whose
 // contraction runs over tokens, comes from ds_read_b64_tr_b16.
+#include "gfx950.hpp"
 #include "kernels.hpp"
 
 namespace gdr {
-
-namespace {
-
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc3(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, static_cast<int>(bytes), 0x00020000);
-}
-__device__ __forceinline__ u32x2_t tr16o(const char* base, int off) {
-  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + off)));
-}
-__device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
-
-}  // namespace
 
 template <int DK, int DV>
 struct Output2 {
@@ -82,10 +67,10 @@ struct Output2 {
                            ((static_cast<int64_t>(a.chunk_base) + chunk) * H + hd) * DV * DK +
                            static_cast<int64_t>(col0) * DK;
       const uint32_t qk_bytes = static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2);
-      const rsrc_t rq = make_rsrc3(qp, qk_bytes);
-      const rsrc_t rk = make_rsrc3(kp, qk_bytes);
-      const rsrc_t rv = make_rsrc3(vp, static_cast<uint32_t>(((nvalid - 1) * H * DV + BVO) * 2));
-      const rsrc_t rh = make_rsrc3(hp, static_cast<uint32_t>(BVO * DK * 2));
+      const rsrc_t rq = make_rsrc(qp, qk_bytes);
+      const rsrc_t rk = make_rsrc(kp, qk_bytes);
+      const rsrc_t rv = make_rsrc(vp, static_cast<uint32_t>(((nvalid - 1) * H * DV + BVO) * 2));
+      const rsrc_t rh = make_rsrc(hp, static_cast<uint32_t>(BVO * DK * 2));
       constexpr int CQ = DK / 8, CV = BVO / 8;
 #pragma unroll
       for (int i = 0; i < kChunk * CQ / NT; ++i) {
@@ -137,13 +122,13 @@ struct Output2 {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * it + 4 * g4 + r;
-        pt[it][r] = (i <= t && t < nvalid) ? pt[it][r] * exp_f(gt - gi[r]) : 0.f;
+        pt[it][r] = (i <= t && t < nvalid) ? pt[it][r] * exp_fast(gt - gi[r]) : 0.f;
       }
     }
     const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(&sm.gam[16 * wave + 4 * g4]);
     f32x4_t eg;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) eg[r] = exp_f(gr[r]);
+    for (int r = 0; r < 4; ++r) eg[r] = exp_fast(gr[r]);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[ct] *= eg;
 
@@ -155,13 +140,13 @@ struct Output2 {
         const frag fa = S::frag_from_f32(pt[2 * s], pt[2 * s + 1]);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
-          S::mma(acc[ct], fa, S::frag_from_quads(tr16o(vb_, 32 * s * SV + 32 * ct), tr16o(vb_, (32 * s + 16) * SV + 32 * ct)));
+          S::mma(acc[ct], fa, S::frag_from_quads(lds_tr16(vb_, 32 * s * SV + 32 * ct), lds_tr16(vb_, (32 * s + 16) * SV + 32 * ct)));
       }
     }
 
     // ---- store o (rows past the tail dropped by the range check) ----
     uint16_t* op = static_cast<uint16_t*>(a.o) + (tok0 * H + hd) * DV + col0;
-    const rsrc_t ro = make_rsrc3(op, static_cast<uint32_t>(((nvalid - 1) * H * DV + BVO) * 2));
+    const rsrc_t ro = make_rsrc(op, static_cast<uint32_t>(((nvalid - 1) * H * DV + BVO) * 2));
     const int rs = static_cast<int>(H * DV * 2);
     const int voff = (16 * wave + 4 * g4) * rs + c16 * 2;
 #pragma unroll

@@ -117,7 +117,11 @@ bool choose_tile(const Problem& p, const int32_t* req, int mode, int64_t rows, T
     // a quarter of a 64-column unit, 64-column blocks of 4 waves with one LDS
     // buffer (several workgroups per CU) win; with very few pairs (one long
     // sequence, a handful of heads) 32-column blocks of 2 waves give more
-    // units and a shorter chain per chunk.
+    // units and a shorter chain per chunk.  The summary pass reads no U for
+    // its transition columns and stores no per-chunk state, so once 128-column
+    // blocks alone fill the 256 CUs, the wider block (K and W read by half as
+    // many workgroups) wins there (16 segments x 8 heads: 144 us against
+    // 174 us for 64-column blocks).
     const int64_t pairs = rows * p.H;
     const int64_t units64 = pairs * ((mode == 1 ? p.DV + p.DK : p.DV) / 64);
     if (p.dtype == 1) {
@@ -128,6 +132,10 @@ bool choose_tile(const Problem& p, const int32_t* req, int mode, int64_t rows, T
         r[0] = 32;
         r[1] = 2;
         r[2] = 2;
+      } else if (mode == 1 && p.DV % 128 == 0 && p.DK % 128 == 0 && units64 / 2 >= 256) {
+        r[0] = 128;
+        r[1] = 4;
+        r[2] = 3;
       }
     } else {
       r[0] = 64;

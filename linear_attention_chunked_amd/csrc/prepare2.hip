@@ -21,23 +21,12 @@
 //     no LDS round trip.
 //   * w and u from T' = T diag(.) split into bf16 hi + lo parts (one rounding:
 //     the final store).
+#include "gfx950.hpp"
 #include "kernels.hpp"
 
 namespace gdr {
 
 namespace {
-
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc2(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, static_cast<int>(bytes), 0x00020000);
-}
-__device__ __forceinline__ u32x2_t tr16(const char* base, int off) {
-  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + off)));
-}
-__device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 // D (16x16, C layout) += X (16x16) Y (16x16) in FP32 with k = 4g + r:
 // a[r] = X[c][4g + r] (row c of X), b[r] = Y[4g + r][c] (the C layout of Y).
@@ -94,8 +83,8 @@ struct Prepare2 {
     {
       const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (tok0 * H + hd) * DK;
       const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + hd) * DV;
-      const rsrc_t rk = make_rsrc2(kp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
-      const rsrc_t rv = make_rsrc2(vp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
+      const rsrc_t rk = make_rsrc(kp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
+      const rsrc_t rv = make_rsrc(vp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
       constexpr int CK = DK / 8, CV = DV / 8;  // 16-byte chunks per row
 #pragma unroll
       for (int i = 0; i < kChunk * CK / NT; ++i) {
@@ -119,7 +108,7 @@ struct Prepare2 {
         const float b = (lane < nvalid) ? a.beta[(tok0 + lane) * H + hd] : 0.f;
         sm.gam[lane] = x;
         sm.beta[lane] = b;
-        sm.bg[lane] = b * exp2f_fast(x);
+        sm.bg[lane] = b * exp_fast(x);
         if (lane < nvalid) a.g_cum[(tok0 + lane) * H + hd] = x;
       }
     }
@@ -151,7 +140,7 @@ struct Prepare2 {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * wave + 4 * g4 + r;
-          sm.a[t * LDA + i] = (i < t) ? sm.beta[t] * exp2f_fast(sm.gam[t] - gi) * acc[tj][r] : 0.f;
+          sm.a[t * LDA + i] = (i < t) ? sm.beta[t] * exp_fast(sm.gam[t] - gi) * acc[tj][r] : 0.f;
         }
       }
     }
@@ -255,8 +244,8 @@ struct Prepare2 {
     const int tr_col = 8 * (c16 & 3);
     uint16_t* wo = static_cast<uint16_t*>(a.w) + (tok0 * H + hd) * DK;
     uint16_t* uo = static_cast<uint16_t*>(a.u) + (tok0 * H + hd) * DV;
-    const rsrc_t rwo = make_rsrc2(wo, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
-    const rsrc_t ruo = make_rsrc2(uo, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
+    const rsrc_t rwo = make_rsrc(wo, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
+    const rsrc_t ruo = make_rsrc(uo, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
 #pragma unroll
     for (int dt = 0; dt < DK / 16; ++dt) {
       f32x4_t acc{0.f, 0.f, 0.f, 0.f};
@@ -264,7 +253,7 @@ struct Prepare2 {
       for (int s = 0; s < 2; ++s) {
         if (s < nsteps) {
           const char* base = sm.k + (32 * s + tr_row) * SKB + 32 * dt + tr_col;
-          const frag fa = S::frag_from_quads(tr16(base, 0), tr16(base, 16 * SKB));
+          const frag fa = S::frag_from_quads(lds_tr16(base, 0), lds_tr16(base, 16 * SKB));
           S::mma(acc, fa, bw_hi[s]);
           S::mma(acc, fa, bw_lo[s]);
         }
@@ -279,7 +268,7 @@ struct Prepare2 {
       for (int s = 0; s < 2; ++s) {
         if (s < nsteps) {
           const char* base = sm.v + (32 * s + tr_row) * SVB + 32 * dt + tr_col;
-          const frag fa = S::frag_from_quads(tr16(base, 0), tr16(base, 16 * SVB));
+          const frag fa = S::frag_from_quads(lds_tr16(base, 0), lds_tr16(base, 16 * SVB));
           S::mma(acc, fa, bu_hi[s]);
           S::mma(acc, fa, bu_lo[s]);
         }

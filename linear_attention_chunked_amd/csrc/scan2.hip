@@ -28,28 +28,10 @@
 //   * U enters the accumulator negated and the sign is folded into the decay
 //     weights, so W needs no negation: acc = -U + W S = -D, v_new = -acc,
 //     D' = acc * (-exp(g_last - g)).
+#include "gfx950.hpp"
 #include "kernels.hpp"
 
 namespace gdr {
-
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, static_cast<int>(bytes), 0x00020000);
-}
-
-__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
-
-__device__ __forceinline__ u32x2_t lds_tr16(const char* base, int byte_off) {
-  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + byte_off));
-  return __builtin_bit_cast(u32x2_t, v);
-}
-
-__device__ __forceinline__ u32x2_t lds_b64(const char* base, int byte_off) {
-  return *reinterpret_cast<const u32x2_t*>(base + byte_off);
-}
 
 template <int DK, int BV, int NW, int PF, int MODE, int NBUF>
 struct Scan2 {

@@ -86,3 +86,20 @@ def test_abc_deterministic(pkg):
     b = run(pkg, inp)
     for key in a:
         assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("T", [65, 300])
+def test_abc_tile_widths_bit_identical(pkg, monkeypatch, T):
+    """Every state element is the same sequence of FP32 operations whatever
+    the tile width (64, 32 or 16 columns per workgroup), so the outputs agree
+    bit for bit; the widest also matches the oracle."""
+    inp = make_abc(960 + T, B=1, T=T, H=2, K=128, M=64, V=192)
+    outs = {}
+    for xw in (64, 32, 16):
+        monkeypatch.setenv("GDR_ABC_XW", str(xw))
+        outs[xw] = run(pkg, inp)
+    for xw in (32, 16):
+        for key in outs[64]:
+            assert torch.equal(outs[64][key], outs[xw][key]), (xw, key)
+    d = inp.f64()
+    compare(outs[64], oracle.abc_recurrent_fp64(d["k"], d["v"], d["s"]), what=f"abc xw T={T}")
