@@ -51,10 +51,24 @@ struct Scan2 {
   static constexpr int OFF_W = 0, OFF_K = kChunk * SW, OFF_U = OFF_K + kChunk * SK;
   static constexpr int OFF_D = OFF_U + kChunk * SU;   // 64 negated decay weights, then exp(g_last)
   static constexpr int BUF = OFF_D + kChunk * 4 + 16;
+  // Output staging (single-buffer loop, plain and segmented passes): the
+  // chunk's h block and v_new tile are written to LDS in their memory layout
+  // and leave the next iteration as whole 16-byte vectors per lane (the h
+  // block of one (chunk, head, column block) is contiguous; v_new rows are BV
+  // columns), instead of 8- and 2-byte pieces straight from the MFMA layout.
+  static constexpr bool STAGE = (MODE == 0) && (NBUF == 1);
+  static constexpr int SHS = DK * 2 + 16;           // staged h rows (one value column each)
+  static constexpr int SVS = BV * 2 + 16;           // staged v_new rows (one token each)
+  static constexpr int OFF_HS = BUF;
+  static constexpr int OFF_VS = OFF_HS + BV * SHS;
+  static constexpr int SMEM = NBUF * BUF + (STAGE ? BV * SHS + kChunk * SVS : 0);
+  static constexpr int H_PT = BV * DK / 8 / NT;     // 16-byte h vectors per thread
+  static constexpr int V_PT = kChunk * BV / 8 / NT; // 16-byte v_new vectors per thread
   static constexpr int W_PT = kChunk * CPW / NT;   // 16-byte vectors per thread (W, and K)
   static constexpr int U_PT = (kChunk * CPU + NT - 1) / NT;
   static_assert(NC >= 1 && BV % (16 * NW) == 0, "each wave owns whole 16-column tiles");
   static_assert((kChunk * CPW) % NT == 0, "W/K tiles split evenly over the threads");
+  static_assert(!STAGE || ((BV * DK / 8) % NT == 0 && (kChunk * BV / 8) % NT == 0), "staged outputs split evenly");
 
   struct Stage {
     u32x4_t w[W_PT];
@@ -122,12 +136,43 @@ struct Scan2 {
     }
   }
 
+  // The staged outputs of chunk c (written before the last barrier) go to
+  // global memory: the h block as one contiguous run, v_new as whole rows
+  // (rows past the chunk's valid tokens fall outside the buffer range).
+  __device__ static __forceinline__ void write_out(const Ctx& x, const Row& row, int c, const char* so) {
+    const ScanArgs& a = *x.a;
+    const int tid = threadIdx.x;
+    const int64_t H = x.H;
+    const int DV = x.DV;
+    const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(c) * kChunk;
+    const int nvalid = min(kChunk, row.len - c * kChunk);
+    uint16_t* hp = static_cast<uint16_t*>(a.h) + ((static_cast<int64_t>(row.chunk_off) + c) * H + x.hd) * DV * DK +
+                   static_cast<int64_t>(x.col_blk) * DK;
+    const rsrc_t rh = make_rsrc(hp, a.h != nullptr ? static_cast<uint32_t>(BV * DK * 2) : 0u);
+#pragma unroll
+    for (int i = 0; i < H_PT; ++i) {
+      const int v = tid + NT * i;  // 16-byte vector of the block, row v / (DK / 8)
+      const u32x4_t q = *reinterpret_cast<const u32x4_t*>(so + (v / (DK / 8)) * SHS + (v % (DK / 8)) * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(q, rh, 16 * v, 0, 0);
+    }
+    uint16_t* vp = static_cast<uint16_t*>(a.v_new) + (tok0 * H + x.hd) * DV + x.col_blk;
+    const rsrc_t rv =
+        make_rsrc(vp, a.v_new != nullptr ? static_cast<uint32_t>(((nvalid - 1) * H * DV + BV) * 2) : 0u);
+#pragma unroll
+    for (int i = 0; i < V_PT; ++i) {
+      const int v = tid + NT * i;  // token v / (BV / 8), 8 columns
+      const int t = v / (BV / 8), p = v % (BV / 8);
+      const u32x4_t q = *reinterpret_cast<const u32x4_t*>(so + (OFF_VS - OFF_HS) + t * SVS + p * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(q, rv, static_cast<int>(t * H * DV * 2) + 16 * p, 0, 0);
+    }
+  }
+
   // One chunk.  The W operand reads are issued before the first matrix
   // instruction, the K operand reads while GEMM1 runs, and the accumulator
   // chains are interleaved, so the chunk pays the LDS and MFMA latencies about
   // once instead of once per product.
   __device__ static __forceinline__ void compute(f32x4_t (&Sacc)[DT][NC], const Ctx& x, const Row& row, int c,
-                                                 const char* buf) {
+                                                 const char* buf, char* smem_out = nullptr) {  // smem_out: staging (STAGE)
     const ScanArgs& a = *x.a;
     const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -187,7 +232,18 @@ struct Scan2 {
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) S::mma(acc[mt][ct], aw[s][mt], Sb[s][ct]);
 
-    if (MODE == 0 && a.h != nullptr) {
+    if (STAGE) {
+      // h block: value column (colw + 16 ct + c16), rows 32 s + 4 g4 (+16)
+      char* hs = smem_out + (colw + c16) * SHS + 8 * g4;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
+          const u32x4_t q = __builtin_bit_cast(u32x4_t, Sb[s][ct].v);
+          *reinterpret_cast<u32x2_t*>(hs + 16 * ct * SHS + 64 * s) = u32x2_t{q.x, q.y};
+          *reinterpret_cast<u32x2_t*>(hs + 16 * ct * SHS + 64 * s + 32) = u32x2_t{q.z, q.w};
+        }
+    } else if (MODE == 0 && a.h != nullptr) {
       uint16_t* hp = static_cast<uint16_t*>(a.h) +
                      ((static_cast<int64_t>(row.chunk_off) + c) * H + x.hd) * DV * DK +
                      static_cast<int64_t>(x.col_blk + colw) * DK;
@@ -217,7 +273,20 @@ struct Scan2 {
     const float eg = reinterpret_cast<const float*>(buf + OFF_D)[kChunk];
 
     // ---- v_new = -acc (tail rows dropped by the range check); D' = acc * nd ----
-    if (MODE == 0 && a.v_new != nullptr) {
+    if (STAGE) {
+      // v_new tile: token 16 mt + 4 g4 + r, column colw + 16 ct + c16
+      uint16_t* vs = reinterpret_cast<uint16_t*>(smem_out + (OFF_VS - OFF_HS)) + (4 * g4) * (SVS / 2) + colw + c16;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; r += 2) {
+            const uint32_t pk = pack_bf16x2(-acc[mt][ct][r], -acc[mt][ct][r + 1]);
+            vs[(16 * mt + r) * (SVS / 2) + 16 * ct] = static_cast<uint16_t>(pk);
+            vs[(16 * mt + r + 1) * (SVS / 2) + 16 * ct] = static_cast<uint16_t>(pk >> 16);
+          }
+    } else if (MODE == 0 && a.v_new != nullptr) {
       uint16_t* vp = static_cast<uint16_t*>(a.v_new) + (tok0 * H + x.hd) * DV + x.col_blk + colw;
       const rsrc_t rv = make_rsrc(vp, static_cast<uint32_t>(((nvalid - 1) * H * DV + BV - colw) * 2));
       const int rs = static_cast<int>(H * DV * 2);
@@ -331,13 +400,19 @@ struct Scan2 {
         // one LDS buffer: fill, compute, and refill behind a second barrier;
         // the next chunk's loads are in flight during the compute
         Stage st;
+        char* so = smem + OFF_HS;
         load(st, x, tok_of(0), nv_of(0));
         for (int c = 0; c < nchunks; ++c) {
           __syncthreads();
+          if (STAGE && c > 0) write_out(x, row, c - 1, so);
           store(st, x, buf0, nv_of(c));
           __syncthreads();
           if (c + 1 < nchunks) load(st, x, tok_of(c + 1), nv_of(c + 1));
-          compute(Sacc, x, row, c, buf0);
+          compute(Sacc, x, row, c, buf0, so);
+        }
+        if (STAGE) {
+          __syncthreads();
+          write_out(x, row, nchunks - 1, so);
         }
       } else if (PF == 1) {
         Stage st;
@@ -408,7 +483,7 @@ struct Scan2 {
 template <int DK, int BV, int NW, int PF, int MODE, int NBUF>
 __global__ __launch_bounds__(NW * 64) void scan2_kernel(const ScanArgs a) {
   using K = Scan2<DK, BV, NW, PF, MODE, NBUF>;
-  __shared__ __align__(16) char smem[NBUF * K::BUF];
+  __shared__ __align__(16) char smem[K::SMEM];
   K::run(a, smem);
 }
 
