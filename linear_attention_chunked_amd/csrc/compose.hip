@@ -65,7 +65,9 @@ struct ComposeKernel {
   __device__ static __forceinline__ void step(f32x4_t& cur, const Ops& ops, Ops& next2, const Ctx& x, int s,
                                               Smem& sm) {
     const ComposeArgs& a = *x.a;
-    if (s + 2 < a.P) load(next2, x, s + 2);
+    // unconditional (the last segment is re-read near the end), so every step
+    // issues the same loads and the compiler's wait counts stay two steps deep
+    load(next2, x, min(s + 2, a.P - 1));
     const int64_t seg = x.n * a.P + s;
     *reinterpret_cast<f32x4_t*>(a.seg_init + (seg * x.H + x.hd) * a.DV * DK + static_cast<int64_t>(x.col) * DK +
                                 x.row0) = cur;
@@ -126,8 +128,10 @@ struct ComposeKernel {
     }
     *reinterpret_cast<f32x4_t*>(&sm.s[0][x.c16 * LDS_ + x.row0]) = cur;
     Ops A, B, C;
-    if (P > 0) load(A, x, 0);
-    if (P > 1) load(B, x, 1);
+    if (P > 0) {
+      load(A, x, 0);
+      load(B, x, min(1, P - 1));
+    }
     __syncthreads();
     for (int s = 0; s < P; s += 3) {
       step(cur, A, C, x, s, sm);
