@@ -53,7 +53,7 @@ def scan_flops(lengths, H, DK, DV):
 
 def source_sha():
     h = hashlib.sha256()
-    for f in ("scan2.hip", "common.hpp", "kernels.hpp"):
+    for f in ("scan2.hip", "gfx950.hpp", "common.hpp", "kernels.hpp", "plan.cpp"):
         with open(os.path.join(ROOT, "linear_attention_chunked_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
