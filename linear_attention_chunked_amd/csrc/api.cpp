@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+#include <atomic>
 #include <string>
 #include <vector>
 
@@ -20,6 +22,20 @@ gdr_status fail(gdr_status s, const std::string& msg) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Compute units of the current device (read once per device and cached; a
+// race between threads stores the same value; 256 on MI355X).
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 gdr_status need(const void* p, const char* name) {
   if (p == nullptr) return fail(GDR_ERR_INVALID_ARG, std::string(name) + " must not be NULL");
@@ -155,7 +171,10 @@ gdr_status gdr_chunk_prepare(const gdr_problem* p, const void* k, const void* v,
     a.n_chunks = l.n_chunks;
     a.chunk_base = l.chunk_base;
     memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
-    hipError_t e = fn(&a, l.grid, static_cast<hipStream_t>(stream));
+    // the bfloat16 kernel is persistent (each workgroup prefetches its next
+    // chunk while computing the current one): two resident workgroups per CU
+    const int grid = pr.dtype == GDR_BF16 ? std::min(l.grid, 2 * cu_count()) : l.grid;
+    hipError_t e = fn(&a, grid, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prepare launch");
   }
   return GDR_OK;
@@ -220,7 +239,9 @@ gdr_status gdr_chunk_output(const gdr_problem* p, const void* q, const void* k, 
     a.n_chunks = l.n_chunks;
     a.chunk_base = l.chunk_base;
     memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
-    hipError_t e = fn(&a, l.grid, static_cast<hipStream_t>(stream));
+    // the bfloat16 kernel is persistent (next item prefetched): two resident workgroups per CU
+    const int grid = pr.dtype == GDR_BF16 ? std::min(l.grid, 2 * cu_count()) : l.grid;
+    hipError_t e = fn(&a, grid, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "output launch");
   }
   return GDR_OK;

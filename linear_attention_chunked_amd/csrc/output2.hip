@@ -42,53 +42,105 @@ struct Output2 {
     return lo;
   }
 
+  // The next item's tiles travel in registers while the current one computes.
+  static constexpr int CQ = DK / 8, CV = BVO / 8;        // 16-byte vectors per row
+  static constexpr int Q_PT = kChunk * CQ / NT;          // per thread: q, k and h rows
+  static constexpr int V_PT = kChunk * CV / NT;
+  struct Pref {
+    u32x4_t q[Q_PT], k[Q_PT], h[Q_PT], v[V_PT];
+    float g;
+  };
+
+  struct Item {
+    int hd, col0, chunk;
+    int64_t tok0;
+    int nvalid;
+  };
+
+  __device__ static Item item_of(const ChunkArgs& a, int item) {
+    constexpr int NVB = DV / BVO;
+    const int vb = item % NVB;
+    const int rest = item / NVB;
+    const int chunk = rest / a.H;
+    const Row row = a.rows[find_row(a, chunk)];
+    const int cl = chunk - row.chunk_off;
+    return Item{rest % a.H, vb * BVO, chunk, static_cast<int64_t>(row.bos) + static_cast<int64_t>(cl) * kChunk,
+                min(kChunk, row.len - cl * kChunk)};
+  }
+
+  // Items past the end get empty buffer ranges (the loads still issue and read nothing).
+  __device__ static void load(Pref& pf, const ChunkArgs& a, int item, int nitems) {
+    const int tid = threadIdx.x;
+    const bool live = item < nitems;
+    const Item it = item_of(a, live ? item : 0);
+    const int64_t H = a.H;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (it.tok0 * H + it.hd) * DK;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (it.tok0 * H + it.hd) * DK;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (it.tok0 * H + it.hd) * DV + it.col0;
+    const uint16_t* hp = static_cast<const uint16_t*>(a.h) +
+                         ((static_cast<int64_t>(a.chunk_base) + it.chunk) * H + it.hd) * DV * DK +
+                         static_cast<int64_t>(it.col0) * DK;
+    const uint32_t qk_bytes = live ? static_cast<uint32_t>(((it.nvalid - 1) * H + 1) * DK * 2) : 0u;
+    const rsrc_t rq = make_rsrc(qp, qk_bytes);
+    const rsrc_t rk = make_rsrc(kp, qk_bytes);
+    const rsrc_t rv = make_rsrc(vp, live ? static_cast<uint32_t>(((it.nvalid - 1) * H * DV + BVO) * 2) : 0u);
+    const rsrc_t rh = make_rsrc(hp, live ? static_cast<uint32_t>(BVO * DK * 2) : 0u);
+#pragma unroll
+    for (int i = 0; i < Q_PT; ++i) {
+      const int vv = tid + i * NT, r = vv / CQ, c = vv % CQ;
+      const int go = static_cast<int>(r * H * DK * 2 + c * 16);
+      pf.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, go, 0, 0);
+      pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, go, 0, 0);
+      pf.h[i] = __builtin_amdgcn_raw_buffer_load_b128(rh, static_cast<int>(r * DK * 2 + c * 16), 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < V_PT; ++i) {
+      const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
+      pf.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
+    }
+    const float* gp = a.g + it.tok0 * H + it.hd;
+    pf.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+        make_rsrc(gp, live ? static_cast<uint32_t>(((it.nvalid - 1) * H + 1) * 4) : 0u),
+        static_cast<int>((tid & 63) * H * 4), 0, 0));
+  }
+
+  // Persistent: workgroup b takes items b, b + gridDim.x, ... (item = (chunk * H + head) * (DV / 64) + block).
   __device__ static void run(const ChunkArgs& a, Smem& sm) {
+    const int nitems = a.n_chunks * a.H * (DV / BVO);
+    int item = blockIdx.x;
+    if (item >= nitems) return;
+    Pref pf;
+    load(pf, a, item, nitems);
+    for (; item < nitems; item += gridDim.x) {
+      one(a, sm, pf, item, nitems);
+      __syncthreads();  // LDS is reused by the next item
+    }
+  }
+
+  __device__ static __forceinline__ void one(const ChunkArgs& a, Smem& sm, Pref& pf, int item, int nitems) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    constexpr int NVB = DV / BVO;
-    const int vb = blockIdx.x % NVB;
-    const int rest = blockIdx.x / NVB;
-    const int hd = rest % a.H;
-    const int chunk = rest / a.H;
-    if (chunk >= a.n_chunks) return;
-    const Row row = a.rows[find_row(a, chunk)];
-    const int cl = chunk - row.chunk_off;
-    const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(cl) * kChunk;
-    const int nvalid = min(kChunk, row.len - cl * kChunk);
+    const Item it = item_of(a, item);
+    const int hd = it.hd;
+    const int64_t tok0 = it.tok0;
+    const int nvalid = it.nvalid;
     const int64_t H = a.H;
-    const int col0 = vb * BVO;
-
-    {
-      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (tok0 * H + hd) * DK;
-      const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (tok0 * H + hd) * DK;
-      const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + hd) * DV + col0;
-      const uint16_t* hp = static_cast<const uint16_t*>(a.h) +
-                           ((static_cast<int64_t>(a.chunk_base) + chunk) * H + hd) * DV * DK +
-                           static_cast<int64_t>(col0) * DK;
-      const uint32_t qk_bytes = static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2);
-      const rsrc_t rq = make_rsrc(qp, qk_bytes);
-      const rsrc_t rk = make_rsrc(kp, qk_bytes);
-      const rsrc_t rv = make_rsrc(vp, static_cast<uint32_t>(((nvalid - 1) * H * DV + BVO) * 2));
-      const rsrc_t rh = make_rsrc(hp, static_cast<uint32_t>(BVO * DK * 2));
-      constexpr int CQ = DK / 8, CV = BVO / 8;
+    const int col0 = it.col0;
 #pragma unroll
-      for (int i = 0; i < kChunk * CQ / NT; ++i) {
-        const int vv = tid + i * NT, r = vv / CQ, c = vv % CQ;
-        const int go = static_cast<int>(r * H * DK * 2 + c * 16);
-        *reinterpret_cast<u32x4_t*>(sm.q + r * SQ + c * 16) = __builtin_amdgcn_raw_buffer_load_b128(rq, go, 0, 0);
-        *reinterpret_cast<u32x4_t*>(sm.k + r * SQ + c * 16) = __builtin_amdgcn_raw_buffer_load_b128(rk, go, 0, 0);
-        *reinterpret_cast<u32x4_t*>(sm.h + r * SQ + c * 16) =
-            __builtin_amdgcn_raw_buffer_load_b128(rh, static_cast<int>(r * DK * 2 + c * 16), 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < kChunk * CV / NT; ++i) {
-        const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
-        *reinterpret_cast<u32x4_t*>(sm.v + r * SV + c * 16) =
-            __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
-      }
-      if (tid < kChunk) sm.gam[tid] = (tid < nvalid) ? a.g[(tok0 + tid) * H + hd] : 0.f;
+    for (int i = 0; i < Q_PT; ++i) {
+      const int vv = tid + i * NT, r = vv / CQ, c = vv % CQ;
+      *reinterpret_cast<u32x4_t*>(sm.q + r * SQ + c * 16) = pf.q[i];
+      *reinterpret_cast<u32x4_t*>(sm.k + r * SQ + c * 16) = pf.k[i];
+      *reinterpret_cast<u32x4_t*>(sm.h + r * SQ + c * 16) = pf.h[i];
     }
+#pragma unroll
+    for (int i = 0; i < V_PT; ++i) {
+      const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
+      *reinterpret_cast<u32x4_t*>(sm.v + r * SV + c * 16) = pf.v[i];
+    }
+    if (tid < kChunk) sm.gam[tid] = (tid < nvalid) ? pf.g : 0.f;
+    load(pf, a, item + gridDim.x, nitems);
     __syncthreads();
 
     const char* rowq = sm.q + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;  // + 16 tile SQ + 64 s (+32)

@@ -66,51 +66,110 @@ struct Prepare2 {
     return lo;
   }
 
+  // The next item's K, V rows (and g, beta for the first wave) travel in
+  // registers while the current item computes.
+  static constexpr int KV_PT = kChunk * (DK / 8) / NT;  // 16-byte K vectors per thread
+  static constexpr int VV_PT = kChunk * (DV / 8) / NT;
+  struct Pref {
+    u32x4_t k[KV_PT];
+    u32x4_t v[VV_PT];
+    float g, b;
+  };
+
+  struct Item {
+    int hd;
+    int64_t tok0;
+    int nvalid;
+  };
+
+  __device__ static Item item_of(const ChunkArgs& a, int item) {
+    const int chunk = item / a.H;
+    const Row row = a.rows[find_row(a, chunk)];
+    const int cl = chunk - row.chunk_off;
+    return Item{item % a.H, static_cast<int64_t>(row.bos) + static_cast<int64_t>(cl) * kChunk,
+                min(kChunk, row.len - cl * kChunk)};
+  }
+
+  // Items past the end get empty buffer ranges: the loads are issued all the
+  // same (so the loop's wait counts stay exact) and read nothing.
+  __device__ static void load(Pref& pf, const ChunkArgs& a, int item, int nitems) {
+    const int tid = threadIdx.x;
+    const bool live = item < nitems;
+    const Item it = item_of(a, live ? item : 0);
+    const int64_t H = a.H;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (it.tok0 * H + it.hd) * DK;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (it.tok0 * H + it.hd) * DV;
+    const rsrc_t rk = make_rsrc(kp, live ? static_cast<uint32_t>(((it.nvalid - 1) * H + 1) * DK * 2) : 0u);
+    const rsrc_t rv = make_rsrc(vp, live ? static_cast<uint32_t>(((it.nvalid - 1) * H + 1) * DV * 2) : 0u);
+    constexpr int CK = DK / 8, CV = DV / 8;  // 16-byte chunks per row
+#pragma unroll
+    for (int i = 0; i < KV_PT; ++i) {
+      const int vv = tid + i * NT, r = vv / CK, c = vv % CK;
+      pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, static_cast<int>(r * H * DK * 2 + c * 16), 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VV_PT; ++i) {
+      const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
+      pf.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
+    }
+    const float* gp = a.g + it.tok0 * H + it.hd;
+    const float* bp = a.beta + it.tok0 * H + it.hd;
+    const uint32_t gb = live ? static_cast<uint32_t>(((it.nvalid - 1) * H + 1) * 4) : 0u;
+    const int go = static_cast<int>((tid & 63) * H * 4);
+    pf.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(gp, gb), go, 0, 0));
+    pf.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(bp, gb), go, 0, 0));
+  }
+
+  // Persistent: workgroup b takes items b, b + gridDim.x, ... (item = chunk * H + head).
   __device__ static void run(const ChunkArgs& a, Smem& sm) {
+    const int nitems = a.n_chunks * a.H;
+    int item = blockIdx.x;
+    if (item >= nitems) return;
+    Pref pf;
+    load(pf, a, item, nitems);
+    for (; item < nitems; item += gridDim.x) {
+      one(a, sm, pf, item, nitems);
+      __syncthreads();  // LDS is reused by the next item
+    }
+  }
+
+  __device__ static __forceinline__ void one(const ChunkArgs& a, Smem& sm, Pref& pf, int item, int nitems) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int chunk = blockIdx.x / a.H;
-    const int hd = blockIdx.x % a.H;
-    if (chunk >= a.n_chunks) return;
-    const Row row = a.rows[find_row(a, chunk)];
-    const int cl = chunk - row.chunk_off;
-    const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(cl) * kChunk;
-    const int nvalid = min(kChunk, row.len - cl * kChunk);
+    const Item it = item_of(a, item);
+    const int hd = it.hd;
+    const int64_t tok0 = it.tok0;
+    const int nvalid = it.nvalid;
     const int64_t H = a.H;
 
-    // ---- K, V rows (zero past the tail), gamma, beta ----
+    // ---- K, V rows (zero past the tail), gamma, beta from the prefetch; the next item's loads go out ----
     {
-      const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (tok0 * H + hd) * DK;
-      const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + hd) * DV;
-      const rsrc_t rk = make_rsrc(kp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
-      const rsrc_t rv = make_rsrc(vp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
-      constexpr int CK = DK / 8, CV = DV / 8;  // 16-byte chunks per row
+      constexpr int CK = DK / 8, CV = DV / 8;
 #pragma unroll
-      for (int i = 0; i < kChunk * CK / NT; ++i) {
+      for (int i = 0; i < KV_PT; ++i) {
         const int vv = tid + i * NT, r = vv / CK, c = vv % CK;
-        *reinterpret_cast<u32x4_t*>(sm.k + r * SKB + c * 16) =
-            __builtin_amdgcn_raw_buffer_load_b128(rk, static_cast<int>(r * H * DK * 2 + c * 16), 0, 0);
+        *reinterpret_cast<u32x4_t*>(sm.k + r * SKB + c * 16) = pf.k[i];
       }
 #pragma unroll
-      for (int i = 0; i < kChunk * CV / NT; ++i) {
+      for (int i = 0; i < VV_PT; ++i) {
         const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
-        *reinterpret_cast<u32x4_t*>(sm.v + r * SVB + c * 16) =
-            __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
+        *reinterpret_cast<u32x4_t*>(sm.v + r * SVB + c * 16) = pf.v[i];
       }
       if (wave == 0) {
-        float x = (lane < nvalid) ? a.g[(tok0 + lane) * H + hd] : 0.f;
+        float x = (lane < nvalid) ? pf.g : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
           const float y = __shfl_up(x, off, 64);
           if (lane >= off) x += y;
         }
-        const float b = (lane < nvalid) ? a.beta[(tok0 + lane) * H + hd] : 0.f;
+        const float b = (lane < nvalid) ? pf.b : 0.f;
         sm.gam[lane] = x;
         sm.beta[lane] = b;
         sm.bg[lane] = b * exp_fast(x);
         if (lane < nvalid) a.g_cum[(tok0 + lane) * H + hd] = x;
       }
+      load(pf, a, item + gridDim.x, nitems);
     }
     __syncthreads();
 
