@@ -42,16 +42,23 @@ struct Prepare2 {
   using S = St<bf16_t>;
   using frag = S::frag;
   static constexpr int NT = 256;
-  static constexpr int SKB = DK * 2 + 32;   // padded row strides (bytes)
-  static constexpr int SVB = DV * 2 + 32;
+  static constexpr int SKB = DK * 2 + 16;   // padded row strides (bytes)
+  static constexpr int SVB = DV * 2 + 16;
   static constexpr int LDA = 64 + 4;        // FP32 64x64 matrices (floats)
   static constexpr int KS = DK / 32;
 
+  // A and T share one matrix: every block of T is written over the block of
+  // A in the same place once nothing reads that A block any more (T[b][b]
+  // after its own substitution, T[1][0] and T[3][2] from the wave that read
+  // their A blocks, the last four blocks after a barrier).  With it the
+  // footprint (≈ 53 KB) lets three workgroups share a CU.
   struct Smem {
     char k[kChunk * SKB];
     char v[kChunk * SVB];
-    float a[kChunk * LDA];
-    float t[kChunk * LDA];
+    union {
+      float a[kChunk * LDA];
+      float t[kChunk * LDA];
+    };
     float gam[kChunk];
     float beta[kChunk];
     float bg[kChunk];  // beta exp(gamma)
@@ -264,6 +271,7 @@ struct Prepare2 {
           mm16(y1, a_rows(sm.a, 48, 16 * k), tb);
         }
       }
+      __syncthreads();  // every wave has read A[2:4][0:2] before any T block replaces it
       f32x4_t x{0.f, 0.f, 0.f, 0.f};
       mm16(x, a_rows(sm.t, 32 + 16 * i, 32), y0);                   // T_hi[i][0] (T[2][2] or T[3][2])
       if (i == 1) mm16(x, a_rows(sm.t, 48, 48), y1);                // T_hi[1][1] = T[3][3]
