@@ -85,6 +85,17 @@ typedef struct {
                                       during the call only                        */
   gdr_dtype dtype;                 /* storage of q, k, v, w, u, v_new, o and h    */
   gdr_state_layout state_layout;   /* layout of h0 and hT                         */
+  /* Indexed states ([kev#259] "Not covered": question rows whose cached states
+   * are addressed by index).  NULL, or N host ints read during the call only:
+   * h0 and hT are then pools of pool_size states, sequence n starts from
+   * h0[idx[n]] and its final state goes to hT[idx[n]]; h0 == hT updates the
+   * pool in place (each state is read by the workgroups that later overwrite
+   * it, and only by them).  Indices must be distinct and in [0, pool_size);
+   * other pool entries are left untouched.  Serial scan only: the segment
+   * entry points and a segmented gdr_state_scan return GDR_ERR_UNSUPPORTED
+   * when it is set. */
+  const int32_t* state_indices_host;
+  int32_t pool_size;
 } gdr_problem;
 
 /* Tile of the serial scans.  bv: value columns per workgroup (the BV of

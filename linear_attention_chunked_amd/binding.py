@@ -40,6 +40,8 @@ class gdr_problem(ctypes.Structure):
         ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
         ("dtype", ctypes.c_int),
         ("state_layout", ctypes.c_int),
+        ("state_indices_host", ctypes.POINTER(ctypes.c_int32)),
+        ("pool_size", ctypes.c_int32),
     ]
 
 
@@ -133,9 +135,11 @@ def _dtype_code(dt: torch.dtype) -> int:
 class Problem:
     """A gdr_problem plus the host cu_seqlens it points to (kept alive)."""
 
-    def __init__(self, k: torch.Tensor, DV: int, cu_seqlens=None, state_layout: str = "kv"):
+    def __init__(self, k: torch.Tensor, DV: int, cu_seqlens=None, state_layout: str = "kv", state_indices=None,
+                 pool_size: int = 0):
         B, T, H, DK = k.shape
         self._cu = None
+        self._idx = None
         if cu_seqlens is not None:
             cu = [int(x) for x in (cu_seqlens.tolist() if torch.is_tensor(cu_seqlens) else cu_seqlens)]
             N = len(cu) - 1
@@ -144,8 +148,13 @@ class Problem:
         else:
             N = B
             cu_ptr = None
+        idx_ptr = None
+        if state_indices is not None:
+            idx = [int(x) for x in (state_indices.tolist() if torch.is_tensor(state_indices) else state_indices)]
+            self._idx = (ctypes.c_int32 * max(1, len(idx)))(*idx)
+            idx_ptr = self._idx
         self.s = gdr_problem(B, T, H, DK, DV, N, cu_ptr, _dtype_code(k.dtype),
-                             GDR_STATE_VK if state_layout == "vk" else GDR_STATE_KV)
+                             GDR_STATE_VK if state_layout == "vk" else GDR_STATE_KV, idx_ptr, int(pool_size))
         self.B, self.T, self.H, self.DK, self.DV, self.N = B, T, H, DK, DV, N
 
     @property
@@ -190,14 +199,23 @@ def gdr_chunk_prepare(k, v, g, beta, cu_seqlens=None, stream=None) -> Tuple[torc
 
 def gdr_state_scan(k, w, u, g_cum, h0=None, cu_seqlens=None, tile=None, n_segments: Optional[int] = None,
                    seg_init=None, state_layout: str = "kv", emit_h: bool = True, emit_v_new: bool = True,
-                   emit_final: bool = True, out=None, stream=None):
+                   emit_final: bool = True, out=None, state_indices=None, stream=None):
     """Returns (h [NT,H,DV,DK] | None, v_new | None, hT [N,H,DK,DV] fp32 | None).
 
-    ``out`` may hold preallocated "h", "v_new" and "hT" tensors to write into."""
+    ``out`` may hold preallocated "h", "v_new" and "hT" tensors to write into.
+    With ``state_indices`` (N ints), h0 and out["hT"] are state pools
+    [pool_size, H, ...]: sequence n reads h0[idx[n]] and writes hT[idx[n]]
+    (the same tensor for an in-place update)."""
     DV = u.shape[-1]
-    p = Problem(k, DV, cu_seqlens, state_layout)
-    L = lib()
     out = out or {}
+    pool_size = 0
+    if state_indices is not None:
+        if emit_final and out.get("hT") is None:
+            raise ValueError("indexed states write into a pool: pass out={'hT': pool}")
+        pool = h0 if h0 is not None else out.get("hT")
+        pool_size = int(pool.shape[0]) if pool is not None else 0
+    p = Problem(k, DV, cu_seqlens, state_layout, state_indices, pool_size)
+    L = lib()
     nt = gdr_num_chunks(k, DV, cu_seqlens)
     h = v_new = hT = None
     if emit_h:

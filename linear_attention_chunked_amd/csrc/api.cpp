@@ -57,8 +57,8 @@ gdr_status opt(const void* p, const char* name) {
 gdr_status parse(const gdr_problem* p, gdr::Problem& out) {
   if (p == nullptr) return fail(GDR_ERR_INVALID_ARG, "problem must not be NULL");
   std::string err;
-  if (!gdr::parse_problem(p->B, p->T, p->H, p->DK, p->DV, p->N, p->cu_seqlens_host, p->dtype, p->state_layout, out,
-                          err))
+  if (!gdr::parse_problem(p->B, p->T, p->H, p->DK, p->DV, p->N, p->cu_seqlens_host, p->dtype, p->state_layout,
+                          p->state_indices_host, p->pool_size, out, err))
     return fail(GDR_ERR_INVALID_ARG, err);
   return GDR_OK;
 }
@@ -198,6 +198,7 @@ gdr_status gdr_state_scan(const gdr_problem* p, const gdr_tile* tile, const gdr_
   const float* h_in = h0;
   int in_vk = pr.state_vk;
   if (seg != nullptr) {
+    if (!pr.pool_idx.empty()) return fail(GDR_ERR_UNSUPPORTED, "indexed states are supported by the serial scan only");
     if (seg->n_segments < 1) return fail(GDR_ERR_INVALID_ARG, "n_segments must be >= 1");
     GDR_TRY(need(seg->seg_init, "seg_init"));
     mode = 2;
@@ -253,6 +254,7 @@ gdr_status gdr_segment_summaries(const gdr_problem* p, const gdr_tile* tile, int
   g_err.clear();
   gdr::Problem pr;
   GDR_TRY(parse(p, pr));
+  if (!pr.pool_idx.empty()) return fail(GDR_ERR_UNSUPPORTED, "indexed states are supported by the serial scan only");
   if (n_segments < 1) return fail(GDR_ERR_INVALID_ARG, "n_segments must be >= 1");
   GDR_TRY(need(k, "k"));
   GDR_TRY(need(w, "w"));
@@ -271,6 +273,7 @@ gdr_status gdr_segment_compose(const gdr_problem* p, int32_t n_segments, const f
   g_err.clear();
   gdr::Problem pr;
   GDR_TRY(parse(p, pr));
+  if (!pr.pool_idx.empty()) return fail(GDR_ERR_UNSUPPORTED, "indexed states are supported by the serial scan only");
   if (n_segments < 1) return fail(GDR_ERR_INVALID_ARG, "n_segments must be >= 1");
   GDR_TRY(need(seg_state, "seg_state"));
   GDR_TRY(need(seg_trans, "seg_trans"));

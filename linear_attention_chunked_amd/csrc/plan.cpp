@@ -11,7 +11,7 @@
 namespace gdr {
 
 bool parse_problem(int B, int64_t T, int H, int DK, int DV, int N, const int32_t* cu, int dtype,
-                   int state_layout, Problem& p, std::string& err) {
+                   int state_layout, const int32_t* pool_idx, int pool_size, Problem& p, std::string& err) {
   if (B < 1 || T < 0 || H < 1) {
     err = "B >= 1, T >= 0 and H >= 1 are required";
     return false;
@@ -81,6 +81,29 @@ bool parse_problem(int B, int64_t T, int H, int DK, int DV, int N, const int32_t
   if (c > INT32_MAX / 2) {
     err = "too many chunks";
     return false;
+  }
+  p.pool_idx.clear();
+  p.pool_size = 0;
+  if (pool_idx != nullptr) {
+    if (pool_size < 1) {
+      err = "pool_size must be >= 1 with state_indices_host";
+      return false;
+    }
+    std::vector<char> seen(static_cast<size_t>(pool_size), 0);
+    for (int n = 0; n < p.N; ++n) {
+      const int32_t i = pool_idx[n];
+      if (i < 0 || i >= pool_size) {
+        err = "state index " + std::to_string(i) + " of sequence " + std::to_string(n) + " is outside the pool";
+        return false;
+      }
+      if (seen[i]) {
+        err = "state index " + std::to_string(i) + " appears twice";
+        return false;
+      }
+      seen[i] = 1;
+      p.pool_idx.push_back(i);
+    }
+    p.pool_size = pool_size;
   }
   return true;
 }
@@ -192,8 +215,9 @@ std::vector<Launch> plan_scan(const Problem& p, const Tile& t, int mode, int P, 
   if (mode == 0) {
     for (int n = 0; n < p.N; ++n) {
       const Seq& s = p.seqs[n];
+      const int32_t st = p.pool_idx.empty() ? n : p.pool_idx[n];  // state row (pool index if any)
       rows.push_back(Row{static_cast<int32_t>(s.bos), static_cast<int32_t>(s.len),
-                         static_cast<int32_t>(s.chunk_off), has_h0 ? n : -1, has_hT ? n : -1});
+                         static_cast<int32_t>(s.chunk_off), has_h0 ? st : -1, has_hT ? st : -1});
     }
   } else {
     std::vector<int64_t> t0, t1;

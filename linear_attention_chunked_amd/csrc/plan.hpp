@@ -38,6 +38,8 @@ struct Problem {
   int state_vk = 0;
   std::vector<Seq> seqs;
   int64_t n_chunks = 0;
+  std::vector<int32_t> pool_idx;  // empty, or the state-pool row of each sequence
+  int pool_size = 0;
 };
 
 struct Tile {
@@ -53,7 +55,7 @@ struct Launch {
 
 // Parses and validates; on failure returns false and sets err.
 bool parse_problem(int B, int64_t T, int H, int DK, int DV, int N, const int32_t* cu_host, int dtype,
-                   int state_layout, Problem& out, std::string& err);
+                   int state_layout, const int32_t* pool_idx_host, int pool_size, Problem& out, std::string& err);
 
 // Tile for the serial scans: explicit request (validated) or the table.
 // `rows` is the number of serial chains per head (sequences, or sequences x

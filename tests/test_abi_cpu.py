@@ -139,3 +139,32 @@ def test_status_strings():
     L = B.lib()
     assert L.gdr_status_string(0) == b"GDR_OK"
     assert L.gdr_status_string(3) == b"GDR_ERR_HIP"
+
+
+def _pool_prob(idx, pool_size):
+    cu = [0, 3, 10, 20]
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    ia = (ctypes.c_int32 * len(idx))(*idx)
+    p = B.gdr_problem(1, 20, 2, 128, 128, 3, arr, B.GDR_BF16, 0, ia, pool_size)
+    return p, (arr, ia)
+
+
+@pytest.mark.parametrize("idx,pool", [([0, 1, 1], 4), ([0, 4, 1], 4), ([0, -1, 2], 4), ([0, 1, 2], 0)])
+def test_bad_state_indices_rejected(idx, pool):
+    p, keep = _pool_prob(idx, pool)
+    assert _scan(p) == B.GDR_ERR_INVALID_ARG
+    assert "index" in B.lib().gdr_last_error().decode() or "pool" in B.lib().gdr_last_error().decode()
+
+
+def test_state_pool_serial_only():
+    p, keep = _pool_prob([3, 0, 2], 4)
+    L = B.lib()
+    assert L.gdr_segment_summaries(ctypes.byref(p), None, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == B.GDR_ERR_UNSUPPORTED
+    assert L.gdr_segment_compose(ctypes.byref(p), 2, FAKE, FAKE, None, FAKE, None, None) == B.GDR_ERR_UNSUPPORTED
+    seg = B.gdr_segments(2, FAKE.value)
+    assert L.gdr_state_scan(ctypes.byref(p), None, ctypes.byref(seg), FAKE, FAKE, FAKE, FAKE, None, None, None, None,
+                            None) == B.GDR_ERR_UNSUPPORTED
+    # a valid pool passes validation up to the pointer checks
+    assert _scan(p, k=None) == B.GDR_ERR_INVALID_ARG
+    assert "k" in L.gdr_last_error().decode()
