@@ -36,6 +36,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
@@ -170,7 +172,14 @@ __global__ __launch_bounds__(256) void abc_weights(const AbcArgs a) {
 // and write empty buffer ranges and act as the identity (E = 0, r = 1), so
 // every iteration issues the same memory operations and the compiler's wait
 // counts keep D chunks in flight.
-template <bool IS_K, int XW>
+//
+// Segments (the map is diagonal-affine, so segments compose exactly): the
+// chunks of a sequence are split into P runs.  MODE 1 walks run j < P-1 from
+// a zero state without storing anything and leaves its end state L_j (FP32,
+// normalised at the run's last chunk).  MODE 0 walks run j from
+//   S_start(j) = sum_{i<j} L_i * exp(zc[end_i] - zc[start_j - 1])   (per slot)
+// storing the pre-chunk states; with P = 1 it is the plain serial walk.
+template <bool IS_K, int XW, int MODE>
 struct AbcStates {
   using S = St<bf16_t>;
   using frag = S::frag;
@@ -201,6 +210,7 @@ struct AbcStates {
   struct Ctx {
     const AbcArgs* a;
     int b, h, x0, X;
+    int c_lo, c_hi;           // this workgroup's chunks
     int vo_x[XB >= 16 ? XB / 16 : 1], vo_e[2];  // per-thread byte offsets inside a chunk
     int lo_x[XB >= 16 ? XB / 16 : 1];           // ... and in the LDS x tile
     int vo_h[NR];             // per-lane byte offsets of the state tile (finals)
@@ -213,7 +223,7 @@ struct AbcStates {
     const int64_t H = a.H;
     const int64_t tok0 = static_cast<int64_t>(x.b) * a.T + static_cast<int64_t>(c) * kChunk;
     const int n = min(kChunk, a.T - c * kChunk);
-    const bool any = n > 0;
+    const bool any = n > 0 && c < x.c_hi;
     const uint16_t* xp = static_cast<const uint16_t*>(IS_K ? a.k : a.v) + (tok0 * H + x.h) * x.X + x.x0;
     const uint16_t* ep = static_cast<const uint16_t*>(a.e) + (tok0 * H + x.h) * a.M;
     const float* lp = a.zc + ((static_cast<int64_t>(x.b) * a.NC + c) * H + x.h) * a.M;
@@ -248,7 +258,7 @@ struct AbcStates {
     const int row = tid >> 3, cv = tid & 7;
 #pragma unroll
     for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4_t*>(eb + (row + 32 * i) * STE + 16 * cv) = st.e[i];
-    if (tid < 64) sm.r[(c + 1) % 3][tid] = (c + 1 < a.NC) ? exp_fast(st.z - nxt.z) : 1.f;  // past the end: r = 1
+    if (tid < 64) sm.r[(c + 1) % 3][tid] = (c + 1 < x.c_hi) ? exp_fast(st.z - nxt.z) : 1.f;  // past the end: r = 1
   }
 
   // The staged state of chunk c (written before the last barrier) goes out in
@@ -257,7 +267,7 @@ struct AbcStates {
   __device__ static __forceinline__ void write_out(const Ctx& x, int c, const Smem& sm) {
     const AbcArgs& a = *x.a;
     const int64_t H = a.H, M = a.M;
-    const bool live = c >= 0 && c < a.NC;
+    const bool live = MODE == 0 && c >= x.c_lo && c < x.c_hi;
     const int64_t cc = live ? c : 0;
     const int64_t plane = static_cast<int64_t>(x.b * a.NC + cc) * H + x.h;
     uint16_t* hp = static_cast<uint16_t*>(IS_K ? a.hk : a.hv) +
@@ -280,10 +290,12 @@ struct AbcStates {
     const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int64_t H = a.H, M = a.M;
+    if (MODE == 0) {
 #pragma unroll
-    for (int j = 0; j < NR; ++j)
-      *reinterpret_cast<u32x2_t*>(sm.hs[c & 1] + x.lo_h[j]) =
-          u32x2_t{pack_bf16x2(acc[j][0], acc[j][1]), pack_bf16x2(acc[j][2], acc[j][3])};
+      for (int j = 0; j < NR; ++j)
+        *reinterpret_cast<u32x2_t*>(sm.hs[c & 1] + x.lo_h[j]) =
+            u32x2_t{pack_bf16x2(acc[j][0], acc[j][1]), pack_bf16x2(acc[j][2], acc[j][3])};
+    }
     const float* rr = sm.r[c % 3];
     // Hk^T: wave w owns slot block w, tiles j = k blocks.  Hv^T: wave w owns
     // v block w % NR, tiles j = slot blocks (w / NR) * NR + j.
@@ -319,7 +331,30 @@ struct AbcStates {
     }
   }
 
-  __device__ static void run(const AbcArgs& a, Smem& sm, int b, int h, int x0) {
+  // Per-slot factors of this lane's accumulator elements: Hk^T rows are slots
+  // (4 per lane), Hv^T columns are slots (one per tile).
+  __device__ static __forceinline__ void slot_scale(f32x4_t (&acc)[NR], const float* z_from, const float* z_to,
+                                                    const f32x4_t (&add)[NR], bool accumulate_add) {
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int rt = IS_K ? wave : wave % NR;
+    const int ct0 = IS_K ? 0 : (wave / NR) * NR;
+    if (IS_K) {
+      f32x4_t f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) f[r] = exp_fast(z_from[16 * rt + 4 * g4 + r] - z_to[16 * rt + 4 * g4 + r]);
+#pragma unroll
+      for (int j = 0; j < NR; ++j) acc[j] += add[j] * f;
+    } else {
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        const int m = 16 * (ct0 + j) + c16;
+        acc[j] += add[j] * exp_fast(z_from[m] - z_to[m]);
+      }
+    }
+  }
+
+  __device__ static void run(const AbcArgs& a, Smem& sm, int b, int h, int x0, int seg, int unit) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -329,6 +364,12 @@ struct AbcStates {
     x.h = h;
     x.x0 = x0;
     x.X = IS_K ? a.K : a.V;
+    // chunks of run `seg`: NC split evenly, the first NC mod P runs one longer
+    {
+      const int base = a.NC / a.P, extra = a.NC % a.P;
+      x.c_lo = seg * base + min(seg, extra);
+      x.c_hi = x.c_lo + base + (seg < extra ? 1 : 0);
+    }
     if constexpr (XB >= 16) {
 #pragma unroll
       for (int i = 0; i < XB / 16; ++i) {
@@ -373,32 +414,64 @@ struct AbcStates {
     f32x4_t acc[NR];
 #pragma unroll
     for (int j = 0; j < NR; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // this lane's slice of a run-end state in the workspace (C-layout order)
+    auto lsum_at = [&](int run) {
+      return a.lsum + ((static_cast<int64_t>(b * a.H + h) * (a.P - 1) + run) * (a.K + a.V) * 64 +
+                       static_cast<int64_t>(unit) * (XW * 64) + tid * 4 * NR);
+    };
+    if (MODE == 0 && seg > 0) {
+      // S_start(seg) from the earlier runs' end states
+      const float* zrow = a.zc + (static_cast<int64_t>(b) * a.NC * a.H + h) * a.M;  // + c * H * M
+      const int64_t zs = static_cast<int64_t>(a.H) * a.M;
+      const float* z_start = zrow + (x.c_lo - 1) * zs;
+      const int base = a.NC / a.P, extra = a.NC % a.P;
+      for (int i = 0; i < seg; ++i) {
+        const int end_i = (i + 1) * base + min(i + 1, extra) - 1;  // last chunk of run i
+        f32x4_t l[NR];
+        const float* lp = lsum_at(i);
+#pragma unroll
+        for (int j = 0; j < NR; ++j) l[j] = *reinterpret_cast<const f32x4_t*>(lp + 4 * j);
+        slot_scale(acc, zrow + end_i * zs, z_start, l, true);
+      }
+    }
 
-    const int NC = a.NC;
-    if (NC > 0) {
+    const int nc = x.c_hi - x.c_lo;
+    if (nc > 0) {
       Stage st[D];
 #pragma unroll
-      for (int i = 0; i < D; ++i) load(st[i], x, i);
-      if (tid < 64) sm.r[0][tid] = 0.f;
+      for (int i = 0; i < D; ++i) load(st[i], x, x.c_lo + i);
+      if (tid < 64) {
+        // r of the run's first chunk (0 at the sequence start: nothing before it)
+        const float* zr = a.zc + ((static_cast<int64_t>(b) * a.NC + x.c_lo) * a.H + h) * a.M + tid;
+        sm.r[x.c_lo % 3][tid] = x.c_lo == 0 ? 0.f : exp_fast(zr[-static_cast<int64_t>(a.H) * a.M] - zr[0]);
+      }
       __syncthreads();
-      const int ncp = (NC + D - 1) / D * D;
-      for (int c0 = 0; c0 < ncp; c0 += D) {
+      const int ncp = (nc + D - 1) / D * D;
+      for (int c0 = x.c_lo; c0 < x.c_lo + ncp; c0 += D) {
 #pragma unroll
         for (int i = 0; i < D; ++i) {
           const int c = c0 + i;
           stage_in(st[i], st[(i + 1) % D], x, c, sm);
           load(st[i], x, c + D);
           __syncthreads();
-          write_out(x, c - 1, sm);
+          if (MODE == 0) write_out(x, c - 1, sm);
           accumulate(acc, x, c, sm);
         }
       }
-      __syncthreads();
-      write_out(x, ncp - 1, sm);
+      if (MODE == 0) {
+        __syncthreads();
+        write_out(x, x.c_lo + ncp - 1, sm);
+      }
     }
 
+    if (MODE == 1) {
+      float* lp = const_cast<float*>(lsum_at(seg));
+#pragma unroll
+      for (int j = 0; j < NR; ++j) *reinterpret_cast<f32x4_t*>(lp + 4 * j) = acc[j];
+      return;
+    }
     float* fp = IS_K ? a.hk_final : a.hv_final;
-    if (fp == nullptr) return;
+    if (fp == nullptr || x.c_hi != a.NC) return;
     const int64_t fb = static_cast<int64_t>(b) * a.H + h;
     float* base = fp + (IS_K ? (fb * a.K + x0) * a.M : fb * a.M * a.V + x0);
 #pragma unroll
@@ -406,29 +479,49 @@ struct AbcStates {
   }
 };
 
-template <int XW>
+template <int XW, int MODE>
 __global__ __launch_bounds__(256) void abc_states(const AbcArgs a) {
-  using SK = AbcStates<true, XW>;
-  using SV = AbcStates<false, XW>;
+  using SK = AbcStates<true, XW, MODE>;
+  using SV = AbcStates<false, XW, MODE>;
   static_assert(sizeof(typename SK::Smem) == sizeof(typename SV::Smem), "one LDS layout");
   __shared__ __align__(16) typename SK::Smem sm;
   const int nk = a.K / XW, tiles = nk + a.V / XW;
-  // tiles of one (b, h) share blockIdx modulo 8 (one XCD, so E comes from its L2)
+  const int nseg = MODE == 1 ? a.P - 1 : a.P;
+  // the units of one (b, h) share blockIdx modulo 8 (one XCD, so E comes from its L2)
   const int bx = blockIdx.x;
   const int xcd = bx & 7, slot = bx >> 3;
-  const int pair = 8 * (slot / tiles) + xcd;
-  const int tile = slot % tiles;
+  const int pair = 8 * (slot / (tiles * nseg)) + xcd;
+  const int u = slot % (tiles * nseg);
+  const int tile = u % tiles, seg = u / tiles;
   if (pair >= a.B * a.H) return;
   if (tile < nk) {
-    SK::run(a, sm, pair / a.H, pair % a.H, XW * tile);
+    SK::run(a, sm, pair / a.H, pair % a.H, XW * tile, seg, tile);
   } else {
-    SV::run(a, *reinterpret_cast<typename SV::Smem*>(&sm), pair / a.H, pair % a.H, XW * (tile - nk));
+    SV::run(a, *reinterpret_cast<typename SV::Smem*>(&sm), pair / a.H, pair % a.H, XW * (tile - nk), seg, tile);
   }
 }
 
-// Tile width: the widest that gives at least half as many workgroups as
-// CUs, else 16 (B=2, H=4, K=256, V=512 on MI355X: 64 -> 258 us, 32 -> 178 us,
-// 16 -> 216 us).  GDR_ABC_XW forces a width (16, 32 or 64).
+// Runs per sequence: enough that the (b, h, 64-column tile, run) units of
+// the state walk reach about three workgroups per CU, each run at least 8
+// chunks, at most 8 runs.  Independent of the tile width, so every width
+// gives the same arithmetic.  GDR_ABC_SEGMENTS forces a count.  Measured on
+// B=2, H=4, K=256, V=512 (MI355X, whole call): 64-wide tiles with 1 / 2 / 4 /
+// 8 runs 230 / 230 / 211 / 195 us; 32-wide 217 / 237 / 233 / 213 us.
+int abc_segments(int B, int H, int K, int V, int NC) {
+  int p = 0;
+  if (const char* env = getenv("GDR_ABC_SEGMENTS")) p = atoi(env);
+  if (p <= 0) {
+    const int64_t units64 = static_cast<int64_t>(B) * H * ((K + V) / 64);
+    p = static_cast<int>((768 + units64 - 1) / units64);
+  }
+  p = std::min(p, 8);
+  p = std::min(p, NC / 8);
+  return std::max(p, 1);
+}
+
+// Tile width: the widest whose walk units (with the runs) give at least one
+// workgroup per CU, else the widest with half as many; GDR_ABC_XW forces one
+// (16, 32 or 64).
 int abc_tile_width(const AbcArgs& a) {
   if (const char* env = getenv("GDR_ABC_XW")) {
     const int w = atoi(env);
@@ -436,7 +529,9 @@ int abc_tile_width(const AbcArgs& a) {
   }
   const int64_t pairs = static_cast<int64_t>(a.B) * a.H;
   for (int w = 64; w > 16; w /= 2)
-    if (pairs * ((a.K + a.V) / w) >= 128) return w;
+    if (pairs * ((a.K + a.V) / w) * a.P >= 256) return w;
+  for (int w = 64; w > 16; w /= 2)
+    if (pairs * ((a.K + a.V) / w) * a.P >= 128) return w;
   return 16;
 }
 
@@ -458,10 +553,19 @@ hipError_t launch_abc(const AbcArgs& a, hipStream_t stream) {
   }
   const int xw = abc_tile_width(a);
   const int tiles_w = (a.K + a.V) / xw;
-  const dim3 grid(8 * tiles_w * ((a.B * a.H + 7) / 8));
-  if (xw == 64) hipLaunchKernelGGL(abc_states<64>, grid, dim3(256), 0, stream, a);
-  else if (xw == 32) hipLaunchKernelGGL(abc_states<32>, grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(abc_states<16>, grid, dim3(256), 0, stream, a);
+  const int pairs8 = (a.B * a.H + 7) / 8;
+  if (a.P > 1) {  // end states of every run but the last
+    const dim3 g1(8 * tiles_w * (a.P - 1) * pairs8);
+    if (xw == 64) hipLaunchKernelGGL((abc_states<64, 1>), g1, dim3(256), 0, stream, a);
+    else if (xw == 32) hipLaunchKernelGGL((abc_states<32, 1>), g1, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((abc_states<16, 1>), g1, dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid(8 * tiles_w * a.P * pairs8);
+  if (xw == 64) hipLaunchKernelGGL((abc_states<64, 0>), grid, dim3(256), 0, stream, a);
+  else if (xw == 32) hipLaunchKernelGGL((abc_states<32, 0>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((abc_states<16, 0>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

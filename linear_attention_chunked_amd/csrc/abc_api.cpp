@@ -55,9 +55,12 @@ size_t abc_workspace_size(const abc_problem* p) {
   std::string err;
   if (!abc_valid(p, err)) return 0;
   const int64_t nc = (p->T + 63) / 64;
-  // chunk log-sum-exps and chunk-end normalisers (FP32), then the weights E (storage dtype)
+  // chunk log-sum-exps and chunk-end normalisers (FP32), the weights E
+  // (storage dtype), then the end states of the state walk's runs (FP32)
+  const int P = gdr::abc_segments(p->B, p->H, p->K, p->V, static_cast<int>(nc));
   return 2 * static_cast<size_t>(p->B) * nc * p->H * p->M * sizeof(float) +
-         static_cast<size_t>(p->B) * p->T * p->H * p->M * 2;
+         static_cast<size_t>(p->B) * p->T * p->H * p->M * 2 +
+         static_cast<size_t>(p->B) * p->H * (P - 1) * (p->K + p->V) * p->M * sizeof(float);
 }
 
 gdr_status abc_affine_scan(const abc_problem* p, const void* k, const void* v, const void* s, float* z, void* hk,
@@ -107,6 +110,12 @@ gdr_status abc_affine_scan(const abc_problem* p, const void* k, const void* v, c
   a.NC = static_cast<int32_t>((p->T + 63) / 64);
   a.zc = a.lse + static_cast<int64_t>(a.B) * a.NC * a.H * a.M;
   a.e = a.zc + static_cast<int64_t>(a.B) * a.NC * a.H * a.M;
+  a.P = gdr::abc_segments(a.B, a.H, a.K, a.V, a.NC);
+  {
+    // after E (B*T*H*M bf16), rounded up to 16 bytes
+    const uintptr_t e_end = reinterpret_cast<uintptr_t>(a.e) + static_cast<uintptr_t>(a.B) * a.T * a.H * a.M * 2;
+    a.lsum = reinterpret_cast<float*>((e_end + 15) & ~static_cast<uintptr_t>(15));
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = gdr::launch_abc(a, st);
   if (e != hipSuccess) {

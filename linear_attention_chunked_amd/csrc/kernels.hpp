@@ -71,6 +71,7 @@ struct AbcArgs {
   float* lse;          // workspace: [B, NC, H, M] log-sum-exp of each chunk
   float* zc;           // workspace: [B, NC, H, M] normaliser at chunk ends
   void* e;             // workspace: [B, T, H, M] weights exp(s - zc), storage dtype
+  float* lsum;         // workspace: [B*H, P-1, K+V, M] end states of the runs (P > 1)
   void* hk;
   void* hv;
   float* hk_final;
@@ -79,6 +80,7 @@ struct AbcArgs {
   int32_t T;
   int32_t H, K, M, V;
   int32_t NC;
+  int32_t P;           // runs per sequence of the state walk
 };
 
 using LaunchFn = hipError_t (*)(const void* args, int grid, hipStream_t stream);
@@ -92,5 +94,6 @@ LaunchFn find_output(int dtype, int dk, int dv);
 LaunchFn find_output2(int dk, int dv);
 LaunchFn find_compose(int dk);
 hipError_t launch_abc(const AbcArgs& a, hipStream_t s);
+int abc_segments(int B, int H, int K, int V, int NC);
 
 }  // namespace gdr

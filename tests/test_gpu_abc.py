@@ -103,3 +103,21 @@ def test_abc_tile_widths_bit_identical(pkg, monkeypatch, T):
             assert torch.equal(outs[64][key], outs[xw][key]), (xw, key)
     d = inp.f64()
     compare(outs[64], oracle.abc_recurrent_fp64(d["k"], d["v"], d["s"]), what=f"abc xw T={T}")
+
+
+@pytest.mark.parametrize("runs", [1, 2, 3])
+def test_abc_runs(pkg, monkeypatch, runs):
+    """The state walk split into runs (end states composed per slot with the
+    normaliser ratios) matches the oracle, and every tile width gives the same
+    bits for a given number of runs."""
+    inp = make_abc(970, B=1, T=1700, H=2, K=128, M=64, V=192)
+    monkeypatch.setenv("GDR_ABC_SEGMENTS", str(runs))
+    outs = {}
+    for xw in (64, 32, 16):
+        monkeypatch.setenv("GDR_ABC_XW", str(xw))
+        outs[xw] = run(pkg, inp)
+    for xw in (32, 16):
+        for key in outs[64]:
+            assert torch.equal(outs[64][key], outs[xw][key]), (runs, xw, key)
+    d = inp.f64()
+    compare(outs[64], oracle.abc_recurrent_fp64(d["k"], d["v"], d["s"]), what=f"abc runs={runs}")
