@@ -13,6 +13,9 @@ gdr_ref   token-serial gated delta rule (outputs, pre-chunk states, final
           product) and their serial composition.
 abc_ref   token-serial ABC normalised slot recurrence (cumulative
           normaliser z, pre-chunk key/value slot states, final states).
+gdr_bwd_ref  the reverse (gradient) recurrence of the gated delta rule:
+          gradients at chunk boundaries, of the initial state and of the
+          chunk form's write vectors.
 
 Every function is the plain definition, token by token, in float64 (or in
 exact rationals when handed ``fractions.Fraction`` object arrays); there is
@@ -31,3 +34,4 @@ from .gdr_ref import (  # noqa: F401
 )
 from .abc_ref import abc_recurrent_fp64, abc_scan_sequence, abc_weighted_scan  # noqa: F401
 from .chunked_ref import gdr_chunked_fp64, chunked_scan_sequence, chunk_factors  # noqa: F401
+from .gdr_bwd_ref import gdr_backward_fp64, gdr_backward_sequence  # noqa: F401

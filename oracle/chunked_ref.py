@@ -50,11 +50,13 @@ def chunk_factors(k, v, g, beta):
     return gamma, W, U
 
 
-def chunked_scan_sequence(q, k, v, g, beta, S0, scale=1.0, chunk: int = CHUNK):
+def chunked_scan_sequence(q, k, v, g, beta, S0, scale=1.0, chunk: int = CHUNK, delta_shift=None):
     """One sequence: q, k [L, H, DK], v [L, H, DV], g, beta [L, H], S0 [H, DK, DV].
 
     Returns dict with o, v_new (Delta), w, u, g_cum [L, H, ...], h (pre-chunk
-    states) [nc, H, DK, DV] and hT [H, DK, DV].
+    states) [nc, H, DK, DV] and hT [H, DK, DV].  ``delta_shift`` [L, H, DV], if
+    given, is added to each chunk's Delta right after it is formed (the tests
+    differentiate the chunk form with respect to Delta by finite differences).
     """
     L, H, DK = k.shape
     DV = v.shape[-1]
@@ -73,6 +75,8 @@ def chunked_scan_sequence(q, k, v, g, beta, S0, scale=1.0, chunk: int = CHUNK):
             gamma, W, U = chunk_factors(kk, vv, g[c0:c1, hh], beta[c0:c1, hh])
             S0h = S[hh]
             D = U - W @ S0h
+            if delta_shift is not None:
+                D = D + delta_shift[c0:c1, hh]
             P = np.tril(qq @ kk.T) * np.exp(gamma[:, None] - gamma[None, :])
             o[c0:c1, hh] = scale * (np.exp(gamma)[:, None] * (qq @ S0h) + P @ D)
             S[hh] = np.exp(gamma[-1]) * S0h + kk.T @ (np.exp(gamma[-1] - gamma)[:, None] * D)

@@ -12,7 +12,11 @@ the independent fact it encodes:
   a = b = 1, the ABC normaliser as a prefix log-sum-exp and the normalised
   states as explicit weighted sums;
 * invariants: linearity in (S0, v), independence of packed sequences, linear
-  output scale, slot weights summing to one.
+  output scale, slot weights summing to one;
+* for the reverse recurrence: central finite differences of the (pinned)
+  forward oracles, which are exact here because the loss is linear in the
+  perturbed state or write vector, the pure-decay closed form, and the
+  reverse chunk relation the GPU kernel uses.
 """
 
 from __future__ import annotations
@@ -412,3 +416,117 @@ def check_abc_chunk_affine(abc_ref):
 
 ABC_CHECKS = [check_abc_closed_form, check_abc_ones, check_abc_constant_logits,
               check_abc_rationals, check_abc_chunk_affine]
+
+
+# --------------------------------------------------------------------------- reverse recurrence
+def _bwd_problem(seed, L=8, H=2, DK=3, DV=2):
+    q, k, v, a, b, S0 = rand_problem(seed, L, H, DK, DV)
+    r = np.random.default_rng(seed + 1)
+    do = r.standard_normal((L, H, DV))
+    dS_end = r.standard_normal((H, DK, DV))
+    return q, k, v, np.log(a), b, S0, do, dS_end
+
+
+def _loss(gdr_ref, q, k, v, g, b, S0, do, dS_end, scale, chunk):
+    o, _, Sf = gdr_ref.gdr_scan_sequence(q, k, v, np.exp(g), b, S0, scale, chunk)
+    return float(np.sum(o * do) + np.sum(Sf * dS_end))
+
+
+def _fd(f, x, eps=1e-6):
+    """Central differences of a scalar function of an array."""
+    grad = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        xp, xm = x.copy(), x.copy()
+        xp[i] += eps
+        xm[i] -= eps
+        grad[i] = (f(xp) - f(xm)) / (2 * eps)
+    return grad
+
+
+def check_bwd_initial_state(bwd_ref, gdr_ref):
+    """dh0 = dL/dS0 of L = sum <do, o> + <dS_end, S_final> (finite differences)."""
+    q, k, v, g, b, S0, do, dS_end = _bwd_problem(91)
+    _, dh0, _ = bwd_ref.gdr_backward_sequence(q, k, g, b, do, dS_end, 0.7, chunk=3)
+    fd = _fd(lambda S: _loss(gdr_ref, q, k, v, g, b, S, do, dS_end, 0.7, 3), S0)
+    _assert_close(dh0, fd, 1e-7, "dh0 vs finite differences")
+
+
+def check_bwd_boundaries(bwd_ref, gdr_ref):
+    """dh[c] = gradient of the loss of the tokens after chunk c with respect to
+    the state they start from (finite differences on a restarted forward)."""
+    chunk = 3
+    q, k, v, g, b, S0, do, dS_end = _bwd_problem(92, L=8)
+    dh, _, _ = bwd_ref.gdr_backward_sequence(q, k, g, b, do, dS_end, 0.7, chunk=chunk)
+    L = q.shape[0]
+    for c in range(dh.shape[0]):
+        t0 = (c + 1) * chunk
+        if t0 >= L:
+            _assert_close(dh[c], dS_end, 1e-12, f"dh[{c}] after the last chunk")
+            continue
+        sl = slice(t0, L)
+        fd = _fd(lambda S: _loss(gdr_ref, q[sl], k[sl], v[sl], g[sl], b[sl], S, do[sl], dS_end, 0.7, chunk),
+                 np.zeros_like(S0))
+        _assert_close(dh[c], fd, 1e-7, f"dh[{c}] vs finite differences")
+
+
+def check_bwd_write_vectors(bwd_ref, chunked_ref):
+    """dv_new = dL/dDelta of the chunk form (finite differences on Delta)."""
+    chunk = 3
+    q, k, v, g, b, S0, do, dS_end = _bwd_problem(93, L=8)
+    _, _, dv = bwd_ref.gdr_backward_sequence(q, k, g, b, do, dS_end, 0.7, chunk=chunk)
+
+    def loss(shift):
+        r = chunked_ref.chunked_scan_sequence(q, k, v, g, b, S0, 0.7, chunk, delta_shift=shift)
+        return float(np.sum(r["o"] * do) + np.sum(r["hT"] * dS_end))
+
+    fd = _fd(loss, np.zeros_like(do))
+    _assert_close(dv, fd, 1e-7, "dv_new vs finite differences")
+
+
+def check_bwd_pure_decay(bwd_ref):
+    """b = 0: dh0 = sum_t scale exp(g_1 + .. + g_t) q_t do_t^T + exp(sum g) dS_end."""
+    q, k, v, g, b, S0, do, dS_end = _bwd_problem(94, L=9)
+    b = np.zeros_like(b)
+    _, dh0, _ = bwd_ref.gdr_backward_sequence(q, k, g, b, do, dS_end, 0.5, chunk=4)
+    cg = np.cumsum(g, axis=0)
+    ref = np.exp(cg[-1])[:, None, None] * dS_end
+    for t in range(q.shape[0]):
+        ref = ref + 0.5 * np.exp(cg[t])[:, None, None] * q[t][:, :, None] * do[t][:, None, :]
+    _assert_close(dh0, ref, 1e-12, "pure decay dh0")
+
+
+def check_bwd_chunk_relation(bwd_ref, chunked_ref):
+    """The reverse chunk step the kernel runs:
+    dS_c = e^{gamma_C} dh[c] + scale Q_c^T diag(e^gamma) dO_c - W_c^T dv_new_c,
+    with dS_c = dh[c-1] (dh0 for the first chunk), W from the chunk form."""
+    L, H, DK, DV, C = 150, 2, 8, 6, 64
+    q, k, v, a, b, S0 = rand_problem(95, L, H, DK, DV)
+    g = np.log(a)
+    r = np.random.default_rng(96)
+    do = r.standard_normal((L, H, DV))
+    dS_end = r.standard_normal((H, DK, DV))
+    dh, dh0, dv = bwd_ref.gdr_backward_sequence(q, k, g, b, do, dS_end, 0.7, chunk=C)
+    fw = chunked_ref.chunked_scan_sequence(q, k, v, g, b, S0, 0.7, C)
+    W, gam = fw["w"], fw["g_cum"]
+    for c in range(dh.shape[0]):
+        c0, c1 = c * C, min(L, (c + 1) * C)
+        for hh in range(H):
+            ga = gam[c0:c1, hh]
+            lhs = (np.exp(ga[-1]) * dh[c, hh] + 0.7 * q[c0:c1, hh].T @ (np.exp(ga)[:, None] * do[c0:c1, hh])
+                   - W[c0:c1, hh].T @ dv[c0:c1, hh])
+            prev = dh0[hh] if c == 0 else dh[c - 1, hh]
+            _assert_close(lhs, prev, 1e-10, f"reverse chunk step {c}")
+
+
+BWD_CHECKS = [check_bwd_initial_state, check_bwd_boundaries, check_bwd_write_vectors, check_bwd_pure_decay,
+              check_bwd_chunk_relation]
+
+
+def run_bwd_check(check, bwd_ref, gdr_ref, chunked_ref):
+    if check in (check_bwd_initial_state, check_bwd_boundaries):
+        return check(bwd_ref, gdr_ref)
+    if check in (check_bwd_write_vectors, check_bwd_chunk_relation):
+        return check(bwd_ref, chunked_ref)
+    return check(bwd_ref)

@@ -91,3 +91,36 @@ def test_abc_pins_catch(mut):
         except Exception:
             failures += 1
     assert failures > 0, f"no pin caught mutation {mut}"
+
+
+BWD_MUTANTS = {
+    "bwd_dropped_scale": ("G = carry + scale * q[t]", "G = carry + q[t]"),
+    "bwd_no_end_gradient": ("carry = np.array(dS_end, dtype=np.float64)",
+                            "carry = 0 * np.array(dS_end, dtype=np.float64)"),
+    "bwd_jacobian_sign": ("(X - beta[t][:, None, None]", "(X + beta[t][:, None, None]"),
+    "bwd_dropped_decay": ("return a[t][:, None, None] * (X", "return (X"),
+    "bwd_boundary_includes_own_output": ("dh[t // chunk] = carry",
+                                         "dh[t // chunk] = carry + scale * q[t][:, :, None] * do[t][:, None, :]"),
+    "bwd_dv_untransposed": ("scale * (P.T @ dd)", "scale * (P @ dd)"),
+    "bwd_dv_no_decay": ("np.exp(ga[-1] - ga)[:, None] * (kk @ dh[c, hh])", "(kk @ dh[c, hh])"),
+    "bwd_dv_wrong_boundary": ("(kk @ dh[c, hh])", "(kk @ dh[max(c - 1, 0), hh])"),
+}
+
+
+@pytest.mark.parametrize("mut", sorted(BWD_MUTANTS))
+def test_bwd_pins_catch(mut):
+    from oracle import chunked_ref, gdr_ref
+
+    old, new = BWD_MUTANTS[mut]
+    src = open(os.path.join(ROOT, "oracle/gdr_bwd_ref.py")).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    src = src.replace(old, new, 1).replace("from .gdr_ref import", "from oracle.gdr_ref import")
+    m = types.ModuleType(f"mut_{mut}")
+    exec(compile(src, "gdr_bwd_ref_mut", "exec"), m.__dict__)
+    failures = 0
+    for check in P.BWD_CHECKS:
+        try:
+            P.run_bwd_check(check, m, gdr_ref, chunked_ref)
+        except Exception:
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {mut}"
