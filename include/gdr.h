@@ -201,6 +201,38 @@ typedef struct {
   gdr_dtype dtype;
 } abc_problem;
 
+/* Reverse (gradient) pass ([fla#23] "Problem": the reverse kernel that walks
+ * the state chunk by chunk; "Proposed Dataflow", item 4: the reverse dH
+ * recurrence).  For a loss L with upstream gradients dO = dL/do (storage
+ * dtype, like v) and dhT = dL/dhT (float32, nullable = zero), per chunk c of
+ * each sequence with gamma = the chunk-local cumulative log decay (g_cum),
+ * gamma_C its last valid value and P[t][i] = (q_t . k_i) e^{gamma_t - gamma_i}
+ * for i <= t (else 0):
+ *   dh[c]      = dL/dS after chunk c as the input of the rest of the sequence
+ *                (dhT after the last chunk)
+ *   dv_local   = scale P^T dO                          (chunk-local part)
+ *   dv_new     = diag(e^{gamma_C - gamma}) K dh[c] + dv_local
+ *                (dL/d v_new, the gradient of the forward scan's write vectors)
+ *   dh[c - 1]  = e^{gamma_C} dh[c] + scale Q^T diag(e^gamma) dO - W^T dv_new
+ *   dh0        = the same expression after the first chunk (dL/dh0).
+ * Bfloat16 storage only; the pool (state_indices_host) is not supported here. */
+
+/* dv_local for every chunk, chunk-parallel: q, k [B,T,H,DK], g_cum [B,T,H],
+ * dO [B,T,H,DV] -> dv_local [B,T,H,DV] (storage dtype).  Rows past a
+ * sequence's last token are not written. */
+gdr_status gdr_chunk_dv_local(const gdr_problem* p, const void* q, const void* k, const float* g_cum, const void* dO,
+                              float scale, void* dv_local, void* stream);
+
+/* The reverse state scan: serial over each sequence's chunks, last to first.
+ * Inputs q, k, w (from gdr_chunk_prepare), g_cum, dO, dv_local (from
+ * gdr_chunk_dv_local), dhT (nullable, [N,H,DK,DV] or [N,H,DV,DK] by
+ * state_layout).  Outputs (each nullable): dh [NT,H,DV,DK] storage dtype,
+ * value-major like h; dv_new_grad [B,T,H,DV] storage dtype; dh0 float32 in
+ * the state layout. */
+gdr_status gdr_state_scan_bwd(const gdr_problem* p, const void* q, const void* k, const void* w, const float* g_cum,
+                              const void* dO, const void* dv_local, const float* dhT, float scale, void* dh,
+                              void* dv_new_grad, float* dh0, void* stream);
+
 /* Device workspace abc_affine_scan needs (bytes). */
 size_t abc_workspace_size(const abc_problem* p);
 

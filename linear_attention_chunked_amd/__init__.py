@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     abc_affine_scan,
     abc_workspace_size,
     chunk_gated_delta_rule,
+    gdr_chunk_dv_local,
     gdr_chunk_output,
     gdr_chunk_prepare,
     gdr_num_chunks,
@@ -16,5 +17,6 @@ from .binding import (  # noqa: F401
     gdr_segment_compose,
     gdr_segment_summaries,
     gdr_state_scan,
+    gdr_state_scan_bwd,
     lib,
 )

@@ -75,6 +75,9 @@ _SIGS = {
     "gdr_segment_summaries": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile), ctypes.c_int32,
                                              _P, _P, _P, _P, _P, _P, _P]),
     "gdr_segment_compose": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
+    "gdr_chunk_dv_local": (ctypes.c_int, [ctypes.POINTER(gdr_problem), _P, _P, _P, _P, ctypes.c_float, _P, _P]),
+    "gdr_state_scan_bwd": (ctypes.c_int, [ctypes.POINTER(gdr_problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                          _P, _P, _P, _P]),
     "abc_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(abc_problem)]),
     "abc_affine_scan": (ctypes.c_int, [ctypes.POINTER(abc_problem), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
@@ -302,6 +305,33 @@ def abc_affine_scan(k, v, s, emit_z: bool = False, emit_final: bool = True, stre
     _check(L.abc_affine_scan(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(s), _ptr(z), _ptr(hk), _ptr(hv), _ptr(hkf),
                              _ptr(hvf), _ptr(ws), ws_bytes, _stream(stream)), "abc_affine_scan")
     return z, hk, hv, hkf, hvf
+
+
+def gdr_chunk_dv_local(q, k, g_cum, dO, scale: float = 1.0, cu_seqlens=None, stream=None) -> torch.Tensor:
+    """Chunk-local part of the write-vector gradient, scale P^T dO, per chunk."""
+    p = Problem(k, dO.shape[-1], cu_seqlens)
+    dvl = torch.empty_like(dO)
+    _check(lib().gdr_chunk_dv_local(p.ref, _ptr(q), _ptr(k), _ptr(g_cum), _ptr(dO), float(scale), _ptr(dvl),
+                                    _stream(stream)), "gdr_chunk_dv_local")
+    return dvl
+
+
+def gdr_state_scan_bwd(q, k, w, g_cum, dO, dv_local, dhT=None, scale: float = 1.0, cu_seqlens=None,
+                       state_layout: str = "kv", emit_dh: bool = True, emit_dv: bool = True, emit_dh0: bool = True,
+                       stream=None):
+    """Reverse state scan.  Returns (dh [NT,H,DV,DK] | None, dv_new_grad [B,T,H,DV] | None,
+    dh0 [N,H,DK,DV] fp32 (or [N,H,DV,DK] for "vk") | None)."""
+    DV = dO.shape[-1]
+    p = Problem(k, DV, cu_seqlens, state_layout)
+    nt = gdr_num_chunks(k, DV, cu_seqlens)
+    dh = torch.empty((nt, p.H, DV, p.DK), dtype=k.dtype, device=k.device) if emit_dh else None
+    dv = torch.empty_like(dO) if emit_dv else None
+    shape = (p.N, p.H, DV, p.DK) if state_layout == "vk" else (p.N, p.H, p.DK, DV)
+    dh0 = torch.empty(shape, dtype=torch.float32, device=k.device) if emit_dh0 else None
+    _check(lib().gdr_state_scan_bwd(p.ref, _ptr(q), _ptr(k), _ptr(w), _ptr(g_cum), _ptr(dO), _ptr(dv_local),
+                                    _ptr(dhT), float(scale), _ptr(dh), _ptr(dv), _ptr(dh0), _stream(stream)),
+           "gdr_state_scan_bwd")
+    return dh, dv, dh0
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, h0=None, cu_seqlens=None, scale: float = 1.0,

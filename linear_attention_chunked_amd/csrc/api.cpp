@@ -248,6 +248,89 @@ gdr_status gdr_chunk_output(const gdr_problem* p, const void* q, const void* k, 
   return GDR_OK;
 }
 
+gdr_status gdr_chunk_dv_local(const gdr_problem* p, const void* q, const void* k, const float* g_cum,
+                              const void* dO, float scale, void* dv_local, void* stream) {
+  g_err.clear();
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  GDR_TRY(need(q, "q"));
+  GDR_TRY(need(k, "k"));
+  GDR_TRY(need(g_cum, "g_cum"));
+  GDR_TRY(need(dO, "dO"));
+  GDR_TRY(need(dv_local, "dv_local"));
+  if (pr.dtype != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "the reverse pass is built for bfloat16 storage");
+  gdr::LaunchFn fn = gdr::find_dv_local(pr.DK, pr.DV);
+  if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no dv_local kernel for this DK/DV");
+  gdr::ChunkArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = dO;
+  a.g = g_cum;
+  a.o = dv_local;
+  a.scale = scale;
+  a.H = pr.H;
+  for (const gdr::Launch& l : gdr::plan_chunks(pr, pr.DV / 64)) {
+    a.n_rows = static_cast<int32_t>(l.rows.size());
+    a.n_chunks = l.n_chunks;
+    a.chunk_base = l.chunk_base;
+    memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
+    hipError_t e = fn(&a, l.grid, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "dv_local launch");
+  }
+  return GDR_OK;
+}
+
+gdr_status gdr_state_scan_bwd(const gdr_problem* p, const void* q, const void* k, const void* w, const float* g_cum,
+                              const void* dO, const void* dv_local, const float* dhT, float scale, void* dh,
+                              void* dv_new_grad, float* dh0, void* stream) {
+  g_err.clear();
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  if (!pr.pool_idx.empty()) return fail(GDR_ERR_UNSUPPORTED, "indexed states are supported by the forward scan only");
+  GDR_TRY(need(q, "q"));
+  GDR_TRY(need(k, "k"));
+  GDR_TRY(need(w, "w"));
+  GDR_TRY(need(g_cum, "g_cum"));
+  GDR_TRY(need(dO, "dO"));
+  GDR_TRY(need(dv_local, "dv_local"));
+  GDR_TRY(opt(dhT, "dhT"));
+  GDR_TRY(opt(dh, "dh"));
+  GDR_TRY(opt(dv_new_grad, "dv_new_grad"));
+  GDR_TRY(opt(dh0, "dh0"));
+  if (pr.dtype != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "the reverse pass is built for bfloat16 storage");
+  gdr::LaunchFn fn = gdr::find_scan_bwd(pr.DK);
+  if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no reverse scan kernel for this DK");
+  if (pr.DV % 64 != 0) return fail(GDR_ERR_UNSUPPORTED, "the reverse scan takes 64-column blocks");
+  gdr::ScanBwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.w = w;
+  a.g_cum = g_cum;
+  a.dO = dO;
+  a.dv_local = dv_local;
+  a.dhT = dhT;
+  a.dh = dh;
+  a.dv = dv_new_grad;
+  a.dh0 = dh0;
+  a.scale = scale;
+  a.H = pr.H;
+  a.DV = pr.DV;
+  a.state_vk = pr.state_vk;
+  gdr::Tile t;
+  t.bv = 64;
+  t.waves = 4;
+  t.stages = 2;
+  for (const gdr::Launch& l : gdr::plan_scan(pr, t, 0, 1, dhT != nullptr, dh0 != nullptr)) {
+    a.n_rows = static_cast<int32_t>(l.rows.size());
+    memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
+    hipError_t e = fn(&a, l.grid, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "reverse scan launch");
+  }
+  return GDR_OK;
+}
+
 gdr_status gdr_segment_summaries(const gdr_problem* p, const gdr_tile* tile, int32_t n_segments, const void* k,
                                  const void* w, const void* u, const float* g_cum, float* seg_state,
                                  float* seg_trans, void* stream) {

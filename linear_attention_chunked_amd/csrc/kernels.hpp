@@ -50,6 +50,26 @@ struct ChunkArgs {
   Row rows[kMaxRows];  // chunk_off relative to chunk_base
 };
 
+// Reverse state scan (rows as in ScanArgs; in_idx = dhT row, out_idx = dh0 row).
+struct ScanBwdArgs {
+  const void* q;
+  const void* k;
+  const void* w;
+  const float* g_cum;
+  const void* dO;
+  const void* dv_local;
+  const float* dhT;    // nullable
+  void* dh;            // [NT, H, DV, DK] storage dtype (nullable)
+  void* dv;            // write-vector gradient [B, T, H, DV] (nullable)
+  float* dh0;          // nullable
+  float scale;
+  int32_t H;
+  int32_t DV;
+  int32_t state_vk;    // layout of dhT / dh0
+  int32_t n_rows;
+  Row rows[kMaxRows];
+};
+
 struct ComposeArgs {
   const float* seg_state;
   const float* seg_trans;
@@ -93,6 +113,8 @@ LaunchFn find_prepare2(int dk, int dv);
 LaunchFn find_output(int dtype, int dk, int dv);
 LaunchFn find_output2(int dk, int dv);
 LaunchFn find_compose(int dk);
+LaunchFn find_dv_local(int dk, int dv);
+LaunchFn find_scan_bwd(int dk);
 hipError_t launch_abc(const AbcArgs& a, hipStream_t s);
 int abc_segments(int B, int H, int K, int V, int NC);
 

@@ -168,3 +168,18 @@ def test_state_pool_serial_only():
     # a valid pool passes validation up to the pointer checks
     assert _scan(p, k=None) == B.GDR_ERR_INVALID_ARG
     assert "k" in L.gdr_last_error().decode()
+
+
+def test_reverse_pass_validation():
+    L = B.lib()
+    p, keep = _prob(dtype=B.GDR_F32)
+    assert L.gdr_chunk_dv_local(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), FAKE,
+                                None) == B.GDR_ERR_UNSUPPORTED
+    assert L.gdr_state_scan_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, ctypes.c_float(1.0),
+                                FAKE, FAKE, FAKE, None) == B.GDR_ERR_UNSUPPORTED
+    p, keep = _prob()
+    assert L.gdr_state_scan_bwd(ctypes.byref(p), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, ctypes.c_float(1.0),
+                                FAKE, FAKE, FAKE, None) == B.GDR_ERR_INVALID_ARG
+    pp, keep2 = _pool_prob([3, 0, 2], 4)
+    assert L.gdr_state_scan_bwd(ctypes.byref(pp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, ctypes.c_float(1.0),
+                                FAKE, FAKE, FAKE, None) == B.GDR_ERR_UNSUPPORTED
