@@ -258,6 +258,7 @@ def main():
         out["long_state"] = long_state(pkg, torch, dev)
         out["new_states"] = new_states(pkg, torch, dev)
         out["abc_affine"] = abc_affine(pkg, torch, dev)
+        out["reverse"] = reverse(pkg, torch, dev, args.workload)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
@@ -350,6 +351,71 @@ def abc_affine(pkg, torch, dev):
     return {"workload": "abc_affine (B=2, T=16384, H=4, K=256, M=64, V=512, bf16)", "us": round(us, 1),
             "Mtok_head_per_s": round(inp.token_heads / us, 1), "alg_bytes": alg,
             "frac_of_hbm": round(alg / (us * 1e-6) / 8e12, 4)}
+
+
+def reverse_alg_bytes(lengths, H, DK, DV, nt, has_dhT):
+    """Reverse pass, minimum traffic of each kernel (bf16 storage, float32
+    gates and state gradients).  dv_local: read q, k, dO, g_cum, write
+    dv_local.  Reverse scan: read q, k, w, dO, dv_local, g_cum (and dhT),
+    write dh at every chunk (bf16), the write-vector gradient and dh0 (fp32)."""
+    tok = int(sum(lengths)) * H
+    n = len(lengths)
+    dvl = tok * (2 * DK * 2 + DV * 2 + 4 + DV * 2)
+    scan = tok * (3 * DK * 2 + 2 * DV * 2 + 4 + DV * 2) + nt * H * DK * DV * 2 + n * H * DK * DV * 4
+    if has_dhT:
+        scan += n * H * DK * DV * 4
+    return dvl, scan
+
+
+def reverse(pkg, torch, dev, workload):
+    """The reverse pass of the same workload: chunk-local write-vector
+    gradient, then the serial reverse state walk (dh per chunk, dv_new
+    gradient, dh0), seeded dO (bf16) and dhT (fp32)."""
+    import numpy as np
+    from workloads import make_config
+
+    inp = make_config(workload)
+    q, k, v, g, beta = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    cu = inp.cu_seqlens
+    DV = v.shape[-1]
+    r = np.random.default_rng(7)
+    dO = torch.from_numpy(r.standard_normal(tuple(v.shape)).astype(np.float32)).to(v.dtype).to(dev)
+    dhT = torch.from_numpy(0.1 * r.standard_normal((inp.N, inp.H, inp.DK, DV)).astype(np.float32)).to(dev)
+    g_cum, w, _ = pkg.gdr_chunk_prepare(k, v, g, beta, cu)
+    nt = pkg.gdr_num_chunks(k, DV, cu)
+    dvl = torch.empty_like(dO)
+    dh = torch.empty((nt, inp.H, DV, inp.DK), dtype=k.dtype, device=dev)
+    dv = torch.empty_like(dO)
+    dh0 = torch.empty((inp.N, inp.H, inp.DK, DV), dtype=torch.float32, device=dev)
+    B = pkg.binding
+    L = pkg.lib()
+    P = B.Problem(k, DV, cu)
+    ptr = B._ptr
+    s_ptr = B._stream(torch.cuda.current_stream())
+    scale = float(inp.scale)
+
+    def dv_local():
+        B._check(L.gdr_chunk_dv_local(P.ref, ptr(q), ptr(k), ptr(g_cum), ptr(dO), scale, ptr(dvl), s_ptr),
+                 "dv_local")
+
+    def scan_bwd():
+        B._check(L.gdr_state_scan_bwd(P.ref, ptr(q), ptr(k), ptr(w), ptr(g_cum), ptr(dO), ptr(dvl), ptr(dhT),
+                                      scale, ptr(dh), ptr(dv), ptr(dh0), s_ptr), "scan_bwd")
+
+    def both():
+        dv_local()
+        scan_bwd()
+
+    a_us = _event_median_us(torch, dv_local, reps=7, per=8)
+    b_us = _event_median_us(torch, scan_bwd, reps=7, per=8)
+    t_us = _event_median_us(torch, both, reps=7, per=8)
+    a_alg, b_alg = reverse_alg_bytes(inp.lengths, inp.H, inp.DK, DV, nt, True)
+    return {"workload": f"{workload} reverse pass (dO bf16, dhT fp32)", "us": round(t_us, 1),
+            "Mtok_head_per_s": round(inp.token_heads / t_us, 1),
+            "dv_local": {"us": round(a_us, 1), "alg_bytes": a_alg,
+                         "frac_of_hbm": round(a_alg / (a_us * 1e-6) / 8e12, 4)},
+            "scan_bwd": {"us": round(b_us, 1), "alg_bytes": b_alg,
+                         "frac_of_hbm": round(b_alg / (b_us * 1e-6) / 8e12, 4)}}
 
 
 if __name__ == "__main__":
