@@ -13,6 +13,9 @@ gdr_ref   token-serial gated delta rule (outputs, pre-chunk states, final
           product) and their serial composition.
 abc_ref   token-serial ABC normalised slot recurrence (cumulative
           normaliser z, pre-chunk key/value slot states, final states).
+abc_bwd_ref  the reverse (dH) recurrence of the ABC slot states: gradients
+          of the states at chunk boundaries from gradients of the slot
+          scores and of the value read.
 gdr_bwd_ref  the reverse (gradient) recurrence of the gated delta rule:
           gradients at chunk boundaries, of the initial state and of the
           chunk form's write vectors.
@@ -32,6 +35,7 @@ from .gdr_ref import (  # noqa: F401
     gdr_segment_summaries_fp64,
     gdr_segment_compose_fp64,
 )
-from .abc_ref import abc_recurrent_fp64, abc_scan_sequence, abc_weighted_scan  # noqa: F401
+from .abc_ref import abc_readout_sequence, abc_recurrent_fp64, abc_scan_sequence, abc_weighted_scan  # noqa: F401
+from .abc_bwd_ref import abc_backward_fp64, abc_backward_sequence  # noqa: F401
 from .chunked_ref import gdr_chunked_fp64, chunked_scan_sequence, chunk_factors  # noqa: F401
 from .gdr_bwd_ref import gdr_backward_fp64, gdr_backward_sequence  # noqa: F401

@@ -34,18 +34,20 @@ import numpy as np
 CHUNK = 64
 
 
-def abc_scan_sequence(k, v, s, chunk: int = CHUNK):
+def abc_scan_sequence(k, v, s, chunk: int = CHUNK, hk0=None, hv0=None, z0=None):
     """One sequence, all heads: k [T, H, K], v [T, H, V], s [T, H, M] (float64).
 
     Returns (z [T, H, M], hk_pre [NC, H, K, M], hv_pre [NC, H, M, V],
-    hk_final [H, K, M], hv_final [H, M, V]).
+    hk_final [H, K, M], hv_final [H, M, V]).  ``hk0``, ``hv0``, ``z0`` resume a
+    sequence from a carried state and normaliser (default: zero states,
+    z0 = -inf, the page's state-free start).
     """
     T, H, K = k.shape
     V = v.shape[-1]
     M = s.shape[-1]
-    z_prev = np.full((H, M), -np.inf)
-    Hk = np.zeros((H, K, M))
-    Hv = np.zeros((H, M, V))
+    z_prev = np.full((H, M), -np.inf) if z0 is None else np.array(z0, dtype=np.float64)
+    Hk = np.zeros((H, K, M)) if hk0 is None else np.array(hk0, dtype=np.float64)
+    Hv = np.zeros((H, M, V)) if hv0 is None else np.array(hv0, dtype=np.float64)
     z = np.zeros((T, H, M))
     hk_pre, hv_pre = [], []
     for t in range(T):
@@ -63,6 +65,47 @@ def abc_scan_sequence(k, v, s, chunk: int = CHUNK):
     hk_pre = np.stack(hk_pre) if nc else np.zeros((0, H, K, M))
     hv_pre = np.stack(hv_pre) if nc else np.zeros((0, H, M, V))
     return z, hk_pre, hv_pre, Hk, Hv
+
+
+def abc_readout_sequence(q, k, v, s, p=None, scale: float = 1.0, hk0=None, hv0=None, z0=None):
+    """The two reads of the slot states, token by token, one sequence, all heads.
+
+    q [T, H, K], k [T, H, K], v [T, H, V], s [T, H, M].  After token t's update:
+
+        score_t = scale * Hk_t^T q_t          (M slot scores)
+        o_t     = Hv_t^T p_t                  (V outputs)
+
+    with p_t the given slot weights ``p`` [T, H, M], or softmax over the slots
+    of score_t when ``p`` is None (the full ABC read: scores, a softmax over
+    the M slots, then the value read).  Returns a dict of float64 arrays:
+    score [T, H, M], p [T, H, M], o [T, H, V], z [T, H, M], hk_final, hv_final.
+    """
+    T, H, K = k.shape
+    V = v.shape[-1]
+    M = s.shape[-1]
+    z_prev = np.full((H, M), -np.inf) if z0 is None else np.array(z0, dtype=np.float64)
+    Hk = np.zeros((H, K, M)) if hk0 is None else np.array(hk0, dtype=np.float64)
+    Hv = np.zeros((H, M, V)) if hv0 is None else np.array(hv0, dtype=np.float64)
+    score = np.zeros((T, H, M))
+    pw = np.zeros((T, H, M))
+    o = np.zeros((T, H, V))
+    z = np.zeros((T, H, M))
+    for t in range(T):
+        zt = np.logaddexp(z_prev, s[t])
+        w = np.exp(s[t] - zt)
+        r = np.exp(z_prev - zt)
+        Hk = Hk * r[:, None, :] + k[t][:, :, None] * w[:, None, :]
+        Hv = Hv * r[:, :, None] + w[:, :, None] * v[t][:, None, :]
+        score[t] = scale * np.einsum("hkm,hk->hm", Hk, q[t])
+        if p is None:
+            e = np.exp(score[t] - score[t].max(axis=-1, keepdims=True))
+            pw[t] = e / e.sum(axis=-1, keepdims=True)
+        else:
+            pw[t] = p[t]
+        o[t] = np.einsum("hmv,hm->hv", Hv, pw[t])
+        z[t] = zt
+        z_prev = zt
+    return {"score": score, "p": pw, "o": o, "z": z, "hk_final": Hk, "hv_final": Hv}
 
 
 def abc_recurrent_fp64(k, v, s, chunk: int = CHUNK, batches=None, heads=None) -> dict:

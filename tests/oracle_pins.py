@@ -530,3 +530,141 @@ def run_bwd_check(check, bwd_ref, gdr_ref, chunked_ref):
     if check in (check_bwd_write_vectors, check_bwd_chunk_relation):
         return check(bwd_ref, chunked_ref)
     return check(bwd_ref)
+
+
+# --------------------------------------------------------------------------- ABC reads and reverse recurrence
+def check_abc_resume(abc_ref):
+    """Resuming from the carried states and normaliser reproduces the whole run."""
+    T, H, K, M, V = 150, 2, 3, 4, 2
+    r = np.random.default_rng(97)
+    k = r.standard_normal((T, H, K))
+    v = r.standard_normal((T, H, V))
+    s = r.standard_normal((T, H, M)) * 2
+    z, hk_pre, hv_pre, hk, hv = abc_ref.abc_scan_sequence(k, v, s, 64)
+    t1 = 64
+    za, _, _, hka, hva = abc_ref.abc_scan_sequence(k[:t1], v[:t1], s[:t1], 64)
+    zb, hk_preb, hv_preb, hkb, hvb = abc_ref.abc_scan_sequence(k[t1:], v[t1:], s[t1:], 64, hka, hva, za[-1])
+    _assert_close(np.concatenate([za, zb]), z, 1e-13, "resumed normaliser")
+    _assert_close(hk_preb, hk_pre[1:], 1e-12, "resumed pre-chunk Hk")
+    _assert_close(hv_preb, hv_pre[1:], 1e-12, "resumed pre-chunk Hv")
+    _assert_close(hkb, hk, 1e-12, "resumed Hk")
+    _assert_close(hvb, hv, 1e-12, "resumed Hv")
+
+
+def check_abc_readout(abc_ref):
+    """The reads against the explicit weighted sums, and the softmax read with
+    constant logits: every slot holds the running mean, so the weights are
+    uniform and o_t is the running mean of v."""
+    T, H, K, M, V = 70, 2, 3, 4, 5
+    r = np.random.default_rng(98)
+    q = r.standard_normal((T, H, K))
+    k = r.standard_normal((T, H, K))
+    v = r.standard_normal((T, H, V))
+    s = r.standard_normal((T, H, M))
+    p = r.uniform(0.0, 1.0, (T, H, M))
+    out = abc_ref.abc_readout_sequence(q, k, v, s, p, 0.6)
+    zc = _cum_lse(s)
+    for t in (0, 1, 33, T - 1):
+        wts = np.exp(s[: t + 1] - zc[t][None])
+        hk = np.einsum("thk,thm->hkm", k[: t + 1], wts)
+        hv = np.einsum("thm,thv->hmv", wts, v[: t + 1])
+        _assert_close(out["score"][t], 0.6 * np.einsum("hkm,hk->hm", hk, q[t]), 1e-12, f"score {t}")
+        _assert_close(out["o"][t], np.einsum("hmv,hm->hv", hv, p[t]), 1e-12, f"o {t}")
+    sc = np.broadcast_to(r.standard_normal((1, H, M)), (T, H, M)).copy()
+    out = abc_ref.abc_readout_sequence(q, k, v, sc, None, 0.6)
+    n = np.arange(1, T + 1)[:, None, None]
+    mk = np.cumsum(k, axis=0) / n
+    mv = np.cumsum(v, axis=0) / n
+    _assert_close(out["score"], 0.6 * np.broadcast_to(np.einsum("thk,thk->th", mk, q)[:, :, None], (T, H, M)),
+                  1e-12, "running-mean scores")
+    _assert_close(out["p"], np.full((T, H, M), 1.0 / M), 1e-12, "uniform slot weights")
+    _assert_close(out["o"], mv, 1e-12, "running-mean output")
+
+
+def _abc_bwd_problem(seed, T, H=1, K=2, M=3, V=2):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((T, H, K))
+    k = r.standard_normal((T, H, K))
+    v = r.standard_normal((T, H, V))
+    s = r.standard_normal((T, H, M))
+    p = r.uniform(0.0, 1.0, (T, H, M))
+    dscore = r.standard_normal((T, H, M))
+    do = r.standard_normal((T, H, V))
+    ek = r.standard_normal((H, K, M))
+    ev = r.standard_normal((H, M, V))
+    return q, k, v, s, p, dscore, do, ek, ev
+
+
+def check_abc_bwd_boundaries(abc_bwd_ref, abc_ref):
+    """dhk[c], dhv[c] = gradients of the reads after chunk c (and of the final
+    states) with respect to the states they start from: finite differences of
+    the resumed forward read."""
+    chunk, T, scale = 3, 10, 0.6
+    q, k, v, s, p, dscore, do, ek, ev = _abc_bwd_problem(99, T)
+    dhk, dhv = abc_bwd_ref.abc_backward_sequence(q, s, p, dscore, do, ek, ev, scale, chunk)
+    zc = _cum_lse(s)
+    for c in range(dhk.shape[0]):
+        t0 = (c + 1) * chunk
+        if t0 >= T:
+            _assert_close(dhk[c], ek, 1e-12, "dhk after the last chunk")
+            _assert_close(dhv[c], ev, 1e-12, "dhv after the last chunk")
+            continue
+        sl = slice(t0, T)
+
+        def loss(xk, xv):
+            o = abc_ref.abc_readout_sequence(q[sl], k[sl], v[sl], s[sl], p[sl], scale, xk, xv, zc[t0 - 1])
+            return float(np.sum(o["score"] * dscore[sl]) + np.sum(o["o"] * do[sl])
+                         + np.sum(o["hk_final"] * ek) + np.sum(o["hv_final"] * ev))
+
+        zk, zv = np.zeros_like(ek), np.zeros_like(ev)
+        _assert_close(dhk[c], _fd(lambda x: loss(x, zv), zk), 1e-7, f"dhk[{c}] vs finite differences")
+        _assert_close(dhv[c], _fd(lambda x: loss(zk, x), zv), 1e-7, f"dhv[{c}] vs finite differences")
+
+
+def check_abc_bwd_running_mean(abc_bwd_ref):
+    """Constant logits: r_t = (t-1)/t (tokens counted from 1), so the state
+    after token e reaches token t > e scaled by e/t:
+    dhk after e = sum_{t>e} scale q_t dscore_t^T e/t + dhk_end e/T (and the
+    same with p_t do_t^T for dhv)."""
+    chunk, T, scale = 4, 11, 0.8
+    q, k, v, s, p, dscore, do, ek, ev = _abc_bwd_problem(100, T, H=2, K=3, M=2, V=4)
+    s = np.broadcast_to(s[:1], s.shape).copy()
+    dhk, dhv = abc_bwd_ref.abc_backward_sequence(q, s, p, dscore, do, ek, ev, scale, chunk)
+    for c in range(dhk.shape[0]):
+        e = min(T, (c + 1) * chunk)
+        rk = ek * e / T
+        rv = ev * e / T
+        for t in range(e + 1, T + 1):
+            rk = rk + scale * q[t - 1][:, :, None] * dscore[t - 1][:, None, :] * e / t
+            rv = rv + p[t - 1][:, :, None] * do[t - 1][:, None, :] * e / t
+        _assert_close(dhk[c], rk, 1e-12, f"running-mean dhk[{c}]")
+        _assert_close(dhv[c], rv, 1e-12, f"running-mean dhv[{c}]")
+
+
+def check_abc_bwd_chunk_relation(abc_bwd_ref):
+    """The reverse chunk step of the state walk, with zc the normaliser at
+    chunk ends:
+      dhk[c-1] = dhk[c] * exp(zc[c-1] - zc[c])[None, :] + scale Q_c^T (dscore_c * exp(zc[c-1] - z_t))
+      dhv[c-1] = exp(zc[c-1] - zc[c])[:, None] * dhv[c] + (p_c * exp(zc[c-1] - z_t))^T dO_c"""
+    C, T, scale = 64, 150, 0.7
+    q, k, v, s, p, dscore, do, ek, ev = _abc_bwd_problem(101, T, H=2, K=5, M=4, V=3)
+    dhk, dhv = abc_bwd_ref.abc_backward_sequence(q, s, p, dscore, do, ek, ev, scale, C)
+    z = _cum_lse(s)
+    for c in range(1, dhk.shape[0]):
+        c0, c1 = c * C, min(T, (c + 1) * C)
+        zp, zl = z[c0 - 1], z[c1 - 1]
+        x = np.exp(zp[None] - z[c0:c1])                          # [n, H, M]
+        rk = dhk[c] * np.exp(zp - zl)[:, None, :] + scale * np.einsum("thk,thm->hkm", q[c0:c1], dscore[c0:c1] * x)
+        rv = np.exp(zp - zl)[:, :, None] * dhv[c] + np.einsum("thm,thv->hmv", p[c0:c1] * x, do[c0:c1])
+        _assert_close(dhk[c - 1], rk, 1e-12, f"reverse chunk step dhk {c}")
+        _assert_close(dhv[c - 1], rv, 1e-12, f"reverse chunk step dhv {c}")
+
+
+ABC_READ_CHECKS = [check_abc_resume, check_abc_readout]
+ABC_BWD_CHECKS = [check_abc_bwd_boundaries, check_abc_bwd_running_mean, check_abc_bwd_chunk_relation]
+
+
+def run_abc_bwd_check(check, abc_bwd_ref, abc_ref):
+    if check is check_abc_bwd_boundaries:
+        return check(abc_bwd_ref, abc_ref)
+    return check(abc_bwd_ref)

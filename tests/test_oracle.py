@@ -5,7 +5,7 @@ forms, invariants)."""
 import pytest
 
 import oracle_pins as P
-from oracle import abc_ref, chunked_ref, gdr_bwd_ref, gdr_ref
+from oracle import abc_bwd_ref, abc_ref, chunked_ref, gdr_bwd_ref, gdr_ref
 
 
 @pytest.mark.parametrize("check", P.GDR_CHECKS, ids=lambda f: f.__name__)
@@ -25,3 +25,13 @@ def test_abc_oracle_pin(check):
 @pytest.mark.parametrize("check", P.BWD_CHECKS, ids=lambda f: f.__name__)
 def test_backward_oracle_pin(check):
     P.run_bwd_check(check, gdr_bwd_ref, gdr_ref, chunked_ref)
+
+
+@pytest.mark.parametrize("check", P.ABC_READ_CHECKS, ids=lambda f: f.__name__)
+def test_abc_read_oracle_pin(check):
+    check(abc_ref)
+
+
+@pytest.mark.parametrize("check", P.ABC_BWD_CHECKS, ids=lambda f: f.__name__)
+def test_abc_backward_oracle_pin(check):
+    P.run_abc_bwd_check(check, abc_bwd_ref, abc_ref)

@@ -77,6 +77,13 @@ ABC_MUTANTS = {
                               "        if t % chunk == 1:\n            hk_pre.append(Hk.copy())"),
     "weighted_scan_sign": ("Hk = Hk * r[t][None, :] + np.outer(k[t], w[t])",
                            "Hk = Hk * r[t][None, :] - np.outer(k[t], w[t])"),
+    "resume_ignores_normaliser": ("z_prev = np.full((H, M), -np.inf) if z0 is None else np.array(z0, dtype=np.float64)",
+                                  "z_prev = np.full((H, M), -np.inf)"),
+    "read_score_unscaled": ("score[t] = scale * np.einsum", "score[t] = np.einsum"),
+    "read_value_with_scores": ('o[t] = np.einsum("hmv,hm->hv", Hv, pw[t])', 'o[t] = np.einsum("hmv,hm->hv", Hv, score[t])'),
+    "read_softmax_unnormalised": ("pw[t] = e / e.sum(axis=-1, keepdims=True)", "pw[t] = e"),
+    "read_query_for_key": ('score[t] = scale * np.einsum("hkm,hk->hm", Hk, q[t])',
+                           'score[t] = scale * np.einsum("hkm,hk->hm", Hk, k[t])'),
 }
 
 
@@ -85,7 +92,7 @@ def test_abc_pins_catch(mut):
     old, new = ABC_MUTANTS[mut]
     m = _load_mutant("oracle/abc_ref.py", old, new, f"mut_abc_{mut}")
     failures = 0
-    for check in P.ABC_CHECKS:
+    for check in P.ABC_CHECKS + P.ABC_READ_CHECKS:
         try:
             check(m)
         except Exception:
@@ -121,6 +128,35 @@ def test_bwd_pins_catch(mut):
     for check in P.BWD_CHECKS:
         try:
             P.run_bwd_check(check, m, gdr_ref, chunked_ref)
+        except Exception:
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {mut}"
+
+
+ABC_BWD_MUTANTS = {
+    "abc_bwd_no_end_gradient": ("ck = np.zeros((H, K, M)) if dhk_end is None else np.array(dhk_end, dtype=np.float64)",
+                                "ck = np.zeros((H, K, M))"),
+    "abc_bwd_boundary_includes_own_read": ("dhk[t // chunk] = ck", "dhk[t // chunk] = ck + scale * q[t][:, :, None] * dscore[t][:, None, :]"),
+    "abc_bwd_dropped_scale": ("Gk = ck + scale * q[t]", "Gk = ck + q[t]"),
+    "abc_bwd_ratio_inverted": ("r = np.exp(zp - z[t])", "r = np.exp(z[t] - zp)"),
+    "abc_bwd_ratio_of_next_token": ("zp = z[t - 1] if t > 0 else z_before", "zp = z[t]"),
+    "abc_bwd_value_uses_scores": ("Gv = cv + p[t][:, :, None] * do[t][:, None, :]",
+                                  "Gv = cv + dscore[t][:, :, None] * do[t][:, None, :]"),
+    "abc_bwd_value_ratio_on_columns": ("cv = Gv * r[:, :, None]", "cv = Gv * r[:, :1, None]"),
+    "abc_bwd_key_ratio_on_rows": ("ck = Gk * r[:, None, :]", "ck = Gk * r[:, :1, None]"),
+}
+
+
+@pytest.mark.parametrize("mut", sorted(ABC_BWD_MUTANTS))
+def test_abc_bwd_pins_catch(mut):
+    from oracle import abc_ref
+
+    old, new = ABC_BWD_MUTANTS[mut]
+    m = _load_mutant("oracle/abc_bwd_ref.py", old, new, f"mut_abc_bwd_{mut}")
+    failures = 0
+    for check in P.ABC_BWD_CHECKS:
+        try:
+            P.run_abc_bwd_check(check, m, abc_ref)
         except Exception:
             failures += 1
     assert failures > 0, f"no pin caught mutation {mut}"
