@@ -240,6 +240,30 @@ gdr_status abc_affine_scan(const abc_problem* p, const void* k, const void* v, c
                            float* z, void* hk, void* hv, float* hk_final, float* hv_final,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* ABC reverse (dH) recurrence ([fla#23] "Problem": the reverse kernel that
+ * walks every state tile chunk by chunk; "Proposed Dataflow", item 4: the
+ * same producer / ordered-scan split for the reverse recurrence).  The slot
+ * states are read after every token as score_t = scale Hk_t^T q_t (M slot
+ * scores) and o_t = Hv_t^T p_t (V outputs).  Given the gradients dscore =
+ * dL/dscore and dO = dL/do (storage dtype) and of the final states (float32,
+ * nullable = zero), per chunk c ending at token e
+ *   dhk[c], dhv[c] = dL/d(state after chunk c) as the input of the tokens
+ *                    after it (the final states' gradient for the last chunk)
+ * by the reverse diagonal-affine walk, r_c = exp(zc[c-1] - zc[c]):
+ *   dhk[c-1] = dhk[c] * r_c[None, :] + scale Q_c^T (dscore_c * e^{zc[c-1] - z})
+ *   dhv[c-1] = r_c[:, None] * dhv[c] + (p_c * e^{zc[c-1] - z})^T dO_c
+ * Layouts: q [B, T, H, K], dscore, p [B, T, H, M], dO [B, T, H, V] (storage
+ * dtype); z [B, T, H, M] float32, the normaliser abc_affine_scan writes;
+ * dhk_final [B, H, K, M], dhv_final [B, H, M, V] float32 (nullable); outputs
+ * dhk [B, NC, H, K, M], dhv [B, NC, H, M, V] in the storage dtype.  Same
+ * shape support as abc_affine_scan; all pointers 16-byte aligned. */
+size_t abc_bwd_workspace_size(const abc_problem* p);
+
+gdr_status abc_affine_scan_bwd(const abc_problem* p, const void* q, const void* dscore, const void* pw,
+                               const void* dO, const float* z, const float* dhk_final, const float* dhv_final,
+                               float scale, void* dhk, void* dhv, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* Human-readable name of a status code. */
 const char* gdr_status_string(gdr_status s);
 /* Message of the last failed call on this thread ("" if none). */

@@ -7,6 +7,7 @@ from .binding import (  # noqa: F401
     GdrError,
     LIB_PATH,
     abc_affine_scan,
+    abc_affine_scan_bwd,
     abc_workspace_size,
     chunk_gated_delta_rule,
     gdr_chunk_dv_local,

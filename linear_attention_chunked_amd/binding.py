@@ -81,6 +81,9 @@ _SIGS = {
     "abc_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(abc_problem)]),
     "abc_affine_scan": (ctypes.c_int, [ctypes.POINTER(abc_problem), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
+    "abc_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(abc_problem)]),
+    "abc_affine_scan_bwd": (ctypes.c_int, [ctypes.POINTER(abc_problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                           _P, _P, _P, ctypes.c_size_t, _P]),
     "gdr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gdr_last_error": (ctypes.c_char_p, []),
     "gdr_plan_query": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile), ctypes.c_int32,
@@ -305,6 +308,26 @@ def abc_affine_scan(k, v, s, emit_z: bool = False, emit_final: bool = True, stre
     _check(L.abc_affine_scan(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(s), _ptr(z), _ptr(hk), _ptr(hv), _ptr(hkf),
                              _ptr(hvf), _ptr(ws), ws_bytes, _stream(stream)), "abc_affine_scan")
     return z, hk, hv, hkf, hvf
+
+
+def abc_affine_scan_bwd(q, dscore, p, dO, z, dhk_final=None, dhv_final=None, scale: float = 1.0, stream=None):
+    """Reverse (dH) walk of the ABC slot states.  Returns (dhk [B,NC,H,K,M],
+    dhv [B,NC,H,M,V]) in the storage dtype: the gradients of the states after
+    every chunk."""
+    B, T, H, K = q.shape
+    V = dO.shape[-1]
+    M = dscore.shape[-1]
+    NC = (T + 63) // 64
+    pr = abc_problem(B, T, H, K, M, V, _dtype_code(q.dtype))
+    L = lib()
+    ws_bytes = int(L.abc_bwd_workspace_size(ctypes.byref(pr)))
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    dhk = torch.empty((B, NC, H, K, M), dtype=q.dtype, device=q.device)
+    dhv = torch.empty((B, NC, H, M, V), dtype=q.dtype, device=q.device)
+    _check(L.abc_affine_scan_bwd(ctypes.byref(pr), _ptr(q), _ptr(dscore), _ptr(p), _ptr(dO), _ptr(z),
+                                 _ptr(dhk_final), _ptr(dhv_final), float(scale), _ptr(dhk), _ptr(dhv), _ptr(ws),
+                                 ws_bytes, _stream(stream)), "abc_affine_scan_bwd")
+    return dhk, dhv
 
 
 def gdr_chunk_dv_local(q, k, g_cum, dO, scale: float = 1.0, cu_seqlens=None, stream=None) -> torch.Tensor:

@@ -163,6 +163,66 @@ __global__ __launch_bounds__(256) void abc_weights(const AbcArgs a) {
   }
 }
 
+// Reverse weights, one workgroup per (b, chunk, h), thread = (token row, 8
+// slots): with zp = zc[c-1] (the forward's normaliser at the previous chunk's
+// last token; -inf for the first chunk, whose weights are then zero)
+//   Yk_t = scale dscore_t e^{zp - z_t},   Yv_t = p_t e^{zp - z_t}     (<= |.|)
+// in the storage dtype, and zc[c] = z at the chunk's last token.
+__global__ __launch_bounds__(256) void abc_bwd_weights(const AbcArgs a) {
+  const int bx = blockIdx.x;
+  const int h = bx % a.H;
+  const int c = (bx / a.H) % a.NC;
+  const int b = bx / (a.H * a.NC);
+  const int tid = threadIdx.x;
+  const int row = tid >> 3, cv = tid & 7;
+  const int n = min(kChunk, a.T - c * kChunk);
+  const int64_t H = a.H, M = a.M;
+  const int64_t tok0 = static_cast<int64_t>(b) * a.T + static_cast<int64_t>(c) * kChunk;
+  float zp[8];
+  if (c > 0) {
+    const float* q = a.z + ((tok0 - 1) * H + h) * M + 8 * cv;
+    const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(q);
+    const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(q + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      zp[j] = p0[j];
+      zp[4 + j] = p1[j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) zp[j] = -INFINITY;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = row + 32 * i;
+    if (r >= n) continue;
+    const int64_t off = ((tok0 + r) * H + h) * M + 8 * cv;
+    const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(a.z + off);
+    const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(a.z + off + 4);
+    const float zt[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
+    const u32x4_t dq = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.s) + off);
+    const u32x4_t pq = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.pw) + off);
+    const uint32_t dw[4] = {dq.x, dq.y, dq.z, dq.w};
+    const uint32_t pw[4] = {pq.x, pq.y, pq.z, pq.w};
+    uint32_t yk[4], yv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x0 = exp_fast(zp[2 * j] - zt[2 * j]);
+      const float x1 = exp_fast(zp[2 * j + 1] - zt[2 * j + 1]);
+      yk[j] = pack_bf16x2(a.scale * __builtin_bit_cast(float, dw[j] << 16) * x0,
+                          a.scale * __builtin_bit_cast(float, dw[j] & 0xffff0000u) * x1);
+      yv[j] = pack_bf16x2(__builtin_bit_cast(float, pw[j] << 16) * x0,
+                          __builtin_bit_cast(float, pw[j] & 0xffff0000u) * x1);
+    }
+    *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.e) + off) = u32x4_t{yk[0], yk[1], yk[2], yk[3]};
+    *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.e2) + off) = u32x4_t{yv[0], yv[1], yv[2], yv[3]};
+  }
+  if (tid < 16) {  // zc[c]: 64 slots, four per thread
+    const f32x4_t zl = *reinterpret_cast<const f32x4_t*>(a.z + ((tok0 + n - 1) * H + h) * M + 4 * tid);
+    *reinterpret_cast<f32x4_t*>(a.zc + ((static_cast<int64_t>(b) * a.NC + c) * H + h) * M + 4 * tid) = zl;
+  }
+}
+
 // ---------------------------------------------------------------- states
 // IS_K: the tile is XW rows (k) of Hk, held as Hk^T [slot][k]; otherwise XW
 // columns (v) of Hv, held as Hv^T [v][slot].  XW (64, 32 or 16) sets how many
@@ -179,7 +239,17 @@ __global__ __launch_bounds__(256) void abc_weights(const AbcArgs a) {
 // normalised at the run's last chunk).  MODE 0 walks run j from
 //   S_start(j) = sum_{i<j} L_i * exp(zc[end_i] - zc[start_j - 1])   (per slot)
 // storing the pre-chunk states; with P = 1 it is the plain serial walk.
-template <bool IS_K, int XW, int MODE>
+//
+// REV: the reverse (dH) walk.  Logical step j handles chunk NC-1-j; per step
+//   store dH[c]; dH <- dH * r_c + c'_c,  r_c = exp(zc[c-1] - zc[c]),
+//   key side c'_c = Q_c^T Yk, value side c'_c = Yv^T dO_c
+// with Yk = scale dscore e^{zc[c-1]-z}, Yv = p e^{zc[c-1]-z} from
+// abc_bwd_weights: the forward step with the chunk order reversed and other
+// operands, so the same code runs it.  The walk starts from the final
+// states' gradient; run j of MODE 0 starts from
+//   G_end e^{zc[p_j] - zc[NC-1]} + sum_{i<j} L_i e^{zc[p_j] - zc[a_i - 1]}
+// (p_j: run j's first chunk, a_i: run i's last, both in chunk order).
+template <bool IS_K, int XW, int MODE, bool REV>
 struct AbcStates {
   using S = St<bf16_t>;
   using frag = S::frag;
@@ -218,18 +288,25 @@ struct AbcStates {
     int vo_o[XB >= 16 ? XB / 16 : 1], lo_o[XB >= 16 ? XB / 16 : 1];  // write-out: global / staging
   };
 
+  // chunk of logical step c
+  __device__ static __forceinline__ int chunk_of(const AbcArgs& a, int c) { return REV ? a.NC - 1 - c : c; }
+
   __device__ static __forceinline__ void load(Stage& st, const Ctx& x, int c) {
     const AbcArgs& a = *x.a;
     const int64_t H = a.H;
-    const int64_t tok0 = static_cast<int64_t>(x.b) * a.T + static_cast<int64_t>(c) * kChunk;
-    const int n = min(kChunk, a.T - c * kChunk);
-    const bool any = n > 0 && c < x.c_hi;
+    const int pc = chunk_of(a, c);
+    const bool exists = pc >= 0 && pc < a.NC;
+    const bool any = exists && c < x.c_hi;
+    const int pcc = exists ? pc : 0;
+    const int n = min(kChunk, a.T - pcc * kChunk);
+    const int64_t tok0 = static_cast<int64_t>(x.b) * a.T + static_cast<int64_t>(pcc) * kChunk;
     const uint16_t* xp = static_cast<const uint16_t*>(IS_K ? a.k : a.v) + (tok0 * H + x.h) * x.X + x.x0;
-    const uint16_t* ep = static_cast<const uint16_t*>(a.e) + (tok0 * H + x.h) * a.M;
-    const float* lp = a.zc + ((static_cast<int64_t>(x.b) * a.NC + c) * H + x.h) * a.M;
+    const uint16_t* ep = static_cast<const uint16_t*>(IS_K ? a.e : a.e2) + (tok0 * H + x.h) * a.M;
+    const float* lp = a.zc + ((static_cast<int64_t>(x.b) * a.NC + pcc) * H + x.h) * a.M;
     const rsrc_t rx = make_rsrc(xp, any ? static_cast<uint32_t>(((n - 1) * H * x.X + XW) * 2) : 0u);
     const rsrc_t re = make_rsrc(ep, any ? static_cast<uint32_t>(((n - 1) * H * a.M + 64) * 2) : 0u);
-    const rsrc_t rl = make_rsrc(lp, any ? 256u : 0u);
+    // the reverse ratio of a run's last step needs zc of the chunk after the run
+    const rsrc_t rl = make_rsrc(lp, (REV ? exists : any) ? 256u : 0u);
     if constexpr (XB >= 16) {
 #pragma unroll
       for (int i = 0; i < XB / 16; ++i) st.x[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, x.vo_x[i], 0, 0);
@@ -258,7 +335,11 @@ struct AbcStates {
     const int row = tid >> 3, cv = tid & 7;
 #pragma unroll
     for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4_t*>(eb + (row + 32 * i) * STE + 16 * cv) = st.e[i];
-    if (tid < 64) sm.r[(c + 1) % 3][tid] = (c + 1 < x.c_hi) ? exp_fast(st.z - nxt.z) : 1.f;  // past the end: r = 1
+    if (REV) {  // this step's ratio, r_pc = exp(zc[pc-1] - zc[pc]); nothing precedes chunk 0
+      if (tid < 64) sm.r[c % 3][tid] = (c < x.c_hi) ? (chunk_of(a, c) > 0 ? exp_fast(nxt.z - st.z) : 0.f) : 1.f;
+    } else {
+      if (tid < 64) sm.r[(c + 1) % 3][tid] = (c + 1 < x.c_hi) ? exp_fast(st.z - nxt.z) : 1.f;  // past the end: r = 1
+    }
   }
 
   // The staged state of chunk c (written before the last barrier) goes out in
@@ -268,7 +349,7 @@ struct AbcStates {
     const AbcArgs& a = *x.a;
     const int64_t H = a.H, M = a.M;
     const bool live = MODE == 0 && c >= x.c_lo && c < x.c_hi;
-    const int64_t cc = live ? c : 0;
+    const int64_t cc = live ? chunk_of(a, c) : 0;
     const int64_t plane = static_cast<int64_t>(x.b * a.NC + cc) * H + x.h;
     uint16_t* hp = static_cast<uint16_t*>(IS_K ? a.hk : a.hv) +
                    (IS_K ? (plane * a.K + x.x0) * M : plane * M * a.V + x.x0);
@@ -334,7 +415,7 @@ struct AbcStates {
   // Per-slot factors of this lane's accumulator elements: Hk^T rows are slots
   // (4 per lane), Hv^T columns are slots (one per tile).
   __device__ static __forceinline__ void slot_scale(f32x4_t (&acc)[NR], const float* z_from, const float* z_to,
-                                                    const f32x4_t (&add)[NR], bool accumulate_add) {
+                                                    const f32x4_t (&add)[NR]) {
     const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int rt = IS_K ? wave : wave % NR;
@@ -419,7 +500,7 @@ struct AbcStates {
       return a.lsum + ((static_cast<int64_t>(b * a.H + h) * (a.P - 1) + run) * (a.K + a.V) * 64 +
                        static_cast<int64_t>(unit) * (XW * 64) + tid * 4 * NR);
     };
-    if (MODE == 0 && seg > 0) {
+    if (MODE == 0 && !REV && seg > 0) {
       // S_start(seg) from the earlier runs' end states
       const float* zrow = a.zc + (static_cast<int64_t>(b) * a.NC * a.H + h) * a.M;  // + c * H * M
       const int64_t zs = static_cast<int64_t>(a.H) * a.M;
@@ -431,7 +512,32 @@ struct AbcStates {
         const float* lp = lsum_at(i);
 #pragma unroll
         for (int j = 0; j < NR; ++j) l[j] = *reinterpret_cast<const f32x4_t*>(lp + 4 * j);
-        slot_scale(acc, zrow + end_i * zs, z_start, l, true);
+        slot_scale(acc, zrow + end_i * zs, z_start, l);
+      }
+    }
+    if (MODE == 0 && REV && x.c_lo < x.c_hi) {
+      // the final states' gradient and the later runs' end states, carried to
+      // this run's first chunk p = NC-1-c_lo
+      const float* zrow = a.zc + (static_cast<int64_t>(b) * a.NC * a.H + h) * a.M;
+      const int64_t zs = static_cast<int64_t>(a.H) * a.M;
+      const float* z_from = zrow + (a.NC - 1 - x.c_lo) * zs;
+      const float* ge = IS_K ? a.gk_end : a.gv_end;
+      if (ge != nullptr) {
+        const int64_t fb = static_cast<int64_t>(b) * a.H + h;
+        const float* gb = ge + (IS_K ? (fb * a.K + x0) * a.M : fb * a.M * a.V + x0);
+        f32x4_t l[NR];
+#pragma unroll
+        for (int j = 0; j < NR; ++j) l[j] = *reinterpret_cast<const f32x4_t*>(gb + x.vo_h[j] / 2);
+        slot_scale(acc, z_from, zrow + (a.NC - 1) * zs, l);
+      }
+      const int base = a.NC / a.P, extra = a.NC % a.P;
+      for (int i = 0; i < seg; ++i) {
+        const int hi_i = (i + 1) * base + min(i + 1, extra);  // run i's steps end here
+        f32x4_t l[NR];
+        const float* lp = lsum_at(i);
+#pragma unroll
+        for (int j = 0; j < NR; ++j) l[j] = *reinterpret_cast<const f32x4_t*>(lp + 4 * j);
+        slot_scale(acc, z_from, zrow + (a.NC - hi_i - 1) * zs, l);  // a_i - 1 = NC - hi_i - 1
       }
     }
 
@@ -440,7 +546,7 @@ struct AbcStates {
       Stage st[D];
 #pragma unroll
       for (int i = 0; i < D; ++i) load(st[i], x, x.c_lo + i);
-      if (tid < 64) {
+      if (!REV && tid < 64) {
         // r of the run's first chunk (0 at the sequence start: nothing before it)
         const float* zr = a.zc + ((static_cast<int64_t>(b) * a.NC + x.c_lo) * a.H + h) * a.M + tid;
         sm.r[x.c_lo % 3][tid] = x.c_lo == 0 ? 0.f : exp_fast(zr[-static_cast<int64_t>(a.H) * a.M] - zr[0]);
@@ -471,7 +577,7 @@ struct AbcStates {
       return;
     }
     float* fp = IS_K ? a.hk_final : a.hv_final;
-    if (fp == nullptr || x.c_hi != a.NC) return;
+    if (REV || fp == nullptr || x.c_hi != a.NC) return;
     const int64_t fb = static_cast<int64_t>(b) * a.H + h;
     float* base = fp + (IS_K ? (fb * a.K + x0) * a.M : fb * a.M * a.V + x0);
 #pragma unroll
@@ -479,10 +585,10 @@ struct AbcStates {
   }
 };
 
-template <int XW, int MODE>
+template <int XW, int MODE, bool REV>
 __global__ __launch_bounds__(256) void abc_states(const AbcArgs a) {
-  using SK = AbcStates<true, XW, MODE>;
-  using SV = AbcStates<false, XW, MODE>;
+  using SK = AbcStates<true, XW, MODE, REV>;
+  using SV = AbcStates<false, XW, MODE, REV>;
   static_assert(sizeof(typename SK::Smem) == sizeof(typename SV::Smem), "one LDS layout");
   __shared__ __align__(16) typename SK::Smem sm;
   const int nk = a.K / XW, tiles = nk + a.V / XW;
@@ -556,16 +662,39 @@ hipError_t launch_abc(const AbcArgs& a, hipStream_t stream) {
   const int pairs8 = (a.B * a.H + 7) / 8;
   if (a.P > 1) {  // end states of every run but the last
     const dim3 g1(8 * tiles_w * (a.P - 1) * pairs8);
-    if (xw == 64) hipLaunchKernelGGL((abc_states<64, 1>), g1, dim3(256), 0, stream, a);
-    else if (xw == 32) hipLaunchKernelGGL((abc_states<32, 1>), g1, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((abc_states<16, 1>), g1, dim3(256), 0, stream, a);
+    if (xw == 64) hipLaunchKernelGGL((abc_states<64, 1, false>), g1, dim3(256), 0, stream, a);
+    else if (xw == 32) hipLaunchKernelGGL((abc_states<32, 1, false>), g1, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((abc_states<16, 1, false>), g1, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const dim3 grid(8 * tiles_w * a.P * pairs8);
-  if (xw == 64) hipLaunchKernelGGL((abc_states<64, 0>), grid, dim3(256), 0, stream, a);
-  else if (xw == 32) hipLaunchKernelGGL((abc_states<32, 0>), grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL((abc_states<16, 0>), grid, dim3(256), 0, stream, a);
+  if (xw == 64) hipLaunchKernelGGL((abc_states<64, 0, false>), grid, dim3(256), 0, stream, a);
+  else if (xw == 32) hipLaunchKernelGGL((abc_states<32, 0, false>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((abc_states<16, 0, false>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_abc_bwd(const AbcArgs& a, hipStream_t stream) {
+  if (a.NC == 0) return hipSuccess;
+  hipLaunchKernelGGL(abc_bwd_weights, dim3(a.B * a.NC * a.H), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int xw = abc_tile_width(a);
+  const int tiles_w = (a.K + a.V) / xw;
+  const int pairs8 = (a.B * a.H + 7) / 8;
+  if (a.P > 1) {  // end states of every run but the last (in reverse chunk order)
+    const dim3 g1(8 * tiles_w * (a.P - 1) * pairs8);
+    if (xw == 64) hipLaunchKernelGGL((abc_states<64, 1, true>), g1, dim3(256), 0, stream, a);
+    else if (xw == 32) hipLaunchKernelGGL((abc_states<32, 1, true>), g1, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((abc_states<16, 1, true>), g1, dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid(8 * tiles_w * a.P * pairs8);
+  if (xw == 64) hipLaunchKernelGGL((abc_states<64, 0, true>), grid, dim3(256), 0, stream, a);
+  else if (xw == 32) hipLaunchKernelGGL((abc_states<32, 0, true>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((abc_states<16, 0, true>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

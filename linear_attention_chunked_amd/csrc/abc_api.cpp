@@ -110,6 +110,7 @@ gdr_status abc_affine_scan(const abc_problem* p, const void* k, const void* v, c
   a.NC = static_cast<int32_t>((p->T + 63) / 64);
   a.zc = a.lse + static_cast<int64_t>(a.B) * a.NC * a.H * a.M;
   a.e = a.zc + static_cast<int64_t>(a.B) * a.NC * a.H * a.M;
+  a.e2 = a.e;
   a.P = gdr::abc_segments(a.B, a.H, a.K, a.V, a.NC);
   {
     // after E (B*T*H*M bf16), rounded up to 16 bytes
@@ -120,6 +121,77 @@ gdr_status abc_affine_scan(const abc_problem* p, const void* k, const void* v, c
   hipError_t e = gdr::launch_abc(a, st);
   if (e != hipSuccess) {
     gdr_internal::set_last_error(std::string("abc launch: ") + hipGetErrorString(e));
+    return GDR_ERR_HIP;
+  }
+  return GDR_OK;
+}
+
+size_t abc_bwd_workspace_size(const abc_problem* p) {
+  std::string err;
+  if (!abc_valid(p, err)) return 0;
+  const int64_t nc = (p->T + 63) / 64;
+  // chunk-end normalisers (FP32), the two weight tensors (storage dtype),
+  // then the end states of the reverse walk's runs (FP32)
+  const int P = gdr::abc_segments(p->B, p->H, p->K, p->V, static_cast<int>(nc));
+  return static_cast<size_t>(p->B) * nc * p->H * p->M * sizeof(float) +
+         2 * static_cast<size_t>(p->B) * p->T * p->H * p->M * 2 +
+         static_cast<size_t>(p->B) * p->H * (P - 1) * (p->K + p->V) * p->M * sizeof(float);
+}
+
+gdr_status abc_affine_scan_bwd(const abc_problem* p, const void* q, const void* dscore, const void* pw,
+                               const void* dO, const float* z, const float* dhk_final, const float* dhv_final,
+                               float scale, void* dhk, void* dhv, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  std::string err;
+  if (!abc_valid(p, err)) {
+    gdr_internal::set_last_error(err);
+    return GDR_ERR_INVALID_ARG;
+  }
+  const void* req[] = {q, dscore, pw, dO, z, dhk, dhv, workspace};
+  const char* names[] = {"q", "dscore", "p", "dO", "z", "dhk", "dhv", "workspace"};
+  for (int i = 0; i < 8; ++i) {
+    if (req[i] == nullptr || !aligned16(req[i])) {
+      gdr_internal::set_last_error(std::string(names[i]) + " must be non-NULL and 16-byte aligned");
+      return GDR_ERR_INVALID_ARG;
+    }
+  }
+  if ((dhk_final != nullptr && !aligned16(dhk_final)) || (dhv_final != nullptr && !aligned16(dhv_final))) {
+    gdr_internal::set_last_error("final-state gradients must be 16-byte aligned");
+    return GDR_ERR_INVALID_ARG;
+  }
+  if (workspace_bytes < abc_bwd_workspace_size(p)) {
+    gdr_internal::set_last_error("workspace smaller than abc_bwd_workspace_size()");
+    return GDR_ERR_INVALID_ARG;
+  }
+  gdr::AbcArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = q;
+  a.v = dO;
+  a.s = dscore;
+  a.pw = pw;
+  a.z = const_cast<float*>(z);
+  a.hk = dhk;
+  a.hv = dhv;
+  a.gk_end = dhk_final;
+  a.gv_end = dhv_final;
+  a.scale = scale;
+  a.B = p->B;
+  a.T = static_cast<int32_t>(p->T);
+  a.H = p->H;
+  a.K = p->K;
+  a.M = p->M;
+  a.V = p->V;
+  a.NC = static_cast<int32_t>((p->T + 63) / 64);
+  a.zc = static_cast<float*>(workspace);
+  const int64_t nzc = static_cast<int64_t>(a.B) * a.NC * a.H * a.M;
+  const int64_t nw = static_cast<int64_t>(a.B) * a.T * a.H * a.M;
+  a.e = a.zc + nzc;
+  a.e2 = static_cast<uint16_t*>(a.e) + nw;
+  a.lsum = reinterpret_cast<float*>(static_cast<uint16_t*>(a.e2) + nw);
+  a.P = gdr::abc_segments(a.B, a.H, a.K, a.V, a.NC);
+  hipError_t e = gdr::launch_abc_bwd(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    gdr_internal::set_last_error(std::string("abc reverse launch: ") + hipGetErrorString(e));
     return GDR_ERR_HIP;
   }
   return GDR_OK;

@@ -83,19 +83,28 @@ struct ComposeArgs {
   int32_t state_vk;
 };
 
+// Forward (slot-state construction) and reverse (dH recurrence) share the
+// state walk.  Reverse: k = q, v = dO, s = dscore, pw = p; z is the
+// forward's normaliser (input); e / e2 hold the key- / value-side weights;
+// hk / hv receive dhk / dhv; gk_end / gv_end are the final states' gradients.
 struct AbcArgs {
   const void* k;
   const void* v;
   const void* s;
-  float* z;            // nullable full normaliser
+  const void* pw;      // reverse: slot weights of the value read
+  float* z;            // forward: nullable full normaliser (output); reverse: input
   float* lse;          // workspace: [B, NC, H, M] log-sum-exp of each chunk
   float* zc;           // workspace: [B, NC, H, M] normaliser at chunk ends
-  void* e;             // workspace: [B, T, H, M] weights exp(s - zc), storage dtype
+  void* e;             // workspace: [B, T, H, M] key-side weights, storage dtype
+  void* e2;            // workspace: value-side weights (the forward: == e)
   float* lsum;         // workspace: [B*H, P-1, K+V, M] end states of the runs (P > 1)
   void* hk;
   void* hv;
   float* hk_final;
   float* hv_final;
+  const float* gk_end;  // reverse: nullable [B, H, K, M]
+  const float* gv_end;  // reverse: nullable [B, H, M, V]
+  float scale;          // reverse: score scale
   int32_t B;
   int32_t T;
   int32_t H, K, M, V;
@@ -116,6 +125,7 @@ LaunchFn find_compose(int dk);
 LaunchFn find_dv_local(int dk, int dv);
 LaunchFn find_scan_bwd(int dk);
 hipError_t launch_abc(const AbcArgs& a, hipStream_t s);
+hipError_t launch_abc_bwd(const AbcArgs& a, hipStream_t s);
 int abc_segments(int B, int H, int K, int V, int NC);
 
 }  // namespace gdr

@@ -183,3 +183,20 @@ def test_reverse_pass_validation():
     pp, keep2 = _pool_prob([3, 0, 2], 4)
     assert L.gdr_state_scan_bwd(ctypes.byref(pp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, ctypes.c_float(1.0),
                                 FAKE, FAKE, FAKE, None) == B.GDR_ERR_UNSUPPORTED
+
+
+def test_abc_reverse_validation():
+    L = B.lib()
+    p = B.abc_problem(1, 128, 2, 64, 64, 64, B.GDR_BF16)
+    ws = L.abc_bwd_workspace_size(ctypes.byref(p))
+    assert ws >= 128 * 2 * 64 * 2 * 2
+    args = [FAKE] * 5 + [None, None, ctypes.c_float(1.0), FAKE, FAKE, FAKE, ws, None]
+    bad = list(args)
+    bad[4] = None  # z is required
+    assert L.abc_affine_scan_bwd(ctypes.byref(p), *bad) == B.GDR_ERR_INVALID_ARG
+    assert "z" in L.gdr_last_error().decode()
+    small = list(args)
+    small[11] = ws - 1
+    assert L.abc_affine_scan_bwd(ctypes.byref(p), *small) == B.GDR_ERR_INVALID_ARG
+    p32 = B.abc_problem(1, 128, 2, 64, 64, 64, B.GDR_F32)
+    assert L.abc_affine_scan_bwd(ctypes.byref(p32), *args) == B.GDR_ERR_INVALID_ARG
