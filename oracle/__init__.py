@@ -35,7 +35,7 @@ from .gdr_ref import (  # noqa: F401
     gdr_segment_summaries_fp64,
     gdr_segment_compose_fp64,
 )
-from .abc_ref import abc_readout_sequence, abc_recurrent_fp64, abc_scan_sequence, abc_weighted_scan  # noqa: F401
+from .abc_ref import abc_forward_fp64, abc_readout_sequence, abc_recurrent_fp64, abc_scan_sequence, abc_weighted_scan  # noqa: F401
 from .abc_bwd_ref import abc_backward_fp64, abc_backward_sequence  # noqa: F401
 from .chunked_ref import gdr_chunked_fp64, chunked_scan_sequence, chunk_factors  # noqa: F401
 from .gdr_bwd_ref import gdr_backward_fp64, gdr_backward_sequence  # noqa: F401

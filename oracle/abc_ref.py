@@ -130,6 +130,21 @@ def abc_recurrent_fp64(k, v, s, chunk: int = CHUNK, batches=None, heads=None) ->
     }
 
 
+def abc_forward_fp64(q, k, v, s, scale: float = 1.0, p=None, batches=None, heads=None) -> dict:
+    """The ABC read over a dense [B, T, H, *] problem (``abc_readout_sequence``
+    per batch row; softmax slot weights unless ``p`` is given).  ``batches`` /
+    ``heads`` restrict to a sample.  Returns float64 o [B', T, H', V] and
+    p [B', T, H', M]."""
+    q, k, v, s = (np.asarray(x, dtype=np.float64) for x in (q, k, v, s))
+    B = k.shape[0]
+    bs = list(range(B)) if batches is None else list(batches)
+    hs = list(range(k.shape[2])) if heads is None else list(heads)
+    outs = [abc_readout_sequence(q[b][:, hs], k[b][:, hs], v[b][:, hs], s[b][:, hs],
+                                 None if p is None else np.asarray(p[b], dtype=np.float64)[:, hs], scale)
+            for b in bs]
+    return {"o": np.stack([x["o"] for x in outs]), "p": np.stack([x["p"] for x in outs])}
+
+
 def abc_weighted_scan(k, v, w, r, chunk: int = CHUNK):
     """The same state update with the weights given directly (no exp/log).
 
