@@ -240,6 +240,20 @@ gdr_status abc_affine_scan(const abc_problem* p, const void* k, const void* v, c
                            float* z, void* hk, void* hv, float* hk_final, float* hv_final,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* ABC read per 64-token chunk ([fla#23] "Problem": chunk_abc, the operator
+ * whose forward reads the slot states).  After token t's update the states
+ * are read as score_t = scale Hk_t^T q_t, p_t = softmax over the M slots of
+ * score_t, o_t = Hv_t^T p_t; per chunk this combines the pre-chunk states
+ * hk[c], hv[c] with the chunk's own tokens.  Inputs: q, k [B, T, H, K],
+ * v [B, T, H, V], s [B, T, H, M] (storage dtype), z [B, T, H, M] float32 and
+ * hk [B, NC, H, K, M], hv [B, NC, H, M, V] as abc_affine_scan writes them.
+ * Outputs: o [B, T, H, V] (storage dtype); p_out (nullable) [B, T, H, M] the
+ * slot weights.  Bfloat16 storage, M = 64, (K, V) in {(64, 128), (128, 128),
+ * (128, 256), (256, 256), (256, 512)} (else GDR_ERR_UNSUPPORTED). */
+gdr_status abc_chunk_output(const abc_problem* p, const void* q, const void* k, const void* v, const void* s,
+                            const float* z, const void* hk, const void* hv, float scale, void* o, void* p_out,
+                            void* stream);
+
 /* ABC reverse (dH) recurrence ([fla#23] "Problem": the reverse kernel that
  * walks every state tile chunk by chunk; "Proposed Dataflow", item 4: the
  * same producer / ordered-scan split for the reverse recurrence).  The slot

@@ -8,6 +8,8 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     abc_affine_scan,
     abc_affine_scan_bwd,
+    abc_chunk_output,
+    abc_forward,
     abc_workspace_size,
     chunk_gated_delta_rule,
     gdr_chunk_dv_local,

@@ -82,6 +82,8 @@ _SIGS = {
     "abc_affine_scan": (ctypes.c_int, [ctypes.POINTER(abc_problem), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
     "abc_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(abc_problem)]),
+    "abc_chunk_output": (ctypes.c_int, [ctypes.POINTER(abc_problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P,
+                                        _P, _P]),
     "abc_affine_scan_bwd": (ctypes.c_int, [ctypes.POINTER(abc_problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                            _P, _P, _P, ctypes.c_size_t, _P]),
     "gdr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -308,6 +310,27 @@ def abc_affine_scan(k, v, s, emit_z: bool = False, emit_final: bool = True, stre
     _check(L.abc_affine_scan(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(s), _ptr(z), _ptr(hk), _ptr(hv), _ptr(hkf),
                              _ptr(hvf), _ptr(ws), ws_bytes, _stream(stream)), "abc_affine_scan")
     return z, hk, hv, hkf, hvf
+
+
+def abc_chunk_output(q, k, v, s, z, hk, hv, scale: float = 1.0, emit_p: bool = False, stream=None):
+    """ABC read per chunk.  Returns (o [B,T,H,V], p [B,T,H,M] | None)."""
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    M = s.shape[-1]
+    pr = abc_problem(B, T, H, K, M, V, _dtype_code(q.dtype))
+    o = torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
+    p = torch.empty((B, T, H, M), dtype=q.dtype, device=q.device) if emit_p else None
+    _check(lib().abc_chunk_output(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(z), _ptr(hk), _ptr(hv),
+                                  float(scale), _ptr(o), _ptr(p), _stream(stream)), "abc_chunk_output")
+    return o, p
+
+
+def abc_forward(q, k, v, s, scale: float = 1.0, emit_p: bool = False, stream=None):
+    """The whole ABC forward: normaliser and slot states (abc_affine_scan),
+    then the chunk read.  Returns (o, p | None, z, hk, hv)."""
+    z, hk, hv, _, _ = abc_affine_scan(k, v, s, emit_z=True, emit_final=False, stream=stream)
+    o, p = abc_chunk_output(q, k, v, s, z, hk, hv, scale, emit_p, stream)
+    return o, p, z, hk, hv
 
 
 def abc_affine_scan_bwd(q, dscore, p, dO, z, dhk_final=None, dhv_final=None, scale: float = 1.0, stream=None):

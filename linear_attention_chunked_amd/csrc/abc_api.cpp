@@ -126,6 +126,56 @@ gdr_status abc_affine_scan(const abc_problem* p, const void* k, const void* v, c
   return GDR_OK;
 }
 
+gdr_status abc_chunk_output(const abc_problem* p, const void* q, const void* k, const void* v, const void* s,
+                            const float* z, const void* hk, const void* hv, float scale, void* o, void* p_out,
+                            void* stream) {
+  std::string err;
+  if (!abc_valid(p, err)) {
+    gdr_internal::set_last_error(err);
+    return GDR_ERR_INVALID_ARG;
+  }
+  if (!gdr::abc_out_supported(p->K, p->V)) {
+    gdr_internal::set_last_error("abc_chunk_output is built for (K, V) in {(64,128), (128,128), (128,256), (256,256), (256,512)}");
+    return GDR_ERR_UNSUPPORTED;
+  }
+  const void* req[] = {q, k, v, s, z, hk, hv, o};
+  const char* names[] = {"q", "k", "v", "s", "z", "hk", "hv", "o"};
+  for (int i = 0; i < 8; ++i) {
+    if (req[i] == nullptr || !aligned16(req[i])) {
+      gdr_internal::set_last_error(std::string(names[i]) + " must be non-NULL and 16-byte aligned");
+      return GDR_ERR_INVALID_ARG;
+    }
+  }
+  if (p_out != nullptr && !aligned16(p_out)) {
+    gdr_internal::set_last_error("p must be 16-byte aligned");
+    return GDR_ERR_INVALID_ARG;
+  }
+  gdr::AbcOutArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.s = s;
+  a.z = z;
+  a.hk = hk;
+  a.hv = hv;
+  a.o = o;
+  a.p = p_out;
+  a.scale = scale;
+  a.B = p->B;
+  a.T = static_cast<int32_t>(p->T);
+  a.H = p->H;
+  a.K = p->K;
+  a.V = p->V;
+  a.NC = static_cast<int32_t>((p->T + 63) / 64);
+  hipError_t e = gdr::launch_abc_out(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    gdr_internal::set_last_error(std::string("abc read launch: ") + hipGetErrorString(e));
+    return GDR_ERR_HIP;
+  }
+  return GDR_OK;
+}
+
 size_t abc_bwd_workspace_size(const abc_problem* p) {
   std::string err;
   if (!abc_valid(p, err)) return 0;

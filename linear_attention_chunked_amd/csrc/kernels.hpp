@@ -126,6 +126,23 @@ LaunchFn find_dv_local(int dk, int dv);
 LaunchFn find_scan_bwd(int dk);
 hipError_t launch_abc(const AbcArgs& a, hipStream_t s);
 hipError_t launch_abc_bwd(const AbcArgs& a, hipStream_t s);
+
+// ABC read per chunk: scores, softmax over the slots, value read.
+struct AbcOutArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* s;
+  const float* z;      // the forward's normaliser [B, T, H, M]
+  const void* hk;      // [B, NC, H, K, M]
+  const void* hv;      // [B, NC, H, M, V]
+  void* o;             // [B, T, H, V]
+  void* p;             // nullable [B, T, H, M]
+  float scale;
+  int32_t B, T, H, K, V, NC;
+};
+bool abc_out_supported(int K, int V);
+hipError_t launch_abc_out(const AbcOutArgs& a, hipStream_t s);
 int abc_segments(int B, int H, int K, int V, int NC);
 
 }  // namespace gdr

@@ -200,3 +200,15 @@ def test_abc_reverse_validation():
     assert L.abc_affine_scan_bwd(ctypes.byref(p), *small) == B.GDR_ERR_INVALID_ARG
     p32 = B.abc_problem(1, 128, 2, 64, 64, 64, B.GDR_F32)
     assert L.abc_affine_scan_bwd(ctypes.byref(p32), *args) == B.GDR_ERR_INVALID_ARG
+
+
+def test_abc_read_validation():
+    L = B.lib()
+    p = B.abc_problem(1, 128, 2, 64, 64, 64, B.GDR_BF16)  # V = 64 is not built
+    args = [FAKE] * 7 + [ctypes.c_float(1.0), FAKE, None, None]
+    assert L.abc_chunk_output(ctypes.byref(p), *args) == B.GDR_ERR_UNSUPPORTED
+    p = B.abc_problem(1, 128, 2, 256, 64, 512, B.GDR_BF16)
+    bad = list(args)
+    bad[4] = None  # z
+    assert L.abc_chunk_output(ctypes.byref(p), *bad) == B.GDR_ERR_INVALID_ARG
+    assert "z" in L.gdr_last_error().decode()
