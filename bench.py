@@ -348,9 +348,35 @@ def abc_affine(pkg, torch, dev):
     k, v, s = (x.to(dev) for x in (inp.k, inp.v, inp.s))
     us = _event_median_us(torch, lambda: pkg.abc_affine_scan(k, v, s))
     alg = abc_alg_bytes(inp.B, inp.T, inp.H, inp.K, inp.M, inp.V)
+    # the reverse (dH) walk on the same shape: seeded q, slot weights, score
+    # and output gradients (bf16), final-state gradients (fp32)
+    import numpy as np
+
+    r = np.random.default_rng(11)
+    B, T, H, K, M, V = inp.B, inp.T, inp.H, inp.K, inp.M, inp.V
+    bf = torch.bfloat16
+
+    def draw(*shape, dt=bf, sc=1.0):
+        return torch.from_numpy((sc * r.standard_normal(shape)).astype(np.float32)).to(dt).to(dev)
+
+    q, ds, dO = draw(B, T, H, K), draw(B, T, H, M), draw(B, T, H, V)
+    p = torch.softmax(draw(B, T, H, M, dt=torch.float32), dim=-1).to(bf)
+    ek, ev = draw(B, H, K, M, dt=torch.float32, sc=0.1), draw(B, H, M, V, dt=torch.float32, sc=0.1)
+    z = pkg.abc_affine_scan(k, v, s, emit_z=True)[0]
+    rus = _event_median_us(torch, lambda: pkg.abc_affine_scan_bwd(q, ds, p, dO, z, ek, ev, 1.0))
+    ralg = abc_bwd_alg_bytes(B, T, H, K, M, V)
     return {"workload": "abc_affine (B=2, T=16384, H=4, K=256, M=64, V=512, bf16)", "us": round(us, 1),
             "Mtok_head_per_s": round(inp.token_heads / us, 1), "alg_bytes": alg,
-            "frac_of_hbm": round(alg / (us * 1e-6) / 8e12, 4)}
+            "frac_of_hbm": round(alg / (us * 1e-6) / 8e12, 4),
+            "reverse": {"us": round(rus, 1), "alg_bytes": ralg, "frac_of_hbm": round(ralg / (rus * 1e-6) / 8e12, 4)}}
+
+
+def abc_bwd_alg_bytes(B, T, H, K, M, V):
+    """Reverse walk: read q, dscore, p, dO (bf16) and z (fp32) once, the final
+    states' gradients (fp32); write dhk, dhv after every chunk (bf16)."""
+    nc = (T + 63) // 64
+    return (B * T * H * ((K + 2 * M + V) * 2 + M * 4) + B * nc * H * (K * M + M * V) * 2
+            + B * H * (K * M + M * V) * 4)
 
 
 def reverse_alg_bytes(lengths, H, DK, DV, nt, has_dhT):
