@@ -84,7 +84,7 @@ gdr_status hip_fail(hipError_t e, const char* what) {
 gdr_status run_scan(const gdr::Problem& pr, const gdr::Tile& t, int mode, int P, const void* k, const void* w,
                     const void* u, const float* g_cum, const float* h_in, int in_vk, void* h, void* v_new,
                     float* h_out, int out_vk, float* trans_out, hipStream_t stream) {
-  const int kmode = (mode == 1) ? 1 : 0;
+  const int kmode = (mode == 1) ? gdr::summary_kernel_mode(pr) : 0;
   gdr::LaunchFn fn = gdr::find_scan(pr.dtype, pr.DK, t.bv, t.waves, t.stages, kmode);
   if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no scan kernel for this dtype/DK/tile");
   const bool has_in = (h_in != nullptr);
@@ -105,7 +105,7 @@ gdr_status run_scan(const gdr::Problem& pr, const gdr::Tile& t, int mode, int P,
   a.DV = pr.DV;
   a.in_vk = in_vk;
   a.out_vk = out_vk;
-  a.n_blk = (kmode == 1) ? (pr.DV + pr.DK) / t.bv : pr.DV / t.bv;
+  a.n_blk = gdr::scan_blocks(pr, t, mode);
   for (const gdr::Launch& l : plan) {
     if (l.grid == 0) continue;
     a.n_rows = static_cast<int32_t>(l.rows.size());
@@ -363,7 +363,7 @@ gdr_status gdr_segment_compose(const gdr_problem* p, int32_t n_segments, const f
   GDR_TRY(need(seg_init, "seg_init"));
   GDR_TRY(opt(h0, "h0"));
   GDR_TRY(opt(hT, "hT"));
-  gdr::LaunchFn fn = gdr::find_compose(pr.DK);
+  gdr::LaunchFn fn = gdr::find_compose(pr.DK, n_segments);
   if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no compose kernel for this DK");
   if (pr.N == 0) return GDR_OK;
   gdr::ComposeArgs a;

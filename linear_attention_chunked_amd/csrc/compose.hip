@@ -7,88 +7,122 @@
 // One workgroup per (sequence, head, 16 value columns) with one wave per 16
 // rows of the state (DK/16 waves).  Wave w keeps its rows of the running
 // state in FP32 accumulator registers and produces its rows of the next one
-// with FP32 MFMA (v_mfma_f32_16x16x4_f32, one independent accumulator per
-// 32-wide k-step so the products overlap): the A operand is its 16 rows of M_s,
-// read straight from global memory, the B operand the whole current state,
-// shared through LDS (double-buffered, one barrier per segment).
+// with FP32 MFMA (v_mfma_f32_16x16x4_f32, 2 DK/32 independent accumulator
+// chains of four products, summed by a pairwise tree): the A operand is its
+// 16 rows of M_s, the B operand the whole current state, shared through LDS
+// (double-buffered, one barrier per segment).
 //
-// The chain is latency-bound (a few dozen workgroups, one product per
-// segment), so the operands of segment s+2 are requested while segment s
-// computes: three register sets rotate through an unrolled loop, and each
-// set's loads are issued ahead of the state stores so that waiting for them
-// never waits for a store.  The workgroups of one (sequence, head) share an
-// XCD (blockIdx modulo 8), so M_s and S_loc(s) come from HBM once per XCD and
-// from that XCD's L2 for the other column blocks.
+// What bounds the chain is moving M_s (DK x DK FP32 per segment) into every
+// workgroup.  An A fragment gives each of 16 lanes a different row, so
+// reading it straight from global memory touches 16 rows per instruction;
+// instead each wave reads its 16 rows as one contiguous block (every load
+// instruction covers whole consecutive 16-byte pieces), stages them in its
+// own LDS region with rows padded by 16 bytes (the fragment reads of 16 rows
+// at one column then fall in distinct banks), and reads the fragments from
+// there.  The wave's region is private, so staging needs no barrier.
+// Pipeline per segment s: the loads of M_{s+2} are issued, the fragments of
+// M_s are read from LDS buffer s & 1, the products run, M_{s+1} (loaded one
+// segment earlier) is staged into buffer (s+1) & 1, and the state is
+// exchanged.  All global accesses go through buffer resources built per
+// segment in scalar registers with per-lane offsets fixed for the whole
+// chain.  With 16 segments (the split of the long-sequence workloads) the
+// chain is straight-line code, so every wait count is exact; other counts
+// run the same steps in a loop.  The workgroups of one (sequence, head)
+// share an XCD (blockIdx modulo 8), so M_s and S_loc(s) come from HBM once
+// per XCD and from that XCD's L2 for the other column blocks.
+#include "gfx950.hpp"
 #include "kernels.hpp"
 
 namespace gdr {
 
-template <int DK>
+template <int DK, int PFIX>
 struct ComposeKernel {
   using S = St<float>;
   using frag = S::frag;
   static constexpr int BVC = 16;
   static constexpr int NW = DK / 16;
   static constexpr int KS = DK / 32;
-  static constexpr int LDS_ = DK + 4;
+  static constexpr int LDS_ = DK + 4;          // state exchange: one value column per row
+  static constexpr int LDM = DK + 4;           // staged M rows (floats), padded by 16 bytes
+  static constexpr int MPW = 16 * DK / 4 / 64; // 16-byte pieces of the wave's 16 rows per lane
+  static constexpr int QPR = DK / 4;           // 16-byte pieces per row
 
   struct Smem {
     float s[2][BVC * LDS_];
+    float m[2][NW][16 * LDM];
   };
 
   struct Ops {
-    frag m[KS];  // this lane's part of the wave's 16 rows of M_s
-    f32x4_t l;   // this lane's four rows of S_loc(s) in its column
+    u32x4_t m[MPW];  // this lane's pieces of the wave's 16 rows of M_s (piece i*64 + lane)
+    f32x4_t l;       // this lane's four rows of S_loc(s) in its column
   };
 
   struct Ctx {
     const ComposeArgs* a;
     int64_t n, hd, H;
-    int col, row0, wave, g4, c16;
+    int col, row0, wave, g4, c16, lane;
+    int vo_s;   // byte offset of this lane's four state rows within a segment-head block
   };
 
   __device__ static __forceinline__ void load(Ops& o, const Ctx& x, int s) {
     const ComposeArgs& a = *x.a;
     const int64_t seg = x.n * a.P + s;
-    const float* mr = a.seg_trans + (seg * x.H + x.hd) * DK * DK + static_cast<int64_t>(16 * x.wave + x.c16) * DK;
+    // the wave's 16 rows: one contiguous 16 * DK * 4-byte block
+    const rsrc_t rm = make_rsrc(a.seg_trans + ((seg * x.H + x.hd) * DK + 16 * x.wave) * DK, 16 * DK * 4);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(mr + 32 * ks + 4 * x.g4);
-      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(mr + 32 * ks + 16 + 4 * x.g4);
-      o.m[ks] = S::frag_from_f32(x0, x1);
-    }
-    o.l = *reinterpret_cast<const f32x4_t*>(a.seg_state + (seg * x.H + x.hd) * a.DV * DK +
-                                            static_cast<int64_t>(x.col) * DK + x.row0);
+    for (int i = 0; i < MPW; ++i) o.m[i] = __builtin_amdgcn_raw_buffer_load_b128(rm, 16 * x.lane, 1024 * i, 0);
+    const rsrc_t rs = make_rsrc(a.seg_state + (seg * x.H + x.hd) * a.DV * DK, static_cast<uint32_t>(a.DV * DK * 4));
+    o.l = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, x.vo_s, 0, 0));
   }
 
-  // Segment s: operands in `cur_ops`, requests segment s+2 into `next2`.
-  __device__ static __forceinline__ void step(f32x4_t& cur, const Ops& ops, Ops& next2, const Ctx& x, int s,
-                                              Smem& sm) {
+  // M pieces -> the wave's LDS region (row-major, padded rows)
+  __device__ static __forceinline__ void stage(const Ops& o, const Ctx& x, Smem& sm, int buf) {
+    float* mb = sm.m[buf][x.wave];
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) {
+      const int p = 64 * i + x.lane;
+      *reinterpret_cast<u32x4_t*>(mb + (p / QPR) * LDM + 4 * (p % QPR)) = o.m[i];
+    }
+  }
+
+  // Segment s: M_s fragments from LDS buffer s & 1, S_loc(s) from `ops`;
+  // requests segment s+2 into `next2`, stages segment s+1 from `next1`.
+  __device__ static __forceinline__ void step(f32x4_t& cur, const Ops& ops, const Ops& next1, Ops& next2,
+                                              const Ctx& x, int s, Smem& sm) {
     const ComposeArgs& a = *x.a;
     // unconditional (the last segment is re-read near the end), so every step
     // issues the same loads and the compiler's wait counts stay two steps deep
     load(next2, x, min(s + 2, a.P - 1));
     const int64_t seg = x.n * a.P + s;
-    *reinterpret_cast<f32x4_t*>(a.seg_init + (seg * x.H + x.hd) * a.DV * DK + static_cast<int64_t>(x.col) * DK +
-                                x.row0) = cur;
+    const rsrc_t ri = make_rsrc(a.seg_init + (seg * x.H + x.hd) * a.DV * DK, static_cast<uint32_t>(a.DV * DK * 4));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, cur), ri, x.vo_s, 0, 0);
     const float* sb = &sm.s[s & 1][x.c16 * LDS_ + 4 * x.g4];
-    frag bs[KS];
+    const float* mb = &sm.m[s & 1][x.wave][x.c16 * LDM + 4 * x.g4];
+    frag bs[KS], am[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
+      am[ks] = S::frag_from_f32(*reinterpret_cast<const f32x4_t*>(mb + 32 * ks),
+                                *reinterpret_cast<const f32x4_t*>(mb + 32 * ks + 16));
       bs[ks] = S::frag_from_f32(*reinterpret_cast<const f32x4_t*>(sb + 32 * ks),
                                 *reinterpret_cast<const f32x4_t*>(sb + 32 * ks + 16));
-    f32x4_t part[KS];
+    }
+    f32x4_t part[2 * KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) part[ks] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 2 * KS; ++i) part[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        part[ks] = __builtin_amdgcn_mfma_f32_16x16x4f32(ops.m[ks].v[e], bs[ks].v[e], part[ks], 0, 0, 0);
-    f32x4_t acc = ops.l;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) acc += part[ks];
-    cur = acc;
+        for (int ks = 0; ks < KS; ++ks)
+          part[2 * ks + h] =
+              __builtin_amdgcn_mfma_f32_16x16x4f32(am[ks].v[4 * h + e], bs[ks].v[4 * h + e], part[2 * ks + h], 0, 0, 0);
+#pragma unroll
+    for (int w = 1; w < 2 * KS; w *= 2)  // pairwise tree over the chains
+#pragma unroll
+      for (int i = 0; i < 2 * KS; i += 2 * w) part[i] += part[i + w];
+    cur = ops.l + part[0];
+    if (s + 1 < (PFIX > 0 ? PFIX : a.P)) stage(next1, x, sm, (s + 1) & 1);
     *reinterpret_cast<f32x4_t*>(&sm.s[(s + 1) & 1][x.c16 * LDS_ + x.row0]) = cur;
     __syncthreads();
   }
@@ -107,11 +141,13 @@ struct ComposeKernel {
     x.n = pair / a.H;
     x.hd = pair % a.H;
     x.H = a.H;
+    x.lane = lane;
     x.g4 = lane >> 4;
     x.c16 = lane & 15;
     x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     x.col = vb * BVC + x.c16;           // this lane's value column
     x.row0 = 16 * x.wave + 4 * x.g4;    // this lane's four state rows
+    x.vo_s = (x.col * DK + x.row0) * 4;
     const int DV = a.DV;
     const int P = a.P;
 
@@ -127,18 +163,31 @@ struct ComposeKernel {
       }
     }
     *reinterpret_cast<f32x4_t*>(&sm.s[0][x.c16 * LDS_ + x.row0]) = cur;
-    Ops A, B, C;
     if (P > 0) {
-      load(A, x, 0);
-      load(B, x, min(1, P - 1));
-    }
-    __syncthreads();
-    for (int s = 0; s < P; s += 3) {
-      step(cur, A, C, x, s, sm);
-      if (s + 1 >= P) break;
-      step(cur, B, A, x, s + 1, sm);
-      if (s + 2 >= P) break;
-      step(cur, C, B, x, s + 2, sm);
+      if constexpr (PFIX > 0) {
+        Ops o[3];
+        load(o[0], x, 0);
+        load(o[1], x, min(1, PFIX - 1));
+        stage(o[0], x, sm, 0);
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < PFIX; ++s) step(cur, o[s % 3], o[(s + 1) % 3], o[(s + 2) % 3], x, s, sm);
+      } else {
+        Ops A, B, C;
+        load(A, x, 0);
+        load(B, x, min(1, P - 1));
+        stage(A, x, sm, 0);
+        __syncthreads();
+        for (int s = 0; s < P; s += 3) {
+          step(cur, A, B, C, x, s, sm);
+          if (s + 1 >= P) break;
+          step(cur, B, C, A, x, s + 1, sm);
+          if (s + 2 >= P) break;
+          step(cur, C, A, B, x, s + 2, sm);
+        }
+      }
+    } else {
+      __syncthreads();
     }
     if (a.hT != nullptr) {
       float* hb = a.hT + (x.n * x.H + x.hd) * DV * DK;
@@ -152,23 +201,25 @@ struct ComposeKernel {
   }
 };
 
-template <int DK>
+template <int DK, int PFIX>
 __global__ __launch_bounds__(DK * 4) void compose_kernel(const ComposeArgs a) {
-  using K = ComposeKernel<DK>;
+  using K = ComposeKernel<DK, PFIX>;
   __shared__ __align__(16) typename K::Smem sm;
   K::run(a, sm);
 }
 
-template <int DK>
+template <int DK, int PFIX>
 static hipError_t launch_compose(const void* args, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((compose_kernel<DK>), dim3(grid), dim3(DK * 4), 0, stream,
+  hipLaunchKernelGGL((compose_kernel<DK, PFIX>), dim3(grid), dim3(DK * 4), 0, stream,
                      *static_cast<const ComposeArgs*>(args));
   return hipGetLastError();
 }
 
-LaunchFn find_compose(int dk) {
-  if (dk == 128) return &launch_compose<128>;
-  if (dk == 64) return &launch_compose<64>;
+// 16 segments (the split the long-sequence workloads use) get the
+// straight-line chain; other counts take the loop.
+LaunchFn find_compose(int dk, int P) {
+  if (dk == 128) return P == 16 ? &launch_compose<128, 16> : &launch_compose<128, 0>;
+  if (dk == 64) return P == 16 ? &launch_compose<64, 16> : &launch_compose<64, 0>;
   return nullptr;
 }
 

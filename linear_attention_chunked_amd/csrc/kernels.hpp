@@ -121,7 +121,7 @@ LaunchFn find_prepare(int dtype, int dk, int dv);
 LaunchFn find_prepare2(int dk, int dv);
 LaunchFn find_output(int dtype, int dk, int dv);
 LaunchFn find_output2(int dk, int dv);
-LaunchFn find_compose(int dk);
+LaunchFn find_compose(int dk, int P);
 LaunchFn find_dv_local(int dk, int dv);
 LaunchFn find_scan_bwd(int dk);
 hipError_t launch_abc(const AbcArgs& a, hipStream_t s);

@@ -109,7 +109,11 @@ bool parse_problem(int B, int64_t T, int H, int DK, int DV, int N, const int32_t
 }
 
 // Built tiles (must match the instantiations in scan.hip).
-static bool tile_built(int dtype, int bv, int waves, int stages) {
+static bool tile_built(int dtype, int bv, int waves, int stages, int kmode) {
+  // the summary pass of bfloat16 storage (kernel mode 2, DK = 128) also has a
+  // 256-column block of 8 waves: one workgroup per (segment, head) holding
+  // the whole local state and the whole transition
+  if (dtype == 1 && kmode == 2 && bv == 256 && waves == 8 && (stages == 2 || stages == 3)) return true;
   static const int bf16_tiles[][3] = {{32, 2, 2}, {32, 2, 3}, {64, 2, 3}, {64, 4, 2},
                                       {64, 4, 3}, {128, 4, 2}, {128, 4, 3}};
   static const int f32_tiles[][3] = {{32, 2, 1}, {32, 2, 2}, {64, 4, 1}, {64, 4, 2}};
@@ -171,16 +175,22 @@ bool choose_tile(const Problem& p, const int32_t* req, int mode, int64_t rows, T
       }
     }
   }
-  if (!tile_built(p.dtype, r[0], r[1], r[2])) {
+  const int kmode = (mode == 1) ? summary_kernel_mode(p) : 0;
+  if (!tile_built(p.dtype, r[0], r[1], r[2], kmode) || (r[0] == 256 && p.DK != 128)) {
     err = "tile (bv=" + std::to_string(r[0]) + ", waves=" + std::to_string(r[1]) +
           ", stages=" + std::to_string(r[2]) + ") is not built for this dtype";
     return false;
   }
-  if (r[0] > p.DV || p.DV % r[0] != 0) {
+  if (kmode == 2) {  // blocks of bv/2 state and bv/2 transition columns
+    if (r[0] / 2 > p.DV || p.DV % (r[0] / 2) != 0) {
+      err = "bv/2 must divide DV for segment summaries";
+      return false;
+    }
+  } else if (r[0] > p.DV || p.DV % r[0] != 0) {
     err = "bv must divide DV";
     return false;
   }
-  if (mode == 1 && p.DK % r[0] != 0) {
+  if (kmode == 1 && p.DK % r[0] != 0) {
     err = "bv must divide DK for segment summaries";
     return false;
   }
@@ -188,6 +198,13 @@ bool choose_tile(const Problem& p, const int32_t* req, int mode, int64_t rows, T
   t.waves = r[1];
   t.stages = r[2];
   return true;
+}
+
+int summary_kernel_mode(const Problem& p) { return (p.dtype == 1 && p.DK == p.DV) ? 2 : 1; }
+
+int scan_blocks(const Problem& p, const Tile& t, int mode) {
+  if (mode != 1) return p.DV / t.bv;
+  return summary_kernel_mode(p) == 2 ? 2 * p.DV / t.bv : (p.DV + p.DK) / t.bv;
 }
 
 void segment_bounds(int64_t len, int P, std::vector<int64_t>& t0, std::vector<int64_t>& t1) {
@@ -243,7 +260,7 @@ std::vector<Launch> plan_scan(const Problem& p, const Tile& t, int mode, int P, 
   }
   // longest first (stable, so equal lengths keep their order)
   std::stable_sort(rows.begin(), rows.end(), [](const Row& a, const Row& b) { return a.len > b.len; });
-  const int nblk = (mode == 1) ? (p.DV + p.DK) / t.bv : p.DV / t.bv;
+  const int nblk = scan_blocks(p, t, mode);
   std::vector<Launch> out;
   for (size_t i = 0; i < rows.size(); i += kMaxRows) {
     Launch l;

@@ -63,6 +63,14 @@ bool parse_problem(int B, int64_t T, int H, int DK, int DV, int N, const int32_t
 bool choose_tile(const Problem& p, const int32_t* req /* bv, waves, stages or null */, int mode, int64_t rows,
                  Tile& out, std::string& err);
 
+// Kernel mode of the summary pass: 2 (each block holds half state and half
+// transition columns, so all blocks of a (segment, head) run at one pace) for
+// bfloat16 storage with DK == DV, else 1 (whole blocks of state columns, then
+// of transition columns).
+int summary_kernel_mode(const Problem& p);
+// Column blocks per (row, head) of a scan launch in host mode `mode`.
+int scan_blocks(const Problem& p, const Tile& t, int mode);
+
 // Segment boundaries of one sequence: [t0, t1) token ranges relative to its start.
 void segment_bounds(int64_t len, int P, std::vector<int64_t>& t0, std::vector<int64_t>& t1);
 

@@ -42,7 +42,12 @@ struct Scan2 {
   static constexpr int KS = DK / 32;
   static constexpr int DT = DK / 16;
   static constexpr int RBW = DK * 2;      // bytes per W / K row
-  static constexpr int RBU = BV * 2;      // bytes per U row (this block's columns)
+  // MODE 2 (balanced summaries): a block holds BV/2 state columns (waves
+  // 0..NW/2-1, which read U) and the same BV/2 columns of the transition
+  // (the other waves), so every block of a (segment, head) does the same work
+  // and reads the same K/W tiles at the same pace (shared through L2).
+  static constexpr int UBV = (MODE == 2) ? BV / 2 : BV;  // U columns staged per block
+  static constexpr int RBU = UBV * 2;     // bytes per U row (this block's columns)
   static constexpr int SW = RBW + 16;     // padded LDS row strides (bytes)
   static constexpr int SK = RBW + 32;
   static constexpr int SU = RBU + 32;
@@ -85,10 +90,16 @@ struct Scan2 {
     int vo_u[U_PT];
   };
 
+  // Issues the loads of one chunk.  A chunk past the row's end (nvalid <= 0)
+  // gets empty buffer ranges: the same instructions are issued and return
+  // zeros, so every loop iteration issues the same number of loads and the
+  // compiler's wait counts keep the younger prefetches in flight.
   __device__ static __forceinline__ void load(Stage& st, const Ctx& x, int64_t tok0, int nvalid) {
     const ScanArgs& a = *x.a;
     const int64_t H = x.H;
-    const uint32_t wk_bytes = static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2);
+    const bool live = nvalid > 0;
+    if (!live) tok0 = 0;
+    const uint32_t wk_bytes = live ? static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2) : 0u;
     const uint16_t* wp = static_cast<const uint16_t*>(a.w) + (tok0 * H + x.hd) * DK;
     const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (tok0 * H + x.hd) * DK;
     const rsrc_t rw = make_rsrc(wp, wk_bytes);
@@ -97,14 +108,14 @@ struct Scan2 {
     for (int i = 0; i < W_PT; ++i) st.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, x.vo_wk[i], 0, 0);
 #pragma unroll
     for (int i = 0; i < W_PT; ++i) st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, x.vo_wk[i], 0, 0);
-    if (x.has_u) {
+    if (MODE != 1 || x.has_u) {
       const uint16_t* up = static_cast<const uint16_t*>(a.u) + (tok0 * H + x.hd) * x.DV + x.col_blk;
-      const rsrc_t ru = make_rsrc(up, static_cast<uint32_t>(((nvalid - 1) * H * x.DV + BV) * 2));
+      const rsrc_t ru = make_rsrc(up, live ? static_cast<uint32_t>(((nvalid - 1) * H * x.DV + UBV) * 2) : 0u);
 #pragma unroll
       for (int i = 0; i < U_PT; ++i) st.u[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, x.vo_u[i], 0, 0);
     }
     const float* gp = a.g_cum + tok0 * H + x.hd;
-    const rsrc_t rg = make_rsrc(gp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * 4));
+    const rsrc_t rg = make_rsrc(gp, live ? static_cast<uint32_t>(((nvalid - 1) * H + 1) * 4) : 0u);
     st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, static_cast<int>(threadIdx.x * H * 4), 0, 0));
   }
 
@@ -117,7 +128,7 @@ struct Scan2 {
       *reinterpret_cast<u32x4_t*>(buf + OFF_W + r * SW + c * 16) = st.w[i];
       *reinterpret_cast<u32x4_t*>(buf + OFF_K + r * SK + c * 16) = st.k[i];
     }
-    if (x.has_u) {
+    if (MODE != 1 || x.has_u) {
 #pragma unroll
       for (int i = 0; i < U_PT; ++i) {
         const int v = tid + i * NT;
@@ -129,7 +140,7 @@ struct Scan2 {
     }
     if (tid < kChunk) {  // first wave: decay weights of the chunk
       const float g_last = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, st.g), nvalid - 1));
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, st.g), max(nvalid, 1) - 1));
       float* d = reinterpret_cast<float*>(buf + OFF_D);
       d[tid] = (tid < nvalid) ? -exp_fast(g_last - st.g) : 0.f;
       if (tid == 0) d[kChunk] = exp_fast(g_last);
@@ -177,6 +188,7 @@ struct Scan2 {
     const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int colw = wave * (BV / NW);
+    const bool use_u = (MODE == 2) ? (wave < NW / 2) : x.has_u;  // wave-uniform
     const int64_t H = x.H;
     const int DV = x.DV;
     const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(c) * kChunk;
@@ -185,11 +197,12 @@ struct Scan2 {
     // per-lane LDS bases (immediates carry the tile/step offsets)
     const char* wb = buf + OFF_W + c16 * SW + (g4 >> 1) * 16 + (g4 & 1) * 8;            // + 16 mt SW + 64 s (+32)
     const char* kb = buf + OFF_K + (4 * g4 + (c16 >> 2)) * SK + (c16 & 3) * 8;          // + 32 s2 SK (+16 SK) + 32 dt
+    // (MODE 2: the state waves' columns colw lie in the first BV/2, the staged U tile)
     const char* ub = buf + OFF_U + (4 * g4 + (c16 >> 2)) * SU + (colw + 4 * (c16 & 3)) * 2;  // + 16 mt SU + 32 ct
     const float* nd_l = reinterpret_cast<const float*>(buf + OFF_D) + 4 * g4;          // + 16 mt
 
     u32x2_t uq[4][NC];
-    if (x.has_u) {
+    if (use_u) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -215,7 +228,7 @@ struct Scan2 {
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int ct = 0; ct < NC; ++ct) {
-        if (x.has_u) {
+        if (use_u) {
           const u32x2_t q = uq[mt][ct];  // bf16 -> f32 with the sign flipped in the same instruction
           acc[mt][ct] = f32x4_t{__builtin_bit_cast(float, (q.x << 16) + 0x80000000u),
                                 __builtin_bit_cast(float, (q.x & 0xffff0000u) ^ 0x80000000u),
@@ -243,11 +256,11 @@ struct Scan2 {
           *reinterpret_cast<u32x2_t*>(hs + 16 * ct * SHS + 64 * s) = u32x2_t{q.x, q.y};
           *reinterpret_cast<u32x2_t*>(hs + 16 * ct * SHS + 64 * s + 32) = u32x2_t{q.z, q.w};
         }
-    } else if (MODE == 0 && a.h != nullptr) {
+    } else if (MODE == 0) {  // (a NULL output gets an empty range: the stores are dropped)
       uint16_t* hp = static_cast<uint16_t*>(a.h) +
                      ((static_cast<int64_t>(row.chunk_off) + c) * H + x.hd) * DV * DK +
                      static_cast<int64_t>(x.col_blk + colw) * DK;
-      const rsrc_t rh = make_rsrc(hp, static_cast<uint32_t>((BV / NW) * DK * 2));
+      const rsrc_t rh = make_rsrc(hp, a.h != nullptr ? static_cast<uint32_t>((BV / NW) * DK * 2) : 0u);
       const int hoff = (c16 * DK + 4 * g4) * 2;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
@@ -286,9 +299,10 @@ struct Scan2 {
             vs[(16 * mt + r) * (SVS / 2) + 16 * ct] = static_cast<uint16_t>(pk);
             vs[(16 * mt + r + 1) * (SVS / 2) + 16 * ct] = static_cast<uint16_t>(pk >> 16);
           }
-    } else if (MODE == 0 && a.v_new != nullptr) {
+    } else if (MODE == 0) {
       uint16_t* vp = static_cast<uint16_t*>(a.v_new) + (tok0 * H + x.hd) * DV + x.col_blk + colw;
-      const rsrc_t rv = make_rsrc(vp, static_cast<uint32_t>(((nvalid - 1) * H * DV + BV - colw) * 2));
+      const rsrc_t rv =
+          make_rsrc(vp, a.v_new != nullptr ? static_cast<uint32_t>(((nvalid - 1) * H * DV + BV - colw) * 2) : 0u);
       const int rs = static_cast<int>(H * DV * 2);
       const int voff = (4 * g4) * rs + c16 * 2;
 #pragma unroll
@@ -339,7 +353,7 @@ struct Scan2 {
     x.hd = pair % a.H;
     x.H = a.H;
     x.DV = a.DV;
-    x.col_blk = jb * BV;
+    x.col_blk = jb * UBV;
     const bool trans = (MODE == 1) && (x.col_blk >= x.DV);
     x.has_u = !trans;
     const int64_t H = a.H;
@@ -356,6 +370,11 @@ struct Scan2 {
     const int colw = wave * (BV / NW);
     const int DV = x.DV;
     const int hd = x.hd;
+    // this wave's columns: of the transition (wtrans) or of the state / h_out,
+    // first column colj
+    const bool wtrans = (MODE == 2) ? (wave >= NW / 2) : trans;
+    const int colj = (MODE == 2) ? x.col_blk + (wave % (NW / 2)) * (BV / NW)
+                                 : x.col_blk + colw - (trans ? DV : 0);
     const int nchunks = (row.len + kChunk - 1) / kChunk;
 
     f32x4_t Sacc[DT][NC];
@@ -380,10 +399,10 @@ struct Scan2 {
         }
       }
     }
-    if (MODE == 1 && trans) {
+    if (MODE != 0 && wtrans) {
 #pragma unroll
       for (int ct = 0; ct < NC; ++ct) {
-        const int jj = x.col_blk + colw + 16 * ct + c16 - DV;
+        const int jj = colj + 16 * ct + c16;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -428,33 +447,35 @@ struct Scan2 {
           __syncthreads();
         }
       } else {
+        // two chunks in flight; loads and LDS fills are unconditional (chunks
+        // past the end load as empty ranges and are never computed)
         Stage A, B;
         load(A, x, tok_of(0), nv_of(0));
-        if (nchunks > 1) load(B, x, tok_of(1), nv_of(1));
+        load(B, x, tok_of(1), nv_of(1));
         store(A, x, buf0, nv_of(0));
         __syncthreads();
         for (int c = 0; c < nchunks; c += 2) {
-          if (c + 2 < nchunks) load(A, x, tok_of(c + 2), nv_of(c + 2));
+          load(A, x, tok_of(c + 2), nv_of(c + 2));
           compute(Sacc, x, row, c, buf0);
-          if (c + 1 < nchunks) store(B, x, buf1, nv_of(c + 1));
+          store(B, x, buf1, nv_of(c + 1));
           __syncthreads();
           if (c + 1 >= nchunks) break;
-          if (c + 3 < nchunks) load(B, x, tok_of(c + 3), nv_of(c + 3));
+          load(B, x, tok_of(c + 3), nv_of(c + 3));
           compute(Sacc, x, row, c + 1, buf1);
-          if (c + 2 < nchunks) store(A, x, buf0, nv_of(c + 2));
+          store(A, x, buf0, nv_of(c + 2));
           __syncthreads();
         }
       }
     }
 
     if (row.out_idx < 0) return;
-    if (MODE == 0 || !trans) {
+    if (MODE == 0 || !wtrans) {
       if (a.h_out == nullptr) return;
       float* base = a.h_out + (static_cast<int64_t>(row.out_idx) * H + hd) * DV * DK;
-      const bool vk = (MODE == 1) ? true : (a.out_vk != 0);
+      const bool vk = (MODE != 0) ? true : (a.out_vk != 0);
 #pragma unroll
       for (int ct = 0; ct < NC; ++ct) {
-        const int j = x.col_blk + colw + 16 * ct + c16;
+        const int j = colj + 16 * ct + c16;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const int i0 = 16 * dt + 4 * g4;
@@ -470,7 +491,7 @@ struct Scan2 {
       float* base = a.trans_out + (static_cast<int64_t>(row.out_idx) * H + hd) * DK * DK;
 #pragma unroll
       for (int ct = 0; ct < NC; ++ct) {
-        const int jj = x.col_blk + colw + 16 * ct + c16 - DV;
+        const int jj = colj + 16 * ct + c16;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -513,8 +534,12 @@ static hipError_t launch_scan2(const void* args, int grid, hipStream_t stream) {
 LaunchFn find_scan2(int dk, int bv, int waves, int stages, int mode) {
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 128, 0)
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 128, 1)
+  GDR_SCAN2_TILES(GDR_SCAN2_CASE, 128, 2)
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 0)
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 1)
+  GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 2)
+  GDR_SCAN2_CASE(128, 256, 8, 2, 2, 1, 1)
+  GDR_SCAN2_CASE(128, 256, 8, 3, 2, 2, 2)
   return nullptr;
 }
 
