@@ -109,11 +109,7 @@ bool parse_problem(int B, int64_t T, int H, int DK, int DV, int N, const int32_t
 }
 
 // Built tiles (must match the instantiations in scan.hip).
-static bool tile_built(int dtype, int bv, int waves, int stages, int kmode) {
-  // the summary pass of bfloat16 storage (kernel mode 2, DK = 128) also has a
-  // 256-column block of 8 waves: one workgroup per (segment, head) holding
-  // the whole local state and the whole transition
-  if (dtype == 1 && kmode == 2 && bv == 256 && waves == 8 && (stages == 2 || stages == 3)) return true;
+static bool tile_built(int dtype, int bv, int waves, int stages) {
   static const int bf16_tiles[][3] = {{32, 2, 2}, {32, 2, 3}, {64, 2, 3}, {64, 4, 2},
                                       {64, 4, 3}, {128, 4, 2}, {128, 4, 3}};
   static const int f32_tiles[][3] = {{32, 2, 1}, {32, 2, 2}, {64, 4, 1}, {64, 4, 2}};
@@ -176,7 +172,7 @@ bool choose_tile(const Problem& p, const int32_t* req, int mode, int64_t rows, T
     }
   }
   const int kmode = (mode == 1) ? summary_kernel_mode(p) : 0;
-  if (!tile_built(p.dtype, r[0], r[1], r[2], kmode) || (r[0] == 256 && p.DK != 128)) {
+  if (!tile_built(p.dtype, r[0], r[1], r[2])) {
     err = "tile (bv=" + std::to_string(r[0]) + ", waves=" + std::to_string(r[1]) +
           ", stages=" + std::to_string(r[2]) + ") is not built for this dtype";
     return false;

@@ -538,8 +538,6 @@ LaunchFn find_scan2(int dk, int bv, int waves, int stages, int mode) {
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 0)
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 1)
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 2)
-  GDR_SCAN2_CASE(128, 256, 8, 2, 2, 1, 1)
-  GDR_SCAN2_CASE(128, 256, 8, 3, 2, 2, 2)
   return nullptr;
 }
 
