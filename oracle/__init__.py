@@ -19,6 +19,8 @@ abc_bwd_ref  the reverse (dH) recurrence of the ABC slot states: gradients
 gdr_bwd_ref  the reverse (gradient) recurrence of the gated delta rule:
           gradients at chunk boundaries, of the initial state and of the
           chunk form's write vectors.
+kda_ref   the delta rule with a per-key-channel decay, token by token, and
+          its per-chunk (WY) form for the prepared factors.
 
 Every function is the plain definition, token by token, in float64 (or in
 exact rationals when handed ``fractions.Fraction`` object arrays); there is
@@ -39,3 +41,4 @@ from .abc_ref import abc_forward_fp64, abc_readout_sequence, abc_recurrent_fp64,
 from .abc_bwd_ref import abc_backward_fp64, abc_backward_sequence  # noqa: F401
 from .chunked_ref import gdr_chunked_fp64, chunked_scan_sequence, chunk_factors  # noqa: F401
 from .gdr_bwd_ref import gdr_backward_fp64, gdr_backward_sequence  # noqa: F401
+from .kda_ref import kda_chunked_fp64, kda_recurrent_fp64, kda_scan_sequence  # noqa: F401

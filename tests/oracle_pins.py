@@ -668,3 +668,142 @@ def run_abc_bwd_check(check, abc_bwd_ref, abc_ref):
     if check is check_abc_bwd_boundaries:
         return check(abc_bwd_ref, abc_ref)
     return check(abc_bwd_ref)
+
+
+# --------------------------------------------------------------------------- per-channel decay (KDA-style)
+def _kda_problem(seed, L, H, DK, DV):
+    """Small float64 problem: unit q, k rows, per-channel decays in (0, 1]."""
+    q, k, v, _, b, S0 = rand_problem(seed, L, H, DK, DV)
+    r = np.random.default_rng(seed + 1000)
+    a = 1.0 / (1.0 + np.exp(-r.normal(2.0, 1.0, (L, H, DK))))
+    return q, k, v, a, b, S0
+
+
+def check_kda_brute_force(kda_ref):
+    """Dense transitions (I - b_t k_t k_t^T) diag(a_t) multiplied out explicitly."""
+    L, H, DK, DV, C = 11, 2, 5, 3, 4
+    q, k, v, a, b, S0 = _kda_problem(41, L, H, DK, DV)
+    o, pre, ST = kda_ref.kda_scan_sequence(q, k, v, a, b, S0, 0.7, C)
+    for h in range(H):
+        S = S0[h]
+        states = []
+        for t in range(L):
+            A = (np.eye(DK) - b[t, h] * np.outer(k[t, h], k[t, h])) @ np.diag(a[t, h])
+            S = A @ S + b[t, h] * np.outer(k[t, h], v[t, h])
+            states.append(S)
+        _assert_close(ST[h], states[-1], what="final state vs dense products")
+        _assert_close(o[:, h], 0.7 * np.stack([states[t].T @ q[t, h] for t in range(L)]), what="outputs vs dense")
+        for c, t0 in enumerate(range(0, L, C)):
+            _assert_close(pre[c, h], S0[h] if t0 == 0 else states[t0 - 1], what=f"pre-chunk state {c}")
+
+
+def check_kda_rationals(kda_ref):
+    """DK = DV = 3, T = 5, per-channel rational decays: exact equality with the
+    dense products (I - b k k^T) diag(a) in Fraction arithmetic."""
+    r = np.random.default_rng(6)
+    L, D = 5, 3
+
+    def fr(x, den=8):
+        return Fr(int(round(x * den)), den)
+
+    q = [[fr(x) for x in r.standard_normal(D)] for _ in range(L)]
+    k = [[fr(x) for x in r.standard_normal(D)] for _ in range(L)]
+    v = [[fr(x) for x in r.standard_normal(D)] for _ in range(L)]
+    a = [[Fr(int(r.integers(5, 16)), 16) for _ in range(D)] for _ in range(L)]
+    b = [Fr(int(r.integers(1, 8)), 8) for _ in range(L)]
+    S0 = [[fr(x, 4) for x in r.standard_normal(D)] for _ in range(D)]
+    S = S0
+    o_ref, pre_ref = [], []
+    for t in range(L):
+        if t % 2 == 0:
+            pre_ref.append(S)
+        A = [[((Fr(1) if i == j else Fr(0)) - b[t] * k[t][i] * k[t][j]) * a[t][j] for j in range(D)]
+             for i in range(D)]
+        S = _fr_matmul(A, S)
+        S = [[S[i][j] + b[t] * k[t][i] * v[t][j] for j in range(D)] for i in range(D)]
+        o_ref.append([sum((S[i][j] * q[t][i] for i in range(D)), Fr(0)) for j in range(D)])
+
+    def obj(x, shape):
+        arr = np.empty(shape, dtype=object)
+        arr[...] = np.array(x, dtype=object).reshape(shape)
+        return arr
+
+    o, pre, ST = kda_ref.kda_scan_sequence(obj(q, (L, 1, D)), obj(k, (L, 1, D)), obj(v, (L, 1, D)),
+                                           obj(a, (L, 1, D)), obj(b, (L, 1)), obj(S0, (1, D, D)), Fr(1), 2)
+    assert all(ST[0, i, j] == S[i][j] for i in range(D) for j in range(D)), "final state not exact"
+    assert all(o[t, 0, j] == o_ref[t][j] for t in range(L) for j in range(D)), "outputs not exact"
+    for c in range(len(pre_ref)):
+        assert all(pre[c, 0, i, j] == pre_ref[c][i][j] for i in range(D) for j in range(D)), \
+            f"pre-chunk state {c} not exact"
+
+
+def check_kda_scalar_reduction(kda_ref, gdr_ref):
+    """Every channel decaying alike is the scalar gated delta rule (itself pinned)."""
+    L, H, DK, DV, C = 70, 2, 6, 4, 16
+    q, k, v, a, b, S0 = rand_problem(51, L, H, DK, DV)
+    ak = np.repeat(a[:, :, None], DK, axis=2)
+    o1, p1, s1 = kda_ref.kda_scan_sequence(q, k, v, ak, b, S0, 0.5, C)
+    o2, p2, s2 = gdr_ref.gdr_scan_sequence(q, k, v, a, b, S0, 0.5, C)
+    _assert_close(o1, o2, 1e-13, "outputs")
+    _assert_close(p1, p2, 1e-13, "pre-chunk states")
+    _assert_close(s1, s2, 1e-13, "final state")
+
+
+def check_kda_pure_decay(kda_ref):
+    """b = 0: every key row keeps its own running product of decays."""
+    L, H, DK, DV, C = 40, 2, 6, 4, 16
+    q, k, v, a, b, S0 = _kda_problem(61, L, H, DK, DV)
+    b = np.zeros_like(b)
+    o, pre, ST = kda_ref.kda_scan_sequence(q, k, v, a, b, S0, 1.0, C)
+    cum = np.cumprod(a, axis=0)                              # [L, H, DK]
+    _assert_close(ST, cum[-1][:, :, None] * S0, what="b=0 final state")
+    _assert_close(o, np.einsum("thk,hkv,thk->thv", cum, S0, q), what="b=0 outputs")
+    for c, t0 in enumerate(range(0, L, C)):
+        f = np.ones((H, DK)) if t0 == 0 else cum[t0 - 1]
+        _assert_close(pre[c], f[:, :, None] * S0, what=f"b=0 pre-chunk {c}")
+
+
+def check_kda_recall(kda_ref):
+    """a = 1, b = 1, orthonormal keys: exact recall; a channel decayed to zero
+    forgets its row of the state before the write."""
+    DK, DV, L = 8, 5, 6
+    r = np.random.default_rng(71)
+    Qm, _ = np.linalg.qr(r.standard_normal((DK, DK)))
+    K = Qm[:L]
+    V = r.standard_normal((L, DV))
+    S0 = r.standard_normal((DK, DV))
+    o, pre, ST = kda_ref.kda_scan_sequence(K[:, None], K[:, None], V[:, None], np.ones((L, 1, DK)),
+                                           np.ones((L, 1)), S0[None], 1.0, 64)
+    _assert_close(ST[0], (np.eye(DK) - K.T @ K) @ S0 + K.T @ V, TOL, "recall closed form")
+    a = np.ones((1, 1, DK))
+    a[0, 0, 2] = 0.0
+    _, _, S1 = kda_ref.kda_scan_sequence(K[:1, None], K[:1, None], V[:1, None], a, np.zeros((1, 1)), S0[None],
+                                         1.0, 64)
+    ref = S0.copy()
+    ref[2] = 0.0
+    _assert_close(S1[0], ref, TOL, "zeroed channel")
+
+
+def check_kda_chunk_algebra(kda_ref):
+    """The chunk (WY) form equals the token recurrence at several chunk sizes,
+    packed sequences with ragged tails, initial states and an output scale."""
+    lengths = [1, 63, 64, 65, 150]
+    H, DK, DV = 2, 8, 6
+    r = np.random.default_rng(81)
+    Ttot = sum(lengths)
+    q = r.standard_normal((1, Ttot, H, DK))
+    k = r.standard_normal((1, Ttot, H, DK))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((1, Ttot, H, DV))
+    g = np.log(1.0 / (1.0 + np.exp(-r.normal(2.0, 1.0, (1, Ttot, H, DK)))))
+    beta = 1.0 / (1.0 + np.exp(-r.standard_normal((1, Ttot, H))))
+    h0 = 0.2 * r.standard_normal((len(lengths), H, DK, DV))
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    for C in (1, 2, 7, 16, 64):
+        ref = kda_ref.kda_recurrent_fp64(q, k, v, g, beta, h0, cu, 0.5, C)
+        got = kda_ref.kda_chunked_fp64(q, k, v, g, beta, h0, cu, 0.5, C)
+        for key in ("o", "v_new", "h", "hT"):
+            _assert_close(got[key], ref[key], 1e-11, f"chunk {C}: {key}")
+
+
+KDA_CHECKS = [check_kda_brute_force, check_kda_rationals, check_kda_pure_decay, check_kda_recall]

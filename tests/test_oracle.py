@@ -5,7 +5,7 @@ forms, invariants)."""
 import pytest
 
 import oracle_pins as P
-from oracle import abc_bwd_ref, abc_ref, chunked_ref, gdr_bwd_ref, gdr_ref
+from oracle import abc_bwd_ref, abc_ref, chunked_ref, gdr_bwd_ref, gdr_ref, kda_ref
 
 
 @pytest.mark.parametrize("check", P.GDR_CHECKS, ids=lambda f: f.__name__)
@@ -35,3 +35,16 @@ def test_abc_read_oracle_pin(check):
 @pytest.mark.parametrize("check", P.ABC_BWD_CHECKS, ids=lambda f: f.__name__)
 def test_abc_backward_oracle_pin(check):
     P.run_abc_bwd_check(check, abc_bwd_ref, abc_ref)
+
+
+@pytest.mark.parametrize("check", P.KDA_CHECKS, ids=lambda f: f.__name__)
+def test_kda_oracle_pin(check):
+    check(kda_ref)
+
+
+def test_kda_reduces_to_scalar_decay():
+    P.check_kda_scalar_reduction(kda_ref, gdr_ref)
+
+
+def test_kda_chunk_form_equals_token_recurrence():
+    P.check_kda_chunk_algebra(kda_ref)

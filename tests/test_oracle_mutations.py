@@ -160,3 +160,43 @@ def test_abc_bwd_pins_catch(mut):
         except Exception:
             failures += 1
     assert failures > 0, f"no pin caught mutation {mut}"
+
+
+KDA_MUTANTS = {
+    "channel_averaged_decay": ("S = a[t][:, :, None] * S", "S = a[t].mean(axis=1)[:, None, None] * S"),
+    "dropped_beta": ("delta = b[t][:, None] * (v[t] - pred)", "delta = v[t] - pred"),
+    "wrong_sign": ("delta = b[t][:, None] * (v[t] - pred)", "delta = b[t][:, None] * (v[t] + pred)"),
+    "decay_after_write": ("        S = a[t][:, :, None] * S\n", "        pass\n"),
+    "w_without_decay": ("W = T @ (beta[:, None] * k * np.exp(Gam))", "W = T @ (beta[:, None] * k)"),
+    "kg_wrong_reference": ("Kg = k * np.exp(Gam[-1][None, :] - Gam)", "Kg = k * np.exp(-Gam)"),
+    "a_includes_diagonal": ('A = np.tril(beta[:, None] * np.einsum("td,id,tid->ti", k, k, dec), -1)',
+                            'A = np.tril(beta[:, None] * np.einsum("td,id,tid->ti", k, k, dec), 0)'),
+    "output_strictly_causal": ("causal = np.tril(np.ones((n, n), dtype=bool))[:, :, None]",
+                               "causal = np.tril(np.ones((n, n), dtype=bool), -1)[:, :, None]"),
+    "state_decay_first_token": ("return Gam, W, U, Kg, np.exp(Gam[-1])", "return Gam, W, U, Kg, np.exp(Gam[0])"),
+}
+
+
+@pytest.mark.parametrize("mut", sorted(KDA_MUTANTS))
+def test_kda_pins_catch(mut):
+    from oracle import gdr_ref
+
+    old, new = KDA_MUTANTS[mut]
+    src = open(os.path.join(ROOT, "oracle/kda_ref.py")).read()
+    assert src.count(old) == 1, f"mutation anchor not found: {old!r}"
+    src = src.replace(old, new, 1)
+    if mut == "decay_after_write":
+        anchor = "        vnew[t] = delta\n"
+        src = src.replace(anchor, anchor + "        S = a[t][:, :, None] * S\n", 1)
+    src = src.replace("from .gdr_ref import _sequences, chunk_counts", "from oracle.gdr_ref import _sequences, chunk_counts")
+    m = types.ModuleType(f"kda_mut_{mut}")
+    exec(compile(src, "kda_ref_mut", "exec"), m.__dict__)
+    checks = [lambda: c(m) for c in P.KDA_CHECKS]
+    checks += [lambda: P.check_kda_scalar_reduction(m, gdr_ref), lambda: P.check_kda_chunk_algebra(m)]
+    failures = 0
+    for check in checks:
+        try:
+            check()
+        except Exception:
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {mut}"
