@@ -278,6 +278,53 @@ gdr_status abc_affine_scan_bwd(const abc_problem* p, const void* q, const void* 
                                float scale, void* dhk, void* dhv, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* ------------------------------------------------------------------------
+ * Per-key-channel decay (the FlashKDA-style gate of [cuLA#127] "Summary" and
+ * "Root cause and implementation": the serial path whose pre-scan that page
+ * parallelises; no recurrence is printed there).  Recurrence, one sequence and
+ * one head, with a per-channel decay a_t = exp(g_t) in R^DK:
+ *     S_t = (I - b_t k_t k_t^T) diag(a_t) S_{t-1} + b_t k_t v_t^T,  o_t = scale * S_t^T q_t
+ * (every key row of the state decays by its own factor, then the delta-rule
+ * write on the decayed state; with all channels equal it is the recurrence
+ * above).  Per 64-token chunk, Gam = chunk-local inclusive cumulative sum of g
+ * per channel:
+ *   A[t,i] = b_t sum_d k_td k_id e^{Gam_td - Gam_id} (i < t), T = (I + A)^-1,
+ *   w = T diag(b) (K * e^{Gam}),  u = T diag(b) V,
+ *   kg = K * e^{Gam_last - Gam},  decay = e^{Gam_last}   (per channel)
+ *   scan:   h[c] = S;  v_new = u - w S;  S <- diag(decay) S + kg^T v_new
+ *   output: o_t = scale ((q_t * e^{Gam_t})^T S_c + sum_{i<=t} P[t,i] v_new_i),
+ *           P[t,i] = sum_d q_td k_id e^{Gam_td - Gam_id}
+ * Layouts as above, except g and g_cum [B, T, H, DK] float32, kg [B, T, H, DK]
+ * (storage dtype) and decay [NT, H, DK] float32 (one vector per chunk and
+ * head, chunks numbered like the rows of h).  Bfloat16 storage only.
+ * Input range: the intra-chunk products are formed per 16-token block with
+ * the block's first token as reference, which stays finite while every
+ * channel's log decay is at least -5 per token; smaller values (a decay
+ * below e^-5 in one token) can overflow to inf/NaN. */
+
+/* Chunk preparation: writes g_cum, w, u and kg for every valid token and the
+ * channel decays of every chunk. */
+gdr_status kda_chunk_prepare(const gdr_problem* p, const void* k, const void* v, const float* g, const float* beta,
+                             float* g_cum, void* w, void* u, void* kg, float* decay, void* stream);
+
+/* The inter-chunk state scan with per-channel decay: gdr_state_scan's
+ * contract (tiles, segmented final pass, pools, layouts, bit-identity across
+ * tiles) with kg in place of k and the chunk decays in place of g_cum. */
+gdr_status kda_state_scan(const gdr_problem* p, const gdr_tile* tile, const gdr_segments* seg, const void* kg,
+                          const void* w, const void* u, const float* decay, const float* h0, void* h, void* v_new,
+                          float* hT, void* stream);
+
+/* Segment summaries with per-channel decay (gdr_segment_summaries' contract;
+ * the transition of a chunk is diag(decay) - kg^T w).  Compose them with
+ * gdr_segment_compose. */
+gdr_status kda_segment_summaries(const gdr_problem* p, const gdr_tile* tile, int32_t n_segments, const void* kg,
+                                 const void* w, const void* u, const float* decay, float* seg_state, float* seg_trans,
+                                 void* stream);
+
+/* Chunk output with per-channel decay (o for every valid token). */
+gdr_status kda_chunk_output(const gdr_problem* p, const void* q, const void* k, const void* v_new, const void* h,
+                            const float* g_cum, float scale, void* o, void* stream);
+
 /* Human-readable name of a status code. */
 const char* gdr_status_string(gdr_status s);
 /* Message of the last failed call on this thread ("" if none). */

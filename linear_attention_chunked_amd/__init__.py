@@ -21,5 +21,10 @@ from .binding import (  # noqa: F401
     gdr_segment_summaries,
     gdr_state_scan,
     gdr_state_scan_bwd,
+    chunk_kda,
+    kda_chunk_output,
+    kda_chunk_prepare,
+    kda_segment_summaries,
+    kda_state_scan,
     lib,
 )

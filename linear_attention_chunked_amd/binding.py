@@ -75,6 +75,12 @@ _SIGS = {
     "gdr_segment_summaries": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile), ctypes.c_int32,
                                              _P, _P, _P, _P, _P, _P, _P]),
     "gdr_segment_compose": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
+    "kda_chunk_prepare": (ctypes.c_int, [ctypes.POINTER(gdr_problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "kda_state_scan": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile),
+                                      ctypes.POINTER(gdr_segments), _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "kda_segment_summaries": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile), ctypes.c_int32,
+                                             _P, _P, _P, _P, _P, _P, _P]),
+    "kda_chunk_output": (ctypes.c_int, [ctypes.POINTER(gdr_problem), _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]),
     "gdr_chunk_dv_local": (ctypes.c_int, [ctypes.POINTER(gdr_problem), _P, _P, _P, _P, ctypes.c_float, _P, _P]),
     "gdr_state_scan_bwd": (ctypes.c_int, [ctypes.POINTER(gdr_problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                           _P, _P, _P, _P]),
@@ -285,6 +291,77 @@ def gdr_segment_compose(k, DV: int, seg_state, seg_trans, n_segments: int, h0=No
     _check(lib().gdr_segment_compose(p.ref, n_segments, _ptr(seg_state), _ptr(seg_trans), _ptr(h0), _ptr(seg_init),
                                      _ptr(hT), _stream(stream)), "gdr_segment_compose")
     return seg_init, hT
+
+
+def kda_chunk_prepare(k, v, g, beta, cu_seqlens=None, stream=None):
+    """Per-channel-decay WY factors: returns (g_cum [B,T,H,DK] fp32, w, u, kg, decay [NT,H,DK] fp32)."""
+    DV = v.shape[-1]
+    p = Problem(k, DV, cu_seqlens)
+    nt = gdr_num_chunks(k, DV, cu_seqlens)
+    g_cum = torch.empty(g.shape, dtype=torch.float32, device=k.device)
+    w = torch.empty_like(k)
+    u = torch.empty_like(v)
+    kg = torch.empty_like(k)
+    decay = torch.empty((nt, p.H, p.DK), dtype=torch.float32, device=k.device)
+    _check(lib().kda_chunk_prepare(p.ref, _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(g_cum), _ptr(w), _ptr(u),
+                                   _ptr(kg), _ptr(decay), _stream(stream)), "kda_chunk_prepare")
+    return g_cum, w, u, kg, decay
+
+
+def kda_state_scan(kg, w, u, decay, h0=None, cu_seqlens=None, tile=None, n_segments: Optional[int] = None,
+                   seg_init=None, state_layout: str = "kv", emit_h: bool = True, emit_v_new: bool = True,
+                   emit_final: bool = True, stream=None):
+    """Per-channel-decay state scan.  Returns (h [NT,H,DV,DK] | None, v_new | None, hT | None)."""
+    DV = u.shape[-1]
+    p = Problem(kg, DV, cu_seqlens, state_layout)
+    nt = gdr_num_chunks(kg, DV, cu_seqlens)
+    h = torch.empty((nt, p.H, DV, p.DK), dtype=kg.dtype, device=kg.device) if emit_h else None
+    v_new = torch.empty_like(u) if emit_v_new else None
+    hT = None
+    if emit_final:
+        shape = (p.N, p.H, DV, p.DK) if state_layout == "vk" else (p.N, p.H, p.DK, DV)
+        hT = torch.empty(shape, dtype=torch.float32, device=kg.device)
+    t = _tile(tile)
+    seg = None
+    if n_segments is not None:
+        if seg_init is None or not seg_init.is_cuda:
+            raise ValueError("the segmented pass needs seg_init on the GPU")
+        seg = gdr_segments(n_segments, seg_init.data_ptr())
+    _check(lib().kda_state_scan(p.ref, ctypes.byref(t) if t is not None else None,
+                                ctypes.byref(seg) if seg is not None else None, _ptr(kg), _ptr(w), _ptr(u),
+                                _ptr(decay), _ptr(h0), _ptr(h), _ptr(v_new), _ptr(hT), _stream(stream)),
+           "kda_state_scan")
+    return h, v_new, hT
+
+
+def kda_segment_summaries(kg, w, u, decay, n_segments: int, cu_seqlens=None, tile=None, stream=None):
+    """Returns (seg_state [N*P,H,DV,DK], seg_trans [N*P,H,DK,DK]) float32."""
+    DV = u.shape[-1]
+    p = Problem(kg, DV, cu_seqlens)
+    seg_state = torch.empty((p.N * n_segments, p.H, DV, p.DK), dtype=torch.float32, device=kg.device)
+    seg_trans = torch.empty((p.N * n_segments, p.H, p.DK, p.DK), dtype=torch.float32, device=kg.device)
+    t = _tile(tile)
+    _check(lib().kda_segment_summaries(p.ref, ctypes.byref(t) if t is not None else None, n_segments, _ptr(kg),
+                                       _ptr(w), _ptr(u), _ptr(decay), _ptr(seg_state), _ptr(seg_trans),
+                                       _stream(stream)), "kda_segment_summaries")
+    return seg_state, seg_trans
+
+
+def kda_chunk_output(q, k, v_new, h, g_cum, scale: float = 1.0, cu_seqlens=None, stream=None) -> torch.Tensor:
+    p = Problem(k, v_new.shape[-1], cu_seqlens)
+    o = torch.empty_like(v_new)
+    _check(lib().kda_chunk_output(p.ref, _ptr(q), _ptr(k), _ptr(v_new), _ptr(h), _ptr(g_cum), float(scale), _ptr(o),
+                                  _stream(stream)), "kda_chunk_output")
+    return o
+
+
+def chunk_kda(q, k, v, g, beta, scale: float = 1.0, h0=None, cu_seqlens=None, tile=None, stream=None):
+    """The whole per-channel-decay forward: prepare, state scan, output.
+    Returns (o, hT, h, v_new)."""
+    g_cum, w, u, kg, decay = kda_chunk_prepare(k, v, g, beta, cu_seqlens, stream)
+    h, v_new, hT = kda_state_scan(kg, w, u, decay, h0, cu_seqlens, tile, stream=stream)
+    o = kda_chunk_output(q, k, v_new, h, g_cum, scale, cu_seqlens, stream)
+    return o, hT, h, v_new
 
 
 def abc_workspace_size(B: int, T: int, H: int, K: int, M: int, V: int, dtype=torch.bfloat16) -> int:

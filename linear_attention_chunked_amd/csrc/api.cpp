@@ -83,9 +83,10 @@ gdr_status hip_fail(hipError_t e, const char* what) {
 
 gdr_status run_scan(const gdr::Problem& pr, const gdr::Tile& t, int mode, int P, const void* k, const void* w,
                     const void* u, const float* g_cum, const float* h_in, int in_vk, void* h, void* v_new,
-                    float* h_out, int out_vk, float* trans_out, hipStream_t stream) {
+                    float* h_out, int out_vk, float* trans_out, hipStream_t stream, const float* decay = nullptr) {
   const int kmode = (mode == 1) ? gdr::summary_kernel_mode(pr) : 0;
-  gdr::LaunchFn fn = gdr::find_scan(pr.dtype, pr.DK, t.bv, t.waves, t.stages, kmode);
+  gdr::LaunchFn fn = decay != nullptr ? gdr::find_scan2(pr.DK, t.bv, t.waves, t.stages, kmode, true)
+                                      : gdr::find_scan(pr.dtype, pr.DK, t.bv, t.waves, t.stages, kmode);
   if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no scan kernel for this dtype/DK/tile");
   const bool has_in = (h_in != nullptr);
   const bool has_out = (h_out != nullptr);
@@ -101,6 +102,7 @@ gdr_status run_scan(const gdr::Problem& pr, const gdr::Tile& t, int mode, int P,
   a.v_new = v_new;
   a.h_out = h_out;
   a.trans_out = trans_out;
+  a.decay = decay;
   a.H = pr.H;
   a.DV = pr.DV;
   a.in_vk = in_vk;
@@ -405,6 +407,137 @@ gdr_status gdr_plan_query(const gdr_problem* p, const gdr_tile* tile, int32_t n_
   out[3] = wg;
   out[4] = static_cast<int64_t>(plan.size());
   out[5] = maxrows;
+  return GDR_OK;
+}
+
+/* ----------------------------------------------------------- per-channel decay */
+
+gdr_status kda_chunk_prepare(const gdr_problem* p, const void* k, const void* v, const float* g, const float* beta,
+                             float* g_cum, void* w, void* u, void* kg, float* decay, void* stream) {
+  g_err.clear();
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  GDR_TRY(need(k, "k"));
+  GDR_TRY(need(v, "v"));
+  GDR_TRY(need(g, "g"));
+  GDR_TRY(need(beta, "beta"));
+  GDR_TRY(need(g_cum, "g_cum"));
+  GDR_TRY(need(w, "w"));
+  GDR_TRY(need(u, "u"));
+  GDR_TRY(need(kg, "kg"));
+  GDR_TRY(need(decay, "decay"));
+  if (pr.dtype != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "the per-channel decay path is built for bfloat16 storage");
+  gdr::LaunchFn fn = gdr::find_kda_prepare(pr.DK, pr.DV);
+  if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no per-channel prepare kernel for this DK/DV");
+  gdr::KdaArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.g_cum = g_cum;
+  a.w = w;
+  a.u = u;
+  a.kg = kg;
+  a.decay = decay;
+  a.H = pr.H;
+  for (const gdr::Launch& l : gdr::plan_chunks(pr, 1)) {
+    a.n_rows = static_cast<int32_t>(l.rows.size());
+    a.n_chunks = l.n_chunks;
+    a.chunk_base = l.chunk_base;
+    memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
+    hipError_t e = fn(&a, l.grid, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "per-channel prepare launch");
+  }
+  return GDR_OK;
+}
+
+gdr_status kda_state_scan(const gdr_problem* p, const gdr_tile* tile, const gdr_segments* seg, const void* kg,
+                          const void* w, const void* u, const float* decay, const float* h0, void* h, void* v_new,
+                          float* hT, void* stream) {
+  g_err.clear();
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  GDR_TRY(need(kg, "kg"));
+  GDR_TRY(need(w, "w"));
+  GDR_TRY(need(u, "u"));
+  GDR_TRY(need(decay, "decay"));
+  GDR_TRY(opt(h0, "h0"));
+  GDR_TRY(opt(h, "h"));
+  GDR_TRY(opt(v_new, "v_new"));
+  GDR_TRY(opt(hT, "hT"));
+  if (pr.dtype != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "the per-channel decay path is built for bfloat16 storage");
+  int mode = 0, P = 1;
+  const float* h_in = h0;
+  int in_vk = pr.state_vk;
+  if (seg != nullptr) {
+    if (!pr.pool_idx.empty()) return fail(GDR_ERR_UNSUPPORTED, "indexed states are supported by the serial scan only");
+    if (seg->n_segments < 1) return fail(GDR_ERR_INVALID_ARG, "n_segments must be >= 1");
+    GDR_TRY(need(seg->seg_init, "seg_init"));
+    mode = 2;
+    P = seg->n_segments;
+    h_in = seg->seg_init;
+    in_vk = 1;
+  }
+  gdr::Tile t;
+  GDR_TRY(tile_for(pr, tile, 0, static_cast<int64_t>(pr.N) * P, t));
+  return run_scan(pr, t, mode, P, kg, w, u, nullptr, h_in, in_vk, h, v_new, hT, pr.state_vk, nullptr,
+                  static_cast<hipStream_t>(stream), decay);
+}
+
+gdr_status kda_segment_summaries(const gdr_problem* p, const gdr_tile* tile, int32_t n_segments, const void* kg,
+                                 const void* w, const void* u, const float* decay, float* seg_state, float* seg_trans,
+                                 void* stream) {
+  g_err.clear();
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  if (!pr.pool_idx.empty()) return fail(GDR_ERR_UNSUPPORTED, "indexed states are supported by the serial scan only");
+  if (n_segments < 1) return fail(GDR_ERR_INVALID_ARG, "n_segments must be >= 1");
+  GDR_TRY(need(kg, "kg"));
+  GDR_TRY(need(w, "w"));
+  GDR_TRY(need(u, "u"));
+  GDR_TRY(need(decay, "decay"));
+  GDR_TRY(need(seg_state, "seg_state"));
+  GDR_TRY(need(seg_trans, "seg_trans"));
+  if (pr.dtype != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "the per-channel decay path is built for bfloat16 storage");
+  gdr::Tile t;
+  GDR_TRY(tile_for(pr, tile, 1, static_cast<int64_t>(pr.N) * n_segments, t));
+  return run_scan(pr, t, 1, n_segments, kg, w, u, nullptr, nullptr, 0, nullptr, nullptr, seg_state, 1, seg_trans,
+                  static_cast<hipStream_t>(stream), decay);
+}
+
+gdr_status kda_chunk_output(const gdr_problem* p, const void* q, const void* k, const void* v_new, const void* h,
+                            const float* g_cum, float scale, void* o, void* stream) {
+  g_err.clear();
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  GDR_TRY(need(q, "q"));
+  GDR_TRY(need(k, "k"));
+  GDR_TRY(need(v_new, "v_new"));
+  GDR_TRY(need(h, "h"));
+  GDR_TRY(need(g_cum, "g_cum"));
+  GDR_TRY(need(o, "o"));
+  if (pr.dtype != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "the per-channel decay path is built for bfloat16 storage");
+  gdr::LaunchFn fn = gdr::find_kda_output(pr.DK, pr.DV);
+  if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no per-channel output kernel for this DK/DV");
+  gdr::KdaArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v_new;
+  a.g = g_cum;
+  a.h = h;
+  a.o = o;
+  a.scale = scale;
+  a.H = pr.H;
+  for (const gdr::Launch& l : gdr::plan_chunks(pr, pr.DV / 64)) {
+    a.n_rows = static_cast<int32_t>(l.rows.size());
+    a.n_chunks = l.n_chunks;
+    a.chunk_base = l.chunk_base;
+    memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
+    hipError_t e = fn(&a, l.grid, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "per-channel output launch");
+  }
   return GDR_OK;
 }
 

@@ -1,0 +1,594 @@
+// Per-key-channel decay (the FlashKDA-style gate of cuLA pull request #127,
+// "Summary"): chunk preparation and chunk output on gfx950, bfloat16
+// storage.  The state scan is scan2.hip with its per-channel decay switch.
+//
+// Per chunk with Gam = the chunk-local cumulative sum of the per-channel log
+// decays (Gam_t in R^DK), derived from the token recurrence
+// S_t = (I - b_t k_t k_t^T) diag(e^{g_t}) S_{t-1} + b_t k_t v_t^T:
+//
+//   A[t,i] = b_t sum_d k_td k_id e^{Gam_td - Gam_id}     (i < t)
+//   T = (I + A)^-1;  w = T diag(b) (K * e^{Gam});  u = T diag(b) V
+//   kg = K * e^{Gam_last - Gam};  decay = e^{Gam_last}
+//   (scan)   v_new = u - w S;  S <- diag(decay) S + kg^T v_new
+//   (output) o_t = scale ((q_t * e^{Gam_t})^T S + sum_{i<=t} P[t,i] v_new_i),
+//            P[t,i] = sum_d q_td k_id e^{Gam_td - Gam_id}
+//
+// The products with a per-pair, per-channel decay are formed per 16-token
+// block of rows I against the columns of every block J <= I, each factor
+// referenced at the block's first token r = 16 I:
+//   x_td e^{Gam_td - Gam_rd}  (t >= r: at most 1)  times  y_id e^{Gam_rd - Gam_id},
+// which is at most 1 for i < r; for i >= r (the diagonal block) it is at most
+// e^{-(Gam over 15 tokens)}, finite while every channel's log decay stays
+// above -5 per token (the documented input range).  The products run on
+// FP32 MFMA (v_mfma_f32_16x16x4_f32): lane (c, g) supplies, for step
+// j = 4 q + m, the channel d = 16 q + 4 g + m of row c, so each lane reads
+// four consecutive channels at a time.
+#include "gfx950.hpp"
+#include "kernels.hpp"
+
+namespace gdr {
+
+namespace {
+
+__device__ __forceinline__ void mm16f(f32x4_t& d, const f32x4_t& a, const f32x4_t& b) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], d, 0, 0, 0);
+}
+
+__device__ __forceinline__ int kda_find_row(const KdaArgs& a, int chunk) {
+  int lo = 0, hi = a.n_rows - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.rows[mid].chunk_off <= chunk) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// bf16 hi + lo split of an FP32 value (hi = RNE bf16, lo = bf16 of the rest)
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16(x);
+  lo = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
+}  // namespace
+
+// Shared by prepare and output: the decayed products of one 16-row block.
+//   xs[j]: this lane's A-side values (row 16 I + c, channel d(j)), already
+//          multiplied by e^{Gam_td - Gam_rd};
+//   ys: bf16 rows (stride SY bytes), gam: FP32 Gam rows (stride GS floats).
+// Returns D[4 g + r][c] = sum_d xs_td ys_id e^{Gam_rd - Gam_id} for i = 16 J + c.
+template <int DK, int SY, int GS>
+__device__ __forceinline__ f32x4_t kda_block_product(const float (&xs)[DK / 4], const char* ys, const float* gam,
+                                                     int I, int J, int g4, int c16) {
+  const float* gr = gam + (16 * I) * GS;            // reference row r = 16 I (broadcast)
+  const float* gi = gam + (16 * J + c16) * GS;      // this lane's column row i
+  const char* yi = ys + (16 * J + c16) * SY;
+  f32x4_t d{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < DK / 16; ++q) {
+    const int d0 = 16 * q + 4 * g4;
+    const f32x4_t grv = *reinterpret_cast<const f32x4_t*>(gr + d0);
+    const f32x4_t giv = *reinterpret_cast<const f32x4_t*>(gi + d0);
+    const u32x2_t yq = *reinterpret_cast<const u32x2_t*>(yi + 2 * d0);
+    f32x4_t yb, xa;
+    yb[0] = __builtin_bit_cast(float, yq.x << 16) * exp_fast(grv[0] - giv[0]);
+    yb[1] = __builtin_bit_cast(float, yq.x & 0xffff0000u) * exp_fast(grv[1] - giv[1]);
+    yb[2] = __builtin_bit_cast(float, yq.y << 16) * exp_fast(grv[2] - giv[2]);
+    yb[3] = __builtin_bit_cast(float, yq.y & 0xffff0000u) * exp_fast(grv[3] - giv[3]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xa[m] = xs[4 * q + m];
+    mm16f(d, xa, yb);
+  }
+  return d;
+}
+
+// This lane's A-side values of row t = 16 I + c16: x_td e^{Gam_td - Gam_rd}.
+template <int DK, int SX, int GS>
+__device__ __forceinline__ void kda_row_side(float (&xs)[DK / 4], const char* xrows, const float* gam, int I, int g4,
+                                             int c16) {
+  const float* gr = gam + (16 * I) * GS;
+  const float* gt = gam + (16 * I + c16) * GS;
+  const char* xt = xrows + (16 * I + c16) * SX;
+#pragma unroll
+  for (int q = 0; q < DK / 16; ++q) {
+    const int d0 = 16 * q + 4 * g4;
+    const f32x4_t grv = *reinterpret_cast<const f32x4_t*>(gr + d0);
+    const f32x4_t gtv = *reinterpret_cast<const f32x4_t*>(gt + d0);
+    const u32x2_t xq = *reinterpret_cast<const u32x2_t*>(xt + 2 * d0);
+    xs[4 * q + 0] = __builtin_bit_cast(float, xq.x << 16) * exp_fast(gtv[0] - grv[0]);
+    xs[4 * q + 1] = __builtin_bit_cast(float, xq.x & 0xffff0000u) * exp_fast(gtv[1] - grv[1]);
+    xs[4 * q + 2] = __builtin_bit_cast(float, xq.y << 16) * exp_fast(gtv[2] - grv[2]);
+    xs[4 * q + 3] = __builtin_bit_cast(float, xq.y & 0xffff0000u) * exp_fast(gtv[3] - grv[3]);
+  }
+}
+
+// ------------------------------------------------------------------ prepare
+template <int DK, int DV>
+struct KdaPrepare {
+  using S = St<bf16_t>;
+  using frag = S::frag;
+  static constexpr int NT = 256;
+  static constexpr int SKB = DK * 2 + 16;   // bf16 rows (bytes)
+  static constexpr int SVB = DV * 2 + 16;
+  static constexpr int GS = DK + 4;         // FP32 Gam rows (floats), padded
+  static constexpr int LDA = 64 + 4;
+
+  struct Smem {
+    char k[kChunk * SKB];
+    char v[kChunk * SVB];
+    char ke_hi[kChunk * SKB];   // K * e^{Gam}: bf16 hi and lo parts
+    char ke_lo[kChunk * SKB];
+    float gam[kChunk * GS];
+    union {
+      float a[kChunk * LDA];
+      float t[kChunk * LDA];
+    };
+    float beta[kChunk];
+  };
+
+  __device__ static void run(const KdaArgs& a, Smem& sm) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int item = blockIdx.x;
+    const int chunk = item / a.H;
+    const int hd = item % a.H;
+    if (chunk >= a.n_chunks) return;
+    const Row row = a.rows[kda_find_row(a, chunk)];
+    const int cl = chunk - row.chunk_off;
+    const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(cl) * kChunk;
+    const int nvalid = min(kChunk, row.len - cl * kChunk);
+    const int64_t H = a.H;
+
+    // ---- K, V (bf16), g (FP32), beta into LDS; rows past the tail read as zero ----
+    {
+      const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (tok0 * H + hd) * DK;
+      const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + hd) * DV;
+      const float* gp = a.g + (tok0 * H + hd) * DK;
+      const rsrc_t rk = make_rsrc(kp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
+      const rsrc_t rv = make_rsrc(vp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
+      const rsrc_t rg = make_rsrc(gp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 4));
+      constexpr int CK = DK / 8, CV = DV / 8, CG = DK / 4;
+#pragma unroll
+      for (int i = 0; i < kChunk * CK / NT; ++i) {
+        const int vv = tid + i * NT, r = vv / CK, c = vv % CK;
+        *reinterpret_cast<u32x4_t*>(sm.k + r * SKB + c * 16) =
+            __builtin_amdgcn_raw_buffer_load_b128(rk, static_cast<int>(r * H * DK * 2 + c * 16), 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kChunk * CV / NT; ++i) {
+        const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
+        *reinterpret_cast<u32x4_t*>(sm.v + r * SVB + c * 16) =
+            __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kChunk * CG / NT; ++i) {
+        const int vv = tid + i * NT, r = vv / CG, c = vv % CG;
+        *reinterpret_cast<u32x4_t*>(sm.gam + r * GS + c * 4) =
+            __builtin_amdgcn_raw_buffer_load_b128(rg, static_cast<int>(r * H * DK * 4 + c * 16), 0, 0);
+      }
+      if (tid < kChunk) {
+        const float* bp = a.beta + tok0 * H + hd;
+        const float b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+            make_rsrc(bp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * 4)), static_cast<int>(tid * H * 4), 0, 0));
+        sm.beta[tid] = b;
+      }
+    }
+    __syncthreads();
+
+    // ---- Gam: inclusive cumulative sum over the chunk's tokens, per channel
+    //      (rows past the tail add zero, so they repeat the last value) ----
+    if (tid < DK) {
+      float x = 0.f;
+      float* go = a.g_cum + (tok0 * H + hd) * DK + tid;
+      for (int t = 0; t < kChunk; ++t) {
+        x += sm.gam[t * GS + tid];
+        sm.gam[t * GS + tid] = x;
+        if (t < nvalid) go[t * H * DK] = x;
+      }
+      a.decay[((static_cast<int64_t>(a.chunk_base) + chunk) * H + hd) * DK + tid] = exp_fast(x);
+    }
+    __syncthreads();
+
+    // ---- K * e^{Gam} (hi / lo parts, LDS) and kg = K * e^{Gam_last - Gam} (global) ----
+    {
+      uint16_t* kgp = static_cast<uint16_t*>(a.kg) + (tok0 * H + hd) * DK;
+      const rsrc_t rkg = make_rsrc(kgp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
+      constexpr int CK = DK / 8;
+#pragma unroll
+      for (int i = 0; i < kChunk * CK / NT; ++i) {
+        const int vv = tid + i * NT, r = vv / CK, c = vv % CK;
+        const u32x4_t kq = *reinterpret_cast<const u32x4_t*>(sm.k + r * SKB + c * 16);
+        const float* gt = sm.gam + r * GS + 8 * c;
+        const float* gl = sm.gam + (kChunk - 1) * GS + 8 * c;
+        uint32_t hw[4], lw[4], gw[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t wd = kq[p];
+          const float k0 = __builtin_bit_cast(float, wd << 16), k1 = __builtin_bit_cast(float, wd & 0xffff0000u);
+          uint16_t h0, l0, h1, l1;
+          split_bf16(k0 * exp_fast(gt[2 * p]), h0, l0);
+          split_bf16(k1 * exp_fast(gt[2 * p + 1]), h1, l1);
+          hw[p] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+          lw[p] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+          gw[p] = pack_bf16x2(k0 * exp_fast(gl[2 * p] - gt[2 * p]), k1 * exp_fast(gl[2 * p + 1] - gt[2 * p + 1]));
+        }
+        *reinterpret_cast<u32x4_t*>(sm.ke_hi + r * SKB + c * 16) = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+        *reinterpret_cast<u32x4_t*>(sm.ke_lo + r * SKB + c * 16) = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{gw[0], gw[1], gw[2], gw[3]}, rkg,
+                                               static_cast<int>(r * H * DK * 2 + c * 16), 0, 0);
+      }
+    }
+
+    // ---- A rows of block `wave`: b_t sum_d k_td k_id e^{Gam_td - Gam_id}, i < t ----
+    {
+      float xs[DK / 4];
+      kda_row_side<DK, SKB, GS>(xs, sm.k, sm.gam, wave, g4, c16);
+      for (int J = 0; J <= wave; ++J) {
+        const f32x4_t d = kda_block_product<DK, SKB, GS>(xs, sm.k, sm.gam, wave, J, g4, c16);
+        const int i = 16 * J + c16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * wave + 4 * g4 + r;
+          sm.a[t * LDA + i] = (i < t) ? sm.beta[t] * d[r] : 0.f;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- T = (I + A)^-1 by 16-blocks: diagonal blocks by forward substitution,
+    //      off-diagonal blocks as FP32 products (A and T share one matrix) ----
+    if (lane < 16) {
+      const int b0 = 16 * wave, j = lane;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s = (r == j) ? 1.f : 0.f;
+        const float* ar = &sm.a[(b0 + r) * LDA + b0];
+#pragma unroll
+        for (int i = 0; i < r; ++i) s -= ar[i] * x[i];
+        x[r] = s;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.t[(b0 + r) * LDA + b0 + j] = x[r];
+    }
+    for (int e = tid; e < kChunk * kChunk; e += NT) {
+      const int r = e >> 6, c = e & 63;
+      if ((c >> 4) > (r >> 4)) sm.t[r * LDA + c] = 0.f;
+    }
+    __syncthreads();
+    auto a_rows = [&](const float* m, int r0, int c0) {
+      return *reinterpret_cast<const f32x4_t*>(m + (r0 + c16) * LDA + c0 + 4 * g4);
+    };
+    auto b_cols = [&](const float* m, int r0, int c0) {
+      f32x4_t y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = m[(r0 + 4 * g4 + r) * LDA + c0 + c16];
+      return y;
+    };
+    auto store_c = [&](float* m, int r0, int c0, const f32x4_t& d) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m[(r0 + 4 * g4 + r) * LDA + c0 + c16] = d[r];
+    };
+    if (wave < 2) {
+      const int p = 32 * wave;
+      f32x4_t y{0.f, 0.f, 0.f, 0.f}, x{0.f, 0.f, 0.f, 0.f};
+      mm16f(y, a_rows(sm.a, p + 16, p), b_cols(sm.t, p, p));
+      mm16f(x, a_rows(sm.t, p + 16, p + 16), y);
+      store_c(sm.t, p + 16, p, -x);
+    }
+    __syncthreads();
+    {
+      const int i = wave >> 1, j = wave & 1;
+      f32x4_t y0{0.f, 0.f, 0.f, 0.f}, y1{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (k >= j) {
+          const f32x4_t tb = b_cols(sm.t, 16 * k, 16 * j);
+          mm16f(y0, a_rows(sm.a, 32, 16 * k), tb);
+          mm16f(y1, a_rows(sm.a, 48, 16 * k), tb);
+        }
+      }
+      __syncthreads();
+      f32x4_t x{0.f, 0.f, 0.f, 0.f};
+      mm16f(x, a_rows(sm.t, 32 + 16 * i, 32), y0);
+      if (i == 1) mm16f(x, a_rows(sm.t, 48, 48), y1);
+      store_c(sm.t, 32 + 16 * i, 16 * j, -x);
+    }
+    __syncthreads();
+
+    // ---- w^T = (K e^Gam)^T (T diag(b))^T, u^T = V^T (T diag(b))^T; wave = token tile ----
+    const int t = 16 * wave + c16;
+    frag bb_hi[2], bb_lo[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int i0 = 32 * s + 4 * g4;
+      const f32x4_t t0 = *reinterpret_cast<const f32x4_t*>(&sm.t[t * LDA + i0]);
+      const f32x4_t t1 = *reinterpret_cast<const f32x4_t*>(&sm.t[t * LDA + i0 + 16]);
+      const f32x4_t be0 = *reinterpret_cast<const f32x4_t*>(&sm.beta[i0]);
+      const f32x4_t be1 = *reinterpret_cast<const f32x4_t*>(&sm.beta[i0 + 16]);
+      const f32x4_t u0 = t0 * be0, u1 = t1 * be1;
+      bb_hi[s] = S::frag_from_f32(u0, u1);
+      f32x4_t l0, l1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        l0[r] = u0[r] - bf16_to_f32(f32_to_bf16(u0[r]));
+        l1[r] = u1[r] - bf16_to_f32(f32_to_bf16(u1[r]));
+      }
+      bb_lo[s] = S::frag_from_f32(l0, l1);
+    }
+    const int nsteps = (16 * wave + 15) / 32 + 1;  // T is lower triangular
+    const int tr_row = 4 * g4 + (c16 >> 2);
+    const int tr_col = 8 * (c16 & 3);
+    uint16_t* wo = static_cast<uint16_t*>(a.w) + (tok0 * H + hd) * DK;
+    uint16_t* uo = static_cast<uint16_t*>(a.u) + (tok0 * H + hd) * DV;
+    const rsrc_t rwo = make_rsrc(wo, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
+    const rsrc_t ruo = make_rsrc(uo, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
+#pragma unroll
+    for (int dt = 0; dt < DK / 16; ++dt) {
+      f32x4_t acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (s < nsteps) {
+          const int off = (32 * s + tr_row) * SKB + 32 * dt + tr_col;
+          const frag fh = S::frag_from_quads(lds_tr16(sm.ke_hi, off), lds_tr16(sm.ke_hi, off + 16 * SKB));
+          const frag fl = S::frag_from_quads(lds_tr16(sm.ke_lo, off), lds_tr16(sm.ke_lo, off + 16 * SKB));
+          S::mma(acc, fh, bb_hi[s]);
+          S::mma(acc, fh, bb_lo[s]);
+          S::mma(acc, fl, bb_hi[s]);
+        }
+      }
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])}, rwo,
+                                            static_cast<int>(t * H * DK * 2 + (16 * dt + 4 * g4) * 2), 0, 0);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) {
+      f32x4_t acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (s < nsteps) {
+          const int off = (32 * s + tr_row) * SVB + 32 * dt + tr_col;
+          const frag fa = S::frag_from_quads(lds_tr16(sm.v, off), lds_tr16(sm.v, off + 16 * SVB));
+          S::mma(acc, fa, bb_hi[s]);
+          S::mma(acc, fa, bb_lo[s]);
+        }
+      }
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])}, ruo,
+                                            static_cast<int>(t * H * DV * 2 + (16 * dt + 4 * g4) * 2), 0, 0);
+    }
+  }
+};
+
+// ------------------------------------------------------------------ output
+// One workgroup (4 waves) per (chunk, head, 64 value columns); wave I owns the
+// rows of token block I.
+template <int DK, int DV>
+struct KdaOutput {
+  using S = St<bf16_t>;
+  using frag = S::frag;
+  static constexpr int NT = 256;
+  static constexpr int BVO = 64;
+  static constexpr int NCT = BVO / 16;
+  static constexpr int SQ = DK * 2 + 16;
+  static constexpr int SV = BVO * 2 + 32;
+  static constexpr int GS = DK + 4;
+  static constexpr int LP = 64 + 4;
+  static constexpr int KS = DK / 32;
+
+  struct Smem {
+    char q[kChunk * SQ];
+    char k[kChunk * SQ];
+    char qe_hi[kChunk * SQ];   // Q * e^{Gam}: bf16 hi and lo parts
+    char qe_lo[kChunk * SQ];
+    char h[BVO * SQ];
+    char v[kChunk * SV];
+    float gam[kChunk * GS];
+    float p[kChunk * LP];
+  };
+
+  __device__ static void run(const KdaArgs& a, Smem& sm) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    constexpr int NVB = DV / BVO;
+    const int item = blockIdx.x;
+    const int vb = item % NVB;
+    const int rest = item / NVB;
+    const int chunk = rest / a.H;
+    const int hd = rest % a.H;
+    if (chunk >= a.n_chunks) return;
+    const Row row = a.rows[kda_find_row(a, chunk)];
+    const int cl = chunk - row.chunk_off;
+    const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(cl) * kChunk;
+    const int nvalid = min(kChunk, row.len - cl * kChunk);
+    const int64_t H = a.H;
+    const int col0 = vb * BVO;
+
+    {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (tok0 * H + hd) * DK;
+      const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (tok0 * H + hd) * DK;
+      const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + hd) * DV + col0;
+      const uint16_t* hp = static_cast<const uint16_t*>(a.h) +
+                           ((static_cast<int64_t>(a.chunk_base) + chunk) * H + hd) * DV * DK +
+                           static_cast<int64_t>(col0) * DK;
+      const float* gp = a.g + (tok0 * H + hd) * DK;
+      const uint32_t qk_bytes = static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2);
+      const rsrc_t rq = make_rsrc(qp, qk_bytes);
+      const rsrc_t rk = make_rsrc(kp, qk_bytes);
+      const rsrc_t rv = make_rsrc(vp, static_cast<uint32_t>(((nvalid - 1) * H * DV + BVO) * 2));
+      const rsrc_t rh = make_rsrc(hp, static_cast<uint32_t>(BVO * DK * 2));
+      const rsrc_t rg = make_rsrc(gp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 4));
+      constexpr int CQ = DK / 8, CV = BVO / 8, CG = DK / 4;
+#pragma unroll
+      for (int i = 0; i < kChunk * CQ / NT; ++i) {
+        const int vv = tid + i * NT, r = vv / CQ, c = vv % CQ;
+        const int go = static_cast<int>(r * H * DK * 2 + c * 16);
+        *reinterpret_cast<u32x4_t*>(sm.q + r * SQ + c * 16) = __builtin_amdgcn_raw_buffer_load_b128(rq, go, 0, 0);
+        *reinterpret_cast<u32x4_t*>(sm.k + r * SQ + c * 16) = __builtin_amdgcn_raw_buffer_load_b128(rk, go, 0, 0);
+        *reinterpret_cast<u32x4_t*>(sm.h + r * SQ + c * 16) =
+            __builtin_amdgcn_raw_buffer_load_b128(rh, static_cast<int>(r * DK * 2 + c * 16), 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kChunk * CV / NT; ++i) {
+        const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
+        *reinterpret_cast<u32x4_t*>(sm.v + r * SV + c * 16) =
+            __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kChunk * CG / NT; ++i) {
+        const int vv = tid + i * NT, r = vv / CG, c = vv % CG;
+        *reinterpret_cast<u32x4_t*>(sm.gam + r * GS + c * 4) =
+            __builtin_amdgcn_raw_buffer_load_b128(rg, static_cast<int>(r * H * DK * 4 + c * 16), 0, 0);
+      }
+    }
+    __syncthreads();
+
+    // ---- Q * e^{Gam} split into bf16 hi / lo (rows past the tail: q is zero) ----
+    {
+      constexpr int CQ = DK / 8;
+#pragma unroll
+      for (int i = 0; i < kChunk * CQ / NT; ++i) {
+        const int vv = tid + i * NT, r = vv / CQ, c = vv % CQ;
+        const u32x4_t qq = *reinterpret_cast<const u32x4_t*>(sm.q + r * SQ + c * 16);
+        const float* gt = sm.gam + r * GS + 8 * c;
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t wd = qq[p];
+          uint16_t h0, l0, h1, l1;
+          split_bf16(__builtin_bit_cast(float, wd << 16) * exp_fast(gt[2 * p]), h0, l0);
+          split_bf16(__builtin_bit_cast(float, wd & 0xffff0000u) * exp_fast(gt[2 * p + 1]), h1, l1);
+          hw[p] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+          lw[p] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+        }
+        *reinterpret_cast<u32x4_t*>(sm.qe_hi + r * SQ + c * 16) = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+        *reinterpret_cast<u32x4_t*>(sm.qe_lo + r * SQ + c * 16) = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+      }
+    }
+
+    // ---- P rows of block `wave`: sum_d q_td k_id e^{Gam_td - Gam_id}, i <= t ----
+    {
+      float xs[DK / 4];
+      kda_row_side<DK, SQ, GS>(xs, sm.q, sm.gam, wave, g4, c16);
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        const int i = 16 * J + c16;
+        if (J <= wave) {
+          const f32x4_t d = kda_block_product<DK, SQ, GS>(xs, sm.k, sm.gam, wave, J, g4, c16);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * wave + 4 * g4 + r;
+            sm.p[t * LP + i] = (i <= t) ? d[r] : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm.p[(16 * wave + 4 * g4 + r) * LP + i] = 0.f;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- O = (Q e^Gam) S_c + P v_new, rows of token tile `wave` ----
+    const char* rowqh = sm.qe_hi + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;
+    const char* rowql = sm.qe_lo + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;
+    const char* rowh = sm.h + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;
+    auto rfrag = [&](const char* base, int tile, int s) {
+      return S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(base + 16 * tile * SQ + 64 * s),
+                                *reinterpret_cast<const u32x2_t*>(base + 16 * tile * SQ + 64 * s + 32));
+    };
+    f32x4_t acc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const frag fh = rfrag(rowqh, wave, s);
+      const frag fl = rfrag(rowql, wave, s);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const frag hb = rfrag(rowh, ct, s);
+        S::mma(acc[ct], fh, hb);
+        S::mma(acc[ct], fl, hb);
+      }
+    }
+    const char* vb_ = sm.v + (4 * g4 + (c16 >> 2)) * SV + 8 * (c16 & 3);
+    const int t = 16 * wave + c16;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (32 * s <= 16 * wave + 15) {
+        const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(&sm.p[t * LP + 32 * s + 4 * g4]);
+        const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(&sm.p[t * LP + 32 * s + 16 + 4 * g4]);
+        f32x4_t l0, l1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          l0[r] = p0[r] - bf16_to_f32(f32_to_bf16(p0[r]));
+          l1[r] = p1[r] - bf16_to_f32(f32_to_bf16(p1[r]));
+        }
+        const frag ph = S::frag_from_f32(p0, p1);
+        const frag pl = S::frag_from_f32(l0, l1);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const frag vf = S::frag_from_quads(lds_tr16(vb_, 32 * s * SV + 32 * ct), lds_tr16(vb_, (32 * s + 16) * SV + 32 * ct));
+          S::mma(acc[ct], ph, vf);
+          S::mma(acc[ct], pl, vf);
+        }
+      }
+    }
+
+    uint16_t* op = static_cast<uint16_t*>(a.o) + (tok0 * H + hd) * DV + col0;
+    const rsrc_t ro = make_rsrc(op, static_cast<uint32_t>(((nvalid - 1) * H * DV + BVO) * 2));
+    const int rs = static_cast<int>(H * DV * 2);
+    const int voff = (16 * wave + 4 * g4) * rs + c16 * 2;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const uint32_t pk = pack_bf16x2(a.scale * acc[ct][r], a.scale * acc[ct][r + 1]);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk), ro, voff, r * rs + 32 * ct, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk >> 16), ro, voff, (r + 1) * rs + 32 * ct, 0);
+      }
+  }
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void kda_prepare_kernel(const KdaArgs a) {
+  using K = KdaPrepare<DK, DV>;
+  __shared__ __align__(16) typename K::Smem sm;
+  K::run(a, sm);
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void kda_output_kernel(const KdaArgs a) {
+  using K = KdaOutput<DK, DV>;
+  __shared__ __align__(16) typename K::Smem sm;
+  K::run(a, sm);
+}
+
+template <int DK, int DV>
+static hipError_t launch_kda_prepare(const void* args, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((kda_prepare_kernel<DK, DV>), dim3(grid), dim3(256), 0, stream, *static_cast<const KdaArgs*>(args));
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t launch_kda_output(const void* args, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((kda_output_kernel<DK, DV>), dim3(grid), dim3(256), 0, stream, *static_cast<const KdaArgs*>(args));
+  return hipGetLastError();
+}
+
+LaunchFn find_kda_prepare(int dk, int dv) {
+  if (dk == 128 && dv == 128) return &launch_kda_prepare<128, 128>;
+  if (dk == 128 && dv == 64) return &launch_kda_prepare<128, 64>;
+  if (dk == 64 && dv == 128) return &launch_kda_prepare<64, 128>;
+  if (dk == 64 && dv == 64) return &launch_kda_prepare<64, 64>;
+  return nullptr;
+}
+
+LaunchFn find_kda_output(int dk, int dv) {
+  if (dk == 128 && dv == 128) return &launch_kda_output<128, 128>;
+  if (dk == 128 && dv == 64) return &launch_kda_output<128, 64>;
+  if (dk == 64 && dv == 128) return &launch_kda_output<64, 128>;
+  if (dk == 64 && dv == 64) return &launch_kda_output<64, 64>;
+  return nullptr;
+}
+
+}  // namespace gdr

@@ -20,6 +20,7 @@ struct ScanArgs {
   void* v_new;         // (nullable)
   float* h_out;        // hT or seg_state (nullable)
   float* trans_out;    // seg_trans (summaries only)
+  const float* decay;  // per-key-channel decay: [NT, H, DK] channel decays of every chunk (else null)
   int32_t H;
   int32_t DV;
   int32_t in_vk;       // layout of h_in: 1 = [.., DV, DK], 0 = [.., DK, DV]
@@ -112,13 +113,39 @@ struct AbcArgs {
   int32_t P;           // runs per sequence of the state walk
 };
 
+// Per-key-channel decay: chunk preparation and chunk output (one workgroup
+// per (chunk, head), resp. (chunk, head, 64 value columns); rows as in
+// ChunkArgs).
+struct KdaArgs {
+  const void* q;
+  const void* k;
+  const void* v;       // v (prepare) or v_new (output)
+  const float* g;      // prepare: per-channel log decays [B,T,H,DK]; output: g_cum
+  const float* beta;
+  const void* h;       // output: pre-chunk states
+  float* g_cum;        // prepare outputs ...
+  void* w;
+  void* u;
+  void* kg;
+  float* decay;        // [NT, H, DK]
+  void* o;             // output output
+  float scale;
+  int32_t H;
+  int32_t n_rows;
+  int32_t n_chunks;
+  int32_t chunk_base;
+  Row rows[kMaxRows];
+};
+
 using LaunchFn = hipError_t (*)(const void* args, int grid, hipStream_t stream);
 
 // Lookup of an instantiated kernel; nullptr when the combination is not built.
 LaunchFn find_scan(int dtype, int dk, int bv, int waves, int stages, int mode);
-LaunchFn find_scan2(int dk, int bv, int waves, int stages, int mode);
+LaunchFn find_scan2(int dk, int bv, int waves, int stages, int mode, bool kd);
 LaunchFn find_prepare(int dtype, int dk, int dv);
 LaunchFn find_prepare2(int dk, int dv);
+LaunchFn find_kda_prepare(int dk, int dv);
+LaunchFn find_kda_output(int dk, int dv);
 LaunchFn find_output(int dtype, int dk, int dv);
 LaunchFn find_output2(int dk, int dv);
 LaunchFn find_compose(int dk, int P);

@@ -383,7 +383,7 @@ static hipError_t launch_scan(const void* args, int grid, hipStream_t stream) {
     return &launch_scan<T, DK, BV, NW, ST, MODE>;
 
 LaunchFn find_scan(int dtype, int dk, int bv, int waves, int stages, int mode) {
-  if (dtype == 1) return find_scan2(dk, bv, waves, stages, mode);
+  if (dtype == 1) return find_scan2(dk, bv, waves, stages, mode, false);
   GDR_SCAN_TILES(GDR_SCAN_CASE, float, 0, 128, 0)
   GDR_SCAN_TILES(GDR_SCAN_CASE, float, 0, 128, 1)
   GDR_SCAN_TILES(GDR_SCAN_CASE, float, 0, 64, 0)

@@ -28,12 +28,17 @@
 //   * U enters the accumulator negated and the sign is folded into the decay
 //     weights, so W needs no negation: acc = -U + W S = -D, v_new = -acc,
 //     D' = acc * (-exp(g_last - g)).
+//   * Per-key-channel decay (KD): the caller passes the decayed keys
+//     kg = K * e^{Gam_last - Gam} in place of K and the chunk's channel decays
+//     e^{Gam_last} (one DK-vector per chunk and head); the weights are then
+//     -1 (0 past the tail) and every state row is scaled by its own channel's
+//     decay: S <- diag(decay) S + kg^T D.
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
 namespace gdr {
 
-template <int DK, int BV, int NW, int PF, int MODE, int NBUF>
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD>
 struct Scan2 {
   using S = St<bf16_t>;
   using frag = S::frag;
@@ -55,7 +60,8 @@ struct Scan2 {
   static constexpr int CPU = RBU / 16;
   static constexpr int OFF_W = 0, OFF_K = kChunk * SW, OFF_U = OFF_K + kChunk * SK;
   static constexpr int OFF_D = OFF_U + kChunk * SU;   // 64 negated decay weights, then exp(g_last)
-  static constexpr int BUF = OFF_D + kChunk * 4 + 16;
+  static constexpr int OFF_DEC = OFF_D + (kChunk + 4) * 4;  // KD: the chunk's DK channel decays
+  static constexpr int BUF = OFF_DEC + (KD ? DK * 4 : 0);
   // Output staging (single-buffer loop, plain and segmented passes): the
   // chunk's h block and v_new tile are written to LDS in their memory layout
   // and leave the next iteration as whole 16-byte vectors per lane (the h
@@ -94,7 +100,7 @@ struct Scan2 {
   // gets empty buffer ranges: the same instructions are issued and return
   // zeros, so every loop iteration issues the same number of loads and the
   // compiler's wait counts keep the younger prefetches in flight.
-  __device__ static __forceinline__ void load(Stage& st, const Ctx& x, int64_t tok0, int nvalid) {
+  __device__ static __forceinline__ void load(Stage& st, const Ctx& x, int64_t tok0, int nvalid, int64_t hrow) {
     const ScanArgs& a = *x.a;
     const int64_t H = x.H;
     const bool live = nvalid > 0;
@@ -114,9 +120,15 @@ struct Scan2 {
 #pragma unroll
       for (int i = 0; i < U_PT; ++i) st.u[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, x.vo_u[i], 0, 0);
     }
-    const float* gp = a.g_cum + tok0 * H + x.hd;
-    const rsrc_t rg = make_rsrc(gp, live ? static_cast<uint32_t>(((nvalid - 1) * H + 1) * 4) : 0u);
-    st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, static_cast<int>(threadIdx.x * H * 4), 0, 0));
+    if constexpr (KD) {  // thread d < DK: channel d's decay over the chunk
+      const float* dp = a.decay + (hrow * H + x.hd) * DK;
+      const rsrc_t rd = make_rsrc(dp, live ? static_cast<uint32_t>(DK * 4) : 0u);
+      st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, static_cast<int>(threadIdx.x * 4), 0, 0));
+    } else {
+      const float* gp = a.g_cum + tok0 * H + x.hd;
+      const rsrc_t rg = make_rsrc(gp, live ? static_cast<uint32_t>(((nvalid - 1) * H + 1) * 4) : 0u);
+      st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, static_cast<int>(threadIdx.x * H * 4), 0, 0));
+    }
   }
 
   __device__ static __forceinline__ void store(const Stage& st, const Ctx& x, char* buf, int nvalid) {
@@ -138,7 +150,10 @@ struct Scan2 {
         }
       }
     }
-    if (tid < kChunk) {  // first wave: decay weights of the chunk
+    if constexpr (KD) {
+      if (tid < kChunk) reinterpret_cast<float*>(buf + OFF_D)[tid] = (tid < nvalid) ? -1.f : 0.f;
+      if (tid < DK) reinterpret_cast<float*>(buf + OFF_DEC)[tid] = st.g;
+    } else if (tid < kChunk) {  // first wave: decay weights of the chunk
       const float g_last = __builtin_bit_cast(
           float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, st.g), max(nvalid, 1) - 1));
       float* d = reinterpret_cast<float*>(buf + OFF_D);
@@ -323,11 +338,21 @@ struct Scan2 {
 #pragma unroll
       for (int ct = 0; ct < NC; ++ct) Db[s2][ct] = S::frag_from_f32(acc[2 * s2][ct] * nd[2 * s2], acc[2 * s2 + 1][ct] * nd[2 * s2 + 1]);
 
-    // ---- S = exp(g_last) S + K^T D' ----
+    // ---- S = exp(g_last) S + K^T D'  (KD: each state row by its channel's decay) ----
+    if constexpr (KD) {
+      const float* dec = reinterpret_cast<const float*>(buf + OFF_DEC) + 4 * g4;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4_t dv4 = *reinterpret_cast<const f32x4_t*>(dec + 16 * dt);
 #pragma unroll
-      for (int ct = 0; ct < NC; ++ct) Sacc[dt][ct] *= eg;
+        for (int ct = 0; ct < NC; ++ct) Sacc[dt][ct] *= dv4;
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) Sacc[dt][ct] *= eg;
+    }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -413,6 +438,7 @@ struct Scan2 {
     char* buf0 = smem;
     char* buf1 = smem + (NBUF == 2 ? BUF : 0);
     auto tok_of = [&](int c) { return static_cast<int64_t>(row.bos) + static_cast<int64_t>(c) * kChunk; };
+    auto hr_of = [&](int c) { return static_cast<int64_t>(row.chunk_off) + c; };
     auto nv_of = [&](int c) { return min(kChunk, row.len - c * kChunk); };
     if (nchunks > 0) {
       if (NBUF == 1) {
@@ -420,13 +446,13 @@ struct Scan2 {
         // the next chunk's loads are in flight during the compute
         Stage st;
         char* so = smem + OFF_HS;
-        load(st, x, tok_of(0), nv_of(0));
+        load(st, x, tok_of(0), nv_of(0), hr_of(0));
         for (int c = 0; c < nchunks; ++c) {
           __syncthreads();
           if (STAGE && c > 0) write_out(x, row, c - 1, so);
           store(st, x, buf0, nv_of(c));
           __syncthreads();
-          if (c + 1 < nchunks) load(st, x, tok_of(c + 1), nv_of(c + 1));
+          if (c + 1 < nchunks) load(st, x, tok_of(c + 1), nv_of(c + 1), hr_of(c + 1));
           compute(Sacc, x, row, c, buf0, so);
         }
         if (STAGE) {
@@ -435,13 +461,13 @@ struct Scan2 {
         }
       } else if (PF == 1) {
         Stage st;
-        load(st, x, tok_of(0), nv_of(0));
+        load(st, x, tok_of(0), nv_of(0), hr_of(0));
         store(st, x, buf0, nv_of(0));
         __syncthreads();
         for (int c = 0; c < nchunks; ++c) {
           char* cur = (c & 1) ? buf1 : buf0;
           char* nxt = (c & 1) ? buf0 : buf1;
-          if (c + 1 < nchunks) load(st, x, tok_of(c + 1), nv_of(c + 1));
+          if (c + 1 < nchunks) load(st, x, tok_of(c + 1), nv_of(c + 1), hr_of(c + 1));
           compute(Sacc, x, row, c, cur);
           if (c + 1 < nchunks) store(st, x, nxt, nv_of(c + 1));
           __syncthreads();
@@ -450,17 +476,17 @@ struct Scan2 {
         // two chunks in flight; loads and LDS fills are unconditional (chunks
         // past the end load as empty ranges and are never computed)
         Stage A, B;
-        load(A, x, tok_of(0), nv_of(0));
-        load(B, x, tok_of(1), nv_of(1));
+        load(A, x, tok_of(0), nv_of(0), hr_of(0));
+        load(B, x, tok_of(1), nv_of(1), hr_of(1));
         store(A, x, buf0, nv_of(0));
         __syncthreads();
         for (int c = 0; c < nchunks; c += 2) {
-          load(A, x, tok_of(c + 2), nv_of(c + 2));
+          load(A, x, tok_of(c + 2), nv_of(c + 2), hr_of(c + 2));
           compute(Sacc, x, row, c, buf0);
           store(B, x, buf1, nv_of(c + 1));
           __syncthreads();
           if (c + 1 >= nchunks) break;
-          load(B, x, tok_of(c + 3), nv_of(c + 3));
+          load(B, x, tok_of(c + 3), nv_of(c + 3), hr_of(c + 3));
           compute(Sacc, x, row, c + 1, buf1);
           store(A, x, buf0, nv_of(c + 2));
           __syncthreads();
@@ -501,16 +527,16 @@ struct Scan2 {
   }
 };
 
-template <int DK, int BV, int NW, int PF, int MODE, int NBUF>
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD>
 __global__ __launch_bounds__(NW * 64) void scan2_kernel(const ScanArgs a) {
-  using K = Scan2<DK, BV, NW, PF, MODE, NBUF>;
+  using K = Scan2<DK, BV, NW, PF, MODE, NBUF, KD>;
   __shared__ __align__(16) char smem[K::SMEM];
   K::run(a, smem);
 }
 
-template <int DK, int BV, int NW, int PF, int MODE, int NBUF>
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD>
 static hipError_t launch_scan2(const void* args, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((scan2_kernel<DK, BV, NW, PF, MODE, NBUF>), dim3(grid), dim3(NW * 64), 0, stream,
+  hipLaunchKernelGGL((scan2_kernel<DK, BV, NW, PF, MODE, NBUF, KD>), dim3(grid), dim3(NW * 64), 0, stream,
                      *static_cast<const ScanArgs*>(args));
   return hipGetLastError();
 }
@@ -528,10 +554,11 @@ static hipError_t launch_scan2(const void* args, int grid, hipStream_t stream) {
   X(DK, 128, 4, 2, MODE, 1, 1)       \
   X(DK, 128, 4, 3, MODE, 2, 2)
 
-#define GDR_SCAN2_CASE(DK, BV, NW, ST, MODE, PF, NBUF) \
-  if (dk == DK && bv == BV && waves == NW && stages == ST && mode == MODE) return &launch_scan2<DK, BV, NW, PF, MODE, NBUF>;
+#define GDR_SCAN2_CASE(DK, BV, NW, ST, MODE, PF, NBUF)                                        \
+  if (dk == DK && bv == BV && waves == NW && stages == ST && mode == MODE)                      \
+    return kd ? &launch_scan2<DK, BV, NW, PF, MODE, NBUF, true> : &launch_scan2<DK, BV, NW, PF, MODE, NBUF, false>;
 
-LaunchFn find_scan2(int dk, int bv, int waves, int stages, int mode) {
+LaunchFn find_scan2(int dk, int bv, int waves, int stages, int mode, bool kd) {
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 128, 0)
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 128, 1)
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 128, 2)

@@ -17,7 +17,7 @@ def _declared():
     src = open(os.path.join(ROOT, "include", "gdr.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", src, flags=re.M)
-    return sorted(set(n for n in names if n.startswith(("gdr_", "abc_"))))
+    return sorted(set(n for n in names if n.startswith(("gdr_", "abc_", "kda_"))))
 
 
 def test_every_declared_symbol_is_exported():
@@ -212,3 +212,22 @@ def test_abc_read_validation():
     bad[4] = None  # z
     assert L.abc_chunk_output(ctypes.byref(p), *bad) == B.GDR_ERR_INVALID_ARG
     assert "z" in L.gdr_last_error().decode()
+
+
+def test_kda_validation():
+    """The per-channel decay entry points validate before any launch."""
+    L = B.lib()
+    p, keep = _prob(T=128, dtype=B.GDR_F32)
+    args = [FAKE] * 9
+    assert L.kda_chunk_prepare(ctypes.byref(p), *args, None) == B.GDR_ERR_UNSUPPORTED  # bfloat16 only
+    p, keep = _prob(T=128)
+    bad = [FAKE] * 9
+    bad[2] = None  # g
+    assert L.kda_chunk_prepare(ctypes.byref(p), *bad, None) == B.GDR_ERR_INVALID_ARG
+    assert "g" in L.gdr_last_error().decode()
+    assert L.kda_state_scan(ctypes.byref(p), None, None, FAKE, FAKE, FAKE, None, None, None, None, None,
+                            None) == B.GDR_ERR_INVALID_ARG  # decay missing
+    assert L.kda_chunk_output(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, ctypes.c_float(1.0), FAKE,
+                              None) == B.GDR_ERR_INVALID_ARG  # g_cum missing
+    assert L.kda_segment_summaries(ctypes.byref(p), None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == B.GDR_ERR_INVALID_ARG  # n_segments

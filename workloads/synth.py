@@ -77,7 +77,7 @@ class GdrInputs:
     """Inputs of one gated-delta-rule problem, stored on the CPU.
 
     q, k: [B, T, H, DK]; v: [B, T, H, DV] in ``dtype``.  g (per-token log decay)
-    and beta: [B, T, H] float32.  Packed variable-length batches use B = 1 with
+    and beta: [B, T, H] float32 (per-channel gates: g [B, T, H, DK]).  Packed variable-length batches use B = 1 with
     ``cu_seqlens`` (int32, N+1 entries).  h0: [N, H, DK, DV] float32 or None.
     """
 
@@ -165,6 +165,10 @@ def make_gdr(seed: int, *, lengths: Optional[Sequence[int]] = None, B: int = 1, 
     if gates == "logsigmoid":
         beta = _sigmoid(rng.standard_normal((B, T, H)))
         g = _logsigmoid(rng.normal(4.0, 1.0, (B, T, H)))
+    elif gates == "logsigmoid_channels":
+        # per-key-channel decays: every (token, head, channel) its own logsigmoid(N(4, 1))
+        beta = _sigmoid(rng.standard_normal((B, T, H)))
+        g = _logsigmoid(rng.normal(4.0, 1.0, (B, T, H, DK)))
     elif gates == "near_one":
         beta = rng.uniform(0.01, 0.05, (B, T, H))
         g = np.log1p(-1e-4 * rng.uniform(0.0, 1.0, (B, T, H)))
@@ -237,7 +241,7 @@ def make_abc(seed: int, *, B: int, T: int, H: int, K: int, M: int, V: int,
     return AbcInputs(name=name, k=k, v=v, s=s, dtype=dtype, meta={"seed": seed})
 
 
-# The five seeded workloads.  Seed i belongs to workload i.
+# The seeded workloads.  Seed i belongs to workload i.
 CONFIGS = {
     "tiny_fp32": dict(kind="gdr", seed=0, B=1, T=256, H=1, DK=64, DV=64, dtype="f32",
                       varlen=False, gates="logsigmoid", h0_std=None),
@@ -252,6 +256,11 @@ CONFIGS = {
     "long_state_h1": dict(kind="gdr", seed=3, B=1, T=65536, H=1, DK=128, DV=128, dtype="bf16",
                           varlen=False, gates="near_one", h0_std=None, n_segments=16),
     "abc_affine": dict(kind="abc", seed=4, B=2, T=16384, H=4, K=256, M=64, V=512, dtype="bf16"),
+    # per-key-channel decay on the question-rows shape (no such workload is on the pages;
+    # the shape of question_rows with a per-channel gate)
+    "kda_question_rows": dict(kind="gdr", seed=5, n_seqs=24, len_lo=16, len_hi=256, avoid=None,
+                              H=16, DK=128, DV=128, dtype="bf16", varlen=True,
+                              gates="logsigmoid_channels", h0_std=0.1),
 }
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
