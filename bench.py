@@ -259,6 +259,7 @@ def main():
         out["new_states"] = new_states(pkg, torch, dev)
         out["abc_affine"] = abc_affine(pkg, torch, dev)
         out["reverse"] = reverse(pkg, torch, dev, args.workload)
+        out["per_channel_decay"] = per_channel_decay(pkg, torch, dev)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
@@ -330,6 +331,47 @@ def new_states(pkg, torch, dev):
     return {"workload": "new_states (8 seqs, 18261 tokens, H=32, dk=dv=128, bf16)", "scan_us": round(us, 1),
             "Mtok_head_per_s": round(inp.token_heads / us, 1), "alg_bytes": alg,
             "frac_of_hbm": round(alg / (us * 1e-6) / 8e12, 4)}
+
+
+def kda_alg_bytes(lengths, H, DK, DV):
+    """Per-channel decay, bf16 storage, FP32 h0/hT: minimum bytes of each call.
+    prepare: read k, v (bf16), g (FP32 per channel), beta; write g_cum (FP32 per
+    channel), w, u, kg (bf16) and the chunk decays (FP32, DK per chunk-head).
+    scan: read kg, w, u, the chunk decays and h0; write v_new, h (bf16) and hT.
+    output: read q, k, v_new (bf16), g_cum (FP32 per channel) and h; write o."""
+    toks = sum(lengths) * H
+    chunks = sum((L + 63) // 64 for L in lengths) * H
+    seqs = len(lengths) * H
+    prep = toks * ((DK + DV) * 2 + DK * 4 + 4 + DK * 4 + (2 * DK + DV) * 2) + chunks * DK * 4
+    scan = toks * ((2 * DK + DV) * 2 + DV * 2) + chunks * (DK * 4 + DK * DV * 2) + seqs * DK * DV * 4 * 2
+    outp = toks * ((2 * DK + DV) * 2 + DK * 4 + DV * 2) + chunks * DK * DV * 2
+    return prep, scan, outp
+
+
+def per_channel_decay(pkg, torch, dev):
+    """The per-key-channel decay forward on the question-rows shape (24 packed
+    sequences, 3400 tokens, 16 heads, per-channel gates): prepare, state scan
+    and output, each timed alone."""
+    from workloads import make_config
+
+    inp = make_config("kda_question_rows")
+    q, k, v, g, beta, h0 = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta, inp.h0))
+    cu = inp.cu_seqlens
+    g_cum, w, u, kg, decay = pkg.kda_chunk_prepare(k, v, g, beta, cu)
+    h, v_new, hT = pkg.kda_state_scan(kg, w, u, decay, h0, cu)
+    scale = inp.DK ** -0.5
+    t_p = _event_median_us(torch, lambda: pkg.kda_chunk_prepare(k, v, g, beta, cu))
+    t_s = _event_median_us(torch, lambda: pkg.kda_state_scan(kg, w, u, decay, h0, cu))
+    t_o = _event_median_us(torch, lambda: pkg.kda_chunk_output(q, k, v_new, h, g_cum, scale, cu))
+    bp, bs, bo = kda_alg_bytes(inp.lengths, inp.H, inp.DK, inp.DV)
+
+    def leg(us, b):
+        return {"us": round(us, 1), "alg_bytes": b, "frac_of_hbm": round(b / (us * 1e-6) / 8e12, 4)}
+
+    return {"workload": "kda_question_rows (24 seqs, 3400 tokens, H=16, dk=dv=128, bf16, per-channel decay)",
+            "prepare": leg(t_p, bp), "scan": leg(t_s, bs), "output": leg(t_o, bo),
+            "step_us": round(t_p + t_s + t_o, 1),
+            "Mtok_head_per_s": round(inp.token_heads / (t_p + t_s + t_o), 1)}
 
 
 def abc_alg_bytes(B, T, H, K, M, V):
