@@ -530,7 +530,7 @@ gdr_status kda_chunk_output(const gdr_problem* p, const void* q, const void* k, 
   a.o = o;
   a.scale = scale;
   a.H = pr.H;
-  for (const gdr::Launch& l : gdr::plan_chunks(pr, pr.DV / 64)) {
+  for (const gdr::Launch& l : gdr::plan_chunks(pr, 1)) {  // one workgroup per (chunk, head)
     a.n_rows = static_cast<int32_t>(l.rows.size());
     a.n_chunks = l.n_chunks;
     a.chunk_base = l.chunk_base;

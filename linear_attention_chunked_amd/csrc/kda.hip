@@ -113,12 +113,21 @@ struct KdaPrepare {
   static constexpr int GS = DK + 4;         // FP32 Gam rows (floats), padded
   static constexpr int LDA = 64 + 4;
 
+  // Regions reused once their first contents are dead, so that two
+  // workgroups share a CU (about 70 KB): K then V (V waits in registers until
+  // the decayed products no longer read K); Gam then the bf16 hi / lo parts
+  // of K e^{Gam}; A then T.
+  static constexpr int RKV = (SKB > SVB ? SKB : SVB) * kChunk;
+  static constexpr int RG = (GS * 4 > 2 * SKB ? GS * 4 : 2 * SKB) * kChunk;
   struct Smem {
-    char k[kChunk * SKB];
-    char v[kChunk * SVB];
-    char ke_hi[kChunk * SKB];   // K * e^{Gam}: bf16 hi and lo parts
-    char ke_lo[kChunk * SKB];
-    float gam[kChunk * GS];
+    union {
+      char k[RKV];
+      char v[RKV];
+    };
+    union {
+      float gam[RG / 4];
+      char ke[RG];              // ke_hi rows [0, 64), ke_lo rows [64, 128), stride SKB
+    };
     union {
       float a[kChunk * LDA];
       float t[kChunk * LDA];
@@ -140,7 +149,9 @@ struct KdaPrepare {
     const int nvalid = min(kChunk, row.len - cl * kChunk);
     const int64_t H = a.H;
 
-    // ---- K, V (bf16), g (FP32), beta into LDS; rows past the tail read as zero ----
+    // ---- K (bf16), g (FP32), beta into LDS, V into registers; rows past the tail read as zero ----
+    constexpr int VPT = kChunk * (DV / 8) / NT;
+    u32x4_t vreg[VPT];
     {
       const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (tok0 * H + hd) * DK;
       const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + hd) * DV;
@@ -158,8 +169,7 @@ struct KdaPrepare {
 #pragma unroll
       for (int i = 0; i < kChunk * CV / NT; ++i) {
         const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
-        *reinterpret_cast<u32x4_t*>(sm.v + r * SVB + c * 16) =
-            __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
+        vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < kChunk * CG / NT; ++i) {
@@ -178,47 +188,27 @@ struct KdaPrepare {
 
     // ---- Gam: inclusive cumulative sum over the chunk's tokens, per channel
     //      (rows past the tail add zero, so they repeat the last value) ----
-    if (tid < DK) {
+    if (tid < DK) {  // the 64 reads are independent; only the adds form a chain
+      float gv[kChunk];
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) gv[t] = sm.gam[t * GS + tid];
       float x = 0.f;
-      float* go = a.g_cum + (tok0 * H + hd) * DK + tid;
+#pragma unroll
       for (int t = 0; t < kChunk; ++t) {
-        x += sm.gam[t * GS + tid];
-        sm.gam[t * GS + tid] = x;
-        if (t < nvalid) go[t * H * DK] = x;
+        x += gv[t];
+        gv[t] = x;
+      }
+      float* go = a.g_cum + (tok0 * H + hd) * DK;
+      const rsrc_t rgo = make_rsrc(go, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 4));
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) {
+        sm.gam[t * GS + tid] = gv[t];
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gv[t]), rgo,
+                                              static_cast<int>((t * H * DK + tid) * 4), 0, 0);
       }
       a.decay[((static_cast<int64_t>(a.chunk_base) + chunk) * H + hd) * DK + tid] = exp_fast(x);
     }
     __syncthreads();
-
-    // ---- K * e^{Gam} (hi / lo parts, LDS) and kg = K * e^{Gam_last - Gam} (global) ----
-    {
-      uint16_t* kgp = static_cast<uint16_t*>(a.kg) + (tok0 * H + hd) * DK;
-      const rsrc_t rkg = make_rsrc(kgp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
-      constexpr int CK = DK / 8;
-#pragma unroll
-      for (int i = 0; i < kChunk * CK / NT; ++i) {
-        const int vv = tid + i * NT, r = vv / CK, c = vv % CK;
-        const u32x4_t kq = *reinterpret_cast<const u32x4_t*>(sm.k + r * SKB + c * 16);
-        const float* gt = sm.gam + r * GS + 8 * c;
-        const float* gl = sm.gam + (kChunk - 1) * GS + 8 * c;
-        uint32_t hw[4], lw[4], gw[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t wd = kq[p];
-          const float k0 = __builtin_bit_cast(float, wd << 16), k1 = __builtin_bit_cast(float, wd & 0xffff0000u);
-          uint16_t h0, l0, h1, l1;
-          split_bf16(k0 * exp_fast(gt[2 * p]), h0, l0);
-          split_bf16(k1 * exp_fast(gt[2 * p + 1]), h1, l1);
-          hw[p] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-          lw[p] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
-          gw[p] = pack_bf16x2(k0 * exp_fast(gl[2 * p] - gt[2 * p]), k1 * exp_fast(gl[2 * p + 1] - gt[2 * p + 1]));
-        }
-        *reinterpret_cast<u32x4_t*>(sm.ke_hi + r * SKB + c * 16) = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-        *reinterpret_cast<u32x4_t*>(sm.ke_lo + r * SKB + c * 16) = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{gw[0], gw[1], gw[2], gw[3]}, rkg,
-                                               static_cast<int>(r * H * DK * 2 + c * 16), 0, 0);
-      }
-    }
 
     // ---- A rows of block `wave`: b_t sum_d k_td k_id e^{Gam_td - Gam_id}, i < t ----
     {
@@ -235,6 +225,53 @@ struct KdaPrepare {
       }
     }
     __syncthreads();
+
+    // ---- K * e^{Gam} (hi / lo parts, registers) and kg = K * e^{Gam_last - Gam} (global) ----
+    constexpr int KPT = kChunk * (DK / 8) / NT;
+    u32x4_t khi[KPT], klo[KPT];
+    {
+      uint16_t* kgp = static_cast<uint16_t*>(a.kg) + (tok0 * H + hd) * DK;
+      const rsrc_t rkg = make_rsrc(kgp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
+      constexpr int CK = DK / 8;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int vv = tid + i * NT, r = vv / CK, c = vv % CK;
+        const u32x4_t kq = *reinterpret_cast<const u32x4_t*>(sm.k + r * SKB + c * 16);
+        const float* gt = sm.gam + r * GS + 8 * c;
+        const float* gl = sm.gam + (kChunk - 1) * GS + 8 * c;
+        uint32_t hw[4], lw[4], gw[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t wd = kq[p];
+          const float k0 = __builtin_bit_cast(float, wd << 16), k1 = __builtin_bit_cast(float, wd & 0xffff0000u);
+          uint16_t h0, l0, h1, l1;
+          split_bf16(k0 * exp_fast(gt[2 * p]), h0, l0);
+          split_bf16(k1 * exp_fast(gt[2 * p + 1]), h1, l1);
+          hw[p] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+          lw[p] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+          gw[p] = pack_bf16x2(k0 * exp_fast(gl[2 * p] - gt[2 * p]), k1 * exp_fast(gl[2 * p + 1] - gt[2 * p + 1]));
+        }
+        khi[i] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+        klo[i] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{gw[0], gw[1], gw[2], gw[3]}, rkg,
+                                               static_cast<int>(r * H * DK * 2 + c * 16), 0, 0);
+      }
+    }
+    __syncthreads();  // K and Gam are dead: V over K, the parts of K e^{Gam} over Gam
+    {
+      constexpr int CK = DK / 8, CV = DV / 8;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int vv = tid + i * NT, r = vv / CK, c = vv % CK;
+        *reinterpret_cast<u32x4_t*>(sm.ke + r * SKB + c * 16) = khi[i];
+        *reinterpret_cast<u32x4_t*>(sm.ke + (kChunk + r) * SKB + c * 16) = klo[i];
+      }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
+        *reinterpret_cast<u32x4_t*>(sm.v + r * SVB + c * 16) = vreg[i];
+      }
+    }
 
     // ---- T = (I + A)^-1 by 16-blocks: diagonal blocks by forward substitution,
     //      off-diagonal blocks as FP32 products (A and T share one matrix) ----
@@ -331,8 +368,8 @@ struct KdaPrepare {
       for (int s = 0; s < 2; ++s) {
         if (s < nsteps) {
           const int off = (32 * s + tr_row) * SKB + 32 * dt + tr_col;
-          const frag fh = S::frag_from_quads(lds_tr16(sm.ke_hi, off), lds_tr16(sm.ke_hi, off + 16 * SKB));
-          const frag fl = S::frag_from_quads(lds_tr16(sm.ke_lo, off), lds_tr16(sm.ke_lo, off + 16 * SKB));
+          const frag fh = S::frag_from_quads(lds_tr16(sm.ke, off), lds_tr16(sm.ke, off + 16 * SKB));
+          const frag fl = S::frag_from_quads(lds_tr16(sm.ke, kChunk * SKB + off), lds_tr16(sm.ke, (kChunk + 16) * SKB + off));
           S::mma(acc, fh, bb_hi[s]);
           S::mma(acc, fh, bb_lo[s]);
           S::mma(acc, fl, bb_hi[s]);
@@ -360,14 +397,16 @@ struct KdaPrepare {
 };
 
 // ------------------------------------------------------------------ output
-// One workgroup (4 waves) per (chunk, head, 64 value columns); wave I owns the
-// rows of token block I.
+// One workgroup (4 waves) per (chunk, head) over all value columns (P is
+// formed once per chunk); wave I owns the rows of token block I.  The A
+// operand (Q e^Gam, bf16 hi and lo parts) is formed in registers from the
+// row-major Q and Gam tiles.
 template <int DK, int DV>
 struct KdaOutput {
   using S = St<bf16_t>;
   using frag = S::frag;
   static constexpr int NT = 256;
-  static constexpr int BVO = 64;
+  static constexpr int BVO = DV;
   static constexpr int NCT = BVO / 16;
   static constexpr int SQ = DK * 2 + 16;
   static constexpr int SV = BVO * 2 + 32;
@@ -378,8 +417,6 @@ struct KdaOutput {
   struct Smem {
     char q[kChunk * SQ];
     char k[kChunk * SQ];
-    char qe_hi[kChunk * SQ];   // Q * e^{Gam}: bf16 hi and lo parts
-    char qe_lo[kChunk * SQ];
     char h[BVO * SQ];
     char v[kChunk * SV];
     float gam[kChunk * GS];
@@ -425,6 +462,10 @@ struct KdaOutput {
         const int go = static_cast<int>(r * H * DK * 2 + c * 16);
         *reinterpret_cast<u32x4_t*>(sm.q + r * SQ + c * 16) = __builtin_amdgcn_raw_buffer_load_b128(rq, go, 0, 0);
         *reinterpret_cast<u32x4_t*>(sm.k + r * SQ + c * 16) = __builtin_amdgcn_raw_buffer_load_b128(rk, go, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < BVO * CQ / NT; ++i) {
+        const int vv = tid + i * NT, r = vv / CQ, c = vv % CQ;
         *reinterpret_cast<u32x4_t*>(sm.h + r * SQ + c * 16) =
             __builtin_amdgcn_raw_buffer_load_b128(rh, static_cast<int>(r * DK * 2 + c * 16), 0, 0);
       }
@@ -442,29 +483,6 @@ struct KdaOutput {
       }
     }
     __syncthreads();
-
-    // ---- Q * e^{Gam} split into bf16 hi / lo (rows past the tail: q is zero) ----
-    {
-      constexpr int CQ = DK / 8;
-#pragma unroll
-      for (int i = 0; i < kChunk * CQ / NT; ++i) {
-        const int vv = tid + i * NT, r = vv / CQ, c = vv % CQ;
-        const u32x4_t qq = *reinterpret_cast<const u32x4_t*>(sm.q + r * SQ + c * 16);
-        const float* gt = sm.gam + r * GS + 8 * c;
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t wd = qq[p];
-          uint16_t h0, l0, h1, l1;
-          split_bf16(__builtin_bit_cast(float, wd << 16) * exp_fast(gt[2 * p]), h0, l0);
-          split_bf16(__builtin_bit_cast(float, wd & 0xffff0000u) * exp_fast(gt[2 * p + 1]), h1, l1);
-          hw[p] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-          lw[p] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
-        }
-        *reinterpret_cast<u32x4_t*>(sm.qe_hi + r * SQ + c * 16) = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-        *reinterpret_cast<u32x4_t*>(sm.qe_lo + r * SQ + c * 16) = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
-      }
-    }
 
     // ---- P rows of block `wave`: sum_d q_td k_id e^{Gam_td - Gam_id}, i <= t ----
     {
@@ -489,9 +507,27 @@ struct KdaOutput {
     __syncthreads();
 
     // ---- O = (Q e^Gam) S_c + P v_new, rows of token tile `wave` ----
-    const char* rowqh = sm.qe_hi + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;
-    const char* rowql = sm.qe_lo + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;
     const char* rowh = sm.h + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;
+    // this lane's A-operand elements of row 16 wave + c16: channels 32 s + 4 g4 + {0..3} and + 16
+    const char* qrow = sm.q + (16 * wave + c16) * SQ;
+    const float* grow = sm.gam + (16 * wave + c16) * GS;
+    auto qe_frags = [&](int s2, frag& fh, frag& fl) {
+      f32x4_t x[2], lo[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int d0 = 32 * s2 + 16 * half + 4 * g4;
+        const u32x2_t qq = *reinterpret_cast<const u32x2_t*>(qrow + 2 * d0);
+        const f32x4_t gv = *reinterpret_cast<const f32x4_t*>(grow + d0);
+        x[half] = f32x4_t{__builtin_bit_cast(float, qq.x << 16) * exp_fast(gv[0]),
+                          __builtin_bit_cast(float, qq.x & 0xffff0000u) * exp_fast(gv[1]),
+                          __builtin_bit_cast(float, qq.y << 16) * exp_fast(gv[2]),
+                          __builtin_bit_cast(float, qq.y & 0xffff0000u) * exp_fast(gv[3])};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lo[half][r] = x[half][r] - bf16_to_f32(f32_to_bf16(x[half][r]));
+      }
+      fh = S::frag_from_f32(x[0], x[1]);
+      fl = S::frag_from_f32(lo[0], lo[1]);
+    };
     auto rfrag = [&](const char* base, int tile, int s) {
       return S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(base + 16 * tile * SQ + 64 * s),
                                 *reinterpret_cast<const u32x2_t*>(base + 16 * tile * SQ + 64 * s + 32));
@@ -501,8 +537,8 @@ struct KdaOutput {
     for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const frag fh = rfrag(rowqh, wave, s);
-      const frag fl = rfrag(rowql, wave, s);
+      frag fh, fl;
+      qe_frags(s, fh, fl);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const frag hb = rfrag(rowh, ct, s);
