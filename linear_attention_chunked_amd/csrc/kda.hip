@@ -398,136 +398,155 @@ struct KdaPrepare {
 
 // ------------------------------------------------------------------ output
 // One workgroup (4 waves) per (chunk, head) over all value columns (P is
-// formed once per chunk); wave I owns the rows of token block I.  The A
-// operand (Q e^Gam, bf16 hi and lo parts) is formed in registers from the
-// row-major Q and Gam tiles.
+// formed once per chunk); wave I owns the rows of token block I.  Two phases
+// share one LDS region so that two workgroups fit on a CU: first Q, K and Gam
+// give each wave its rows of P and its A operand Q e^{Gam} (bf16 hi and lo
+// parts), both kept in registers; then the pre-chunk state and v_new (read
+// into registers at the start) and P take the region for the two products.
 template <int DK, int DV>
 struct KdaOutput {
   using S = St<bf16_t>;
   using frag = S::frag;
   static constexpr int NT = 256;
-  static constexpr int BVO = DV;
-  static constexpr int NCT = BVO / 16;
+  static constexpr int NCT = DV / 16;
   static constexpr int SQ = DK * 2 + 16;
-  static constexpr int SV = BVO * 2 + 32;
+  static constexpr int SV = DV * 2 + 32;
   static constexpr int GS = DK + 4;
   static constexpr int LP = 64 + 4;
   static constexpr int KS = DK / 32;
 
-  struct Smem {
+  struct PhaseA {
     char q[kChunk * SQ];
     char k[kChunk * SQ];
-    char h[BVO * SQ];
-    char v[kChunk * SV];
     float gam[kChunk * GS];
+  };
+  struct PhaseB {
+    char h[DV * SQ];
+    char v[kChunk * SV];
     float p[kChunk * LP];
   };
+  union Smem {
+    PhaseA A;
+    PhaseB B;
+  };
+
+  static constexpr int CQ = DK / 8, CV = DV / 8, CG = DK / 4;
+  static constexpr int HPT = DV * CQ / NT, VPT = kChunk * CV / NT;
 
   __device__ static void run(const KdaArgs& a, Smem& sm) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    constexpr int NVB = DV / BVO;
     const int item = blockIdx.x;
-    const int vb = item % NVB;
-    const int rest = item / NVB;
-    const int chunk = rest / a.H;
-    const int hd = rest % a.H;
+    const int chunk = item / a.H;
+    const int hd = item % a.H;
     if (chunk >= a.n_chunks) return;
     const Row row = a.rows[kda_find_row(a, chunk)];
     const int cl = chunk - row.chunk_off;
     const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(cl) * kChunk;
     const int nvalid = min(kChunk, row.len - cl * kChunk);
     const int64_t H = a.H;
-    const int col0 = vb * BVO;
 
+    // ---- Q, K, Gam into LDS; S_c and v_new into registers (rows past the tail read as zero) ----
+    u32x4_t hreg[HPT], vreg[VPT];
     {
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (tok0 * H + hd) * DK;
       const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (tok0 * H + hd) * DK;
-      const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + hd) * DV + col0;
-      const uint16_t* hp = static_cast<const uint16_t*>(a.h) +
-                           ((static_cast<int64_t>(a.chunk_base) + chunk) * H + hd) * DV * DK +
-                           static_cast<int64_t>(col0) * DK;
+      const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + hd) * DV;
+      const uint16_t* hp = static_cast<const uint16_t*>(a.h) + ((static_cast<int64_t>(a.chunk_base) + chunk) * H + hd) * DV * DK;
       const float* gp = a.g + (tok0 * H + hd) * DK;
       const uint32_t qk_bytes = static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2);
       const rsrc_t rq = make_rsrc(qp, qk_bytes);
       const rsrc_t rk = make_rsrc(kp, qk_bytes);
-      const rsrc_t rv = make_rsrc(vp, static_cast<uint32_t>(((nvalid - 1) * H * DV + BVO) * 2));
-      const rsrc_t rh = make_rsrc(hp, static_cast<uint32_t>(BVO * DK * 2));
+      const rsrc_t rv = make_rsrc(vp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
+      const rsrc_t rh = make_rsrc(hp, static_cast<uint32_t>(DV * DK * 2));
       const rsrc_t rg = make_rsrc(gp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 4));
-      constexpr int CQ = DK / 8, CV = BVO / 8, CG = DK / 4;
+#pragma unroll
+      for (int i = 0; i < HPT; ++i) {
+        const int vv = tid + i * NT, r = vv / CQ, c = vv % CQ;
+        hreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rh, static_cast<int>(r * DK * 2 + c * 16), 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
+        vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
+      }
 #pragma unroll
       for (int i = 0; i < kChunk * CQ / NT; ++i) {
         const int vv = tid + i * NT, r = vv / CQ, c = vv % CQ;
         const int go = static_cast<int>(r * H * DK * 2 + c * 16);
-        *reinterpret_cast<u32x4_t*>(sm.q + r * SQ + c * 16) = __builtin_amdgcn_raw_buffer_load_b128(rq, go, 0, 0);
-        *reinterpret_cast<u32x4_t*>(sm.k + r * SQ + c * 16) = __builtin_amdgcn_raw_buffer_load_b128(rk, go, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < BVO * CQ / NT; ++i) {
-        const int vv = tid + i * NT, r = vv / CQ, c = vv % CQ;
-        *reinterpret_cast<u32x4_t*>(sm.h + r * SQ + c * 16) =
-            __builtin_amdgcn_raw_buffer_load_b128(rh, static_cast<int>(r * DK * 2 + c * 16), 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < kChunk * CV / NT; ++i) {
-        const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
-        *reinterpret_cast<u32x4_t*>(sm.v + r * SV + c * 16) =
-            __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
+        *reinterpret_cast<u32x4_t*>(sm.A.q + r * SQ + c * 16) = __builtin_amdgcn_raw_buffer_load_b128(rq, go, 0, 0);
+        *reinterpret_cast<u32x4_t*>(sm.A.k + r * SQ + c * 16) = __builtin_amdgcn_raw_buffer_load_b128(rk, go, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < kChunk * CG / NT; ++i) {
         const int vv = tid + i * NT, r = vv / CG, c = vv % CG;
-        *reinterpret_cast<u32x4_t*>(sm.gam + r * GS + c * 4) =
+        *reinterpret_cast<u32x4_t*>(sm.A.gam + r * GS + c * 4) =
             __builtin_amdgcn_raw_buffer_load_b128(rg, static_cast<int>(r * H * DK * 4 + c * 16), 0, 0);
       }
     }
     __syncthreads();
 
-    // ---- P rows of block `wave`: sum_d q_td k_id e^{Gam_td - Gam_id}, i <= t ----
+    // ---- P rows of block `wave` (registers): sum_d q_td k_id e^{Gam_td - Gam_id}, i <= t ----
+    f32x4_t pr[4];
     {
       float xs[DK / 4];
-      kda_row_side<DK, SQ, GS>(xs, sm.q, sm.gam, wave, g4, c16);
+      kda_row_side<DK, SQ, GS>(xs, sm.A.q, sm.A.gam, wave, g4, c16);
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
-        const int i = 16 * J + c16;
+        pr[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (J <= wave) {
-          const f32x4_t d = kda_block_product<DK, SQ, GS>(xs, sm.k, sm.gam, wave, J, g4, c16);
+          const f32x4_t d = kda_block_product<DK, SQ, GS>(xs, sm.A.k, sm.A.gam, wave, J, g4, c16);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 16 * wave + 4 * g4 + r;
-            sm.p[t * LP + i] = (i <= t) ? d[r] : 0.f;
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sm.p[(16 * wave + 4 * g4 + r) * LP + i] = 0.f;
+          for (int r = 0; r < 4; ++r) pr[J][r] = (16 * J + c16 <= 16 * wave + 4 * g4 + r) ? d[r] : 0.f;
         }
       }
     }
+    // ---- this lane's A-operand fragments of Q e^{Gam} (row 16 wave + c16) ----
+    frag qh[KS], ql[KS];
+    {
+      const char* qrow = sm.A.q + (16 * wave + c16) * SQ;
+      const float* grow = sm.A.gam + (16 * wave + c16) * GS;
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) {
+        f32x4_t x[2], lo[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int d0 = 32 * s2 + 16 * half + 4 * g4;
+          const u32x2_t qq = *reinterpret_cast<const u32x2_t*>(qrow + 2 * d0);
+          const f32x4_t gv = *reinterpret_cast<const f32x4_t*>(grow + d0);
+          x[half] = f32x4_t{__builtin_bit_cast(float, qq.x << 16) * exp_fast(gv[0]),
+                            __builtin_bit_cast(float, qq.x & 0xffff0000u) * exp_fast(gv[1]),
+                            __builtin_bit_cast(float, qq.y << 16) * exp_fast(gv[2]),
+                            __builtin_bit_cast(float, qq.y & 0xffff0000u) * exp_fast(gv[3])};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) lo[half][r] = x[half][r] - bf16_to_f32(f32_to_bf16(x[half][r]));
+        }
+        qh[s2] = S::frag_from_f32(x[0], x[1]);
+        ql[s2] = S::frag_from_f32(lo[0], lo[1]);
+      }
+    }
+    __syncthreads();  // Q, K, Gam are dead
+
+    // ---- phase B: S_c, v_new and P into the region ----
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) {
+      const int vv = tid + i * NT, r = vv / CQ, c = vv % CQ;
+      *reinterpret_cast<u32x4_t*>(sm.B.h + r * SQ + c * 16) = hreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
+      *reinterpret_cast<u32x4_t*>(sm.B.v + r * SV + c * 16) = vreg[i];
+    }
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.B.p[(16 * wave + 4 * g4 + r) * LP + 16 * J + c16] = pr[J][r];
     __syncthreads();
 
     // ---- O = (Q e^Gam) S_c + P v_new, rows of token tile `wave` ----
-    const char* rowh = sm.h + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;
-    // this lane's A-operand elements of row 16 wave + c16: channels 32 s + 4 g4 + {0..3} and + 16
-    const char* qrow = sm.q + (16 * wave + c16) * SQ;
-    const float* grow = sm.gam + (16 * wave + c16) * GS;
-    auto qe_frags = [&](int s2, frag& fh, frag& fl) {
-      f32x4_t x[2], lo[2];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int d0 = 32 * s2 + 16 * half + 4 * g4;
-        const u32x2_t qq = *reinterpret_cast<const u32x2_t*>(qrow + 2 * d0);
-        const f32x4_t gv = *reinterpret_cast<const f32x4_t*>(grow + d0);
-        x[half] = f32x4_t{__builtin_bit_cast(float, qq.x << 16) * exp_fast(gv[0]),
-                          __builtin_bit_cast(float, qq.x & 0xffff0000u) * exp_fast(gv[1]),
-                          __builtin_bit_cast(float, qq.y << 16) * exp_fast(gv[2]),
-                          __builtin_bit_cast(float, qq.y & 0xffff0000u) * exp_fast(gv[3])};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) lo[half][r] = x[half][r] - bf16_to_f32(f32_to_bf16(x[half][r]));
-      }
-      fh = S::frag_from_f32(x[0], x[1]);
-      fl = S::frag_from_f32(lo[0], lo[1]);
-    };
+    const char* rowh = sm.B.h + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;
     auto rfrag = [&](const char* base, int tile, int s) {
       return S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(base + 16 * tile * SQ + 64 * s),
                                 *reinterpret_cast<const u32x2_t*>(base + 16 * tile * SQ + 64 * s + 32));
@@ -536,23 +555,20 @@ struct KdaOutput {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      frag fh, fl;
-      qe_frags(s, fh, fl);
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const frag hb = rfrag(rowh, ct, s);
-        S::mma(acc[ct], fh, hb);
-        S::mma(acc[ct], fl, hb);
+        S::mma(acc[ct], qh[s], hb);
+        S::mma(acc[ct], ql[s], hb);
       }
-    }
-    const char* vb_ = sm.v + (4 * g4 + (c16 >> 2)) * SV + 8 * (c16 & 3);
+    const char* vb_ = sm.B.v + (4 * g4 + (c16 >> 2)) * SV + 8 * (c16 & 3);
     const int t = 16 * wave + c16;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (32 * s <= 16 * wave + 15) {
-        const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(&sm.p[t * LP + 32 * s + 4 * g4]);
-        const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(&sm.p[t * LP + 32 * s + 16 + 4 * g4]);
+        const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(&sm.B.p[t * LP + 32 * s + 4 * g4]);
+        const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(&sm.B.p[t * LP + 32 * s + 16 + 4 * g4]);
         f32x4_t l0, l1;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -570,8 +586,8 @@ struct KdaOutput {
       }
     }
 
-    uint16_t* op = static_cast<uint16_t*>(a.o) + (tok0 * H + hd) * DV + col0;
-    const rsrc_t ro = make_rsrc(op, static_cast<uint32_t>(((nvalid - 1) * H * DV + BVO) * 2));
+    uint16_t* op = static_cast<uint16_t*>(a.o) + (tok0 * H + hd) * DV;
+    const rsrc_t ro = make_rsrc(op, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
     const int rs = static_cast<int>(H * DV * 2);
     const int voff = (16 * wave + 4 * g4) * rs + c16 * 2;
 #pragma unroll
