@@ -134,6 +134,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="question_rows", choices=["question_rows", "new_states"])
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-state", action="store_true")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -219,6 +220,29 @@ def main():
         "mfma_frac": round(scan_flops(inp.lengths, inp.H, inp.DK, DV) / (scan_mean_ms * 1e-3) / 1e12
                            / BF16_PEAK_TFLOPS, 4),
     }
+
+    # Cold-cache figures (after the timed region): before every rep a 1 GiB
+    # fill evicts L2 and the 256 MB Infinity Cache (the step's 141 MB of scan
+    # traffic would otherwise partly stay resident between back-to-back steps).
+    if not args.no_cold:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cold_scan, cold_step = [], []
+        for _ in range(20):
+            flush.fill_(1.0)
+            e = (HipEvent(), HipEvent())
+            s0, s1 = HipEvent(), HipEvent()
+            s0.record(stream)
+            step(e)
+            s1.record(stream)
+            torch.cuda.synchronize()
+            cold_scan.append(e[0].elapsed_ms(e[1]) * 1e3)
+            cold_step.append(s0.elapsed_ms(s1) * 1e3)
+        del flush
+        cs = sorted(cold_scan)[len(cold_scan) // 2]
+        roofline["cold_cache"] = {"scan_us_median": round(cs, 2),
+                                  "step_us_median": round(sorted(cold_step)[len(cold_step) // 2], 2),
+                                  "scan_frac": round(alg / (cs * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "flush": "1 GiB fill before each of 20 single steps"}
 
     out = {
         "metric": "gated-delta state-scan Mtok-head/s + % roofline (varlen batch, 64K seq)",

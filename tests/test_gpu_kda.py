@@ -152,3 +152,37 @@ def test_kda_question_rows_workload(pkg):
     again = gpu_forward(pkg, inp, 128 ** -0.5)
     for key in ("o", "h", "hT", "v_new"):
         assert torch.equal(out[key], again[key]), f"run to run: {key}"
+
+
+def test_kda_empty_single_token_and_pool(pkg):
+    """Empty and one-token sequences (an empty sequence keeps its initial
+    state and writes nothing else), and indexed states: sequence n reads and
+    writes pool row idx[n] in place, other rows untouched."""
+    inp = problem(667, [0, 1, 0, 2, 70, 0], H=2, DK=64, DV=64, h0_std=0.3)
+    out = gpu_forward(pkg, inp, 1.0)
+    check_against_oracle(out, inp, 1.0, "kda empty/single", factors=False)
+    h0 = inp.h0.numpy()
+    for n, L in enumerate(inp.lengths):
+        if L == 0:
+            assert np.array_equal(out["hT"][n].cpu().numpy(), h0[n]), "an empty sequence keeps its initial state"
+    # pooled states, updated in place
+    q, k, v, g, b = (dev(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    g_cum, w, u, kg, decay = pkg.kda_chunk_prepare(k, v, g, b, inp.cu_seqlens)
+    idx = [5, 0, 3, 7, 2, 6]
+    pool = torch.randn(9, 2, 64, 64, device="cuda") * 0.1
+    for n, i in enumerate(idx):
+        pool[i] = inp.h0[n].cuda()
+    before = pool.clone()
+    B = pkg.binding
+    p = B.Problem(kg, 64, inp.cu_seqlens, "kv", idx, pool.shape[0])
+    nt = pkg.gdr_num_chunks(kg, 64, inp.cu_seqlens)
+    h = torch.empty((nt, 2, 64, 64), dtype=torch.bfloat16, device="cuda")
+    vn = torch.empty_like(u)
+    B._check(B.lib().kda_state_scan(p.ref, None, None, B._ptr(kg), B._ptr(w), B._ptr(u), B._ptr(decay),
+                                    B._ptr(pool), B._ptr(h), B._ptr(vn), B._ptr(pool), None), "kda_state_scan")
+    torch.cuda.synchronize()
+    for n, i in enumerate(idx):
+        assert torch.equal(pool[i], out["hT"][n]), f"pool row {i} (sequence {n})"
+    for i in (1, 4, 8):
+        assert torch.equal(pool[i], before[i]), f"untouched pool row {i}"
+    assert torch.equal(h, out["h"]) and torch.equal(vn, out["v_new"])
