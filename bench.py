@@ -14,7 +14,10 @@ Mtok-head/s), plus
                 each scan launch inside the timed region, against 8 TB/s;
   cpu_baseline  the FP64 numpy oracle timed on the host on the same batch;
   long_state    the 64K-token single-sequence workload (8 heads), serial
-                and 16-segment, measured after the timed region.
+                and 16-segment (whole path and each phase), measured after
+                the timed region.
+The roofline fractions are also given against the measured rate of a plain
+512 MiB device copy ("copy_gbs", "frac_of_copy").
 """
 
 from __future__ import annotations
@@ -278,8 +281,15 @@ def main():
         torch.cuda.synchronize()
         out["copy_ref"] = {"bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}
 
+    copy_gbs = copy_bandwidth(torch, dev)
+    roofline["copy_gbs"] = round(copy_gbs, 1)
+    roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
+    if "cold_cache" in roofline:
+        roofline["cold_cache"]["scan_frac_of_copy"] = round(
+            alg / (roofline["cold_cache"]["scan_us_median"] * 1e-6) / 1e9 / copy_gbs, 4)
+
     if not args.no_long_state:
-        out["long_state"] = long_state(pkg, torch, dev)
+        out["long_state"] = long_state(pkg, torch, dev, copy_gbs=copy_gbs)
         out["new_states"] = new_states(pkg, torch, dev)
         out["abc_affine"] = abc_affine(pkg, torch, dev)
         out["reverse"] = reverse(pkg, torch, dev, args.workload)
@@ -291,7 +301,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def long_state(pkg, torch, dev, reps=5):
+def long_state(pkg, torch, dev, reps=5, copy_gbs=None):
     """64K-token single sequence, 8 heads: serial scan and the 16-segment
     path (summaries + compose + segmented final pass), timed with HIP events."""
     from workloads import make_config
@@ -311,13 +321,48 @@ def long_state(pkg, torch, dev, reps=5):
         return pkg.gdr_state_scan(k, w, u, g_cum, None, None, None, P, si)
 
     res = {}
+    serial_alg = scan_alg_bytes(inp.lengths, inp.H, inp.DK, DV, 2, 2, False, True)
+    # segmented path: summaries read k, w, u, g_cum and write (S_loc, M) in
+    # FP32; compose reads them and writes S_init; the final pass is the serial
+    # scan's traffic plus reading S_init
+    summ = P * inp.H * inp.DK * (DV + inp.DK) * 4
+    init = P * inp.H * inp.DK * DV * 4
+    alg_phase = {"summaries": inp.token_heads * ((2 * inp.DK + DV) * 2 + 4) + summ,
+                 "compose": summ + init,
+                 "final_pass": serial_alg + init}
+    seg_alg = sum(alg_phase.values())
     for name, fn in (("serial", serial), ("segmented", segmented)):
         t = _event_median_us(torch, fn, reps=reps) * 1e-6
-        alg = scan_alg_bytes(inp.lengths, inp.H, inp.DK, DV, 2, 2, False, True)
         res[name] = {"us": round(t * 1e6, 1), "Mtok_head_per_s": round(inp.token_heads / t / 1e6, 1),
-                     "serial_alg_bytes": alg, "frac_of_hbm_at_serial_bytes": round(alg / t / 8e12, 4)}
+                     "serial_alg_bytes": serial_alg, "frac_of_hbm_at_serial_bytes": round(serial_alg / t / 8e12, 4)}
+    t = res["segmented"]["us"] * 1e-6
+    res["segmented"].update(alg_bytes=seg_alg, frac_of_hbm=round(seg_alg / t / 8e12, 4))
+    if copy_gbs:
+        res["segmented"]["frac_of_copy"] = round(seg_alg / t / 1e9 / copy_gbs, 4)
+    # each phase alone (inputs of the later phases computed once beforehand)
+    ss, st = pkg.gdr_segment_summaries(k, w, u, g_cum, P)
+    si, _ = pkg.gdr_segment_compose(k, DV, ss, st, P)
+    phases = {"summaries": lambda: pkg.gdr_segment_summaries(k, w, u, g_cum, P),
+              "compose": lambda: pkg.gdr_segment_compose(k, DV, ss, st, P),
+              "final_pass": lambda: pkg.gdr_state_scan(k, w, u, g_cum, None, None, None, P, si)}
+    res["segmented"]["phases"] = {}
+    for name, fn in phases.items():
+        tp = _event_median_us(torch, fn, reps=reps) * 1e-6
+        res["segmented"]["phases"][name] = {"us": round(tp * 1e6, 1), "alg_bytes": alg_phase[name],
+                                            "frac_of_hbm": round(alg_phase[name] / tp / 8e12, 4)}
     res["workload"] = "long_state_h8 (T=65536, H=8, dk=dv=128, bf16, 16 segments)"
     return res
+
+
+def copy_bandwidth(torch, dev, mib=512, reps=5):
+    """Achievable HBM rate of a plain device copy (torch copy_ of `mib` MiB:
+    the bytes read plus the bytes written, over the median of `reps`)."""
+    n = mib * (1 << 20) // 4
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    us = _event_median_us(torch, lambda: b.copy_(a), reps=reps, per=2)
+    del a, b
+    return 2 * n * 4 / (us * 1e-6) / 1e9
 
 
 def _event_median_us(torch, fn, reps=5, per=4):

@@ -110,6 +110,7 @@ bool parse_problem(int B, int64_t T, int H, int DK, int DV, int N, const int32_t
 
 // Built tiles (must match the instantiations in scan.hip).
 static bool tile_built(int dtype, int bv, int waves, int stages) {
+  if (dtype == 1 && bv == 256 && waves == 8 && (stages == 2 || stages == 3)) return true;  // summaries (mode 2)
   static const int bf16_tiles[][3] = {{32, 2, 2}, {32, 2, 3}, {64, 2, 3}, {64, 4, 2},
                                       {64, 4, 3}, {128, 4, 2}, {128, 4, 3}};
   static const int f32_tiles[][3] = {{32, 2, 1}, {32, 2, 2}, {64, 4, 1}, {64, 4, 2}};

@@ -28,6 +28,16 @@
 //   * U enters the accumulator negated and the sign is folded into the decay
 //     weights, so W needs no negation: acc = -U + W S = -D, v_new = -acc,
 //     D' = acc * (-exp(g_last - g)).
+//   * Segment summaries (MODE 1, 2) keep the state as a scalar multiple,
+//     S = sig * S', so the chunk's decay e^{g_last} is folded into the 64
+//     token weights (and the U tile into -1/sig) instead of multiplying all
+//     DK x BV accumulators every chunk: S' <- S' + K^T (acc' * nd / e^{g_last})
+//     with acc' = -U / sig + W S', sig <- sig e^{g_last}.  When sig would leave
+//     [2^-40, 2^40] the chunk instead renormalises (S' <- sig e^{g_last} S',
+//     weights nd * sig, sig <- 1), so no scale factor can overflow.  The
+//     result is the same state up to where bfloat16 rounding falls; it is
+//     still the same for every tile.  The plain pass (MODE 0) emits h from
+//     the true state every chunk and keeps the direct form.
 //   * Per-key-channel decay (KD): the caller passes the decayed keys
 //     kg = K * e^{Gam_last - Gam} in place of K and the chunk's channel decays
 //     e^{Gam_last} (one DK-vector per chunk and head); the weights are then
@@ -59,8 +69,11 @@ struct Scan2 {
   static constexpr int CPW = RBW / 16;    // 16-byte chunks per W row
   static constexpr int CPU = RBU / 16;
   static constexpr int OFF_W = 0, OFF_K = kChunk * SW, OFF_U = OFF_K + kChunk * SK;
-  static constexpr int OFF_D = OFF_U + kChunk * SU;   // 64 negated decay weights, then exp(g_last)
+  // 64 negated decay weights, then exp(g_last) (SIG: the state multiplier,
+  // the U scale -1/sig and sig after the chunk)
+  static constexpr int OFF_D = OFF_U + kChunk * SU;
   static constexpr int OFF_DEC = OFF_D + (kChunk + 4) * 4;  // KD: the chunk's DK channel decays
+  static constexpr bool SIG = (MODE != 0) && !KD;           // scaled-state form (summaries)
   static constexpr int BUF = OFF_DEC + (KD ? DK * 4 : 0);
   // Output staging (single-buffer loop, plain and segmented passes): the
   // chunk's h block and v_new tile are written to LDS in their memory layout
@@ -131,7 +144,7 @@ struct Scan2 {
     }
   }
 
-  __device__ static __forceinline__ void store(const Stage& st, const Ctx& x, char* buf, int nvalid) {
+  __device__ static __forceinline__ void store(const Stage& st, const Ctx& x, char* buf, int nvalid, float& sig) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < W_PT; ++i) {
@@ -157,8 +170,22 @@ struct Scan2 {
       const float g_last = __builtin_bit_cast(
           float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, st.g), max(nvalid, 1) - 1));
       float* d = reinterpret_cast<float*>(buf + OFF_D);
-      d[tid] = (tid < nvalid) ? -exp_fast(g_last - st.g) : 0.f;
-      if (tid == 0) d[kChunk] = exp_fast(g_last);
+      const float eg = exp_fast(g_last);
+      if constexpr (SIG) {  // (sig is tracked by the first wave only)
+        const float sn = sig * eg;
+        const bool keep = (sn >= 0x1p-40f) && (sn <= 0x1p40f);
+        const float f = keep ? 1.f / eg : sig;
+        d[tid] = (tid < nvalid) ? -exp_fast(g_last - st.g) * f : 0.f;
+        if (tid == 0) {
+          d[kChunk] = keep ? 1.f : sn;
+          d[kChunk + 1] = -1.f / sig;
+          d[kChunk + 2] = keep ? sn : 1.f;
+        }
+        sig = keep ? sn : 1.f;
+      } else {
+        d[tid] = (tid < nvalid) ? -exp_fast(g_last - st.g) : 0.f;
+        if (tid == 0) d[kChunk] = eg;
+      }
     }
   }
 
@@ -196,14 +223,17 @@ struct Scan2 {
   // One chunk.  The W operand reads are issued before the first matrix
   // instruction, the K operand reads while GEMM1 runs, and the accumulator
   // chains are interleaved, so the chunk pays the LDS and MFMA latencies about
-  // once instead of once per product.
+  // once instead of once per product.  HASU: this wave's columns read U (the
+  // state columns); the transition columns start GEMM1 from a zero
+  // accumulator.  sig_out (SIG): the state's scale after the chunk.
+  template <bool HASU>
   __device__ static __forceinline__ void compute(f32x4_t (&Sacc)[DT][NC], const Ctx& x, const Row& row, int c,
-                                                 const char* buf, char* smem_out = nullptr) {  // smem_out: staging (STAGE)
+                                                 const char* buf, float& sig_out,
+                                                 char* smem_out = nullptr) {  // smem_out: staging (STAGE)
     const ScanArgs& a = *x.a;
     const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int colw = wave * (BV / NW);
-    const bool use_u = (MODE == 2) ? (wave < NW / 2) : x.has_u;  // wave-uniform
     const int64_t H = x.H;
     const int DV = x.DV;
     const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(c) * kChunk;
@@ -217,7 +247,7 @@ struct Scan2 {
     const float* nd_l = reinterpret_cast<const float*>(buf + OFF_D) + 4 * g4;          // + 16 mt
 
     u32x2_t uq[4][NC];
-    if (use_u) {
+    if constexpr (HASU) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -237,28 +267,40 @@ struct Scan2 {
 #pragma unroll
       for (int ct = 0; ct < NC; ++ct) Sb[s][ct] = S::frag_from_f32(Sacc[2 * s][ct], Sacc[2 * s + 1][ct]);
 
-    // ---- acc = -U + W S  (= -D); independent chains interleaved ----
+    // ---- acc = -U + W S  (= -D; SIG: -U / sig + W S'); independent chains interleaved ----
     f32x4_t acc[4][NC];
+    if constexpr (HASU) {
+      const float us = SIG ? reinterpret_cast<const float*>(buf + OFF_D)[kChunk + 1] : -1.f;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int ct = 0; ct < NC; ++ct) {
-        if (use_u) {
-          const u32x2_t q = uq[mt][ct];  // bf16 -> f32 with the sign flipped in the same instruction
-          acc[mt][ct] = f32x4_t{__builtin_bit_cast(float, (q.x << 16) + 0x80000000u),
-                                __builtin_bit_cast(float, (q.x & 0xffff0000u) ^ 0x80000000u),
-                                __builtin_bit_cast(float, (q.y << 16) + 0x80000000u),
-                                __builtin_bit_cast(float, (q.y & 0xffff0000u) ^ 0x80000000u)};
-        } else {
-          acc[mt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int ct = 0; ct < NC; ++ct) {
+          const u32x2_t q = uq[mt][ct];
+          if constexpr (SIG) {  // bf16 -> f32, times -1/sig
+            acc[mt][ct] = f32x4_t{__builtin_bit_cast(float, q.x << 16) * us,
+                                  __builtin_bit_cast(float, q.x & 0xffff0000u) * us,
+                                  __builtin_bit_cast(float, q.y << 16) * us,
+                                  __builtin_bit_cast(float, q.y & 0xffff0000u) * us};
+          } else {  // bf16 -> f32 with the sign flipped in the same instruction
+            acc[mt][ct] = f32x4_t{__builtin_bit_cast(float, (q.x << 16) + 0x80000000u),
+                                  __builtin_bit_cast(float, (q.x & 0xffff0000u) ^ 0x80000000u),
+                                  __builtin_bit_cast(float, (q.y << 16) + 0x80000000u),
+                                  __builtin_bit_cast(float, (q.y & 0xffff0000u) ^ 0x80000000u)};
+          }
         }
-      }
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int ct = 0; ct < NC; ++ct) S::mma(acc[mt][ct], aw[s][mt], Sb[s][ct]);
+        for (int ct = 0; ct < NC; ++ct) {
+          if (!HASU && s == 0)
+            acc[mt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[s][mt].v, Sb[s][ct].v,
+                                                                  f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          else
+            S::mma(acc[mt][ct], aw[s][mt], Sb[s][ct]);
+        }
 
     if (STAGE) {
       // h block: value column (colw + 16 ct + c16), rows 32 s + 4 g4 (+16)
@@ -347,6 +389,15 @@ struct Scan2 {
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) Sacc[dt][ct] *= dv4;
       }
+    } else if constexpr (SIG) {  // renormalising chunks only (eg holds the multiplier, 1 otherwise)
+      sig_out = reinterpret_cast<const float*>(buf + OFF_D)[kChunk + 2];
+      const float m = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, eg)));
+      if (m != 1.f) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int ct = 0; ct < NC; ++ct) Sacc[dt][ct] *= m;
+      }
     } else {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -359,6 +410,74 @@ struct Scan2 {
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) S::mma(Sacc[dt][ct], ak[s2][dt], Db[s2][ct]);
+  }
+
+  // The serial chunk loop of one block (HASU: this wave's columns read U).
+  template <bool HASU>
+  __device__ static __forceinline__ void chunk_loop(f32x4_t (&Sacc)[DT][NC], const Ctx& x, const Row& row, char* smem,
+                                                    float& sig_out) {
+    char* buf0 = smem;
+    char* buf1 = smem + (NBUF == 2 ? BUF : 0);
+    float sig = 1.f;  // SIG: scale of the staged chunks (first wave)
+    auto step = [&](int c, const char* b, char* so) { compute<HASU>(Sacc, x, row, c, b, sig_out, so); };
+    const int nchunks = (row.len + kChunk - 1) / kChunk;
+    auto tok_of = [&](int c) { return static_cast<int64_t>(row.bos) + static_cast<int64_t>(c) * kChunk; };
+    auto hr_of = [&](int c) { return static_cast<int64_t>(row.chunk_off) + c; };
+    auto nv_of = [&](int c) { return min(kChunk, row.len - c * kChunk); };
+    if (nchunks > 0) {
+      if (NBUF == 1) {
+        // one LDS buffer: fill, compute, and refill behind a second barrier;
+        // the next chunk's loads are in flight during the compute
+        Stage st;
+        char* so = smem + OFF_HS;
+        load(st, x, tok_of(0), nv_of(0), hr_of(0));
+        for (int c = 0; c < nchunks; ++c) {
+          __syncthreads();
+          if (STAGE && c > 0) write_out(x, row, c - 1, so);
+          store(st, x, buf0, nv_of(c), sig);
+          __syncthreads();
+          if (c + 1 < nchunks) load(st, x, tok_of(c + 1), nv_of(c + 1), hr_of(c + 1));
+          step(c, buf0, so);
+        }
+        if (STAGE) {
+          __syncthreads();
+          write_out(x, row, nchunks - 1, so);
+        }
+      } else if (PF == 1) {
+        Stage st;
+        load(st, x, tok_of(0), nv_of(0), hr_of(0));
+        store(st, x, buf0, nv_of(0), sig);
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+          char* cur = (c & 1) ? buf1 : buf0;
+          char* nxt = (c & 1) ? buf0 : buf1;
+          if (c + 1 < nchunks) load(st, x, tok_of(c + 1), nv_of(c + 1), hr_of(c + 1));
+          step(c, cur, nullptr);
+          if (c + 1 < nchunks) store(st, x, nxt, nv_of(c + 1), sig);
+          __syncthreads();
+        }
+      } else {
+        // two chunks in flight; loads and LDS fills are unconditional (chunks
+        // past the end load as empty ranges and are never computed)
+        Stage A, B;
+        load(A, x, tok_of(0), nv_of(0), hr_of(0));
+        load(B, x, tok_of(1), nv_of(1), hr_of(1));
+        store(A, x, buf0, nv_of(0), sig);
+        __syncthreads();
+        for (int c = 0; c < nchunks; c += 2) {
+          load(A, x, tok_of(c + 2), nv_of(c + 2), hr_of(c + 2));
+          step(c, buf0, nullptr);
+          store(B, x, buf1, nv_of(c + 1), sig);
+          __syncthreads();
+          if (c + 1 >= nchunks) break;
+          load(B, x, tok_of(c + 3), nv_of(c + 3), hr_of(c + 3));
+          step(c + 1, buf1, nullptr);
+          store(A, x, buf0, nv_of(c + 2), sig);
+          __syncthreads();
+        }
+      }
+    }
+
   }
 
   __device__ static void run(const ScanArgs& a, char* smem) {
@@ -400,7 +519,6 @@ struct Scan2 {
     const bool wtrans = (MODE == 2) ? (wave >= NW / 2) : trans;
     const int colj = (MODE == 2) ? x.col_blk + (wave % (NW / 2)) * (BV / NW)
                                  : x.col_blk + colw - (trans ? DV : 0);
-    const int nchunks = (row.len + kChunk - 1) / kChunk;
 
     f32x4_t Sacc[DT][NC];
 #pragma unroll
@@ -435,66 +553,21 @@ struct Scan2 {
       }
     }
 
-    char* buf0 = smem;
-    char* buf1 = smem + (NBUF == 2 ? BUF : 0);
-    auto tok_of = [&](int c) { return static_cast<int64_t>(row.bos) + static_cast<int64_t>(c) * kChunk; };
-    auto hr_of = [&](int c) { return static_cast<int64_t>(row.chunk_off) + c; };
-    auto nv_of = [&](int c) { return min(kChunk, row.len - c * kChunk); };
-    if (nchunks > 0) {
-      if (NBUF == 1) {
-        // one LDS buffer: fill, compute, and refill behind a second barrier;
-        // the next chunk's loads are in flight during the compute
-        Stage st;
-        char* so = smem + OFF_HS;
-        load(st, x, tok_of(0), nv_of(0), hr_of(0));
-        for (int c = 0; c < nchunks; ++c) {
-          __syncthreads();
-          if (STAGE && c > 0) write_out(x, row, c - 1, so);
-          store(st, x, buf0, nv_of(c));
-          __syncthreads();
-          if (c + 1 < nchunks) load(st, x, tok_of(c + 1), nv_of(c + 1), hr_of(c + 1));
-          compute(Sacc, x, row, c, buf0, so);
-        }
-        if (STAGE) {
-          __syncthreads();
-          write_out(x, row, nchunks - 1, so);
-        }
-      } else if (PF == 1) {
-        Stage st;
-        load(st, x, tok_of(0), nv_of(0), hr_of(0));
-        store(st, x, buf0, nv_of(0));
-        __syncthreads();
-        for (int c = 0; c < nchunks; ++c) {
-          char* cur = (c & 1) ? buf1 : buf0;
-          char* nxt = (c & 1) ? buf0 : buf1;
-          if (c + 1 < nchunks) load(st, x, tok_of(c + 1), nv_of(c + 1), hr_of(c + 1));
-          compute(Sacc, x, row, c, cur);
-          if (c + 1 < nchunks) store(st, x, nxt, nv_of(c + 1));
-          __syncthreads();
-        }
-      } else {
-        // two chunks in flight; loads and LDS fills are unconditional (chunks
-        // past the end load as empty ranges and are never computed)
-        Stage A, B;
-        load(A, x, tok_of(0), nv_of(0), hr_of(0));
-        load(B, x, tok_of(1), nv_of(1), hr_of(1));
-        store(A, x, buf0, nv_of(0));
-        __syncthreads();
-        for (int c = 0; c < nchunks; c += 2) {
-          load(A, x, tok_of(c + 2), nv_of(c + 2), hr_of(c + 2));
-          compute(Sacc, x, row, c, buf0);
-          store(B, x, buf1, nv_of(c + 1));
-          __syncthreads();
-          if (c + 1 >= nchunks) break;
-          load(B, x, tok_of(c + 3), nv_of(c + 3), hr_of(c + 3));
-          compute(Sacc, x, row, c + 1, buf1);
-          store(A, x, buf0, nv_of(c + 2));
-          __syncthreads();
-        }
-      }
-    }
+    // wave-uniform: this wave's columns read U
+    const bool use_u = (MODE == 0) || ((MODE == 2) ? (wave < NW / 2) : !trans);
+    float sig_out = 1.f;  // SIG: the state's scale after the last chunk
+    if (use_u)
+      chunk_loop<true>(Sacc, x, row, smem, sig_out);
+    else if constexpr (MODE != 0)
+      chunk_loop<false>(Sacc, x, row, smem, sig_out);
 
     if (row.out_idx < 0) return;
+    if constexpr (SIG) {  // the true state
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) Sacc[dt][ct] *= sig_out;
+    }
     if (MODE == 0 || !wtrans) {
       if (a.h_out == nullptr) return;
       float* base = a.h_out + (static_cast<int64_t>(row.out_idx) * H + hd) * DV * DK;
@@ -565,6 +638,8 @@ LaunchFn find_scan2(int dk, int bv, int waves, int stages, int mode, bool kd) {
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 0)
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 1)
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 2)
+  GDR_SCAN2_CASE(128, 256, 8, 2, 2, 1, 1)
+  GDR_SCAN2_CASE(128, 256, 8, 3, 2, 2, 2)
   return nullptr;
 }
 

@@ -188,6 +188,33 @@ def test_segment_summaries_and_compose(pkg, dt):
     check(r, ref_of(inp), tol, what="segmented path")
 
 
+@pytest.mark.parametrize("gates", ["logsigmoid_mid", "logsigmoid_fast"])
+def test_segment_summaries_strong_decay(pkg, gates):
+    """Segments long enough for the summaries' state scale to leave its range:
+    with about -0.08 per token a 500-token segment decays by e^-40 (one
+    renormalising chunk per segment); with about -1.4 per token every chunk's
+    decay underflows float32 and every chunk renormalises."""
+    lengths = [1500, 300]
+    P = 3
+    inp = make_gdr(311, lengths=lengths, H=2, DK=128, DV=128, dtype=torch.bfloat16, varlen=True, h0_std=0.1,
+                   gates=gates)
+    r = run_path(pkg, inp, n_segments=P)
+    if gates == "logsigmoid_mid":
+        d = inp.f64()
+        cu = d["cu_seqlens"]
+        for n in range(len(lengths)):
+            s, e = cu[n], cu[n + 1]
+            S_loc, M = oracle.gdr_segment_summaries_fp64(d["k"][0, s:e], d["v"][0, s:e], d["g"][0, s:e],
+                                                         d["beta"][0, s:e], oracle.segment_bounds(e - s, P))
+            gs = to_np(r["seg_state"][n * P:(n + 1) * P]).transpose(0, 1, 3, 2)
+            gm = to_np(r["seg_trans"][n * P:(n + 1) * P])
+            for j in range(P):  # per segment: the transitions differ by orders of magnitude
+                es, em = rel(gs[j], S_loc[j]), rel(gm[j], M[j])
+                print(f"{gates} seq {n} segment {j}: S_loc {es:.3e} M {em:.3e} (|M| {np.abs(M[j]).max():.2e})")
+                assert es <= 1e-2 and em <= 1e-2
+    check(r, ref_of(inp), 1e-2, what=f"segmented path, {gates}")
+
+
 def test_empty_and_single_token_sequences(pkg):
     inp = make_gdr(404, lengths=[0, 1, 0, 2, 0], H=2, DK=64, DV=64, dtype=torch.float32, varlen=True, h0_std=0.3)
     r = run_path(pkg, inp)

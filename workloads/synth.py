@@ -16,6 +16,10 @@ Gate recipes
 ------------
 ``logsigmoid``   beta = sigmoid(N(0,1)), g = log(sigmoid(N(4,1)))  (decay close
                  to 1 but clearly contracting: a = sigmoid(x) with x ~ N(4,1)).
+``logsigmoid_mid``  beta as above, g = log(sigmoid(N(2.5, 0.3))) (about -0.08
+                 per token: the state shrinks by e^-40 over 500 tokens).
+``logsigmoid_fast`` beta as above, g = log(sigmoid(N(-1, 1))) (about -1.4 per
+                 token: a chunk's total decay underflows float32).
 ``near_one``     a = 1 - 1e-4 * U(0,1), g = log(a) evaluated as log1p in
                  float64, and beta = U(0.01, 0.05): the transition-sensitive,
                  nearly non-contracting long-context regime.
@@ -169,6 +173,10 @@ def make_gdr(seed: int, *, lengths: Optional[Sequence[int]] = None, B: int = 1, 
         # per-key-channel decays: every (token, head, channel) its own logsigmoid(N(4, 1))
         beta = _sigmoid(rng.standard_normal((B, T, H)))
         g = _logsigmoid(rng.normal(4.0, 1.0, (B, T, H, DK)))
+    elif gates in ("logsigmoid_mid", "logsigmoid_fast"):
+        beta = _sigmoid(rng.standard_normal((B, T, H)))
+        mu, sd = (2.5, 0.3) if gates == "logsigmoid_mid" else (-1.0, 1.0)
+        g = _logsigmoid(rng.normal(mu, sd, (B, T, H)))
     elif gates == "near_one":
         beta = rng.uniform(0.01, 0.05, (B, T, H))
         g = np.log1p(-1e-4 * rng.uniform(0.0, 1.0, (B, T, H)))
