@@ -23,6 +23,7 @@ The roofline fractions are also given against the measured rate of a plain
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -312,13 +313,43 @@ def long_state(pkg, torch, dev, reps=5, copy_gbs=None):
     DV = v.shape[-1]
     P = 16
 
+    # every buffer allocated once; the timed calls go straight through the C ABI
+    B = pkg.binding
+    L = pkg.lib()
+    pr = B.Problem(k, DV)
+    nt = pkg.gdr_num_chunks(k, DV)
+    H, DK = inp.H, inp.DK
+    h = torch.empty((nt, H, DV, DK), dtype=k.dtype, device=dev)
+    v_new = torch.empty_like(u)
+    hT = torch.empty((1, H, DK, DV), dtype=torch.float32, device=dev)
+    ss = torch.empty((P, H, DV, DK), dtype=torch.float32, device=dev)
+    st = torch.empty((P, H, DK, DK), dtype=torch.float32, device=dev)
+    si = torch.empty((P, H, DV, DK), dtype=torch.float32, device=dev)
+    ws_bytes = int(L.gdr_segment_summaries_workspace_size(pr.ref, P))
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    seg = B.gdr_segments(P, si.data_ptr())
+    sp = B._stream(torch.cuda.current_stream())
+    ptr = B._ptr
+
     def serial():
-        return pkg.gdr_state_scan(k, w, u, g_cum)
+        B._check(L.gdr_state_scan(pr.ref, None, None, ptr(k), ptr(w), ptr(u), ptr(g_cum), None, ptr(h), ptr(v_new),
+                                  ptr(hT), sp), "scan")
+
+    def summaries():
+        B._check(L.gdr_segment_summaries_ws(pr.ref, None, P, ptr(k), ptr(w), ptr(u), ptr(g_cum), ptr(ss), ptr(st),
+                                            ptr(ws), ws_bytes, sp), "summaries")
+
+    def compose():
+        B._check(L.gdr_segment_compose(pr.ref, P, ptr(ss), ptr(st), None, ptr(si), None, sp), "compose")
+
+    def final_pass():
+        B._check(L.gdr_state_scan(pr.ref, None, ctypes.byref(seg), ptr(k), ptr(w), ptr(u), ptr(g_cum), None, ptr(h),
+                                  ptr(v_new), ptr(hT), sp), "final pass")
 
     def segmented():
-        ss, st = pkg.gdr_segment_summaries(k, w, u, g_cum, P)
-        si, _ = pkg.gdr_segment_compose(k, DV, ss, st, P)
-        return pkg.gdr_state_scan(k, w, u, g_cum, None, None, None, P, si)
+        summaries()
+        compose()
+        final_pass()
 
     res = {}
     serial_alg = scan_alg_bytes(inp.lengths, inp.H, inp.DK, DV, 2, 2, False, True)
@@ -339,12 +370,8 @@ def long_state(pkg, torch, dev, reps=5, copy_gbs=None):
     res["segmented"].update(alg_bytes=seg_alg, frac_of_hbm=round(seg_alg / t / 8e12, 4))
     if copy_gbs:
         res["segmented"]["frac_of_copy"] = round(seg_alg / t / 1e9 / copy_gbs, 4)
-    # each phase alone (inputs of the later phases computed once beforehand)
-    ss, st = pkg.gdr_segment_summaries(k, w, u, g_cum, P)
-    si, _ = pkg.gdr_segment_compose(k, DV, ss, st, P)
-    phases = {"summaries": lambda: pkg.gdr_segment_summaries(k, w, u, g_cum, P),
-              "compose": lambda: pkg.gdr_segment_compose(k, DV, ss, st, P),
-              "final_pass": lambda: pkg.gdr_state_scan(k, w, u, g_cum, None, None, None, P, si)}
+    # each phase alone (the buffers hold the previous phases' outputs)
+    phases = {"summaries": summaries, "compose": compose, "final_pass": final_pass}
     res["segmented"]["phases"] = {}
     for name, fn in phases.items():
         tp = _event_median_us(torch, fn, reps=reps) * 1e-6

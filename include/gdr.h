@@ -173,6 +173,28 @@ gdr_status gdr_segment_summaries(const gdr_problem* p, const gdr_tile* tile, int
                                  const float* g_cum, float* seg_state, float* seg_trans,
                                  void* stream);
 
+/* Device workspace (bytes) gdr_segment_summaries_ws uses for this problem and
+ * segment count; 0 when the summaries are formed directly (host only). */
+size_t gdr_segment_summaries_workspace_size(const gdr_problem* p, int32_t n_segments);
+
+/* gdr_segment_summaries with a caller-owned device workspace (16-byte
+ * aligned, at least gdr_segment_summaries_workspace_size bytes, else
+ * GDR_ERR_INVALID_ARG; NULL or a zero size runs the direct form).  When the
+ * size is nonzero the (segment, head) chains alone would leave most of the
+ * GPU idle, so every segment is cut at half its chunk count, the two halves'
+ * summaries are formed in parallel into the workspace (each from zero and
+ * from the identity), and each segment's pair is composed by the same rule as
+ * gdr_segment_compose ([cuLA#127] "Root cause and implementation": segments
+ * are composed one after another), in FP32:
+ *   S_loc = M_b S_loc(a) + S_loc(b),   M_s = M_b M_a   (a first half, b second).
+ * Same outputs and layouts as gdr_segment_summaries; equal to them up to
+ * rounding, and bit-identical for every tile.  The workspace holds nothing
+ * after the call. */
+gdr_status gdr_segment_summaries_ws(const gdr_problem* p, const gdr_tile* tile, int32_t n_segments,
+                                    const void* k, const void* w, const void* u,
+                                    const float* g_cum, float* seg_state, float* seg_trans,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Segment composition ([cuLA#127] "Root cause and implementation"), in FP32,
  * serially over the segments of each sequence:
  *   S_init(0) = h0[n] (NULL = zeros);  S_init(s+1) = M_s S_init(s) + S_loc(s).
@@ -331,8 +353,9 @@ const char* gdr_status_string(gdr_status s);
 const char* gdr_last_error(void);
 
 /* Scheduler introspection (host only, no GPU needed): the tile and grid the
- * scan would use.  out[0..5] = bv, waves, stages, workgroups, launches,
- * rows per launch (max). */
+ * scan would use (n_segments > 0: the summary pass as gdr_segment_summaries_ws
+ * runs it with its workspace, i.e. on half segments when that form applies).
+ * out[0..5] = bv, waves, stages, workgroups, launches, rows per launch (max). */
 gdr_status gdr_plan_query(const gdr_problem* p, const gdr_tile* tile, int32_t n_segments,
                           int64_t out[6]);
 

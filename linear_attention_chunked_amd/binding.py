@@ -74,6 +74,9 @@ _SIGS = {
     "gdr_chunk_output": (ctypes.c_int, [ctypes.POINTER(gdr_problem), _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]),
     "gdr_segment_summaries": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile), ctypes.c_int32,
                                              _P, _P, _P, _P, _P, _P, _P]),
+    "gdr_segment_summaries_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(gdr_problem), ctypes.c_int32]),
+    "gdr_segment_summaries_ws": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile),
+                                                ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "gdr_segment_compose": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
     "kda_chunk_prepare": (ctypes.c_int, [ctypes.POINTER(gdr_problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "kda_state_scan": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile),
@@ -266,17 +269,36 @@ def gdr_chunk_output(q, k, v_new, h, g_cum, scale: float = 1.0, cu_seqlens=None,
     return o
 
 
-def gdr_segment_summaries(k, w, u, g_cum, n_segments: int, cu_seqlens=None, tile=None, stream=None):
-    """Returns (seg_state [N*P,H,DV,DK], seg_trans [N*P,H,DK,DK]) float32."""
+def gdr_segment_summaries(k, w, u, g_cum, n_segments: int, cu_seqlens=None, tile=None, stream=None,
+                          workspace: bool = True):
+    """Returns (seg_state [N*P,H,DV,DK], seg_trans [N*P,H,DK,DK]) float32.
+
+    With ``workspace`` (the default) the call passes the device workspace
+    ``gdr_segment_summaries_workspace_size`` asks for (the half-segment form
+    when it is nonzero); ``workspace=False`` calls the direct form."""
     DV = u.shape[-1]
     p = Problem(k, DV, cu_seqlens)
     seg_state = torch.empty((p.N * n_segments, p.H, DV, p.DK), dtype=torch.float32, device=k.device)
     seg_trans = torch.empty((p.N * n_segments, p.H, p.DK, p.DK), dtype=torch.float32, device=k.device)
     t = _tile(tile)
-    _check(lib().gdr_segment_summaries(p.ref, ctypes.byref(t) if t is not None else None, n_segments, _ptr(k),
-                                       _ptr(w), _ptr(u), _ptr(g_cum), _ptr(seg_state), _ptr(seg_trans),
-                                       _stream(stream)), "gdr_segment_summaries")
+    L = lib()
+    tp = ctypes.byref(t) if t is not None else None
+    ws_bytes = int(L.gdr_segment_summaries_workspace_size(p.ref, n_segments)) if workspace else 0
+    if ws_bytes > 0:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=k.device)
+        _check(L.gdr_segment_summaries_ws(p.ref, tp, n_segments, _ptr(k), _ptr(w), _ptr(u), _ptr(g_cum),
+                                          _ptr(seg_state), _ptr(seg_trans), _ptr(ws), ws_bytes, _stream(stream)),
+               "gdr_segment_summaries_ws")
+    else:
+        _check(L.gdr_segment_summaries(p.ref, tp, n_segments, _ptr(k), _ptr(w), _ptr(u), _ptr(g_cum),
+                                       _ptr(seg_state), _ptr(seg_trans), _stream(stream)), "gdr_segment_summaries")
     return seg_state, seg_trans
+
+
+def gdr_segment_summaries_workspace_size(k, DV: int, n_segments: int, cu_seqlens=None) -> int:
+    """Bytes of device workspace the half-segment summaries need (0: direct form)."""
+    p = Problem(k, DV, cu_seqlens)
+    return int(lib().gdr_segment_summaries_workspace_size(p.ref, n_segments))
 
 
 def gdr_segment_compose(k, DV: int, seg_state, seg_trans, n_segments: int, h0=None, cu_seqlens=None,

@@ -83,14 +83,15 @@ gdr_status hip_fail(hipError_t e, const char* what) {
 
 gdr_status run_scan(const gdr::Problem& pr, const gdr::Tile& t, int mode, int P, const void* k, const void* w,
                     const void* u, const float* g_cum, const float* h_in, int in_vk, void* h, void* v_new,
-                    float* h_out, int out_vk, float* trans_out, hipStream_t stream, const float* decay = nullptr) {
+                    float* h_out, int out_vk, float* trans_out, hipStream_t stream, const float* decay = nullptr,
+                    int split = 1) {
   const int kmode = (mode == 1) ? gdr::summary_kernel_mode(pr) : 0;
   gdr::LaunchFn fn = decay != nullptr ? gdr::find_scan2(pr.DK, t.bv, t.waves, t.stages, kmode, true)
                                       : gdr::find_scan(pr.dtype, pr.DK, t.bv, t.waves, t.stages, kmode);
   if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no scan kernel for this dtype/DK/tile");
   const bool has_in = (h_in != nullptr);
   const bool has_out = (h_out != nullptr);
-  std::vector<gdr::Launch> plan = gdr::plan_scan(pr, t, mode, P, has_in, has_out);
+  std::vector<gdr::Launch> plan = gdr::plan_scan(pr, t, mode, P, has_in, has_out, split);
   gdr::ScanArgs a;
   memset(&a, 0, sizeof(a));
   a.k = k;
@@ -333,9 +334,18 @@ gdr_status gdr_state_scan_bwd(const gdr_problem* p, const void* q, const void* k
   return GDR_OK;
 }
 
-gdr_status gdr_segment_summaries(const gdr_problem* p, const gdr_tile* tile, int32_t n_segments, const void* k,
-                                 const void* w, const void* u, const float* g_cum, float* seg_state,
-                                 float* seg_trans, void* stream) {
+size_t gdr_segment_summaries_workspace_size(const gdr_problem* p, int32_t n_segments) {
+  g_err.clear();
+  gdr::Problem pr;
+  if (parse(p, pr) != GDR_OK || n_segments < 1) return 0;
+  if (gdr::summary_split(pr, n_segments) != 2) return 0;
+  // the half-segment summaries: 2 N P (S_loc, M) pairs in FP32
+  return static_cast<size_t>(2) * pr.N * n_segments * pr.H * pr.DK * (pr.DV + pr.DK) * sizeof(float);
+}
+
+gdr_status gdr_segment_summaries_ws(const gdr_problem* p, const gdr_tile* tile, int32_t n_segments, const void* k,
+                                    const void* w, const void* u, const float* g_cum, float* seg_state,
+                                    float* seg_trans, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   gdr::Problem pr;
   GDR_TRY(parse(p, pr));
@@ -347,10 +357,45 @@ gdr_status gdr_segment_summaries(const gdr_problem* p, const gdr_tile* tile, int
   GDR_TRY(need(g_cum, "g_cum"));
   GDR_TRY(need(seg_state, "seg_state"));
   GDR_TRY(need(seg_trans, "seg_trans"));
+  GDR_TRY(opt(workspace, "workspace"));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int split = workspace != nullptr ? gdr::summary_split(pr, n_segments) : 1;
+  const size_t need_bytes = gdr_segment_summaries_workspace_size(p, n_segments);
+  if (split == 2 && workspace_bytes < need_bytes)
+    return fail(GDR_ERR_INVALID_ARG, "workspace_bytes " + std::to_string(workspace_bytes) + " < the " +
+                                         std::to_string(need_bytes) + " bytes this problem needs");
   gdr::Tile t;
-  GDR_TRY(tile_for(pr, tile, 1, static_cast<int64_t>(pr.N) * n_segments, t));
-  return run_scan(pr, t, 1, n_segments, k, w, u, g_cum, nullptr, 0, nullptr, nullptr, seg_state, 1, seg_trans,
-                  static_cast<hipStream_t>(stream));
+  GDR_TRY(tile_for(pr, tile, 1, static_cast<int64_t>(pr.N) * n_segments * split, t));
+  if (split == 1)
+    return run_scan(pr, t, 1, n_segments, k, w, u, g_cum, nullptr, 0, nullptr, nullptr, seg_state, 1, seg_trans, st);
+  gdr::LaunchFn fn = gdr::find_combine(pr.DK);
+  if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no summary combine kernel for this DK");
+  float* half_state = static_cast<float*>(workspace);
+  float* half_trans = half_state + static_cast<size_t>(2) * pr.N * n_segments * pr.H * pr.DV * pr.DK;
+  GDR_TRY(run_scan(pr, t, 1, n_segments, k, w, u, g_cum, nullptr, 0, nullptr, nullptr, half_state, 1, half_trans, st,
+                   nullptr, 2));
+  if (pr.N == 0) return GDR_OK;
+  gdr::CombineArgs a;
+  memset(&a, 0, sizeof(a));
+  a.half_state = half_state;
+  a.half_trans = half_trans;
+  a.seg_state = seg_state;
+  a.seg_trans = seg_trans;
+  a.H = pr.H;
+  a.DV = pr.DV;
+  a.n_seg = pr.N * n_segments;
+  const int64_t pairs = static_cast<int64_t>(pr.N) * n_segments * pr.H;
+  // 64-column blocks (DV and DK are multiples of 64 here: the split needs DK = DV = 128)
+  const int grid = static_cast<int>(8 * ((pr.DV + pr.DK) / 64) * ((pairs + 7) / 8));
+  hipError_t e = fn(&a, grid, st);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return GDR_OK;
+}
+
+gdr_status gdr_segment_summaries(const gdr_problem* p, const gdr_tile* tile, int32_t n_segments, const void* k,
+                                 const void* w, const void* u, const float* g_cum, float* seg_state,
+                                 float* seg_trans, void* stream) {
+  return gdr_segment_summaries_ws(p, tile, n_segments, k, w, u, g_cum, seg_state, seg_trans, nullptr, 0, stream);
 }
 
 gdr_status gdr_segment_compose(const gdr_problem* p, int32_t n_segments, const float* seg_state,
@@ -393,9 +438,10 @@ gdr_status gdr_plan_query(const gdr_problem* p, const gdr_tile* tile, int32_t n_
   gdr::Problem pr;
   GDR_TRY(parse(p, pr));
   const int mode = n_segments > 0 ? 1 : 0;
+  const int split = mode == 1 ? gdr::summary_split(pr, n_segments) : 1;  // as gdr_segment_summaries_ws runs it
   gdr::Tile t;
-  GDR_TRY(tile_for(pr, tile, mode, static_cast<int64_t>(pr.N) * (n_segments > 0 ? n_segments : 1), t));
-  std::vector<gdr::Launch> plan = gdr::plan_scan(pr, t, mode, n_segments > 0 ? n_segments : 1, true, true);
+  GDR_TRY(tile_for(pr, tile, mode, static_cast<int64_t>(pr.N) * (n_segments > 0 ? n_segments : 1) * split, t));
+  std::vector<gdr::Launch> plan = gdr::plan_scan(pr, t, mode, n_segments > 0 ? n_segments : 1, true, true, split);
   int64_t wg = 0, maxrows = 0;
   for (auto& l : plan) {
     wg += l.grid;

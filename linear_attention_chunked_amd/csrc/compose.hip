@@ -215,6 +215,117 @@ static hipError_t launch_compose(const void* args, int grid, hipStream_t stream)
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Pairwise combination of half-segment summaries (the same composition rule
+// applied to the two halves of one segment, all segments in parallel):
+//   S = M_b S_a + S_b,   M = M_b M_a
+// in FP32 MFMA (v_mfma_f32_16x16x4_f32).  One workgroup per (segment, head,
+// 64 of the DV + DK output columns), one wave per 16 rows.  The 64 columns
+// of [S_a | M_a] are staged once in LDS (S_a value-major as stored, one
+// column per padded LDS row; M_a row-major as stored, one matrix row per
+// padded LDS row); each wave keeps its 16 rows of M_b in registers and runs
+// the four 16-column tiles one after another.  Lane group g of instruction
+// 4i + j contracts index 16 i + 4 g + j (four consecutive entries per lane,
+// so the M_b rows come in as 16-byte loads); four interleaved accumulator
+// chains are summed per tile.
+template <int DK>
+struct Combine {
+  static constexpr int NW = DK / 16;
+  static constexpr int CW = 64;        // output columns per workgroup
+  static constexpr int LDC = DK + 4;   // state block: one column per row (floats), padded
+  static constexpr int LDR = CW + 4;   // transition block: one row per row (floats), padded
+  static constexpr int SMEM = (CW * LDC > DK * LDR ? CW * LDC : DK * LDR);
+
+  __device__ static void run(const CombineArgs& a, float* sm) {
+    const int NB = (a.DV + DK) / CW;
+    const int bx = blockIdx.x;
+    const int xcd = bx & 7, slot = bx >> 3;
+    const int pair = 8 * (slot / NB) + xcd;  // the column blocks of one (segment, head) share an XCD
+    const int cb = slot % NB;
+    if (pair >= a.n_seg * a.H) return;
+    const int64_t seg = pair / a.H, hd = pair % a.H, H = a.H;
+    const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g4 = lane >> 4;
+    const int wave = tid >> 6;
+    const int DV = a.DV;
+    const bool state = CW * cb < DV;
+    const int col0 = state ? CW * cb : CW * cb - DV;  // first column of the block within S or M
+    // stage the 64 columns of [S_a | M_a] (16-byte pieces, coalesced)
+    if (state) {
+      const float* src = a.half_state + ((2 * seg) * H + hd) * DV * DK + static_cast<int64_t>(col0) * DK;
+      for (int v = tid; v < CW * DK / 4; v += NW * 64) {
+        const int c = v / (DK / 4), r4 = v % (DK / 4);
+        *reinterpret_cast<f32x4_t*>(sm + c * LDC + 4 * r4) = *reinterpret_cast<const f32x4_t*>(src + 4 * v);
+      }
+    } else {
+      const float* src = a.half_trans + ((2 * seg) * H + hd) * DK * DK + col0;
+      for (int v = tid; v < DK * CW / 4; v += NW * 64) {
+        const int r = v / (CW / 4), c4 = v % (CW / 4);
+        *reinterpret_cast<f32x4_t*>(sm + r * LDR + 4 * c4) =
+            *reinterpret_cast<const f32x4_t*>(src + static_cast<int64_t>(r) * DK + 4 * c4);
+      }
+    }
+    // this wave's 16 rows of M_b (A operand)
+    const float* arow = a.half_trans + ((2 * seg + 1) * H + hd) * DK * DK +
+                        static_cast<int64_t>(16 * wave + c16) * DK + 4 * g4;
+    float av[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x4_t q = *reinterpret_cast<const f32x4_t*>(arow + 16 * i);
+      av[4 * i] = q[0], av[4 * i + 1] = q[1], av[4 * i + 2] = q[2], av[4 * i + 3] = q[3];
+    }
+    __syncthreads();
+    const int row0 = 16 * wave + 4 * g4;  // this lane's four output rows
+#pragma unroll 1
+    for (int ct = 0; ct < CW / 16; ++ct) {
+      const int c = 16 * ct + c16;  // column within the block
+      float bv[32];
+      f32x4_t acc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (state) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const f32x4_t q = *reinterpret_cast<const f32x4_t*>(sm + c * LDC + 16 * i + 4 * g4);
+          bv[4 * i] = q[0], bv[4 * i + 1] = q[1], bv[4 * i + 2] = q[2], bv[4 * i + 3] = q[3];
+        }
+        acc[0] = *reinterpret_cast<const f32x4_t*>(a.half_state + ((2 * seg + 1) * H + hd) * DV * DK +
+                                                   static_cast<int64_t>(col0 + c) * DK + row0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bv[4 * i + j] = sm[(16 * i + 4 * g4 + j) * LDR + c];
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) acc[i & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[i], acc[i & 3], 0, 0, 0);
+      const f32x4_t r = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      if (state) {
+        *reinterpret_cast<f32x4_t*>(a.seg_state + (seg * H + hd) * DV * DK + static_cast<int64_t>(col0 + c) * DK +
+                                    row0) = r;
+      } else {
+        float* mo = a.seg_trans + (seg * H + hd) * DK * DK + static_cast<int64_t>(row0) * DK + col0 + c;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mo[static_cast<int64_t>(j) * DK] = r[j];
+      }
+    }
+  }
+};
+
+template <int DK>
+__global__ __launch_bounds__(DK * 4) void combine_kernel(const CombineArgs a) {
+  __shared__ __align__(16) float sm[Combine<DK>::SMEM];
+  Combine<DK>::run(a, sm);
+}
+
+template <int DK>
+static hipError_t launch_combine(const void* args, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((combine_kernel<DK>), dim3(grid), dim3(DK * 4), 0, stream,
+                     *static_cast<const CombineArgs*>(args));
+  return hipGetLastError();
+}
+
+LaunchFn find_combine(int dk) { return dk == 128 ? &launch_combine<128> : nullptr; }
+
 // 16 segments (the split the long-sequence workloads use) get the
 // straight-line chain; other counts take the loop.
 LaunchFn find_compose(int dk, int P) {

@@ -84,6 +84,18 @@ struct ComposeArgs {
   int32_t state_vk;
 };
 
+// Pairwise combination of half-segment summaries: for every segment s,
+// (S, M) = (M_b S_a + S_b, M_b M_a) with a = half 2s, b = half 2s + 1.
+struct CombineArgs {
+  const float* half_state;  // [2 n_seg, H, DV, DK]
+  const float* half_trans;  // [2 n_seg, H, DK, DK]
+  float* seg_state;         // [n_seg, H, DV, DK]
+  float* seg_trans;         // [n_seg, H, DK, DK]
+  int32_t H;
+  int32_t DV;
+  int32_t n_seg;
+};
+
 // Forward (slot-state construction) and reverse (dH recurrence) share the
 // state walk.  Reverse: k = q, v = dO, s = dscore, pw = p; z is the
 // forward's normaliser (input); e / e2 hold the key- / value-side weights;
@@ -149,6 +161,7 @@ LaunchFn find_kda_output(int dk, int dv);
 LaunchFn find_output(int dtype, int dk, int dv);
 LaunchFn find_output2(int dk, int dv);
 LaunchFn find_compose(int dk, int P);
+LaunchFn find_combine(int dk);
 LaunchFn find_dv_local(int dk, int dv);
 LaunchFn find_scan_bwd(int dk);
 hipError_t launch_abc(const AbcArgs& a, hipStream_t s);

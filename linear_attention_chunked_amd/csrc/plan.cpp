@@ -110,7 +110,7 @@ bool parse_problem(int B, int64_t T, int H, int DK, int DV, int N, const int32_t
 
 // Built tiles (must match the instantiations in scan.hip).
 static bool tile_built(int dtype, int bv, int waves, int stages) {
-  if (dtype == 1 && bv == 256 && waves == 8 && (stages == 2 || stages == 3)) return true;  // summaries (mode 2)
+  if (dtype == 1 && bv == 256 && waves == 8 && stages == 2) return true;  // balanced summaries only
   static const int bf16_tiles[][3] = {{32, 2, 2}, {32, 2, 3}, {64, 2, 3}, {64, 4, 2},
                                       {64, 4, 3}, {128, 4, 2}, {128, 4, 3}};
   static const int f32_tiles[][3] = {{32, 2, 1}, {32, 2, 2}, {64, 4, 1}, {64, 4, 2}};
@@ -145,7 +145,10 @@ bool choose_tile(const Problem& p, const int32_t* req, int mode, int64_t rows, T
     // its transition columns and stores no per-chunk state, so once 128-column
     // blocks alone fill the 256 CUs, the wider block (K and W read by half as
     // many workgroups) wins there (16 segments x 8 heads: 144 us against
-    // 174 us for 64-column blocks).
+    // 174 us for 64-column blocks), and once one 8-wave block of all 256
+    // columns per (segment, head) fills them, that block (two waves per SIMD,
+    // K and W staged once per segment-head) wins again (32 segments x 8
+    // heads: 108 us against 128 us).
     const int64_t pairs = rows * p.H;
     const int64_t units64 = pairs * ((mode == 1 ? p.DV + p.DK : p.DV) / 64);
     if (p.dtype == 1) {
@@ -155,6 +158,10 @@ bool choose_tile(const Problem& p, const int32_t* req, int mode, int64_t rows, T
       if (units64 < 64) {
         r[0] = 32;
         r[1] = 2;
+        r[2] = 2;
+      } else if (mode == 1 && p.DK == 128 && p.DV == 128 && summary_kernel_mode(p) == 2 && pairs >= 256) {
+        r[0] = 256;
+        r[1] = 8;
         r[2] = 2;
       } else if (mode == 1 && p.DV % 128 == 0 && p.DK % 128 == 0 && units64 / 2 >= 256) {
         r[0] = 128;
@@ -199,6 +206,12 @@ bool choose_tile(const Problem& p, const int32_t* req, int mode, int64_t rows, T
 
 int summary_kernel_mode(const Problem& p) { return (p.dtype == 1 && p.DK == p.DV) ? 2 : 1; }
 
+int summary_split(const Problem& p, int P) {
+  if (summary_kernel_mode(p) != 2 || p.DK != 128 || p.DV != 128) return 1;
+  const int64_t blocks = static_cast<int64_t>(p.N) * P * p.H * 2;  // 128-column blocks of a direct pass
+  return (blocks > 0 && blocks < 512) ? 2 : 1;
+}
+
 int scan_blocks(const Problem& p, const Tile& t, int mode) {
   if (mode != 1) return p.DV / t.bv;
   return summary_kernel_mode(p) == 2 ? 2 * p.DV / t.bv : (p.DV + p.DK) / t.bv;
@@ -224,7 +237,8 @@ static void finish_scan_launch(Launch& l, int H, int nblk) {
   l.grid = static_cast<int>(8 * nblk * ((pairs + 7) / 8));
 }
 
-std::vector<Launch> plan_scan(const Problem& p, const Tile& t, int mode, int P, bool has_h0, bool has_hT) {
+std::vector<Launch> plan_scan(const Problem& p, const Tile& t, int mode, int P, bool has_h0, bool has_hT,
+                              int split) {
   std::vector<Row> rows;
   if (mode == 0) {
     for (int n = 0; n < p.N; ++n) {
@@ -240,6 +254,22 @@ std::vector<Launch> plan_scan(const Problem& p, const Tile& t, int mode, int P, 
       segment_bounds(s.len, P, t0, t1);
       for (int k = 0; k < P; ++k) {
         const int seg = n * P + k;
+        if (mode == 1 && split == 2) {
+          // halves: the first ceil(chunks / 2) chunks, then the rest
+          const int64_t nc = (t1[k] - t0[k] + kChunk - 1) / kChunk;
+          const int64_t mid = std::min(t0[k] + ((nc + 1) / 2) * kChunk, t1[k]);
+          const int64_t lo[2] = {t0[k], mid}, hi[2] = {mid, t1[k]};
+          for (int hf = 0; hf < 2; ++hf) {
+            Row r;
+            r.bos = static_cast<int32_t>(s.bos + lo[hf]);
+            r.len = static_cast<int32_t>(hi[hf] - lo[hf]);
+            r.chunk_off = static_cast<int32_t>(s.chunk_off + lo[hf] / kChunk);
+            r.in_idx = -1;
+            r.out_idx = 2 * seg + hf;
+            rows.push_back(r);
+          }
+          continue;
+        }
         Row r;
         r.bos = static_cast<int32_t>(s.bos + t0[k]);
         r.len = static_cast<int32_t>(t1[k] - t0[k]);

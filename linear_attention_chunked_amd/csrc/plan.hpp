@@ -74,8 +74,18 @@ int scan_blocks(const Problem& p, const Tile& t, int mode);
 // Segment boundaries of one sequence: [t0, t1) token ranges relative to its start.
 void segment_bounds(int64_t len, int P, std::vector<int64_t>& t0, std::vector<int64_t>& t1);
 
+// Sub-segments per segment in the summary pass: 2 when the (segment, head)
+// chains of a direct pass would leave the CUs with one wave per SIMD
+// (bfloat16, DK = DV = 128, fewer than 512 column blocks of 128), so each
+// segment's summary is formed from its two halves, else 1.  Depends on the
+// problem shape and P only (not on the tile).
+int summary_split(const Problem& p, int P);
+
 // Plans.  mode 0 = plain scan, 2 = segmented final pass, 1 = summaries.
-std::vector<Launch> plan_scan(const Problem& p, const Tile& t, int mode, int P, bool has_h0, bool has_hT);
+// With split = 2 (summaries only) every segment becomes two rows, its first
+// ceil(chunks / 2) chunks and the rest, written to summary slots 2s and 2s+1.
+std::vector<Launch> plan_scan(const Problem& p, const Tile& t, int mode, int P, bool has_h0, bool has_hT,
+                              int split = 1);
 std::vector<Launch> plan_chunks(const Problem& p, int blocks_per_chunk);
 
 }  // namespace gdr

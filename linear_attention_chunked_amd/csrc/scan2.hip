@@ -638,8 +638,8 @@ LaunchFn find_scan2(int dk, int bv, int waves, int stages, int mode, bool kd) {
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 0)
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 1)
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 2)
+  // summaries only: one 8-wave block of all 256 columns of a (segment, head)
   GDR_SCAN2_CASE(128, 256, 8, 2, 2, 1, 1)
-  GDR_SCAN2_CASE(128, 256, 8, 3, 2, 2, 2)
   return nullptr;
 }
 

@@ -111,11 +111,36 @@ def test_plan_grid_and_launch_split():
 
 
 def test_plan_segments_and_table():
+    # 16 segments x 8 heads: 256 direct 128-column blocks would give one wave per
+    # SIMD, so every segment's summary comes from its two halves (32 rows), one
+    # 8-wave block of all DV + DK columns per (half, head)
     p, _ = _prob(B_=1, T=65536, H=8)
     bv, waves, stages, wgs, launches, maxrows = _query(p, nseg=16)
-    assert maxrows == 16 and launches == 1
-    # summaries run DV + DK columns
-    assert wgs == 8 * ((128 + 128) // bv) * ((16 * 8 + 7) // 8)
+    assert maxrows == 32 and launches == 1
+    assert (bv, waves, stages) == (256, 8, 2)
+    assert wgs == 8 * ((128 + 128) // bv) * ((32 * 8 + 7) // 8)
+    # 64 segments: direct (512 blocks of 128 columns already fill the CUs twice)
+    bv, waves, stages, wgs, launches, maxrows = _query(p, nseg=64)
+    assert maxrows == 64 and (bv, waves, stages) == (256, 8, 2)
+
+
+def test_summary_workspace_size():
+    L = B.lib()
+    p, _ = _prob(B_=1, T=65536, H=8)
+    # the half summaries: 2 N P (S_loc, M) pairs in FP32
+    assert L.gdr_segment_summaries_workspace_size(ctypes.byref(p), 16) == 2 * 16 * 8 * 128 * 256 * 4
+    assert L.gdr_segment_summaries_workspace_size(ctypes.byref(p), 32) == 0  # 512 blocks: direct
+    for kw in (dict(dtype=B.GDR_F32), dict(DK=64, DV=64), dict(DK=128, DV=64)):
+        q, _ = _prob(B_=1, T=4096, H=2, **kw)
+        assert L.gdr_segment_summaries_workspace_size(ctypes.byref(q), 4) == 0, kw
+    assert L.gdr_segment_summaries_workspace_size(ctypes.byref(p), 0) == 0
+    # a workspace smaller than asked for is an argument error (before any launch)
+    small = 2 * 16 * 8 * 128 * 256 * 4 - 16
+    assert L.gdr_segment_summaries_ws(ctypes.byref(p), None, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, small,
+                                      None) == B.GDR_ERR_INVALID_ARG
+    assert "workspace_bytes" in L.gdr_last_error().decode()
+    assert L.gdr_segment_summaries_ws(ctypes.byref(p), None, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      ctypes.c_void_p(0x10008), 1 << 30, None) == B.GDR_ERR_INVALID_ARG
 
 
 def test_force_tile_env(monkeypatch):

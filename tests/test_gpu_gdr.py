@@ -215,6 +215,36 @@ def test_segment_summaries_strong_decay(pkg, gates):
     check(r, ref_of(inp), 1e-2, what=f"segmented path, {gates}")
 
 
+def test_half_segment_summaries_match_direct_and_oracle(pkg):
+    """The summaries formed from two half segments (with the workspace) and the
+    direct ones both match the FP64 oracle's; 11 and 3 chunks over 4 segments
+    give odd halves, one-chunk segments (an empty second half) and an empty
+    segment."""
+    lengths = [700, 130]
+    P = 4
+    inp = make_gdr(309, lengths=lengths, H=2, DK=128, DV=128, dtype=torch.bfloat16, varlen=True)
+    k, v, g, b = (dev(x) for x in (inp.k, inp.v, inp.g, inp.beta))
+    cu = inp.cu_seqlens
+    assert pkg.gdr_segment_summaries_workspace_size(k, 128, P, cu) == 2 * 2 * P * 2 * 128 * 256 * 4
+    g_cum, w, u = pkg.gdr_chunk_prepare(k, v, g, b, cu)
+    split = pkg.gdr_segment_summaries(k, w, u, g_cum, P, cu)
+    direct = pkg.gdr_segment_summaries(k, w, u, g_cum, P, cu, workspace=False)
+    torch.cuda.synchronize()
+    d = inp.f64()
+    cuh = d["cu_seqlens"]
+    for n in range(len(lengths)):
+        s, e = cuh[n], cuh[n + 1]
+        S_loc, M = oracle.gdr_segment_summaries_fp64(d["k"][0, s:e], d["v"][0, s:e], d["g"][0, s:e],
+                                                     d["beta"][0, s:e], oracle.segment_bounds(e - s, P))
+        for name, (ss, st) in (("split", split), ("direct", direct)):
+            es = rel(to_np(ss[n * P:(n + 1) * P]).transpose(0, 1, 3, 2), S_loc)
+            em = rel(to_np(st[n * P:(n + 1) * P]), M)
+            print(f"seq {n} {name}: S_loc {es:.3e} M {em:.3e}", flush=True)
+            assert es <= 1e-2 and em <= 1e-2
+    # the two forms agree closely (FP32 composition of the halves)
+    assert rel(to_np(split[1]), to_np(direct[1])) <= 1e-2
+
+
 def test_empty_and_single_token_sequences(pkg):
     inp = make_gdr(404, lengths=[0, 1, 0, 2, 0], H=2, DK=64, DV=64, dtype=torch.float32, varlen=True, h0_std=0.3)
     r = run_path(pkg, inp)
@@ -252,6 +282,10 @@ def test_bit_identical_across_tiles(pkg, dt):
 def test_bit_identical_segment_summaries_across_tiles(pkg, dt):
     inp = make_gdr(607, lengths=[900], H=2, DK=128, DV=128, dtype=dt, varlen=True)
     base = run_path(pkg, inp, n_segments=3, tile=TILES[dt][0])
+    if dt == torch.bfloat16:  # the summary-only tile (all 256 columns of a segment-head in one block)
+        k, w, u, g_cum = (base[x] if x in base else dev(getattr(inp, x)) for x in ("k", "w", "u", "g_cum"))
+        ss, st = pkg.gdr_segment_summaries(k, w, u, g_cum, 3, inp.cu_seqlens, (256, 8, 2))
+        assert torch.equal(ss, base["seg_state"]) and torch.equal(st, base["seg_trans"]), "tile (256, 8, 2)"
     for t in TILES[dt][1:]:
         r = run_path(pkg, inp, n_segments=3, tile=t)
         for key in ("seg_state", "seg_trans", "seg_init", "h", "hT", "o"):
