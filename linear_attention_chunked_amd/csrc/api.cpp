@@ -238,14 +238,13 @@ gdr_status gdr_chunk_output(const gdr_problem* p, const void* q, const void* k, 
   a.o = o;
   a.scale = scale;
   a.H = pr.H;
-  for (const gdr::Launch& l : gdr::plan_chunks(pr, pr.DV / 64)) {
+  // bfloat16: one workgroup per (chunk, head) for all value columns; float32: per 64 columns
+  for (const gdr::Launch& l : gdr::plan_chunks(pr, pr.dtype == GDR_BF16 ? 1 : pr.DV / 64)) {
     a.n_rows = static_cast<int32_t>(l.rows.size());
     a.n_chunks = l.n_chunks;
     a.chunk_base = l.chunk_base;
     memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
-    // the bfloat16 kernel is persistent (next item prefetched): two resident workgroups per CU
-    const int grid = pr.dtype == GDR_BF16 ? std::min(l.grid, 2 * cu_count()) : l.grid;
-    hipError_t e = fn(&a, grid, static_cast<hipStream_t>(stream));
+    hipError_t e = fn(&a, l.grid, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "output launch");
   }
   return GDR_OK;
