@@ -175,8 +175,8 @@ gdr_status gdr_chunk_prepare(const gdr_problem* p, const void* k, const void* v,
     a.chunk_base = l.chunk_base;
     memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
     // the bfloat16 kernel is persistent (each workgroup prefetches its next
-    // chunk while computing the current one): three resident workgroups per CU
-    const int grid = pr.dtype == GDR_BF16 ? std::min(l.grid, 3 * cu_count()) : l.grid;
+    // chunk while computing the current one): four resident workgroups per CU
+    const int grid = pr.dtype == GDR_BF16 ? std::min(l.grid, 4 * cu_count()) : l.grid;
     hipError_t e = fn(&a, grid, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prepare launch");
   }

@@ -21,6 +21,10 @@
 //     no LDS round trip.
 //   * w and u from T' = T diag(.) split into bf16 hi + lo parts (one rounding:
 //     the final store).
+//   * V is loaded (into registers) once the diagonal blocks are done and
+//     takes the place of A / T in LDS for the last product, once every wave
+//     holds its rows of T' as operand fragments; the footprint (35.6 KB at
+//     128 x 128) and 128 VGPRs let four workgroups share a CU.
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
@@ -50,14 +54,14 @@ struct Prepare2 {
   // A and T share one matrix: every block of T is written over the block of
   // A in the same place once nothing reads that A block any more (T[b][b]
   // after its own substitution, T[1][0] and T[3][2] from the wave that read
-  // their A blocks, the last four blocks after a barrier).  With it the
-  // footprint (≈ 53 KB) lets three workgroups share a CU.
+  // their A blocks, the last four blocks after a barrier); V replaces T for
+  // the last product.
   struct Smem {
     char k[kChunk * SKB];
-    char v[kChunk * SVB];
     union {
       float a[kChunk * LDA];
       float t[kChunk * LDA];
+      char v[kChunk * SVB];
     };
     float gam[kChunk];
     float beta[kChunk];
@@ -73,13 +77,12 @@ struct Prepare2 {
     return lo;
   }
 
-  // The next item's K, V rows (and g, beta for the first wave) travel in
+  // The next item's K rows (and g, beta for the first wave) travel in
   // registers while the current item computes.
   static constexpr int KV_PT = kChunk * (DK / 8) / NT;  // 16-byte K vectors per thread
   static constexpr int VV_PT = kChunk * (DV / 8) / NT;
   struct Pref {
     u32x4_t k[KV_PT];
-    u32x4_t v[VV_PT];
     float g, b;
   };
 
@@ -105,19 +108,12 @@ struct Prepare2 {
     const Item it = item_of(a, live ? item : 0);
     const int64_t H = a.H;
     const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (it.tok0 * H + it.hd) * DK;
-    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (it.tok0 * H + it.hd) * DV;
     const rsrc_t rk = make_rsrc(kp, live ? static_cast<uint32_t>(((it.nvalid - 1) * H + 1) * DK * 2) : 0u);
-    const rsrc_t rv = make_rsrc(vp, live ? static_cast<uint32_t>(((it.nvalid - 1) * H + 1) * DV * 2) : 0u);
-    constexpr int CK = DK / 8, CV = DV / 8;  // 16-byte chunks per row
+    constexpr int CK = DK / 8;  // 16-byte chunks per row
 #pragma unroll
     for (int i = 0; i < KV_PT; ++i) {
       const int vv = tid + i * NT, r = vv / CK, c = vv % CK;
       pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, static_cast<int>(r * H * DK * 2 + c * 16), 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < VV_PT; ++i) {
-      const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
-      pf.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
     }
     const float* gp = a.g + it.tok0 * H + it.hd;
     const float* bp = a.beta + it.tok0 * H + it.hd;
@@ -150,18 +146,14 @@ struct Prepare2 {
     const int nvalid = it.nvalid;
     const int64_t H = a.H;
 
-    // ---- K, V rows (zero past the tail), gamma, beta from the prefetch; the next item's loads go out ----
+    // ---- K rows (zero past the tail), gamma, beta from the prefetch; the next item's loads go out ----
+    constexpr int CV = DV / 8;
     {
-      constexpr int CK = DK / 8, CV = DV / 8;
+      constexpr int CK = DK / 8;
 #pragma unroll
       for (int i = 0; i < KV_PT; ++i) {
         const int vv = tid + i * NT, r = vv / CK, c = vv % CK;
         *reinterpret_cast<u32x4_t*>(sm.k + r * SKB + c * 16) = pf.k[i];
-      }
-#pragma unroll
-      for (int i = 0; i < VV_PT; ++i) {
-        const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
-        *reinterpret_cast<u32x4_t*>(sm.v + r * SVB + c * 16) = pf.v[i];
       }
       if (wave == 0) {
         float x = (lane < nvalid) ? pf.g : 0.f;
@@ -232,6 +224,17 @@ struct Prepare2 {
       const int r = e >> 6, c = e & 63;
       if ((c >> 4) > (r >> 4)) sm.t[r * LDA + c] = 0.f;
     }
+    // V rows for the last product (zero past the tail): in flight during the off-diagonal blocks
+    u32x4_t vcur[VV_PT];
+    {
+      const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + hd) * DV;
+      const rsrc_t rv = make_rsrc(vp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
+#pragma unroll
+      for (int i = 0; i < VV_PT; ++i) {
+        const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
+        vcur[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
+      }
+    }
     __syncthreads();
 
     // FP32 operand reads for mm16: row-major rows (a) and C-layout columns (b)
@@ -281,73 +284,68 @@ struct Prepare2 {
 
     // ---- w^T = K^T T'^T and u^T = V^T T''^T; wave = token tile of the output ----
     const int t = 16 * wave + c16;
-    frag bw_hi[2], bw_lo[2], bu_hi[2], bu_lo[2];
+    // this lane's operand fragments of row t of T diag(coef), split into bf16 hi + lo
+    auto row_frags = [&](const float* coef, frag (&hi)[2], frag (&lo)[2]) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int i0 = 32 * s + 4 * g4;
-      const f32x4_t t0 = *reinterpret_cast<const f32x4_t*>(&sm.t[t * LDA + i0]);
-      const f32x4_t t1 = *reinterpret_cast<const f32x4_t*>(&sm.t[t * LDA + i0 + 16]);
-      const f32x4_t bg0 = *reinterpret_cast<const f32x4_t*>(&sm.bg[i0]);
-      const f32x4_t bg1 = *reinterpret_cast<const f32x4_t*>(&sm.bg[i0 + 16]);
-      const f32x4_t be0 = *reinterpret_cast<const f32x4_t*>(&sm.beta[i0]);
-      const f32x4_t be1 = *reinterpret_cast<const f32x4_t*>(&sm.beta[i0 + 16]);
-      const f32x4_t w0 = t0 * bg0, w1 = t1 * bg1, u0 = t0 * be0, u1 = t1 * be1;
-      bw_hi[s] = S::frag_from_f32(w0, w1);
-      bu_hi[s] = S::frag_from_f32(u0, u1);
-      f32x4_t wl0, wl1, ul0, ul1;
+      for (int s = 0; s < 2; ++s) {
+        const int i0 = 32 * s + 4 * g4;
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(&sm.t[t * LDA + i0]) *
+                           *reinterpret_cast<const f32x4_t*>(&coef[i0]);
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(&sm.t[t * LDA + i0 + 16]) *
+                           *reinterpret_cast<const f32x4_t*>(&coef[i0 + 16]);
+        hi[s] = S::frag_from_f32(x0, x1);
+        f32x4_t l0, l1;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        wl0[r] = w0[r] - bf16_to_f32(f32_to_bf16(w0[r]));
-        wl1[r] = w1[r] - bf16_to_f32(f32_to_bf16(w1[r]));
-        ul0[r] = u0[r] - bf16_to_f32(f32_to_bf16(u0[r]));
-        ul1[r] = u1[r] - bf16_to_f32(f32_to_bf16(u1[r]));
+        for (int r = 0; r < 4; ++r) {
+          l0[r] = x0[r] - bf16_to_f32(f32_to_bf16(x0[r]));
+          l1[r] = x1[r] - bf16_to_f32(f32_to_bf16(x1[r]));
+        }
+        lo[s] = S::frag_from_f32(l0, l1);
       }
-      bw_lo[s] = S::frag_from_f32(wl0, wl1);
-      bu_lo[s] = S::frag_from_f32(ul0, ul1);
-    }
+    };
     const int nsteps = (16 * wave + 15) / 32 + 1;  // T is lower triangular
     // A operand K^T[d][i] / V^T[d][i] via transpose reads of the row-major tiles
     const int tr_row = 4 * g4 + (c16 >> 2);
     const int tr_col = 8 * (c16 & 3);
-    uint16_t* wo = static_cast<uint16_t*>(a.w) + (tok0 * H + hd) * DK;
-    uint16_t* uo = static_cast<uint16_t*>(a.u) + (tok0 * H + hd) * DV;
-    const rsrc_t rwo = make_rsrc(wo, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
-    const rsrc_t ruo = make_rsrc(uo, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
+    auto product = [&](const char* tile, int stride, int D, const frag (&hi)[2], const frag (&lo)[2], void* out) {
+      uint16_t* op = static_cast<uint16_t*>(out) + (tok0 * H + hd) * D;
+      const rsrc_t ro = make_rsrc(op, static_cast<uint32_t>(((nvalid - 1) * H + 1) * D * 2));
 #pragma unroll
-    for (int dt = 0; dt < DK / 16; ++dt) {
-      f32x4_t acc{0.f, 0.f, 0.f, 0.f};
+      for (int dt = 0; dt < D / 16; ++dt) {
+        f32x4_t acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (s < nsteps) {
-          const char* base = sm.k + (32 * s + tr_row) * SKB + 32 * dt + tr_col;
-          const frag fa = S::frag_from_quads(lds_tr16(base, 0), lds_tr16(base, 16 * SKB));
-          S::mma(acc, fa, bw_hi[s]);
-          S::mma(acc, fa, bw_lo[s]);
+        for (int s = 0; s < 2; ++s) {
+          if (s < nsteps) {
+            const char* base = tile + (32 * s + tr_row) * stride + 32 * dt + tr_col;
+            const frag fa = S::frag_from_quads(lds_tr16(base, 0), lds_tr16(base, 16 * stride));
+            S::mma(acc, fa, hi[s]);
+            S::mma(acc, fa, lo[s]);
+          }
         }
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])}, ro,
+                                              static_cast<int>(t * H * D * 2 + (16 * dt + 4 * g4) * 2), 0, 0);
       }
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])}, rwo,
-                                            static_cast<int>(t * H * DK * 2 + (16 * dt + 4 * g4) * 2), 0, 0);
+    };
+    {
+      frag hi[2], lo[2];
+      row_frags(sm.bg, hi, lo);  // T diag(beta e^gamma)
+      product(sm.k, SKB, DK, hi, lo, a.w);
     }
+    frag uh[2], ul[2];
+    row_frags(sm.beta, uh, ul);  // T diag(beta)
+    __syncthreads();  // every wave holds its rows of T diag(beta): V replaces T
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) {
-      f32x4_t acc{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (s < nsteps) {
-          const char* base = sm.v + (32 * s + tr_row) * SVB + 32 * dt + tr_col;
-          const frag fa = S::frag_from_quads(lds_tr16(base, 0), lds_tr16(base, 16 * SVB));
-          S::mma(acc, fa, bu_hi[s]);
-          S::mma(acc, fa, bu_lo[s]);
-        }
-      }
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])}, ruo,
-                                            static_cast<int>(t * H * DV * 2 + (16 * dt + 4 * g4) * 2), 0, 0);
+    for (int i = 0; i < VV_PT; ++i) {
+      const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
+      *reinterpret_cast<u32x4_t*>(sm.v + r * SVB + c * 16) = vcur[i];
     }
+    __syncthreads();
+    product(sm.v, SVB, DV, uh, ul, a.u);
   }
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void prepare2_kernel(const ChunkArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void prepare2_kernel(const ChunkArgs a) {
   using K = Prepare2<DK, DV>;
   __shared__ __align__(16) typename K::Smem sm;
   K::run(a, sm);
