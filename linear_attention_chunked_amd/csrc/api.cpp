@@ -272,7 +272,7 @@ gdr_status gdr_chunk_dv_local(const gdr_problem* p, const void* q, const void* k
   a.o = dv_local;
   a.scale = scale;
   a.H = pr.H;
-  for (const gdr::Launch& l : gdr::plan_chunks(pr, pr.DV / 64)) {
+  for (const gdr::Launch& l : gdr::plan_chunks(pr, 1)) {
     a.n_rows = static_cast<int32_t>(l.rows.size());
     a.n_chunks = l.n_chunks;
     a.chunk_base = l.chunk_base;

@@ -28,12 +28,14 @@
 namespace gdr {
 
 // ---------------------------------------------------------------- scale P^T dO
+// One workgroup per (chunk, head) for all DV value columns (Q and K read and
+// P formed once per chunk-head); wave w owns key tile w.
 template <int DK, int DV>
 struct DvLocal {
   using S = St<bf16_t>;
   using frag = S::frag;
   static constexpr int NT = 256;
-  static constexpr int BVO = 64;
+  static constexpr int BVO = DV;
   static constexpr int NCT = BVO / 16;
   static constexpr int SQ = DK * 2 + 16;   // Q, K rows (bytes)
   static constexpr int SD = BVO * 2 + 32;  // dO rows (transpose reads)
