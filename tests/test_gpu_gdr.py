@@ -245,6 +245,29 @@ def test_half_segment_summaries_match_direct_and_oracle(pkg):
     assert rel(to_np(split[1]), to_np(direct[1])) <= 1e-2
 
 
+def test_many_sequences_span_several_launches(pkg):
+    """More packed sequences than one launch's work list holds (112 rows): the
+    scan, prepare and output split the batch over launches; empty and
+    one-token sequences are mixed in."""
+    rng = np.random.default_rng(5)
+    lengths = [int(x) for x in rng.integers(0, 71, 250)]
+    lengths[:4] = [0, 1, 64, 65]
+    inp = make_gdr(313, lengths=lengths, H=2, DK=64, DV=64, dtype=torch.bfloat16, varlen=True, h0_std=0.1)
+    r = run_path(pkg, inp)
+    check(r, ref_of(inp), TOL[torch.bfloat16], what=f"{len(lengths)} sequences")
+
+
+def test_segmented_many_sequences_span_several_launches(pkg):
+    """40 sequences x 3 segments: 120 summary rows (240 half rows with the
+    workspace) and 120 final-pass rows, each over several launches."""
+    rng = np.random.default_rng(6)
+    lengths = [int(x) for x in rng.integers(1, 400, 40)]
+    inp = make_gdr(314, lengths=lengths, H=2, DK=128, DV=128, dtype=torch.bfloat16, varlen=True, h0_std=0.1)
+    assert pkg.gdr_segment_summaries_workspace_size(inp.k.cuda(), 128, 3, inp.cu_seqlens) > 0
+    r = run_path(pkg, inp, n_segments=3)
+    check(r, ref_of(inp), TOL[torch.bfloat16], what="40 sequences, 3 segments")
+
+
 def test_empty_and_single_token_sequences(pkg):
     inp = make_gdr(404, lengths=[0, 1, 0, 2, 0], H=2, DK=64, DV=64, dtype=torch.float32, varlen=True, h0_std=0.3)
     r = run_path(pkg, inp)

@@ -154,6 +154,17 @@ def test_kda_question_rows_workload(pkg):
         assert torch.equal(out[key], again[key]), f"run to run: {key}"
 
 
+def test_kda_many_sequences_span_several_launches(pkg):
+    """More packed sequences than one launch's work list holds (112 rows):
+    prepare, scan and output split the batch over launches."""
+    rng = np.random.default_rng(7)
+    lengths = [int(x) for x in rng.integers(0, 71, 200)]
+    lengths[:3] = [0, 1, 65]
+    inp = problem(671, lengths, H=2, DK=64, DV=64)
+    out = gpu_forward(pkg, inp, 0.5)
+    check_against_oracle(out, inp, 0.5, f"kda {len(lengths)} sequences", factors=False)
+
+
 def test_kda_empty_single_token_and_pool(pkg):
     """Empty and one-token sequences (an empty sequence keeps its initial
     state and writes nothing else), and indexed states: sequence n reads and
