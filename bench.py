@@ -377,6 +377,26 @@ def long_state(pkg, torch, dev, reps=5, copy_gbs=None):
         tp = _event_median_us(torch, fn, reps=reps) * 1e-6
         res["segmented"]["phases"][name] = {"us": round(tp * 1e6, 1), "alg_bytes": alg_phase[name],
                                             "frac_of_hbm": round(alg_phase[name] / tp / 8e12, 4)}
+    # CP vs serial, reported as the pages' accuracy table does (not a gate:
+    # each path is checked against the FP64 oracle in the tests): relative L2
+    # between the segmented and the serial path's outputs o, final states and
+    # o over the last 8K tokens
+    q = inp.q.to(dev)
+    outs = {}
+    for name, fn in (("serial", serial), ("segmented", segmented)):
+        fn()
+        o = torch.empty_like(v)
+        B._check(L.gdr_chunk_output(pr.ref, ptr(q), ptr(k), ptr(v_new), ptr(h), ptr(g_cum), float(inp.scale), ptr(o),
+                                    sp), "output")
+        torch.cuda.synchronize()
+        outs[name] = (o.double(), hT.double().clone())
+
+    def rl(x, y):
+        return float(torch.linalg.vector_norm(x - y) / torch.linalg.vector_norm(y))
+
+    (os_, hs), (oc, hc) = outs["serial"], outs["segmented"]
+    res["cp_vs_serial_rel_l2"] = {"out": rl(oc, os_), "final": rl(hc, hs),
+                                  "last_8k": rl(oc[:, -8192:], os_[:, -8192:])}
     res["workload"] = "long_state_h8 (T=65536, H=8, dk=dv=128, bf16, 16 segments)"
     return res
 

@@ -140,6 +140,21 @@ def test_long_state_h8_sampled_heads(pkg, segmented):
     check(r, ref_of(inp, heads=heads), TOL[torch.bfloat16], heads=heads, what=f"long_state_h8 seg={segmented}")
 
 
+def test_long_state_h1_cp_vs_serial_report(pkg):
+    """The 16-segment path against the serial scan on the 64K one-head state,
+    reported as relative L2 of the outputs, the final state and the outputs of
+    the last 8K tokens (a report, not a gate: both paths are gated against the
+    FP64 oracle above)."""
+    inp = config("long_state_h1")
+    a = run_path(pkg, inp)
+    b = run_path(pkg, inp, n_segments=16)
+    out = rel(to_np(b["o"]), to_np(a["o"]))
+    fin = rel(to_np(b["hT"]), to_np(a["hT"]))
+    last = rel(to_np(b["o"][:, -8192:]), to_np(a["o"][:, -8192:]))
+    print(f"CP vs serial (long_state_h1, 16 segments): out {out:.3e} final {fin:.3e} last-8K {last:.3e}", flush=True)
+    assert np.isfinite([out, fin, last]).all()
+
+
 # --------------------------------------------------------------------------- shapes and edges
 CASES = [
     # dtype, DK, DV, lengths, h0, scale
