@@ -141,6 +141,9 @@ def main():
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-state", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the bench line: time every built tile on the workloads the scheduler's table "
+                         "covers (one JSON line per workload and tile)")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="also run a plain 'copy' of this many MiB (counter reference for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -158,6 +161,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pkg.lib()
     dev = torch.device("cuda:0")
+    if args.sweep:
+        sweep(pkg, torch, dev)
+        return
     inp = make_config(args.workload)
     q, k, v, g, beta = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
     h0 = inp.h0.to(dev) if inp.h0 is not None else None
@@ -221,6 +227,7 @@ def main():
         "alg_bytes_per_launch": alg,
         "launch_us_mean": round(scan_mean_ms * 1e3, 2),
         "launch_us_median": round(scan_ms[len(scan_ms) // 2] * 1e3, 2),
+        "launch_us_stats": _stats_us(scan_ms),
         "mfma_frac": round(scan_flops(inp.lengths, inp.H, inp.DK, DV) / (scan_mean_ms * 1e-3) / 1e12
                            / BF16_PEAK_TFLOPS, 4),
     }
@@ -300,6 +307,57 @@ def main():
         out["cpu_baseline"] = cpu_baseline(inp)
 
     print(json.dumps(out), flush=True)
+
+
+def _stats_us(ms_sorted):
+    """n, mean, std, min and the 10/20/50/80/90th percentiles (us) of sorted
+    durations in ms."""
+    import statistics
+
+    us = [x * 1e3 for x in ms_sorted]
+    pct = lambda p: us[min(len(us) - 1, int(round(p / 100 * (len(us) - 1))))]
+    return {"n": len(us), "mean": round(statistics.fmean(us), 2), "std": round(statistics.pstdev(us), 2),
+            "min": round(us[0], 2), "p10": round(pct(10), 2), "p20": round(pct(20), 2), "p50": round(pct(50), 2),
+            "p80": round(pct(80), 2), "p90": round(pct(90), 2)}
+
+
+def sweep(pkg, torch, dev):
+    """Every built bfloat16 tile on the workloads the scheduler's table covers:
+    the state scan on question_rows and new_states, and the 64K x 8-head
+    segmented pass (summaries per tile, with and without the half-segment
+    split, and the final pass per tile).  One JSON line per measurement, each
+    the median of 5 x the mean of 4 back-to-back calls between HIP events."""
+    from workloads import make_config
+
+    tiles = [(32, 2, 2), (32, 2, 3), (64, 2, 3), (64, 4, 2), (64, 4, 3), (128, 4, 2), (128, 4, 3)]
+    for name in ("question_rows", "new_states"):
+        inp = make_config(name)
+        k, v, g, b = (x.to(dev) for x in (inp.k, inp.v, inp.g, inp.beta))
+        h0 = inp.h0.to(dev) if inp.h0 is not None else None
+        cu = inp.cu_seqlens
+        g_cum, w, u = pkg.gdr_chunk_prepare(k, v, g, b, cu)
+        h, v_new, hT = pkg.gdr_state_scan(k, w, u, g_cum, h0, cu)
+        out = {"h": h, "v_new": v_new, "hT": hT}
+        default = pkg.gdr_plan_query(k, v.shape[-1], cu)[:3]
+        for t in tiles:
+            us = _event_median_us(torch, lambda: pkg.gdr_state_scan(k, w, u, g_cum, h0, cu, t, out=out))
+            print(json.dumps({"sweep": "state scan", "workload": name, "tile": t, "default": tuple(default) == t,
+                              "us": round(us, 1)}), flush=True)
+    inp = make_config("long_state_h8")
+    k, v, g, b = (x.to(dev) for x in (inp.k, inp.v, inp.g, inp.beta))
+    g_cum, w, u = pkg.gdr_chunk_prepare(k, v, g, b)
+    P = 16
+    for t in tiles + [(256, 8, 2)]:
+        for ws in (False, True):
+            us = _event_median_us(torch, lambda: pkg.gdr_segment_summaries(k, w, u, g_cum, P, None, t, workspace=ws))
+            print(json.dumps({"sweep": "segment summaries", "workload": "long_state_h8, 16 segments", "tile": t,
+                              "half_segments": ws, "us": round(us, 1)}), flush=True)
+    ss, st = pkg.gdr_segment_summaries(k, w, u, g_cum, P)
+    si, _ = pkg.gdr_segment_compose(k, v.shape[-1], ss, st, P)
+    for t in tiles:
+        us = _event_median_us(torch, lambda: pkg.gdr_state_scan(k, w, u, g_cum, None, None, t, P, si))
+        print(json.dumps({"sweep": "segmented final pass", "workload": "long_state_h8, 16 segments", "tile": t,
+                          "us": round(us, 1)}), flush=True)
 
 
 def long_state(pkg, torch, dev, reps=5, copy_gbs=None):
