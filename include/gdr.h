@@ -50,8 +50,12 @@
  *    A packed batch uses B = 1, T = total tokens and cu_seqlens_host with N+1
  *    entries; sequence n is tokens [cu[n], cu[n+1]).  Chunks restart at each
  *    sequence start; NT = sum_n ceil(L_n / 64), sequences in order.
- *  - Supported: DK, DV in {64, 128}; float32 or bfloat16 storage.  Chunk size
- *    is 64 tokens.
+ *  - Supported: DK, DV in {64, 128}, float32 or bfloat16 storage, for every
+ *    entry point.  With bfloat16 storage DK and DV may also be 256 (each of
+ *    them; (256, 256), (256, 128), (128, 256)) for gdr_chunk_prepare,
+ *    gdr_state_scan and gdr_chunk_output; the segment summaries and
+ *    composition, the reverse pass and the per-channel decay entry points
+ *    return GDR_ERR_UNSUPPORTED there.  Chunk size is 64 tokens.
  */
 #ifndef GDR_H_
 #define GDR_H_

@@ -77,6 +77,12 @@ gdr_status tile_for(const gdr::Problem& pr, const gdr_tile* tile, int mode, int6
   return GDR_OK;
 }
 
+// bfloat16 up to 128 x 128 runs the gfx950 kernels of prepare2.hip /
+// output2.hip (persistent prepare; output per (chunk, head)); DK or DV = 256
+// and float32 run the generic kernels (per (chunk, head); output per 64 value
+// columns).
+bool fast_bf16(const gdr::Problem& pr) { return pr.dtype == GDR_BF16 && pr.DK <= 128 && pr.DV <= 128; }
+
 gdr_status hip_fail(hipError_t e, const char* what) {
   return fail(GDR_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
@@ -176,7 +182,7 @@ gdr_status gdr_chunk_prepare(const gdr_problem* p, const void* k, const void* v,
     memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
     // the bfloat16 kernel is persistent (each workgroup prefetches its next
     // chunk while computing the current one): four resident workgroups per CU
-    const int grid = pr.dtype == GDR_BF16 ? std::min(l.grid, 4 * cu_count()) : l.grid;
+    const int grid = fast_bf16(pr) ? std::min(l.grid, 4 * cu_count()) : l.grid;
     hipError_t e = fn(&a, grid, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prepare launch");
   }
@@ -238,8 +244,8 @@ gdr_status gdr_chunk_output(const gdr_problem* p, const void* q, const void* k, 
   a.o = o;
   a.scale = scale;
   a.H = pr.H;
-  // bfloat16: one workgroup per (chunk, head) for all value columns; float32: per 64 columns
-  for (const gdr::Launch& l : gdr::plan_chunks(pr, pr.dtype == GDR_BF16 ? 1 : pr.DV / 64)) {
+  // bfloat16 up to 128 x 128: one workgroup per (chunk, head) for all value columns; else per 64 columns
+  for (const gdr::Launch& l : gdr::plan_chunks(pr, fast_bf16(pr) ? 1 : pr.DV / 64)) {
     a.n_rows = static_cast<int32_t>(l.rows.size());
     a.n_chunks = l.n_chunks;
     a.chunk_base = l.chunk_base;

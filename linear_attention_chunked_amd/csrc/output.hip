@@ -192,9 +192,14 @@ static hipError_t launch_output(const void* args, int grid, hipStream_t stream) 
 }
 
 LaunchFn find_output(int dtype, int dk, int dv) {
-  if (dtype == 1) return find_output2(dk, dv);  // bfloat16 storage: the gfx950 fast path
+  // bfloat16 storage: the gfx950 kernel of output2.hip up to 128 x 128; this
+  // generic kernel when DK or DV is 256
+  if (dtype == 1 && dk <= 128 && dv <= 128) return find_output2(dk, dv);
 #define GDR_OUT_CASE(T, DT, DK, DV) \
   if (dtype == DT && dk == DK && dv == DV) return &launch_output<T, DK, DV>;
+  GDR_OUT_CASE(bf16_t, 1, 256, 256)
+  GDR_OUT_CASE(bf16_t, 1, 256, 128)
+  GDR_OUT_CASE(bf16_t, 1, 128, 256)
   GDR_OUT_CASE(bf16_t, 1, 128, 128)
   GDR_OUT_CASE(bf16_t, 1, 128, 64)
   GDR_OUT_CASE(bf16_t, 1, 64, 128)

@@ -16,8 +16,13 @@ bool parse_problem(int B, int64_t T, int H, int DK, int DV, int N, const int32_t
     err = "B >= 1, T >= 0 and H >= 1 are required";
     return false;
   }
-  if (!((DK == 64 || DK == 128) && (DV == 64 || DV == 128))) {
-    err = "DK and DV must each be 64 or 128";
+  auto dim_ok = [](int d) { return d == 64 || d == 128 || d == 256; };
+  if (!(dim_ok(DK) && dim_ok(DV))) {
+    err = "DK and DV must each be 64, 128 or 256";
+    return false;
+  }
+  if (dtype == 0 && (DK == 256 || DV == 256)) {
+    err = "DK or DV = 256 is supported for bfloat16 storage only";
     return false;
   }
   if (dtype != 0 && dtype != 1) {
@@ -108,8 +113,15 @@ bool parse_problem(int B, int64_t T, int H, int DK, int DV, int N, const int32_t
   return true;
 }
 
-// Built tiles (must match the instantiations in scan.hip).
-static bool tile_built(int dtype, int bv, int waves, int stages) {
+// Built tiles (must match the instantiations in scan.hip and scan2.hip).  DK =
+// 256 (bfloat16) runs the generic kernel of scan.hip with its four tiles.
+static bool tile_built(int dtype, int dk, int bv, int waves, int stages) {
+  if (dtype == 1 && dk == 256) {
+    static const int g_tiles[][3] = {{32, 2, 1}, {32, 2, 2}, {64, 4, 1}, {64, 4, 2}};
+    for (auto& t : g_tiles)
+      if (t[0] == bv && t[1] == waves && t[2] == stages) return true;
+    return false;
+  }
   if (dtype == 1 && bv == 256 && waves == 8 && stages == 2) return true;  // balanced summaries only
   static const int bf16_tiles[][3] = {{32, 2, 2}, {32, 2, 3}, {64, 2, 3}, {64, 4, 2},
                                       {64, 4, 3}, {128, 4, 2}, {128, 4, 3}};
@@ -180,7 +192,7 @@ bool choose_tile(const Problem& p, const int32_t* req, int mode, int64_t rows, T
     }
   }
   const int kmode = (mode == 1) ? summary_kernel_mode(p) : 0;
-  if (!tile_built(p.dtype, r[0], r[1], r[2])) {
+  if (!tile_built(p.dtype, p.DK, r[0], r[1], r[2])) {
     err = "tile (bv=" + std::to_string(r[0]) + ", waves=" + std::to_string(r[1]) +
           ", stages=" + std::to_string(r[2]) + ") is not built for this dtype";
     return false;

@@ -277,9 +277,14 @@ static hipError_t launch_prepare(const void* args, int grid, hipStream_t stream)
 }
 
 LaunchFn find_prepare(int dtype, int dk, int dv) {
-  if (dtype == 1) return find_prepare2(dk, dv);  // bfloat16 storage: the gfx950 fast path
+  // bfloat16 storage: the gfx950 kernel of prepare2.hip up to 128 x 128; this
+  // generic kernel when DK or DV is 256
+  if (dtype == 1 && dk <= 128 && dv <= 128) return find_prepare2(dk, dv);
 #define GDR_PREP_CASE(T, DT, DK, DV) \
   if (dtype == DT && dk == DK && dv == DV) return &launch_prepare<T, DK, DV>;
+  GDR_PREP_CASE(bf16_t, 1, 256, 256)
+  GDR_PREP_CASE(bf16_t, 1, 256, 128)
+  GDR_PREP_CASE(bf16_t, 1, 128, 256)
   GDR_PREP_CASE(bf16_t, 1, 128, 128)
   GDR_PREP_CASE(bf16_t, 1, 128, 64)
   GDR_PREP_CASE(bf16_t, 1, 64, 128)

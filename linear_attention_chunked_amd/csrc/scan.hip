@@ -382,8 +382,11 @@ static hipError_t launch_scan(const void* args, int grid, hipStream_t stream) {
   if (dtype == DTYPE && dk == DK && bv == BV && waves == NW && stages == ST && mode == MODE) \
     return &launch_scan<T, DK, BV, NW, ST, MODE>;
 
+// bfloat16 storage takes the gfx950 kernel of scan2.hip up to DK = 128 and
+// this generic kernel (plain and segmented passes) at DK = 256.
 LaunchFn find_scan(int dtype, int dk, int bv, int waves, int stages, int mode) {
-  if (dtype == 1) return find_scan2(dk, bv, waves, stages, mode, false);
+  if (dtype == 1 && dk <= 128) return find_scan2(dk, bv, waves, stages, mode, false);
+  GDR_SCAN_TILES(GDR_SCAN_CASE, bf16_t, 1, 256, 0)
   GDR_SCAN_TILES(GDR_SCAN_CASE, float, 0, 128, 0)
   GDR_SCAN_TILES(GDR_SCAN_CASE, float, 0, 128, 1)
   GDR_SCAN_TILES(GDR_SCAN_CASE, float, 0, 64, 0)

@@ -59,10 +59,32 @@ def test_packed_needs_single_row():
     assert _scan(p) == B.GDR_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("dk,dv", [(32, 128), (128, 96), (256, 128)])
+@pytest.mark.parametrize("dk,dv", [(32, 128), (128, 96), (512, 128)])
 def test_unsupported_dims(dk, dv):
     p, _ = _prob(DK=dk, DV=dv)
     assert _scan(p) == B.GDR_ERR_INVALID_ARG
+
+
+def test_dims_256():
+    """DK or DV = 256: bfloat16 only; the plain pass takes the generic kernel's
+    tiles; the segment summaries, the reverse pass and the per-channel decay
+    entry points report GDR_ERR_UNSUPPORTED (before any launch)."""
+    L = B.lib()
+    p, _ = _prob(DK=256, DV=64, dtype=B.GDR_F32)
+    assert _scan(p) == B.GDR_ERR_INVALID_ARG
+    assert b"bfloat16" in L.gdr_last_error()
+    q, _ = _prob(B_=1, DK=256, DV=256, T=4096, H=8)
+    assert _query(q)[:3] == (32, 2, 2)  # few units: the narrower tile
+    p, _ = _prob(B_=8, DK=256, DV=256, T=4096, H=8)
+    assert _query(p)[:3] == (64, 4, 2)
+    assert _scan(p, tile=(128, 4, 3)) == B.GDR_ERR_UNSUPPORTED  # a scan2 tile: not built at DK = 256
+    assert L.gdr_segment_summaries(ctypes.byref(p), None, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == B.GDR_ERR_UNSUPPORTED
+    assert L.gdr_segment_compose(ctypes.byref(p), 2, FAKE, FAKE, None, FAKE, None, None) == B.GDR_ERR_UNSUPPORTED
+    assert L.gdr_chunk_dv_local(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), FAKE,
+                                None) == B.GDR_ERR_UNSUPPORTED
+    assert L.kda_chunk_output(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), FAKE,
+                              None) == B.GDR_ERR_UNSUPPORTED
 
 
 def test_null_and_misaligned_pointers():

@@ -283,6 +283,27 @@ def test_segmented_many_sequences_span_several_launches(pkg):
     check(r, ref_of(inp), TOL[torch.bfloat16], what="40 sequences, 3 segments")
 
 
+@pytest.mark.parametrize("DK,DV", [(256, 256), (256, 128), (128, 256)])
+def test_parity_dims_256(pkg, DK, DV):
+    """Key or value width 256 (bfloat16): prepare, scan and output against the
+    oracle on ragged packed sequences with initial states."""
+    inp = make_gdr(321 + DK + DV, lengths=[1, 63, 65, 200, 0], H=2, DK=DK, DV=DV, dtype=torch.bfloat16,
+                   varlen=True, h0_std=0.1, scale=DK ** -0.5)
+    r = run_path(pkg, inp)
+    check(r, ref_of(inp), TOL[torch.bfloat16], what=f"dims {DK}x{DV}")
+
+
+def test_bit_identical_across_tiles_dims_256(pkg):
+    inp = make_gdr(333, lengths=[1, 64, 65, 300, 129], H=2, DK=256, DV=256, dtype=torch.bfloat16, varlen=True,
+                   h0_std=0.1)
+    tiles = [(32, 2, 1), (32, 2, 2), (64, 4, 1), (64, 4, 2)]
+    base = run_path(pkg, inp, tile=tiles[0])
+    for t in tiles[1:]:
+        r = run_path(pkg, inp, tile=t)
+        for key in ("h", "v_new", "hT", "o"):
+            assert torch.equal(r[key], base[key]), f"tile {t} changed {key}"
+
+
 def test_empty_and_single_token_sequences(pkg):
     inp = make_gdr(404, lengths=[0, 1, 0, 2, 0], H=2, DK=64, DV=64, dtype=torch.float32, varlen=True, h0_std=0.3)
     r = run_path(pkg, inp)
