@@ -178,7 +178,9 @@ gdr_status gdr_segment_summaries(const gdr_problem* p, const gdr_tile* tile, int
                                  void* stream);
 
 /* Device workspace (bytes) gdr_segment_summaries_ws uses for this problem and
- * segment count; 0 when the summaries are formed directly (host only). */
+ * segment count; 0 when the summaries are formed directly, and also for an
+ * invalid problem or n_segments < 1 (then gdr_last_error() says why; "" when
+ * the problem is valid).  Host only. */
 size_t gdr_segment_summaries_workspace_size(const gdr_problem* p, int32_t n_segments);
 
 /* gdr_segment_summaries with a caller-owned device workspace (16-byte

@@ -342,7 +342,11 @@ gdr_status gdr_state_scan_bwd(const gdr_problem* p, const void* q, const void* k
 size_t gdr_segment_summaries_workspace_size(const gdr_problem* p, int32_t n_segments) {
   g_err.clear();
   gdr::Problem pr;
-  if (parse(p, pr) != GDR_OK || n_segments < 1) return 0;
+  if (parse(p, pr) != GDR_OK) return 0;  // (gdr_last_error says why)
+  if (n_segments < 1) {
+    fail(GDR_ERR_INVALID_ARG, "n_segments must be >= 1");
+    return 0;
+  }
   if (gdr::summary_split(pr, n_segments) != 2) return 0;
   // the half-segment summaries: 2 N P (S_loc, M) pairs in FP32
   return static_cast<size_t>(2) * pr.N * n_segments * pr.H * pr.DK * (pr.DV + pr.DK) * sizeof(float);

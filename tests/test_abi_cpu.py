@@ -156,6 +156,8 @@ def test_summary_workspace_size():
         q, _ = _prob(B_=1, T=4096, H=2, **kw)
         assert L.gdr_segment_summaries_workspace_size(ctypes.byref(q), 4) == 0, kw
     assert L.gdr_segment_summaries_workspace_size(ctypes.byref(p), 0) == 0
+    assert b"n_segments" in L.gdr_last_error()
+    assert L.gdr_segment_summaries_workspace_size(ctypes.byref(p), 32) == 0 and L.gdr_last_error() == b""
     # a workspace smaller than asked for is an argument error (before any launch)
     small = 2 * 16 * 8 * 128 * 256 * 4 - 16
     assert L.gdr_segment_summaries_ws(ctypes.byref(p), None, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, small,
