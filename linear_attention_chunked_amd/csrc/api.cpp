@@ -4,7 +4,6 @@
 #include <string.h>
 
 #include <algorithm>
-#include <atomic>
 #include <string>
 #include <vector>
 
@@ -22,20 +21,6 @@ gdr_status fail(gdr_status s, const std::string& msg) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-// Compute units of the current device (read once per device and cached; a
-// race between threads stores the same value; 256 on MI355X).
-int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 gdr_status need(const void* p, const char* name) {
   if (p == nullptr) return fail(GDR_ERR_INVALID_ARG, std::string(name) + " must not be NULL");
@@ -78,7 +63,7 @@ gdr_status tile_for(const gdr::Problem& pr, const gdr_tile* tile, int mode, int6
 }
 
 // bfloat16 up to 128 x 128 runs the gfx950 kernels of prepare2.hip /
-// output2.hip (persistent prepare; output per (chunk, head)); DK or DV = 256
+// output2.hip (each one workgroup per (chunk, head)); DK or DV = 256
 // and float32 run the generic kernels (per (chunk, head); output per 64 value
 // columns).
 bool fast_bf16(const gdr::Problem& pr) { return pr.dtype == GDR_BF16 && pr.DK <= 128 && pr.DV <= 128; }
@@ -180,10 +165,7 @@ gdr_status gdr_chunk_prepare(const gdr_problem* p, const void* k, const void* v,
     a.n_chunks = l.n_chunks;
     a.chunk_base = l.chunk_base;
     memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
-    // the bfloat16 kernel is persistent (each workgroup prefetches its next
-    // chunk while computing the current one): four resident workgroups per CU
-    const int grid = fast_bf16(pr) ? std::min(l.grid, 4 * cu_count()) : l.grid;
-    hipError_t e = fn(&a, grid, static_cast<hipStream_t>(stream));
+    hipError_t e = fn(&a, l.grid, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prepare launch");
   }
   return GDR_OK;

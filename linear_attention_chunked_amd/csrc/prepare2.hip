@@ -22,9 +22,9 @@
 //   * w and u from T' = T diag(.) split into bf16 hi + lo parts (one rounding:
 //     the final store).
 //   * V is loaded (into registers) once the diagonal blocks are done and
-//     takes the place of A / T in LDS for the last product, once every wave
-//     holds its rows of T' as operand fragments; the footprint (35.6 KB at
-//     128 x 128) and 128 VGPRs let four workgroups share a CU.
+//     takes the place of K in LDS once the w product has read K.  A and T
+//     keep only their blocks on or below the diagonal; the footprint (29.4 KB
+//     at 128 x 128) and at most 96 VGPRs let five workgroups share a CU.
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
@@ -48,25 +48,31 @@ struct Prepare2 {
   static constexpr int NT = 256;
   static constexpr int SKB = DK * 2 + 16;   // padded row strides (bytes)
   static constexpr int SVB = DV * 2 + 16;
-  static constexpr int LDA = 64 + 4;        // FP32 64x64 matrices (floats)
+  static constexpr int SKV = SKB > SVB ? SKB : SVB;
   static constexpr int KS = DK / 32;
+  static constexpr int kTri = 2816;         // floats of the lower block triangle (rows below)
 
-  // A and T share one matrix: every block of T is written over the block of
-  // A in the same place once nothing reads that A block any more (T[b][b]
-  // after its own substitution, T[1][0] and T[3][2] from the wave that read
-  // their A blocks, the last four blocks after a barrier); V replaces T for
-  // the last product.
+  // A and T (64 x 64, FP32) keep only their blocks on or below the diagonal:
+  // row t of block row b = t / 16 holds columns 0 .. 16 b + 15, with a row
+  // stride of 16 b + 20 floats (pads keep the column and 16-byte row reads
+  // free of bank conflicts).  Every block of T is written over the block of A
+  // in the same place once nothing reads that A block any more (T[b][b] after
+  // its own substitution, T[1][0] and T[3][2] from the wave that read their A
+  // blocks, the last four blocks after a barrier).  V takes the place of K
+  // once the w product has read K.  29.4 KB at 128 x 128: five workgroups
+  // share a CU.
   struct Smem {
-    char k[kChunk * SKB];
-    union {
-      float a[kChunk * LDA];
-      float t[kChunk * LDA];
-      char v[kChunk * SVB];
-    };
+    char kv[kChunk * SKV];
+    float t[kTri];
     float gam[kChunk];
     float beta[kChunk];
     float bg[kChunk];  // beta exp(gamma)
   };
+  // first float of row t in Smem::t
+  __device__ static __forceinline__ int toff(int t) {
+    const int b = t >> 4;
+    return 128 * b * (b - 1) + 320 * b + (t & 15) * (16 * b + 20);
+  }
 
   __device__ static int find_row(const ChunkArgs& a, int chunk) {
     int lo = 0, hi = a.n_rows - 1;
@@ -77,8 +83,8 @@ struct Prepare2 {
     return lo;
   }
 
-  // The next item's K rows (and g, beta for the first wave) travel in
-  // registers while the current item computes.
+  // K rows (and g, beta for the first wave) pass through registers on their
+  // way to LDS.
   static constexpr int KV_PT = kChunk * (DK / 8) / NT;  // 16-byte K vectors per thread
   static constexpr int VV_PT = kChunk * (DV / 8) / NT;
   struct Pref {
@@ -100,15 +106,11 @@ struct Prepare2 {
                 min(kChunk, row.len - cl * kChunk)};
   }
 
-  // Items past the end get empty buffer ranges: the loads are issued all the
-  // same (so the loop's wait counts stay exact) and read nothing.
-  __device__ static void load(Pref& pf, const ChunkArgs& a, int item, int nitems) {
+  __device__ static void load(Pref& pf, const ChunkArgs& a, const Item& it) {
     const int tid = threadIdx.x;
-    const bool live = item < nitems;
-    const Item it = item_of(a, live ? item : 0);
     const int64_t H = a.H;
     const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (it.tok0 * H + it.hd) * DK;
-    const rsrc_t rk = make_rsrc(kp, live ? static_cast<uint32_t>(((it.nvalid - 1) * H + 1) * DK * 2) : 0u);
+    const rsrc_t rk = make_rsrc(kp, static_cast<uint32_t>(((it.nvalid - 1) * H + 1) * DK * 2));
     constexpr int CK = DK / 8;  // 16-byte chunks per row
 #pragma unroll
     for (int i = 0; i < KV_PT; ++i) {
@@ -117,43 +119,40 @@ struct Prepare2 {
     }
     const float* gp = a.g + it.tok0 * H + it.hd;
     const float* bp = a.beta + it.tok0 * H + it.hd;
-    const uint32_t gb = live ? static_cast<uint32_t>(((it.nvalid - 1) * H + 1) * 4) : 0u;
+    const uint32_t gb = static_cast<uint32_t>(((it.nvalid - 1) * H + 1) * 4);
     const int go = static_cast<int>((tid & 63) * H * 4);
     pf.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(gp, gb), go, 0, 0));
     pf.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(bp, gb), go, 0, 0));
   }
 
-  // Persistent: workgroup b takes items b, b + gridDim.x, ... (item = chunk * H + head).
+  // One workgroup per item (item = chunk * H + head).
   __device__ static void run(const ChunkArgs& a, Smem& sm) {
     const int nitems = a.n_chunks * a.H;
-    int item = blockIdx.x;
+    const int item = blockIdx.x;
     if (item >= nitems) return;
+    const Item it = item_of(a, item);
     Pref pf;
-    load(pf, a, item, nitems);
-    for (; item < nitems; item += gridDim.x) {
-      one(a, sm, pf, item, nitems);
-      __syncthreads();  // LDS is reused by the next item
-    }
+    load(pf, a, it);
+    one(a, sm, pf, it);
   }
 
-  __device__ static __forceinline__ void one(const ChunkArgs& a, Smem& sm, Pref& pf, int item, int nitems) {
+  __device__ static __forceinline__ void one(const ChunkArgs& a, Smem& sm, Pref& pf, const Item& it) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const Item it = item_of(a, item);
     const int hd = it.hd;
     const int64_t tok0 = it.tok0;
     const int nvalid = it.nvalid;
     const int64_t H = a.H;
 
-    // ---- K rows (zero past the tail), gamma, beta from the prefetch; the next item's loads go out ----
+    // ---- K rows (zero past the tail), gamma and beta, from the loads issued at entry ----
     constexpr int CV = DV / 8;
     {
       constexpr int CK = DK / 8;
 #pragma unroll
       for (int i = 0; i < KV_PT; ++i) {
         const int vv = tid + i * NT, r = vv / CK, c = vv % CK;
-        *reinterpret_cast<u32x4_t*>(sm.k + r * SKB + c * 16) = pf.k[i];
+        *reinterpret_cast<u32x4_t*>(sm.kv + r * SKB + c * 16) = pf.k[i];
       }
       if (wave == 0) {
         float x = (lane < nvalid) ? pf.g : 0.f;
@@ -168,16 +167,18 @@ struct Prepare2 {
         sm.bg[lane] = b * exp_fast(x);
         if (lane < nvalid) a.g_cum[(tok0 + lane) * H + hd] = x;
       }
-      load(pf, a, item + gridDim.x, nitems);
     }
     __syncthreads();
 
     // ---- Gram matrix row tile `wave`; A = beta_t e^{gamma_t - gamma_i} G (i < t) ----
+    // the wave's diagonal block of A stays in registers too: lane (c16, g4)
+    // holds rows 4 g4 + r of column c16, the layout of the MFMA accumulator
+    float diag[4] = {0.f, 0.f, 0.f, 0.f};
     {
       f32x4_t acc[4];
 #pragma unroll
       for (int tj = 0; tj < 4; ++tj) acc[tj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const char* kr = sm.k + c16 * SKB + (g4 >> 1) * 16 + (g4 & 1) * 8;
+      const char* kr = sm.kv + c16 * SKB + (g4 >> 1) * 16 + (g4 & 1) * 8;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const frag fa = S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(kr + 16 * wave * SKB + 64 * s),
@@ -191,40 +192,58 @@ struct Prepare2 {
           }
         }
       }
+      // Every LDS read is issued before any exponent: the (i < t) mask is a
+      // select on values already in registers, not a branch around each
+      // read.  e^{gamma_t - gamma_i} may overflow where i > t; the select
+      // drops it.  Blocks above the diagonal (tj > wave) are not stored.
+      const int t0 = 16 * wave + 4 * g4;
+      const f32x4_t gt = *reinterpret_cast<const f32x4_t*>(&sm.gam[t0]);
+      const f32x4_t bt = *reinterpret_cast<const f32x4_t*>(&sm.beta[t0]);
+      float gi[4];
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj) gi[tj] = sm.gam[16 * tj + c16];
 #pragma unroll
       for (int tj = 0; tj < 4; ++tj) {
         const int i = 16 * tj + c16;
-        const float gi = sm.gam[i];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = 16 * wave + 4 * g4 + r;
-          sm.a[t * LDA + i] = (i < t) ? sm.beta[t] * exp_fast(sm.gam[t] - gi) * acc[tj][r] : 0.f;
+          const int t = t0 + r;
+          if (tj <= wave) {
+            const float full = bt[r] * exp_fast(gt[r] - gi[tj]) * acc[tj][r];
+            const float val = (i < t) ? full : 0.f;
+            sm.t[toff(t) + i] = val;
+            diag[r] = (tj == wave) ? val : diag[r];
+          }
         }
       }
     }
-    __syncthreads();
 
-    // ---- diagonal blocks: T[b][b] = (I + A[b][b])^-1, wave b, lane j = column ----
-    if (lane < 16) {
-      const int b0 = 16 * wave, j = lane;
+    // ---- diagonal blocks: T[b][b] = (I + A[b][b])^-1 by forward substitution, wave b ----
+    // Lane j (of each group of 16) solves column j.  The entries of A[b][b]
+    // come from the wave's own registers (v_readlane of the lane holding
+    // each), so the dependent chain has no LDS round trip.  Right-looking:
+    // once x[i] is final every later row takes its term, so row r still
+    // subtracts its terms in the order i = 0, 1, ...  T[b][b] is written over
+    // A[b][b], which nothing reads from LDS.
+    {
+      const int b0 = 16 * wave, j = c16;
       float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = (r == j) ? 1.f : 0.f;
-        const float* ar = &sm.a[(b0 + r) * LDA + b0];
+      for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
 #pragma unroll
-        for (int i = 0; i < r; ++i) s -= ar[i] * x[i];
-        x[r] = s;
+      for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int r = i + 1; r < 16; ++r) {
+          const int src = __builtin_amdgcn_readlane(__builtin_bit_cast(int, diag[r & 3]), 16 * (r >> 2) + i);
+          x[r] -= __builtin_bit_cast(float, src) * x[i];
+        }
       }
+      if (lane < 16) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sm.t[(b0 + r) * LDA + b0 + j] = x[r];
+        for (int r = 0; r < 16; ++r) sm.t[toff(b0 + r) + b0 + j] = x[r];
+      }
     }
-    // strictly-upper blocks of T are zero
-    for (int e = tid; e < kChunk * kChunk; e += NT) {
-      const int r = e >> 6, c = e & 63;
-      if ((c >> 4) > (r >> 4)) sm.t[r * LDA + c] = 0.f;
-    }
-    // V rows for the last product (zero past the tail): in flight during the off-diagonal blocks
+    // V rows for the last product (zero past the tail): in flight during the off-diagonal blocks and w
     u32x4_t vcur[VV_PT];
     {
       const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + hd) * DV;
@@ -239,24 +258,24 @@ struct Prepare2 {
 
     // FP32 operand reads for mm16: row-major rows (a) and C-layout columns (b)
     auto a_rows = [&](const float* m, int r0, int c0) {  // X[c16][4 g4 + r] of the block at (r0, c0)
-      return *reinterpret_cast<const f32x4_t*>(m + (r0 + c16) * LDA + c0 + 4 * g4);
+      return *reinterpret_cast<const f32x4_t*>(m + toff(r0 + c16) + c0 + 4 * g4);
     };
     auto b_cols = [&](const float* m, int r0, int c0) {  // Y[4 g4 + r][c16]
       f32x4_t y;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) y[r] = m[(r0 + 4 * g4 + r) * LDA + c0 + c16];
+      for (int r = 0; r < 4; ++r) y[r] = m[toff(r0 + 4 * g4 + r) + c0 + c16];
       return y;
     };
     auto store_c = [&](float* m, int r0, int c0, const f32x4_t& d) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) m[(r0 + 4 * g4 + r) * LDA + c0 + c16] = d[r];
+      for (int r = 0; r < 4; ++r) m[toff(r0 + 4 * g4 + r) + c0 + c16] = d[r];
     };
 
     // ---- T[1][0] (wave 0) and T[3][2] (wave 1) ----
     if (wave < 2) {
       const int p = 32 * wave;  // block (p+16, p)
       f32x4_t y{0.f, 0.f, 0.f, 0.f}, x{0.f, 0.f, 0.f, 0.f};
-      mm16(y, a_rows(sm.a, p + 16, p), b_cols(sm.t, p, p));      // A[1][0] T[0][0]
+      mm16(y, a_rows(sm.t, p + 16, p), b_cols(sm.t, p, p));      // A[1][0] T[0][0]
       mm16(x, a_rows(sm.t, p + 16, p + 16), y);                  // T[1][1] (.)
       store_c(sm.t, p + 16, p, -x);
     }
@@ -270,8 +289,8 @@ struct Prepare2 {
       for (int k = 0; k < 2; ++k) {
         if (k >= j) {  // T[0][1] is zero
           const f32x4_t tb = b_cols(sm.t, 16 * k, 16 * j);
-          mm16(y0, a_rows(sm.a, 32, 16 * k), tb);
-          mm16(y1, a_rows(sm.a, 48, 16 * k), tb);
+          mm16(y0, a_rows(sm.t, 32, 16 * k), tb);
+          mm16(y1, a_rows(sm.t, 48, 16 * k), tb);
         }
       }
       __syncthreads();  // every wave has read A[2:4][0:2] before any T block replaces it
@@ -284,15 +303,20 @@ struct Prepare2 {
 
     // ---- w^T = K^T T'^T and u^T = V^T T''^T; wave = token tile of the output ----
     const int t = 16 * wave + c16;
-    // this lane's operand fragments of row t of T diag(coef), split into bf16 hi + lo
+    const int nsteps = (16 * wave + 15) / 32 + 1;  // T is lower triangular
+    // this lane's operand fragments of row t of T diag(coef), split into bf16
+    // hi + lo; column blocks past the diagonal (not stored) are zero
     auto row_frags = [&](const float* coef, frag (&hi)[2], frag (&lo)[2]) {
+      const float* tr = &sm.t[toff(t)];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
+        if (s >= nsteps) continue;
         const int i0 = 32 * s + 4 * g4;
-        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(&sm.t[t * LDA + i0]) *
-                           *reinterpret_cast<const f32x4_t*>(&coef[i0]);
-        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(&sm.t[t * LDA + i0 + 16]) *
-                           *reinterpret_cast<const f32x4_t*>(&coef[i0 + 16]);
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(&tr[i0]) * *reinterpret_cast<const f32x4_t*>(&coef[i0]);
+        const f32x4_t x1 = (2 * s + 1 <= wave)
+                               ? *reinterpret_cast<const f32x4_t*>(&tr[i0 + 16]) *
+                                     *reinterpret_cast<const f32x4_t*>(&coef[i0 + 16])
+                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
         hi[s] = S::frag_from_f32(x0, x1);
         f32x4_t l0, l1;
 #pragma unroll
@@ -303,7 +327,6 @@ struct Prepare2 {
         lo[s] = S::frag_from_f32(l0, l1);
       }
     };
-    const int nsteps = (16 * wave + 15) / 32 + 1;  // T is lower triangular
     // A operand K^T[d][i] / V^T[d][i] via transpose reads of the row-major tiles
     const int tr_row = 4 * g4 + (c16 >> 2);
     const int tr_col = 8 * (c16 & 3);
@@ -329,23 +352,25 @@ struct Prepare2 {
     {
       frag hi[2], lo[2];
       row_frags(sm.bg, hi, lo);  // T diag(beta e^gamma)
-      product(sm.k, SKB, DK, hi, lo, a.w);
+      product(sm.kv, SKB, DK, hi, lo, a.w);
     }
-    frag uh[2], ul[2];
-    row_frags(sm.beta, uh, ul);  // T diag(beta)
-    __syncthreads();  // every wave holds its rows of T diag(beta): V replaces T
+    __syncthreads();  // every wave is done with K: V replaces it
 #pragma unroll
     for (int i = 0; i < VV_PT; ++i) {
       const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
-      *reinterpret_cast<u32x4_t*>(sm.v + r * SVB + c * 16) = vcur[i];
+      *reinterpret_cast<u32x4_t*>(sm.kv + r * SVB + c * 16) = vcur[i];
     }
     __syncthreads();
-    product(sm.v, SVB, DV, uh, ul, a.u);
+    {
+      frag hi[2], lo[2];
+      row_frags(sm.beta, hi, lo);  // T diag(beta)
+      product(sm.kv, SVB, DV, hi, lo, a.u);
+    }
   }
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void prepare2_kernel(const ChunkArgs a) {
+__global__ __launch_bounds__(256) void prepare2_kernel(const ChunkArgs a) {
   using K = Prepare2<DK, DV>;
   __shared__ __align__(16) typename K::Smem sm;
   K::run(a, sm);
