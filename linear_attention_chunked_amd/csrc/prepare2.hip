@@ -171,9 +171,6 @@ struct Prepare2 {
     __syncthreads();
 
     // ---- Gram matrix row tile `wave`; A = beta_t e^{gamma_t - gamma_i} G (i < t) ----
-    // the wave's diagonal block of A stays in registers too: lane (c16, g4)
-    // holds rows 4 g4 + r of column c16, the layout of the MFMA accumulator
-    float diag[4] = {0.f, 0.f, 0.f, 0.f};
     {
       f32x4_t acc[4];
 #pragma unroll
@@ -212,36 +209,50 @@ struct Prepare2 {
             const float full = bt[r] * exp_fast(gt[r] - gi[tj]) * acc[tj][r];
             const float val = (i < t) ? full : 0.f;
             sm.t[toff(t) + i] = val;
-            diag[r] = (tj == wave) ? val : diag[r];
           }
         }
       }
     }
 
     // ---- diagonal blocks: T[b][b] = (I + A[b][b])^-1 by forward substitution, wave b ----
-    // Lane j (of each group of 16) solves column j.  The entries of A[b][b]
-    // come from the wave's own registers (v_readlane of the lane holding
-    // each), so the dependent chain has no LDS round trip.  Right-looking:
-    // once x[i] is final every later row takes its term, so row r still
-    // subtracts its terms in the order i = 0, 1, ...  T[b][b] is written over
-    // A[b][b], which nothing reads from LDS.
+    // Lane (j, g) solves rows 4 g .. 4 g + 3 of column j, by blocks of four
+    // rows: the lanes owning block q finish its rows, ds_bpermute hands the
+    // four values to every lane of the same column, and the lanes of later
+    // blocks subtract their terms.  Row r still subtracts its terms in the
+    // order i = 0, 1, ...  The entries of A are 16-byte LDS reads of the
+    // wave's own rows, off the dependent chain.  T[b][b] is written over
+    // A[b][b] (both in the wave's own rows: no barrier).
     {
-      const int b0 = 16 * wave, j = c16;
-      float x[16];
+      const int b0 = 16 * wave, j = c16, g = g4;
+      float xr[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+      for (int rr = 0; rr < 4; ++rr) xr[rr] = (4 * g + rr == j) ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int q = 0; q < 4; ++q) {
+        f32x4_t R[4];  // R[rr][ii] = A[b][b][4 g + rr][4 q + ii]
 #pragma unroll
-        for (int r = i + 1; r < 16; ++r) {
-          const int src = __builtin_amdgcn_readlane(__builtin_bit_cast(int, diag[r & 3]), 16 * (r >> 2) + i);
-          x[r] -= __builtin_bit_cast(float, src) * x[i];
+        for (int rr = 0; rr < 4; ++rr)
+          R[rr] = *reinterpret_cast<const f32x4_t*>(&sm.t[toff(b0 + 4 * g + rr) + b0 + 4 * q]);
+        if (g == q) {
+#pragma unroll
+          for (int rr = 1; rr < 4; ++rr)
+#pragma unroll
+            for (int ii = 0; ii < rr; ++ii) xr[rr] -= R[rr][ii] * xr[ii];
+        }
+        if (q < 3) {
+          float xq[4];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) xq[ii] = __shfl(xr[ii], j + 16 * q, 64);
+          if (g > q) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+              for (int ii = 0; ii < 4; ++ii) xr[rr] -= R[rr][ii] * xq[ii];
+          }
         }
       }
-      if (lane < 16) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sm.t[toff(b0 + r) + b0 + j] = x[r];
-      }
+      for (int rr = 0; rr < 4; ++rr) sm.t[toff(b0 + 4 * g + rr) + b0 + j] = xr[rr];
     }
     // V rows for the last product (zero past the tail): in flight during the off-diagonal blocks and w
     u32x4_t vcur[VV_PT];
