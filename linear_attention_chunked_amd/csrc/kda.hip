@@ -107,16 +107,18 @@ template <int DK, int DV>
 struct KdaPrepare {
   using S = St<bf16_t>;
   using frag = S::frag;
-  static constexpr int NT = 256;
+  static constexpr int NT = 512;            // 8 waves
   static constexpr int SKB = DK * 2 + 16;   // bf16 rows (bytes)
   static constexpr int SVB = DV * 2 + 16;
   static constexpr int GS = DK + 4;         // FP32 Gam rows (floats), padded
-  static constexpr int LDA = 64 + 4;
+  static constexpr int kTri = 2816;         // floats of the lower block triangle of A / T
 
-  // Regions reused once their first contents are dead, so that two
-  // workgroups share a CU (about 70 KB): K then V (V waits in registers until
-  // the decayed products no longer read K); Gam then the bf16 hi / lo parts
-  // of K e^{Gam}; A then T.
+  // Regions reused once their first contents are dead, so that two 8-wave
+  // workgroups share a CU (about 66 KB at 128 x 128): K then V (V waits in
+  // registers until the decayed products no longer read K); Gam then the
+  // bf16 hi / lo parts of K e^{Gam}; A then T.  A and T keep only their
+  // blocks on or below the diagonal: row t of block row b = t / 16 holds
+  // columns 0 .. 16 b + 15 with a row stride of 16 b + 20 floats.
   static constexpr int RKV = (SKB > SVB ? SKB : SVB) * kChunk;
   static constexpr int RG = (GS * 4 > 2 * SKB ? GS * 4 : 2 * SKB) * kChunk;
   struct Smem {
@@ -128,12 +130,15 @@ struct KdaPrepare {
       float gam[RG / 4];
       char ke[RG];              // ke_hi rows [0, 64), ke_lo rows [64, 128), stride SKB
     };
-    union {
-      float a[kChunk * LDA];
-      float t[kChunk * LDA];
-    };
+    float t[kTri];              // A, then T
     float beta[kChunk];
+    float part[3][DK];          // per-channel sums of the first three 16-token quarters
   };
+  // first float of row t in Smem::t
+  __device__ static __forceinline__ int toff(int t) {
+    const int b = t >> 4;
+    return 128 * b * (b - 1) + 320 * b + (t & 15) * (16 * b + 20);
+  }
 
   __device__ static void run(const KdaArgs& a, Smem& sm) {
     const int tid = threadIdx.x;
@@ -187,40 +192,60 @@ struct KdaPrepare {
     __syncthreads();
 
     // ---- Gam: inclusive cumulative sum over the chunk's tokens, per channel
-    //      (rows past the tail add zero, so they repeat the last value) ----
-    if (tid < DK) {  // the 64 reads are independent; only the adds form a chain
-      float gv[kChunk];
+    //      (rows past the tail add zero, so they repeat the last value):
+    //      thread (quarter, channel) sums its 16 tokens, then adds the sums of
+    //      the quarters before it ----
+    {
+      constexpr int QL = kChunk / 4;
+      const int gd = tid % DK, gq = tid / DK;
+      float gv[QL];
+      if (gq < 4) {
 #pragma unroll
-      for (int t = 0; t < kChunk; ++t) gv[t] = sm.gam[t * GS + tid];
-      float x = 0.f;
+        for (int t = 0; t < QL; ++t) gv[t] = sm.gam[(QL * gq + t) * GS + gd];
+        float x = 0.f;
 #pragma unroll
-      for (int t = 0; t < kChunk; ++t) {
-        x += gv[t];
-        gv[t] = x;
+        for (int t = 0; t < QL; ++t) {
+          x += gv[t];
+          gv[t] = x;
+        }
+        if (gq < 3) sm.part[gq][gd] = x;
       }
-      float* go = a.g_cum + (tok0 * H + hd) * DK;
-      const rsrc_t rgo = make_rsrc(go, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 4));
+      __syncthreads();
+      if (gq < 4) {
+        float off = 0.f;
 #pragma unroll
-      for (int t = 0; t < kChunk; ++t) {
-        sm.gam[t * GS + tid] = gv[t];
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gv[t]), rgo,
-                                              static_cast<int>((t * H * DK + tid) * 4), 0, 0);
+        for (int p = 0; p < 3; ++p)
+          if (p < gq) off += sm.part[p][gd];
+        float* go = a.g_cum + (tok0 * H + hd) * DK;
+        const rsrc_t rgo = make_rsrc(go, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 4));
+#pragma unroll
+        for (int t = 0; t < QL; ++t) {
+          const float x = off + gv[t];
+          const int row = QL * gq + t;
+          sm.gam[row * GS + gd] = x;
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rgo,
+                                                static_cast<int>((row * H * DK + gd) * 4), 0, 0);
+        }
+        if (gq == 3) a.decay[((static_cast<int64_t>(a.chunk_base) + chunk) * H + hd) * DK + gd] = exp_fast(off + gv[QL - 1]);
       }
-      a.decay[((static_cast<int64_t>(a.chunk_base) + chunk) * H + hd) * DK + tid] = exp_fast(x);
     }
     __syncthreads();
 
-    // ---- A rows of block `wave`: b_t sum_d k_td k_id e^{Gam_td - Gam_id}, i < t ----
+    // ---- A rows of block I = wave % 4: b_t sum_d k_td k_id e^{Gam_td - Gam_id}, i < t;
+    //      the column blocks J <= I are split between waves I and I + 4 ----
     {
-      float xs[DK / 4];
-      kda_row_side<DK, SKB, GS>(xs, sm.k, sm.gam, wave, g4, c16);
-      for (int J = 0; J <= wave; ++J) {
-        const f32x4_t d = kda_block_product<DK, SKB, GS>(xs, sm.k, sm.gam, wave, J, g4, c16);
-        const int i = 16 * J + c16;
+      const int I = wave & 3, nj = I + 1;
+      const int j0 = (wave >> 2) ? (nj + 1) / 2 : 0, j1 = (wave >> 2) ? nj : (nj + 1) / 2;
+      if (j0 < j1) {
+        float xs[DK / 4];
+        kda_row_side<DK, SKB, GS>(xs, sm.k, sm.gam, I, g4, c16);
+        const int t0 = 16 * I + 4 * g4;
+        const f32x4_t bt = *reinterpret_cast<const f32x4_t*>(&sm.beta[t0]);
+        for (int J = j0; J < j1; ++J) {
+          const f32x4_t d = kda_block_product<DK, SKB, GS>(xs, sm.k, sm.gam, I, J, g4, c16);
+          const int i = 16 * J + c16;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * wave + 4 * g4 + r;
-          sm.a[t * LDA + i] = (i < t) ? sm.beta[t] * d[r] : 0.f;
+          for (int r = 0; r < 4; ++r) sm.t[toff(t0 + r) + i] = (i < t0 + r) ? bt[r] * d[r] : 0.f;
         }
       }
     }
@@ -273,75 +298,103 @@ struct KdaPrepare {
       }
     }
 
-    // ---- T = (I + A)^-1 by 16-blocks: diagonal blocks by forward substitution,
-    //      off-diagonal blocks as FP32 products (A and T share one matrix) ----
-    if (lane < 16) {
-      const int b0 = 16 * wave, j = lane;
-      float x[16];
+    // ---- T = (I + A)^-1 by 16-blocks: diagonal blocks by forward substitution
+    //      (wave b < 4; lane (j, g) solves rows 4 g .. 4 g + 3 of column j by
+    //      blocks of four rows, each finished block handed to the later lanes
+    //      of its column by ds_bpermute, so row r still subtracts its terms in
+    //      the order i = 0, 1, ...), off-diagonal blocks as FP32 products
+    //      (A and T share one matrix) ----
+    if (wave < 4) {
+      const int b0 = 16 * wave, j = c16, g = g4;
+      float xr[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = (r == j) ? 1.f : 0.f;
-        const float* ar = &sm.a[(b0 + r) * LDA + b0];
+      for (int rr = 0; rr < 4; ++rr) xr[rr] = (4 * g + rr == j) ? 1.f : 0.f;
 #pragma unroll
-        for (int i = 0; i < r; ++i) s -= ar[i] * x[i];
-        x[r] = s;
+      for (int q = 0; q < 4; ++q) {
+        f32x4_t R[4];  // R[rr][ii] = A[b][b][4 g + rr][4 q + ii]
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          R[rr] = *reinterpret_cast<const f32x4_t*>(&sm.t[toff(b0 + 4 * g + rr) + b0 + 4 * q]);
+        if (g == q) {
+#pragma unroll
+          for (int rr = 1; rr < 4; ++rr)
+#pragma unroll
+            for (int ii = 0; ii < rr; ++ii) xr[rr] -= R[rr][ii] * xr[ii];
+        }
+        if (q < 3) {
+          float xq[4];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) xq[ii] = __shfl(xr[ii], j + 16 * q, 64);
+          if (g > q) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+              for (int ii = 0; ii < 4; ++ii) xr[rr] -= R[rr][ii] * xq[ii];
+          }
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sm.t[(b0 + r) * LDA + b0 + j] = x[r];
-    }
-    for (int e = tid; e < kChunk * kChunk; e += NT) {
-      const int r = e >> 6, c = e & 63;
-      if ((c >> 4) > (r >> 4)) sm.t[r * LDA + c] = 0.f;
+      for (int rr = 0; rr < 4; ++rr) sm.t[toff(b0 + 4 * g + rr) + b0 + j] = xr[rr];
     }
     __syncthreads();
     auto a_rows = [&](const float* m, int r0, int c0) {
-      return *reinterpret_cast<const f32x4_t*>(m + (r0 + c16) * LDA + c0 + 4 * g4);
+      return *reinterpret_cast<const f32x4_t*>(m + toff(r0 + c16) + c0 + 4 * g4);
     };
     auto b_cols = [&](const float* m, int r0, int c0) {
       f32x4_t y;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) y[r] = m[(r0 + 4 * g4 + r) * LDA + c0 + c16];
+      for (int r = 0; r < 4; ++r) y[r] = m[toff(r0 + 4 * g4 + r) + c0 + c16];
       return y;
     };
     auto store_c = [&](float* m, int r0, int c0, const f32x4_t& d) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) m[(r0 + 4 * g4 + r) * LDA + c0 + c16] = d[r];
+      for (int r = 0; r < 4; ++r) m[toff(r0 + 4 * g4 + r) + c0 + c16] = d[r];
     };
     if (wave < 2) {
       const int p = 32 * wave;
       f32x4_t y{0.f, 0.f, 0.f, 0.f}, x{0.f, 0.f, 0.f, 0.f};
-      mm16f(y, a_rows(sm.a, p + 16, p), b_cols(sm.t, p, p));
+      mm16f(y, a_rows(sm.t, p + 16, p), b_cols(sm.t, p, p));
       mm16f(x, a_rows(sm.t, p + 16, p + 16), y);
       store_c(sm.t, p + 16, p, -x);
     }
     __syncthreads();
     {
-      const int i = wave >> 1, j = wave & 1;
+      const int i = (wave >> 1) & 1, j = wave & 1;  // waves 0 .. 3
       f32x4_t y0{0.f, 0.f, 0.f, 0.f}, y1{0.f, 0.f, 0.f, 0.f};
+      if (wave < 4) {
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        if (k >= j) {
-          const f32x4_t tb = b_cols(sm.t, 16 * k, 16 * j);
-          mm16f(y0, a_rows(sm.a, 32, 16 * k), tb);
-          mm16f(y1, a_rows(sm.a, 48, 16 * k), tb);
+        for (int k = 0; k < 2; ++k) {
+          if (k >= j) {
+            const f32x4_t tb = b_cols(sm.t, 16 * k, 16 * j);
+            mm16f(y0, a_rows(sm.t, 32, 16 * k), tb);
+            mm16f(y1, a_rows(sm.t, 48, 16 * k), tb);
+          }
         }
       }
-      __syncthreads();
-      f32x4_t x{0.f, 0.f, 0.f, 0.f};
-      mm16f(x, a_rows(sm.t, 32 + 16 * i, 32), y0);
-      if (i == 1) mm16f(x, a_rows(sm.t, 48, 48), y1);
-      store_c(sm.t, 32 + 16 * i, 16 * j, -x);
+      __syncthreads();  // every wave has read A[2:4][0:2] before any T block replaces it
+      if (wave < 4) {
+        f32x4_t x{0.f, 0.f, 0.f, 0.f};
+        mm16f(x, a_rows(sm.t, 32 + 16 * i, 32), y0);
+        if (i == 1) mm16f(x, a_rows(sm.t, 48, 48), y1);
+        store_c(sm.t, 32 + 16 * i, 16 * j, -x);
+      }
     }
     __syncthreads();
 
-    // ---- w^T = (K e^Gam)^T (T diag(b))^T, u^T = V^T (T diag(b))^T; wave = token tile ----
-    const int t = 16 * wave + c16;
+    // ---- w^T = (K e^Gam)^T (T diag(b))^T, u^T = V^T (T diag(b))^T; wave = (token tile,
+    //      half of the columns) ----
+    const int tt = wave & 3, half = wave >> 2;
+    const int t = 16 * tt + c16;
+    const int nsteps = (16 * tt + 15) / 32 + 1;  // T is lower triangular
     frag bb_hi[2], bb_lo[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
+      if (s >= nsteps) continue;
       const int i0 = 32 * s + 4 * g4;
-      const f32x4_t t0 = *reinterpret_cast<const f32x4_t*>(&sm.t[t * LDA + i0]);
-      const f32x4_t t1 = *reinterpret_cast<const f32x4_t*>(&sm.t[t * LDA + i0 + 16]);
+      const float* tr = &sm.t[toff(t)];
+      const f32x4_t t0 = *reinterpret_cast<const f32x4_t*>(&tr[i0]);
+      const f32x4_t t1 = (2 * s + 1 <= tt) ? *reinterpret_cast<const f32x4_t*>(&tr[i0 + 16])
+                                           : f32x4_t{0.f, 0.f, 0.f, 0.f};  // blocks past the diagonal
       const f32x4_t be0 = *reinterpret_cast<const f32x4_t*>(&sm.beta[i0]);
       const f32x4_t be1 = *reinterpret_cast<const f32x4_t*>(&sm.beta[i0 + 16]);
       const f32x4_t u0 = t0 * be0, u1 = t1 * be1;
@@ -354,7 +407,6 @@ struct KdaPrepare {
       }
       bb_lo[s] = S::frag_from_f32(l0, l1);
     }
-    const int nsteps = (16 * wave + 15) / 32 + 1;  // T is lower triangular
     const int tr_row = 4 * g4 + (c16 >> 2);
     const int tr_col = 8 * (c16 & 3);
     uint16_t* wo = static_cast<uint16_t*>(a.w) + (tok0 * H + hd) * DK;
@@ -362,7 +414,8 @@ struct KdaPrepare {
     const rsrc_t rwo = make_rsrc(wo, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
     const rsrc_t ruo = make_rsrc(uo, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
 #pragma unroll
-    for (int dt = 0; dt < DK / 16; ++dt) {
+    for (int e = 0; e < DK / 32; ++e) {
+      const int dt = half * (DK / 32) + e;
       f32x4_t acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -379,7 +432,8 @@ struct KdaPrepare {
                                             static_cast<int>(t * H * DK * 2 + (16 * dt + 4 * g4) * 2), 0, 0);
     }
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) {
+    for (int e = 0; e < DV / 32; ++e) {
+      const int dt = half * (DV / 32) + e;
       f32x4_t acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -602,7 +656,7 @@ struct KdaOutput {
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void kda_prepare_kernel(const KdaArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void kda_prepare_kernel(const KdaArgs a) {
   using K = KdaPrepare<DK, DV>;
   __shared__ __align__(16) typename K::Smem sm;
   K::run(a, sm);
@@ -617,7 +671,8 @@ __global__ __launch_bounds__(256) void kda_output_kernel(const KdaArgs a) {
 
 template <int DK, int DV>
 static hipError_t launch_kda_prepare(const void* args, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((kda_prepare_kernel<DK, DV>), dim3(grid), dim3(256), 0, stream, *static_cast<const KdaArgs*>(args));
+  hipLaunchKernelGGL((kda_prepare_kernel<DK, DV>), dim3(grid), dim3(KdaPrepare<DK, DV>::NT), 0, stream,
+                     *static_cast<const KdaArgs*>(args));
   return hipGetLastError();
 }
 

@@ -126,8 +126,7 @@ struct AbcArgs {
 };
 
 // Per-key-channel decay: chunk preparation and chunk output (one workgroup
-// per (chunk, head), resp. (chunk, head, 64 value columns); rows as in
-// ChunkArgs).
+// per (chunk, head) each; rows as in ChunkArgs).
 struct KdaArgs {
   const void* q;
   const void* k;
