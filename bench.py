@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+EV_EVERY = 8
 BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -53,6 +54,24 @@ def scan_alg_bytes(lengths, H, DK, DV, in_bytes, h_bytes, has_h0, has_hT):
 def scan_flops(lengths, H, DK, DV):
     """4 DK DV per token-head: W S (2 DK DV) and K^T D' (2 DK DV)."""
     return 4 * DK * DV * sum(lengths) * H
+
+
+def fused_alg_bytes(lengths, H, DK, DV, in_bytes, h_bytes, has_h0, has_hT):
+    """The scan's bytes plus the chunk output's own: read q (DK) and write o
+    (DV) per token-head (h, v_new, k and g_cum it takes on chip)."""
+    return (scan_alg_bytes(lengths, H, DK, DV, in_bytes, h_bytes, has_h0, has_hT)
+            + sum(lengths) * H * (DK + DV) * in_bytes)
+
+
+def fused_flops(lengths, H, DK, DV):
+    """The scan's flops plus the output's: Q S (2 DK DV per token-head) and,
+    for token j of a chunk, its j + 1 causal terms of Q K^T (2 DK each) and of
+    P v_new (2 DV each)."""
+    causal = 0
+    for L in lengths:
+        full, tail = divmod(L, 64)
+        causal += full * (64 * 65 // 2) + tail * (tail + 1) // 2
+    return scan_flops(lengths, H, DK, DV) + H * (2 * DK * DV * sum(lengths) + 2 * (DK + DV) * causal)
 
 
 def source_sha():
@@ -190,30 +209,32 @@ def main():
                  "prepare")
         if ev is not None:
             ev[0].record(stream)
-        B._check(L.gdr_state_scan(P.ref, None, None, ptr(k), ptr(w), ptr(u), ptr(g_cum), ptr(h0), ptr(h),
-                                  ptr(v_new), ptr(hT), s_ptr), "scan")
+        B._check(L.gdr_state_scan_output(P.ref, None, None, ptr(q), ptr(k), ptr(w), ptr(u), ptr(g_cum), ptr(h0),
+                                         float(inp.scale), ptr(h), ptr(v_new), ptr(hT), ptr(o), s_ptr),
+                 "scan + output")
         if ev is not None:
             ev[1].record(stream)
-        B._check(L.gdr_chunk_output(P.ref, ptr(q), ptr(k), ptr(v_new), ptr(h), ptr(g_cum), float(inp.scale),
-                                    ptr(o), s_ptr), "output")
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
+    # The roofline kernel is timed by a pair of HIP events around it on every
+    # EV_EVERY-th timed step: event records cost the stream several us each,
+    # so an event pair in every step would depress the step rate itself.
+    evs = {i: (HipEvent(), HipEvent()) for i in range(0, args.steps, EV_EVERY)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(evs.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    scan_ms = sorted(a.elapsed_ms(b) for a, b in evs)
+    scan_ms = sorted(a.elapsed_ms(b) for a, b in evs.values())
     scan_mean_ms = sum(scan_ms) / len(scan_ms)
     ms_per_step = elapsed * 1e3 / args.steps
     value = inp.token_heads / (elapsed / args.steps) / 1e6
 
     in_bytes = 2 if inp.dtype == torch.bfloat16 else 4
-    alg = scan_alg_bytes(inp.lengths, inp.H, inp.DK, DV, in_bytes, in_bytes, h0 is not None, True)
+    alg = fused_alg_bytes(inp.lengths, inp.H, inp.DK, DV, in_bytes, in_bytes, h0 is not None, True)
     achieved = alg / (scan_mean_ms * 1e-3) / 1e9
     tile = pkg.gdr_plan_query(k, DV, cu)
     roofline = {
@@ -223,18 +244,20 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": load_traffic(args.workload),
-        "kernel": f"gdr state scan (bv={tile[0]}, waves={tile[1]}, stages={tile[2]}, {tile[3]} workgroups)",
+        "kernel": f"gdr state scan with the chunk output fused (bv={tile[0]}, waves={tile[1]}, stages={tile[2]}, "
+                  f"{tile[3]} workgroups)",
         "alg_bytes_per_launch": alg,
         "launch_us_mean": round(scan_mean_ms * 1e3, 2),
         "launch_us_median": round(scan_ms[len(scan_ms) // 2] * 1e3, 2),
         "launch_us_stats": _stats_us(scan_ms),
-        "mfma_frac": round(scan_flops(inp.lengths, inp.H, inp.DK, DV) / (scan_mean_ms * 1e-3) / 1e12
+        "launch_us_sampled": f"every {EV_EVERY}th timed step ({len(scan_ms)} of {args.steps})",
+        "mfma_frac": round(fused_flops(inp.lengths, inp.H, inp.DK, DV) / (scan_mean_ms * 1e-3) / 1e12
                            / BF16_PEAK_TFLOPS, 4),
     }
 
     # Cold-cache figures (after the timed region): before every rep a 1 GiB
-    # fill evicts L2 and the 256 MB Infinity Cache (the step's 141 MB of scan
-    # traffic would otherwise partly stay resident between back-to-back steps).
+    # fill evicts L2 and the 256 MB Infinity Cache (the step's 169 MB of fused
+    # scan traffic would otherwise partly stay resident between back-to-back steps).
     if not args.no_cold:
         flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         cold_scan, cold_step = [], []
@@ -275,7 +298,7 @@ def main():
             "heads": inp.H,
             "dk": inp.DK,
             "dv": DV,
-            "step": "chunk prepare + state scan + chunk output",
+            "step": "chunk prepare + state scan with the chunk output fused",
         },
         "roofline": roofline,
     }

@@ -162,6 +162,24 @@ gdr_status gdr_chunk_output(const gdr_problem* p, const void* q, const void* k,
                             const void* v_new, const void* h, const float* g_cum, float scale,
                             void* o, void* stream);
 
+/* The state scan with the chunk output fused into it: the h, v_new and hT of
+ * gdr_state_scan and the o of gdr_chunk_output on them, bit for bit, from one
+ * pass over the chunks (the two definitions above: [kev#259] opening section
+ * for the scan; the output formula of gdr_chunk_output).  The pre-chunk state
+ * and v_new of every chunk feed the output on chip, so they are not read
+ * back from memory.  Fused for bfloat16, DK 64 or 128, DV <= 128 and the
+ * tiles (bv 64 or 128, 4 waves, 2 stages); with tile NULL the planner's tile
+ * when it is one of those, else (64, 4, 2).  There h and v_new may be NULL
+ * (not written).  Any other problem or explicit tile runs gdr_state_scan and
+ * then gdr_chunk_output, and then h and v_new must be given (else
+ * GDR_ERR_UNSUPPORTED).  q [B, T, H, DK] and o [B, T, H, DV] in the storage
+ * dtype, layouts and the other arguments as in the two calls; seg as in
+ * gdr_state_scan (the segmented final pass). */
+gdr_status gdr_state_scan_output(const gdr_problem* p, const gdr_tile* tile, const gdr_segments* seg,
+                                 const void* q, const void* k, const void* w, const void* u,
+                                 const float* g_cum, const float* h0, float scale, void* h,
+                                 void* v_new, float* hT, void* o, void* stream);
+
 /* Segment summaries, the pre-scan of [cuLA#127] ("Root cause and
  * implementation"): each sequence is split into n_segments chunk-aligned
  * segments (NT_n chunks dealt out evenly, the first NT_n mod P segments one

@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     gdr_segment_summaries,
     gdr_segment_summaries_workspace_size,
     gdr_state_scan,
+    gdr_state_scan_output,
     gdr_state_scan_bwd,
     chunk_kda,
     kda_chunk_output,

@@ -72,6 +72,9 @@ _SIGS = {
     "gdr_state_scan": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile),
                                       ctypes.POINTER(gdr_segments), _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdr_chunk_output": (ctypes.c_int, [ctypes.POINTER(gdr_problem), _P, _P, _P, _P, _P, ctypes.c_float, _P, _P]),
+    "gdr_state_scan_output": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile),
+                                             ctypes.POINTER(gdr_segments), _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                             _P, _P, _P, _P, _P]),
     "gdr_segment_summaries": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile), ctypes.c_int32,
                                              _P, _P, _P, _P, _P, _P, _P]),
     "gdr_segment_summaries_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(gdr_problem), ctypes.c_int32]),
@@ -259,6 +262,54 @@ def gdr_state_scan(k, w, u, g_cum, h0=None, cu_seqlens=None, tile=None, n_segmen
                             _ptr(k), _ptr(w), _ptr(u), _ptr(g_cum), _ptr(h0), _ptr(h), _ptr(v_new), _ptr(hT),
                             _stream(stream)), "gdr_state_scan")
     return h, v_new, hT
+
+
+def gdr_state_scan_output(q, k, w, u, g_cum, scale: float = 1.0, h0=None, cu_seqlens=None, tile=None,
+                          n_segments: Optional[int] = None, seg_init=None, state_layout: str = "kv",
+                          emit_h: bool = True, emit_v_new: bool = True, emit_final: bool = True, out=None,
+                          state_indices=None, stream=None):
+    """The state scan with the chunk output fused: returns (o, h | None, v_new | None, hT | None), the
+    same tensors as ``gdr_state_scan`` followed by ``gdr_chunk_output``.  ``out`` may hold preallocated
+    "o", "h", "v_new" and "hT"; other arguments as in ``gdr_state_scan``."""
+    DV = u.shape[-1]
+    out = out or {}
+    pool_size = 0
+    if state_indices is not None:
+        if emit_final and out.get("hT") is None:
+            raise ValueError("indexed states write into a pool: pass out={'hT': pool}")
+        pool = h0 if h0 is not None else out.get("hT")
+        pool_size = int(pool.shape[0]) if pool is not None else 0
+    p = Problem(k, DV, cu_seqlens, state_layout, state_indices, pool_size)
+    nt = gdr_num_chunks(k, DV, cu_seqlens)
+    o = out.get("o")
+    if o is None:
+        o = torch.empty_like(u)
+    h = v_new = hT = None
+    if emit_h:
+        h = out.get("h")
+        if h is None:
+            h = torch.empty((nt, p.H, DV, p.DK), dtype=k.dtype, device=k.device)
+    if emit_v_new:
+        v_new = out.get("v_new")
+        if v_new is None:
+            v_new = torch.empty_like(u)
+    if emit_final:
+        hT = out.get("hT")
+        if hT is None:
+            shape = (p.N, p.H, DV, p.DK) if state_layout == "vk" else (p.N, p.H, p.DK, DV)
+            hT = torch.empty(shape, dtype=torch.float32, device=k.device)
+    t = _tile(tile)
+    seg = None
+    if n_segments is not None:
+        if seg_init is None or not seg_init.is_cuda:
+            raise ValueError("the segmented pass needs seg_init on the GPU")
+        seg = gdr_segments(n_segments, seg_init.data_ptr())
+    _check(lib().gdr_state_scan_output(p.ref, ctypes.byref(t) if t is not None else None,
+                                       ctypes.byref(seg) if seg is not None else None,
+                                       _ptr(q), _ptr(k), _ptr(w), _ptr(u), _ptr(g_cum), _ptr(h0), float(scale),
+                                       _ptr(h), _ptr(v_new), _ptr(hT), _ptr(o), _stream(stream)),
+           "gdr_state_scan_output")
+    return o, h, v_new, hT
 
 
 def gdr_chunk_output(q, k, v_new, h, g_cum, scale: float = 1.0, cu_seqlens=None, stream=None) -> torch.Tensor:
@@ -482,18 +533,19 @@ def gdr_state_scan_bwd(q, k, w, g_cum, dO, dv_local, dhT=None, scale: float = 1.
 def chunk_gated_delta_rule(q, k, v, g, beta, h0=None, cu_seqlens=None, scale: float = 1.0,
                            n_segments: Optional[int] = None, tile=None, stream=None) -> dict:
     """The whole forward path: prepare -> scan (serial, or summaries + compose +
-    segmented pass when n_segments is given) -> output.  Returns a dict with
-    o, h, v_new, hT, g_cum, w, u (and seg_state, seg_trans, seg_init)."""
+    segmented pass when n_segments is given) with the chunk output fused into
+    the scan where a fused kernel exists (else scan, then output).  Returns a
+    dict with o, h, v_new, hT, g_cum, w, u (and seg_state, seg_trans, seg_init)."""
     g_cum, w, u = gdr_chunk_prepare(k, v, g, beta, cu_seqlens, stream)
     out = {"g_cum": g_cum, "w": w, "u": u}
     if n_segments is None:
-        h, v_new, hT = gdr_state_scan(k, w, u, g_cum, h0, cu_seqlens, tile, stream=stream)
+        o, h, v_new, hT = gdr_state_scan_output(q, k, w, u, g_cum, scale, h0, cu_seqlens, tile, stream=stream)
     else:
         seg_state, seg_trans = gdr_segment_summaries(k, w, u, g_cum, n_segments, cu_seqlens, tile, stream)
         seg_init, _ = gdr_segment_compose(k, v.shape[-1], seg_state, seg_trans, n_segments, h0, cu_seqlens,
                                           stream=stream)
-        h, v_new, hT = gdr_state_scan(k, w, u, g_cum, None, cu_seqlens, tile, n_segments, seg_init, stream=stream)
+        o, h, v_new, hT = gdr_state_scan_output(q, k, w, u, g_cum, scale, None, cu_seqlens, tile, n_segments,
+                                                seg_init, stream=stream)
         out.update(seg_state=seg_state, seg_trans=seg_trans, seg_init=seg_init)
-    o = gdr_chunk_output(q, k, v_new, h, g_cum, scale, cu_seqlens, stream)
     out.update(o=o, h=h, v_new=v_new, hT=hT)
     return out

@@ -72,13 +72,27 @@ gdr_status hip_fail(hipError_t e, const char* what) {
   return fail(GDR_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// The chunk output fused into the plain pass (queries, output, scale).
+struct FusedOut {
+  const void* q;
+  void* o;
+  float scale;
+};
+
+// The plain pass has the chunk output fused for bfloat16 with DK 64 or 128
+// and the scalar gate on the one-buffer four-wave tiles.
+bool fusable(const gdr::Problem& pr, const gdr::Tile& t) {
+  return pr.dtype == GDR_BF16 && pr.DV <= 128 && gdr::find_scan2_fused(pr.DK, t.bv, t.waves, t.stages) != nullptr;
+}
+
 gdr_status run_scan(const gdr::Problem& pr, const gdr::Tile& t, int mode, int P, const void* k, const void* w,
                     const void* u, const float* g_cum, const float* h_in, int in_vk, void* h, void* v_new,
                     float* h_out, int out_vk, float* trans_out, hipStream_t stream, const float* decay = nullptr,
-                    int split = 1) {
+                    int split = 1, const FusedOut* fo = nullptr) {
   const int kmode = (mode == 1) ? gdr::summary_kernel_mode(pr) : 0;
-  gdr::LaunchFn fn = decay != nullptr ? gdr::find_scan2(pr.DK, t.bv, t.waves, t.stages, kmode, true)
-                                      : gdr::find_scan(pr.dtype, pr.DK, t.bv, t.waves, t.stages, kmode);
+  gdr::LaunchFn fn = fo != nullptr      ? gdr::find_scan2_fused(pr.DK, t.bv, t.waves, t.stages)
+                     : decay != nullptr ? gdr::find_scan2(pr.DK, t.bv, t.waves, t.stages, kmode, true)
+                                        : gdr::find_scan(pr.dtype, pr.DK, t.bv, t.waves, t.stages, kmode);
   if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no scan kernel for this dtype/DK/tile");
   const bool has_in = (h_in != nullptr);
   const bool has_out = (h_out != nullptr);
@@ -95,6 +109,11 @@ gdr_status run_scan(const gdr::Problem& pr, const gdr::Tile& t, int mode, int P,
   a.h_out = h_out;
   a.trans_out = trans_out;
   a.decay = decay;
+  if (fo != nullptr) {
+    a.q = fo->q;
+    a.o = fo->o;
+    a.scale = fo->scale;
+  }
   a.H = pr.H;
   a.DV = pr.DV;
   a.in_vk = in_vk;
@@ -201,6 +220,54 @@ gdr_status gdr_state_scan(const gdr_problem* p, const gdr_tile* tile, const gdr_
   GDR_TRY(tile_for(pr, tile, 0, static_cast<int64_t>(pr.N) * P, t));
   return run_scan(pr, t, mode, P, k, w, u, g_cum, h_in, in_vk, h, v_new, hT, pr.state_vk, nullptr,
                   static_cast<hipStream_t>(stream));
+}
+
+gdr_status gdr_state_scan_output(const gdr_problem* p, const gdr_tile* tile, const gdr_segments* seg, const void* q,
+                                 const void* k, const void* w, const void* u, const float* g_cum, const float* h0,
+                                 float scale, void* h, void* v_new, float* hT, void* o, void* stream) {
+  g_err.clear();
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  GDR_TRY(need(q, "q"));
+  GDR_TRY(need(k, "k"));
+  GDR_TRY(need(w, "w"));
+  GDR_TRY(need(u, "u"));
+  GDR_TRY(need(g_cum, "g_cum"));
+  GDR_TRY(need(o, "o"));
+  GDR_TRY(opt(h0, "h0"));
+  GDR_TRY(opt(h, "h"));
+  GDR_TRY(opt(v_new, "v_new"));
+  GDR_TRY(opt(hT, "hT"));
+  int mode = 0, P = 1;
+  const float* h_in = h0;
+  int in_vk = pr.state_vk;
+  if (seg != nullptr) {
+    if (!pr.pool_idx.empty()) return fail(GDR_ERR_UNSUPPORTED, "indexed states are supported by the serial scan only");
+    if (seg->n_segments < 1) return fail(GDR_ERR_INVALID_ARG, "n_segments must be >= 1");
+    GDR_TRY(need(seg->seg_init, "seg_init"));
+    mode = 2;
+    P = seg->n_segments;
+    h_in = seg->seg_init;
+    in_vk = 1;
+  }
+  gdr::Tile t;
+  GDR_TRY(tile_for(pr, tile, 0, static_cast<int64_t>(pr.N) * P, t));
+  if (tile == nullptr && !fusable(pr, t)) {
+    // the planner's tile has no fused form: the one-buffer four-wave tile of 64 columns
+    const gdr::Tile t64{64, 4, 2};
+    if (fusable(pr, t64)) t = t64;
+  }
+  if (fusable(pr, t)) {
+    const FusedOut fo{q, o, scale};
+    return run_scan(pr, t, mode, P, k, w, u, g_cum, h_in, in_vk, h, v_new, hT, pr.state_vk, nullptr,
+                    static_cast<hipStream_t>(stream), nullptr, 1, &fo);
+  }
+  // no fused kernel: the plain pass, then the chunk output from h and v_new
+  if (h == nullptr || v_new == nullptr)
+    return fail(GDR_ERR_UNSUPPORTED, "this dtype / DK / tile has no fused output: h and v_new must be given");
+  GDR_TRY(run_scan(pr, t, mode, P, k, w, u, g_cum, h_in, in_vk, h, v_new, hT, pr.state_vk, nullptr,
+                   static_cast<hipStream_t>(stream)));
+  return gdr_chunk_output(p, q, k, v_new, h, g_cum, scale, o, stream);
 }
 
 gdr_status gdr_chunk_output(const gdr_problem* p, const void* q, const void* k, const void* v_new, const void* h,

@@ -21,6 +21,9 @@ struct ScanArgs {
   float* h_out;        // hT or seg_state (nullable)
   float* trans_out;    // seg_trans (summaries only)
   const float* decay;  // per-key-channel decay: [NT, H, DK] channel decays of every chunk (else null)
+  const void* q;       // fused chunk output (scan2 with FO): queries, output o, scale
+  void* o;
+  float scale;
   int32_t H;
   int32_t DV;
   int32_t in_vk;       // layout of h_in: 1 = [.., DV, DK], 0 = [.., DK, DV]
@@ -153,6 +156,7 @@ using LaunchFn = hipError_t (*)(const void* args, int grid, hipStream_t stream);
 // Lookup of an instantiated kernel; nullptr when the combination is not built.
 LaunchFn find_scan(int dtype, int dk, int bv, int waves, int stages, int mode);
 LaunchFn find_scan2(int dk, int bv, int waves, int stages, int mode, bool kd);
+LaunchFn find_scan2_fused(int dk, int bv, int waves, int stages);  // plain pass + chunk output (bf16)
 LaunchFn find_prepare(int dtype, int dk, int dv);
 LaunchFn find_prepare2(int dk, int dv);
 LaunchFn find_kda_prepare(int dk, int dv);

@@ -43,12 +43,20 @@
 //     e^{Gam_last} (one DK-vector per chunk and head); the weights are then
 //     -1 (0 past the tail) and every state row is scaled by its own channel's
 //     decay: S <- diag(decay) S + kg^T D.
+//   * Fused chunk output (FO, staged plain pass with four waves): once every
+//     wave has staged its h columns and v_new columns of the chunk, wave w
+//     forms the output of token tile w over the block's BV columns,
+//       o_t = scale (e^{gamma_t} q_t^T S_c + sum_{i <= t} e^{gamma_t - gamma_i} (q_t . k_i) v_new_i),
+//     from the staged (bf16) S_c and v_new, the K tile still in LDS and Q
+//     fragments read from HBM straight into registers, with the operations
+//     of output2.hip in the same order (so o is the same bits), and without
+//     reading h or v_new back from HBM.
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
 namespace gdr {
 
-template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD>
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false>
 struct Scan2 {
   using S = St<bf16_t>;
   using frag = S::frag;
@@ -74,7 +82,8 @@ struct Scan2 {
   static constexpr int OFF_D = OFF_U + kChunk * SU;
   static constexpr int OFF_DEC = OFF_D + (kChunk + 4) * 4;  // KD: the chunk's DK channel decays
   static constexpr bool SIG = (MODE != 0) && !KD;           // scaled-state form (summaries)
-  static constexpr int BUF = OFF_DEC + (KD ? DK * 4 : 0);
+  static constexpr int OFF_GM = OFF_DEC + (KD ? DK * 4 : 0);  // FO: the chunk's gamma (zero past the tail)
+  static constexpr int BUF = OFF_GM + (FO ? kChunk * 4 : 0);
   // Output staging (single-buffer loop, plain and segmented passes): the
   // chunk's h block and v_new tile are written to LDS in their memory layout
   // and leave the next iteration as whole 16-byte vectors per lane (the h
@@ -93,6 +102,7 @@ struct Scan2 {
   static_assert(NC >= 1 && BV % (16 * NW) == 0, "each wave owns whole 16-column tiles");
   static_assert((kChunk * CPW) % NT == 0, "W/K tiles split evenly over the threads");
   static_assert(!STAGE || ((BV * DK / 8) % NT == 0 && (kChunk * BV / 8) % NT == 0), "staged outputs split evenly");
+  static_assert(!FO || (STAGE && NW == 4 && !KD), "the fused output runs on the staged plain pass, one token tile per wave");
 
   struct Stage {
     u32x4_t w[W_PT];
@@ -186,7 +196,94 @@ struct Scan2 {
         d[tid] = (tid < nvalid) ? -exp_fast(g_last - st.g) : 0.f;
         if (tid == 0) d[kChunk] = eg;
       }
+      if constexpr (FO) reinterpret_cast<float*>(buf + OFF_GM)[tid] = (tid < nvalid) ? st.g : 0.f;
     }
+  }
+
+  // FO: the chunk output of token tile `wave` over the block's BV columns
+  // (fq: this wave's Q fragments of the chunk).  Called by every wave once
+  // the chunk's h and v_new are staged; reads only LDS and registers, and
+  // the K tile and the staging stay untouched until the next chunk's first
+  // barrier.
+  __device__ static __forceinline__ void fused_output(const Ctx& x, const Row& row, int c, const char* buf,
+                                                      const char* so, const frag (&fq)[KS]) {
+    const ScanArgs& a = *x.a;
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t H = x.H;
+    const int DV = x.DV;
+    const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(c) * kChunk;
+    const int nvalid = min(kChunk, row.len - c * kChunk);
+    __syncthreads();  // every wave's h and v_new columns are staged
+
+    // P^T[i][t] = k_i . q_t for t in tile `wave`, i tiles 0..wave
+    const char* rowk = buf + OFF_K + c16 * SK + (g4 >> 1) * 16 + (g4 & 1) * 8;  // + 16 tile SK + 64 s (+32)
+    f32x4_t pt[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) pt[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+        if (it <= wave)
+          S::mma(pt[it], S::frag_from_quads(lds_b64(rowk, 16 * it * SK + 64 * s), lds_b64(rowk, 16 * it * SK + 64 * s + 32)),
+                 fq[s]);
+    const float* gm = reinterpret_cast<const float*>(buf + OFF_GM);
+    const int t = 16 * wave + c16;
+    const float gt = gm[t];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const f32x4_t gi = *reinterpret_cast<const f32x4_t*>(&gm[16 * it + 4 * g4]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * it + 4 * g4 + r;
+        pt[it][r] = (i <= t && t < nvalid) ? pt[it][r] * exp_fast(gt - gi[r]) : 0.f;
+      }
+    }
+    const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(&gm[16 * wave + 4 * g4]);
+    f32x4_t eg;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) eg[r] = exp_fast(gr[r]);
+
+    // O = e^{gamma} (Q S_c) + P v_new: S_c from the staged h rows (one value
+    // column each), v_new's operand (contraction over tokens) by transpose reads
+    constexpr int NCT = BV / 16;
+    const char* rowh = so + c16 * SHS + (g4 >> 1) * 16 + (g4 & 1) * 8;  // + 16 ct SHS + 64 s (+32)
+    f32x4_t acc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        S::mma(acc[ct], fq[s], S::frag_from_quads(lds_b64(rowh, 16 * ct * SHS + 64 * s), lds_b64(rowh, 16 * ct * SHS + 64 * s + 32)));
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] *= eg;
+    const char* vb = so + (OFF_VS - OFF_HS) + (4 * g4 + (c16 >> 2)) * SVS + 8 * (c16 & 3);  // + 32 s SVS (+16 SVS) + 32 ct
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (32 * s <= 16 * wave + 15) {
+        const frag fa = S::frag_from_f32(pt[2 * s], pt[2 * s + 1]);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          S::mma(acc[ct], fa, S::frag_from_quads(lds_tr16(vb, 32 * s * SVS + 32 * ct),
+                                                  lds_tr16(vb, (32 * s + 16) * SVS + 32 * ct)));
+      }
+    }
+
+    // o of the block's columns (rows past the tail dropped by the range check)
+    uint16_t* op = static_cast<uint16_t*>(a.o) + (tok0 * H + x.hd) * DV + x.col_blk;
+    const rsrc_t ro = make_rsrc(op, static_cast<uint32_t>(((nvalid - 1) * H * DV + BV) * 2));
+    const int rs = static_cast<int>(H * DV * 2);
+    const int voff = (16 * wave + 4 * g4) * rs + c16 * 2;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const uint32_t pk = pack_bf16x2(a.scale * acc[ct][r], a.scale * acc[ct][r + 1]);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk), ro, voff, r * rs + 32 * ct, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk >> 16), ro, voff, (r + 1) * rs + 32 * ct, 0);
+      }
   }
 
   // The staged outputs of chunk c (written before the last barrier) go to
@@ -246,6 +343,17 @@ struct Scan2 {
     const char* ub = buf + OFF_U + (4 * g4 + (c16 >> 2)) * SU + (colw + 4 * (c16 & 3)) * 2;  // + 16 mt SU + 32 ct
     const float* nd_l = reinterpret_cast<const float*>(buf + OFF_D) + 4 * g4;          // + 16 mt
 
+    // FO: this wave's Q fragments (token tile `wave`), in flight during the chunk step
+    frag fq[KS];
+    if constexpr (FO) {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (tok0 * H + x.hd) * DK;
+      const rsrc_t rq = make_rsrc(qp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
+      const int qo = static_cast<int>((16 * wave + c16) * H * DK * 2) + (g4 >> 1) * 16 + (g4 & 1) * 8;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        fq[s] = S::frag_from_quads(__builtin_amdgcn_raw_buffer_load_b64(rq, qo + 64 * s, 0, 0),
+                                   __builtin_amdgcn_raw_buffer_load_b64(rq, qo + 64 * s + 32, 0, 0));
+    }
     u32x2_t uq[4][NC];
     if constexpr (HASU) {
 #pragma unroll
@@ -410,6 +518,7 @@ struct Scan2 {
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) S::mma(Sacc[dt][ct], ak[s2][dt], Db[s2][ct]);
+    if constexpr (FO) fused_output(x, row, c, buf, smem_out, fq);
   }
 
   // The serial chunk loop of one block (HASU: this wave's columns read U).
@@ -600,16 +709,16 @@ struct Scan2 {
   }
 };
 
-template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD>
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false>
 __global__ __launch_bounds__(NW * 64) void scan2_kernel(const ScanArgs a) {
-  using K = Scan2<DK, BV, NW, PF, MODE, NBUF, KD>;
+  using K = Scan2<DK, BV, NW, PF, MODE, NBUF, KD, FO>;
   __shared__ __align__(16) char smem[K::SMEM];
   K::run(a, smem);
 }
 
-template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD>
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false>
 static hipError_t launch_scan2(const void* args, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((scan2_kernel<DK, BV, NW, PF, MODE, NBUF, KD>), dim3(grid), dim3(NW * 64), 0, stream,
+  hipLaunchKernelGGL((scan2_kernel<DK, BV, NW, PF, MODE, NBUF, KD, FO>), dim3(grid), dim3(NW * 64), 0, stream,
                      *static_cast<const ScanArgs*>(args));
   return hipGetLastError();
 }
@@ -640,6 +749,16 @@ LaunchFn find_scan2(int dk, int bv, int waves, int stages, int mode, bool kd) {
   GDR_SCAN2_TILES(GDR_SCAN2_CASE, 64, 2)
   // summaries only: one 8-wave block of all 256 columns of a (segment, head)
   GDR_SCAN2_CASE(128, 256, 8, 2, 2, 1, 1)
+  return nullptr;
+}
+
+// The plain pass with the chunk output fused (tiles with stages 2 and four waves).
+LaunchFn find_scan2_fused(int dk, int bv, int waves, int stages) {
+  if (waves != 4 || stages != 2) return nullptr;
+  if (dk == 128 && bv == 64) return &launch_scan2<128, 64, 4, 1, 0, 1, false, true>;
+  if (dk == 128 && bv == 128) return &launch_scan2<128, 128, 4, 1, 0, 1, false, true>;
+  if (dk == 64 && bv == 64) return &launch_scan2<64, 64, 4, 1, 0, 1, false, true>;
+  if (dk == 64 && bv == 128) return &launch_scan2<64, 128, 4, 1, 0, 1, false, true>;
   return nullptr;
 }
 
