@@ -280,3 +280,25 @@ def test_kda_validation():
                               None) == B.GDR_ERR_INVALID_ARG  # g_cum missing
     assert L.kda_segment_summaries(ctypes.byref(p), None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                    None) == B.GDR_ERR_INVALID_ARG  # n_segments
+
+
+def _scan_out(p, q=FAKE, k=FAKE, o=FAKE, h=None, v_new=None, seg=None, tile=None):
+    t = None if tile is None else ctypes.byref(B.gdr_tile(*tile))
+    s = None if seg is None else ctypes.byref(seg)
+    return B.lib().gdr_state_scan_output(ctypes.byref(p), t, s, q, k, FAKE, FAKE, FAKE, None, ctypes.c_float(1.0),
+                                         h, v_new, None, o, None)
+
+
+def test_fused_scan_output_validation():
+    L = B.lib()
+    p, keep = _prob()
+    assert _scan_out(p, q=None) == B.GDR_ERR_INVALID_ARG and "q" in L.gdr_last_error().decode()
+    assert _scan_out(p, o=None) == B.GDR_ERR_INVALID_ARG and "o" in L.gdr_last_error().decode()
+    assert _scan_out(p, q=ctypes.c_void_p(0x10004)) == B.GDR_ERR_INVALID_ARG
+    assert _scan_out(p, seg=B.gdr_segments(0, FAKE.value)) == B.GDR_ERR_INVALID_ARG
+    # without a fused kernel (float32 storage, or a tile that has none) h and v_new must be given
+    p32, keep32 = _prob(dtype=B.GDR_F32)
+    assert _scan_out(p32) == B.GDR_ERR_UNSUPPORTED and "h and v_new" in L.gdr_last_error().decode()
+    assert _scan_out(p, tile=(32, 2, 2), h=FAKE) == B.GDR_ERR_UNSUPPORTED
+    pool, keepp = _pool_prob([3, 0, 2], 4)
+    assert _scan_out(pool, seg=B.gdr_segments(2, FAKE.value)) == B.GDR_ERR_UNSUPPORTED
