@@ -98,7 +98,8 @@ def test_pool_in_place(pkg):
     assert torch.equal(p[untouched].cpu(), pool[untouched])
 
 
-def test_graph_capture_matches_eager(pkg):
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_capture_matches_eager(pkg, fused):
     inp, pool = _inputs()
     q, k, v, g, b = (x.cuda() for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
     cu = inp.cu_seqlens
@@ -117,6 +118,12 @@ def test_graph_capture_matches_eager(pkg):
         B._check(L.gdr_chunk_prepare(P.ref, B._ptr(k), B._ptr(v), B._ptr(g), B._ptr(b), B._ptr(bf["g_cum"]),
                                      B._ptr(bf["w"]), B._ptr(bf["u"]), s), "prepare")
         Pp = B.Problem(k, 128, cu, "kv", IDX, POOL)
+        if fused:  # the state scan with the chunk output fused
+            B._check(L.gdr_state_scan_output(Pp.ref, None, None, B._ptr(q), B._ptr(k), B._ptr(bf["w"]),
+                                             B._ptr(bf["u"]), B._ptr(bf["g_cum"]), B._ptr(bf["pool"]),
+                                             float(inp.scale), B._ptr(bf["h"]), B._ptr(bf["v_new"]),
+                                             B._ptr(bf["pool"]), B._ptr(bf["o"]), s), "scan + output")
+            return
         B._check(L.gdr_state_scan(Pp.ref, None, None, B._ptr(k), B._ptr(bf["w"]), B._ptr(bf["u"]),
                                   B._ptr(bf["g_cum"]), B._ptr(bf["pool"]), B._ptr(bf["h"]), B._ptr(bf["v_new"]),
                                   B._ptr(bf["pool"]), s), "scan")
