@@ -48,9 +48,11 @@
 //     forms the output of token tile w over the block's BV columns,
 //       o_t = scale (e^{gamma_t} q_t^T S_c + sum_{i <= t} e^{gamma_t - gamma_i} (q_t . k_i) v_new_i),
 //     from the staged (bf16) S_c and v_new, the K tile still in LDS and Q
-//     fragments read from HBM straight into registers, with the operations
-//     of output2.hip in the same order (so o is the same bits), and without
-//     reading h or v_new back from HBM.
+//     fragments read from HBM straight into registers, without reading h or
+//     v_new back from HBM.  The products are output2.hip's with the operand
+//     roles exchanged (O^T = S_c^T Q^T e^gamma + v_new^T P^T: the same
+//     products in the same k order, so o is the same bits), which leaves
+//     each lane four consecutive value columns of one token: 8-byte stores.
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
@@ -240,13 +242,13 @@ struct Scan2 {
         pt[it][r] = (i <= t && t < nvalid) ? pt[it][r] * exp_fast(gt - gi[r]) : 0.f;
       }
     }
-    const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(&gm[16 * wave + 4 * g4]);
-    f32x4_t eg;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) eg[r] = exp_fast(gr[r]);
+    const float eg = exp_fast(gt);  // e^{gamma_t} of this lane's token
 
-    // O = e^{gamma} (Q S_c) + P v_new: S_c from the staged h rows (one value
-    // column each), v_new's operand (contraction over tokens) by transpose reads
+    // O^T = (S_c^T Q^T) e^{gamma} + v_new^T P^T, so that each lane ends with
+    // four consecutive value columns of its token t = 16 wave + c16:
+    // acc[ct][r] = O[t][16 ct + 4 g4 + r].  S_c^T is read from the staged h
+    // rows (one value column each); v_new^T by transpose reads of the staged
+    // v_new rows.
     constexpr int NCT = BV / 16;
     const char* rowh = so + c16 * SHS + (g4 >> 1) * 16 + (g4 & 1) * 8;  // + 16 ct SHS + 64 s (+32)
     f32x4_t acc[NCT];
@@ -256,34 +258,32 @@ struct Scan2 {
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
-        S::mma(acc[ct], fq[s], S::frag_from_quads(lds_b64(rowh, 16 * ct * SHS + 64 * s), lds_b64(rowh, 16 * ct * SHS + 64 * s + 32)));
+        S::mma(acc[ct], S::frag_from_quads(lds_b64(rowh, 16 * ct * SHS + 64 * s), lds_b64(rowh, 16 * ct * SHS + 64 * s + 32)),
+               fq[s]);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[ct] *= eg;
     const char* vb = so + (OFF_VS - OFF_HS) + (4 * g4 + (c16 >> 2)) * SVS + 8 * (c16 & 3);  // + 32 s SVS (+16 SVS) + 32 ct
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (32 * s <= 16 * wave + 15) {
-        const frag fa = S::frag_from_f32(pt[2 * s], pt[2 * s + 1]);
+        const frag fp = S::frag_from_f32(pt[2 * s], pt[2 * s + 1]);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
-          S::mma(acc[ct], fa, S::frag_from_quads(lds_tr16(vb, 32 * s * SVS + 32 * ct),
-                                                  lds_tr16(vb, (32 * s + 16) * SVS + 32 * ct)));
+          S::mma(acc[ct], S::frag_from_quads(lds_tr16(vb, 32 * s * SVS + 32 * ct), lds_tr16(vb, (32 * s + 16) * SVS + 32 * ct)),
+                 fp);
       }
     }
 
-    // o of the block's columns (rows past the tail dropped by the range check)
+    // o of the block's columns, 8 bytes per lane and column tile (rows past
+    // the tail dropped by the range check)
     uint16_t* op = static_cast<uint16_t*>(a.o) + (tok0 * H + x.hd) * DV + x.col_blk;
     const rsrc_t ro = make_rsrc(op, static_cast<uint32_t>(((nvalid - 1) * H * DV + BV) * 2));
-    const int rs = static_cast<int>(H * DV * 2);
-    const int voff = (16 * wave + 4 * g4) * rs + c16 * 2;
+    const int voff = t * static_cast<int>(H * DV * 2) + 8 * g4;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const uint32_t pk = pack_bf16x2(a.scale * acc[ct][r], a.scale * acc[ct][r + 1]);
-        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk), ro, voff, r * rs + 32 * ct, 0);
-        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk >> 16), ro, voff, (r + 1) * rs + 32 * ct, 0);
-      }
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(a.scale * acc[ct][0], a.scale * acc[ct][1]),
+                                                    pack_bf16x2(a.scale * acc[ct][2], a.scale * acc[ct][3])},
+                                            ro, voff, 32 * ct, 0);
   }
 
   // The staged outputs of chunk c (written before the last barrier) go to

@@ -6,9 +6,10 @@
   gathered states, and every other pool entry must stay untouched, also when
   the update is in place (h0 and hT the same buffer).
 * Graphs (the same page's "Test plan": graphs match eager): the whole forward
-  step (prepare, scan with an in-place pool, output) captured once in a HIP
-  graph and replayed several times, with eager work and synchronisation in
-  between, must give bit for bit what the eager steps give.
+  step (prepare, scan with an in-place pool, output; also with the scan and
+  output fused) captured once in a HIP graph and replayed several times, with
+  eager work and synchronisation in between, must give bit for bit what the
+  eager steps give.
 """
 
 import numpy as np
