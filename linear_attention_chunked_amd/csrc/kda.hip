@@ -599,7 +599,8 @@ struct KdaOutput {
       for (int r = 0; r < 4; ++r) sm.B.p[(16 * wave + 4 * g4 + r) * LP + 16 * J + c16] = pr[J][r];
     __syncthreads();
 
-    // ---- O = (Q e^Gam) S_c + P v_new, rows of token tile `wave` ----
+    // ---- O^T = S_c^T (Q e^Gam)^T + v_new^T P^T for the tokens of tile `wave`: each
+    //      lane ends with four consecutive value columns of its token (8-byte stores) ----
     const char* rowh = sm.B.h + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;
     auto rfrag = [&](const char* base, int tile, int s) {
       return S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(base + 16 * tile * SQ + 64 * s),
@@ -613,8 +614,8 @@ struct KdaOutput {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const frag hb = rfrag(rowh, ct, s);
-        S::mma(acc[ct], qh[s], hb);
-        S::mma(acc[ct], ql[s], hb);
+        S::mma(acc[ct], hb, qh[s]);
+        S::mma(acc[ct], hb, ql[s]);
       }
     const char* vb_ = sm.B.v + (4 * g4 + (c16 >> 2)) * SV + 8 * (c16 & 3);
     const int t = 16 * wave + c16;
@@ -634,24 +635,20 @@ struct KdaOutput {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const frag vf = S::frag_from_quads(lds_tr16(vb_, 32 * s * SV + 32 * ct), lds_tr16(vb_, (32 * s + 16) * SV + 32 * ct));
-          S::mma(acc[ct], ph, vf);
-          S::mma(acc[ct], pl, vf);
+          S::mma(acc[ct], vf, ph);
+          S::mma(acc[ct], vf, pl);
         }
       }
     }
 
     uint16_t* op = static_cast<uint16_t*>(a.o) + (tok0 * H + hd) * DV;
     const rsrc_t ro = make_rsrc(op, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
-    const int rs = static_cast<int>(H * DV * 2);
-    const int voff = (16 * wave + 4 * g4) * rs + c16 * 2;
+    const int voff = t * static_cast<int>(H * DV * 2) + 8 * g4;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const uint32_t pk = pack_bf16x2(a.scale * acc[ct][r], a.scale * acc[ct][r + 1]);
-        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk), ro, voff, r * rs + 32 * ct, 0);
-        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk >> 16), ro, voff, (r + 1) * rs + 32 * ct, 0);
-      }
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(a.scale * acc[ct][0], a.scale * acc[ct][1]),
+                                                    pack_bf16x2(a.scale * acc[ct][2], a.scale * acc[ct][3])},
+                                            ro, voff, 32 * ct, 0);
   }
 };
 
