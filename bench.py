@@ -632,17 +632,10 @@ def reverse_alg_bytes(lengths, H, DK, DV, nt, has_dhT):
     return dvl, scan
 
 
-def reverse_fused_alg_bytes(lengths, H, DK, DV, nt, has_dhT):
-    """The reverse scan with the chunk-local term formed inside it: the scan's
-    bytes without the dv_local read (q, k, dO, g_cum it already reads)."""
-    return reverse_alg_bytes(lengths, H, DK, DV, nt, has_dhT)[1] - int(sum(lengths)) * H * DV * 2
-
-
 def reverse(pkg, torch, dev, workload):
-    """The reverse pass of the same workload, seeded dO (bf16) and dhT (fp32):
-    the serial reverse state walk (dh per chunk, dv_new gradient, dh0) with
-    the chunk-local write-vector gradient formed inside it; beside it the two
-    kernels (chunk-parallel dv_local, then the walk reading it)."""
+    """The reverse pass of the same workload: chunk-local write-vector
+    gradient, then the serial reverse state walk (dh per chunk, dv_new
+    gradient, dh0), seeded dO (bf16) and dhT (fp32)."""
     import numpy as np
     from workloads import make_config
 
@@ -678,24 +671,16 @@ def reverse(pkg, torch, dev, workload):
         dv_local()
         scan_bwd()
 
-    def fused():
-        B._check(L.gdr_state_scan_bwd(P.ref, ptr(q), ptr(k), ptr(w), ptr(g_cum), ptr(dO), None, ptr(dhT),
-                                      scale, ptr(dh), ptr(dv), ptr(dh0), s_ptr), "scan_bwd (fused)")
-
     a_us = _event_median_us(torch, dv_local, reps=7, per=8)
     b_us = _event_median_us(torch, scan_bwd, reps=7, per=8)
     t_us = _event_median_us(torch, both, reps=7, per=8)
-    f_us = _event_median_us(torch, fused, reps=7, per=8)
     a_alg, b_alg = reverse_alg_bytes(inp.lengths, inp.H, inp.DK, DV, nt, True)
-    f_alg = reverse_fused_alg_bytes(inp.lengths, inp.H, inp.DK, DV, nt, True)
-    return {"workload": f"{workload} reverse pass (dO bf16, dhT fp32)", "us": round(f_us, 1),
-            "Mtok_head_per_s": round(inp.token_heads / f_us, 1), "alg_bytes": f_alg,
-            "frac_of_hbm": round(f_alg / (f_us * 1e-6) / 8e12, 4),
-            "two_kernels": {"us": round(t_us, 1),
-                            "dv_local": {"us": round(a_us, 1), "alg_bytes": a_alg,
-                                         "frac_of_hbm": round(a_alg / (a_us * 1e-6) / 8e12, 4)},
-                            "scan_bwd": {"us": round(b_us, 1), "alg_bytes": b_alg,
-                                         "frac_of_hbm": round(b_alg / (b_us * 1e-6) / 8e12, 4)}}}
+    return {"workload": f"{workload} reverse pass (dO bf16, dhT fp32)", "us": round(t_us, 1),
+            "Mtok_head_per_s": round(inp.token_heads / t_us, 1),
+            "dv_local": {"us": round(a_us, 1), "alg_bytes": a_alg,
+                         "frac_of_hbm": round(a_alg / (a_us * 1e-6) / 8e12, 4)},
+            "scan_bwd": {"us": round(b_us, 1), "alg_bytes": b_alg,
+                         "frac_of_hbm": round(b_alg / (b_us * 1e-6) / 8e12, 4)}}
 
 
 if __name__ == "__main__":

@@ -271,9 +271,8 @@ gdr_status gdr_chunk_dv_local(const gdr_problem* p, const void* q, const void* k
 
 /* The reverse state scan: serial over each sequence's chunks, last to first.
  * Inputs q, k, w (from gdr_chunk_prepare), g_cum, dO, dv_local (from
- * gdr_chunk_dv_local; NULL = formed inside the scan from the chunk's q, k,
- * g_cum and dO, the same bits, without the round trip through memory), dhT
- * (nullable, [N,H,DK,DV] or [N,H,DV,DK] by state_layout).  Outputs (each nullable): dh [NT,H,DV,DK] storage dtype,
+ * gdr_chunk_dv_local), dhT (nullable, [N,H,DK,DV] or [N,H,DV,DK] by
+ * state_layout).  Outputs (each nullable): dh [NT,H,DV,DK] storage dtype,
  * value-major like h; dv_new_grad [B,T,H,DV] storage dtype; dh0 float32 in
  * the state layout. */
 gdr_status gdr_state_scan_bwd(const gdr_problem* p, const void* q, const void* k, const void* w, const float* g_cum,

@@ -516,8 +516,7 @@ def gdr_state_scan_bwd(q, k, w, g_cum, dO, dv_local, dhT=None, scale: float = 1.
                        state_layout: str = "kv", emit_dh: bool = True, emit_dv: bool = True, emit_dh0: bool = True,
                        stream=None):
     """Reverse state scan.  Returns (dh [NT,H,DV,DK] | None, dv_new_grad [B,T,H,DV] | None,
-    dh0 [N,H,DK,DV] fp32 (or [N,H,DV,DK] for "vk") | None).  ``dv_local=None`` forms the
-    chunk-local term inside the scan (the same bits as ``gdr_chunk_dv_local``)."""
+    dh0 [N,H,DK,DV] fp32 (or [N,H,DV,DK] for "vk") | None)."""
     DV = dO.shape[-1]
     p = Problem(k, DV, cu_seqlens, state_layout)
     nt = gdr_num_chunks(k, DV, cu_seqlens)

@@ -350,13 +350,13 @@ gdr_status gdr_state_scan_bwd(const gdr_problem* p, const void* q, const void* k
   GDR_TRY(need(w, "w"));
   GDR_TRY(need(g_cum, "g_cum"));
   GDR_TRY(need(dO, "dO"));
-  GDR_TRY(opt(dv_local, "dv_local"));
+  GDR_TRY(need(dv_local, "dv_local"));
   GDR_TRY(opt(dhT, "dhT"));
   GDR_TRY(opt(dh, "dh"));
   GDR_TRY(opt(dv_new_grad, "dv_new_grad"));
   GDR_TRY(opt(dh0, "dh0"));
   if (pr.dtype != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "the reverse pass is built for bfloat16 storage");
-  gdr::LaunchFn fn = gdr::find_scan_bwd(pr.DK, dv_local == nullptr);
+  gdr::LaunchFn fn = gdr::find_scan_bwd(pr.DK);
   if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no reverse scan kernel for this DK");
   if (pr.DV % 64 != 0) return fail(GDR_ERR_UNSUPPORTED, "the reverse scan takes 64-column blocks");
   gdr::ScanBwdArgs a;

@@ -166,7 +166,7 @@ LaunchFn find_output2(int dk, int dv);
 LaunchFn find_compose(int dk, int P);
 LaunchFn find_combine(int dk);
 LaunchFn find_dv_local(int dk, int dv);
-LaunchFn find_scan_bwd(int dk, bool fused);  // fused: dv_local formed in the scan
+LaunchFn find_scan_bwd(int dk);
 hipError_t launch_abc(const AbcArgs& a, hipStream_t s);
 hipError_t launch_abc_bwd(const AbcArgs& a, hipStream_t s);
 

@@ -15,11 +15,7 @@
 //
 // and dh0 = dS after the first chunk.  The chunk-local term scale P^T dO does
 // not depend on dS: `dv_local_kernel` forms it for every chunk in parallel,
-// and the serial `scan_bwd_kernel` adds the K dS part (or, with FL, forms
-// the chunk-local term itself: once a chunk's tiles are in LDS, wave w forms
-// it for key tile w with the operations of dv_local_kernel, over the block's
-// columns, into the LDS tile the loaded dv_local would have filled; the
-// result is the same bits, and dv_local never goes through HBM).  The serial kernel is
+// and the serial `scan_bwd_kernel` adds the K dS part.  The serial kernel is
 // the forward scan run backwards with the same gfx950 organisation: one
 // workgroup per (sequence, head, 64 value columns), dS in FP32 MFMA
 // accumulators for the whole loop, K as row fragments (K dS contracts over
@@ -184,7 +180,7 @@ LaunchFn find_dv_local(int dk, int dv) {
 }
 
 // ---------------------------------------------------------------- reverse scan
-template <int DK, bool FL = false>
+template <int DK>
 struct ScanBwd {
   using S = St<bf16_t>;
   using frag = S::frag;
@@ -201,8 +197,7 @@ struct ScanBwd {
   static constexpr int OFF_K = 0, OFF_Q = kChunk * SKR, OFF_W = OFF_Q + kChunk * SQT;
   static constexpr int OFF_DO = OFF_W + kChunk * SQT, OFF_DL = OFF_DO + kChunk * SDV;
   static constexpr int OFF_F = OFF_DL + kChunk * SDV;  // d_i = e^{gC - g_i}, f_t = scale e^{g_t}, then e^{gC}
-  static constexpr int OFF_GM = OFF_F + 2 * kChunk * 4 + 16;  // FL: the chunk's gamma (zero past the tail)
-  static constexpr int BUF = OFF_GM + (FL ? kChunk * 4 : 0);
+  static constexpr int BUF = OFF_F + 2 * kChunk * 4 + 16;
   static constexpr int SHS = DK * 2 + 16, SVS = BV * 2 + 16;  // staged dh / dv_new rows
   static constexpr int OFF_HS = BUF, OFF_VS = OFF_HS + BV * SHS;
   static constexpr int SMEM = OFF_VS + kChunk * SVS;
@@ -243,7 +238,7 @@ struct ScanBwd {
 #pragma unroll
     for (int i = 0; i < V_PT; ++i) {
       st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(rd, x.vo_v[i], 0, 0);
-      if (!FL) st.l[i] = __builtin_amdgcn_raw_buffer_load_b128(rl, x.vo_v[i], 0, 0);
+      st.l[i] = __builtin_amdgcn_raw_buffer_load_b128(rl, x.vo_v[i], 0, 0);
     }
     const rsrc_t rg = make_rsrc(a.g_cum + tok0 * H + x.hd, any ? static_cast<uint32_t>(((nvalid - 1) * H + 1) * 4) : 0u);
     st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, static_cast<int>((threadIdx.x & 63) * H * 4), 0, 0));
@@ -262,7 +257,7 @@ struct ScanBwd {
     for (int i = 0; i < V_PT; ++i) {
       const int v = tid + i * NT, r = v / CPV, c = v % CPV;
       *reinterpret_cast<u32x4_t*>(buf + OFF_DO + r * SDV + c * 16) = st.d[i];
-      if (!FL) *reinterpret_cast<u32x4_t*>(buf + OFF_DL + r * SDV + c * 16) = st.l[i];
+      *reinterpret_cast<u32x4_t*>(buf + OFF_DL + r * SDV + c * 16) = st.l[i];
     }
     if (tid < kChunk) {  // first wave: the chunk's decay factors
       const float g_last = __builtin_bit_cast(
@@ -272,68 +267,7 @@ struct ScanBwd {
       f[tid] = ok ? exp_fast(g_last - st.g) : 0.f;                      // d_i
       f[kChunk + tid] = ok ? x.a->scale * exp_fast(st.g) : 0.f;        // f_t
       if (tid == 0) f[2 * kChunk] = exp_fast(g_last);
-      if (FL) reinterpret_cast<float*>(buf + OFF_GM)[tid] = ok ? st.g : 0.f;
     }
-  }
-
-  // FL: the chunk-local term scale P^T dO for the rows of key tile `wave`
-  // over this block's BV columns, written (bf16) into the dv_local tile; the
-  // operations of dv_local_kernel in its order.
-  __device__ static __forceinline__ void local_term(const ScanBwdArgs& a, char* buf, int nvalid) {
-    const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    // P[t][i] for the wave's key tile i (C layout: rows t, column i), t tiles >= the key tile
-    const char* rq = buf + OFF_Q + c16 * SQT + 8 * g4;  // + 16 tile SQT + 64 s (+32)
-    const char* rk = buf + OFF_K + c16 * SKR + 8 * g4;
-    f32x4_t p[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) p[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const frag fk = S::frag_from_quads(lds_b64(rk, 16 * wave * SKR + 64 * s), lds_b64(rk, 16 * wave * SKR + 64 * s + 32));
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-        if (tt >= wave)
-          S::mma(p[tt], S::frag_from_quads(lds_b64(rq, 16 * tt * SQT + 64 * s), lds_b64(rq, 16 * tt * SQT + 64 * s + 32)),
-                 fk);
-    }
-    const float* gm = reinterpret_cast<const float*>(buf + OFF_GM);
-    const int i = 16 * wave + c16;
-    const float gi = gm[i];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const f32x4_t gt = *reinterpret_cast<const f32x4_t*>(&gm[16 * tt + 4 * g4]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tt + 4 * g4 + r;
-        p[tt][r] = (i <= t && t < nvalid) ? a.scale * p[tt][r] * exp_fast(gt[r] - gi) : 0.f;
-      }
-    }
-    // rows i of the wave's key tile = sum_t P[t][i] dO[t][:]
-    constexpr int NCT = BV / 16;
-    f32x4_t acc[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const char* db = buf + OFF_DO + (4 * g4 + (c16 >> 2)) * SDV + 8 * (c16 & 3);
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      if (32 * s2 + 31 >= 16 * wave) {
-        const frag fa = S::frag_from_f32(p[2 * s2], p[2 * s2 + 1]);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          S::mma(acc[ct], fa, S::frag_from_quads(lds_tr16(db, 32 * s2 * SDV + 32 * ct),
-                                                 lds_tr16(db, (32 * s2 + 16) * SDV + 32 * ct)));
-      }
-    }
-    uint16_t* dl = reinterpret_cast<uint16_t*>(buf + OFF_DL) + (16 * wave + 4 * g4) * (SDV / 2) + c16;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const uint32_t pk = pack_bf16x2(acc[ct][r], acc[ct][r + 1]);
-        dl[r * (SDV / 2) + 16 * ct] = static_cast<uint16_t>(pk);
-        dl[(r + 1) * (SDV / 2) + 16 * ct] = static_cast<uint16_t>(pk >> 16);
-      }
   }
 
   __device__ static __forceinline__ void write_out(const Ctx& x, const Row& row, int c, const char* so) {
@@ -514,10 +448,6 @@ struct ScanBwd {
         store(st, x, buf, nv_of(c));
         __syncthreads();
         load(st, x, tok_of(c - 1 >= 0 ? c - 1 : 0), nv_of(c - 1));
-        if (FL) {
-          local_term(a, buf, nv_of(c));
-          __syncthreads();  // every key tile's rows are in the dv_local tile
-        }
         compute(Sacc, buf, so);
       }
       __syncthreads();
@@ -540,24 +470,22 @@ struct ScanBwd {
   }
 };
 
-template <int DK, bool FL>
+template <int DK>
 __global__ __launch_bounds__(256) void scan_bwd_kernel(const ScanBwdArgs a) {
-  using K = ScanBwd<DK, FL>;
+  using K = ScanBwd<DK>;
   __shared__ __align__(16) char smem[K::SMEM];
   K::run(a, smem);
 }
 
-template <int DK, bool FL>
+template <int DK>
 static hipError_t launch_scan_bwd(const void* args, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((scan_bwd_kernel<DK, FL>), dim3(grid), dim3(256), 0, stream,
-                     *static_cast<const ScanBwdArgs*>(args));
+  hipLaunchKernelGGL((scan_bwd_kernel<DK>), dim3(grid), dim3(256), 0, stream, *static_cast<const ScanBwdArgs*>(args));
   return hipGetLastError();
 }
 
-// fused: the chunk-local term formed in the scan (no dv_local input)
-LaunchFn find_scan_bwd(int dk, bool fused) {
-  if (dk == 128) return fused ? &launch_scan_bwd<128, true> : &launch_scan_bwd<128, false>;
-  if (dk == 64) return fused ? &launch_scan_bwd<64, true> : &launch_scan_bwd<64, false>;
+LaunchFn find_scan_bwd(int dk) {
+  if (dk == 128) return &launch_scan_bwd<128>;
+  if (dk == 64) return &launch_scan_bwd<64>;
   return nullptr;
 }
 

@@ -127,39 +127,3 @@ def test_backward_packed_equals_dense_and_deterministic(pkg):
     c = run_bwd(pkg, dense, dO, dhT, 1.0)
     for key in a:
         assert torch.equal(a[key], c[key]), key
-
-
-def run_bwd_fused(pkg, inp, dO, dhT, scale, state_layout="kv"):
-    """The reverse scan with dv_local = None: the chunk-local term is formed inside the scan."""
-    q, k, v, g, b = (x.cuda() for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
-    cu = inp.cu_seqlens
-    g_cum, w, u = pkg.gdr_chunk_prepare(k, v, g, b, cu)
-    dhT_d = None
-    if dhT is not None:
-        dhT_d = dhT.cuda() if state_layout == "kv" else dhT.transpose(-1, -2).contiguous().cuda()
-    dh, dv, dh0 = pkg.gdr_state_scan_bwd(q, k, w, g_cum, dO.cuda(), None, dhT_d, scale, cu, state_layout=state_layout)
-    torch.cuda.synchronize()
-    if state_layout == "vk":
-        dh0 = dh0.transpose(-1, -2)
-    return {"dh": dh, "dv": dv, "dh0": dh0}
-
-
-@pytest.mark.parametrize("DK,DV", [(128, 128), (64, 64), (128, 64), (64, 128)])
-@pytest.mark.parametrize("state_layout", ["kv", "vk"])
-def test_backward_fused_local_term_equals_two_kernels(pkg, DK, DV, state_layout):
-    inp = make_gdr(870 + DK + DV, lengths=[1, 63, 64, 65, 150, 0, 200], H=2, DK=DK, DV=DV, dtype=torch.bfloat16,
-                   varlen=True)
-    dO, dhT = grads(inp, 871)
-    a = run_bwd(pkg, inp, dO, dhT, 0.3, state_layout)
-    b = run_bwd_fused(pkg, inp, dO, dhT, 0.3, state_layout)
-    for key in ("dh", "dv", "dh0"):
-        assert torch.equal(a[key], b[key]), f"{DK}x{DV} {state_layout}: {key} differs"
-
-
-def test_backward_fused_local_term_question_rows(pkg):
-    inp = make_config("question_rows")
-    dO, dhT = grads(inp, 872)
-    a = run_bwd(pkg, inp, dO, dhT, 1.0)
-    b = run_bwd_fused(pkg, inp, dO, dhT, 1.0)
-    for key in ("dh", "dv", "dh0"):
-        assert torch.equal(a[key], b[key]), f"question_rows: {key} differs"
