@@ -255,6 +255,27 @@ def main():
                            / BF16_PEAK_TFLOPS, 4),
     }
 
+    # The state scan alone (gdr_state_scan, the unfused kernel, same outputs
+    # but o), after the timed region: 30 launches through the C ABI into the
+    # same buffers, each between a pair of HIP events on the launch stream.
+    def scan_alone(ev):
+        ev[0].record(stream)
+        B._check(L.gdr_state_scan(P.ref, None, None, ptr(k), ptr(w), ptr(u), ptr(g_cum), ptr(h0), ptr(h),
+                                  ptr(v_new), ptr(hT), s_ptr), "scan")
+        ev[1].record(stream)
+
+    for _ in range(5):
+        scan_alone((HipEvent(), HipEvent()))
+    sa = [(HipEvent(), HipEvent()) for _ in range(30)]
+    for ev in sa:
+        scan_alone(ev)
+    torch.cuda.synchronize()
+    sa_us = sorted(a.elapsed_ms(b) * 1e3 for a, b in sa)
+    sa_alg = scan_alg_bytes(inp.lengths, inp.H, inp.DK, DV, in_bytes, in_bytes, h0 is not None, True)
+    roofline["state_scan_alone"] = {"launch_us_median": round(sa_us[len(sa_us) // 2], 2),
+                                    "alg_bytes_per_launch": sa_alg,
+                                    "frac": round(sa_alg / (sa_us[len(sa_us) // 2] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
     # Cold-cache figures (after the timed region): before every rep a 1 GiB
     # fill evicts L2 and the 256 MB Infinity Cache (the step's 169 MB of fused
     # scan traffic would otherwise partly stay resident between back-to-back steps).
@@ -315,6 +336,8 @@ def main():
     copy_gbs = copy_bandwidth(torch, dev)
     roofline["copy_gbs"] = round(copy_gbs, 1)
     roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
+    sa = roofline["state_scan_alone"]
+    sa["frac_of_copy"] = round(sa["alg_bytes_per_launch"] / (sa["launch_us_median"] * 1e-6) / 1e9 / copy_gbs, 4)
     if "cold_cache" in roofline:
         roofline["cold_cache"]["scan_frac_of_copy"] = round(
             alg / (roofline["cold_cache"]["scan_us_median"] * 1e-6) / 1e9 / copy_gbs, 4)
