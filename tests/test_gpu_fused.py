@@ -130,6 +130,8 @@ def test_fused_question_rows_against_oracle(pkg):
     ref2 = two_calls(pkg, q, k, w, u, g_cum, h0, inp.cu_seqlens, inp.scale)
     got = pkg.gdr_state_scan_output(q, k, w, u, g_cum, inp.scale, h0, inp.cu_seqlens)
     assert_same(got, ref2, "question_rows")
+    again = pkg.gdr_state_scan_output(q, k, w, u, g_cum, inp.scale, h0, inp.cu_seqlens)
+    assert_same(again, got, "question_rows run to run")
     d = inp.f64()
     ref = oracle.gdr_recurrent_fp64(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"], inp.scale)
     o, h, v_new, hT = (t.detach().to(torch.float64).cpu().numpy() for t in got)
