@@ -525,6 +525,8 @@ BWD_CHECKS = [check_bwd_initial_state, check_bwd_boundaries, check_bwd_write_vec
 
 
 def run_bwd_check(check, bwd_ref, gdr_ref, chunked_ref):
+    if check.__name__ == "check_bwd_wrapper_packed":
+        return check(bwd_ref, gdr_ref, chunked_ref)
     if check in (check_bwd_initial_state, check_bwd_boundaries):
         return check(bwd_ref, gdr_ref)
     if check in (check_bwd_write_vectors, check_bwd_chunk_relation):
@@ -665,7 +667,7 @@ ABC_BWD_CHECKS = [check_abc_bwd_boundaries, check_abc_bwd_running_mean, check_ab
 
 
 def run_abc_bwd_check(check, abc_bwd_ref, abc_ref):
-    if check is check_abc_bwd_boundaries:
+    if check.__name__ in ("check_abc_bwd_boundaries", "check_abc_bwd_wrapper_sampled"):
         return check(abc_bwd_ref, abc_ref)
     return check(abc_bwd_ref)
 
@@ -807,3 +809,198 @@ def check_kda_chunk_algebra(kda_ref):
 
 
 KDA_CHECKS = [check_kda_brute_force, check_kda_rationals, check_kda_pure_decay, check_kda_recall]
+
+
+# --------------------------------------------------------------------------- batch wrappers
+# The GPU parity tests compare against the oracle's whole-problem wrappers
+# (packed sequences, sampled heads / batch rows).  These pins hold each
+# wrapper's packing and sampling against facts computed here, sequence by
+# sequence and head by head, from the raw inputs: dense transition products,
+# closed-form weighted sums and finite differences.
+def _packed_problem(seed, lengths, H, DK, DV):
+    r = np.random.default_rng(seed)
+    T = sum(lengths)
+    q = r.standard_normal((1, T, H, DK))
+    k = r.standard_normal((1, T, H, DK))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((1, T, H, DV))
+    g = np.log(1.0 / (1.0 + np.exp(-r.normal(2.0, 1.0, (1, T, H)))))
+    beta = 1.0 / (1.0 + np.exp(-r.standard_normal((1, T, H))))
+    h0 = 0.3 * r.standard_normal((len(lengths), H, DK, DV))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    return q, k, v, g, beta, h0, cu
+
+
+def check_wrapper_packed_heads(gdr_ref):
+    """gdr_recurrent_fp64 on packed sequences with a head sample: every
+    sampled head of every sequence equals the dense transition products of
+    that head alone, started from that sequence's and head's h0 (outputs,
+    write vectors, pre-chunk rows at the packed chunk offsets, final state)."""
+    lengths, H, DK, DV, C, scale = [9, 4, 0, 6, 11], 3, 3, 2, 4, 0.7
+    hs = [2, 0]
+    q, k, v, g, beta, h0, cu = _packed_problem(71, lengths, H, DK, DV)
+    out = gdr_ref.gdr_recurrent_fp64(q, k, v, g, beta, h0, cu, scale, chunk=C, heads=hs)
+    counts = [(L + C - 1) // C for L in lengths]
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    assert list(out["chunk_offsets"]) == list(offs), "chunk offsets"
+    assert out["h"].shape == (offs[-1], len(hs), DK, DV) and out["hT"].shape == (len(lengths), len(hs), DK, DV)
+    a = np.exp(g)
+    for n, L in enumerate(lengths):
+        s = int(cu[n])
+        for j, hh in enumerate(hs):
+            kk, vv, aa, bb = k[0, s:s + L, hh], v[0, s:s + L, hh], a[0, s:s + L, hh], beta[0, s:s + L, hh]
+            Ss = brute_force_states(kk, vv, aa, bb, h0[n, hh])
+            fin = Ss[-1] if L else h0[n, hh]
+            _assert_close(out["hT"][n, j], fin, 1e-12, f"seq {n} head {hh} final")
+            for t in range(L):
+                prev = h0[n, hh] if t == 0 else Ss[t - 1]
+                _assert_close(out["o"][0, s + t, j], scale * Ss[t].T @ q[0, s + t, hh], 1e-12,
+                              f"seq {n} head {hh} o_{t}")
+                _assert_close(out["v_new"][0, s + t, j], bb[t] * (vv[t] - aa[t] * prev.T @ kk[t]), 1e-12,
+                              f"seq {n} head {hh} delta_{t}")
+            for c in range(counts[n]):
+                ref = h0[n, hh] if c == 0 else Ss[c * C - 1]
+                _assert_close(out["h"][offs[n] + c, j], ref, 1e-12, f"seq {n} head {hh} pre-chunk {c}")
+
+
+def check_bwd_wrapper_packed(bwd_ref, gdr_ref, chunked_ref):
+    """gdr_backward_fp64 on packed sequences with a head sample, against
+    finite differences of a linear loss (upstream dO on every output, dhT on
+    every final state) of the packed forward of each sampled head: dh0[n] by
+    perturbing h0[n], dh[row] by restarting sequence n after that chunk, and
+    the write-vector gradient through the chunk form's write vectors."""
+    lengths, H, DK, DV, C, scale = [7, 0, 3, 5], 2, 3, 2, 3, 0.6
+    hs = [1]
+    q, k, v, g, beta, h0, cu = _packed_problem(72, lengths, H, DK, DV)
+    r = np.random.default_rng(73)
+    do = r.standard_normal((1, sum(lengths), H, DV))
+    dhT = r.standard_normal((len(lengths), H, DK, DV))
+    out = bwd_ref.gdr_backward_fp64(q, k, g, beta, do, dhT, cu, scale, chunk=C, heads=hs)
+    counts = [(L + C - 1) // C for L in lengths]
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    assert list(out["chunk_offsets"]) == list(offs), "chunk offsets"
+    hh = hs[0]
+
+    def loss_tail(n, t0, S):
+        """Loss of sequence n's tokens from t0 on, started from S (head hh)."""
+        s, e = int(cu[n]), int(cu[n + 1])
+        sl = slice(s + t0, e)
+        o, _, Sf = gdr_ref.gdr_scan_sequence(q[0, sl][:, [hh]], k[0, sl][:, [hh]], v[0, sl][:, [hh]],
+                                             np.exp(g[0, sl][:, [hh]]), beta[0, sl][:, [hh]], S[None], scale, C)
+        return float(np.sum(o[:, 0] * do[0, sl, hh]) + np.sum(Sf[0] * dhT[n, hh]))
+
+    for n, L in enumerate(lengths):
+        fd0 = _fd(lambda S: loss_tail(n, 0, S), h0[n, hh].copy())
+        _assert_close(out["dh0"][n, 0], fd0, 1e-7, f"seq {n} dh0")
+        for c in range(counts[n]):
+            t0 = (c + 1) * C
+            if t0 >= L:
+                _assert_close(out["dh"][offs[n] + c, 0], dhT[n, hh], 1e-12, f"seq {n} last dh row")
+                continue
+            fd = _fd(lambda S: loss_tail(n, t0, S), np.zeros((DK, DV)))
+            _assert_close(out["dh"][offs[n] + c, 0], fd, 1e-7, f"seq {n} dh row {c}")
+        if L:
+            s, e = int(cu[n]), int(cu[n + 1])
+
+            def loss_shift(shift):
+                rr = chunked_ref.chunked_scan_sequence(q[0, s:e][:, [hh]], k[0, s:e][:, [hh]], v[0, s:e][:, [hh]],
+                                                       g[0, s:e][:, [hh]], beta[0, s:e][:, [hh]], h0[n][[hh]],
+                                                       scale, C, delta_shift=shift)
+                return float(np.sum(rr["o"][:, 0] * do[0, s:e, hh]) + np.sum(rr["hT"][0] * dhT[n, hh]))
+
+            fdv = _fd(loss_shift, np.zeros((L, 1, DV)))
+            _assert_close(out["dv_new"][0, s:e, 0], fdv[:, 0], 1e-7, f"seq {n} dv_new")
+
+
+def _abc_batch(seed, B, T, H, K, M, V):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((B, T, H, K))
+    k = r.standard_normal((B, T, H, K))
+    v = r.standard_normal((B, T, H, V))
+    s = 1.5 * r.standard_normal((B, T, H, M))
+    return q, k, v, s
+
+
+def check_abc_wrapper_sampled(abc_ref):
+    """abc_recurrent_fp64 and abc_forward_fp64 on a batch-row and head sample:
+    every sampled (row, head) equals the closed-form weighted sums of that
+    row's and head's own inputs (normaliser, pre-chunk and final states, the
+    score / softmax / value reads, and the value read with given weights)."""
+    B, T, H, K, M, V, C, scale = 2, 9, 3, 3, 2, 2, 4, 0.8
+    bs, hs = [1, 0], [2, 0]
+    q, k, v, s = _abc_batch(74, B, T, H, K, M, V)
+    p = np.random.default_rng(75).uniform(0.0, 1.0, (B, T, H, M))
+    rec = abc_ref.abc_recurrent_fp64(k, v, s, C, batches=bs, heads=hs)
+    fwd = abc_ref.abc_forward_fp64(q, k, v, s, scale, batches=bs, heads=hs)
+    fwp = abc_ref.abc_forward_fp64(q, k, v, s, scale, p=p, batches=bs, heads=hs)
+    for i, b in enumerate(bs):
+        for j, hh in enumerate(hs):
+            kk, vv, ss, qq = k[b, :, hh], v[b, :, hh], s[b, :, hh], q[b, :, hh]
+            zc = _cum_lse(ss)
+            _assert_close(rec["z"][i, :, j], zc, 1e-13, f"({b},{hh}) z")
+            for c, t0 in enumerate(range(0, T, C)):
+                if t0 == 0:
+                    assert np.all(rec["hk"][i, 0, j] == 0) and np.all(rec["hv"][i, 0, j] == 0)
+                    continue
+                wts = np.exp(ss[:t0] - zc[t0 - 1][None])
+                _assert_close(rec["hk"][i, c, j], kk[:t0].T @ wts, 1e-12, f"({b},{hh}) Hk pre {c}")
+                _assert_close(rec["hv"][i, c, j], wts.T @ vv[:t0], 1e-12, f"({b},{hh}) Hv pre {c}")
+            wts = np.exp(ss - zc[-1][None])
+            _assert_close(rec["hk_final"][i, j], kk.T @ wts, 1e-12, f"({b},{hh}) Hk final")
+            _assert_close(rec["hv_final"][i, j], wts.T @ vv, 1e-12, f"({b},{hh}) Hv final")
+            for t in range(T):
+                wt = np.exp(ss[:t + 1] - zc[t][None])                  # [t+1, M]
+                hk_t, hv_t = kk[:t + 1].T @ wt, wt.T @ vv[:t + 1]
+                sc = scale * hk_t.T @ qq[t]
+                e = np.exp(sc - sc.max())
+                pt = e / e.sum()
+                _assert_close(fwd["p"][i, t, j], pt, 1e-12, f"({b},{hh}) p_{t}")
+                _assert_close(fwd["o"][i, t, j], hv_t.T @ pt, 1e-12, f"({b},{hh}) o_{t}")
+                _assert_close(fwp["o"][i, t, j], hv_t.T @ p[b, t, hh], 1e-12, f"({b},{hh}) o_{t} (given p)")
+
+
+def check_abc_bwd_wrapper_sampled(abc_bwd_ref, abc_ref):
+    """abc_backward_fp64 on a batch-row and head sample: the gradient rows of
+    every sampled (row, head) against finite differences of that row's and
+    head's read-out, resumed after each chunk from a perturbed state
+    (loss: dscore on the scores, dO on the outputs, the final-state gradients
+    on the final states)."""
+    B, T, H, K, M, V, C, scale = 2, 7, 3, 2, 2, 2, 3, 0.7
+    bs, hs = [1, 0], [2]
+    q, k, v, s = _abc_batch(76, B, T, H, K, M, V)
+    r = np.random.default_rng(77)
+    p = r.uniform(0.0, 1.0, (B, T, H, M))
+    dscore = r.standard_normal((B, T, H, M))
+    do = r.standard_normal((B, T, H, V))
+    ek = r.standard_normal((B, H, K, M))
+    ev = r.standard_normal((B, H, M, V))
+    out = abc_bwd_ref.abc_backward_fp64(q, s, p, dscore, do, ek, ev, scale, C, batches=bs, heads=hs)
+    nc = (T + C - 1) // C
+    assert out["dhk"].shape == (len(bs), nc, len(hs), K, M)
+    for i, b in enumerate(bs):
+        for j, hh in enumerate(hs):
+            zc = _cum_lse(s[b, :, [hh]].transpose(1, 0, 2))           # [T, 1, M]
+            for c in range(nc):
+                t0 = (c + 1) * C
+                if t0 >= T:
+                    _assert_close(out["dhk"][i, c, j], ek[b, hh], 1e-12, f"({b},{hh}) dhk after the last chunk")
+                    _assert_close(out["dhv"][i, c, j], ev[b, hh], 1e-12, f"({b},{hh}) dhv after the last chunk")
+                    continue
+                sl = slice(t0, T)
+                sel = lambda x: x[b, sl][:, [hh]]
+
+                def loss(xk, xv):
+                    o = abc_ref.abc_readout_sequence(sel(q), sel(k), sel(v), sel(s), sel(p), scale,
+                                                     xk[None], xv[None], zc[t0 - 1])
+                    return float(np.sum(o["score"] * sel(dscore)) + np.sum(o["o"] * sel(do))
+                                 + np.sum(o["hk_final"][0] * ek[b, hh]) + np.sum(o["hv_final"][0] * ev[b, hh]))
+
+                zk, zv = np.zeros((K, M)), np.zeros((M, V))
+                _assert_close(out["dhk"][i, c, j], _fd(lambda x: loss(x, zv), zk), 1e-7, f"({b},{hh}) dhk[{c}]")
+                _assert_close(out["dhv"][i, c, j], _fd(lambda x: loss(zk, x), zv), 1e-7, f"({b},{hh}) dhv[{c}]")
+
+
+GDR_CHECKS.append(check_wrapper_packed_heads)
+ABC_CHECKS.append(check_abc_wrapper_sampled)
+BWD_CHECKS.append(check_bwd_wrapper_packed)
+ABC_BWD_CHECKS.append(check_abc_bwd_wrapper_sampled)

@@ -39,6 +39,10 @@ GDR_MUTANTS = {
     "compose_drop_local": ("S = np.matmul(M[s], S) + S_loc[s]", "S = np.matmul(M[s], S)"),
     "segment_extra_to_last": ("nc = base + (1 if s < extra else 0)",
                               "nc = base + (1 if s >= n_segments - extra else 0)"),
+    # batch wrapper: packing and head sampling
+    "wrapper_h0_unsampled": ("np.array(h0[n][hs], dtype=np.float64)", "np.array(h0[n][:Hs], dtype=np.float64)"),
+    "wrapper_beta_unsampled": ("beta[b, s:e][:, hs], S0, scale", "beta[b, s:e][:, :Hs], S0, scale"),
+    "wrapper_h_rows_by_sequence": ("h[offsets[n]:offsets[n + 1]] = pre", "h[n:n + len(pre)] = pre"),
 }
 
 
@@ -84,6 +88,11 @@ ABC_MUTANTS = {
     "read_softmax_unnormalised": ("pw[t] = e / e.sum(axis=-1, keepdims=True)", "pw[t] = e"),
     "read_query_for_key": ('score[t] = scale * np.einsum("hkm,hk->hm", Hk, q[t])',
                            'score[t] = scale * np.einsum("hkm,hk->hm", Hk, k[t])'),
+    # batch wrappers: row and head sampling
+    "wrapper_logits_unsampled": ("s[b][:, hs], chunk) for b in bs]", "s[b][:, :len(hs)], chunk) for b in bs]"),
+    "wrapper_read_weights_unsampled": ("np.asarray(p[b], dtype=np.float64)[:, hs]",
+                                       "np.asarray(p[b], dtype=np.float64)[:, :len(hs)]"),
+    "wrapper_read_query_of_first_row": ("abc_readout_sequence(q[b][:, hs]", "abc_readout_sequence(q[bs[0]][:, hs]"),
 }
 
 
@@ -111,6 +120,12 @@ BWD_MUTANTS = {
     "bwd_dv_untransposed": ("scale * (P.T @ dd)", "scale * (P @ dd)"),
     "bwd_dv_no_decay": ("np.exp(ga[-1] - ga)[:, None] * (kk @ dh[c, hh])", "(kk @ dh[c, hh])"),
     "bwd_dv_wrong_boundary": ("(kk @ dh[c, hh])", "(kk @ dh[max(c - 1, 0), hh])"),
+    # batch wrapper: packing, final-gradient rows and head sampling
+    "bwd_wrapper_dhT_first_sequence": ("np.array(dhT[n][hs], dtype=np.float64)",
+                                       "np.array(dhT[0][hs], dtype=np.float64)"),
+    "bwd_wrapper_dhT_unsampled": ("np.array(dhT[n][hs], dtype=np.float64)", "np.array(dhT[n][:Hs], dtype=np.float64)"),
+    "bwd_wrapper_do_unsampled": ("do[b, s:e][:, hs], dS_end", "do[b, s:e][:, :Hs], dS_end"),
+    "bwd_wrapper_dh_rows_by_sequence": ('out["dh"][offsets[n]:offsets[n + 1]] = dh', 'out["dh"][n:n + len(dh)] = dh'),
 }
 
 
@@ -144,6 +159,12 @@ ABC_BWD_MUTANTS = {
                                   "Gv = cv + dscore[t][:, :, None] * do[t][:, None, :]"),
     "abc_bwd_value_ratio_on_columns": ("cv = Gv * r[:, :, None]", "cv = Gv * r[:, :1, None]"),
     "abc_bwd_key_ratio_on_rows": ("ck = Gk * r[:, None, :]", "ck = Gk * r[:, :1, None]"),
+    # batch wrapper: final-gradient rows and head sampling
+    "abc_bwd_wrapper_final_unsampled": ("np.asarray(dhk_final[b], dtype=np.float64)[hs]",
+                                        "np.asarray(dhk_final[b], dtype=np.float64)[:len(hs)]"),
+    "abc_bwd_wrapper_weights_unsampled": ("p[b][:, hs], dscore[b]", "p[b][:, :len(hs)], dscore[b]"),
+    "abc_bwd_wrapper_final_first_row": ("np.asarray(dhv_final[b], dtype=np.float64)[hs]",
+                                        "np.asarray(dhv_final[bs[0]], dtype=np.float64)[hs]"),
 }
 
 
