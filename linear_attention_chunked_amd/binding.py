@@ -171,6 +171,8 @@ class Problem:
         idx_ptr = None
         if state_indices is not None:
             idx = [int(x) for x in (state_indices.tolist() if torch.is_tensor(state_indices) else state_indices)]
+            if len(idx) != N:
+                raise ValueError(f"state_indices has {len(idx)} entries for {N} sequences")
             self._idx = (ctypes.c_int32 * max(1, len(idx)))(*idx)
             idx_ptr = self._idx
         self.s = gdr_problem(B, T, H, DK, DV, N, cu_ptr, _dtype_code(k.dtype),
@@ -180,6 +182,26 @@ class Problem:
     @property
     def ref(self):
         return ctypes.byref(self.s)
+
+
+def _pool_size(h0, hT, k, DV, state_layout) -> int:
+    """Entries of the state pools h0 / hT addressed by state_indices: each
+    given pool must be a float32 [pool_size, H, DK, DV] (or [.., DV, DK] for
+    the "vk" layout) tensor; with two pools of different sizes the smaller
+    bounds the indices, so no index can reach past either pool."""
+    H, DK = k.shape[2], k.shape[3]
+    state = (H, DV, DK) if state_layout == "vk" else (H, DK, DV)
+    sizes = []
+    for name, t in (("h0", h0), ("hT", hT)):
+        if t is None:
+            continue
+        if t.dtype != torch.float32 or t.dim() != 4 or tuple(t.shape[1:]) != state:
+            raise ValueError(f"state pool {name} must be float32 [pool_size, {state[0]}, {state[1]}, {state[2]}], "
+                             f"got {t.dtype} {tuple(t.shape)}")
+        sizes.append(int(t.shape[0]))
+    if not sizes:
+        raise ValueError("indexed states need a pool (h0 or hT)")
+    return min(sizes)
 
 
 def _tile(tile) -> Optional[gdr_tile]:
@@ -232,8 +254,7 @@ def gdr_state_scan(k, w, u, g_cum, h0=None, cu_seqlens=None, tile=None, n_segmen
     if state_indices is not None:
         if emit_final and out.get("hT") is None:
             raise ValueError("indexed states write into a pool: pass out={'hT': pool}")
-        pool = h0 if h0 is not None else out.get("hT")
-        pool_size = int(pool.shape[0]) if pool is not None else 0
+        pool_size = _pool_size(h0, out.get("hT") if emit_final else None, k, DV, state_layout)
     p = Problem(k, DV, cu_seqlens, state_layout, state_indices, pool_size)
     L = lib()
     nt = gdr_num_chunks(k, DV, cu_seqlens)
@@ -277,8 +298,7 @@ def gdr_state_scan_output(q, k, w, u, g_cum, scale: float = 1.0, h0=None, cu_seq
     if state_indices is not None:
         if emit_final and out.get("hT") is None:
             raise ValueError("indexed states write into a pool: pass out={'hT': pool}")
-        pool = h0 if h0 is not None else out.get("hT")
-        pool_size = int(pool.shape[0]) if pool is not None else 0
+        pool_size = _pool_size(h0, out.get("hT") if emit_final else None, k, DV, state_layout)
     p = Problem(k, DV, cu_seqlens, state_layout, state_indices, pool_size)
     nt = gdr_num_chunks(k, DV, cu_seqlens)
     o = out.get("o")

@@ -302,3 +302,27 @@ def test_fused_scan_output_validation():
     assert _scan_out(p, tile=(32, 2, 2), h=FAKE) == B.GDR_ERR_UNSUPPORTED
     pool, keepp = _pool_prob([3, 0, 2], 4)
     assert _scan_out(pool, seg=B.gdr_segments(2, FAKE.value)) == B.GDR_ERR_UNSUPPORTED
+
+
+def test_binding_rejects_mismatched_state_pools():
+    """The Python binding checks the state pools before any call: the index
+    list must have one entry per sequence, each pool must be float32 with the
+    state's shape, and with two pools the smaller bounds the indices."""
+    import torch
+
+    k = torch.zeros((1, 20, 2, 128), dtype=torch.bfloat16)
+    w, u = torch.zeros_like(k), torch.zeros((1, 20, 2, 128), dtype=torch.bfloat16)
+    g = torch.zeros((1, 20, 2))
+    cu = [0, 5, 12, 20]
+    pool = torch.zeros((4, 2, 128, 128))
+    with pytest.raises(ValueError, match="entries for 3 sequences"):
+        B.gdr_state_scan(k, w, u, g, pool, cu, out={"hT": pool}, state_indices=[0, 1])
+    with pytest.raises(ValueError, match="float32"):
+        B.gdr_state_scan(k, w, u, g, pool, cu, out={"hT": pool.to(torch.bfloat16)}, state_indices=[0, 1, 2])
+    with pytest.raises(ValueError, match="float32"):
+        B.gdr_state_scan_output(k, k, w, u, g, 1.0, pool[:, :1], cu, out={"hT": pool}, state_indices=[0, 1, 2])
+    small = torch.zeros((2, 2, 128, 128))
+    assert B._pool_size(pool, small, k, 128, "kv") == 2
+    assert B._pool_size(None, pool, k, 128, "kv") == 4
+    with pytest.raises(ValueError):
+        B._pool_size(torch.zeros((4, 2, 64, 128)), None, k, 128, "kv")

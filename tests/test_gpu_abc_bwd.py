@@ -10,6 +10,8 @@ import pytest
 import torch
 
 import oracle
+import oracle_pool
+from parity import per_row_head_max, rel
 from workloads import make_abc, make_config
 
 pytestmark = pytest.mark.gpu
@@ -25,12 +27,6 @@ def pkg():
 
     p.lib()
     return p
-
-
-def rel(a, b):
-    a = np.asarray(a, dtype=np.float64)
-    b = np.asarray(b, dtype=np.float64)
-    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
 def upstream(inp, seed, with_end=True):
@@ -62,25 +58,22 @@ def run_bwd(pkg, inp, up, scale):
     return dhk, dhv
 
 
-def check(pkg, inp, up, scale, batches=None, heads=None, what=""):
+def check(pkg, inp, up, scale, pool=False, what=""):
+    """Every (batch row, head) against the oracle (``pool``: in worker
+    processes, one per (row, head)), whole tensors and per slice."""
     dhk, dhv = run_bwd(pkg, inp, up, scale)
     q, p, ds, do, ek, ev = up
     f = lambda t: None if t is None else t.to(torch.float64).numpy()
-    ref = oracle.abc_backward_fp64(f(q), inp.s.to(torch.float64).numpy(), f(p), f(ds), f(do), f(ek), f(ev), scale,
-                                   batches=batches, heads=heads)
-
-    def pick(t):
-        x = t.detach().to(torch.float64).cpu().numpy()
-        if batches is not None:
-            x = np.take(x, batches, axis=0)
-        if heads is not None:
-            x = np.take(x, heads, axis=2)
-        return x
-
-    errs = {"dhk": rel(pick(dhk), ref["dhk"]), "dhv": rel(pick(dhv), ref["dhv"])}
-    print(what, " ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+    args = (f(q), inp.s.to(torch.float64).numpy(), f(p), f(ds), f(do), f(ek), f(ev), scale)
+    ref = oracle_pool.abc_backward_all(*args) if pool else oracle.abc_backward_fp64(*args)
+    got = {"dhk": dhk.detach().to(torch.float64).cpu().numpy(), "dhv": dhv.detach().to(torch.float64).cpu().numpy()}
+    errs = {k: rel(got[k], ref[k]) for k in got}
+    worst = per_row_head_max({k: (got[k], ref[k], 2) for k in got})
+    print(what, " ".join(f"{k}={v:.3e}" for k, v in errs.items()), "| per (row, head) max:",
+          " ".join(f"{k}={v[0]:.3e}@{v[1:]}" for k, v in worst.items()), flush=True)
     for key, e in errs.items():
         assert e <= TOL, f"{what} {key}: rel-L2 {e:.3e}"
+        assert worst[key][0] <= TOL, f"{what} {key}: {worst[key]}"
     return dhk, dhv
 
 
@@ -117,9 +110,9 @@ def test_abc_bwd_runs(pkg, monkeypatch, runs):
 
 def test_abc_bwd_benchmark_shape(pkg):
     """B=2, T=16384, H=4, K=256, M=64, V=512 (eight runs by default), against
-    the oracle on batch row 1, heads 0 and 3; deterministic run to run."""
+    the oracle on every (batch row, head); deterministic run to run."""
     inp = make_config("abc_affine")
     up = upstream(inp, 989)
-    a = check(pkg, inp, up, 1.0, batches=[1], heads=[0, 3], what="abc bwd abc_affine b1 h0,3")
+    a = check(pkg, inp, up, 1.0, pool=True, what="abc bwd abc_affine (all rows and heads)")
     b = run_bwd(pkg, inp, up, 1.0)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

@@ -10,6 +10,8 @@ import pytest
 import torch
 
 import oracle
+import oracle_pool
+from parity import per_row_head_max, rel
 from workloads import make_abc, make_config
 
 pytestmark = pytest.mark.gpu
@@ -27,36 +29,27 @@ def pkg():
     return p
 
 
-def rel(a, b):
-    a = np.asarray(a, dtype=np.float64)
-    b = np.asarray(b, dtype=np.float64)
-    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
-
-
 def queries(inp, seed):
     r = np.random.default_rng(seed)
     return torch.from_numpy(r.standard_normal(tuple(inp.k.shape)).astype(np.float32)).to(torch.bfloat16)
 
 
-def check(pkg, inp, q, scale, batches=None, heads=None, what=""):
+def check(pkg, inp, q, scale, pool=False, what=""):
+    """Every (batch row, head) against the oracle (``pool``: in worker
+    processes, one per (row, head)), whole tensors and per slice."""
     o, p, _, _, _ = pkg.abc_forward(q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.s.cuda(), scale, emit_p=True)
     torch.cuda.synchronize()
     d = inp.f64()
-    ref = oracle.abc_forward_fp64(q.to(torch.float64).numpy(), d["k"], d["v"], d["s"], scale,
-                                  batches=batches, heads=heads)
-
-    def pick(t):
-        x = t.detach().to(torch.float64).cpu().numpy()
-        if batches is not None:
-            x = np.take(x, batches, axis=0)
-        if heads is not None:
-            x = np.take(x, heads, axis=2)
-        return x
-
-    errs = {"o": rel(pick(o), ref["o"]), "p": rel(pick(p), ref["p"])}
-    print(what, " ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+    args = (q.to(torch.float64).numpy(), d["k"], d["v"], d["s"], scale)
+    ref = oracle_pool.abc_read_all(*args) if pool else oracle.abc_forward_fp64(*args)
+    got = {"o": o.detach().to(torch.float64).cpu().numpy(), "p": p.detach().to(torch.float64).cpu().numpy()}
+    errs = {k: rel(got[k], ref[k]) for k in got}
+    worst = per_row_head_max({k: (got[k], ref[k], 2) for k in got})
+    print(what, " ".join(f"{k}={v:.3e}" for k, v in errs.items()), "| per (row, head) max:",
+          " ".join(f"{k}={v[0]:.3e}@{v[1:]}" for k, v in worst.items()), flush=True)
     for key, e in errs.items():
         assert e <= TOL, f"{what} {key}: rel-L2 {e:.3e}"
+        assert worst[key][0] <= TOL, f"{what} {key}: {worst[key]}"
     return o, p
 
 
@@ -70,10 +63,10 @@ def test_abc_read_parity(pkg, shape):
 
 
 def test_abc_read_benchmark_shape(pkg):
-    """B=2, T=16384, H=4, K=256, M=64, V=512 against the oracle on batch row 0,
-    heads 1 and 2; deterministic run to run."""
+    """B=2, T=16384, H=4, K=256, M=64, V=512 against the oracle on every
+    (batch row, head); deterministic run to run."""
     inp = make_config("abc_affine")
     q = queries(inp, 992)
-    a = check(pkg, inp, q, 256 ** -0.5, batches=[0], heads=[1, 2], what="abc read abc_affine b0 h1,2")
+    a = check(pkg, inp, q, 256 ** -0.5, pool=True, what="abc read abc_affine (all rows and heads)")
     o2, p2, _, _, _ = pkg.abc_forward(q.cuda(), inp.k.cuda(), inp.v.cuda(), inp.s.cuda(), 256 ** -0.5, emit_p=True)
     assert torch.equal(a[0], o2) and torch.equal(a[1], p2)

@@ -10,6 +10,8 @@ import pytest
 import torch
 
 import oracle
+import oracle_pool
+from parity import gate, per_sequence_max, rel
 from workloads import make_config, make_gdr
 
 pytestmark = pytest.mark.gpu
@@ -25,12 +27,6 @@ def pkg():
 
     p.lib()
     return p
-
-
-def rel(a, b):
-    a = np.asarray(a, dtype=np.float64)
-    b = np.asarray(b, dtype=np.float64)
-    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
 def grads(inp, seed, with_dhT=True):
@@ -58,23 +54,23 @@ def run_bwd(pkg, inp, dO, dhT, scale, state_layout="kv"):
     return {"dh": dh, "dv": dv, "dh0": dh0, "dvl": dvl}
 
 
-def check(pkg, inp, dO, dhT, scale, heads=None, state_layout="kv", what=""):
+def check(pkg, inp, dO, dhT, scale, state_layout="kv", what=""):
+    """Every head against the oracle (a pool of worker processes over groups
+    of heads for the named workloads), whole tensors and per (sequence, head)."""
     r = run_bwd(pkg, inp, dO, dhT, scale, state_layout)
     d = inp.f64()
-    ref = oracle.gdr_backward_fp64(d["q"], d["k"], d["g"], d["beta"], dO.to(torch.float64).numpy(),
-                                   None if dhT is None else dhT.to(torch.float64).numpy(), d["cu_seqlens"], scale,
-                                   heads=heads)
+    args = (d["q"], d["k"], d["g"], d["beta"], dO.to(torch.float64).numpy(),
+            None if dhT is None else dhT.to(torch.float64).numpy(), d["cu_seqlens"], scale)
+    ref = oracle.gdr_backward_fp64(*args) if inp.name == "custom" else oracle_pool.gdr_backward_all_heads(*args)
 
-    def pick(t, hdim):
-        x = t.detach().to(torch.float64).cpu()
-        return (x if heads is None else x.index_select(hdim, torch.tensor(heads))).numpy()
+    def np64(t):
+        return t.detach().to(torch.float64).cpu().numpy()
 
-    errs = {"dh": rel(np.swapaxes(pick(r["dh"], 1), -1, -2), ref["dh"]),
-            "dv_new": rel(pick(r["dv"], 2), ref["dv_new"]),
-            "dh0": rel(pick(r["dh0"], 1), ref["dh0"])}
-    print(what, " ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
-    for key, e in errs.items():
-        assert e <= TOL, f"{what} {key}: rel-L2 {e:.3e}"
+    got = {"dh": np.swapaxes(np64(r["dh"]), -1, -2), "dv_new": np64(r["dv"]), "dh0": np64(r["dh0"])}
+    errs = {k: rel(got[k], ref[k]) for k in got}
+    kinds = {"dh": "chunk", "dv_new": "token", "dh0": "seq"}
+    worst = per_sequence_max({k: (got[k], ref[k], kinds[k]) for k in kinds}, d["cu_seqlens"], ref["chunk_offsets"])
+    gate(errs, worst, TOL, what)
     return r
 
 
@@ -104,7 +100,7 @@ def test_backward_no_final_gradient_and_vk_layout(pkg):
 def test_backward_question_rows_workload(pkg):
     inp = make_config("question_rows")
     dO, dhT = grads(inp, 852)
-    check(pkg, inp, dO, dhT, 1.0, heads=[0, 7, 15], what="bwd question_rows heads 0,7,15")
+    check(pkg, inp, dO, dhT, 1.0, what="bwd question_rows (all 16 heads)")
 
 
 def test_backward_long_state_h1(pkg):

@@ -173,6 +173,12 @@ def make_gdr(seed: int, *, lengths: Optional[Sequence[int]] = None, B: int = 1, 
         # per-key-channel decays: every (token, head, channel) its own logsigmoid(N(4, 1))
         beta = _sigmoid(rng.standard_normal((B, T, H)))
         g = _logsigmoid(rng.normal(4.0, 1.0, (B, T, H, DK)))
+    elif gates == "channels_to_limit":
+        # per-channel log decays across the whole supported range [-5, 0): U(-5, 0)
+        # per (token, head, channel), every fourth channel at exactly -5
+        beta = _sigmoid(rng.standard_normal((B, T, H)))
+        g = -5.0 * rng.uniform(0.0, 1.0, (B, T, H, DK))
+        g[..., ::4] = -5.0
     elif gates in ("logsigmoid_mid", "logsigmoid_fast"):
         beta = _sigmoid(rng.standard_normal((B, T, H)))
         mu, sd = (2.5, 0.3) if gates == "logsigmoid_mid" else (-1.0, 1.0)
