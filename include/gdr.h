@@ -37,7 +37,10 @@
  *    return nothing has been enqueued and no output was written.
  *    gdr_last_error() gives a message for the calling thread.
  *  - No C++ exception crosses the ABI; the library holds no mutable global
- *    state, so concurrent calls from several threads are safe.
+ *    state (apart from the per-device address of the static scratch of
+ *    gdr_segment_summaries_noalloc, looked up once under a lock), so
+ *    concurrent calls from several threads are safe (that entry point's
+ *    calls on one GPU excepted: they share its scratch).
  *  - Layouts are contiguous, time-major ("public layout", [fla#23] fixture
  *    contract):
  *        q, k, w            [B, T, H, DK]   storage dtype
@@ -218,6 +221,24 @@ gdr_status gdr_segment_summaries_ws(const gdr_problem* p, const gdr_tile* tile, 
                                     const void* k, const void* w, const void* u,
                                     const float* g_cum, float* seg_state, float* seg_trans,
                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* gdr_segment_summaries_ws for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the half-segment workspace is a static device array inside the
+ * library, GDR_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.
+ * The call allocates nothing.  Same arguments (less the workspace), outputs
+ * and results as gdr_segment_summaries_ws given a workspace of
+ * gdr_segment_summaries_workspace_size bytes; a problem that needs more than
+ * GDR_NOALLOC_SCRATCH_BYTES returns GDR_ERR_INVALID_ARG before any launch
+ * (64K tokens x 8 heads x 16 segments at DK = DV = 128 needs 32 MiB; with
+ * 16 segments of one 64K sequence up to 12 heads fit).
+ * Every call on one GPU uses that GPU's one array: calls that overlap on the
+ * same GPU (other streams, other threads) race and must be serialised by the
+ * caller.  The array holds nothing a later call relies on. */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+gdr_status gdr_segment_summaries_noalloc(const gdr_problem* p, const gdr_tile* tile, int32_t n_segments,
+                                         const void* k, const void* w, const void* u, const float* g_cum,
+                                         float* seg_state, float* seg_trans, void* stream);
 
 /* Segment composition ([cuLA#127] "Root cause and implementation"), in FP32,
  * serially over the segments of each sequence:

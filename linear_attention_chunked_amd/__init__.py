@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     gdr_plan_query,
     gdr_segment_compose,
     gdr_segment_summaries,
+    gdr_segment_summaries_noalloc,
     gdr_segment_summaries_workspace_size,
     gdr_state_scan,
     gdr_state_scan_output,

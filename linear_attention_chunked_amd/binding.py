@@ -80,6 +80,8 @@ _SIGS = {
     "gdr_segment_summaries_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(gdr_problem), ctypes.c_int32]),
     "gdr_segment_summaries_ws": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile),
                                                 ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "gdr_segment_summaries_noalloc": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile),
+                                                     ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]),
     "gdr_segment_compose": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
     "kda_chunk_prepare": (ctypes.c_int, [ctypes.POINTER(gdr_problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "kda_state_scan": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile),
@@ -363,6 +365,27 @@ def gdr_segment_summaries(k, w, u, g_cum, n_segments: int, cu_seqlens=None, tile
     else:
         _check(L.gdr_segment_summaries(p.ref, tp, n_segments, _ptr(k), _ptr(w), _ptr(u), _ptr(g_cum),
                                        _ptr(seg_state), _ptr(seg_trans), _stream(stream)), "gdr_segment_summaries")
+    return seg_state, seg_trans
+
+
+def gdr_segment_summaries_noalloc(k, w, u, g_cum, n_segments: int, cu_seqlens=None, tile=None, out=None,
+                                  stream=None):
+    """gdr_segment_summaries with the library's static scratch as the
+    half-segment workspace (the C call allocates nothing).  ``out`` may hold
+    preallocated "seg_state" and "seg_trans".  Returns (seg_state, seg_trans)."""
+    DV = u.shape[-1]
+    p = Problem(k, DV, cu_seqlens)
+    out = out or {}
+    seg_state = out.get("seg_state")
+    if seg_state is None:
+        seg_state = torch.empty((p.N * n_segments, p.H, DV, p.DK), dtype=torch.float32, device=k.device)
+    seg_trans = out.get("seg_trans")
+    if seg_trans is None:
+        seg_trans = torch.empty((p.N * n_segments, p.H, p.DK, p.DK), dtype=torch.float32, device=k.device)
+    t = _tile(tile)
+    _check(lib().gdr_segment_summaries_noalloc(p.ref, ctypes.byref(t) if t is not None else None, n_segments,
+                                               _ptr(k), _ptr(w), _ptr(u), _ptr(g_cum), _ptr(seg_state),
+                                               _ptr(seg_trans), _stream(stream)), "gdr_segment_summaries_noalloc")
     return seg_state, seg_trans
 
 

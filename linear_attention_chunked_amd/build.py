@@ -29,7 +29,7 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
 ]
-SOURCES = ["scan.hip", "scan2.hip", "prepare.hip", "prepare2.hip", "output.hip", "output2.hip", "compose.hip", "abc.hip", "abc_out.hip", "kda.hip", "scan_bwd.hip", "plan.cpp", "api.cpp", "abc_api.cpp"]
+SOURCES = ["scan.hip", "scan2.hip", "prepare.hip", "prepare2.hip", "output.hip", "output2.hip", "compose.hip", "abc.hip", "abc_out.hip", "kda.hip", "scan_bwd.hip", "plan.cpp", "api.cpp", "abc_api.cpp", "noalloc.hip"]
 
 
 def _compile(src: str) -> str:

@@ -326,3 +326,19 @@ def test_binding_rejects_mismatched_state_pools():
     assert B._pool_size(None, pool, k, 128, "kv") == 4
     with pytest.raises(ValueError):
         B._pool_size(torch.zeros((4, 2, 64, 128)), None, k, 128, "kv")
+
+
+def test_noalloc_summaries_reject_oversized_problems():
+    """gdr_segment_summaries_noalloc refuses, before any device call, a
+    problem whose half-segment workspace exceeds the static scratch."""
+    L = B.lib()
+    cu = (ctypes.c_int32 * 2)(0, 65536)
+    # 64K tokens x 13 heads x 16 segments: 2 * 16 * 13 * 128 * 256 * 4 bytes = 52 MiB > 48 MiB
+    p = B.gdr_problem(1, 65536, 13, 128, 128, 1, cu, B.GDR_BF16, 0, None, 0)
+    assert L.gdr_segment_summaries_workspace_size(ctypes.byref(p), 16) == 52 << 20
+    s = L.gdr_segment_summaries_noalloc(ctypes.byref(p), None, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert s == B.GDR_ERR_INVALID_ARG
+    assert "static scratch" in L.gdr_last_error().decode()
+    bad = B.gdr_problem(1, 65536, 17, 128, 128, 1, cu, B.GDR_BF16, 0, None, 0)
+    assert L.gdr_segment_summaries_noalloc(ctypes.byref(bad), None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           None) == B.GDR_ERR_INVALID_ARG
