@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-EV_EVERY = 8
+ROOF_REPS = 30
 BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -132,6 +132,26 @@ class HipEvent:
             HipEvent._hip.hipEventDestroy(self.ev)
 
 
+class Evictor:
+    """Evicts L2 and the 256 MB Infinity Cache between timed launches: a fill
+    of a 1 GiB scratch buffer, then a read of another 1 GiB buffer, so that
+    the caches hold only unrelated, clean lines when the timed kernel starts
+    (the lines the fill leaves behind would otherwise be written back to HBM
+    while the timed kernel runs)."""
+
+    what = "a 1 GiB fill, then a 1 GiB read of another buffer"
+
+    def __init__(self, torch, dev):
+        self.torch = torch
+        self.a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        self.b = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        self.s = torch.empty((), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.a.fill_(1.0)
+        self.torch.sum(self.b, dim=0, out=self.s)
+
+
 def cpu_baseline(inp):
     """The FP64 oracle on the same batch, on the host cores."""
     import oracle
@@ -148,7 +168,36 @@ def cpu_baseline(inp):
         "kind": "oracle",
         "sample": f"the whole {inp.name} batch ({inp.N} sequences, {sum(inp.lengths)} tokens x {inp.H} heads), "
                   f"token-serial FP64 numpy; {wall:.2f} s wall, {cpu:.2f} s CPU",
+        "host": host_info(),
     }
+
+
+def host_info():
+    """The host the CPU baseline ran on: logical cores (os.cpu_count()), the
+    cores this process may use, the CPU model and the BLAS thread pools numpy
+    would use (the oracle's token loop itself is serial numpy)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = [{"api": d.get("internal_api"), "threads": d.get("num_threads")} for d in threadpool_info()]
+    except Exception:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_count": os.cpu_count(), "usable_cores": usable, "cpu_model": model, "blas_threads": blas,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
 def main():
@@ -157,7 +206,6 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="question_rows", choices=["question_rows", "new_states"])
-    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-state", action="store_true")
     ap.add_argument("--sweep", action="store_true",
@@ -218,25 +266,53 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # The roofline kernel is timed by a pair of HIP events around it on every
-    # EV_EVERY-th timed step: event records cost the stream several us each,
-    # so an event pair in every step would depress the step rate itself.
-    evs = {i: (HipEvent(), HipEvent()) for i in range(0, args.steps, EV_EVERY)}
-    torch.cuda.synchronize()
+    # the timed region: K steps back to back, no events inside
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs.get(i))
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    scan_ms = sorted(a.elapsed_ms(b) for a, b in evs.values())
-    scan_mean_ms = sum(scan_ms) / len(scan_ms)
     ms_per_step = elapsed * 1e3 / args.steps
     value = inp.token_heads / (elapsed / args.steps) / 1e6
 
     in_bytes = 2 if inp.dtype == torch.bfloat16 else 4
     alg = fused_alg_bytes(inp.lengths, inp.H, inp.DK, DV, in_bytes, in_bytes, h0 is not None, True)
-    achieved = alg / (scan_mean_ms * 1e-3) / 1e9
+    flops = fused_flops(inp.lengths, inp.H, inp.DK, DV)
     tile = pkg.gdr_plan_query(k, DV, cu)
+
+    # The roofline kernel (the fused scan) after the timed region, over
+    # ROOF_REPS dedicated steps each, with a pair of HIP events on the launch
+    # stream around the kernel alone:
+    #   cold: before every step the caches are evicted (evict_caches(), outside
+    #         the events), so the step's inputs come from HBM, as when the
+    #         question rows arrive from elsewhere; this is the headline figure;
+    #   warm: steps back to back (inputs and part of the outputs still in the
+    #         256 MB Infinity Cache from the previous step).
+    flush = Evictor(torch, dev)
+    cold_k, cold_s, warm_k = [], [], []
+    for i in range(ROOF_REPS + 3):
+        flush()
+        e, s0, s1 = (HipEvent(), HipEvent()), HipEvent(), HipEvent()
+        s0.record(stream)
+        step(e)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 3:
+            cold_k.append(e[0].elapsed_ms(e[1]))
+            cold_s.append(s0.elapsed_ms(s1))
+    evs = [(HipEvent(), HipEvent()) for _ in range(ROOF_REPS)]
+    for _ in range(3):
+        step()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    warm_k = [a.elapsed_ms(b) for a, b in evs]
+    cold_k.sort()
+    warm_k.sort()
+    cold_mean = sum(cold_k) / len(cold_k)
+    warm_mean = sum(warm_k) / len(warm_k)
+    achieved = alg / (cold_mean * 1e-3) / 1e9
+    warm_achieved = alg / (warm_mean * 1e-3) / 1e9
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 1),
@@ -247,57 +323,54 @@ def main():
         "kernel": f"gdr state scan with the chunk output fused (bv={tile[0]}, waves={tile[1]}, stages={tile[2]}, "
                   f"{tile[3]} workgroups)",
         "alg_bytes_per_launch": alg,
-        "launch_us_mean": round(scan_mean_ms * 1e3, 2),
-        "launch_us_median": round(scan_ms[len(scan_ms) // 2] * 1e3, 2),
-        "launch_us_stats": _stats_us(scan_ms),
-        "launch_us_sampled": f"every {EV_EVERY}th timed step ({len(scan_ms)} of {args.steps})",
-        "mfma_frac": round(fused_flops(inp.lengths, inp.H, inp.DK, DV) / (scan_mean_ms * 1e-3) / 1e12
-                           / BF16_PEAK_TFLOPS, 4),
+        "cache": f"cold: {flush.what} before each of {ROOF_REPS} dedicated steps, outside the events",
+        "launch_us_mean": round(cold_mean * 1e3, 2),
+        "launch_us_median": round(cold_k[len(cold_k) // 2] * 1e3, 2),
+        "launch_us_stats": _stats_us(cold_k),
+        "step_us_median": round(sorted(cold_s)[len(cold_s) // 2] * 1e3, 2),
+        "mfma_frac": round(flops / (cold_mean * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "warm": {"launch_us_mean": round(warm_mean * 1e3, 2), "launch_us_stats": _stats_us(warm_k),
+                 "achieved": round(warm_achieved, 1), "frac": round(warm_achieved / HBM_PEAK_GBS, 4),
+                 "cache": f"{ROOF_REPS} steps back to back after 3 more (part of the working set stays in the "
+                          "256 MB Infinity Cache)"},
     }
 
     # The state scan alone (gdr_state_scan, the unfused kernel, same outputs
-    # but o), after the timed region: 30 launches through the C ABI into the
-    # same buffers, each between a pair of HIP events on the launch stream.
+    # but o): cold (caches evicted before each launch) and warm (back to
+    # back), ROOF_REPS launches each between a pair of HIP events.
     def scan_alone(ev):
         ev[0].record(stream)
         B._check(L.gdr_state_scan(P.ref, None, None, ptr(k), ptr(w), ptr(u), ptr(g_cum), ptr(h0), ptr(h),
                                   ptr(v_new), ptr(hT), s_ptr), "scan")
         ev[1].record(stream)
 
+    sa_alg = scan_alg_bytes(inp.lengths, inp.H, inp.DK, DV, in_bytes, in_bytes, h0 is not None, True)
+    cold_sa = []
+    for i in range(ROOF_REPS + 3):
+        flush()
+        B._check(L.gdr_chunk_prepare(P.ref, ptr(k), ptr(v), ptr(g), ptr(beta), ptr(g_cum), ptr(w), ptr(u), s_ptr),
+                 "prepare")
+        e = (HipEvent(), HipEvent())
+        scan_alone(e)
+        torch.cuda.synchronize()
+        if i >= 3:
+            cold_sa.append(e[0].elapsed_ms(e[1]) * 1e3)
     for _ in range(5):
         scan_alone((HipEvent(), HipEvent()))
-    sa = [(HipEvent(), HipEvent()) for _ in range(30)]
+    sa = [(HipEvent(), HipEvent()) for _ in range(ROOF_REPS)]
     for ev in sa:
         scan_alone(ev)
     torch.cuda.synchronize()
     sa_us = sorted(a.elapsed_ms(b) * 1e3 for a, b in sa)
-    sa_alg = scan_alg_bytes(inp.lengths, inp.H, inp.DK, DV, in_bytes, in_bytes, h0 is not None, True)
-    roofline["state_scan_alone"] = {"launch_us_median": round(sa_us[len(sa_us) // 2], 2),
-                                    "alg_bytes_per_launch": sa_alg,
-                                    "frac": round(sa_alg / (sa_us[len(sa_us) // 2] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-
-    # Cold-cache figures (after the timed region): before every rep a 1 GiB
-    # fill evicts L2 and the 256 MB Infinity Cache (the step's 169 MB of fused
-    # scan traffic would otherwise partly stay resident between back-to-back steps).
-    if not args.no_cold:
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        cold_scan, cold_step = [], []
-        for _ in range(20):
-            flush.fill_(1.0)
-            e = (HipEvent(), HipEvent())
-            s0, s1 = HipEvent(), HipEvent()
-            s0.record(stream)
-            step(e)
-            s1.record(stream)
-            torch.cuda.synchronize()
-            cold_scan.append(e[0].elapsed_ms(e[1]) * 1e3)
-            cold_step.append(s0.elapsed_ms(s1) * 1e3)
-        del flush
-        cs = sorted(cold_scan)[len(cold_scan) // 2]
-        roofline["cold_cache"] = {"scan_us_median": round(cs, 2),
-                                  "step_us_median": round(sorted(cold_step)[len(cold_step) // 2], 2),
-                                  "scan_frac": round(alg / (cs * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                                  "flush": "1 GiB fill before each of 20 single steps"}
+    cold_sa.sort()
+    cmed, wmed = cold_sa[len(cold_sa) // 2], sa_us[len(sa_us) // 2]
+    roofline["state_scan_alone"] = {
+        "alg_bytes_per_launch": sa_alg,
+        "cold": {"launch_us_median": round(cmed, 2), "frac": round(sa_alg / (cmed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                 "cache": f"{flush.what} and the chunk prepare before each launch"},
+        "warm": {"launch_us_median": round(wmed, 2), "frac": round(sa_alg / (wmed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    del flush
 
     out = {
         "metric": "gated-delta state-scan Mtok-head/s + % roofline (varlen batch, 64K seq)",
@@ -336,14 +409,13 @@ def main():
     copy_gbs = copy_bandwidth(torch, dev)
     roofline["copy_gbs"] = round(copy_gbs, 1)
     roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
-    sa = roofline["state_scan_alone"]
-    sa["frac_of_copy"] = round(sa["alg_bytes_per_launch"] / (sa["launch_us_median"] * 1e-6) / 1e9 / copy_gbs, 4)
-    if "cold_cache" in roofline:
-        roofline["cold_cache"]["scan_frac_of_copy"] = round(
-            alg / (roofline["cold_cache"]["scan_us_median"] * 1e-6) / 1e9 / copy_gbs, 4)
+    roofline["warm"]["frac_of_copy"] = round(warm_achieved / copy_gbs, 4)
+    for leg in roofline["state_scan_alone"]["cold"], roofline["state_scan_alone"]["warm"]:
+        leg["frac_of_copy"] = round(sa_alg / (leg["launch_us_median"] * 1e-6) / 1e9 / copy_gbs, 4)
 
     if not args.no_long_state:
         out["long_state"] = long_state(pkg, torch, dev, copy_gbs=copy_gbs)
+        out["long_state_h1"] = long_state(pkg, torch, dev, name="long_state_h1", copy_gbs=copy_gbs)
         out["new_states"] = new_states(pkg, torch, dev)
         out["abc_affine"] = abc_affine(pkg, torch, dev)
         out["reverse"] = reverse(pkg, torch, dev, args.workload)
@@ -406,12 +478,14 @@ def sweep(pkg, torch, dev):
                           "us": round(us, 1)}), flush=True)
 
 
-def long_state(pkg, torch, dev, reps=5, copy_gbs=None):
-    """64K-token single sequence, 8 heads: serial scan and the 16-segment
-    path (summaries + compose + segmented final pass), timed with HIP events."""
+def long_state(pkg, torch, dev, name="long_state_h8", reps=5, copy_gbs=None, cp_splits=(2, 4, 8, 16)):
+    """One 64K-token sequence (8 heads, or 1 with name="long_state_h1"):
+    serial scan and the 16-segment path (summaries + compose + segmented
+    final pass, whole and each phase), timed with HIP events; then the
+    CP-vs-serial accuracy table at each split count in ``cp_splits``."""
     from workloads import make_config
 
-    inp = make_config("long_state_h8")
+    inp = make_config(name)
     k, v, g, beta = (x.to(dev) for x in (inp.k, inp.v, inp.g, inp.beta))
     g_cum, w, u = pkg.gdr_chunk_prepare(k, v, g, beta)
     DV = v.shape[-1]
@@ -426,35 +500,44 @@ def long_state(pkg, torch, dev, reps=5, copy_gbs=None):
     h = torch.empty((nt, H, DV, DK), dtype=k.dtype, device=dev)
     v_new = torch.empty_like(u)
     hT = torch.empty((1, H, DK, DV), dtype=torch.float32, device=dev)
-    ss = torch.empty((P, H, DV, DK), dtype=torch.float32, device=dev)
-    st = torch.empty((P, H, DK, DK), dtype=torch.float32, device=dev)
-    si = torch.empty((P, H, DV, DK), dtype=torch.float32, device=dev)
-    ws_bytes = int(L.gdr_segment_summaries_workspace_size(pr.ref, P))
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    seg = B.gdr_segments(P, si.data_ptr())
     sp = B._stream(torch.cuda.current_stream())
     ptr = B._ptr
+
+    def seg_buffers(P):
+        ss = torch.empty((P, H, DV, DK), dtype=torch.float32, device=dev)
+        st = torch.empty((P, H, DK, DK), dtype=torch.float32, device=dev)
+        si = torch.empty((P, H, DV, DK), dtype=torch.float32, device=dev)
+        ws_bytes = int(L.gdr_segment_summaries_workspace_size(pr.ref, P))
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        return ss, st, si, ws, ws_bytes, B.gdr_segments(P, si.data_ptr())
 
     def serial():
         B._check(L.gdr_state_scan(pr.ref, None, None, ptr(k), ptr(w), ptr(u), ptr(g_cum), None, ptr(h), ptr(v_new),
                                   ptr(hT), sp), "scan")
 
-    def summaries():
-        B._check(L.gdr_segment_summaries_ws(pr.ref, None, P, ptr(k), ptr(w), ptr(u), ptr(g_cum), ptr(ss), ptr(st),
-                                            ptr(ws), ws_bytes, sp), "summaries")
+    def path(P, bufs):
+        ss, st, si, ws, ws_bytes, seg = bufs
 
-    def compose():
-        B._check(L.gdr_segment_compose(pr.ref, P, ptr(ss), ptr(st), None, ptr(si), None, sp), "compose")
+        def summaries():
+            B._check(L.gdr_segment_summaries_ws(pr.ref, None, P, ptr(k), ptr(w), ptr(u), ptr(g_cum), ptr(ss),
+                                                ptr(st), ptr(ws), ws_bytes, sp), "summaries")
 
-    def final_pass():
-        B._check(L.gdr_state_scan(pr.ref, None, ctypes.byref(seg), ptr(k), ptr(w), ptr(u), ptr(g_cum), None, ptr(h),
-                                  ptr(v_new), ptr(hT), sp), "final pass")
+        def compose():
+            B._check(L.gdr_segment_compose(pr.ref, P, ptr(ss), ptr(st), None, ptr(si), None, sp), "compose")
 
-    def segmented():
-        summaries()
-        compose()
-        final_pass()
+        def final_pass():
+            B._check(L.gdr_state_scan(pr.ref, None, ctypes.byref(seg), ptr(k), ptr(w), ptr(u), ptr(g_cum), None,
+                                      ptr(h), ptr(v_new), ptr(hT), sp), "final pass")
 
+        def segmented():
+            summaries()
+            compose()
+            final_pass()
+
+        return {"summaries": summaries, "compose": compose, "final_pass": final_pass, "segmented": segmented}
+
+    bufs16 = seg_buffers(P)
+    fns = path(P, bufs16)
     res = {}
     serial_alg = scan_alg_bytes(inp.lengths, inp.H, inp.DK, DV, 2, 2, False, True)
     # segmented path: summaries read k, w, u, g_cum and write (S_loc, M) in
@@ -466,42 +549,51 @@ def long_state(pkg, torch, dev, reps=5, copy_gbs=None):
                  "compose": summ + init,
                  "final_pass": serial_alg + init}
     seg_alg = sum(alg_phase.values())
-    for name, fn in (("serial", serial), ("segmented", segmented)):
+    for leg, fn in (("serial", serial), ("segmented", fns["segmented"])):
         t = _event_median_us(torch, fn, reps=reps) * 1e-6
-        res[name] = {"us": round(t * 1e6, 1), "Mtok_head_per_s": round(inp.token_heads / t / 1e6, 1),
-                     "serial_alg_bytes": serial_alg, "frac_of_hbm_at_serial_bytes": round(serial_alg / t / 8e12, 4)}
+        res[leg] = {"us": round(t * 1e6, 1), "Mtok_head_per_s": round(inp.token_heads / t / 1e6, 1),
+                    "serial_alg_bytes": serial_alg, "frac_of_hbm_at_serial_bytes": round(serial_alg / t / 8e12, 4)}
     t = res["segmented"]["us"] * 1e-6
-    res["segmented"].update(alg_bytes=seg_alg, frac_of_hbm=round(seg_alg / t / 8e12, 4))
+    res["segmented"].update(alg_bytes=seg_alg, frac_of_hbm=round(seg_alg / t / 8e12, 4), segments=P)
     if copy_gbs:
         res["segmented"]["frac_of_copy"] = round(seg_alg / t / 1e9 / copy_gbs, 4)
     # each phase alone (the buffers hold the previous phases' outputs)
-    phases = {"summaries": summaries, "compose": compose, "final_pass": final_pass}
     res["segmented"]["phases"] = {}
-    for name, fn in phases.items():
-        tp = _event_median_us(torch, fn, reps=reps) * 1e-6
-        res["segmented"]["phases"][name] = {"us": round(tp * 1e6, 1), "alg_bytes": alg_phase[name],
-                                            "frac_of_hbm": round(alg_phase[name] / tp / 8e12, 4)}
+    for ph in ("summaries", "compose", "final_pass"):
+        tp = _event_median_us(torch, fns[ph], reps=reps) * 1e-6
+        res["segmented"]["phases"][ph] = {"us": round(tp * 1e6, 1), "alg_bytes": alg_phase[ph],
+                                          "frac_of_hbm": round(alg_phase[ph] / tp / 8e12, 4)}
     # CP vs serial, reported as the pages' accuracy table does (not a gate:
     # each path is checked against the FP64 oracle in the tests): relative L2
     # between the segmented and the serial path's outputs o, final states and
-    # o over the last 8K tokens
+    # o over the last 8K tokens, at each split count (with the time of the
+    # whole segmented path at that split)
     q = inp.q.to(dev)
-    outs = {}
-    for name, fn in (("serial", serial), ("segmented", segmented)):
-        fn()
+
+    def output():
         o = torch.empty_like(v)
-        B._check(L.gdr_chunk_output(pr.ref, ptr(q), ptr(k), ptr(v_new), ptr(h), ptr(g_cum), float(inp.scale), ptr(o),
-                                    sp), "output")
+        B._check(L.gdr_chunk_output(pr.ref, ptr(q), ptr(k), ptr(v_new), ptr(h), ptr(g_cum), float(inp.scale),
+                                    ptr(o), sp), "output")
         torch.cuda.synchronize()
-        outs[name] = (o.double(), hT.double().clone())
+        return o.double(), hT.double().clone()
 
     def rl(x, y):
         return float(torch.linalg.vector_norm(x - y) / torch.linalg.vector_norm(y))
 
-    (os_, hs), (oc, hc) = outs["serial"], outs["segmented"]
-    res["cp_vs_serial_rel_l2"] = {"out": rl(oc, os_), "final": rl(hc, hs),
-                                  "last_8k": rl(oc[:, -8192:], os_[:, -8192:])}
-    res["workload"] = "long_state_h8 (T=65536, H=8, dk=dv=128, bf16, 16 segments)"
+    serial()
+    os_, hs = output()
+    table = {}
+    for Pc in cp_splits:
+        bf = bufs16 if Pc == P else seg_buffers(Pc)
+        f = path(Pc, bf)["segmented"]
+        us = _event_median_us(torch, f, reps=3)
+        f()
+        oc, hc = output()
+        table[str(Pc)] = {"out": rl(oc, os_), "final": rl(hc, hs), "last_8k": rl(oc[:, -8192:], os_[:, -8192:]),
+                          "segmented_us": round(us, 1)}
+        del bf
+    res["cp_vs_serial_rel_l2"] = table
+    res["workload"] = f"{name} (T=65536, H={H}, dk=dv=128, bf16, 16 segments)"
     return res
 
 
