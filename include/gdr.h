@@ -397,6 +397,29 @@ const char* gdr_status_string(gdr_status s);
 /* Message of the last failed call on this thread ("" if none). */
 const char* gdr_last_error(void);
 
+/* The state scan with the segmentation chosen by the scheduler ([kev#259]
+ * "Why 4 sequences": one long state, or a few, leave most of the GPU idle in
+ * the serial scan; [cuLA#127] "Summary": the same scan split into segments
+ * whose affine summaries are composed in FP32).  gdr_plan_segments gives the
+ * segment count P it takes for this problem: 0 = the serial scan (many
+ * sequence-head chains, short sequences, state pools, DK or DV of 256),
+ * else P >= 2.  gdr_state_scan_auto then runs, on `stream`:
+ *   P = 0: gdr_state_scan_output (q and o given) or gdr_state_scan;
+ *   P > 0: gdr_segment_summaries_ws, gdr_segment_compose (from h0) and the
+ *          segmented final pass (with the chunk output fused when q and o
+ *          are given), the summaries and initial states in the workspace.
+ * Results are those of the explicit calls with n_segments = P, bit for bit.
+ * workspace: device memory of at least gdr_state_scan_auto_workspace_size
+ * bytes (0 when P = 0; NULL is then allowed), 16-byte aligned; it holds
+ * nothing after the call.  q and o are given together or not at all; other
+ * arguments as in gdr_state_scan_output.  gdr_plan_segments returns -1 for
+ * an invalid problem. */
+int32_t gdr_plan_segments(const gdr_problem* p);
+size_t gdr_state_scan_auto_workspace_size(const gdr_problem* p);
+gdr_status gdr_state_scan_auto(const gdr_problem* p, const void* q, const void* k, const void* w, const void* u,
+                               const float* g_cum, const float* h0, float scale, void* h, void* v_new, float* hT,
+                               void* o, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Scheduler introspection (host only, no GPU needed): the tile and grid the
  * scan would use (n_segments > 0: the summary pass as gdr_segment_summaries_ws
  * runs it with its workspace, i.e. on half segments when that form applies).

@@ -17,6 +17,8 @@ from .binding import (  # noqa: F401
     gdr_chunk_prepare,
     gdr_num_chunks,
     gdr_plan_query,
+    gdr_plan_segments,
+    gdr_state_scan_auto,
     gdr_segment_compose,
     gdr_segment_summaries,
     gdr_segment_summaries_noalloc,

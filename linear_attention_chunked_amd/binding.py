@@ -100,6 +100,10 @@ _SIGS = {
                                         _P, _P]),
     "abc_affine_scan_bwd": (ctypes.c_int, [ctypes.POINTER(abc_problem), _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                            _P, _P, _P, ctypes.c_size_t, _P]),
+    "gdr_plan_segments": (ctypes.c_int32, [ctypes.POINTER(gdr_problem)]),
+    "gdr_state_scan_auto_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(gdr_problem)]),
+    "gdr_state_scan_auto": (ctypes.c_int, [ctypes.POINTER(gdr_problem), _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                           _P, _P, _P, ctypes.c_size_t, _P]),
     "gdr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gdr_last_error": (ctypes.c_char_p, []),
     "gdr_plan_query": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile), ctypes.c_int32,
@@ -573,15 +577,61 @@ def gdr_state_scan_bwd(q, k, w, g_cum, dO, dv_local, dhT=None, scale: float = 1.
     return dh, dv, dh0
 
 
+def gdr_plan_segments(k, DV: int, cu_seqlens=None) -> int:
+    """Segments per sequence the scheduler picks for this problem (0 = the serial scan)."""
+    n = int(lib().gdr_plan_segments(Problem(k, DV, cu_seqlens).ref))
+    if n < 0:
+        _check(GDR_ERR_INVALID_ARG, "gdr_plan_segments")
+    return n
+
+
+def gdr_state_scan_auto(q, k, w, u, g_cum, scale: float = 1.0, h0=None, cu_seqlens=None, out=None, stream=None):
+    """The state scan (with the chunk output fused when q is given) with the
+    scheduler's segmentation: returns (o | None, h, v_new, hT).  ``out`` may
+    hold preallocated "o", "h", "v_new", "hT" and "workspace" tensors."""
+    DV = u.shape[-1]
+    out = out or {}
+    p = Problem(k, DV, cu_seqlens)
+    L = lib()
+    nt = gdr_num_chunks(k, DV, cu_seqlens)
+    h = out.get("h")
+    if h is None:
+        h = torch.empty((nt, p.H, DV, p.DK), dtype=k.dtype, device=k.device)
+    v_new = out.get("v_new")
+    if v_new is None:
+        v_new = torch.empty_like(u)
+    hT = out.get("hT")
+    if hT is None:
+        hT = torch.empty((p.N, p.H, p.DK, DV), dtype=torch.float32, device=k.device)
+    o = None
+    if q is not None:
+        o = out.get("o")
+        if o is None:
+            o = torch.empty_like(u)
+    ws_bytes = int(L.gdr_state_scan_auto_workspace_size(p.ref))
+    ws = out.get("workspace")
+    if ws_bytes > 0 and (ws is None or ws.numel() * ws.element_size() < ws_bytes):
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=k.device)
+    _check(L.gdr_state_scan_auto(p.ref, _ptr(q), _ptr(k), _ptr(w), _ptr(u), _ptr(g_cum), _ptr(h0), float(scale),
+                                 _ptr(h), _ptr(v_new), _ptr(hT), _ptr(o), _ptr(ws) if ws_bytes > 0 else None,
+                                 ws_bytes, _stream(stream)), "gdr_state_scan_auto")
+    return o, h, v_new, hT
+
+
 def chunk_gated_delta_rule(q, k, v, g, beta, h0=None, cu_seqlens=None, scale: float = 1.0,
                            n_segments: Optional[int] = None, tile=None, stream=None) -> dict:
-    """The whole forward path: prepare -> scan (serial, or summaries + compose +
-    segmented pass when n_segments is given) with the chunk output fused into
-    the scan where a fused kernel exists (else scan, then output).  Returns a
-    dict with o, h, v_new, hT, g_cum, w, u (and seg_state, seg_trans, seg_init)."""
+    """The whole forward path: prepare -> scan with the chunk output fused
+    into the scan where a fused kernel exists (else scan, then output).  The
+    scan is split into segments (summaries + compose + segmented pass) as the
+    scheduler chooses when n_segments is None (gdr_state_scan_auto), serial
+    with n_segments = 0, and split into n_segments when that is >= 1.  Returns
+    a dict with o, h, v_new, hT, g_cum, w, u (and seg_state, seg_trans,
+    seg_init for an explicit split)."""
     g_cum, w, u = gdr_chunk_prepare(k, v, g, beta, cu_seqlens, stream)
     out = {"g_cum": g_cum, "w": w, "u": u}
-    if n_segments is None:
+    if n_segments is None and tile is None:
+        o, h, v_new, hT = gdr_state_scan_auto(q, k, w, u, g_cum, scale, h0, cu_seqlens, stream=stream)
+    elif not n_segments:
         o, h, v_new, hT = gdr_state_scan_output(q, k, w, u, g_cum, scale, h0, cu_seqlens, tile, stream=stream)
     else:
         seg_state, seg_trans = gdr_segment_summaries(k, w, u, g_cum, n_segments, cu_seqlens, tile, stream)

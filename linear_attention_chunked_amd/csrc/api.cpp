@@ -490,6 +490,92 @@ gdr_status gdr_segment_compose(const gdr_problem* p, int32_t n_segments, const f
   return GDR_OK;
 }
 
+int32_t gdr_plan_segments(const gdr_problem* p) {
+  g_err.clear();
+  gdr::Problem pr;
+  if (parse(p, pr) != GDR_OK) return -1;
+  return gdr::auto_segments(pr);
+}
+
+namespace {
+// Byte offsets of the auto scan's workspace parts (each 256-byte aligned):
+// seg_state, seg_trans, seg_init, then the summaries' own workspace.
+struct AutoWs {
+  size_t state, trans, init, summ, total;
+};
+
+AutoWs auto_layout(const gdr::Problem& pr, int P, size_t summ_bytes) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const size_t n = static_cast<size_t>(pr.N) * P * pr.H;
+  AutoWs w;
+  w.state = 0;
+  w.trans = up(w.state + n * pr.DV * pr.DK * sizeof(float));
+  w.init = up(w.trans + n * pr.DK * pr.DK * sizeof(float));
+  w.summ = up(w.init + n * pr.DV * pr.DK * sizeof(float));
+  w.total = w.summ + summ_bytes;
+  return w;
+}
+}  // namespace
+
+size_t gdr_state_scan_auto_workspace_size(const gdr_problem* p) {
+  g_err.clear();
+  gdr::Problem pr;
+  if (parse(p, pr) != GDR_OK) return 0;
+  const int P = gdr::auto_segments(pr);
+  if (P == 0) return 0;
+  return auto_layout(pr, P, gdr_segment_summaries_workspace_size(p, P)).total;
+}
+
+gdr_status gdr_state_scan_auto(const gdr_problem* p, const void* q, const void* k, const void* w, const void* u,
+                               const float* g_cum, const float* h0, float scale, void* h, void* v_new, float* hT,
+                               void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  if ((q == nullptr) != (o == nullptr)) return fail(GDR_ERR_INVALID_ARG, "q and o are given together or not at all");
+  const int P = gdr::auto_segments(pr);
+  if (P == 0) {
+    if (o != nullptr)
+      return gdr_state_scan_output(p, nullptr, nullptr, q, k, w, u, g_cum, h0, scale, h, v_new, hT, o, stream);
+    return gdr_state_scan(p, nullptr, nullptr, k, w, u, g_cum, h0, h, v_new, hT, stream);
+  }
+  // every check of the three calls below, before the first launch
+  GDR_TRY(need(k, "k"));
+  GDR_TRY(need(w, "w"));
+  GDR_TRY(need(u, "u"));
+  GDR_TRY(need(g_cum, "g_cum"));
+  GDR_TRY(opt(q, "q"));
+  GDR_TRY(opt(o, "o"));
+  GDR_TRY(opt(h0, "h0"));
+  GDR_TRY(opt(h, "h"));
+  GDR_TRY(opt(v_new, "v_new"));
+  GDR_TRY(opt(hT, "hT"));
+  GDR_TRY(need(workspace, "workspace"));
+  const size_t summ_bytes = gdr_segment_summaries_workspace_size(p, P);
+  const AutoWs lay = auto_layout(pr, P, summ_bytes);
+  if (workspace_bytes < lay.total)
+    return fail(GDR_ERR_INVALID_ARG, "workspace_bytes " + std::to_string(workspace_bytes) + " < the " +
+                                         std::to_string(lay.total) + " bytes this problem needs");
+  if (o != nullptr) {
+    gdr::Tile t;
+    GDR_TRY(tile_for(pr, nullptr, 0, static_cast<int64_t>(pr.N) * P, t));
+    if (!fusable(pr, t)) t = gdr::Tile{64, 4, 2};  // the fallback gdr_state_scan_output takes
+    if (!fusable(pr, t) && (h == nullptr || v_new == nullptr))
+      return fail(GDR_ERR_UNSUPPORTED, "the output is not fused for this problem: h and v_new must be given");
+  }
+  char* ws = static_cast<char*>(workspace);
+  float* seg_state = reinterpret_cast<float*>(ws + lay.state);
+  float* seg_trans = reinterpret_cast<float*>(ws + lay.trans);
+  float* seg_init = reinterpret_cast<float*>(ws + lay.init);
+  GDR_TRY(gdr_segment_summaries_ws(p, nullptr, P, k, w, u, g_cum, seg_state, seg_trans,
+                                   summ_bytes ? ws + lay.summ : nullptr, summ_bytes, stream));
+  GDR_TRY(gdr_segment_compose(p, P, seg_state, seg_trans, h0, seg_init, nullptr, stream));
+  const gdr_segments seg{P, seg_init};
+  if (o != nullptr)
+    return gdr_state_scan_output(p, nullptr, &seg, q, k, w, u, g_cum, nullptr, scale, h, v_new, hT, o, stream);
+  return gdr_state_scan(p, nullptr, &seg, k, w, u, g_cum, nullptr, h, v_new, hT, stream);
+}
+
 gdr_status gdr_plan_query(const gdr_problem* p, const gdr_tile* tile, int32_t n_segments, int64_t out[6]) {
   g_err.clear();
   if (out == nullptr) return fail(GDR_ERR_INVALID_ARG, "out must not be NULL");

@@ -224,6 +224,20 @@ int summary_split(const Problem& p, int P) {
   return (blocks > 0 && blocks < 512) ? 2 : 1;
 }
 
+int auto_segments(const Problem& p) {
+  if (!p.pool_idx.empty() || p.DK > 128 || p.DV > 128) return 0;
+  int64_t chains = 0, nt_max = 0;
+  for (const Seq& s : p.seqs) {
+    if (s.len == 0) continue;
+    chains += p.H;
+    nt_max = std::max<int64_t>(nt_max, (s.len + kChunk - 1) / kChunk);
+  }
+  if (chains == 0 || chains * (p.DV / 64) >= 128 || nt_max < 8) return 0;
+  int P = (chains <= 4 && nt_max >= 1024) ? 32 : 16;
+  while (P > 1 && nt_max / P < 4) P /= 2;
+  return P >= 2 ? P : 0;
+}
+
 int scan_blocks(const Problem& p, const Tile& t, int mode) {
   if (mode != 1) return p.DV / t.bv;
   return summary_kernel_mode(p) == 2 ? 2 * p.DV / t.bv : (p.DV + p.DK) / t.bv;

@@ -81,6 +81,18 @@ void segment_bounds(int64_t len, int P, std::vector<int64_t>& t0, std::vector<in
 // problem shape and P only (not on the tile).
 int summary_split(const Problem& p, int P);
 
+// Segments per sequence the planner picks for the state scan when the caller
+// names none (gdr_state_scan_auto): 0 (the serial scan) unless the serial
+// units (sequence, head, 64 value columns) would leave more than half the 256
+// CUs idle and the longest sequence has at least 8 chunks; then 32 segments
+// for at most 4 non-empty (sequence, head) chains with 1024 or more chunks,
+// else 16, halved until every segment of the longest sequence keeps at least
+// 4 chunks (from a segment-count sweep of the summaries + compose + final
+// pass on MI355X, DK = DV = 128: 64K tokens x 1, 2, 4 heads best at 32;
+// x 8 heads, 16K x 2 and x 8, 8K x 4 and 4K x 16 best at 16).  Pools
+// (state_indices) always get 0: the segmented passes do not take them.
+int auto_segments(const Problem& p);
+
 // Plans.  mode 0 = plain scan, 2 = segmented final pass, 1 = summaries.
 // With split = 2 (summaries only) every segment becomes two rows, its first
 // ceil(chunks / 2) chunks and the rest, written to summary slots 2s and 2s+1.

@@ -6,6 +6,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 from linear_attention_chunked_amd import binding as B
@@ -342,3 +344,54 @@ def test_noalloc_summaries_reject_oversized_problems():
     bad = B.gdr_problem(1, 65536, 17, 128, 128, 1, cu, B.GDR_BF16, 0, None, 0)
     assert L.gdr_segment_summaries_noalloc(ctypes.byref(bad), None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                            None) == B.GDR_ERR_INVALID_ARG
+
+
+def _lens_problem(lengths, H, dtype=None, DK=128, DV=128, pool=None):
+    cu = (ctypes.c_int32 * (len(lengths) + 1))(*([0] + list(np.cumsum(lengths))))
+    ia = None if pool is None else (ctypes.c_int32 * len(pool))(*pool)
+    p = B.gdr_problem(1, int(sum(lengths)), H, DK, DV, len(lengths), cu, B.GDR_BF16 if dtype is None else dtype, 0,
+                      ia, 0 if pool is None else len(pool))
+    return p, (cu, ia)
+
+
+@pytest.mark.parametrize("lengths,H,want", [
+    ([65536], 8, 16), ([65536], 1, 32), ([65536], 2, 32), ([65536], 4, 32), ([16384], 8, 16), ([16384], 2, 16),
+    ([8192], 4, 16), ([4096], 16, 16), ([600], 2, 2), ([300], 1, 0),
+    ([130, 139, 197, 245, 24, 50, 214, 244, 76, 91, 225, 118, 81, 215, 77, 114, 171, 148, 36, 22, 224, 197, 217, 145],
+     16, 0),
+    ([3597, 1827, 1359, 1941, 2295, 3526, 2410, 1306], 32, 0),
+])
+def test_plan_segments_rule(lengths, H, want):
+    """The scheduler's segment count: the serial scan when the (sequence,
+    head, 64-column) units fill half the GPU or the sequences are short, else
+    16 (32 for up to four chains of 64K tokens), fewer when segments would
+    drop below 4 chunks."""
+    p, keep = _lens_problem(lengths, H)
+    assert B.lib().gdr_plan_segments(ctypes.byref(p)) == want
+    ws = B.lib().gdr_state_scan_auto_workspace_size(ctypes.byref(p))
+    assert (ws == 0) == (want == 0)
+    if want:
+        n = want * H
+        assert ws >= 3 * n * 128 * 128 * 4
+
+
+def test_plan_segments_pools_and_wide_states_are_serial():
+    p, keep = _lens_problem([65536], 2, pool=[0])
+    assert B.lib().gdr_plan_segments(ctypes.byref(p)) == 0
+    p, keep = _lens_problem([65536], 2, DK=256, DV=256)
+    assert B.lib().gdr_plan_segments(ctypes.byref(p)) == 0
+    bad = B.gdr_problem(1, 10, 2, 100, 128, 1, None, B.GDR_BF16, 0, None, 0)
+    assert B.lib().gdr_plan_segments(ctypes.byref(bad)) == -1
+
+
+def test_state_scan_auto_validates_before_launch():
+    """Arguments are checked before any launch: q without o, a missing or
+    small workspace."""
+    L = B.lib()
+    p, keep = _lens_problem([65536], 8)
+    ws = L.gdr_state_scan_auto_workspace_size(ctypes.byref(p))
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, None, ctypes.c_float(1.0), FAKE, FAKE, FAKE]
+    assert L.gdr_state_scan_auto(ctypes.byref(p), *args, None, FAKE, ws, None) == B.GDR_ERR_INVALID_ARG  # q, no o
+    assert L.gdr_state_scan_auto(ctypes.byref(p), *args, FAKE, None, ws, None) == B.GDR_ERR_INVALID_ARG
+    assert L.gdr_state_scan_auto(ctypes.byref(p), *args, FAKE, FAKE, ws - 16, None) == B.GDR_ERR_INVALID_ARG
+    assert "workspace" in L.gdr_last_error().decode()
