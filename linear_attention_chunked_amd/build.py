@@ -60,5 +60,65 @@ def build(verbose: bool = True, jobs: int | None = None) -> str:
     return OUT
 
 
+def resource_table(out_path: str, jobs: int | None = None) -> str:
+    """Per-kernel resource use as the compiler reports it for gfx950
+    (-Rpass-analysis=kernel-resource-usage on every source, the same flags as
+    build()): VGPRs, AGPRs, SGPRs, scratch (spills), LDS and the occupancy in
+    waves per SIMD those allow.  Writes a text table to ``out_path``."""
+    import re
+    import tempfile
+
+    rows = []
+
+    def one(src):
+        path = os.path.join(CSRC, src)
+        lang = [] if src.endswith(".hip") else ["-x", "hip"]
+        with tempfile.TemporaryDirectory() as td:
+            cmd = [HIPCC, *COMMON, *lang, "-Rpass-analysis=kernel-resource-usage", "-c", path, "-o",
+                   os.path.join(td, "x.o")]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(r.stderr[-2000:])
+        cur, found = None, []
+        for line in r.stderr.splitlines():
+            m = re.search(r"remark:\s+(.*?):\s+(.*?) \[-Rpass-analysis", line)
+            if not m:
+                continue
+            key, val = m.group(1).strip(), m.group(2).strip()
+            if key == "Function Name":
+                cur = {"kernel": val, "source": src}
+                found.append(cur)
+            elif cur is not None:
+                cur[key] = val
+        return found
+
+    srcs = [s for s in SOURCES if s.endswith(".hip")]
+    with cf.ThreadPoolExecutor(max_workers=jobs or min(8, os.cpu_count() or 4)) as ex:
+        for found in ex.map(one, srcs):
+            rows.extend(found)
+
+    def demangle(names):
+        r = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True)
+        return r.stdout.splitlines() if r.returncode == 0 else names
+
+    names = demangle([r["kernel"] for r in rows])
+    cols = [("VGPRs", "vgpr"), ("AGPRs", "agpr"), ("TotalSGPRs", "sgpr"), ("ScratchSize [bytes/lane]", "scratch"),
+            ("VGPRs Spill", "vspill"), ("SGPRs Spill", "sspill"), ("LDS Size [bytes/block]", "lds_bytes"),
+            ("Occupancy [waves/SIMD]", "waves/SIMD")]
+    lines = ["# Per-kernel resource use on gfx950 as the compiler reports it (-Rpass-analysis=kernel-resource-usage,",
+             "# the library's own build flags); scratch = private memory per lane (register spills), 0 everywhere",
+             "#",
+             "# command (from the repository root):",
+             f"#   python -c 'from linear_attention_chunked_amd.build import resource_table; "
+             f"resource_table(\"{os.path.relpath(out_path, ROOT)}\")'",
+             "#",
+             "# " + " ".join(f"{c[1]:>10}" for c in cols) + "  kernel (source)"]
+    for r, name in sorted(zip(rows, names), key=lambda x: (x[0]["source"], x[1])):
+        lines.append("  " + " ".join(f"{r.get(c[0], '?'):>10}" for c in cols) + f"  {name} ({r['source']})")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return out_path
+
+
 if __name__ == "__main__":
     build()

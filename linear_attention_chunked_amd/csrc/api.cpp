@@ -1,6 +1,7 @@
 // C-ABI entry points (include/gdr.h): argument checks, planning, dispatch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -66,6 +67,8 @@ gdr_status tile_for(const gdr::Problem& pr, const gdr_tile* tile, int mode, int6
 // output2.hip (each one workgroup per (chunk, head)); DK or DV = 256
 // and float32 run the generic kernels (per (chunk, head); output per 64 value
 // columns).
+constexpr int kCUs = 256;  // compute units of one MI355X
+
 bool fast_bf16(const gdr::Problem& pr) { return pr.dtype == GDR_BF16 && pr.DK <= 128 && pr.DV <= 128; }
 
 gdr_status hip_fail(hipError_t e, const char* what) {
@@ -119,11 +122,20 @@ gdr_status run_scan(const gdr::Problem& pr, const gdr::Tile& t, int mode, int P,
   a.in_vk = in_vk;
   a.out_vk = out_vk;
   a.n_blk = gdr::scan_blocks(pr, t, mode);
+  // A launch with more workgroups than two per CU runs the dense form where
+  // one exists (the same results bit for bit); GDR_SCAN_DENSE=0 / 1 forces
+  // the full / dense form.
+  gdr::LaunchFn dense = (pr.dtype == GDR_BF16 && kmode == 0)
+                            ? gdr::find_scan2_dense(pr.DK, t.bv, t.waves, t.stages, 0, decay != nullptr, fo != nullptr)
+                            : nullptr;
+  int force = -1;
+  if (const char* env = getenv("GDR_SCAN_DENSE")) force = atoi(env) != 0 ? 1 : 0;
   for (const gdr::Launch& l : plan) {
     if (l.grid == 0) continue;
     a.n_rows = static_cast<int32_t>(l.rows.size());
     memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
-    hipError_t e = fn(&a, l.grid, stream);
+    const bool use_dense = dense != nullptr && (force >= 0 ? force == 1 : l.grid > 2 * kCUs);
+    hipError_t e = (use_dense ? dense : fn)(&a, l.grid, stream);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
   }
   return GDR_OK;

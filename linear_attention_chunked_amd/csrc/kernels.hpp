@@ -157,6 +157,9 @@ using LaunchFn = hipError_t (*)(const void* args, int grid, hipStream_t stream);
 LaunchFn find_scan(int dtype, int dk, int bv, int waves, int stages, int mode);
 LaunchFn find_scan2(int dk, int bv, int waves, int stages, int mode, bool kd);
 LaunchFn find_scan2_fused(int dk, int bv, int waves, int stages);  // plain pass + chunk output (bf16)
+// The same plain pass (optionally with per-channel decay or the fused output)
+// in its dense form, three workgroups per CU; null where there is none.
+LaunchFn find_scan2_dense(int dk, int bv, int waves, int stages, int mode, bool kd, bool fo);
 LaunchFn find_prepare(int dtype, int dk, int dv);
 LaunchFn find_prepare2(int dk, int dv);
 LaunchFn find_kda_prepare(int dk, int dv);

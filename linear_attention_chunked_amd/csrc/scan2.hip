@@ -43,6 +43,20 @@
 //     e^{Gam_last} (one DK-vector per chunk and head); the weights are then
 //     -1 (0 past the tail) and every state row is scaled by its own channel's
 //     decay: S <- diag(decay) S + kg^T D.
+//   * Dense form (DENSE, the staged plain pass of 64-column blocks with four
+//     waves): three workgroups share a CU instead of two.  The full form
+//     holds every W and K operand fragment of a chunk in registers at once
+//     and stages h and v_new in LDS of their own (about 250 VGPRs and 73 KB:
+//     two workgroups per CU).  The dense form reads the W fragments of one
+//     contraction step and the K fragments of one token step at a time,
+//     issues the fused output's Q loads after GEMM1, and stages h in the W
+//     tile's place and v_new in the U tile's (dead once every wave holds its
+//     W and U operands of the chunk; one more barrier there and one between
+//     the staged stores leaving and the next tiles arriving): at most 168
+//     VGPRs and 46 KB.  The products and their order are the same, so the
+//     results are the same bits; the planner takes it when a launch has more
+//     workgroups than two per CU (many short sequences), where the third
+//     resident block shortens the tail of the last round.
 //   * Fused chunk output (FO, staged plain pass with four waves): once every
 //     wave has staged its h columns and v_new columns of the chunk, wave w
 //     forms the output of token tile w over the block's BV columns,
@@ -58,7 +72,7 @@
 
 namespace gdr {
 
-template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false>
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false, bool DENSE = false>
 struct Scan2 {
   using S = St<bf16_t>;
   using frag = S::frag;
@@ -94,9 +108,11 @@ struct Scan2 {
   static constexpr bool STAGE = (MODE == 0) && (NBUF == 1);
   static constexpr int SHS = DK * 2 + 16;           // staged h rows (one value column each)
   static constexpr int SVS = BV * 2 + 16;           // staged v_new rows (one token each)
-  static constexpr int OFF_HS = BUF;
-  static constexpr int OFF_VS = OFF_HS + BV * SHS;
-  static constexpr int SMEM = NBUF * BUF + (STAGE ? BV * SHS + kChunk * SVS : 0);
+  // DENSE: the h staging takes the W tile's place, v_new the U tile's
+  static constexpr bool ALIAS = DENSE && STAGE && (BV * SHS <= kChunk * SW) && (SVS <= SU);
+  static constexpr int OFF_HS = ALIAS ? OFF_W : BUF;
+  static constexpr int OFF_VS = ALIAS ? OFF_U : OFF_HS + BV * SHS;
+  static constexpr int SMEM = NBUF * BUF + ((STAGE && !ALIAS) ? BV * SHS + kChunk * SVS : 0);
   static constexpr int H_PT = BV * DK / 8 / NT;     // 16-byte h vectors per thread
   static constexpr int V_PT = kChunk * BV / 8 / NT; // 16-byte v_new vectors per thread
   static constexpr int W_PT = kChunk * CPW / NT;   // 16-byte vectors per thread (W, and K)
@@ -105,6 +121,7 @@ struct Scan2 {
   static_assert((kChunk * CPW) % NT == 0, "W/K tiles split evenly over the threads");
   static_assert(!STAGE || ((BV * DK / 8) % NT == 0 && (kChunk * BV / 8) % NT == 0), "staged outputs split evenly");
   static_assert(!FO || (STAGE && NW == 4 && !KD), "the fused output runs on the staged plain pass, one token tile per wave");
+  static_assert(!DENSE || ALIAS, "the dense form needs the staging to fit the W and U tiles");
 
   struct Stage {
     u32x4_t w[W_PT];
@@ -345,7 +362,7 @@ struct Scan2 {
 
     // FO: this wave's Q fragments (token tile `wave`), in flight during the chunk step
     frag fq[KS];
-    if constexpr (FO) {
+    auto load_q = [&]() {
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (tok0 * H + x.hd) * DK;
       const rsrc_t rq = make_rsrc(qp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
       const int qo = static_cast<int>((16 * wave + c16) * H * DK * 2) + (g4 >> 1) * 16 + (g4 & 1) * 8;
@@ -353,7 +370,8 @@ struct Scan2 {
       for (int s = 0; s < KS; ++s)
         fq[s] = S::frag_from_quads(__builtin_amdgcn_raw_buffer_load_b64(rq, qo + 64 * s, 0, 0),
                                    __builtin_amdgcn_raw_buffer_load_b64(rq, qo + 64 * s + 32, 0, 0));
-    }
+    };
+    if constexpr (FO && !DENSE) load_q();
     u32x2_t uq[4][NC];
     if constexpr (HASU) {
 #pragma unroll
@@ -361,12 +379,16 @@ struct Scan2 {
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) uq[mt][ct] = lds_tr16(ub, 16 * mt * SU + 32 * ct);
     }
-    frag aw[KS][4];
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
+    auto w_frags = [&](frag (&f)[4], int s) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        aw[s][mt] = S::frag_from_quads(lds_b64(wb, 16 * mt * SW + 64 * s), lds_b64(wb, 16 * mt * SW + 64 * s + 32));
+        f[mt] = S::frag_from_quads(lds_b64(wb, 16 * mt * SW + 64 * s), lds_b64(wb, 16 * mt * SW + 64 * s + 32));
+    };
+    frag aw[DENSE ? 1 : KS][4];
+    if constexpr (!DENSE) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) w_frags(aw[s], s);
+    }
 
     // ---- S as B operand; pre-chunk state h[c] ----
     frag Sb[KS][NC];
@@ -398,17 +420,22 @@ struct Scan2 {
         }
     }
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < KS; ++s) {
+      if constexpr (DENSE) w_frags(aw[0], s);
+      const frag (&ws)[4] = aw[DENSE ? 0 : s];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
           if (!HASU && s == 0)
-            acc[mt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[s][mt].v, Sb[s][ct].v,
+            acc[mt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ws[mt].v, Sb[s][ct].v,
                                                                   f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
           else
-            S::mma(acc[mt][ct], aw[s][mt], Sb[s][ct]);
+            S::mma(acc[mt][ct], ws[mt], Sb[s][ct]);
         }
+    }
+    if constexpr (FO && DENSE) load_q();
+    if constexpr (ALIAS) __syncthreads();  // every wave holds its W and U operands: their tiles become staging
 
     if (STAGE) {
       // h block: value column (colw + 16 ct + c16), rows 32 s + 4 g4 (+16)
@@ -438,13 +465,16 @@ struct Scan2 {
     }
 
     // ---- K operand reads overlap GEMM1 ----
-    frag ak[2][DT];
+    auto k_frag = [&](int s2, int dt) {
+      return S::frag_from_quads(lds_tr16(kb, 32 * s2 * SK + 32 * dt), lds_tr16(kb, (32 * s2 + 16) * SK + 32 * dt));
+    };
+    frag ak[DENSE ? 1 : 2][DENSE ? 1 : DT];
+    if constexpr (!DENSE) {
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        ak[s2][dt] = S::frag_from_quads(lds_tr16(kb, 32 * s2 * SK + 32 * dt),
-                                        lds_tr16(kb, (32 * s2 + 16) * SK + 32 * dt));
+        for (int dt = 0; dt < DT; ++dt) ak[s2][dt] = k_frag(s2, dt);
+    }
     f32x4_t nd[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) nd[mt] = *reinterpret_cast<const f32x4_t*>(nd_l + 16 * mt);
@@ -515,9 +545,12 @@ struct Scan2 {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt) {
+        if constexpr (DENSE) ak[0][0] = k_frag(s2, dt);
+        const frag& kf = ak[DENSE ? 0 : s2][DENSE ? 0 : dt];
 #pragma unroll
-        for (int ct = 0; ct < NC; ++ct) S::mma(Sacc[dt][ct], ak[s2][dt], Db[s2][ct]);
+        for (int ct = 0; ct < NC; ++ct) S::mma(Sacc[dt][ct], kf, Db[s2][ct]);
+      }
     if constexpr (FO) fused_output(x, row, c, buf, smem_out, fq);
   }
 
@@ -543,6 +576,7 @@ struct Scan2 {
         for (int c = 0; c < nchunks; ++c) {
           __syncthreads();
           if (STAGE && c > 0) write_out(x, row, c - 1, so);
+          if constexpr (ALIAS) __syncthreads();  // the staged outputs have left before the tiles refill them
           store(st, x, buf0, nv_of(c), sig);
           __syncthreads();
           if (c + 1 < nchunks) load(st, x, tok_of(c + 1), nv_of(c + 1), hr_of(c + 1));
@@ -709,16 +743,16 @@ struct Scan2 {
   }
 };
 
-template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false>
-__global__ __launch_bounds__(NW * 64) void scan2_kernel(const ScanArgs a) {
-  using K = Scan2<DK, BV, NW, PF, MODE, NBUF, KD, FO>;
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false, bool DENSE = false>
+__global__ __launch_bounds__(NW * 64, DENSE ? 3 : 1) void scan2_kernel(const ScanArgs a) {
+  using K = Scan2<DK, BV, NW, PF, MODE, NBUF, KD, FO, DENSE>;
   __shared__ __align__(16) char smem[K::SMEM];
   K::run(a, smem);
 }
 
-template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false>
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false, bool DENSE = false>
 static hipError_t launch_scan2(const void* args, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((scan2_kernel<DK, BV, NW, PF, MODE, NBUF, KD, FO>), dim3(grid), dim3(NW * 64), 0, stream,
+  hipLaunchKernelGGL((scan2_kernel<DK, BV, NW, PF, MODE, NBUF, KD, FO, DENSE>), dim3(grid), dim3(NW * 64), 0, stream,
                      *static_cast<const ScanArgs*>(args));
   return hipGetLastError();
 }
@@ -759,6 +793,19 @@ LaunchFn find_scan2_fused(int dk, int bv, int waves, int stages) {
   if (dk == 128 && bv == 128) return &launch_scan2<128, 128, 4, 1, 0, 1, false, true>;
   if (dk == 64 && bv == 64) return &launch_scan2<64, 64, 4, 1, 0, 1, false, true>;
   if (dk == 64 && bv == 128) return &launch_scan2<64, 128, 4, 1, 0, 1, false, true>;
+  return nullptr;
+}
+
+// The dense form of the staged plain pass (64-column blocks, four waves,
+// stages 2): plain, per-channel decay (kd) or with the chunk output fused (fo).
+LaunchFn find_scan2_dense(int dk, int bv, int waves, int stages, int mode, bool kd, bool fo) {
+  if (bv != 64 || waves != 4 || stages != 2 || mode != 0 || (kd && fo)) return nullptr;
+  if (dk == 128)
+    return fo ? &launch_scan2<128, 64, 4, 1, 0, 1, false, true, true>
+              : (kd ? &launch_scan2<128, 64, 4, 1, 0, 1, true, false, true> : &launch_scan2<128, 64, 4, 1, 0, 1, false, false, true>);
+  if (dk == 64)
+    return fo ? &launch_scan2<64, 64, 4, 1, 0, 1, false, true, true>
+              : (kd ? &launch_scan2<64, 64, 4, 1, 0, 1, true, false, true> : &launch_scan2<64, 64, 4, 1, 0, 1, false, false, true>);
   return nullptr;
 }
 

@@ -141,3 +141,29 @@ def test_fused_question_rows_against_oracle(pkg):
     kinds = {"o": "token", "v_new": "token", "h": "chunk", "hT": "seq"}
     worst = per_sequence_max({k: (got[k], ref[k], kinds[k]) for k in kinds}, d["cu_seqlens"], ref["chunk_offsets"])
     gate(errs, worst, TOL, "fused question_rows")
+
+
+@pytest.mark.parametrize("name", ["question_rows", "kda_question_rows"])
+def test_dense_and_full_forms_bit_identical(pkg, monkeypatch, name):
+    """The scan's dense form (three workgroups per CU: operands read step by
+    step, staging in the chunk tiles' place) and its full form give the same
+    bits: plain scan and fused scan + output on question rows, and the
+    per-channel-decay scan."""
+    inp = make_config(name)
+    q, k, v, g, b = (x.cuda() for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    h0 = inp.h0.cuda()
+    cu = inp.cu_seqlens
+    outs = {}
+    for form in ("0", "1"):
+        monkeypatch.setenv("GDR_SCAN_DENSE", form)
+        if name == "question_rows":
+            g_cum, w, u = pkg.gdr_chunk_prepare(k, v, g, b, cu)
+            scan = pkg.gdr_state_scan(k, w, u, g_cum, h0, cu)
+            fused = pkg.gdr_state_scan_output(q, k, w, u, g_cum, inp.scale, h0, cu)
+            outs[form] = list(scan) + list(fused)
+        else:
+            g_cum, w, u, kg, decay = pkg.kda_chunk_prepare(k, v, g, b, cu)
+            outs[form] = list(pkg.kda_state_scan(kg, w, u, decay, h0, cu))
+        torch.cuda.synchronize()
+    for i, (x, y) in enumerate(zip(outs["0"], outs["1"])):
+        assert torch.equal(x, y), f"{name}: output {i} differs between the dense and the full form"
