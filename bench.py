@@ -76,7 +76,7 @@ def fused_flops(lengths, H, DK, DV):
 
 def source_sha():
     h = hashlib.sha256()
-    for f in ("scan2.hip", "gfx950.hpp", "common.hpp", "kernels.hpp", "plan.cpp"):
+    for f in ("scan2.hip", "gfx950.hpp", "common.hpp", "kernels.hpp", "plan.cpp", "api.cpp"):
         with open(os.path.join(ROOT, "linear_attention_chunked_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -321,7 +321,7 @@ def main():
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": load_traffic(args.workload),
         "kernel": f"gdr state scan with the chunk output fused (bv={tile[0]}, waves={tile[1]}, stages={tile[2]}, "
-                  f"{tile[3]} workgroups)",
+                  f"{tile[3]} workgroups" + (", dense form: three workgroups per CU" if tile[3] > 512 else "") + ")",
         "alg_bytes_per_launch": alg,
         "cache": f"cold: {flush.what} before each of {ROOF_REPS} dedicated steps, outside the events",
         "launch_us_mean": round(cold_mean * 1e3, 2),
