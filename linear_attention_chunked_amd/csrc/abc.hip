@@ -359,7 +359,8 @@ struct AbcStates {
     if constexpr (XB >= 16) {
 #pragma unroll
       for (int i = 0; i < XB / 16; ++i)
-        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t*>(hs + x.lo_o[i]), rh, x.vo_o[i], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t*>(hs + x.lo_o[i]), rh, x.vo_o[i], 0,
+                                               kStreamStore);
     } else {
       __builtin_amdgcn_raw_buffer_store_b64(*reinterpret_cast<const u32x2_t*>(hs + x.lo_o[0]), rh, x.vo_o[0], 0, 0);
     }

@@ -284,7 +284,7 @@ struct ScanBwd {
     for (int i = 0; i < H_PT; ++i) {
       const int v = tid + NT * i;
       const u32x4_t q = *reinterpret_cast<const u32x4_t*>(so + (v / (DK / 8)) * SHS + (v % (DK / 8)) * 16);
-      __builtin_amdgcn_raw_buffer_store_b128(q, rh, 16 * v, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(q, rh, 16 * v, 0, kStreamStore);
     }
     uint16_t* vp = static_cast<uint16_t*>(a.dv) + (tok0 * H + x.hd) * DV + x.col_blk;
     const rsrc_t rv = make_rsrc(vp, a.dv != nullptr ? static_cast<uint32_t>(((nvalid - 1) * H * DV + BV) * 2) : 0u);
@@ -293,7 +293,7 @@ struct ScanBwd {
       const int v = tid + NT * i;
       const int t = v / (BV / 8), p = v % (BV / 8);
       const u32x4_t q = *reinterpret_cast<const u32x4_t*>(so + (OFF_VS - OFF_HS) + t * SVS + p * 16);
-      __builtin_amdgcn_raw_buffer_store_b128(q, rv, static_cast<int>(t * H * DV * 2) + 16 * p, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(q, rv, static_cast<int>(t * H * DV * 2) + 16 * p, 0, kStreamStore);
     }
   }
 
