@@ -253,7 +253,16 @@ template <bool IS_K, int XW, int MODE, bool REV>
 struct AbcStates {
   using S = St<bf16_t>;
   using frag = S::frag;
-  static constexpr int D = 8;             // chunks in flight
+  // HS: the walk stores the pre-chunk states (through the LDS staging
+  // buffers).  The run-end pass (MODE 1) stores nothing: without the staging
+  // buffers and with 4 chunks in flight (132 VGPRs, 41 KB of LDS at XW = 64)
+  // three of its workgroups share a CU, so its 7 x 96 units at B = 2, H = 4,
+  // K = 256, V = 512 run in one round instead of two (whole forward call
+  // 156 -> 148 us, reverse 161 -> 155 us).  The walk itself moves the states
+  // out at about the copy rate with two workgroups per CU (three, with one
+  // staging buffer and 4 chunks in flight, measured the same).
+  static constexpr bool HS = (MODE == 0);
+  static constexpr int D = HS ? 8 : 4;    // chunks in flight
   static constexpr int NR = XW / 16;      // 16-wide blocks of the x dimension = MFMA tiles per wave
   static constexpr int STE = 128 + 32;    // LDS row stride (bytes) of the 64-slot E tile
   static constexpr int STX = XW * 2 + (XW == 64 ? 32 : 16);  // ... and of the x tile
@@ -267,7 +276,7 @@ struct AbcStates {
   struct Smem {
     char x[2][kChunk * STX];  // k or v tile of the chunk, row-major [token][column]
     char e[2][kChunk * STE];  // E, row-major [token][slot]
-    char hs[2][HSZ];          // staged pre-chunk state, by chunk parity
+    char hs[HS ? 2 : 1][HS ? HSZ : 16];  // staged pre-chunk state, by chunk parity
     float r[3][64];           // r_c by chunk modulo 3
   };
 
@@ -372,7 +381,7 @@ struct AbcStates {
     const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int64_t H = a.H, M = a.M;
-    if (MODE == 0) {
+    if constexpr (HS) {
 #pragma unroll
       for (int j = 0; j < NR; ++j)
         *reinterpret_cast<u32x2_t*>(sm.hs[c & 1] + x.lo_h[j]) =
@@ -561,11 +570,11 @@ struct AbcStates {
           stage_in(st[i], st[(i + 1) % D], x, c, sm);
           load(st[i], x, c + D);
           __syncthreads();
-          if (MODE == 0) write_out(x, c - 1, sm);
+          if constexpr (HS) write_out(x, c - 1, sm);
           accumulate(acc, x, c, sm);
         }
       }
-      if (MODE == 0) {
+      if constexpr (HS) {
         __syncthreads();
         write_out(x, x.c_lo + ncp - 1, sm);
       }
