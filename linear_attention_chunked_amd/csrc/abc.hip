@@ -4,11 +4,12 @@
 //
 // Normaliser: z_t = log(e^{z_{t-1}} + e^{s_t}) per slot.  Three levels:
 //   abc_chunk_lse   one workgroup per (b, chunk, h): four waves take 16 tokens
-//                   each (lane = slot), combine through LDS, and write the
-//                   chunk's total (and, when requested, the chunk-local
-//                   running values into z);
+//                   each (lane = slot, every score load issued ahead of the
+//                   chain), combine through LDS, and write the chunk's total
+//                   lse[c] (and, when requested, the chunk-local running
+//                   values into z);
 //   abc_carry       one workgroup per (b, h): zc[c] = logaddexp(zc[c-1], lse[c])
-//                   in four interleaved quarters of the chunk range;
+//                   over 64 stretches of the chunk range in parallel;
 //   abc_weights     one workgroup per (b, chunk, h): the chunk's weights
 //                   E_t = exp(s_t - zc[c]) in the storage dtype, once for all
 //                   the state tiles that use them, and (when z is requested)
@@ -54,69 +55,136 @@ __device__ __forceinline__ float logaddexp_f(float a, float b) {
 __global__ __launch_bounds__(256) void abc_chunk_lse(const AbcArgs a) {
   __shared__ float tot[4][64];
   const int m = threadIdx.x & 63;  // slot (M == 64)
-  const int grp = threadIdx.x >> 6;  // 16-token group
+  const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 16-token group (one per wave)
   const int bx = blockIdx.x;
   const int h = bx % a.H;
   const int c = (bx / a.H) % a.NC;
   const int b = bx / (a.H * a.NC);
-  const uint16_t* s = static_cast<const uint16_t*>(a.s);
   const int t0 = c * kChunk + 16 * grp;
-  const int n = max(0, min(16, a.T - t0));
-  float run[16];
-  float L = -INFINITY;
+  const int n = __builtin_amdgcn_readfirstlane(max(0, min(16, a.T - t0)));  // (uniform: a scalar resource)
+  const int64_t rs = static_cast<int64_t>(a.H) * a.M;  // elements between tokens
+  // the group's 16 scores of slot m, all loads ahead of the chain (tokens
+  // past the end read as zero through the range check and are skipped)
+  const uint16_t* sp = static_cast<const uint16_t*>(a.s) + ((static_cast<int64_t>(b) * a.T + t0) * a.H + h) * a.M;
+  const rsrc_t rsr = make_rsrc(sp, n > 0 ? static_cast<uint32_t>(((n - 1) * rs + a.M) * 2) : 0u);
+  uint16_t v[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (i < n) L = logaddexp_f(L, bf16_to_f32(s[((static_cast<int64_t>(b) * a.T + t0 + i) * a.H + h) * a.M + m]));
-    run[i] = L;
-  }
+  for (int i = 0; i < 16; ++i)
+    v[i] = __builtin_amdgcn_raw_buffer_load_b16(rsr, static_cast<int>((i * rs + m) * 2), 0, 0);
+  // the group's total as max + log(sum of exp(x - max)): independent exponentials
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (i < n) mx = fmaxf(mx, bf16_to_f32(v[i]));
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (i < n) sum += exp_fast(bf16_to_f32(v[i]) - mx);
+  const float L = n > 0 ? mx + 0.69314718055994531f * __builtin_amdgcn_logf(sum) : -INFINITY;
   tot[grp][m] = L;
   __syncthreads();
   float off = -INFINITY;
   for (int g = 0; g < grp; ++g) off = logaddexp_f(off, tot[g][m]);
-  if (a.z != nullptr) {
+  if (a.z != nullptr) {  // the chunk-local running values (a chain, only when z is requested)
+    float run = off;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (i < n) a.z[((static_cast<int64_t>(b) * a.T + t0 + i) * a.H + h) * a.M + m] = logaddexp_f(off, run[i]);
+      if (i < n) {
+        run = logaddexp_f(run, bf16_to_f32(v[i]));
+        a.z[((static_cast<int64_t>(b) * a.T + t0 + i) * a.H + h) * a.M + m] = run;
+      }
   }
   if (grp == 3) a.lse[((static_cast<int64_t>(b) * a.NC + c) * a.H + h) * a.M + m] = logaddexp_f(off, L);
 }
 
-__global__ __launch_bounds__(256) void abc_carry(const AbcArgs a) {
-  // pass 1: each quarter's total; pass 2: each quarter re-runs its chain from
-  // the log-sum-exp of the quarters before it and writes zc
-  __shared__ float tot[4][64];
-  const int m = threadIdx.x & 63;
-  const int q = threadIdx.x >> 6;  // quarter of the chunk range
+__global__ __launch_bounds__(1024) void abc_carry(const AbcArgs a) {
+  // zc[c] = logaddexp(zc[c-1], lse[c]) per slot (M == 64).  Thread (s, p):
+  // slots 4p .. 4p + 3 (16-byte loads and stores) of stretch s, one of 64
+  // contiguous stretches of the chunk range.  Pass 1 forms each stretch's
+  // total as max + log(sum of exp(x - max)); an inclusive scan of the stretch
+  // totals in LDS (six doubling steps) gives each stretch the total of the
+  // ones before it; pass 2 re-runs the stretch's chain from there and writes
+  // zc.  Stretches of up to 8 chunks stay in registers (up to 512 chunks per
+  // call); longer ones read their totals again in pass 2.
+  __shared__ f32x4_t tot[2][64][16];
+  const int tid = threadIdx.x;
+  const int p = tid & 15, st = tid >> 4;
   const int h = blockIdx.x % a.H;
   const int b = blockIdx.x / a.H;
-  const int per = (a.NC + 3) / 4;
-  const int c0 = min(a.NC, q * per), c1 = min(a.NC, c0 + per);
-  const float* lse = a.lse + (static_cast<int64_t>(b) * a.NC * a.H + h) * a.M + m;
-  float* zc = a.zc + (static_cast<int64_t>(b) * a.NC * a.H + h) * a.M + m;
+  const int per = (a.NC + 63) / 64;
+  const int c0 = min(a.NC, st * per), c1 = min(a.NC, c0 + per);
   const int64_t step = static_cast<int64_t>(a.H) * a.M;
-  auto chain = [&](float z, bool write) {
-    int c = c0;
-    for (; c + 8 <= c1; c += 8) {  // eight independent loads ahead of the serial chain
-      float l[8];
+  const int64_t row0 = (static_cast<int64_t>(b) * a.NC * a.H + h) * a.M + 4 * p;
+  auto lse_at = [&](int c) { return *reinterpret_cast<const f32x4_t*>(a.lse + row0 + c * step); };
+  auto lae4 = [](f32x4_t x, f32x4_t y) {
+    f32x4_t r;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) l[i] = lse[(c + i) * step];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        z = logaddexp_f(z, l[i]);
-        if (write) zc[(c + i) * step] = z;
-      }
-    }
-    for (; c < c1; ++c) {
-      z = logaddexp_f(z, lse[c * step]);
-      if (write) zc[c * step] = z;
-    }
-    return z;
+    for (int j = 0; j < 4; ++j) r[j] = logaddexp_f(x[j], y[j]);
+    return r;
   };
-  tot[q][m] = chain(-INFINITY, false);
+  constexpr int R = 8;
+  const int nr = min(R, c1 - c0);
+  f32x4_t l[R];
+  {
+    // one resource for the (b, h) slice (uniform, so no per-lane descriptors);
+    // chunks past this stretch are masked below, past the slice read as zero
+    const float* bh = a.lse + (static_cast<int64_t>(b) * a.NC * a.H + h) * a.M;
+    const rsrc_t rl = make_rsrc(bh, static_cast<uint32_t>(((a.NC - 1) * step + a.M) * 4));
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      l[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rl, static_cast<int>(((c0 + i) * step + 4 * p) * 4), 0, 0));
+  }
+  const f32x4_t ninf{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  f32x4_t mx = ninf;
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (i < nr)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx[j] = fmaxf(mx[j], l[i][j]);
+  for (int c = c0 + R; c < c1; ++c) {
+    const f32x4_t v = lse_at(c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx[j] = fmaxf(mx[j], v[j]);
+  }
+  f32x4_t sm{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (i < nr)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm[j] += exp_fast(l[i][j] - mx[j]);
+  for (int c = c0 + R; c < c1; ++c) {
+    const f32x4_t v = lse_at(c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sm[j] += exp_fast(v[j] - mx[j]);
+  }
+  f32x4_t t;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    t[j] = mx[j] == -INFINITY ? -INFINITY : mx[j] + 0.69314718055994531f * __builtin_amdgcn_logf(sm[j]);
+  tot[0][st][p] = t;
   __syncthreads();
-  float off = -INFINITY;
-  for (int g = 0; g < q; ++g) off = logaddexp_f(off, tot[g][m]);
-  chain(off, true);
+  int src = 0;
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) {
+    f32x4_t v = tot[src][st][p];
+    if (st >= d) v = lae4(tot[src][st - d][p], v);
+    tot[src ^ 1][st][p] = v;
+    src ^= 1;
+    __syncthreads();
+  }
+  f32x4_t z = st > 0 ? tot[src][st - 1][p] : ninf;
+  float* zc = a.zc + row0;
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (i < nr) {
+      z = lae4(z, l[i]);
+      *reinterpret_cast<f32x4_t*>(zc + (c0 + i) * step) = z;
+    }
+  for (int c = c0 + R; c < c1; ++c) {
+    z = lae4(z, lse_at(c));
+    *reinterpret_cast<f32x4_t*>(zc + c * step) = z;
+  }
 }
 
 __global__ __launch_bounds__(256) void abc_weights(const AbcArgs a) {
@@ -658,7 +726,7 @@ hipError_t launch_abc(const AbcArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (a.NC > 0) {
-    hipLaunchKernelGGL(abc_carry, dim3(a.B * a.H), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(abc_carry, dim3(a.B * a.H), dim3(1024), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
