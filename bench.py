@@ -128,8 +128,9 @@ class HipEvent:
         return ms.value
 
     def __del__(self):
-        if HipEvent._hip is not None and self.ev:
-            HipEvent._hip.hipEventDestroy(self.ev)
+        hip = getattr(HipEvent, "_hip", None) if HipEvent is not None else None
+        if hip is not None and self.ev:  # (at interpreter exit the module's globals may already be gone)
+            hip.hipEventDestroy(self.ev)
 
 
 class Evictor:

@@ -112,3 +112,13 @@ def test_abc_runs(pkg, monkeypatch, runs):
             assert torch.equal(outs[64][key], outs[xw][key]), (runs, xw, key)
     d = inp.f64()
     compare(outs[64], oracle.abc_recurrent_fp64(d["k"], d["v"], d["s"]), what=f"abc runs={runs}")
+
+
+def test_abc_long_carry(pkg):
+    """More than 512 chunks in one row: the normaliser carry's stretches are
+    longer than the part it keeps in registers (its second read of the chunk
+    totals), and the state runs are longer than in the benchmark shape."""
+    inp = make_abc(990, B=1, T=40000, H=1, K=64, M=64, V=64)
+    d = inp.f64()
+    ref = oracle.abc_recurrent_fp64(d["k"], d["v"], d["s"])
+    compare(run(pkg, inp), ref, what="abc T=40000")
