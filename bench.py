@@ -76,7 +76,7 @@ def fused_flops(lengths, H, DK, DV):
 
 def source_sha():
     h = hashlib.sha256()
-    for f in ("scan2.hip", "gfx950.hpp", "common.hpp", "kernels.hpp", "plan.cpp", "api.cpp"):
+    for f in ("scan2.hip", "gfx950.hpp", "common.hpp", "kernels.hpp", "plan.cpp", "api.cpp", "wy_core.hpp"):
         with open(os.path.join(ROOT, "linear_attention_chunked_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

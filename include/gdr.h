@@ -183,6 +183,22 @@ gdr_status gdr_state_scan_output(const gdr_problem* p, const gdr_tile* tile, con
                                  const float* g_cum, const float* h0, float scale, void* h,
                                  void* v_new, float* hT, void* o, void* stream);
 
+/* The whole forward step of the chunkwise form in one pass over the chunks:
+ * the chunk prepare (gdr_chunk_prepare: gamma, the WY factors w and u), the
+ * state scan (gdr_state_scan) and the chunk output (gdr_chunk_output), with
+ * w and u formed per chunk on chip instead of going through memory.  The
+ * same arithmetic as gdr_chunk_prepare followed by gdr_state_scan_output, so
+ * o, h, v_new, hT and g_cum are the same bits.  bfloat16 storage, DK = 128,
+ * DV a multiple of 64 (64-column blocks, four waves); any other problem
+ * returns GDR_ERR_UNSUPPORTED (run the two calls).  Arguments as in those
+ * calls: q, k [B, T, H, DK], v [B, T, H, DV], g, beta [B, T, H] (FP32), h0
+ * (nullable), o [B, T, H, DV]; g_cum, h, v_new and hT may be NULL (not
+ * written).  Plain pass only (no segments); indexed states as in
+ * gdr_state_scan.  No workspace. */
+gdr_status gdr_chunk_forward(const gdr_problem* p, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, const float* h0, float scale,
+                             float* g_cum, void* h, void* v_new, float* hT, void* o, void* stream);
+
 /* Segment summaries, the pre-scan of [cuLA#127] ("Root cause and
  * implementation"): each sequence is split into n_segments chunk-aligned
  * segments (NT_n chunks dealt out evenly, the first NT_n mod P segments one

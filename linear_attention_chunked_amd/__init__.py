@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     abc_workspace_size,
     chunk_gated_delta_rule,
     gdr_chunk_dv_local,
+    gdr_chunk_forward,
     gdr_chunk_output,
     gdr_chunk_prepare,
     gdr_num_chunks,

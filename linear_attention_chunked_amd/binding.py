@@ -75,6 +75,8 @@ _SIGS = {
     "gdr_state_scan_output": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile),
                                              ctypes.POINTER(gdr_segments), _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                              _P, _P, _P, _P, _P]),
+    "gdr_chunk_forward": (ctypes.c_int, [ctypes.POINTER(gdr_problem), _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                         _P, _P, _P, _P, _P, _P]),
     "gdr_segment_summaries": (ctypes.c_int, [ctypes.POINTER(gdr_problem), ctypes.POINTER(gdr_tile), ctypes.c_int32,
                                              _P, _P, _P, _P, _P, _P, _P]),
     "gdr_segment_summaries_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(gdr_problem), ctypes.c_int32]),
@@ -336,6 +338,51 @@ def gdr_state_scan_output(q, k, w, u, g_cum, scale: float = 1.0, h0=None, cu_seq
                                        _ptr(h), _ptr(v_new), _ptr(hT), _ptr(o), _stream(stream)),
            "gdr_state_scan_output")
     return o, h, v_new, hT
+
+
+def gdr_chunk_forward(q, k, v, g, beta, scale: float = 1.0, h0=None, cu_seqlens=None, state_layout: str = "kv",
+                      emit_g_cum: bool = True, emit_h: bool = True, emit_v_new: bool = True, emit_final: bool = True,
+                      out=None, state_indices=None, stream=None):
+    """The forward step in one kernel (chunk prepare, state scan and chunk
+    output fused): returns (o, g_cum | None, h | None, v_new | None, hT | None),
+    the same bits as ``gdr_chunk_prepare`` followed by
+    ``gdr_state_scan_output``.  bfloat16, DK = 128, DV a multiple of 64 (else
+    GdrError GDR_ERR_UNSUPPORTED).  ``out`` may hold preallocated "o",
+    "g_cum", "h", "v_new" and "hT"; other arguments as in ``gdr_state_scan``."""
+    DV = v.shape[-1]
+    out = out or {}
+    pool_size = 0
+    if state_indices is not None:
+        if emit_final and out.get("hT") is None:
+            raise ValueError("indexed states write into a pool: pass out={'hT': pool}")
+        pool_size = _pool_size(h0, out.get("hT") if emit_final else None, k, DV, state_layout)
+    p = Problem(k, DV, cu_seqlens, state_layout, state_indices, pool_size)
+    nt = gdr_num_chunks(k, DV, cu_seqlens)
+    o = out.get("o")
+    if o is None:
+        o = torch.empty_like(v)
+    g_cum = h = v_new = hT = None
+    if emit_g_cum:
+        g_cum = out.get("g_cum")
+        if g_cum is None:
+            g_cum = torch.empty(g.shape, dtype=torch.float32, device=k.device)
+    if emit_h:
+        h = out.get("h")
+        if h is None:
+            h = torch.empty((nt, p.H, DV, p.DK), dtype=k.dtype, device=k.device)
+    if emit_v_new:
+        v_new = out.get("v_new")
+        if v_new is None:
+            v_new = torch.empty_like(v)
+    if emit_final:
+        hT = out.get("hT")
+        if hT is None:
+            shape = (p.N, p.H, DV, p.DK) if state_layout == "vk" else (p.N, p.H, p.DK, DV)
+            hT = torch.empty(shape, dtype=torch.float32, device=k.device)
+    _check(lib().gdr_chunk_forward(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), float(scale),
+                                   _ptr(g_cum), _ptr(h), _ptr(v_new), _ptr(hT), _ptr(o), _stream(stream)),
+           "gdr_chunk_forward")
+    return o, g_cum, h, v_new, hT
 
 
 def gdr_chunk_output(q, k, v_new, h, g_cum, scale: float = 1.0, cu_seqlens=None, stream=None) -> torch.Tensor:

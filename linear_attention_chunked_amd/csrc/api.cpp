@@ -282,6 +282,57 @@ gdr_status gdr_state_scan_output(const gdr_problem* p, const gdr_tile* tile, con
   return gdr_chunk_output(p, q, k, v_new, h, g_cum, scale, o, stream);
 }
 
+gdr_status gdr_chunk_forward(const gdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const float* h0, float scale, float* g_cum, void* h, void* v_new,
+                             float* hT, void* o, void* stream) {
+  g_err.clear();
+  gdr::Problem pr;
+  GDR_TRY(parse(p, pr));
+  GDR_TRY(need(q, "q"));
+  GDR_TRY(need(k, "k"));
+  GDR_TRY(need(v, "v"));
+  GDR_TRY(need(g, "g"));
+  GDR_TRY(need(beta, "beta"));
+  GDR_TRY(need(o, "o"));
+  GDR_TRY(opt(h0, "h0"));
+  GDR_TRY(opt(g_cum, "g_cum"));
+  GDR_TRY(opt(h, "h"));
+  GDR_TRY(opt(v_new, "v_new"));
+  GDR_TRY(opt(hT, "hT"));
+  if (pr.dtype != GDR_BF16 || pr.DK != 128 || pr.DV % 64 != 0)
+    return fail(GDR_ERR_UNSUPPORTED, "the fused forward step is built for bfloat16, DK = 128, DV a multiple of 64");
+  gdr::LaunchFn fn = gdr::find_scan2_prep(pr.DK);
+  if (fn == nullptr) return fail(GDR_ERR_UNSUPPORTED, "no fused forward kernel for this DK");
+  const gdr::Tile t{64, 4, 2};
+  gdr::ScanArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.g_cum_out = g_cum;
+  a.q = q;
+  a.o = o;
+  a.scale = scale;
+  a.h_in = h0;
+  a.h = h;
+  a.v_new = v_new;
+  a.h_out = hT;
+  a.H = pr.H;
+  a.DV = pr.DV;
+  a.in_vk = pr.state_vk;
+  a.out_vk = pr.state_vk;
+  a.n_blk = gdr::scan_blocks(pr, t, 0);
+  for (const gdr::Launch& l : gdr::plan_scan(pr, t, 0, 1, h0 != nullptr, hT != nullptr)) {
+    if (l.grid == 0) continue;
+    a.n_rows = static_cast<int32_t>(l.rows.size());
+    memcpy(a.rows, l.rows.data(), l.rows.size() * sizeof(gdr::Row));
+    hipError_t e = fn(&a, l.grid, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+  }
+  return GDR_OK;
+}
+
 gdr_status gdr_chunk_output(const gdr_problem* p, const void* q, const void* k, const void* v_new, const void* h,
                             const float* g_cum, float scale, void* o, void* stream) {
   g_err.clear();

@@ -24,6 +24,12 @@ struct ScanArgs {
   const void* q;       // fused chunk output (scan2 with FO): queries, output o, scale
   void* o;
   float scale;
+  // prepare fused in (scan2 with PREP): v, g, beta in place of w, u, g_cum;
+  // g_cum_out (nullable) receives the chunk-local cumsum of g
+  const void* v;
+  const float* g;
+  const float* beta;
+  float* g_cum_out;
   int32_t H;
   int32_t DV;
   int32_t in_vk;       // layout of h_in: 1 = [.., DV, DK], 0 = [.., DK, DV]
@@ -160,6 +166,9 @@ LaunchFn find_scan2_fused(int dk, int bv, int waves, int stages);  // plain pass
 // The same plain pass (optionally with per-channel decay or the fused output)
 // in its dense form, three workgroups per CU; null where there is none.
 LaunchFn find_scan2_dense(int dk, int bv, int waves, int stages, int mode, bool kd, bool fo);
+// The plain pass with the chunk prepare and the chunk output fused (bf16,
+// DK = 128, 64-column blocks, four waves, the dense form).
+LaunchFn find_scan2_prep(int dk);
 LaunchFn find_prepare(int dtype, int dk, int dv);
 LaunchFn find_prepare2(int dk, int dv);
 LaunchFn find_kda_prepare(int dk, int dv);

@@ -69,10 +69,12 @@
 //     each lane four consecutive value columns of one token: 8-byte stores.
 #include "gfx950.hpp"
 #include "kernels.hpp"
+#include "wy_core.hpp"
 
 namespace gdr {
 
-template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false, bool DENSE = false>
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false, bool DENSE = false,
+          bool PREP = false>
 struct Scan2 {
   using S = St<bf16_t>;
   using frag = S::frag;
@@ -99,7 +101,10 @@ struct Scan2 {
   static constexpr int OFF_DEC = OFF_D + (kChunk + 4) * 4;  // KD: the chunk's DK channel decays
   static constexpr bool SIG = (MODE != 0) && !KD;           // scaled-state form (summaries)
   static constexpr int OFF_GM = OFF_DEC + (KD ? DK * 4 : 0);  // FO: the chunk's gamma (zero past the tail)
-  static constexpr int BUF = OFF_GM + (FO ? kChunk * 4 : 0);
+  // PREP: the chunk's gamma, beta and beta e^gamma for the WY factors (the
+  // A / T scratch takes the W tile's place until w replaces it)
+  static constexpr int OFF_PG = OFF_GM + (FO ? kChunk * 4 : 0);
+  static constexpr int BUF = OFF_PG + (PREP ? 3 * kChunk * 4 : 0);
   // Output staging (single-buffer loop, plain and segmented passes): the
   // chunk's h block and v_new tile are written to LDS in their memory layout
   // and leave the next iteration as whole 16-byte vectors per lane (the h
@@ -126,12 +131,16 @@ struct Scan2 {
   static_assert(!STAGE || ((BV * DK / 8) % NT == 0 && (kChunk * BV / 8) % NT == 0), "staged outputs split evenly");
   static_assert(!FO || (STAGE && NW == 4 && !KD), "the fused output runs on the staged plain pass, one token tile per wave");
   static_assert(!DENSE || ALIAS, "the dense form needs the staging to fit the W and U tiles");
+  static_assert(!PREP || (FO && MODE == 0 && NBUF == 1 && NW == 4 && !KD && UBV % 16 == 0),
+                "the prepare is fused into the staged plain pass with the chunk output, four waves");
+  static_assert(!PREP || WyCore<DK>::kTri * 4 <= kChunk * SW, "the A / T scratch fits the W tile");
 
   struct Stage {
-    u32x4_t w[W_PT];
+    u32x4_t w[PREP ? 1 : W_PT];
     u32x4_t k[W_PT];
-    u32x4_t u[U_PT];
-    float g;
+    u32x4_t u[U_PT];  // PREP: the block's columns of v
+    float g;          // g_cum (PREP: g) of token threadIdx.x
+    float b;          // PREP: beta of token threadIdx.x
   };
 
   struct Ctx {
@@ -154,8 +163,22 @@ struct Scan2 {
     const uint32_t wk_bytes = live ? static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2) : 0u;
     const uint16_t* wp = static_cast<const uint16_t*>(a.w) + (tok0 * H + x.hd) * DK;
     const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (tok0 * H + x.hd) * DK;
-    const rsrc_t rw = make_rsrc(wp, wk_bytes);
     const rsrc_t rk = make_rsrc(kp, wk_bytes);
+    if constexpr (PREP) {
+#pragma unroll
+      for (int i = 0; i < W_PT; ++i) st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, x.vo_wk[i], 0, 0);
+      const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + x.hd) * x.DV + x.col_blk;
+      const rsrc_t rv = make_rsrc(vp, live ? static_cast<uint32_t>(((nvalid - 1) * H * x.DV + UBV) * 2) : 0u);
+#pragma unroll
+      for (int i = 0; i < U_PT; ++i) st.u[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, x.vo_u[i], 0, 0);
+      const uint32_t gb = live ? static_cast<uint32_t>(((nvalid - 1) * H + 1) * 4) : 0u;
+      const int go = static_cast<int>(threadIdx.x * H * 4);
+      st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.g + tok0 * H + x.hd, gb), go, 0, 0));
+      st.b = __builtin_bit_cast(float,
+                                __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.beta + tok0 * H + x.hd, gb), go, 0, 0));
+      return;
+    }
+    const rsrc_t rw = make_rsrc(wp, wk_bytes);
 #pragma unroll
     for (int i = 0; i < W_PT; ++i) st.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, x.vo_wk[i], 0, 0);
 #pragma unroll
@@ -177,8 +200,38 @@ struct Scan2 {
     }
   }
 
-  __device__ static __forceinline__ void store(const Stage& st, const Ctx& x, char* buf, int nvalid, float& sig) {
+  __device__ static __forceinline__ void store(const Stage& st, const Ctx& x, char* buf, int nvalid, float& sig,
+                                               int64_t tok0 = 0) {
     const int tid = threadIdx.x;
+    if constexpr (PREP) {  // K and V tiles; the first wave forms gamma, beta, the decay weights
+#pragma unroll
+      for (int i = 0; i < W_PT; ++i) {
+        const int v = tid + i * NT;
+        const int r = v / CPW, c = v % CPW;
+        *reinterpret_cast<u32x4_t*>(buf + OFF_K + r * SK + c * 16) = st.k[i];
+      }
+#pragma unroll
+      for (int i = 0; i < U_PT; ++i) {
+        const int v = tid + i * NT;
+        if ((kChunk * CPU) % NT == 0 || v < kChunk * CPU) {
+          const int r = v / CPU, c = v % CPU;
+          *reinterpret_cast<u32x4_t*>(buf + OFF_U + r * SU + c * 16) = st.u[i];
+        }
+      }
+      if (tid < kChunk) {
+        float* pg = reinterpret_cast<float*>(buf + OFF_PG);
+        const float gam = WyCore<DK>::gamma_beta(st.g, st.b, nvalid, pg, pg + kChunk, pg + 2 * kChunk);
+        const ScanArgs& a = *x.a;
+        if (a.g_cum_out != nullptr && tid < nvalid) a.g_cum_out[(tok0 + tid) * x.H + x.hd] = gam;
+        const float g_last = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), max(nvalid, 1) - 1));
+        float* d = reinterpret_cast<float*>(buf + OFF_D);
+        d[tid] = (tid < nvalid) ? -exp_fast(g_last - gam) : 0.f;
+        if (tid == 0) d[kChunk] = exp_fast(g_last);
+        reinterpret_cast<float*>(buf + OFF_GM)[tid] = (tid < nvalid) ? gam : 0.f;
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < W_PT; ++i) {
       const int v = tid + i * NT;
@@ -221,6 +274,39 @@ struct Scan2 {
       }
       if constexpr (FO) reinterpret_cast<float*>(buf + OFF_GM)[tid] = (tid < nvalid) ? st.g : 0.f;
     }
+  }
+
+  // PREP: the chunk's w and u from the K and V tiles (wy_core.hpp), into the
+  // W tile and the U tile (V's place) in the layout the loads give; the
+  // A / T scratch sits in the W tile until w replaces it.  Starts after the
+  // barrier that follows store(); ends with a barrier.
+  __device__ static __forceinline__ void prep_wy(char* buf) {
+    using W = WyCore<DK>;
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    float* t = reinterpret_cast<float*>(buf + OFF_W);
+    const float* pg = reinterpret_cast<const float*>(buf + OFF_PG);
+    W::gram_diag(buf + OFF_K, SK, t, pg, pg + kChunk);
+    __syncthreads();
+    W::off_diag(t);
+    frag hw[2], lw[2], hu[2], lu[2];
+    W::row_frags(t, pg + 2 * kChunk, hw, lw);  // T diag(beta e^gamma)
+    W::row_frags(t, pg + kChunk, hu, lu);      // T diag(beta)
+    __syncthreads();  // T is read: w takes the W tile
+    const int row = 16 * wave + c16;
+    char* wrow = buf + OFF_W + row * SW + 8 * g4;
+    W::template product<DK>(buf + OFF_K, SK, hw, lw, [&](int dt, const f32x4_t& acc) {
+      *reinterpret_cast<u32x2_t*>(wrow + 32 * dt) = u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    });
+    f32x4_t uacc[UBV / 16];
+    W::template product<UBV>(buf + OFF_U, SU, hu, lu, [&](int dt, const f32x4_t& acc) { uacc[dt] = acc; });
+    __syncthreads();  // every wave has read V: u takes the U tile
+    char* urow = buf + OFF_U + row * SU + 8 * g4;
+#pragma unroll
+    for (int dt = 0; dt < UBV / 16; ++dt)
+      *reinterpret_cast<u32x2_t*>(urow + 32 * dt) =
+          u32x2_t{pack_bf16x2(uacc[dt][0], uacc[dt][1]), pack_bf16x2(uacc[dt][2], uacc[dt][3])};
+    __syncthreads();
   }
 
   // FO: the chunk output of token tile `wave` over the block's BV columns
@@ -581,9 +667,10 @@ struct Scan2 {
           __syncthreads();
           if (STAGE && c > 0) write_out(x, row, c - 1, so);
           if constexpr (ALIAS) __syncthreads();  // the staged outputs have left before the tiles refill them
-          store(st, x, buf0, nv_of(c), sig);
+          store(st, x, buf0, nv_of(c), sig, tok_of(c));
           __syncthreads();
           if (c + 1 < nchunks) load(st, x, tok_of(c + 1), nv_of(c + 1), hr_of(c + 1));
+          if constexpr (PREP) prep_wy(buf0);
           step(c, buf0, so);
         }
         if (STAGE) {
@@ -747,16 +834,19 @@ struct Scan2 {
   }
 };
 
-template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false, bool DENSE = false>
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false, bool DENSE = false,
+          bool PREP = false>
 __global__ __launch_bounds__(NW * 64, DENSE ? 3 : 1) void scan2_kernel(const ScanArgs a) {
-  using K = Scan2<DK, BV, NW, PF, MODE, NBUF, KD, FO, DENSE>;
+  using K = Scan2<DK, BV, NW, PF, MODE, NBUF, KD, FO, DENSE, PREP>;
   __shared__ __align__(16) char smem[K::SMEM];
   K::run(a, smem);
 }
 
-template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false, bool DENSE = false>
+template <int DK, int BV, int NW, int PF, int MODE, int NBUF, bool KD, bool FO = false, bool DENSE = false,
+          bool PREP = false>
 static hipError_t launch_scan2(const void* args, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((scan2_kernel<DK, BV, NW, PF, MODE, NBUF, KD, FO, DENSE>), dim3(grid), dim3(NW * 64), 0, stream,
+  hipLaunchKernelGGL((scan2_kernel<DK, BV, NW, PF, MODE, NBUF, KD, FO, DENSE, PREP>), dim3(grid), dim3(NW * 64), 0,
+                     stream,
                      *static_cast<const ScanArgs*>(args));
   return hipGetLastError();
 }
@@ -811,6 +901,14 @@ LaunchFn find_scan2_dense(int dk, int bv, int waves, int stages, int mode, bool 
     return fo ? &launch_scan2<64, 64, 4, 1, 0, 1, false, true, true>
               : (kd ? &launch_scan2<64, 64, 4, 1, 0, 1, true, false, true> : &launch_scan2<64, 64, 4, 1, 0, 1, false, false, true>);
   return nullptr;
+}
+
+// The plain pass with the chunk prepare and the chunk output fused: the
+// dense form only (with the prepare, the full form holds 253 VGPRs, one
+// workgroup per CU).
+LaunchFn find_scan2_prep(int dk) {
+  if (dk == 128) return &launch_scan2<128, 64, 4, 1, 0, 1, false, true, true, true>;
+  return nullptr;  // (DK = 64: the A / T scratch does not fit the W tile)
 }
 
 }  // namespace gdr

@@ -395,3 +395,21 @@ def test_state_scan_auto_validates_before_launch():
     assert L.gdr_state_scan_auto(ctypes.byref(p), *args, FAKE, None, ws, None) == B.GDR_ERR_INVALID_ARG
     assert L.gdr_state_scan_auto(ctypes.byref(p), *args, FAKE, FAKE, ws - 16, None) == B.GDR_ERR_INVALID_ARG
     assert "workspace" in L.gdr_last_error().decode()
+
+
+def _fwd(p, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE):
+    return B.lib().gdr_chunk_forward(ctypes.byref(p), q, k, v, g, beta, None, ctypes.c_float(1.0), None, None, None,
+                                     None, o, None)
+
+
+def test_chunk_forward_validation():
+    """The fused forward step checks its arguments before any launch: missing
+    inputs are invalid, and problems outside its build (float32 storage,
+    DK = 64, DV not a multiple of 64) are unsupported."""
+    p, keep = _prob()
+    for kw in ("q", "k", "v", "g", "beta", "o"):
+        assert _fwd(p, **{kw: None}) == B.GDR_ERR_INVALID_ARG, kw
+    q, keep3 = _prob(dtype=B.GDR_F32)
+    assert _fwd(q) == B.GDR_ERR_UNSUPPORTED
+    q, keep4 = _prob(DK=64)
+    assert _fwd(q) == B.GDR_ERR_UNSUPPORTED
