@@ -449,8 +449,14 @@ def sweep(pkg, torch, dev):
     from workloads import make_config
 
     tiles = [(32, 2, 2), (32, 2, 3), (64, 2, 3), (64, 4, 2), (64, 4, 3), (128, 4, 2), (128, 4, 3)]
-    for name in ("question_rows", "new_states"):
-        inp = make_config(name)
+    # the named packed workloads, the same lengths at 48 heads and at
+    # dk = dv = 64, and two long rows at 8 heads
+    cases = [("question_rows", {}), ("question_rows", {"H": 48}), ("question_rows", {"DK": 64, "DV": 64}),
+             ("new_states", {}), ("new_states", {"H": 48}), ("new_states", {"DK": 64, "DV": 64}),
+             ("long_state_h8", {"B": 2, "T": 16384})]
+    for name, over in cases:
+        inp = make_config(name, **over)
+        label = name + "".join(f" {k}={v}" for k, v in over.items())
         k, v, g, b = (x.to(dev) for x in (inp.k, inp.v, inp.g, inp.beta))
         h0 = inp.h0.to(dev) if inp.h0 is not None else None
         cu = inp.cu_seqlens
@@ -459,9 +465,12 @@ def sweep(pkg, torch, dev):
         out = {"h": h, "v_new": v_new, "hT": hT}
         default = pkg.gdr_plan_query(k, v.shape[-1], cu)[:3]
         for t in tiles:
+            if t[0] > v.shape[-1]:
+                continue
             us = _event_median_us(torch, lambda: pkg.gdr_state_scan(k, w, u, g_cum, h0, cu, t, out=out))
-            print(json.dumps({"sweep": "state scan", "workload": name, "tile": t, "default": tuple(default) == t,
+            print(json.dumps({"sweep": "state scan", "workload": label, "tile": t, "default": tuple(default) == t,
                               "us": round(us, 1)}), flush=True)
+        del k, v, g, b, g_cum, w, u, h, v_new, hT, out
     inp = make_config("long_state_h8")
     k, v, g, b = (x.to(dev) for x in (inp.k, inp.v, inp.g, inp.beta))
     g_cum, w, u = pkg.gdr_chunk_prepare(k, v, g, b)

@@ -160,14 +160,25 @@ bool choose_tile(const Problem& p, const int32_t* req, int mode, int64_t rows, T
     // 174 us for 64-column blocks), and once one 8-wave block of all 256
     // columns per (segment, head) fills them, that block (two waves per SIMD,
     // K and W staged once per segment-head) wins again (32 segments x 8
-    // heads: 108 us against 128 us).
+    // heads: 108 us against 128 us).  In the plain pass, once 64-column
+    // blocks would exceed two per CU (the dense form, three sharing a CU) on
+    // long rows (16 chunks or more per row on average), 128-column blocks
+    // win: their serial chains share a CU with fewer others (8 rows of 1.3K
+    // to 3.6K tokens x 48 heads: 295 us against 323 us; at 32 heads, 512
+    // blocks of 64 columns, 218 us against 243 us; 24 short rows x 48 heads:
+    // 95 us against 105 us).
     const int64_t pairs = rows * p.H;
     const int64_t units64 = pairs * ((mode == 1 ? p.DV + p.DK : p.DV) / 64);
+    const bool long_rows = rows > 0 && p.n_chunks >= 16 * static_cast<int64_t>(p.N);
     if (p.dtype == 1) {
       r[0] = 64;
       r[1] = 4;
       r[2] = 2;
-      if (units64 < 64) {
+      if (mode == 0 && p.DV % 128 == 0 && units64 > 512 && long_rows) {
+        r[0] = 128;
+        r[1] = 4;
+        r[2] = 2;
+      } else if (units64 < 64) {
         r[0] = 32;
         r[1] = 2;
         r[2] = 2;

@@ -413,3 +413,25 @@ def test_chunk_forward_validation():
     assert _fwd(q) == B.GDR_ERR_UNSUPPORTED
     q, keep4 = _prob(DK=64)
     assert _fwd(q) == B.GDR_ERR_UNSUPPORTED
+
+
+def test_plan_table_long_rows():
+    """The plain pass takes 128-column blocks when 64-column blocks would exceed
+    two per CU on long rows (16+ chunks per row on average), else 64-column
+    blocks of four waves (the measured sweep behind the table)."""
+    def packed(lengths, H, DK=128, DV=128):
+        cu = [0]
+        for n in lengths:
+            cu.append(cu[-1] + n)
+        return _prob(T=cu[-1], cu=cu, H=H, DK=DK, DV=DV)
+
+    long8 = [1306, 1359, 1827, 1941, 2295, 2410, 3526, 3597]
+    p, keep = packed(long8, 48)
+    assert _query(p)[:3] == (128, 4, 2)
+    p, keep = packed(long8, 32)  # 512 blocks of 64 columns: two per CU
+    assert _query(p)[:3] == (64, 4, 2)
+    p, keep = packed(long8, 48, DK=64, DV=64)  # one 64-column block per (row, head)
+    assert _query(p)[:3] == (64, 4, 2)
+    short = [16 + (37 * i) % 240 for i in range(24)]
+    p, keep = packed(short, 48)
+    assert _query(p)[:3] == (64, 4, 2)
