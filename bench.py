@@ -565,6 +565,20 @@ def long_state(pkg, torch, dev, name="long_state_h8", reps=5, copy_gbs=None, cp_
                     "serial_alg_bytes": serial_alg, "frac_of_hbm_at_serial_bytes": round(serial_alg / t / 8e12, 4)}
     t = res["segmented"]["us"] * 1e-6
     res["segmented"].update(alg_bytes=seg_alg, frac_of_hbm=round(seg_alg / t / 8e12, 4), segments=P)
+    # the same pass through the scheduler's entry point (gdr_state_scan_auto:
+    # it picks the segment count), workspace allocated once
+    ap = L.gdr_plan_segments(pr.ref)
+    aws_bytes = int(L.gdr_state_scan_auto_workspace_size(pr.ref))
+    aws = torch.empty(max(aws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    def auto():
+        B._check(L.gdr_state_scan_auto(pr.ref, None, ptr(k), ptr(w), ptr(u), ptr(g_cum), None, 1.0, ptr(h),
+                                       ptr(v_new), ptr(hT), None, ptr(aws), aws_bytes, sp), "auto")
+
+    ta = _event_median_us(torch, auto, reps=reps) * 1e-6
+    res["segmented_auto"] = {"us": round(ta * 1e6, 1), "segments": int(ap),
+                             "Mtok_head_per_s": round(inp.token_heads / ta / 1e6, 1),
+                             "alg_bytes": seg_alg, "frac_of_hbm": round(seg_alg / ta / 8e12, 4)}
     if copy_gbs:
         res["segmented"]["frac_of_copy"] = round(seg_alg / t / 1e9 / copy_gbs, 4)
     # each phase alone (the buffers hold the previous phases' outputs)

@@ -469,3 +469,38 @@ def test_auto_segmentation(pkg, name, want):
     for key in ("o", "h", "v_new", "hT"):
         assert torch.equal(auto[key], expl[key]), f"{name}: auto and explicit split differ in {key}"
     check(auto, ref_of(inp), TOL[torch.bfloat16], inp.cu_seqlens, what=f"{name} auto ({P} segments)")
+
+
+def test_auto_segmentation_with_h0_and_graph_capture(pkg):
+    """The scheduler's split with an initial state gives the explicit split's
+    bits; captured in a HIP graph, replays give the eager bits, with eager
+    work and synchronisation between them."""
+    inp = make_gdr(1201, lengths=[9000, 700, 5000], H=2, dtype=torch.bfloat16, varlen=True, h0_std=0.1)
+    q, k, v, g, b = (dev(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    h0 = dev(inp.h0)
+    P = pkg.gdr_plan_segments(k, v.shape[-1], inp.cu_seqlens)
+    assert P >= 2
+    g_cum, w, u = pkg.gdr_chunk_prepare(k, v, g, b, inp.cu_seqlens)
+    eager = pkg.gdr_state_scan_auto(q, k, w, u, g_cum, inp.scale, h0, inp.cu_seqlens)
+    expl = pkg.chunk_gated_delta_rule(q, k, v, g, b, h0, inp.cu_seqlens, inp.scale, n_segments=P)
+    torch.cuda.synchronize()
+    for i, key in enumerate(("o", "h", "v_new", "hT")):
+        assert torch.equal(eager[i], expl[key]), f"auto with h0 and explicit split differ in {key}"
+    outs = [torch.empty_like(x) for x in eager]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        cap = pkg.gdr_state_scan_auto(q, k, w, u, g_cum, inp.scale, h0, inp.cu_seqlens, stream=s)  # warm-up
+        s.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            cap = pkg.gdr_state_scan_auto(q, k, w, u, g_cum, inp.scale, h0, inp.cu_seqlens, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in cap:
+            x.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, key in enumerate(("o", "h", "v_new", "hT")):
+            assert torch.equal(cap[i], eager[i]), f"graph replay {rep}: {key} differs"
