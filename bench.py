@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 ROOF_REPS = 30
+SETTLE_MS = 50.0  # untimed back-to-back work before each timed measurement (see settle())
 BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -264,6 +265,7 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
+    settle(torch, step)  # the clocks reach their level under this load (untimed)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -380,6 +382,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": SETTLE_MS,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -632,12 +635,27 @@ def copy_bandwidth(torch, dev, mib=512, reps=5):
     return 2 * n * 4 / (us * 1e-6) / 1e9
 
 
+def settle(torch, fn, ms=SETTLE_MS):
+    """Runs fn back to back for at least `ms` milliseconds of wall time (then
+    synchronizes): the GPU's clocks take tens of milliseconds to reach their
+    level under a new load (the 64K x 8-head segmented pass measured 350 us
+    on its first calls and 300 us after 30 ms), so every timed leg starts
+    from that level."""
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            return
+
+
 def _event_median_us(torch, fn, reps=5, per=4):
     """Median over `reps` of the mean time of `per` back-to-back calls,
     between two HIP events on the current stream (so a call's host-side
-    argument marshalling overlaps the previous call's kernels)."""
-    fn()
-    torch.cuda.synchronize()
+    argument marshalling overlaps the previous call's kernels), after
+    settle()."""
+    settle(torch, fn)
     stream = torch.cuda.current_stream()
     times = []
     for _ in range(reps):

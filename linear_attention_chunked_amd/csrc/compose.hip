@@ -219,24 +219,39 @@ static hipError_t launch_compose(const void* args, int grid, hipStream_t stream)
 // Pairwise combination of half-segment summaries (the same composition rule
 // applied to the two halves of one segment, all segments in parallel):
 //   S = M_b S_a + S_b,   M = M_b M_a
-// in FP32 MFMA (v_mfma_f32_16x16x4_f32).  One workgroup per (segment, head,
-// 64 of the DV + DK output columns), one wave per 16 rows.  The 64 columns
-// of [S_a | M_a] are staged once in LDS (S_a value-major as stored, one
-// column per padded LDS row; M_a row-major as stored, one matrix row per
-// padded LDS row); each wave keeps its 16 rows of M_b in registers and runs
-// the four 16-column tiles one after another.  Lane group g of instruction
-// 4i + j contracts index 16 i + 4 g + j (four consecutive entries per lane,
-// so the M_b rows come in as 16-byte loads); four interleaved accumulator
-// chains are summed per tile.
+// The split into halves runs for bfloat16 storage only, and there the
+// products run as three bf16 matrix-core products per FP32 product:
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi) (16 bits of the 24-bit
+// mantissa), and M_b X ~ lo(M_b) hi(X) + hi(M_b) lo(X) + hi(M_b) hi(X)
+// (the lo x lo term, below 2^-16 of the product, dropped), accumulated in
+// FP32 on v_mfma_f32_16x16x32_bf16: about 1e-5 relative to each product,
+// far below the bfloat16 rounding of every stored state.  One workgroup per
+// (segment, head, 64 of the DV + DK output columns), one wave per 16 rows.
+// The 64 columns of [S_a | M_a] are split once and staged in LDS as bf16
+// hi and lo tiles, S_a value-major as stored (one column per padded row), M_a
+// row-major as stored (one matrix row per padded row, read through
+// ds_read_b64_tr_b16); each wave splits its 16 rows of M_b in registers and
+// runs the four 16-column tiles.  Lane group g of a fragment holds the
+// contraction indices 32 s + 4 g + e and 32 s + 16 + 4 g + e (e < 4) in both
+// operands.
 template <int DK>
 struct Combine {
+  using S = St<bf16_t>;
+  using frag = S::frag;
   static constexpr int NW = DK / 16;
-  static constexpr int CW = 64;        // output columns per workgroup
-  static constexpr int LDC = DK + 4;   // state block: one column per row (floats), padded
-  static constexpr int LDR = CW + 4;   // transition block: one row per row (floats), padded
-  static constexpr int SMEM = (CW * LDC > DK * LDR ? CW * LDC : DK * LDR);
+  static constexpr int KS = DK / 32;
+  static constexpr int CW = 64;          // output columns per workgroup
+  static constexpr int LDC = DK * 2 + 16;  // state tile: one column per row (bytes), padded
+  static constexpr int LDR = CW * 2 + 32;  // transition tile: one matrix row per row (bytes), padded
+  static constexpr int TB = (CW * LDC > DK * LDR ? CW * LDC : DK * LDR);  // bytes of one tile
+  static constexpr int SMEM = 2 * TB;      // hi, lo
 
-  __device__ static void run(const CombineArgs& a, float* sm) {
+  __device__ static __forceinline__ void split(float x, uint16_t& h, uint16_t& l) {
+    h = f32_to_bf16(x);
+    l = f32_to_bf16(x - bf16_to_f32(h));
+  }
+
+  __device__ static void run(const CombineArgs& a, char* sm) {
     const int NB = (a.DV + DK) / CW;
     const int bx = blockIdx.x;
     const int xcd = bx & 7, slot = bx >> 3;
@@ -245,67 +260,88 @@ struct Combine {
     if (pair >= a.n_seg * a.H) return;
     const int64_t seg = pair / a.H, hd = pair % a.H, H = a.H;
     const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g4 = lane >> 4;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int DV = a.DV;
     const bool state = CW * cb < DV;
     const int col0 = state ? CW * cb : CW * cb - DV;  // first column of the block within S or M
-    // stage the 64 columns of [S_a | M_a] (16-byte pieces, coalesced)
+    char* thi = sm;
+    char* tlo = sm + TB;
+    // stage the 64 columns of [S_a | M_a] as bf16 hi / lo (16-byte loads, coalesced)
     if (state) {
       const float* src = a.half_state + ((2 * seg) * H + hd) * DV * DK + static_cast<int64_t>(col0) * DK;
       for (int v = tid; v < CW * DK / 4; v += NW * 64) {
-        const int c = v / (DK / 4), r4 = v % (DK / 4);
-        *reinterpret_cast<f32x4_t*>(sm + c * LDC + 4 * r4) = *reinterpret_cast<const f32x4_t*>(src + 4 * v);
+        const int c = v / (DK / 4), k4 = v % (DK / 4);
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + 4 * v);
+        uint16_t h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split(x[i], h[i], l[i]);
+        *reinterpret_cast<u32x2_t*>(thi + c * LDC + 8 * k4) =
+            u32x2_t{h[0] | (static_cast<uint32_t>(h[1]) << 16), h[2] | (static_cast<uint32_t>(h[3]) << 16)};
+        *reinterpret_cast<u32x2_t*>(tlo + c * LDC + 8 * k4) =
+            u32x2_t{l[0] | (static_cast<uint32_t>(l[1]) << 16), l[2] | (static_cast<uint32_t>(l[3]) << 16)};
       }
     } else {
       const float* src = a.half_trans + ((2 * seg) * H + hd) * DK * DK + col0;
       for (int v = tid; v < DK * CW / 4; v += NW * 64) {
         const int r = v / (CW / 4), c4 = v % (CW / 4);
-        *reinterpret_cast<f32x4_t*>(sm + r * LDR + 4 * c4) =
-            *reinterpret_cast<const f32x4_t*>(src + static_cast<int64_t>(r) * DK + 4 * c4);
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + static_cast<int64_t>(r) * DK + 4 * c4);
+        uint16_t h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split(x[i], h[i], l[i]);
+        *reinterpret_cast<u32x2_t*>(thi + r * LDR + 8 * c4) =
+            u32x2_t{h[0] | (static_cast<uint32_t>(h[1]) << 16), h[2] | (static_cast<uint32_t>(h[3]) << 16)};
+        *reinterpret_cast<u32x2_t*>(tlo + r * LDR + 8 * c4) =
+            u32x2_t{l[0] | (static_cast<uint32_t>(l[1]) << 16), l[2] | (static_cast<uint32_t>(l[3]) << 16)};
       }
     }
-    // this wave's 16 rows of M_b (A operand)
+    // this wave's 16 rows of M_b (A operand), split in registers
     const float* arow = a.half_trans + ((2 * seg + 1) * H + hd) * DK * DK +
                         static_cast<int64_t>(16 * wave + c16) * DK + 4 * g4;
-    float av[32];
+    frag ah[KS], al[KS];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const f32x4_t q = *reinterpret_cast<const f32x4_t*>(arow + 16 * i);
-      av[4 * i] = q[0], av[4 * i + 1] = q[1], av[4 * i + 2] = q[2], av[4 * i + 3] = q[3];
+    for (int s = 0; s < KS; ++s) {
+      const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(arow + 32 * s);
+      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(arow + 32 * s + 16);
+      ah[s] = S::frag_from_f32(x0, x1);
+      f32x4_t l0, l1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        l0[r] = x0[r] - bf16_to_f32(f32_to_bf16(x0[r]));
+        l1[r] = x1[r] - bf16_to_f32(f32_to_bf16(x1[r]));
+      }
+      al[s] = S::frag_from_f32(l0, l1);
     }
     __syncthreads();
     const int row0 = 16 * wave + 4 * g4;  // this lane's four output rows
+    // B fragments of column tile ct, contraction step s
+    auto bfrag = [&](const char* t, int ct, int s) {
+      if (state) {
+        const char* cp = t + (16 * ct + c16) * LDC + 2 * (32 * s + 4 * g4);
+        return S::frag_from_quads(lds_b64(cp, 0), lds_b64(cp, 32));
+      }
+      const char* tb = t + (4 * g4 + (c16 >> 2)) * LDR + 8 * (c16 & 3) + 32 * ct;
+      return S::frag_from_quads(lds_tr16(tb, 32 * s * LDR), lds_tr16(tb, (32 * s + 16) * LDR));
+    };
 #pragma unroll 1
     for (int ct = 0; ct < CW / 16; ++ct) {
       const int c = 16 * ct + c16;  // column within the block
-      float bv[32];
-      f32x4_t acc[4];
+      f32x4_t acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if (state) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const f32x4_t q = *reinterpret_cast<const f32x4_t*>(sm + c * LDC + 16 * i + 4 * g4);
-          bv[4 * i] = q[0], bv[4 * i + 1] = q[1], bv[4 * i + 2] = q[2], bv[4 * i + 3] = q[3];
-        }
-        acc[0] = *reinterpret_cast<const f32x4_t*>(a.half_state + ((2 * seg + 1) * H + hd) * DV * DK +
-                                                   static_cast<int64_t>(col0 + c) * DK + row0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bv[4 * i + j] = sm[(16 * i + 4 * g4 + j) * LDR + c];
+      for (int s = 0; s < KS; ++s) {
+        const frag bh = bfrag(thi, ct, s), bl = bfrag(tlo, ct, s);
+        S::mma(acc, al[s], bh);
+        S::mma(acc, ah[s], bl);
+        S::mma(acc, ah[s], bh);
       }
-#pragma unroll
-      for (int i = 0; i < 32; ++i) acc[i & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[i], acc[i & 3], 0, 0, 0);
-      const f32x4_t r = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       if (state) {
-        *reinterpret_cast<f32x4_t*>(a.seg_state + (seg * H + hd) * DV * DK + static_cast<int64_t>(col0 + c) * DK +
-                                    row0) = r;
+        const int64_t off = (seg * H + hd) * DV * DK + static_cast<int64_t>(col0 + c) * DK + row0;
+        const f32x4_t sb = *reinterpret_cast<const f32x4_t*>(a.half_state + ((2 * seg + 1) * H + hd) * DV * DK +
+                                                             static_cast<int64_t>(col0 + c) * DK + row0);
+        *reinterpret_cast<f32x4_t*>(a.seg_state + off) = acc + sb;
       } else {
         float* mo = a.seg_trans + (seg * H + hd) * DK * DK + static_cast<int64_t>(row0) * DK + col0 + c;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mo[static_cast<int64_t>(j) * DK] = r[j];
+        for (int j = 0; j < 4; ++j) mo[static_cast<int64_t>(j) * DK] = acc[j];
       }
     }
   }
@@ -313,7 +349,7 @@ struct Combine {
 
 template <int DK>
 __global__ __launch_bounds__(DK * 4) void combine_kernel(const CombineArgs a) {
-  __shared__ __align__(16) float sm[Combine<DK>::SMEM];
+  __shared__ __align__(16) char sm[Combine<DK>::SMEM];
   Combine<DK>::run(a, sm);
 }
 
