@@ -172,4 +172,26 @@ struct Row {
 constexpr int kChunk = 64;
 constexpr int kMaxRows = 112;  // rows carried by value in one launch's arguments
 
+// The row of a launch's plan that holds chunk `chunk` (chunks relative to the
+// launch; rows sorted by chunk_off, the first at 0): the last row whose first
+// chunk is at or before it.  One round of vector loads from the argument
+// block instead of a chain of dependent scalar loads: lane l reads rows l and
+// l + 64, a ballot counts the rows that start at or before the chunk, and the
+// fields come from the lane that read that row.  Call with the whole wave
+// active; the result is uniform.
+static_assert(kMaxRows <= 128, "row lookup reads two rows per lane");
+__device__ __forceinline__ Row row_of_chunk(const Row* rows, int n_rows, int chunk) {
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  const Row x0 = rows[min(lane, n_rows - 1)];
+  const Row x1 = rows[min(lane + 64, n_rows - 1)];
+  const uint64_t m0 = __ballot(lane < n_rows && x0.chunk_off <= chunk);
+  const uint64_t m1 = __ballot(lane + 64 < n_rows && x1.chunk_off <= chunk);
+  const int idx = __builtin_amdgcn_readfirstlane(__popcll(m0) + __popcll(m1) - 1);
+  const Row& x = idx < 64 ? x0 : x1;
+  const int l = idx & 63;
+  return Row{__builtin_amdgcn_readlane(x.bos, l), __builtin_amdgcn_readlane(x.len, l),
+             __builtin_amdgcn_readlane(x.chunk_off, l), __builtin_amdgcn_readlane(x.in_idx, l),
+             __builtin_amdgcn_readlane(x.out_idx, l)};
+}
+
 }  // namespace gdr

@@ -35,15 +35,6 @@ __device__ __forceinline__ void mm16f(f32x4_t& d, const f32x4_t& a, const f32x4_
   for (int r = 0; r < 4; ++r) d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], d, 0, 0, 0);
 }
 
-__device__ __forceinline__ int kda_find_row(const KdaArgs& a, int chunk) {
-  int lo = 0, hi = a.n_rows - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.rows[mid].chunk_off <= chunk) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 // bf16 hi + lo split of an FP32 value (hi = RNE bf16, lo = bf16 of the rest)
 __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
   hi = f32_to_bf16(x);
@@ -148,7 +139,7 @@ struct KdaPrepare {
     const int chunk = item / a.H;
     const int hd = item % a.H;
     if (chunk >= a.n_chunks) return;
-    const Row row = a.rows[kda_find_row(a, chunk)];
+    const Row row = row_of_chunk(a.rows, a.n_rows, chunk);
     const int cl = chunk - row.chunk_off;
     const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(cl) * kChunk;
     const int nvalid = min(kChunk, row.len - cl * kChunk);
@@ -495,7 +486,7 @@ struct KdaOutput {
     const int chunk = item / a.H;
     const int hd = item % a.H;
     if (chunk >= a.n_chunks) return;
-    const Row row = a.rows[kda_find_row(a, chunk)];
+    const Row row = row_of_chunk(a.rows, a.n_rows, chunk);
     const int cl = chunk - row.chunk_off;
     const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(cl) * kChunk;
     const int nvalid = min(kChunk, row.len - cl * kChunk);

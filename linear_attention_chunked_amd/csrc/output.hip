@@ -34,15 +34,6 @@ struct OutputKernel {
     float gam[kChunk];
   };
 
-  __device__ static int find_row(const ChunkArgs& a, int chunk) {
-    int lo = 0, hi = a.n_rows - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.rows[mid].chunk_off <= chunk) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-  }
-
   __device__ static void run(const ChunkArgs& a, Smem& sm) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
@@ -52,7 +43,7 @@ struct OutputKernel {
     const int hd = rest % a.H;
     const int chunk = rest / a.H;
     if (chunk >= a.n_chunks) return;
-    const Row row = a.rows[find_row(a, chunk)];
+    const Row row = row_of_chunk(a.rows, a.n_rows, chunk);
     const int cl = chunk - row.chunk_off;
     const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(cl) * kChunk;
     const int nvalid = min(kChunk, row.len - cl * kChunk);

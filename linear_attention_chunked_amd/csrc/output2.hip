@@ -48,15 +48,6 @@ struct Output2 {
   static constexpr int CQ = DK / 8, CV = DV / 8;  // 16-byte vectors per row
   static constexpr int QPT = kChunk * CQ / NT, HPT = DV * CQ / NT, VPT = kChunk * CV / NT;
 
-  __device__ static int find_row(const ChunkArgs& a, int chunk) {
-    int lo = 0, hi = a.n_rows - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.rows[mid].chunk_off <= chunk) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-  }
-
   __device__ static void run(const ChunkArgs& a, Smem& sm) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
@@ -65,7 +56,7 @@ struct Output2 {
     const int chunk = item / a.H;
     const int hd = item % a.H;
     if (chunk >= a.n_chunks) return;
-    const Row row = a.rows[find_row(a, chunk)];
+    const Row row = row_of_chunk(a.rows, a.n_rows, chunk);
     const int cl = chunk - row.chunk_off;
     const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(cl) * kChunk;
     const int nvalid = min(kChunk, row.len - cl * kChunk);

@@ -11,8 +11,9 @@
 //     range check); the products that contract over tokens read them as MFMA
 //     operands with ds_read_b64_tr_b16.
 //   * Gram matrix, T by 16-row blocks and the hi + lo products: wy_core.hpp.
-//   * V is loaded (into registers) once the diagonal blocks are done and
-//     takes the place of K in LDS once the w product has read K.  A and T
+//   * Every load of the item (K, V, g, beta) issues at entry, after one round
+//     of loads that finds the item's row (row_of_chunk); V waits in registers
+//     and takes the place of K in LDS once the w product has read K.  A and T
 //     keep only their blocks on or below the diagonal; the footprint (29.4 KB
 //     at 128 x 128) and at most 96 VGPRs let five workgroups share a CU.
 #include "gfx950.hpp"
@@ -44,21 +45,14 @@ struct Prepare2 {
     float bg[kChunk];  // beta exp(gamma)
   };
 
-  __device__ static int find_row(const ChunkArgs& a, int chunk) {
-    int lo = 0, hi = a.n_rows - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.rows[mid].chunk_off <= chunk) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-  }
-
-  // K rows (and g, beta for the first wave) pass through registers on their
-  // way to LDS.
+  // K and V rows, g and beta are loaded at entry, all in one round: K, g and
+  // beta pass through registers to LDS at once, V waits in registers until
+  // the w product has read K.
   static constexpr int KV_PT = kChunk * (DK / 8) / NT;  // 16-byte K vectors per thread
   static constexpr int VV_PT = kChunk * (DV / 8) / NT;
   struct Pref {
     u32x4_t k[KV_PT];
+    u32x4_t v[VV_PT];
     float g, b;
   };
 
@@ -70,7 +64,7 @@ struct Prepare2 {
 
   __device__ static Item item_of(const ChunkArgs& a, int item) {
     const int chunk = item / a.H;
-    const Row row = a.rows[find_row(a, chunk)];
+    const Row row = row_of_chunk(a.rows, a.n_rows, chunk);
     const int cl = chunk - row.chunk_off;
     return Item{item % a.H, static_cast<int64_t>(row.bos) + static_cast<int64_t>(cl) * kChunk,
                 min(kChunk, row.len - cl * kChunk)};
@@ -79,20 +73,30 @@ struct Prepare2 {
   __device__ static void load(Pref& pf, const ChunkArgs& a, const Item& it) {
     const int tid = threadIdx.x;
     const int64_t H = a.H;
+    const uint32_t rows = static_cast<uint32_t>((it.nvalid - 1) * H + 1);
+    // every wave loads g and beta (only the first uses them): loads taken
+    // under that wave's branch would issue after K has arrived
+    const float* gp = a.g + it.tok0 * H + it.hd;
+    const float* bp = a.beta + it.tok0 * H + it.hd;
+    const int go = static_cast<int>((tid & 63) * H * 4);
+    pf.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(gp, rows * 4), go, 0, 0));
+    pf.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(bp, rows * 4), go, 0, 0));
     const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (it.tok0 * H + it.hd) * DK;
-    const rsrc_t rk = make_rsrc(kp, static_cast<uint32_t>(((it.nvalid - 1) * H + 1) * DK * 2));
+    const rsrc_t rk = make_rsrc(kp, rows * DK * 2);
     constexpr int CK = DK / 8;  // 16-byte chunks per row
 #pragma unroll
     for (int i = 0; i < KV_PT; ++i) {
       const int vv = tid + i * NT, r = vv / CK, c = vv % CK;
       pf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, static_cast<int>(r * H * DK * 2 + c * 16), 0, 0);
     }
-    const float* gp = a.g + it.tok0 * H + it.hd;
-    const float* bp = a.beta + it.tok0 * H + it.hd;
-    const uint32_t gb = static_cast<uint32_t>(((it.nvalid - 1) * H + 1) * 4);
-    const int go = static_cast<int>((tid & 63) * H * 4);
-    pf.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(gp, gb), go, 0, 0));
-    pf.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(bp, gb), go, 0, 0));
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (it.tok0 * H + it.hd) * DV;
+    const rsrc_t rv = make_rsrc(vp, rows * DV * 2);
+    constexpr int CV = DV / 8;
+#pragma unroll
+    for (int i = 0; i < VV_PT; ++i) {
+      const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
+      pf.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
+    }
   }
 
   // One workgroup per item (item = chunk * H + head).
@@ -124,6 +128,7 @@ struct Prepare2 {
         const int vv = tid + i * NT, r = vv / CK, c = vv % CK;
         *reinterpret_cast<u32x4_t*>(sm.kv + r * SKB + c * 16) = pf.k[i];
       }
+      asm volatile("" ::"v"(pf.g), "v"(pf.b));  // g and beta arrive with K, not after it
       if (wave == 0) {
         const float x = W::gamma_beta(pf.g, pf.b, nvalid, sm.gam, sm.beta, sm.bg);
         if (lane < nvalid) a.g_cum[(tok0 + lane) * H + hd] = x;
@@ -133,17 +138,6 @@ struct Prepare2 {
 
     // ---- Gram matrix and the diagonal blocks of T ----
     W::gram_diag(sm.kv, SKB, sm.t, sm.gam, sm.beta);
-    // V rows for the last product (zero past the tail): in flight during the off-diagonal blocks and w
-    u32x4_t vcur[VV_PT];
-    {
-      const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + hd) * DV;
-      const rsrc_t rv = make_rsrc(vp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DV * 2));
-#pragma unroll
-      for (int i = 0; i < VV_PT; ++i) {
-        const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
-        vcur[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>(r * H * DV * 2 + c * 16), 0, 0);
-      }
-    }
     __syncthreads();
     W::off_diag(sm.t);
 
@@ -167,7 +161,7 @@ struct Prepare2 {
 #pragma unroll
     for (int i = 0; i < VV_PT; ++i) {
       const int vv = tid + i * NT, r = vv / CV, c = vv % CV;
-      *reinterpret_cast<u32x4_t*>(sm.kv + r * SVB + c * 16) = vcur[i];
+      *reinterpret_cast<u32x4_t*>(sm.kv + r * SVB + c * 16) = pf.v[i];
     }
     __syncthreads();
     {

@@ -73,55 +73,72 @@ struct WyCore {
     return x;
   }
 
-  // Gram matrix row tile `wave`; A = beta_t e^{gamma_t - gamma_i} G (i < t),
-  // then the wave's diagonal block T[b][b] = (I + A[b][b])^-1 (both in the
-  // wave's own rows of t: no barrier).  K: row-major tile of stride skb.
-  __device__ static void gram_diag(const char* kt, int skb, float* t, const float* gam, const float* beta) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    {
-      f32x4_t acc[4];
+  // Gram matrix row tile WV (the calling wave); A = beta_t e^{gamma_t -
+  // gamma_i} G (i < t) for its blocks on or below the diagonal.  The block
+  // count is a compile-time constant per wave, so every LDS read of the tile
+  // is issued ahead of the products (no branch between them).
+  template <int WV>
+  __device__ static __forceinline__ void gram_rows(const char* kt, int skb, float* t, const float* gam,
+                                                   const float* beta) {
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
+    f32x4_t acc[WV + 1];
 #pragma unroll
-      for (int tj = 0; tj < 4; ++tj) acc[tj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const char* kr = kt + c16 * skb + (g4 >> 1) * 16 + (g4 & 1) * 8;
+    for (int tj = 0; tj <= WV; ++tj) acc[tj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const char* kr = kt + c16 * skb + (g4 >> 1) * 16 + (g4 & 1) * 8;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const frag fa = S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(kr + 16 * wave * skb + 64 * s),
-                                           *reinterpret_cast<const u32x2_t*>(kr + 16 * wave * skb + 64 * s + 32));
+    for (int s = 0; s < KS; ++s) {
+      const frag fa = S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(kr + 16 * WV * skb + 64 * s),
+                                         *reinterpret_cast<const u32x2_t*>(kr + 16 * WV * skb + 64 * s + 32));
 #pragma unroll
-        for (int tj = 0; tj < 4; ++tj) {
-          if (tj <= wave) {
-            const frag fb = S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(kr + 16 * tj * skb + 64 * s),
-                                               *reinterpret_cast<const u32x2_t*>(kr + 16 * tj * skb + 64 * s + 32));
-            S::mma(acc[tj], fa, fb);
-          }
-        }
-      }
-      // Every LDS read is issued before any exponent: the (i < t) mask is a
-      // select on values already in registers, not a branch around each
-      // read.  e^{gamma_t - gamma_i} may overflow where i > t; the select
-      // drops it.  Blocks above the diagonal (tj > wave) are not stored.
-      const int t0 = 16 * wave + 4 * g4;
-      const f32x4_t gt = *reinterpret_cast<const f32x4_t*>(&gam[t0]);
-      const f32x4_t bt = *reinterpret_cast<const f32x4_t*>(&beta[t0]);
-      float gi[4];
-#pragma unroll
-      for (int tj = 0; tj < 4; ++tj) gi[tj] = gam[16 * tj + c16];
-#pragma unroll
-      for (int tj = 0; tj < 4; ++tj) {
-        const int i = 16 * tj + c16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tt = t0 + r;
-          if (tj <= wave) {
-            const float full = bt[r] * exp_fast(gt[r] - gi[tj]) * acc[tj][r];
-            const float val = (i < tt) ? full : 0.f;
-            t[toff(tt) + i] = val;
-          }
-        }
+      for (int tj = 0; tj <= WV; ++tj) {
+        const frag fb = S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(kr + 16 * tj * skb + 64 * s),
+                                           *reinterpret_cast<const u32x2_t*>(kr + 16 * tj * skb + 64 * s + 32));
+        S::mma(acc[tj], fa, fb);
       }
     }
+    // Every LDS read is issued before any exponent: the (i < t) mask is a
+    // select on values already in registers, not a branch around each read.
+    // e^{gamma_t - gamma_i} may overflow where i > t; the select drops it.
+    // Blocks above the diagonal are not stored.
+    const int t0 = 16 * WV + 4 * g4;
+    const f32x4_t gt = *reinterpret_cast<const f32x4_t*>(&gam[t0]);
+    const f32x4_t bt = *reinterpret_cast<const f32x4_t*>(&beta[t0]);
+    float gi[WV + 1];
+#pragma unroll
+    for (int tj = 0; tj <= WV; ++tj) gi[tj] = gam[16 * tj + c16];
+#pragma unroll
+    for (int tj = 0; tj <= WV; ++tj) {
+      const int i = 16 * tj + c16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tt = t0 + r;
+        const float full = bt[r] * exp_fast(gt[r] - gi[tj]) * acc[tj][r];
+        const float val = (i < tt) ? full : 0.f;
+        t[toff(tt) + i] = val;
+      }
+    }
+  }
+
+  // Gram matrix row tile `wave` (gram_rows), then the wave's diagonal block
+  // T[b][b] = (I + A[b][b])^-1 (both in the wave's own rows of t: no
+  // barrier).  K: row-major tile of stride skb.
+  __device__ static __forceinline__ void gram_diag(const char* kt, int skb, float* t, const float* gam,
+                                                   const float* beta) {
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    switch (wave) {
+      case 0: gram_rows<0>(kt, skb, t, gam, beta); break;
+      case 1: gram_rows<1>(kt, skb, t, gam, beta); break;
+      case 2: gram_rows<2>(kt, skb, t, gam, beta); break;
+      default: gram_rows<3>(kt, skb, t, gam, beta); break;
+    }
+    diag_solve(t);
+  }
+
+  // The calling wave's diagonal block T[b][b] = (I + A[b][b])^-1, b = wave,
+  // from its own rows of A (written by gram_rows of the same wave).
+  __device__ static __forceinline__ void diag_solve(float* t) {
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     // ---- diagonal blocks: T[b][b] = (I + A[b][b])^-1 by forward substitution, wave b ----
     // Lane (j, g) solves rows 4 g .. 4 g + 3 of column j, by blocks of four
     // rows: the lanes owning block q finish its rows, a shuffle hands the four
@@ -165,7 +182,7 @@ struct WyCore {
 
   // The off-diagonal blocks of T, after a barrier that follows gram_diag.
   // Ends with a barrier: every block of T is in place.
-  __device__ static void off_diag(float* t) {
+  __device__ static __forceinline__ void off_diag(float* t) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -247,30 +264,38 @@ struct WyCore {
   // Rows 16 wave .. 16 wave + 15 of (T diag(coef)) X for a row-major bf16 tile
   // X (64 rows, stride `stride`, D columns): for every 16-column tile dt,
   // out(dt, acc) with acc[r] = result[16 wave + c16][16 dt + 4 g4 + r] in FP32.
-  // A operand X^T[d][i] by transpose reads of the row-major tile.
-  template <int D, class Out>
-  __device__ static __forceinline__ void product(const char* tile, int stride, const frag (&hi)[2],
-                                                 const frag (&lo)[2], Out out) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nsteps = (16 * wave + 15) / 32 + 1;
+  // A operand X^T[d][i] by transpose reads of the row-major tile.  NS = the
+  // 32-token steps below the diagonal (1 for the first two waves, 2 for the
+  // others), a compile-time constant, so the reads of later tiles can be
+  // issued ahead of the products of earlier ones.
+  template <int NS, int D, class Out>
+  __device__ static __forceinline__ void product_ns(const char* tile, int stride, const frag (&hi)[2],
+                                                    const frag (&lo)[2], Out& out) {
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
     const int tr_row = 4 * g4 + (c16 >> 2);
     const int tr_col = 8 * (c16 & 3);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       f32x4_t acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (s < nsteps) {
-          const char* base = tile + (32 * s + tr_row) * stride + 32 * dt + tr_col;
-          const frag fa = S::frag_from_quads(lds_tr16(base, 0), lds_tr16(base, 16 * stride));
-          S::mma(acc, fa, hi[s]);
-          S::mma(acc, fa, lo[s]);
-        }
+      for (int s = 0; s < NS; ++s) {
+        const char* base = tile + (32 * s + tr_row) * stride + 32 * dt + tr_col;
+        const frag fa = S::frag_from_quads(lds_tr16(base, 0), lds_tr16(base, 16 * stride));
+        S::mma(acc, fa, hi[s]);
+        S::mma(acc, fa, lo[s]);
       }
       out(dt, acc);
     }
+  }
+
+  template <int D, class Out>
+  __device__ static __forceinline__ void product(const char* tile, int stride, const frag (&hi)[2],
+                                                 const frag (&lo)[2], Out out) {
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    if (wave >= 2)
+      product_ns<2, D>(tile, stride, hi, lo, out);
+    else
+      product_ns<1, D>(tile, stride, hi, lo, out);
   }
 };
 
