@@ -55,17 +55,27 @@ struct WyCore {
     return 128 * b * (b - 1) + 320 * b + (t & 15) * (16 * b + 20);
   }
 
-  // First wave (lane = token): gamma by a shuffle scan of g (zero past the
-  // chunk's nvalid tokens), beta and beta e^gamma into LDS; returns gamma.
+  // First wave (lane = token): gamma by an inclusive scan of g (zero past
+  // the chunk's nvalid tokens), beta and beta e^gamma into LDS; returns gamma.
+  // The scan runs on DPP lane moves (no LDS round trip): shifts by 1, 2, 4, 8
+  // within each row of 16 lanes, then the total of row 0 into row 1 and of
+  // row 2 into row 3 (broadcast of lane 15 of a row to the next), then the
+  // total of rows 0-1 into rows 2-3 (broadcast of lane 31).
+  template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+  __device__ static __forceinline__ float dpp_add(float x) {
+    const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, BOUND_ZERO);
+    return x + __builtin_bit_cast(float, y);
+  }
   __device__ static __forceinline__ float gamma_beta(float g, float b, int nvalid, float* gam, float* beta,
                                                      float* bg) {
     const int lane = threadIdx.x & 63;
     float x = (lane < nvalid) ? g : 0.f;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
+    x = dpp_add<0x111, 0xf, true>(x);   // row_shr:1
+    x = dpp_add<0x112, 0xf, true>(x);   // row_shr:2
+    x = dpp_add<0x114, 0xf, true>(x);   // row_shr:4
+    x = dpp_add<0x118, 0xf, true>(x);   // row_shr:8
+    x = dpp_add<0x142, 0xa, false>(x);  // row_bcast:15 into rows 1 and 3
+    x = dpp_add<0x143, 0xc, false>(x);  // row_bcast:31 into rows 2 and 3
     const float bb = (lane < nvalid) ? b : 0.f;
     gam[lane] = x;
     beta[lane] = bb;
