@@ -8,8 +8,8 @@
 //                   chain), combine through LDS, and write the chunk's total
 //                   lse[c] (and, when requested, the chunk-local running
 //                   values into z);
-//   abc_carry       one workgroup per (b, h): zc[c] = logaddexp(zc[c-1], lse[c])
-//                   over 64 stretches of the chunk range in parallel;
+//   abc_carry       one wave per (b, h, 4 slots): zc[c] = logaddexp(zc[c-1],
+//                   lse[c]) over 64 stretches of the chunk range in parallel;
 //   abc_weights     one workgroup per (b, chunk, h): the chunk's weights
 //                   E_t = exp(s_t - zc[c]) in the storage dtype, once for all
 //                   the state tiles that use them, and (when z is requested)
@@ -97,20 +97,37 @@ __global__ __launch_bounds__(256) void abc_chunk_lse(const AbcArgs a) {
   if (grp == 3) a.lse[((static_cast<int64_t>(b) * a.NC + c) * a.H + h) * a.M + m] = logaddexp_f(off, L);
 }
 
-__global__ __launch_bounds__(1024) void abc_carry(const AbcArgs a) {
-  // zc[c] = logaddexp(zc[c-1], lse[c]) per slot (M == 64).  Thread (s, p):
-  // slots 4p .. 4p + 3 (16-byte loads and stores) of stretch s, one of 64
-  // contiguous stretches of the chunk range.  Pass 1 forms each stretch's
-  // total as max + log(sum of exp(x - max)); an inclusive scan of the stretch
-  // totals in LDS (six doubling steps) gives each stretch the total of the
-  // ones before it; pass 2 re-runs the stretch's chain from there and writes
-  // zc.  Stretches of up to 8 chunks stay in registers (up to 512 chunks per
-  // call); longer ones read their totals again in pass 2.
-  __shared__ f32x4_t tot[2][64][16];
-  const int tid = threadIdx.x;
-  const int p = tid & 15, st = tid >> 4;
-  const int h = blockIdx.x % a.H;
-  const int b = blockIdx.x / a.H;
+// DPP lane move of x with -inf where the move has no source (or the row is
+// masked off): the identity of logaddexp.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_ninf(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, -INFINITY),
+                                                               __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, false));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ f32x4_t lae4_dpp(f32x4_t x) {
+  f32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = logaddexp_f(dpp_ninf<CTRL, ROW_MASK>(x[j]), x[j]);
+  return r;
+}
+
+__global__ __launch_bounds__(64) void abc_carry(const AbcArgs a) {
+  // zc[c] = logaddexp(zc[c-1], lse[c]) per slot (M == 64).  One wave per
+  // (b, h, quad of slots 4p .. 4p + 3; 16-byte loads and stores); lane s
+  // takes stretch s, one of 64 contiguous stretches of the chunk range.
+  // Pass 1 forms each stretch's total as max + log(sum of exp(x - max)); an
+  // inclusive scan of the stretch totals across the wave on DPP lane moves
+  // (shifts by 1, 2, 4, 8 within rows of 16 lanes, then the row broadcasts of
+  // lanes 15 and 31; no LDS, no barrier) and a shift by one lane give each
+  // stretch the total of the ones before it; pass 2 re-runs the stretch's
+  // chain from there and writes zc.  Stretches of up to 8 chunks stay in
+  // registers (up to 512 chunks per call); longer ones read their totals
+  // again in pass 2.
+  const int st = threadIdx.x & 63;
+  const int p = blockIdx.x & 15;
+  const int h = (blockIdx.x >> 4) % a.H;
+  const int b = (blockIdx.x >> 4) / a.H;
   const int per = (a.NC + 63) / 64;
   const int c0 = min(a.NC, st * per), c1 = min(a.NC, c0 + per);
   const int64_t step = static_cast<int64_t>(a.H) * a.M;
@@ -162,18 +179,15 @@ __global__ __launch_bounds__(1024) void abc_carry(const AbcArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     t[j] = mx[j] == -INFINITY ? -INFINITY : mx[j] + 0.69314718055994531f * __builtin_amdgcn_logf(sm[j]);
-  tot[0][st][p] = t;
-  __syncthreads();
-  int src = 0;
+  t = lae4_dpp<0x111, 0xf>(t);  // row_shr:1
+  t = lae4_dpp<0x112, 0xf>(t);  // row_shr:2
+  t = lae4_dpp<0x114, 0xf>(t);  // row_shr:4
+  t = lae4_dpp<0x118, 0xf>(t);  // row_shr:8
+  t = lae4_dpp<0x142, 0xa>(t);  // row_bcast:15 into rows 1 and 3
+  t = lae4_dpp<0x143, 0xc>(t);  // row_bcast:31 into rows 2 and 3
+  f32x4_t z;
 #pragma unroll
-  for (int d = 1; d < 64; d *= 2) {
-    f32x4_t v = tot[src][st][p];
-    if (st >= d) v = lae4(tot[src][st - d][p], v);
-    tot[src ^ 1][st][p] = v;
-    src ^= 1;
-    __syncthreads();
-  }
-  f32x4_t z = st > 0 ? tot[src][st - 1][p] : ninf;
+  for (int j = 0; j < 4; ++j) z[j] = dpp_ninf<0x138, 0xf>(t[j]);  // wave_shr:1: the stretches before this one
   float* zc = a.zc + row0;
 #pragma unroll
   for (int i = 0; i < R; ++i)
@@ -726,7 +740,7 @@ hipError_t launch_abc(const AbcArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (a.NC > 0) {
-    hipLaunchKernelGGL(abc_carry, dim3(a.B * a.H), dim3(1024), 0, stream, a);
+    hipLaunchKernelGGL(abc_carry, dim3(a.B * a.H * 16), dim3(64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
