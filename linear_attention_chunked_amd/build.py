@@ -105,8 +105,12 @@ def resource_table(out_path: str, jobs: int | None = None) -> str:
     cols = [("VGPRs", "vgpr"), ("AGPRs", "agpr"), ("TotalSGPRs", "sgpr"), ("ScratchSize [bytes/lane]", "scratch"),
             ("VGPRs Spill", "vspill"), ("SGPRs Spill", "sspill"), ("LDS Size [bytes/block]", "lds_bytes"),
             ("Occupancy [waves/SIMD]", "waves/SIMD")]
+    spilled = [n for r, n in zip(rows, names) if str(r.get("ScratchSize [bytes/lane]", "0")) != "0"]
+    note = ("0 everywhere" if not spilled else
+            f"0 except in {len(spilled)} kernel(s): " + "; ".join(n.split("(")[0].replace("void ", "") for n in spilled))
     lines = ["# Per-kernel resource use on gfx950 as the compiler reports it (-Rpass-analysis=kernel-resource-usage,",
-             "# the library's own build flags); scratch = private memory per lane (register spills), 0 everywhere",
+             "# the library's own build flags); scratch = private memory per lane (register spills),",
+             "# " + note,
              "#",
              "# command (from the repository root):",
              f"#   python -c 'from linear_attention_chunked_amd.build import resource_table; "
