@@ -182,8 +182,9 @@ constexpr int kMaxRows = 112;  // rows carried by value in one launch's argument
 static_assert(kMaxRows <= 128, "row lookup reads two rows per lane");
 __device__ __forceinline__ Row row_of_chunk(const Row* rows, int n_rows, int chunk) {
   const int lane = static_cast<int>(threadIdx.x & 63);
-  const Row x0 = rows[min(lane, n_rows - 1)];
-  const Row x1 = rows[min(lane + 64, n_rows - 1)];
+  const int last = max(n_rows - 1, 0);  // every lane reads inside the list, also for an empty one
+  const Row x0 = rows[min(lane, last)];
+  const Row x1 = rows[min(lane + 64, last)];
   const uint64_t m0 = __ballot(lane < n_rows && x0.chunk_off <= chunk);
   const uint64_t m1 = __ballot(lane + 64 < n_rows && x1.chunk_off <= chunk);
   const int idx = __builtin_amdgcn_readfirstlane(__popcll(m0) + __popcll(m1) - 1);
