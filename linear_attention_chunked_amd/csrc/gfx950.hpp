@@ -25,7 +25,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 // 202 -> 159 us, reverse 188 -> 163 us).
 // Stores of partial 128-byte lines (the fused output's 8-byte pieces) stay on
 // the default policy: non-temporal there, L2 no longer merges them before
-// they go to HBM (88 -> 97 MB written per question_rows launch).
+// they go to HBM (88 -> 97 MB written per question_rows launch).  The same
+// policy bit on a load marks a stream that one workgroup reads once (the
+// scan's U columns on long chains).
 constexpr int kStreamStore = 2;
 
 // e^x on the hardware base-2 exponential.

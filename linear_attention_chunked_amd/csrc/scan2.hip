@@ -122,6 +122,15 @@ struct Scan2 {
   // pass, whose own 8-byte output pieces share the lines' trip through L2
   // (non-temporal h / v_new there measured 0.5 us slower with cold caches)
   static constexpr int ST_POL = FO ? 0 : kStreamStore;
+  // U is read by one column block only (K and W by every block of the
+  // (sequence, head)): on long chains it is loaded non-temporally so its
+  // stream does not push the shared K / W tiles out of L2 before the other
+  // block reads them (new_states: 571 -> 509 MB fetched, 213 -> 199 us; the
+  // 64K summaries 118 -> 114 us).  The dense form (short packed sequences)
+  // keeps the default policy: there U written by the chunk prepare just
+  // before is still in the Infinity Cache (non-temporal loads measured
+  // 24.6 -> 30.6 us on back-to-back question_rows scans).
+  static constexpr int U_POL = (DENSE || FO) ? 0 : kStreamStore;
   static constexpr int H_PT = BV * DK / 8 / NT;     // 16-byte h vectors per thread
   static constexpr int V_PT = kChunk * BV / 8 / NT; // 16-byte v_new vectors per thread
   static constexpr int W_PT = kChunk * CPW / NT;   // 16-byte vectors per thread (W, and K)
@@ -187,7 +196,7 @@ struct Scan2 {
       const uint16_t* up = static_cast<const uint16_t*>(a.u) + (tok0 * H + x.hd) * x.DV + x.col_blk;
       const rsrc_t ru = make_rsrc(up, live ? static_cast<uint32_t>(((nvalid - 1) * H * x.DV + UBV) * 2) : 0u);
 #pragma unroll
-      for (int i = 0; i < U_PT; ++i) st.u[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, x.vo_u[i], 0, 0);
+      for (int i = 0; i < U_PT; ++i) st.u[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, x.vo_u[i], 0, U_POL);
     }
     if constexpr (KD) {  // thread d < DK: channel d's decay over the chunk
       const float* dp = a.decay + (hrow * H + x.hd) * DK;
