@@ -276,7 +276,8 @@ gdr_status gdr_segment_compose(const gdr_problem* p, int32_t n_segments, const f
  * z (nullable) [B, T, H, M] float32; hk [B, NC, H, K, M] and hv [B, NC, H, M, V]
  * the states before every chunk (storage dtype); hk_final [B, H, K, M] and
  * hv_final [B, H, M, V] float32 (nullable).  Supported: K, V multiples of 64,
- * M = 64, bfloat16 storage. */
+ * M = 32 or 64 ([fla#23] "Fixture-First Correctness Contract" names both),
+ * bfloat16 storage. */
 typedef struct {
   int32_t B;
   int64_t T;

@@ -54,7 +54,8 @@ __device__ __forceinline__ float logaddexp_f(float a, float b) {
 // ---------------------------------------------------------------- normaliser
 __global__ __launch_bounds__(256) void abc_chunk_lse(const AbcArgs a) {
   __shared__ float tot[4][64];
-  const int m = threadIdx.x & 63;  // slot (M == 64)
+  const int m = threadIdx.x & 63;  // slot (lanes past M (32) carry -inf and write nothing)
+  const bool live_m = m < a.M;
   const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 16-token group (one per wave)
   const int bx = blockIdx.x;
   const int h = bx % a.H;
@@ -80,12 +81,12 @@ __global__ __launch_bounds__(256) void abc_chunk_lse(const AbcArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i)
     if (i < n) sum += exp_fast(bf16_to_f32(v[i]) - mx);
-  const float L = n > 0 ? mx + 0.69314718055994531f * __builtin_amdgcn_logf(sum) : -INFINITY;
+  const float L = (n > 0 && live_m) ? mx + 0.69314718055994531f * __builtin_amdgcn_logf(sum) : -INFINITY;
   tot[grp][m] = L;
   __syncthreads();
   float off = -INFINITY;
   for (int g = 0; g < grp; ++g) off = logaddexp_f(off, tot[g][m]);
-  if (a.z != nullptr) {  // the chunk-local running values (a chain, only when z is requested)
+  if (a.z != nullptr && live_m) {  // the chunk-local running values (a chain, only when z is requested)
     float run = off;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(256) void abc_chunk_lse(const AbcArgs a) {
         a.z[((static_cast<int64_t>(b) * a.T + t0 + i) * a.H + h) * a.M + m] = run;
       }
   }
-  if (grp == 3) a.lse[((static_cast<int64_t>(b) * a.NC + c) * a.H + h) * a.M + m] = logaddexp_f(off, L);
+  if (grp == 3 && live_m) a.lse[((static_cast<int64_t>(b) * a.NC + c) * a.H + h) * a.M + m] = logaddexp_f(off, L);
 }
 
 // DPP lane move of x with -inf where the move has no source (or the row is
@@ -113,7 +114,7 @@ __device__ __forceinline__ f32x4_t lae4_dpp(f32x4_t x) {
 }
 
 __global__ __launch_bounds__(64) void abc_carry(const AbcArgs a) {
-  // zc[c] = logaddexp(zc[c-1], lse[c]) per slot (M == 64).  One wave per
+  // zc[c] = logaddexp(zc[c-1], lse[c]) per slot (M = 32 or 64).  One wave per
   // (b, h, quad of slots 4p .. 4p + 3; 16-byte loads and stores); lane s
   // takes stretch s, one of 64 contiguous stretches of the chunk range.
   // Pass 1 forms each stretch's total as max + log(sum of exp(x - max)); an
@@ -125,9 +126,10 @@ __global__ __launch_bounds__(64) void abc_carry(const AbcArgs a) {
   // registers (up to 512 chunks per call); longer ones read their totals
   // again in pass 2.
   const int st = threadIdx.x & 63;
-  const int p = blockIdx.x & 15;
-  const int h = (blockIdx.x >> 4) % a.H;
-  const int b = (blockIdx.x >> 4) / a.H;
+  const int nq = a.M / 4;  // quads of slots per (b, h)
+  const int p = blockIdx.x % nq;
+  const int h = (blockIdx.x / nq) % a.H;
+  const int b = (blockIdx.x / nq) / a.H;
   const int per = (a.NC + 63) / 64;
   const int c0 = min(a.NC, st * per), c1 = min(a.NC, c0 + per);
   const int64_t step = static_cast<int64_t>(a.H) * a.M;
@@ -209,6 +211,7 @@ __global__ __launch_bounds__(256) void abc_weights(const AbcArgs a) {
   const int b = bx / (a.H * a.NC);
   const int tid = threadIdx.x;
   const int row = tid >> 3, cv = tid & 7;
+  if (8 * cv >= a.M) return;  // M = 32: half the threads
   const int n = min(kChunk, a.T - c * kChunk);
   const int64_t H = a.H, M = a.M;
   const float* zp = a.zc + ((static_cast<int64_t>(b) * a.NC + c) * H + h) * M + 8 * cv;
@@ -260,6 +263,11 @@ __global__ __launch_bounds__(256) void abc_bwd_weights(const AbcArgs a) {
   const int n = min(kChunk, a.T - c * kChunk);
   const int64_t H = a.H, M = a.M;
   const int64_t tok0 = static_cast<int64_t>(b) * a.T + static_cast<int64_t>(c) * kChunk;
+  if (tid < a.M / 4) {  // zc[c]: the M slots, four per thread
+    const f32x4_t zl = *reinterpret_cast<const f32x4_t*>(a.z + ((tok0 + n - 1) * H + h) * M + 4 * tid);
+    *reinterpret_cast<f32x4_t*>(a.zc + ((static_cast<int64_t>(b) * a.NC + c) * H + h) * M + 4 * tid) = zl;
+  }
+  if (8 * cv >= a.M) return;  // M = 32: half the threads
   float zp[8];
   if (c > 0) {
     const float* q = a.z + ((tok0 - 1) * H + h) * M + 8 * cv;
@@ -298,10 +306,6 @@ __global__ __launch_bounds__(256) void abc_bwd_weights(const AbcArgs a) {
     }
     *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.e) + off) = u32x4_t{yk[0], yk[1], yk[2], yk[3]};
     *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.e2) + off) = u32x4_t{yv[0], yv[1], yv[2], yv[3]};
-  }
-  if (tid < 16) {  // zc[c]: 64 slots, four per thread
-    const f32x4_t zl = *reinterpret_cast<const f32x4_t*>(a.z + ((tok0 + n - 1) * H + h) * M + 4 * tid);
-    *reinterpret_cast<f32x4_t*>(a.zc + ((static_cast<int64_t>(b) * a.NC + c) * H + h) * M + 4 * tid) = zl;
   }
 }
 
@@ -395,9 +399,10 @@ struct AbcStates {
     const uint16_t* ep = static_cast<const uint16_t*>(IS_K ? a.e : a.e2) + (tok0 * H + x.h) * a.M;
     const float* lp = a.zc + ((static_cast<int64_t>(x.b) * a.NC + pcc) * H + x.h) * a.M;
     const rsrc_t rx = make_rsrc(xp, any ? static_cast<uint32_t>(((n - 1) * H * x.X + XW) * 2) : 0u);
-    const rsrc_t re = make_rsrc(ep, any ? static_cast<uint32_t>(((n - 1) * H * a.M + 64) * 2) : 0u);
+    const rsrc_t re = make_rsrc(ep, any ? static_cast<uint32_t>(((n - 1) * H * a.M + a.M) * 2) : 0u);
     // the reverse ratio of a run's last step needs zc of the chunk after the run
-    const rsrc_t rl = make_rsrc(lp, (REV ? exists : any) ? 256u : 0u);
+    // (slots past M read as zero: r = 1 there)
+    const rsrc_t rl = make_rsrc(lp, (REV ? exists : any) ? static_cast<uint32_t>(4 * a.M) : 0u);
     if constexpr (XB >= 16) {
 #pragma unroll
       for (int i = 0; i < XB / 16; ++i) st.x[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, x.vo_x[i], 0, 0);
@@ -424,8 +429,10 @@ struct AbcStates {
       *reinterpret_cast<u32x2_t*>(xb + x.lo_x[0]) = u32x2_t{st.x[0].x, st.x[0].y};
     }
     const int row = tid >> 3, cv = tid & 7;
+    const bool slots = 8 * cv < a.M;  // M = 32: the upper 32 slots of the tile stay zero
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4_t*>(eb + (row + 32 * i) * STE + 16 * cv) = st.e[i];
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<u32x4_t*>(eb + (row + 32 * i) * STE + 16 * cv) = slots ? st.e[i] : u32x4_t{0u, 0u, 0u, 0u};
     if (REV) {  // this step's ratio, r_pc = exp(zc[pc-1] - zc[pc]); nothing precedes chunk 0
       if (tid < 64) sm.r[c % 3][tid] = (c < x.c_hi) ? (chunk_of(a, c) > 0 ? exp_fast(nxt.z - st.z) : 0.f) : 1.f;
     } else {
@@ -506,13 +513,15 @@ struct AbcStates {
 
   // Per-slot factors of this lane's accumulator elements: Hk^T rows are slots
   // (4 per lane), Hv^T columns are slots (one per tile).
+  // Slots past M (32) are padding: nothing is read for them.
   __device__ static __forceinline__ void slot_scale(f32x4_t (&acc)[NR], const float* z_from, const float* z_to,
-                                                    const f32x4_t (&add)[NR]) {
+                                                    const f32x4_t (&add)[NR], int M) {
     const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int rt = IS_K ? wave : wave % NR;
     const int ct0 = IS_K ? 0 : (wave / NR) * NR;
     if (IS_K) {
+      if (16 * rt >= M) return;
       f32x4_t f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) f[r] = exp_fast(z_from[16 * rt + 4 * g4 + r] - z_to[16 * rt + 4 * g4 + r]);
@@ -522,9 +531,19 @@ struct AbcStates {
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
         const int m = 16 * (ct0 + j) + c16;
-        acc[j] += add[j] * exp_fast(z_from[m] - z_to[m]);
+        if (m < M) acc[j] += add[j] * exp_fast(z_from[m] - z_to[m]);
       }
     }
+  }
+
+  // Whether this lane's accumulator tile j holds real slots (M = 32 pads the
+  // slot dimension to 64): Hk^T rows are slots, Hv^T columns are slots.
+  __device__ static __forceinline__ bool slot_live(int j, int M) {
+    const int lane = threadIdx.x & 63, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int rt = IS_K ? wave : wave % NR;
+    const int ct0 = IS_K ? 0 : (wave / NR) * NR;
+    return IS_K ? 16 * rt < M : 16 * (ct0 + j) + c16 < M;
   }
 
   __device__ static void run(const AbcArgs& a, Smem& sm, int b, int h, int x0, int seg, int unit) {
@@ -582,6 +601,10 @@ struct AbcStates {
         const int row = byte / RB, off = byte % RB;
         x.lo_o[i] = row * STH + off;
         x.vo_o[i] = IS_K ? row * a.M * 2 + off : row * a.V * 2 + off;
+        // M = 32: the staged Hk rows hold 64 slots; the upper half is never
+        // stored (an offset past every slab, dropped by the range check).
+        // Hv rows past M already fall past the slab.
+        if (IS_K && off >= a.M * 2) x.vo_o[i] = 0x40000000;
       }
     }
     f32x4_t acc[NR];
@@ -604,7 +627,7 @@ struct AbcStates {
         const float* lp = lsum_at(i);
 #pragma unroll
         for (int j = 0; j < NR; ++j) l[j] = *reinterpret_cast<const f32x4_t*>(lp + 4 * j);
-        slot_scale(acc, zrow + end_i * zs, z_start, l);
+        slot_scale(acc, zrow + end_i * zs, z_start, l, a.M);
       }
     }
     if (MODE == 0 && REV && x.c_lo < x.c_hi) {
@@ -619,8 +642,9 @@ struct AbcStates {
         const float* gb = ge + (IS_K ? (fb * a.K + x0) * a.M : fb * a.M * a.V + x0);
         f32x4_t l[NR];
 #pragma unroll
-        for (int j = 0; j < NR; ++j) l[j] = *reinterpret_cast<const f32x4_t*>(gb + x.vo_h[j] / 2);
-        slot_scale(acc, z_from, zrow + (a.NC - 1) * zs, l);
+        for (int j = 0; j < NR; ++j)
+          l[j] = slot_live(j, a.M) ? *reinterpret_cast<const f32x4_t*>(gb + x.vo_h[j] / 2) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        slot_scale(acc, z_from, zrow + (a.NC - 1) * zs, l, a.M);
       }
       const int base = a.NC / a.P, extra = a.NC % a.P;
       for (int i = 0; i < seg; ++i) {
@@ -629,7 +653,7 @@ struct AbcStates {
         const float* lp = lsum_at(i);
 #pragma unroll
         for (int j = 0; j < NR; ++j) l[j] = *reinterpret_cast<const f32x4_t*>(lp + 4 * j);
-        slot_scale(acc, z_from, zrow + (a.NC - hi_i - 1) * zs, l);  // a_i - 1 = NC - hi_i - 1
+        slot_scale(acc, z_from, zrow + (a.NC - hi_i - 1) * zs, l, a.M);  // a_i - 1 = NC - hi_i - 1
       }
     }
 
@@ -639,9 +663,10 @@ struct AbcStates {
 #pragma unroll
       for (int i = 0; i < D; ++i) load(st[i], x, x.c_lo + i);
       if (!REV && tid < 64) {
-        // r of the run's first chunk (0 at the sequence start: nothing before it)
+        // r of the run's first chunk (0 at the sequence start: nothing before it; 1 on padding slots)
         const float* zr = a.zc + ((static_cast<int64_t>(b) * a.NC + x.c_lo) * a.H + h) * a.M + tid;
-        sm.r[x.c_lo % 3][tid] = x.c_lo == 0 ? 0.f : exp_fast(zr[-static_cast<int64_t>(a.H) * a.M] - zr[0]);
+        sm.r[x.c_lo % 3][tid] =
+            tid >= a.M ? 1.f : x.c_lo == 0 ? 0.f : exp_fast(zr[-static_cast<int64_t>(a.H) * a.M] - zr[0]);
       }
       __syncthreads();
       const int ncp = (nc + D - 1) / D * D;
@@ -673,7 +698,8 @@ struct AbcStates {
     const int64_t fb = static_cast<int64_t>(b) * a.H + h;
     float* base = fp + (IS_K ? (fb * a.K + x0) * a.M : fb * a.M * a.V + x0);
 #pragma unroll
-    for (int j = 0; j < NR; ++j) *reinterpret_cast<f32x4_t*>(base + x.vo_h[j] / 2) = acc[j];
+    for (int j = 0; j < NR; ++j)
+      if (slot_live(j, a.M)) *reinterpret_cast<f32x4_t*>(base + x.vo_h[j] / 2) = acc[j];
   }
 };
 
@@ -740,7 +766,7 @@ hipError_t launch_abc(const AbcArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (a.NC > 0) {
-    hipLaunchKernelGGL(abc_carry, dim3(a.B * a.H * 16), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(abc_carry, dim3(a.B * a.H * (a.M / 4)), dim3(64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -24,8 +24,8 @@ bool abc_valid(const abc_problem* p, std::string& err) {
     err = "T too large";
     return false;
   }
-  if (p->M != 64) {
-    err = "M (slots) must be 64";
+  if (p->M != 64 && p->M != 32) {
+    err = "M (slots) must be 32 or 64";
     return false;
   }
   if (p->K < 64 || p->K % 64 != 0 || p->V < 64 || p->V % 64 != 0 || p->K > 4096 || p->V > 4096) {
@@ -56,11 +56,12 @@ size_t abc_workspace_size(const abc_problem* p) {
   if (!abc_valid(p, err)) return 0;
   const int64_t nc = (p->T + 63) / 64;
   // chunk log-sum-exps and chunk-end normalisers (FP32), the weights E
-  // (storage dtype), then the end states of the state walk's runs (FP32)
+  // (storage dtype), then the end states of the state walk's runs (FP32,
+  // always 64 slots: M = 32 is padded)
   const int P = gdr::abc_segments(p->B, p->H, p->K, p->V, static_cast<int>(nc));
   return 2 * static_cast<size_t>(p->B) * nc * p->H * p->M * sizeof(float) +
-         static_cast<size_t>(p->B) * p->T * p->H * p->M * 2 +
-         static_cast<size_t>(p->B) * p->H * (P - 1) * (p->K + p->V) * p->M * sizeof(float);
+         static_cast<size_t>(p->B) * p->T * p->H * p->M * 2 + 16 +
+         static_cast<size_t>(p->B) * p->H * (P - 1) * (p->K + p->V) * 64 * sizeof(float);
 }
 
 gdr_status abc_affine_scan(const abc_problem* p, const void* k, const void* v, const void* s, float* z, void* hk,
@@ -134,6 +135,10 @@ gdr_status abc_chunk_output(const abc_problem* p, const void* q, const void* k, 
     gdr_internal::set_last_error(err);
     return GDR_ERR_INVALID_ARG;
   }
+  if (p->M != 64) {
+    gdr_internal::set_last_error("abc_chunk_output is built for M = 64 slots");
+    return GDR_ERR_UNSUPPORTED;
+  }
   if (!gdr::abc_out_supported(p->K, p->V)) {
     gdr_internal::set_last_error("abc_chunk_output is built for (K, V) in {(64,128), (128,128), (128,256), (256,256), (256,512)}");
     return GDR_ERR_UNSUPPORTED;
@@ -181,11 +186,11 @@ size_t abc_bwd_workspace_size(const abc_problem* p) {
   if (!abc_valid(p, err)) return 0;
   const int64_t nc = (p->T + 63) / 64;
   // chunk-end normalisers (FP32), the two weight tensors (storage dtype),
-  // then the end states of the reverse walk's runs (FP32)
+  // then the end states of the reverse walk's runs (FP32, always 64 slots)
   const int P = gdr::abc_segments(p->B, p->H, p->K, p->V, static_cast<int>(nc));
   return static_cast<size_t>(p->B) * nc * p->H * p->M * sizeof(float) +
-         2 * static_cast<size_t>(p->B) * p->T * p->H * p->M * 2 +
-         static_cast<size_t>(p->B) * p->H * (P - 1) * (p->K + p->V) * p->M * sizeof(float);
+         2 * static_cast<size_t>(p->B) * p->T * p->H * p->M * 2 + 16 +
+         static_cast<size_t>(p->B) * p->H * (P - 1) * (p->K + p->V) * 64 * sizeof(float);
 }
 
 gdr_status abc_affine_scan_bwd(const abc_problem* p, const void* q, const void* dscore, const void* pw,
@@ -237,7 +242,10 @@ gdr_status abc_affine_scan_bwd(const abc_problem* p, const void* q, const void* 
   const int64_t nw = static_cast<int64_t>(a.B) * a.T * a.H * a.M;
   a.e = a.zc + nzc;
   a.e2 = static_cast<uint16_t*>(a.e) + nw;
-  a.lsum = reinterpret_cast<float*>(static_cast<uint16_t*>(a.e2) + nw);
+  {
+    const uintptr_t e2_end = reinterpret_cast<uintptr_t>(static_cast<uint16_t*>(a.e2) + nw);
+    a.lsum = reinterpret_cast<float*>((e2_end + 15) & ~static_cast<uintptr_t>(15));
+  }
   a.P = gdr::abc_segments(a.B, a.H, a.K, a.V, a.NC);
   hipError_t e = gdr::launch_abc_bwd(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {

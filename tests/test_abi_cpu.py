@@ -253,6 +253,30 @@ def test_abc_reverse_validation():
     assert L.abc_affine_scan_bwd(ctypes.byref(p32), *args) == B.GDR_ERR_INVALID_ARG
 
 
+def test_abc_slot_counts():
+    """M = 32 and 64 slots are accepted by the scan (its run end states keep 64
+    padded slots whatever M is, which the workspace size covers); other counts
+    are argument errors before any launch; the read is built for M = 64 only."""
+    L = B.lib()
+    B_, T, H, K, V = 2, 16384, 4, 256, 512
+    for m in (32, 64):
+        p = B.abc_problem(B_, T, H, K, m, V, B.GDR_BF16)
+        ws = L.abc_workspace_size(ctypes.byref(p))
+        nc = T // 64
+        runs = 8  # the run split of this shape (64-column tiles: 768 units)
+        assert ws >= 2 * B_ * nc * H * m * 4 + B_ * T * H * m * 2 + B_ * H * (runs - 1) * (K + V) * 64 * 4, m
+        assert L.abc_bwd_workspace_size(ctypes.byref(p)) >= B_ * H * (runs - 1) * (K + V) * 64 * 4
+    for m in (16, 48, 128):
+        p = B.abc_problem(1, 128, 2, 64, m, 64, B.GDR_BF16)
+        assert L.abc_workspace_size(ctypes.byref(p)) == 0, m
+        args = [FAKE] * 3 + [None, FAKE, FAKE, None, None, FAKE, 1 << 20, None]
+        assert L.abc_affine_scan(ctypes.byref(p), *args) == B.GDR_ERR_INVALID_ARG
+        assert "M" in L.gdr_last_error().decode()
+    p = B.abc_problem(1, 128, 2, 256, 32, 512, B.GDR_BF16)
+    args = [FAKE] * 7 + [ctypes.c_float(1.0), FAKE, None, None]
+    assert L.abc_chunk_output(ctypes.byref(p), *args) == B.GDR_ERR_UNSUPPORTED
+
+
 def test_abc_read_validation():
     L = B.lib()
     p = B.abc_problem(1, 128, 2, 64, 64, 64, B.GDR_BF16)  # V = 64 is not built

@@ -54,12 +54,32 @@ def compare(r, ref, what=""):
         assert worst.get(key, (0.0,))[0] <= 1e-2, f"{what} {key} {worst[key]}"
 
 
-@pytest.mark.parametrize("T", [1, 63, 64, 65, 257])
-def test_abc_small(pkg, T):
-    inp = make_abc(900 + T, B=2, T=T, H=2, K=128, M=64, V=192)
+@pytest.mark.parametrize("M", [64, 32])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 127, 257])
+def test_abc_small(pkg, T, M):
+    """The fixture lengths and slot counts of fla#23's "Fixture-First
+    Correctness Contract" (T = 63/64/65/127/257, M = 32/64) and one token."""
+    inp = make_abc(900 + T + M, B=2, T=T, H=2, K=128, M=M, V=192)
     d = inp.f64()
     ref = oracle.abc_recurrent_fp64(d["k"], d["v"], d["s"])
-    compare(run(pkg, inp), ref, what=f"abc T={T}")
+    compare(run(pkg, inp), ref, what=f"abc T={T} M={M}")
+
+
+@pytest.mark.parametrize("runs", [1, 3])
+def test_abc_32_slots_tiles_and_runs(pkg, monkeypatch, runs):
+    """M = 32 (the slot dimension padded to 64 inside the kernels): every tile
+    width gives the same bits, split into runs or not, against the oracle."""
+    inp = make_abc(975 + runs, B=2, T=1100, H=2, K=128, M=32, V=192)
+    monkeypatch.setenv("GDR_ABC_SEGMENTS", str(runs))
+    outs = {}
+    for xw in (64, 32, 16):
+        monkeypatch.setenv("GDR_ABC_XW", str(xw))
+        outs[xw] = run(pkg, inp)
+    for xw in (32, 16):
+        for key in outs[64]:
+            assert torch.equal(outs[64][key], outs[xw][key]), (runs, xw, key)
+    d = inp.f64()
+    compare(outs[64], oracle.abc_recurrent_fp64(d["k"], d["v"], d["s"]), what=f"abc M=32 runs={runs}")
 
 
 def test_abc_affine_workload(pkg):

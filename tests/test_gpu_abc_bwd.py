@@ -85,6 +85,14 @@ def test_abc_bwd_parity(pkg, shape):
     check(pkg, inp, upstream(inp, 981 + T), 0.7, what=f"abc bwd {shape}")
 
 
+@pytest.mark.parametrize("runs", [1, 3])
+def test_abc_bwd_32_slots(pkg, monkeypatch, runs):
+    """M = 32 slots (padded to 64 inside the walk) against the oracle."""
+    inp = make_abc(989 + runs, B=2, T=1100, H=2, K=128, M=32, V=192)
+    monkeypatch.setenv("GDR_ABC_SEGMENTS", str(runs))
+    check(pkg, inp, upstream(inp, 990 + runs), 0.8, what=f"abc bwd M=32 runs={runs}")
+
+
 def test_abc_bwd_without_final_gradient(pkg):
     inp = make_abc(985, B=1, T=300, H=2, K=64, M=64, V=64)
     check(pkg, inp, upstream(inp, 986, with_end=False), 1.0, what="abc bwd no end gradient")
