@@ -332,7 +332,7 @@ gdr_status abc_affine_scan(const abc_problem* p, const void* k, const void* v, c
  * v [B, T, H, V], s [B, T, H, M] (storage dtype), z [B, T, H, M] float32 and
  * hk [B, NC, H, K, M], hv [B, NC, H, M, V] as abc_affine_scan writes them.
  * Outputs: o [B, T, H, V] (storage dtype); p_out (nullable) [B, T, H, M] the
- * slot weights.  Bfloat16 storage, M = 64, (K, V) in {(64, 128), (128, 128),
+ * slot weights.  Bfloat16 storage, M = 32 or 64, (K, V) in {(64, 128), (128, 128),
  * (128, 256), (256, 256), (256, 512)} (else GDR_ERR_UNSUPPORTED). */
 gdr_status abc_chunk_output(const abc_problem* p, const void* q, const void* k, const void* v, const void* s,
                             const float* z, const void* hk, const void* hv, float scale, void* o, void* p_out,

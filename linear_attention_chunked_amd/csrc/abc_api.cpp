@@ -135,10 +135,6 @@ gdr_status abc_chunk_output(const abc_problem* p, const void* q, const void* k, 
     gdr_internal::set_last_error(err);
     return GDR_ERR_INVALID_ARG;
   }
-  if (p->M != 64) {
-    gdr_internal::set_last_error("abc_chunk_output is built for M = 64 slots");
-    return GDR_ERR_UNSUPPORTED;
-  }
   if (!gdr::abc_out_supported(p->K, p->V)) {
     gdr_internal::set_last_error("abc_chunk_output is built for (K, V) in {(64,128), (128,128), (128,256), (256,256), (256,512)}");
     return GDR_ERR_UNSUPPORTED;
@@ -173,6 +169,7 @@ gdr_status abc_chunk_output(const abc_problem* p, const void* q, const void* k, 
   a.K = p->K;
   a.V = p->V;
   a.NC = static_cast<int32_t>((p->T + 63) / 64);
+  a.M = p->M;
   hipError_t e = gdr::launch_abc_out(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     gdr_internal::set_last_error(std::string("abc read launch: ") + hipGetErrorString(e));

@@ -30,7 +30,7 @@ struct AbcOut {
   using S = St<bf16_t>;
   using frag = S::frag;
   static constexpr int NT = 512;
-  static constexpr int M = 64;
+  static constexpr int M = 64;            // slots of the tiles (a.M = 32 is padding above it)
   static constexpr int SQ = K * 2 + 16;   // Q, K rows (row fragments)
   static constexpr int SHK = M * 2 + 32;  // Hk rows (transpose reads)
   static constexpr int SVV = V * 2 + 32;  // Hv, V rows (transpose reads)
@@ -66,17 +66,18 @@ struct AbcOut {
     const int64_t H = a.H;
     const int64_t tok0 = static_cast<int64_t>(b) * a.T + static_cast<int64_t>(c) * kChunk;
     const int64_t plane = (static_cast<int64_t>(b) * a.NC + c) * H + h;
+    const int MS = a.M;  // stored slots (32 or 64): slots past MS are padding, score -inf, p = 0
 
     const rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(a.q) + (tok0 * H + h) * K,
                                 static_cast<uint32_t>(((n - 1) * H * K + K) * 2));
     const rsrc_t rk = make_rsrc(static_cast<const uint16_t*>(a.k) + (tok0 * H + h) * K,
                                 static_cast<uint32_t>(((n - 1) * H * K + K) * 2));
-    const rsrc_t rhk = make_rsrc(static_cast<const uint16_t*>(a.hk) + plane * K * M, K * M * 2);
-    const rsrc_t rs = make_rsrc(static_cast<const uint16_t*>(a.s) + (tok0 * H + h) * M,
-                                static_cast<uint32_t>(((n - 1) * H * M + M) * 2));
-    const rsrc_t rz = make_rsrc(a.z + (tok0 * H + h) * M, static_cast<uint32_t>(((n - 1) * H * M + M) * 4));
-    const rsrc_t rzp = make_rsrc(a.z + (c > 0 ? ((tok0 - 1) * H + h) * M : 0), c > 0 ? M * 4 : 0u);
-    const rsrc_t rhv = make_rsrc(static_cast<const uint16_t*>(a.hv) + plane * M * V, M * V * 2);
+    const rsrc_t rhk = make_rsrc(static_cast<const uint16_t*>(a.hk) + plane * K * MS, K * MS * 2);
+    const rsrc_t rs = make_rsrc(static_cast<const uint16_t*>(a.s) + (tok0 * H + h) * MS,
+                                static_cast<uint32_t>(((n - 1) * H * MS + MS) * 2));
+    const rsrc_t rz = make_rsrc(a.z + (tok0 * H + h) * MS, static_cast<uint32_t>(((n - 1) * H * MS + MS) * 4));
+    const rsrc_t rzp = make_rsrc(a.z + (c > 0 ? ((tok0 - 1) * H + h) * MS : 0), c > 0 ? MS * 4 : 0u);
+    const rsrc_t rhv = make_rsrc(static_cast<const uint16_t*>(a.hv) + plane * MS * V, MS * V * 2);
     const rsrc_t rv = make_rsrc(static_cast<const uint16_t*>(a.v) + (tok0 * H + h) * V,
                                 static_cast<uint32_t>(((n - 1) * H * V + V) * 2));
 
@@ -88,11 +89,15 @@ struct AbcOut {
       const int go = static_cast<int>(r * H * K * 2 + cc * 16);
       lq[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, go, 0, 0);
       lk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, go, 0, 0);
-      lh[i] = __builtin_amdgcn_raw_buffer_load_b128(rhk, static_cast<int>(v * 16), 0, 0);
+      // Hk row v >> 3, 16-byte piece v & 7 (pieces past the stored slots read as zero)
+      lh[i] = 8 * (v & 7) < MS ? __builtin_amdgcn_raw_buffer_load_b128(
+                                     rhk, static_cast<int>((v >> 3) * MS * 2 + (v & 7) * 16), 0, 0)
+                               : u32x4_t{0u, 0u, 0u, 0u};
     }
     const int srow = tid >> 3, scv = tid & 7;
-    const u32x4_t ls = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>((srow * H * M + 8 * scv) * 2), 0, 0);
-    const int zlo = static_cast<int>(((n - 1) * H * M) * 4);
+    const bool sl = 8 * scv < MS;  // this thread's eight slots are stored ones
+    const u32x4_t ls = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>((srow * H * MS + 8 * scv) * 2), 0, 0);
+    const int zlo = static_cast<int>(((n - 1) * H * MS) * 4);
     const f32x4_t zl0 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rz, zlo + 32 * scv, 0, 0));
     const f32x4_t zl1 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rz, zlo + 32 * scv + 16, 0, 0));
     // score rows of waves 0-3: z[t][m] for t = 16 wave + 4 g4 + r, m = 16 mt + c16
@@ -104,7 +109,7 @@ struct AbcOut {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         zt[mt][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                  rz, static_cast<int>(((16 * tb + 4 * g4 + r) * H * M + m) * 4), 0, 0));
+                                                  rz, static_cast<int>(((16 * tb + 4 * g4 + r) * H * MS + m) * 4), 0, 0));
       zpv[mt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rzp, 4 * m, 0, 0));
       zlv[mt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, zlo + 4 * m, 0, 0));
     }
@@ -130,7 +135,7 @@ struct AbcOut {
       uint32_t pk[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        pk[j] = srow < n ? pack_bf16x2(exp_fast(__builtin_bit_cast(float, w[j] << 16) - zz[2 * j]),
+        pk[j] = (srow < n && sl) ? pack_bf16x2(exp_fast(__builtin_bit_cast(float, w[j] << 16) - zz[2 * j]),
                                        exp_fast(__builtin_bit_cast(float, w[j] & 0xffff0000u) - zz[2 * j + 1]))
                          : 0u;
       *reinterpret_cast<u32x4_t*>(sm + OFF_E + srow * SP + 16 * scv) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
@@ -178,12 +183,12 @@ struct AbcOut {
         for (int r = 0; r < 4; ++r) {
           x1[mt][r] = exp_fast(zp - zt[mt][r]);
           x2[mt][r] = exp_fast(zlv[mt] - zt[mt][r]);
-          sc[mt][r] = a.scale * (x1[mt][r] * s1[mt][r] + x2[mt][r] * s2[mt][r]);
+          sc[mt][r] = 16 * mt + c16 < MS ? a.scale * (x1[mt][r] * s1[mt][r] + x2[mt][r] * s2[mt][r]) : -INFINITY;
         }
       }
       uint16_t* pp = static_cast<uint16_t*>(a.p);
-      const rsrc_t rp = make_rsrc(pp + (pp != nullptr ? (tok0 * H + h) * M : 0),
-                                  pp != nullptr ? static_cast<uint32_t>(((n - 1) * H * M + M) * 2) : 0u);
+      const rsrc_t rp = make_rsrc(pp + (pp != nullptr ? (tok0 * H + h) * MS : 0),
+                                  pp != nullptr ? static_cast<uint32_t>(((n - 1) * H * MS + MS) * 2) : 0u);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tr = 16 * tb + 4 * g4 + r;
@@ -201,12 +206,13 @@ struct AbcOut {
         const float inv = 1.f / sum;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const bool live = tr < n;  // rows past the end read zeros and may hold non-finite scores
-          const float p = live ? e[mt] * inv : 0.f;
           const int m = 16 * mt + c16;
+          // rows past the end read zeros and may hold non-finite scores; padding slots hold none
+          const bool live = tr < n && m < MS;
+          const float p = live ? e[mt] * inv : 0.f;
           *reinterpret_cast<__bf16*>(sm + OFF_P1 + tr * SP + 2 * m) = static_cast<__bf16>(live ? p * x1[mt][r] : 0.f);
           *reinterpret_cast<__bf16*>(sm + OFF_P2 + tr * SP + 2 * m) = static_cast<__bf16>(live ? p * x2[mt][r] : 0.f);
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(p), rp, static_cast<int>((tr * H * M + m) * 2), 0, 0);
+          if (m < MS) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(p), rp, static_cast<int>((tr * H * MS + m) * 2), 0, 0);
         }
       }
     }

@@ -195,6 +195,7 @@ struct AbcOutArgs {
   void* p;             // nullable [B, T, H, M]
   float scale;
   int32_t B, T, H, K, V, NC;
+  int32_t M;           // slots: 64, or 32 (padded to 64 inside the kernel)
 };
 bool abc_out_supported(int K, int V);
 hipError_t launch_abc_out(const AbcOutArgs& a, hipStream_t s);

@@ -256,7 +256,7 @@ def test_abc_reverse_validation():
 def test_abc_slot_counts():
     """M = 32 and 64 slots are accepted by the scan (its run end states keep 64
     padded slots whatever M is, which the workspace size covers); other counts
-    are argument errors before any launch; the read is built for M = 64 only."""
+    are argument errors before any launch, for the scan and the read."""
     L = B.lib()
     B_, T, H, K, V = 2, 16384, 4, 256, 512
     for m in (32, 64):
@@ -272,9 +272,8 @@ def test_abc_slot_counts():
         args = [FAKE] * 3 + [None, FAKE, FAKE, None, None, FAKE, 1 << 20, None]
         assert L.abc_affine_scan(ctypes.byref(p), *args) == B.GDR_ERR_INVALID_ARG
         assert "M" in L.gdr_last_error().decode()
-    p = B.abc_problem(1, 128, 2, 256, 32, 512, B.GDR_BF16)
-    args = [FAKE] * 7 + [ctypes.c_float(1.0), FAKE, None, None]
-    assert L.abc_chunk_output(ctypes.byref(p), *args) == B.GDR_ERR_UNSUPPORTED
+        rargs = [FAKE] * 7 + [ctypes.c_float(1.0), FAKE, None, None]
+        assert L.abc_chunk_output(ctypes.byref(p), *rargs) == B.GDR_ERR_INVALID_ARG
 
 
 def test_abc_read_validation():

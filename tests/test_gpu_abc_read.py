@@ -62,6 +62,15 @@ def test_abc_read_parity(pkg, shape):
     check(pkg, inp, queries(inp, 991 + T), K ** -0.5, what=f"abc read {shape}")
 
 
+@pytest.mark.parametrize("shape", [(2, 127, 2, 128, 128), (1, 257, 1, 256, 512)], ids=lambda s: "x".join(map(str, s)))
+def test_abc_read_32_slots(pkg, shape):
+    """M = 32 slots (padded to 64 inside the kernel, the padding scored -inf):
+    the whole forward, scan then read, against the oracle."""
+    B, T, H, K, V = shape
+    inp = make_abc(995 + T, B=B, T=T, H=H, K=K, M=32, V=V)
+    check(pkg, inp, queries(inp, 996 + T), K ** -0.5, what=f"abc read M=32 {shape}")
+
+
 def test_abc_read_benchmark_shape(pkg):
     """B=2, T=16384, H=4, K=256, M=64, V=512 against the oracle on every
     (batch row, head); deterministic run to run."""
