@@ -20,8 +20,8 @@
 // workgroup per (sequence, head, 64 value columns), dS in FP32 MFMA
 // accumulators for the whole loop, K as row fragments (K dS contracts over
 // dk), Q and W through ds_read_b64_tr_b16 (Q^T and W^T contract over tokens),
-// the next chunk's tiles prefetched in registers, dh and dv_new staged in LDS
-// and written as whole 16-byte vectors.
+// the next chunk's tiles prefetched in registers, dh and dv_new stored straight
+// from the accumulators (no LDS staging, so two 128-key workgroups share a CU).
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
@@ -189,12 +189,9 @@ struct ScanBwd {
   static constexpr int OFF_DO = OFF_W + kChunk * SQT, OFF_DL = OFF_DO + kChunk * SDV;
   static constexpr int OFF_F = OFF_DL + kChunk * SDV;  // d_i = e^{gC - g_i}, f_t = scale e^{g_t}, then e^{gC}
   static constexpr int BUF = OFF_F + 2 * kChunk * 4 + 16;
-  static constexpr int SHS = DK * 2 + 16, SVS = BV * 2 + 16;  // staged dh / dv_new rows
-  static constexpr int OFF_HS = BUF, OFF_VS = OFF_HS + BV * SHS;
-  static constexpr int SMEM = OFF_VS + kChunk * SVS;
+  static constexpr int SMEM = BUF;
   static constexpr int R_PT = kChunk * CPR / NT;   // 16-byte K / Q / W vectors per thread
   static constexpr int V_PT = kChunk * CPV / NT;   // 16-byte dO / dv_local vectors per thread
-  static constexpr int H_PT = BV * DK / 8 / NT;
 
   struct Stage {
     u32x4_t k[R_PT], q[R_PT], w[R_PT];
@@ -261,50 +258,32 @@ struct ScanBwd {
     }
   }
 
-  __device__ static __forceinline__ void write_out(const Ctx& x, const Row& row, int c, const char* so) {
+  // One chunk, dS carried in from the later chunks.
+  __device__ static __forceinline__ void compute(f32x4_t (&Sacc)[DT], const char* buf, const Ctx& x, const Row& row,
+                                                 int c) {
     const ScanBwdArgs& a = *x.a;
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int colw = 16 * wave;  // this wave's 16 columns of the block
     const int64_t H = x.H;
     const int DV = x.DV;
     const int64_t tok0 = static_cast<int64_t>(row.bos) + static_cast<int64_t>(c) * kChunk;
     const int nvalid = min(kChunk, row.len - c * kChunk);
-    uint16_t* hp = static_cast<uint16_t*>(a.dh) + ((static_cast<int64_t>(row.chunk_off) + c) * H + x.hd) * DV * DK +
-                   static_cast<int64_t>(x.col_blk) * DK;
-    const rsrc_t rh = make_rsrc(hp, a.dh != nullptr ? static_cast<uint32_t>(BV * DK * 2) : 0u);
-#pragma unroll
-    for (int i = 0; i < H_PT; ++i) {
-      const int v = tid + NT * i;
-      const u32x4_t q = *reinterpret_cast<const u32x4_t*>(so + (v / (DK / 8)) * SHS + (v % (DK / 8)) * 16);
-      __builtin_amdgcn_raw_buffer_store_b128(q, rh, 16 * v, 0, kStreamStore);
-    }
-    uint16_t* vp = static_cast<uint16_t*>(a.dv) + (tok0 * H + x.hd) * DV + x.col_blk;
-    const rsrc_t rv = make_rsrc(vp, a.dv != nullptr ? static_cast<uint32_t>(((nvalid - 1) * H * DV + BV) * 2) : 0u);
-#pragma unroll
-    for (int i = 0; i < V_PT; ++i) {
-      const int v = tid + NT * i;
-      const int t = v / (BV / 8), p = v % (BV / 8);
-      const u32x4_t q = *reinterpret_cast<const u32x4_t*>(so + (OFF_VS - OFF_HS) + t * SVS + p * 16);
-      __builtin_amdgcn_raw_buffer_store_b128(q, rv, static_cast<int>(t * H * DV * 2) + 16 * p, 0, kStreamStore);
-    }
-  }
 
-  // One chunk, dS carried in from the later chunks.
-  __device__ static __forceinline__ void compute(f32x4_t (&Sacc)[DT], const char* buf, char* so) {
-    const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    const int colw = 16 * wave;  // this wave's 16 columns of the block
-
-    // dS as B operand; dh[c] = dS (staged)
+    // dS as B operand; dh[c] = dS, stored from the registers (value row colw + c16, 4 keys per piece)
     frag Sb[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) Sb[s] = S::frag_from_f32(Sacc[2 * s], Sacc[2 * s + 1]);
     {
-      char* hs = so + (colw + c16) * SHS + 8 * g4;
+      uint16_t* hp = static_cast<uint16_t*>(a.dh) + ((static_cast<int64_t>(row.chunk_off) + c) * H + x.hd) * DV * DK +
+                     static_cast<int64_t>(x.col_blk) * DK;
+      const rsrc_t rh = make_rsrc(hp, a.dh != nullptr ? static_cast<uint32_t>(BV * DK * 2) : 0u);
+      const int ho = ((colw + c16) * DK + 4 * g4) * 2;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const u32x4_t q = __builtin_bit_cast(u32x4_t, Sb[s].v);
-        *reinterpret_cast<u32x2_t*>(hs + 64 * s) = u32x2_t{q.x, q.y};
-        *reinterpret_cast<u32x2_t*>(hs + 64 * s + 32) = u32x2_t{q.z, q.w};
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{q.x, q.y}, rh, ho, 64 * s, kStreamStore);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{q.z, q.w}, rh, ho, 64 * s + 32, kStreamStore);
       }
     }
     // GEMM1: acc = K dS (tokens x this wave's columns)
@@ -334,15 +313,20 @@ struct ScanBwd {
                        __builtin_bit_cast(float, l.y << 16), __builtin_bit_cast(float, l.y & 0xffff0000u)};
       acc[mt] = acc[mt] * d + lf;
     }
-    {  // stage dv_new (rows = tokens)
-      uint16_t* vs = reinterpret_cast<uint16_t*>(so + (OFF_VS - OFF_HS)) + (4 * g4) * (SVS / 2) + colw + c16;
+    {  // dv_new (rows = tokens, rows past the tail dropped by the range check)
+      uint16_t* vp = static_cast<uint16_t*>(a.dv) + (tok0 * H + x.hd) * DV + x.col_blk;
+      const rsrc_t rv =
+          make_rsrc(vp, a.dv != nullptr ? static_cast<uint32_t>(((nvalid - 1) * H * DV + BV) * 2) : 0u);
+      const int rs = static_cast<int>(H * DV * 2);
+      const int voff = (4 * g4) * rs + (colw + c16) * 2;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; r += 2) {
           const uint32_t pk = pack_bf16x2(acc[mt][r], acc[mt][r + 1]);
-          vs[(16 * mt + r) * (SVS / 2)] = static_cast<uint16_t>(pk);
-          vs[(16 * mt + r + 1) * (SVS / 2)] = static_cast<uint16_t>(pk >> 16);
+          const int so2 = (16 * mt + r) * rs;
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk), rv, voff, so2, kStreamStore);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk >> 16), rv, voff, so2 + rs, kStreamStore);
         }
     }
     // B operands over tokens: -dv_new, and f_t dO_t
@@ -427,7 +411,6 @@ struct ScanBwd {
     }
 
     char* buf = smem;
-    char* so = smem + OFF_HS;
     auto tok_of = [&](int c) { return static_cast<int64_t>(row.bos) + static_cast<int64_t>(c) * kChunk; };
     auto nv_of = [&](int c) { return c >= 0 ? min(kChunk, row.len - c * kChunk) : 0; };
     if (nchunks > 0) {
@@ -435,14 +418,11 @@ struct ScanBwd {
       load(st, x, tok_of(nchunks - 1), nv_of(nchunks - 1));
       for (int c = nchunks - 1; c >= 0; --c) {
         __syncthreads();
-        if (c + 1 < nchunks) write_out(x, row, c + 1, so);
         store(st, x, buf, nv_of(c));
         __syncthreads();
         load(st, x, tok_of(c - 1 >= 0 ? c - 1 : 0), nv_of(c - 1));
-        compute(Sacc, buf, so);
+        compute(Sacc, buf, x, row, c);
       }
-      __syncthreads();
-      write_out(x, row, 0, so);
     }
 
     if (row.out_idx < 0 || a.dh0 == nullptr) return;
