@@ -19,6 +19,14 @@
 // r -> elements 4 + r.  That is what lets the scan keep its FP32 state in
 // accumulator registers and feed it straight back as a matrix-core operand,
 // with no LDS round trip.
+//
+// A product whose two operands are both read from memory (not from an
+// accumulator) may use the contiguous map k(g, e) = 8 g + e instead: each
+// lane then reads 16 contiguous bytes of a row, one ds_read_b128, where the
+// map above needs two 8-byte pieces 32 bytes apart (one ds_read2_b64, which
+// gfx950 serves at half the rate).  Kernels whose results must agree bit for
+// bit (the chunk output and the state scan with the output fused) use the
+// same map for the same product.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -45,4 +45,11 @@ __device__ __forceinline__ u32x2_t lds_b64(const char* base, int byte_off) {
   return *reinterpret_cast<const u32x2_t*>(base + byte_off);
 }
 
+// A bf16 row fragment in the contiguous k map (common.hpp): the lane's 16
+// bytes at base + byte_off, one ds_read_b128 (16-byte aligned).
+__device__ __forceinline__ St<bf16_t>::frag lds_frag16(const char* base, int byte_off) {
+  const u32x4_t q = *reinterpret_cast<const u32x4_t*>(base + byte_off);
+  return St<bf16_t>::frag_from_quads(u32x2_t{q.x, q.y}, u32x2_t{q.z, q.w});
+}
+
 }  // namespace gdr

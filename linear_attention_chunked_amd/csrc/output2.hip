@@ -101,12 +101,10 @@ struct Output2 {
     }
     __syncthreads();
 
-    const char* rowq = sm.A.q + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;  // + 16 tile SQ + 64 s (+32)
-    const char* rowk = sm.A.k + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;
-    auto rfrag = [&](const char* base, int tile, int s) {
-      return S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(base + 16 * tile * SQ + 64 * s),
-                                *reinterpret_cast<const u32x2_t*>(base + 16 * tile * SQ + 64 * s + 32));
-    };
+    // row fragments in the contiguous k map (16 bytes per lane)
+    const char* rowq = sm.A.q + c16 * SQ + 16 * g4;  // + 16 tile SQ + 64 s
+    const char* rowk = sm.A.k + c16 * SQ + 16 * g4;
+    auto rfrag = [&](const char* base, int tile, int s) { return lds_frag16(base, 16 * tile * SQ + 64 * s); };
 
     // ---- P^T[i][t] = k_i . q_t for t in tile `wave`, i tiles 0..wave; Q fragments kept ----
     frag fq[KS];
@@ -151,7 +149,7 @@ struct Output2 {
     __syncthreads();
 
     // ---- O = e^{gamma} (Q S_c) + P v_new, rows of token tile `wave` ----
-    const char* rowh = sm.B.h + c16 * SQ + (g4 >> 1) * 16 + (g4 & 1) * 8;
+    const char* rowh = sm.B.h + c16 * SQ + 16 * g4;
     f32x4_t acc[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};

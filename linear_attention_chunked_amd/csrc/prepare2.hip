@@ -27,8 +27,13 @@ struct Prepare2 {
   using S = St<bf16_t>;
   using frag = S::frag;
   static constexpr int NT = 256;
-  static constexpr int SKB = DK * 2 + 16;   // padded row strides (bytes)
-  static constexpr int SVB = DV * 2 + 16;
+  // Padded row strides (bytes).  K is read by rows (Gram) and transposed
+  // (w); rows 8..15 of every 16 sit KX bytes further on, so that both read
+  // patterns are free of LDS bank conflicts (64 banks of 4 bytes); V is only
+  // read transposed.
+  static constexpr int SKB = DK * 2 + 32;
+  static constexpr int SVB = DV * 2 + 32;
+  static constexpr int KX = 16;
   static constexpr int SKV = SKB > SVB ? SKB : SVB;
   static constexpr int KS = DK / 32;
   using W = WyCore<DK>;
@@ -126,7 +131,7 @@ struct Prepare2 {
 #pragma unroll
       for (int i = 0; i < KV_PT; ++i) {
         const int vv = tid + i * NT, r = vv / CK, c = vv % CK;
-        *reinterpret_cast<u32x4_t*>(sm.kv + r * SKB + c * 16) = pf.k[i];
+        *reinterpret_cast<u32x4_t*>(sm.kv + r * SKB + KX * ((r >> 3) & 1) + c * 16) = pf.k[i];
       }
       asm volatile("" ::"v"(pf.g), "v"(pf.b));  // g and beta arrive with K, not after it
       if (wave == 0) {
@@ -137,7 +142,7 @@ struct Prepare2 {
     __syncthreads();
 
     // ---- Gram matrix and the diagonal blocks of T ----
-    W::gram_diag(sm.kv, SKB, sm.t, sm.gam, sm.beta);
+    W::gram_diag(sm.kv, SKB, KX, sm.t, sm.gam, sm.beta);
     __syncthreads();
     W::off_diag(sm.t);
 
@@ -155,7 +160,7 @@ struct Prepare2 {
     {
       frag hi[2], lo[2];
       W::row_frags(sm.t, sm.bg, hi, lo);  // T diag(beta e^gamma)
-      W::template product<DK>(sm.kv, SKB, hi, lo, store_to(a.w, DK));
+      W::template product<DK>(sm.kv, SKB, KX, hi, lo, store_to(a.w, DK));
     }
     __syncthreads();  // every wave is done with K: V replaces it
 #pragma unroll
@@ -167,7 +172,7 @@ struct Prepare2 {
     {
       frag hi[2], lo[2];
       W::row_frags(sm.t, sm.beta, hi, lo);  // T diag(beta)
-      W::template product<DV>(sm.kv, SVB, hi, lo, store_to(a.u, DV));
+      W::template product<DV>(sm.kv, SVB, 0, hi, lo, store_to(a.u, DV));
     }
   }
 };

@@ -89,8 +89,20 @@ struct Scan2 {
   // and reads the same K/W tiles at the same pace (shared through L2).
   static constexpr int UBV = (MODE == 2) ? BV / 2 : BV;  // U columns staged per block
   static constexpr int RBU = UBV * 2;     // bytes per U row (this block's columns)
-  static constexpr int SW = RBW + 16;     // padded LDS row strides (bytes)
+  // Padded LDS row strides (bytes).  W rows are read as row fragments, two
+  // 8-byte pieces 32 bytes apart that the compiler issues as one
+  // ds_read2_b64: with a 24-byte pad those run at twice the rate of a
+  // 16-byte pad on gfx950 (measured: 118 against 61 bytes per clock and CU).
+  // The rows are then only 8-byte aligned, so the tile is stored in 8-byte
+  // pieces.
+  static constexpr int SW = RBW + 24;
   static constexpr int SK = RBW + 32;
+  // The fused output (P^T) and the fused prepare (Gram) also read K by rows,
+  // not only transposed: rows 8..15 of every 16 then sit 16 bytes further on
+  // (KX), which keeps the transposed reads free of LDS bank conflicts and
+  // makes the row reads free of them too (64 banks of 4 bytes: at the plain
+  // 288-byte stride rows r and r + 8 of a row read share their banks).
+  static constexpr int KX = (FO && DENSE) ? 16 : 0;
   static constexpr int SU = RBU + 32;
   static constexpr int CPW = RBW / 16;    // 16-byte chunks per W row
   static constexpr int CPU = RBU / 16;
@@ -217,7 +229,7 @@ struct Scan2 {
       for (int i = 0; i < W_PT; ++i) {
         const int v = tid + i * NT;
         const int r = v / CPW, c = v % CPW;
-        *reinterpret_cast<u32x4_t*>(buf + OFF_K + r * SK + c * 16) = st.k[i];
+        *reinterpret_cast<u32x4_t*>(buf + OFF_K + r * SK + KX * ((r >> 3) & 1) + c * 16) = st.k[i];
       }
 #pragma unroll
       for (int i = 0; i < U_PT; ++i) {
@@ -245,8 +257,10 @@ struct Scan2 {
     for (int i = 0; i < W_PT; ++i) {
       const int v = tid + i * NT;
       const int r = v / CPW, c = v % CPW;
-      *reinterpret_cast<u32x4_t*>(buf + OFF_W + r * SW + c * 16) = st.w[i];
-      *reinterpret_cast<u32x4_t*>(buf + OFF_K + r * SK + c * 16) = st.k[i];
+      u32x2_t* wd = reinterpret_cast<u32x2_t*>(buf + OFF_W + r * SW + c * 16);
+      wd[0] = u32x2_t{st.w[i].x, st.w[i].y};
+      wd[1] = u32x2_t{st.w[i].z, st.w[i].w};
+      *reinterpret_cast<u32x4_t*>(buf + OFF_K + r * SK + KX * ((r >> 3) & 1) + c * 16) = st.k[i];
     }
     if (MODE != 1 || x.has_u) {
 #pragma unroll
@@ -295,7 +309,7 @@ struct Scan2 {
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     float* t = reinterpret_cast<float*>(buf + OFF_W);
     const float* pg = reinterpret_cast<const float*>(buf + OFF_PG);
-    W::gram_diag(buf + OFF_K, SK, t, pg, pg + kChunk);
+    W::gram_diag(buf + OFF_K, SK, KX, t, pg, pg + kChunk);
     __syncthreads();
     W::off_diag(t);
     frag hw[2], lw[2], hu[2], lu[2];
@@ -304,11 +318,11 @@ struct Scan2 {
     __syncthreads();  // T is read: w takes the W tile
     const int row = 16 * wave + c16;
     char* wrow = buf + OFF_W + row * SW + 8 * g4;
-    W::template product<DK>(buf + OFF_K, SK, hw, lw, [&](int dt, const f32x4_t& acc) {
+    W::template product<DK>(buf + OFF_K, SK, KX, hw, lw, [&](int dt, const f32x4_t& acc) {
       *reinterpret_cast<u32x2_t*>(wrow + 32 * dt) = u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
     });
     f32x4_t uacc[UBV / 16];
-    W::template product<UBV>(buf + OFF_U, SU, hu, lu, [&](int dt, const f32x4_t& acc) { uacc[dt] = acc; });
+    W::template product<UBV>(buf + OFF_U, SU, 0, hu, lu, [&](int dt, const f32x4_t& acc) { uacc[dt] = acc; });
     __syncthreads();  // every wave has read V: u takes the U tile
     char* urow = buf + OFF_U + row * SU + 8 * g4;
 #pragma unroll
@@ -335,7 +349,7 @@ struct Scan2 {
     __syncthreads();  // every wave's h and v_new columns are staged
 
     // P^T[i][t] = k_i . q_t for t in tile `wave`, i tiles 0..wave
-    const char* rowk = buf + OFF_K + c16 * SK + (g4 >> 1) * 16 + (g4 & 1) * 8;  // + 16 tile SK + 64 s (+32)
+    const char* rowk = buf + OFF_K + c16 * SK + KX * (c16 >> 3) + 16 * g4;  // + 16 tile SK + 64 s
     f32x4_t pt[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) pt[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -344,8 +358,7 @@ struct Scan2 {
 #pragma unroll
       for (int it = 0; it < 4; ++it)
         if (it <= wave)
-          S::mma(pt[it], S::frag_from_quads(lds_b64(rowk, 16 * it * SK + 64 * s), lds_b64(rowk, 16 * it * SK + 64 * s + 32)),
-                 fq[s]);
+          S::mma(pt[it], lds_frag16(rowk, 16 * it * SK + 64 * s), fq[s]);
     const float* gm = reinterpret_cast<const float*>(buf + OFF_GM);
     const int t = 16 * wave + c16;
     const float gt = gm[t];
@@ -366,7 +379,7 @@ struct Scan2 {
     // rows (one value column each); v_new^T by transpose reads of the staged
     // v_new rows.
     constexpr int NCT = BV / 16;
-    const char* rowh = so + c16 * SHS + (g4 >> 1) * 16 + (g4 & 1) * 8;  // + 16 ct SHS + 64 s (+32)
+    const char* rowh = so + c16 * SHS + 16 * g4;  // + 16 ct SHS + 64 s
     f32x4_t acc[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -374,8 +387,7 @@ struct Scan2 {
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
-        S::mma(acc[ct], S::frag_from_quads(lds_b64(rowh, 16 * ct * SHS + 64 * s), lds_b64(rowh, 16 * ct * SHS + 64 * s + 32)),
-               fq[s]);
+        S::mma(acc[ct], lds_frag16(rowh, 16 * ct * SHS + 64 * s), fq[s]);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[ct] *= eg;
     const char* vb = so + (OFF_VS - OFF_HS) + (4 * g4 + (c16 >> 2)) * SVS + 8 * (c16 & 3);  // + 32 s SVS (+16 SVS) + 32 ct
@@ -454,7 +466,7 @@ struct Scan2 {
 
     // per-lane LDS bases (immediates carry the tile/step offsets)
     const char* wb = buf + OFF_W + c16 * SW + (g4 >> 1) * 16 + (g4 & 1) * 8;            // + 16 mt SW + 64 s (+32)
-    const char* kb = buf + OFF_K + (4 * g4 + (c16 >> 2)) * SK + (c16 & 3) * 8;          // + 32 s2 SK (+16 SK) + 32 dt
+    const char* kb = buf + OFF_K + (4 * g4 + (c16 >> 2)) * SK + KX * (g4 >> 1) + (c16 & 3) * 8;  // + 32 s2 SK (+16 SK) + 32 dt
     // (MODE 2: the state waves' columns colw lie in the first BV/2, the staged U tile)
     const char* ub = buf + OFF_U + (4 * g4 + (c16 >> 2)) * SU + (colw + 4 * (c16 & 3)) * 2;  // + 16 mt SU + 32 ct
     const float* nd_l = reinterpret_cast<const float*>(buf + OFF_D) + 4 * g4;          // + 16 mt
@@ -464,11 +476,11 @@ struct Scan2 {
     auto load_q = [&]() {
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (tok0 * H + x.hd) * DK;
       const rsrc_t rq = make_rsrc(qp, static_cast<uint32_t>(((nvalid - 1) * H + 1) * DK * 2));
-      const int qo = static_cast<int>((16 * wave + c16) * H * DK * 2) + (g4 >> 1) * 16 + (g4 & 1) * 8;
+      const int qo = static_cast<int>((16 * wave + c16) * H * DK * 2) + 16 * g4;  // contiguous k map
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         fq[s] = S::frag_from_quads(__builtin_amdgcn_raw_buffer_load_b64(rq, qo + 64 * s, 0, 0),
-                                   __builtin_amdgcn_raw_buffer_load_b64(rq, qo + 64 * s + 32, 0, 0));
+                                   __builtin_amdgcn_raw_buffer_load_b64(rq, qo + 64 * s + 8, 0, 0));
     };
     if constexpr (FO && !DENSE) load_q();
     u32x2_t uq[4][NC];

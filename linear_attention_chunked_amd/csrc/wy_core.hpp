@@ -8,7 +8,7 @@
 //   w      = T diag(beta exp(gamma)) K,   u = T diag(beta) V
 //
 // The caller owns the LDS: the K tile (row-major bf16 rows, any padded
-// stride), the 64 x 64 FP32 scratch of A and T (lower block triangle, kTri
+// stride; rows 8..15 of every 16 may sit kx bytes further on), the 64 x 64 FP32 scratch of A and T (lower block triangle, kTri
 // floats, 16-byte aligned) and three 64-float vectors (gamma, beta,
 // beta e^gamma).  The steps are the same instructions in the same order for
 // both callers, so w and u come out as the same bits.
@@ -88,23 +88,19 @@ struct WyCore {
   // count is a compile-time constant per wave, so every LDS read of the tile
   // is issued ahead of the products (no branch between them).
   template <int WV>
-  __device__ static __forceinline__ void gram_rows(const char* kt, int skb, float* t, const float* gam,
+  __device__ static __forceinline__ void gram_rows(const char* kt, int skb, int kx, float* t, const float* gam,
                                                    const float* beta) {
     const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
     f32x4_t acc[WV + 1];
 #pragma unroll
     for (int tj = 0; tj <= WV; ++tj) acc[tj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const char* kr = kt + c16 * skb + (g4 >> 1) * 16 + (g4 & 1) * 8;
+    // both operands are K rows: the contiguous k map, 16 bytes per lane (skb a multiple of 16)
+    const char* kr = kt + c16 * skb + kx * (c16 >> 3) + 16 * g4;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const frag fa = S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(kr + 16 * WV * skb + 64 * s),
-                                         *reinterpret_cast<const u32x2_t*>(kr + 16 * WV * skb + 64 * s + 32));
+      const frag fa = lds_frag16(kr, 16 * WV * skb + 64 * s);
 #pragma unroll
-      for (int tj = 0; tj <= WV; ++tj) {
-        const frag fb = S::frag_from_quads(*reinterpret_cast<const u32x2_t*>(kr + 16 * tj * skb + 64 * s),
-                                           *reinterpret_cast<const u32x2_t*>(kr + 16 * tj * skb + 64 * s + 32));
-        S::mma(acc[tj], fa, fb);
-      }
+      for (int tj = 0; tj <= WV; ++tj) S::mma(acc[tj], fa, lds_frag16(kr, 16 * tj * skb + 64 * s));
     }
     // Every LDS read is issued before any exponent: the (i < t) mask is a
     // select on values already in registers, not a branch around each read.
@@ -131,15 +127,15 @@ struct WyCore {
 
   // Gram matrix row tile `wave` (gram_rows), then the wave's diagonal block
   // T[b][b] = (I + A[b][b])^-1 (both in the wave's own rows of t: no
-  // barrier).  K: row-major tile of stride skb.
-  __device__ static __forceinline__ void gram_diag(const char* kt, int skb, float* t, const float* gam,
+  // barrier).  K: row-major tile of stride skb (row shift kx).
+  __device__ static __forceinline__ void gram_diag(const char* kt, int skb, int kx, float* t, const float* gam,
                                                    const float* beta) {
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     switch (wave) {
-      case 0: gram_rows<0>(kt, skb, t, gam, beta); break;
-      case 1: gram_rows<1>(kt, skb, t, gam, beta); break;
-      case 2: gram_rows<2>(kt, skb, t, gam, beta); break;
-      default: gram_rows<3>(kt, skb, t, gam, beta); break;
+      case 0: gram_rows<0>(kt, skb, kx, t, gam, beta); break;
+      case 1: gram_rows<1>(kt, skb, kx, t, gam, beta); break;
+      case 2: gram_rows<2>(kt, skb, kx, t, gam, beta); break;
+      default: gram_rows<3>(kt, skb, kx, t, gam, beta); break;
     }
     diag_solve(t);
   }
@@ -272,18 +268,19 @@ struct WyCore {
   }
 
   // Rows 16 wave .. 16 wave + 15 of (T diag(coef)) X for a row-major bf16 tile
-  // X (64 rows, stride `stride`, D columns): for every 16-column tile dt,
+  // X (64 rows, stride `stride`, rows 8..15 of every 16 kx bytes further on,
+  // D columns): for every 16-column tile dt,
   // out(dt, acc) with acc[r] = result[16 wave + c16][16 dt + 4 g4 + r] in FP32.
   // A operand X^T[d][i] by transpose reads of the row-major tile.  NS = the
   // 32-token steps below the diagonal (1 for the first two waves, 2 for the
   // others), a compile-time constant, so the reads of later tiles can be
   // issued ahead of the products of earlier ones.
   template <int NS, int D, class Out>
-  __device__ static __forceinline__ void product_ns(const char* tile, int stride, const frag (&hi)[2],
+  __device__ static __forceinline__ void product_ns(const char* tile, int stride, int kx, const frag (&hi)[2],
                                                     const frag (&lo)[2], Out& out) {
     const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
     const int tr_row = 4 * g4 + (c16 >> 2);
-    const int tr_col = 8 * (c16 & 3);
+    const int tr_col = 8 * (c16 & 3) + kx * (g4 >> 1);  // (row tr_row has bit 3 = g4 >> 1)
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       f32x4_t acc{0.f, 0.f, 0.f, 0.f};
@@ -299,13 +296,13 @@ struct WyCore {
   }
 
   template <int D, class Out>
-  __device__ static __forceinline__ void product(const char* tile, int stride, const frag (&hi)[2],
+  __device__ static __forceinline__ void product(const char* tile, int stride, int kx, const frag (&hi)[2],
                                                  const frag (&lo)[2], Out out) {
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     if (wave >= 2)
-      product_ns<2, D>(tile, stride, hi, lo, out);
+      product_ns<2, D>(tile, stride, kx, hi, lo, out);
     else
-      product_ns<1, D>(tile, stride, hi, lo, out);
+      product_ns<1, D>(tile, stride, kx, hi, lo, out);
   }
 };
 
