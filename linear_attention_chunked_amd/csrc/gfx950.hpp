@@ -17,15 +17,17 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 
 // Cache policy of a buffer store whose data no later access of the same
 // kernel reads (the staged per-chunk states and v_new rows of the scans, the
-// ABC states, the reverse walk's dh and dv; all written as whole 16-byte
-// pieces of full lines): non-temporal, so the streamed output does not push
+// ABC states; all written as whole 16-byte pieces of full lines):
+// non-temporal, so the streamed output does not push
 // the inputs that the column blocks of one (sequence, head) share out of the
 // XCD's L2.  Measured: the 64K x 8-head segmented pass 179 -> 172 us, the
 // 32-head packed scan 229 -> 222 us, ABC's slot-state walk (forward call
 // 202 -> 159 us, reverse 188 -> 163 us).
-// Stores of partial 128-byte lines (the fused output's 8-byte pieces) stay on
+// Stores of partial 128-byte lines (the fused output's 8-byte pieces, the
+// reverse walk's dh and dv pieces straight from its accumulators) stay on
 // the default policy: non-temporal there, L2 no longer merges them before
-// they go to HBM (88 -> 97 MB written per question_rows launch).  The same
+// they go to HBM (88 -> 97 MB written per question_rows launch of the fused
+// pass; 97 -> 74 MB and 40.5 -> 37.0 us for the reverse walk).  The same
 // policy bit on a load marks a stream that one workgroup reads once (the
 // scan's U columns on long chains).
 constexpr int kStreamStore = 2;

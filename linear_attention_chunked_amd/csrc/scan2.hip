@@ -168,9 +168,23 @@ struct Scan2 {
     const ScanArgs* a;
     int hd, col_blk, H, DV;
     bool has_u;
-    int vo_wk[W_PT];   // global byte offsets of this thread's W/K vectors (row-relative)
-    int vo_u[U_PT];
+    // global byte offsets (row-relative) of this thread's first W/K and U
+    // vectors; vector i sits i strides further on (NT / CPW rows, NT / CPU
+    // rows), added at each load (off_at) rather than held in registers
+    int vo_wk, vo_u;
+    int st_wk, st_u;
   };
+
+  // o + i s, formed next to the load that uses it: an asm add is not hoisted
+  // out of the chunk loop, so the per-vector offsets never occupy registers
+  // across it (holding them pushed the fused dense pass past its register
+  // budget into scratch spills)
+  __device__ static __forceinline__ int off_at(int o, int s, int i) {
+    if (i == 0) return o;
+    int r;
+    asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(i * s), "v"(o));
+    return r;
+  }
 
   // Issues the loads of one chunk.  A chunk past the row's end (nvalid <= 0)
   // gets empty buffer ranges: the same instructions are issued and return
@@ -187,11 +201,11 @@ struct Scan2 {
     const rsrc_t rk = make_rsrc(kp, wk_bytes);
     if constexpr (PREP) {
 #pragma unroll
-      for (int i = 0; i < W_PT; ++i) st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, x.vo_wk[i], 0, 0);
+      for (int i = 0; i < W_PT; ++i) st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_at(x.vo_wk, x.st_wk, i), 0, 0);
       const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (tok0 * H + x.hd) * x.DV + x.col_blk;
       const rsrc_t rv = make_rsrc(vp, live ? static_cast<uint32_t>(((nvalid - 1) * H * x.DV + UBV) * 2) : 0u);
 #pragma unroll
-      for (int i = 0; i < U_PT; ++i) st.u[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, x.vo_u[i], 0, 0);
+      for (int i = 0; i < U_PT; ++i) st.u[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off_at(x.vo_u, x.st_u, i), 0, 0);
       const uint32_t gb = live ? static_cast<uint32_t>(((nvalid - 1) * H + 1) * 4) : 0u;
       const int go = static_cast<int>(threadIdx.x * H * 4);
       st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.g + tok0 * H + x.hd, gb), go, 0, 0));
@@ -201,14 +215,14 @@ struct Scan2 {
     }
     const rsrc_t rw = make_rsrc(wp, wk_bytes);
 #pragma unroll
-    for (int i = 0; i < W_PT; ++i) st.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, x.vo_wk[i], 0, 0);
+    for (int i = 0; i < W_PT; ++i) st.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, off_at(x.vo_wk, x.st_wk, i), 0, 0);
 #pragma unroll
-    for (int i = 0; i < W_PT; ++i) st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, x.vo_wk[i], 0, 0);
+    for (int i = 0; i < W_PT; ++i) st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_at(x.vo_wk, x.st_wk, i), 0, 0);
     if (MODE != 1 || x.has_u) {
       const uint16_t* up = static_cast<const uint16_t*>(a.u) + (tok0 * H + x.hd) * x.DV + x.col_blk;
       const rsrc_t ru = make_rsrc(up, live ? static_cast<uint32_t>(((nvalid - 1) * H * x.DV + UBV) * 2) : 0u);
 #pragma unroll
-      for (int i = 0; i < U_PT; ++i) st.u[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, x.vo_u[i], 0, U_POL);
+      for (int i = 0; i < U_PT; ++i) st.u[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, off_at(x.vo_u, x.st_u, i), 0, U_POL);
     }
     if constexpr (KD) {  // thread d < DK: channel d's decay over the chunk
       const float* dp = a.decay + (hrow * H + x.hd) * DK;
@@ -756,16 +770,14 @@ struct Scan2 {
     const bool trans = (MODE == 1) && (x.col_blk >= x.DV);
     x.has_u = !trans;
     const int64_t H = a.H;
-#pragma unroll
-    for (int i = 0; i < W_PT; ++i) {
-      const int v = tid + i * NT;
-      x.vo_wk[i] = static_cast<int>((v / CPW) * H * DK * 2 + (v % CPW) * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < U_PT; ++i) {
-      const int v = min(tid + i * NT, kChunk * CPU - 1);
-      x.vo_u[i] = static_cast<int>((v / CPU) * H * x.DV * 2 + (v % CPU) * 16);
-    }
+    // vector i of a thread is tid + i NT: row tid / CPW + i NT / CPW, column tid % CPW
+    // (vectors past the U tile, if any, fall on rows past the chunk: the
+    // buffer range check returns zero and the LDS store skips them)
+    static_assert(NT % CPW == 0 && NT % CPU == 0, "whole rows per round of vectors");
+    x.vo_wk = static_cast<int>((tid / CPW) * H * DK * 2 + (tid % CPW) * 16);
+    x.st_wk = static_cast<int>((NT / CPW) * H * DK * 2);
+    x.vo_u = static_cast<int>((tid / CPU) * H * x.DV * 2 + (tid % CPU) * 16);
+    x.st_u = static_cast<int>((NT / CPU) * H * x.DV * 2);
     const int colw = wave * (BV / NW);
     const int DV = x.DV;
     const int hd = x.hd;

@@ -282,8 +282,8 @@ struct ScanBwd {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const u32x4_t q = __builtin_bit_cast(u32x4_t, Sb[s].v);
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{q.x, q.y}, rh, ho, 64 * s, kStreamStore);
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{q.z, q.w}, rh, ho, 64 * s + 32, kStreamStore);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{q.x, q.y}, rh, ho, 64 * s, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{q.z, q.w}, rh, ho, 64 * s + 32, 0);
       }
     }
     // GEMM1: acc = K dS (tokens x this wave's columns)
@@ -325,8 +325,8 @@ struct ScanBwd {
         for (int r = 0; r < 4; r += 2) {
           const uint32_t pk = pack_bf16x2(acc[mt][r], acc[mt][r + 1]);
           const int so2 = (16 * mt + r) * rs;
-          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk), rv, voff, so2, kStreamStore);
-          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk >> 16), rv, voff, so2 + rs, kStreamStore);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk), rv, voff, so2, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk >> 16), rv, voff, so2 + rs, 0);
         }
     }
     // B operands over tokens: -dv_new, and f_t dO_t
