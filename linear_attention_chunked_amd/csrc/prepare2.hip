@@ -16,6 +16,8 @@
 //     and takes the place of K in LDS once the w product has read K.  A and T
 //     keep only their blocks on or below the diagonal; the footprint (29.4 KB
 //     at 128 x 128) and at most 96 VGPRs let five workgroups share a CU.
+#include <type_traits>
+
 #include "gfx950.hpp"
 #include "kernels.hpp"
 #include "wy_core.hpp"
@@ -146,22 +148,38 @@ struct Prepare2 {
     __syncthreads();
     W::off_diag(sm.t);
 
-    // ---- w^T = K^T T'^T and u^T = V^T T''^T; wave = token tile of the output ----
-    const int t = 16 * wave + c16;
-    auto store_to = [&](void* out, int D) {
+    // ---- w^T = K^T T'^T and u^T = V^T T''^T by 16-token row blocks rb ----
+    // Row blocks 2 and 3 contract over twice the tokens of blocks 0 and 1 (T
+    // is lower triangular), so waves 2 and 3 form all but the last D / 64
+    // column tiles of their own block and waves 0 and 1 form those tiles
+    // after their own blocks: twelve tile-steps per wave at D = 128 instead
+    // of 8, 8, 16, 16.  Each element is the same products either way.
+    auto store_to = [&](void* out, int D, int rb) {
       uint16_t* op = static_cast<uint16_t*>(out) + (tok0 * H + hd) * D;
       const rsrc_t ro = make_rsrc(op, static_cast<uint32_t>(((nvalid - 1) * H + 1) * D * 2));
-      const int base = static_cast<int>(t * H * D * 2 + 4 * g4 * 2);
+      const int base = static_cast<int>((16 * rb + c16) * H * D * 2 + 4 * g4 * 2);
       return [=](int dt, const f32x4_t& acc) {
         __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])}, ro,
                                               base + 32 * dt, 0, 0);
       };
     };
-    {
+    auto product = [&](const float* coef, const char* tile, int stride, int kx, void* out, auto dcols) {
+      constexpr int D = decltype(dcols)::value;
+      constexpr int NT16 = D / 16, XT = D / 64;  // column tiles; tiles moved to waves 0 and 1
       frag hi[2], lo[2];
-      W::row_frags(sm.t, sm.bg, hi, lo);  // T diag(beta e^gamma)
-      W::template product<DK>(sm.kv, SKB, KX, hi, lo, store_to(a.w, DK));
-    }
+      W::row_frags(sm.t, coef, hi, lo);
+      if (wave >= 2) {
+        auto o = store_to(out, D, wave);
+        W::template product_tiles<2, 0, NT16 - XT>(tile, stride, kx, hi, lo, o);
+      } else {
+        auto o = store_to(out, D, wave);
+        W::template product_tiles<1, 0, NT16>(tile, stride, kx, hi, lo, o);
+        W::row_frags_of(wave + 2, sm.t, coef, hi, lo);
+        auto o2 = store_to(out, D, wave + 2);
+        W::template product_tiles<2, NT16 - XT, NT16>(tile, stride, kx, hi, lo, o2);
+      }
+    };
+    product(sm.bg, sm.kv, SKB, KX, a.w, std::integral_constant<int, DK>{});  // T diag(beta e^gamma) K
     __syncthreads();  // every wave is done with K: V replaces it
 #pragma unroll
     for (int i = 0; i < VV_PT; ++i) {
@@ -169,11 +187,7 @@ struct Prepare2 {
       *reinterpret_cast<u32x4_t*>(sm.kv + r * SVB + c * 16) = pf.v[i];
     }
     __syncthreads();
-    {
-      frag hi[2], lo[2];
-      W::row_frags(sm.t, sm.beta, hi, lo);  // T diag(beta)
-      W::template product<DV>(sm.kv, SVB, 0, hi, lo, store_to(a.u, DV));
-    }
+    product(sm.beta, sm.kv, SVB, 0, a.u, std::integral_constant<int, DV>{});  // T diag(beta) V
   }
 };
 

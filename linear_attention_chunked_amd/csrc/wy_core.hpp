@@ -241,9 +241,19 @@ struct WyCore {
   // This lane's operand fragments of row 16 wave + c16 of T diag(coef), split
   // into bf16 hi + lo; column blocks past the diagonal (not stored) are zero.
   __device__ static __forceinline__ void row_frags(const float* t, const float* coef, frag (&hi)[2], frag (&lo)[2]) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    row_frags_of(__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)), t, coef, hi, lo);
+  }
+
+  // The same for row 16 rb + c16 (rb: a 16-row block, uniform over the wave).
+  // No multiply-add contraction here: lo = x - bf16(x) of the rounded product
+  // x = T coef, whichever wave and kernel form it (the compiler would fuse
+  // the product into the subtraction in some inlined copies and not in
+  // others, and w / u would differ in their last bits between callers).
+  __device__ static __forceinline__ void row_frags_of(int rb, const float* t, const float* coef, frag (&hi)[2],
+                                                      frag (&lo)[2]) {
+#pragma clang fp contract(off)
+    const int wave = rb;
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
     const int tt = 16 * wave + c16;
     const int nsteps = (16 * wave + 15) / 32 + 1;  // T is lower triangular
     const float* tr = &t[toff(tt)];
@@ -278,11 +288,20 @@ struct WyCore {
   template <int NS, int D, class Out>
   __device__ static __forceinline__ void product_ns(const char* tile, int stride, int kx, const frag (&hi)[2],
                                                     const frag (&lo)[2], Out& out) {
+    product_tiles<NS, 0, D / 16>(tile, stride, kx, hi, lo, out);
+  }
+
+  // The same for the 16-column tiles T0 <= dt < T1 only (rows: those of the
+  // fragments).  Every output element is the same products in the same order
+  // whichever wave forms it.
+  template <int NS, int T0, int T1, class Out>
+  __device__ static __forceinline__ void product_tiles(const char* tile, int stride, int kx, const frag (&hi)[2],
+                                                       const frag (&lo)[2], Out& out) {
     const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
     const int tr_row = 4 * g4 + (c16 >> 2);
     const int tr_col = 8 * (c16 & 3) + kx * (g4 >> 1);  // (row tr_row has bit 3 = g4 >> 1)
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
+    for (int dt = T0; dt < T1; ++dt) {
       f32x4_t acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
