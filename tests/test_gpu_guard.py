@@ -1,7 +1,8 @@
 """GPU tests that the kernels write nothing past their output tensors.
 
-The token-row outputs (o, v_new, w, u, dv_local, the gradient of v_new) of
-the last packed sequence end inside a 64-token chunk; the kernels issue the
+The token-row outputs (o, v_new, w, u, dv_local, the gradient of v_new, the
+per-channel-decay kg, the ABC read's o and p) of the last sequence end
+inside a 64-token chunk; the kernels issue the
 whole chunk's stores and rely on the buffer range check to drop the rows
 past the tensor's last token.  Each output here is a view at the start of a
 larger buffer whose tail holds a sentinel pattern: after the call the tail
@@ -136,3 +137,49 @@ def test_reverse_pass_stays_in_bounds(pkg, problem):
     assert tail_intact(hb, dh.numel()), "dh: past the last chunk was written"
     assert tail_intact(vb, dv.numel()), "dv_new gradient: rows past the last token were written"
     assert torch.equal(dh, dh_ref) and torch.equal(dv, dv_ref)
+
+
+def test_per_channel_decay_stays_in_bounds(pkg):
+    """kda_chunk_prepare's w, u, kg and kda_chunk_output's o on the same
+    ragged batch, per-channel log decays."""
+    inp = make_gdr(43, lengths=LENGTHS, H=2, DK=128, DV=128, varlen=True, gates="logsigmoid_channels", h0_std=0.1)
+    q, k, v, g, beta, h0 = (getattr(inp, n).cuda() for n in ("q", "k", "v", "g", "beta", "h0"))
+    cu = inp.cu_seqlens
+    B, L = pkg.binding, pkg.lib()
+    P = B.Problem(k, v.shape[-1], cu)
+    g_ref, w_ref, u_ref, kg_ref, dec_ref = pkg.kda_chunk_prepare(k, v, g, beta, cu)
+    (wb, w), (ub, u), (kb, kg) = guarded(w_ref), guarded(u_ref), guarded(kg_ref)
+    g_cum, dec = torch.empty_like(g_ref), torch.empty_like(dec_ref)
+    B._check(L.kda_chunk_prepare(P.ref, B._ptr(k), B._ptr(v), B._ptr(g), B._ptr(beta), B._ptr(g_cum), B._ptr(w),
+                                 B._ptr(u), B._ptr(kg), B._ptr(dec), None), "kda prepare")
+    assert tail_intact(wb, w.numel()) and tail_intact(ub, u.numel()) and tail_intact(kb, kg.numel())
+    assert torch.equal(w, w_ref) and torch.equal(u, u_ref) and torch.equal(kg, kg_ref)
+    h, v_new, _ = pkg.kda_state_scan(kg_ref, w_ref, u_ref, dec_ref, h0, cu)
+    o_ref = pkg.kda_chunk_output(q, k, v_new, h, g_ref, inp.scale, cu)
+    ob, o = guarded(o_ref)
+    B._check(L.kda_chunk_output(P.ref, B._ptr(q), B._ptr(k), B._ptr(v_new), B._ptr(h), B._ptr(g_ref),
+                                ctypes.c_float(inp.scale), B._ptr(o), None), "kda output")
+    assert tail_intact(ob, o.numel()), "o: rows past the last token were written"
+    assert torch.equal(o, o_ref)
+
+
+def test_abc_read_stays_in_bounds(pkg):
+    """The ABC read's o (and slot weights p) of a sequence that ends 17 rows
+    into its last chunk."""
+    from workloads import make_abc
+
+    inp = make_abc(47, B=1, T=64 * 2 + 17, H=2, K=128, M=64, V=128)
+    k, v, s = inp.k.cuda(), inp.v.cuda(), inp.s.cuda()
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    q = torch.randn(k.shape, generator=gen, device="cuda").to(k.dtype)
+    z, hk, hv, _, _ = pkg.abc_affine_scan(k, v, s, emit_z=True, emit_final=False)
+    o_ref, p_ref = pkg.abc_chunk_output(q, k, v, s, z, hk, hv, 1.0, emit_p=True)
+    ob, o = guarded(o_ref)
+    pb, p = guarded(p_ref)
+    B, L = pkg.binding, pkg.lib()
+    pr = B.abc_problem(1, k.shape[1], 2, 128, 64, 128, B.GDR_BF16)
+    B._check(L.abc_chunk_output(ctypes.byref(pr), B._ptr(q), B._ptr(k), B._ptr(v), B._ptr(s), B._ptr(z), B._ptr(hk),
+                                B._ptr(hv), ctypes.c_float(1.0), B._ptr(o), B._ptr(p), None), "abc read")
+    assert tail_intact(ob, o.numel()), "o: rows past the last token were written"
+    assert tail_intact(pb, p.numel()), "p: rows past the last token were written"
+    assert torch.equal(o, o_ref) and torch.equal(p, p_ref)
